@@ -1,0 +1,42 @@
+"""CPU oracle for one tensor-parallel rank's share of the column->row MLP block.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it. It shares no code with the GPU
+library (``tensor_transformer_mlp_rank_amd``); both draw inputs from the
+separate ``synth`` module.
+
+Everything is plain float64 NumPy (SciPy's logistic function for the sigmoid),
+written as the definitions stated by the pages:
+
+* the block: a column-parallel fc1 (weight split along its output features),
+  a fused bias+GELU or the gated SwiGLU variant, then a row-parallel fc2 that
+  yields this rank's partial sum -- Megatron-LM code tour (pyshine.com),
+  sections "The Tensor-Parallel Primitives" and "The Transformer Stack";
+* the conjugate operators f (identity forward, all-reduce backward) and g
+  (all-reduce forward, identity backward) that fix which tensors are
+  replicated and which are partial -- "Megatron-LM / Megatron-Core" concept
+  note, section "Key math / How it works";
+* FP8 (per-tensor current scaling into OCP E4M3) for the forward pass --
+  code tour, "Honest Limits"; concept note, "Key math / How it works".
+
+Where the pages are silent (activation formulas, gated layout, scaling
+recipe) the readings are the textbook ones and are recorded in the design doc.
+
+Parity status: every function here is pinned by the CPU tests in
+``tests/test_oracle.py`` (library routines, closed forms, finite
+differences, the shard-sum invariant, brute force, the OCP E4M3 table).
+"""
+from .activations import gelu_tanh, gelu_tanh_grad, silu, silu_grad, sigmoid
+from .block import (shard_rank, select_features, rank_forward, rank_dgrad, rank_wgrad,
+                    unsharded_forward, unsharded_backward, block_loss, to_f64)
+from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, current_scale, quantize_e4m3,
+                  dequantize_e4m3)
+
+__all__ = [
+    "gelu_tanh", "gelu_tanh_grad", "silu", "silu_grad", "sigmoid",
+    "shard_rank", "select_features", "rank_forward", "rank_dgrad", "rank_wgrad",
+    "unsharded_forward", "unsharded_backward", "block_loss", "to_f64",
+    "E4M3_MAX", "e4m3_decode", "e4m3_encode", "current_scale", "quantize_e4m3",
+    "dequantize_e4m3",
+]
