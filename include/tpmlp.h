@@ -1,0 +1,181 @@
+/*
+ * libtpmlp -- one tensor-parallel rank's share of a column->row transformer MLP
+ * block on AMD Instinct MI355X (gfx950), forward and backward.
+ *
+ * The block (Megatron-LM code tour, pyshine.com, sections "The Tensor-Parallel
+ * Primitives" and "The Transformer Stack"):
+ *   fc1  column-parallel linear: its weight is split along the output features,
+ *        so this rank computes a slice of fc1's outputs from the full input;
+ *   act  a fused bias + GELU (tanh form), or the gated SwiGLU variant
+ *        a = silu(gate) * up;
+ *   fc2  row-parallel linear: its weight is split along the input features, so
+ *        this rank produces a partial sum of the block output that the caller
+ *        all-reduces across ranks.
+ * The conjugate operators of the concept note "Megatron-LM / Megatron-Core"
+ * (section "Key math / How it works") fix the boundary: the input x and the
+ * output gradient dy are replicated on every rank and used as given; the
+ * outputs y_partial and dx_partial are partial sums whose all-reduce is the
+ * caller's job. No call communicates.
+ *
+ * Notation and layouts (all row-major, contiguous, 16-byte aligned):
+ *   T tokens, H hidden, Fs intermediate features of this shard, G = 2 for
+ *   SwiGLU (gate and up halves), 1 for GELU.
+ *   x, dy, y_partial, dx_partial : [T, H]
+ *   W1_shard : [G*Fs, H]  ([out, in]; for SwiGLU rows [0,Fs) gate, [Fs,2Fs) up)
+ *   b1_shard : [G*Fs]     (GELU only)
+ *   W2_shard : [H, Fs]
+ *   h_saved  : [T, G*Fs]  pre-activation including the bias (saved for backward)
+ *   a_saved  : [T, Fs]    activation output (fc2's input)
+ *   dH       : [T, G*Fs]  gradient at the pre-activation
+ *   dW1 [G*Fs, H], db1 [G*Fs], dW2 [H, Fs] : float32 always.
+ *
+ * Element types by tpmlp_desc.dtype:
+ *   TPMLP_F32  : everything float32.
+ *   TPMLP_BF16 : x, W1, b1, W2, dy, h, a, dH, y_partial, dx_partial bfloat16;
+ *                products accumulate in float32.
+ *   TPMLP_E4M3 : forward only, GELU only. x, W1, W2 are OCP E4M3 codes with
+ *                per-tensor float32 dequantisation factors (scale_inv);
+ *                b1, h_saved and y_partial are bfloat16; a_saved receives the
+ *                E4M3 codes of the activation, quantised with per-tensor
+ *                current scaling (scale = 448 / amax(a), amax 0 -> scale 1).
+ *
+ * Ownership: the caller allocates and frees every buffer, the workspace too
+ * (size from tpmlp_workspace_size). Pointers are device pointers unless noted.
+ * The library keeps no per-call state. Its only global state is the timing
+ * facility at the end of this header.
+ *
+ * Asynchrony: compute calls validate their arguments on the host, then only
+ * enqueue kernels on `stream` (NULL = the default stream) and return. On a
+ * validation error nothing is enqueued. Device faults surface at the caller's
+ * next synchronisation.
+ *
+ * Aliasing: no output may overlap any input or another output.
+ */
+#ifndef TPMLP_H
+#define TPMLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TPMLP_ABI_VERSION 1
+
+typedef enum {
+  TPMLP_OK = 0,
+  TPMLP_E_NULL = 1,        /* a required pointer is NULL */
+  TPMLP_E_SHAPE = 2,       /* T < 0, H <= 0, Fs <= 0, H or Fs not a multiple of 16, or too large */
+  TPMLP_E_DTYPE = 3,       /* unknown dtype or activation code */
+  TPMLP_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  TPMLP_E_UNSUPPORTED = 5, /* valid but not provided (E4M3 backward, E4M3 SwiGLU, SwiGLU bias) */
+  TPMLP_E_WORKSPACE = 6,   /* workspace NULL or smaller than tpmlp_workspace_size */
+  TPMLP_E_HIP = 7          /* a HIP runtime call failed while enqueuing */
+} tpmlp_status;
+
+typedef enum { TPMLP_F32 = 0, TPMLP_BF16 = 1, TPMLP_E4M3 = 2 } tpmlp_dtype;
+typedef enum { TPMLP_ACT_GELU_TANH = 0, TPMLP_ACT_SWIGLU = 1 } tpmlp_act;
+typedef enum { TPMLP_CALL_FWD = 0, TPMLP_CALL_DGRAD = 1, TPMLP_CALL_WGRAD = 2 } tpmlp_call;
+
+/* Problem description (host memory). */
+typedef struct tpmlp_desc {
+  int64_t tokens;     /* T >= 0 (0: calls are valid and enqueue nothing, except
+                         wgrad with accumulate = 0, which zero-fills its outputs) */
+  int64_t hidden;     /* H > 0, multiple of 16 */
+  int64_t ffn_shard;  /* Fs > 0, multiple of 16 */
+  int32_t act;        /* tpmlp_act */
+  int32_t dtype;      /* tpmlp_dtype */
+  int32_t has_bias;   /* 1: b1_shard is used (GELU only); 0: no bias */
+  int32_t reserved;   /* must be 0 */
+} tpmlp_desc;
+
+/* FP8 forward scales (host struct holding device pointers to single floats). */
+typedef struct tpmlp_fp8_scales {
+  const float* x_scale_inv;   /* in: dequantisation factor of x */
+  const float* w1_scale_inv;  /* in: of W1_shard */
+  const float* w2_scale_inv;  /* in: of W2_shard */
+  float* a_amax;              /* out: max |a| over the bfloat16-rounded activation */
+  float* a_scale_inv;         /* out: 1 / (448 / a_amax) in float32, as used by fc2 */
+} tpmlp_fp8_scales;
+
+/* Bytes of workspace the call needs (0 if none). Returns 0 for an invalid desc. */
+size_t tpmlp_workspace_size(const tpmlp_desc* desc, int32_t call);
+
+/*
+ * Forward (fc1 -> activation -> fc2), enqueued on `stream`:
+ *   h = x . W1_shard^T (+ b1_shard);  a = act(h);  y_partial = a . W2_shard^T.
+ * For E4M3 the fc1 accumulator is multiplied by x_scale_inv * w1_scale_inv
+ * before the bias; `a` is rounded to bfloat16, its amax taken, quantised to
+ * E4M3 into a_saved; fc2's accumulator is multiplied by a_scale_inv *
+ * w2_scale_inv. h_saved may be NULL (inference: nothing saved for backward).
+ * a_saved is required. b1_shard is required iff desc->has_bias. fp8 must be
+ * non-NULL iff dtype is E4M3.
+ */
+tpmlp_status tpmlp_fwd(const tpmlp_desc* desc, const void* x, const void* W1_shard,
+                       const void* b1_shard, const void* W2_shard, void* y_partial,
+                       void* h_saved, void* a_saved, const tpmlp_fp8_scales* fp8,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Data gradient (fc2 dgrad with the activation derivative fused, then fc1 dgrad):
+ *   dA = dy . W2_shard;
+ *   GELU:   dH = dA * gelu'(h)
+ *   SwiGLU: dH = [dA * up * silu'(gate) | dA * silu(gate)]  (gate, up = halves of h)
+ *   dx_partial = dH . W1_shard.
+ * dH is written (the caller keeps it for tpmlp_bwd_wgrad). F32 or BF16 only.
+ */
+tpmlp_status tpmlp_bwd_dgrad(const tpmlp_desc* desc, const void* dy, const void* W1_shard,
+                             const void* W2_shard, const void* h_saved, void* dH,
+                             void* dx_partial, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
+ * Weight gradients, float32 results:
+ *   dW2 = dy^T . a_saved;  dW1 = dH^T . x;  db1 = column sums of dH (if has_bias).
+ * accumulate = 0 overwrites the outputs; accumulate = 1 adds into them
+ * (gradient accumulation across micro-batches). db1 may be NULL only when
+ * has_bias = 0. F32 or BF16 only.
+ */
+tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* desc, const void* dy, const void* x,
+                             const void* a_saved, const void* dH, float* dW1, float* db1,
+                             float* dW2, int32_t accumulate, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Per-tensor current-scaling quantiser (the FP8 recipe used for `a` inside
+ * tpmlp_fwd, exported so callers can produce E4M3 inputs on the device):
+ *   amax = max |src|; scale = 448 / amax in float32 (1 if amax is 0);
+ *   dst[i] = E4M3(clamp(fl32(src[i] * scale), -448, 448)), round to nearest even;
+ *   *amax_out = amax; *scale_inv_out = 1 / scale in float32.
+ * src_dtype is TPMLP_F32 or TPMLP_BF16; n >= 0 elements; dst n bytes.
+ * Workspace: tpmlp_quantize_workspace_size(n) bytes.
+ */
+size_t tpmlp_quantize_workspace_size(int64_t n);
+tpmlp_status tpmlp_quantize_e4m3(int32_t src_dtype, const void* src, int64_t n, uint8_t* dst,
+                                 float* amax_out, float* scale_inv_out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+const char* tpmlp_strerror(tpmlp_status status);
+int32_t tpmlp_abi_version(void);
+/* Text of the last HIP error seen by the library on this thread ("" if none). */
+const char* tpmlp_last_hip_error(void);
+
+/*
+ * Kernel timing (host-side facility; not thread-safe, one stream at a time).
+ * While enabled, every kernel the library launches whose name contains
+ * `name_filter` (NULL or "" = all) is bracketed by two HIP events recorded on
+ * its launch stream. tpmlp_timing_collect synchronises on those events and
+ * returns, per kernel name, the launch count and total milliseconds.
+ * tpmlp_timing_enable(0, NULL) disables and discards records.
+ */
+tpmlp_status tpmlp_timing_enable(int32_t enable, const char* name_filter);
+/* Fills up to `cap` entries; returns the number of distinct kernel names (or -1 on error). */
+int32_t tpmlp_timing_collect(const char** names, int64_t* counts, double* total_ms, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPMLP_H */

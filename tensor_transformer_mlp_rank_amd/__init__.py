@@ -1,0 +1,243 @@
+"""Python binding of libtpmlp: one tensor-parallel rank's share of the
+column->row MLP block (fc1 column-parallel, bias+GELU or SwiGLU, fc2
+row-parallel partial sum), forward and backward, on MI355X.
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the block runs in the library's HIP kernels
+(``libtpmlp.so``, built in-tree by ``build.py``). If the library is missing
+this module raises on import -- there is no fallback path.
+
+The C entry points keep their names here (``tpmlp_fwd``, ``tpmlp_bwd_dgrad``,
+``tpmlp_bwd_wgrad``, ``tpmlp_quantize_e4m3``) and take preallocated output
+tensors; ``fwd``, ``bwd_dgrad`` and ``bwd_wgrad`` are conveniences that
+allocate the outputs with torch and call them. Layouts are those of
+``include/tpmlp.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtpmlp.so")
+
+F32, BF16, E4M3 = 0, 1, 2
+GELU, SWIGLU = 0, 1
+CALL_FWD, CALL_DGRAD, CALL_WGRAD = 0, 1, 2
+
+STATUS = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_DTYPE", 4: "E_ALIGN", 5: "E_UNSUPPORTED",
+          6: "E_WORKSPACE", 7: "E_HIP"}
+
+_DTYPE_CODES = {"f32": F32, "bf16": BF16, "e4m3": E4M3}
+_ACT_CODES = {"gelu": GELU, "swiglu": SWIGLU}
+_TORCH = {F32: torch.float32, BF16: torch.bfloat16, E4M3: torch.uint8}
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
+                ("ffn_shard", ctypes.c_int64), ("act", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("has_bias", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class Fp8Scales(ctypes.Structure):
+    _fields_ = [("x_scale_inv", ctypes.c_void_p), ("w1_scale_inv", ctypes.c_void_p),
+                ("w2_scale_inv", ctypes.c_void_p), ("a_amax", ctypes.c_void_p),
+                ("a_scale_inv", ctypes.c_void_p)]
+
+
+class TpmlpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {STATUS.get(status, status)} ({lib.tpmlp_strerror(status).decode()})"
+        if status == 7:
+            msg += f": {lib.tpmlp_last_hip_error().decode()}"
+        super().__init__(msg)
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(or python tensor_transformer_mlp_rank_amd/build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    pdesc = ctypes.POINTER(Desc)
+    L.tpmlp_fwd.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Fp8Scales), vp, sz, vp]
+    L.tpmlp_bwd_dgrad.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.tpmlp_bwd_wgrad.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.tpmlp_quantize_e4m3.argtypes = [i32, vp, i64, vp, vp, vp, vp, sz, vp]
+    L.tpmlp_quantize_workspace_size.argtypes = [i64]
+    L.tpmlp_quantize_workspace_size.restype = sz
+    L.tpmlp_workspace_size.argtypes = [pdesc, i32]
+    L.tpmlp_workspace_size.restype = sz
+    for f in ("tpmlp_fwd", "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad", "tpmlp_quantize_e4m3",
+              "tpmlp_timing_enable"):
+        getattr(L, f).restype = i32
+    L.tpmlp_strerror.argtypes = [i32]
+    L.tpmlp_strerror.restype = ctypes.c_char_p
+    L.tpmlp_last_hip_error.restype = ctypes.c_char_p
+    L.tpmlp_abi_version.restype = i32
+    L.tpmlp_timing_enable.argtypes = [i32, ctypes.c_char_p]
+    L.tpmlp_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(i64),
+                                       ctypes.POINTER(ctypes.c_double), i32]
+    L.tpmlp_timing_collect.restype = i32
+    return L
+
+
+lib = _load()
+
+
+# ------------------------------------------------------------------ marshalling
+def make_desc(tokens: int, hidden: int, ffn_shard: int, act="gelu", dtype="bf16",
+              has_bias: bool = True) -> Desc:
+    a = _ACT_CODES[act] if isinstance(act, str) else int(act)
+    d = _DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
+    return Desc(int(tokens), int(hidden), int(ffn_shard), a, d, int(bool(has_bias)), 0)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libtpmlp must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libtpmlp must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise TpmlpError(status, where)
+
+
+def workspace_size(desc: Desc, call: int) -> int:
+    return int(lib.tpmlp_workspace_size(ctypes.byref(desc), call))
+
+
+def tpmlp_fwd(desc, x, W1, b1, W2, y, h, a, fp8=None, workspace=None, stream=None):
+    ws = _ptr(workspace)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sc = None if fp8 is None else ctypes.byref(fp8)
+    _check(lib.tpmlp_fwd(ctypes.byref(desc), _ptr(x), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(y),
+                         _ptr(h), _ptr(a), sc, ws, nbytes, _stream(stream)), "tpmlp_fwd")
+
+
+def tpmlp_bwd_dgrad(desc, dy, W1, W2, h, dH, dx, workspace=None, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.tpmlp_bwd_dgrad(ctypes.byref(desc), _ptr(dy), _ptr(W1), _ptr(W2), _ptr(h),
+                               _ptr(dH), _ptr(dx), _ptr(workspace), nbytes, _stream(stream)),
+           "tpmlp_bwd_dgrad")
+
+
+def tpmlp_bwd_wgrad(desc, dy, x, a, dH, dW1, db1, dW2, accumulate=False, workspace=None,
+                    stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.tpmlp_bwd_wgrad(ctypes.byref(desc), _ptr(dy), _ptr(x), _ptr(a), _ptr(dH),
+                               _ptr(dW1), _ptr(db1), _ptr(dW2), int(bool(accumulate)),
+                               _ptr(workspace), nbytes, _stream(stream)), "tpmlp_bwd_wgrad")
+
+
+def tpmlp_quantize_e4m3(src, dst, amax, scale_inv, workspace, stream=None):
+    dt = BF16 if src.dtype == torch.bfloat16 else F32 if src.dtype == torch.float32 else -1
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.tpmlp_quantize_e4m3(dt, _ptr(src), src.numel(), _ptr(dst), _ptr(amax),
+                                   _ptr(scale_inv), _ptr(workspace), nbytes, _stream(stream)),
+           "tpmlp_quantize_e4m3")
+
+
+# ------------------------------------------------------------------ conveniences
+def _empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+def fwd(desc, x, W1, b1, W2, save_h=True, fp8_in_scales=None, stream=None):
+    """Run the forward; returns dict y, h (or None), a, and for E4M3 a_amax,
+    a_scale_inv. ``fp8_in_scales`` = (x_scale_inv, w1_scale_inv, w2_scale_inv)
+    one-element fp32 device tensors."""
+    dev = x.device
+    T, H, Fs = desc.tokens, desc.hidden, desc.ffn_shard
+    G = 2 if desc.act == SWIGLU else 1
+    act_t = torch.bfloat16 if desc.dtype in (BF16, E4M3) else torch.float32
+    out = {"y": _empty((T, H), act_t, dev),
+           "h": _empty((T, G * Fs), act_t, dev) if save_h else None,
+           "a": _empty((T, Fs), torch.uint8 if desc.dtype == E4M3 else act_t, dev)}
+    sc = None
+    if desc.dtype == E4M3:
+        out["a_amax"] = torch.zeros(1, dtype=torch.float32, device=dev)
+        out["a_scale_inv"] = torch.zeros(1, dtype=torch.float32, device=dev)
+        xs, w1s, w2s = fp8_in_scales
+        sc = Fp8Scales(_ptr(xs), _ptr(w1s), _ptr(w2s), _ptr(out["a_amax"]), _ptr(out["a_scale_inv"]))
+    n = workspace_size(desc, CALL_FWD)
+    ws = _empty((max(n, 1),), torch.uint8, dev) if n else None
+    tpmlp_fwd(desc, x, W1, b1, W2, out["y"], out["h"], out["a"], sc, ws, stream)
+    return out
+
+
+def bwd_dgrad(desc, dy, W1, W2, h, stream=None):
+    dev = dy.device
+    T, H, Fs = desc.tokens, desc.hidden, desc.ffn_shard
+    G = 2 if desc.act == SWIGLU else 1
+    t = _TORCH[desc.dtype]
+    out = {"dH": _empty((T, G * Fs), t, dev), "dx": _empty((T, H), t, dev)}
+    tpmlp_bwd_dgrad(desc, dy, W1, W2, h, out["dH"], out["dx"], None, stream)
+    return out
+
+
+def bwd_wgrad(desc, dy, x, a, dH, accumulate_into=None, stream=None):
+    """fp32 weight gradients. ``accumulate_into`` = dict dW1, db1, dW2 of
+    existing fp32 buffers to add into (accumulate mode)."""
+    dev = dy.device
+    H, Fs = desc.hidden, desc.ffn_shard
+    G = 2 if desc.act == SWIGLU else 1
+    if accumulate_into is not None:
+        out = accumulate_into
+    else:
+        out = {"dW1": _empty((G * Fs, H), torch.float32, dev),
+               "db1": _empty((G * Fs,), torch.float32, dev) if desc.has_bias else None,
+               "dW2": _empty((H, Fs), torch.float32, dev)}
+    tpmlp_bwd_wgrad(desc, dy, x, a, dH, out["dW1"], out.get("db1"), out["dW2"],
+                    accumulate=accumulate_into is not None, stream=stream)
+    return out
+
+
+def quantize_e4m3(src, stream=None):
+    """E4M3 codes (uint8, same shape) plus one-element amax and scale_inv."""
+    dev = src.device
+    dst = _empty(src.shape, torch.uint8, dev)
+    amax = torch.zeros(1, dtype=torch.float32, device=dev)
+    sinv = torch.zeros(1, dtype=torch.float32, device=dev)
+    n = int(lib.tpmlp_quantize_workspace_size(src.numel()))
+    ws = _empty((max(n, 256),), torch.uint8, dev)
+    tpmlp_quantize_e4m3(src, dst, amax, sinv, ws, stream)
+    return dst, amax, sinv
+
+
+# ------------------------------------------------------------------ timing
+def timing_enable(enable: bool, name_filter: str | None = None):
+    lib.tpmlp_timing_enable(int(bool(enable)), None if name_filter is None else name_filter.encode())
+
+
+def timing_collect(cap: int = 64) -> dict:
+    names = (ctypes.c_char_p * cap)()
+    counts = (ctypes.c_int64 * cap)()
+    tot = (ctypes.c_double * cap)()
+    n = lib.tpmlp_timing_collect(names, counts, tot, cap)
+    if n < 0:
+        raise RuntimeError("tpmlp_timing_collect failed")
+    return {names[i].decode(): (int(counts[i]), float(tot[i])) for i in range(min(n, cap))}
+
+
+__all__ = ["Desc", "Fp8Scales", "TpmlpError", "make_desc", "workspace_size", "tpmlp_fwd",
+           "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad", "tpmlp_quantize_e4m3", "fwd", "bwd_dgrad",
+           "bwd_wgrad", "quantize_e4m3", "timing_enable", "timing_collect", "lib", "LIB_PATH",
+           "F32", "BF16", "E4M3", "GELU", "SWIGLU"]

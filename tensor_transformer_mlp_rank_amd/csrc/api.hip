@@ -1,0 +1,381 @@
+// libtpmlp C ABI: argument validation, kernel selection and launch, and the
+// kernel timing facility. The interface is documented in include/tpmlp.h.
+#include <string.h>
+
+#include <initializer_list>
+
+#include <string>
+#include <vector>
+
+#include "../../include/tpmlp.h"
+#include "launch.h"
+
+using namespace tpmlp;
+
+namespace {
+
+thread_local std::string g_last_hip_error;
+
+tpmlp_status hip_fail(hipError_t err) {
+  g_last_hip_error = hipGetErrorString(err);
+  return TPMLP_E_HIP;
+}
+
+// ---------------------------------------------------------------- timing
+struct TimingRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+bool g_timing = false;
+std::string g_filter;
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+std::vector<std::string> g_names_out;
+
+hipError_t take_event(hipEvent_t* ev) {
+  if (!g_pool.empty()) {
+    *ev = g_pool.back();
+    g_pool.pop_back();
+    return hipSuccess;
+  }
+  return hipEventCreate(ev);
+}
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  if (!g_timing || (!g_filter.empty() && strstr(name, g_filter.c_str()) == nullptr))
+    return launch();
+  TimingRec r{name, nullptr, nullptr};
+  hipError_t err = take_event(&r.start);
+  if (err == hipSuccess) err = take_event(&r.stop);
+  if (err == hipSuccess) err = hipEventRecord(r.start, s);
+  if (err != hipSuccess) return err;
+  err = launch();
+  if (err != hipSuccess) return err;
+  err = hipEventRecord(r.stop, s);
+  if (err != hipSuccess) return err;
+  g_recs.push_back(r);
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------- validation
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 22;     // H and G*Fs (row length bound)
+constexpr int64_t kMaxTokens = int64_t(1) << 30;
+
+tpmlp_status check_desc(const tpmlp_desc* d) {
+  if (!d) return TPMLP_E_NULL;
+  if (d->reserved != 0) return TPMLP_E_DTYPE;
+  if (d->dtype < TPMLP_F32 || d->dtype > TPMLP_E4M3) return TPMLP_E_DTYPE;
+  if (d->act != TPMLP_ACT_GELU_TANH && d->act != TPMLP_ACT_SWIGLU) return TPMLP_E_DTYPE;
+  if (d->has_bias != 0 && d->has_bias != 1) return TPMLP_E_DTYPE;
+  if (d->tokens < 0 || d->hidden <= 0 || d->ffn_shard <= 0) return TPMLP_E_SHAPE;
+  if (d->hidden % 16 != 0 || d->ffn_shard % 16 != 0) return TPMLP_E_SHAPE;
+  const int64_t g = d->act == TPMLP_ACT_SWIGLU ? 2 : 1;
+  if (d->hidden > kMaxDim || g * d->ffn_shard > kMaxDim || d->tokens > kMaxTokens)
+    return TPMLP_E_SHAPE;
+  if (d->act == TPMLP_ACT_SWIGLU && d->has_bias) return TPMLP_E_UNSUPPORTED;
+  if (d->dtype == TPMLP_E4M3 && d->act != TPMLP_ACT_GELU_TANH) return TPMLP_E_UNSUPPORTED;
+  return TPMLP_OK;
+}
+
+// Pointers that must be present and 16-byte aligned.
+tpmlp_status check_ptrs(std::initializer_list<const void*> req) {
+  for (const void* p : req)
+    if (!p) return TPMLP_E_NULL;
+  for (const void* p : req)
+    if (!aligned16(p)) return TPMLP_E_ALIGN;
+  return TPMLP_OK;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int fp8_fc1_parts(const tpmlp_desc* d) {
+  GemmArgs g{};
+  g.M = (int)d->tokens;
+  g.N = (int)d->ffn_shard;
+  return mfma_grid(FC1_FWD_GELU, g);
+}
+
+size_t workspace_bytes(const tpmlp_desc* d, int32_t call) {
+  if (call == TPMLP_CALL_FWD && d->dtype == TPMLP_E4M3) {
+    const size_t a_bytes = align_up((size_t)d->tokens * (size_t)d->ffn_shard * 2, 256);
+    const size_t parts = align_up((size_t)fp8_fc1_parts(d) * 4 + 4, 256);
+    return a_bytes + parts;
+  }
+  return 0;
+}
+
+tpmlp_status check_workspace(const tpmlp_desc* d, int32_t call, void* ws, size_t ws_bytes) {
+  const size_t need = workspace_bytes(d, call);
+  if (need == 0) return TPMLP_OK;
+  if (!ws || ws_bytes < need) return TPMLP_E_WORKSPACE;
+  if (!aligned16(ws)) return TPMLP_E_ALIGN;
+  return TPMLP_OK;
+}
+
+// ---------------------------------------------------------------- GEMM step dispatch
+const char* step_name(Kind kind, Step step) {
+  static const char* names[3][kNumSteps] = {
+      {"fc1_fwd_gelu.f32", "fc1_fwd_swiglu.f32", "fc2_fwd.f32", "fc2_dgrad_gelu.f32",
+       "fc2_dgrad_swiglu.f32", "fc1_dgrad.f32", "wgrad.f32", "wgrad_colsum.f32"},
+      {"fc1_fwd_gelu.bf16", "fc1_fwd_swiglu.bf16", "fc2_fwd.bf16", "fc2_dgrad_gelu.bf16",
+       "fc2_dgrad_swiglu.bf16", "fc1_dgrad.bf16", "wgrad.bf16", "wgrad_colsum.bf16"},
+      {"fc1_fwd_gelu.e4m3", "fc1_fwd_swiglu.e4m3", "fc2_fwd.e4m3", "fc2_dgrad_gelu.e4m3",
+       "fc2_dgrad_swiglu.e4m3", "fc1_dgrad.e4m3", "wgrad.e4m3", "wgrad_colsum.e4m3"}};
+  return names[kind][step];
+}
+
+hipError_t run_step(Kind kind, Step step, GemmArgs g, const EpiArgs& e, hipStream_t s) {
+  const int nb = (kind == KIND_F32) ? f32_grid(step, g) : mfma_grid(step, g);
+  if (nb == 0) return hipSuccess;
+  return timed(step_name(kind, step), s, [&]() {
+    return kind == KIND_F32 ? f32_launch(step, g, e, s)
+                            : mfma_launch(kind == KIND_E4M3, step, g, e, s);
+  });
+}
+
+GemmArgs make_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
+                   int64_t K, int64_t pair_off) {
+  GemmArgs g{};
+  g.A = A;
+  g.B = B;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.pair_off = (int)pair_off;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tpmlp_strerror(tpmlp_status s) {
+  switch (s) {
+    case TPMLP_OK: return "success";
+    case TPMLP_E_NULL: return "a required pointer is NULL";
+    case TPMLP_E_SHAPE: return "invalid sizes (T >= 0; H, Fs > 0 and multiples of 16; within limits)";
+    case TPMLP_E_DTYPE: return "unknown dtype, activation or flag value";
+    case TPMLP_E_ALIGN: return "a pointer is not 16-byte aligned";
+    case TPMLP_E_UNSUPPORTED: return "combination not provided (E4M3 backward, E4M3 SwiGLU, SwiGLU bias)";
+    case TPMLP_E_WORKSPACE: return "workspace missing or too small";
+    case TPMLP_E_HIP: return "HIP runtime error while enqueuing (see tpmlp_last_hip_error)";
+  }
+  return "unknown status";
+}
+
+int32_t tpmlp_abi_version(void) { return TPMLP_ABI_VERSION; }
+
+const char* tpmlp_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+size_t tpmlp_workspace_size(const tpmlp_desc* desc, int32_t call) {
+  if (check_desc(desc) != TPMLP_OK) return 0;
+  if (call < TPMLP_CALL_FWD || call > TPMLP_CALL_WGRAD) return 0;
+  return workspace_bytes(desc, call);
+}
+
+tpmlp_status tpmlp_fwd(const tpmlp_desc* d, const void* x, const void* W1, const void* b1,
+                       const void* W2, void* y, void* h_saved, void* a_saved,
+                       const tpmlp_fp8_scales* fp8, void* ws, size_t ws_bytes,
+                       hipStream_t s) {
+  tpmlp_status st = check_desc(d);
+  if (st != TPMLP_OK) return st;
+  if ((st = check_ptrs({x, W1, W2, y, a_saved})) != TPMLP_OK) return st;
+  if (d->has_bias && (st = check_ptrs({b1})) != TPMLP_OK) return st;
+  if (h_saved && !aligned16(h_saved)) return TPMLP_E_ALIGN;
+  const bool is_fp8 = d->dtype == TPMLP_E4M3;
+  if (is_fp8 != (fp8 != nullptr)) return is_fp8 ? TPMLP_E_NULL : TPMLP_E_DTYPE;
+  if (is_fp8 && (!fp8->x_scale_inv || !fp8->w1_scale_inv || !fp8->w2_scale_inv ||
+                 !fp8->a_amax || !fp8->a_scale_inv))
+    return TPMLP_E_NULL;
+  if ((st = check_workspace(d, TPMLP_CALL_FWD, ws, ws_bytes)) != TPMLP_OK) return st;
+
+  const int64_t T = d->tokens, H = d->hidden, Fs = d->ffn_shard;
+  const bool swiglu = d->act == TPMLP_ACT_SWIGLU;
+  const int64_t GFs = swiglu ? 2 * Fs : Fs;
+  const Kind kind = d->dtype == TPMLP_F32 ? KIND_F32 : d->dtype == TPMLP_BF16 ? KIND_BF16 : KIND_E4M3;
+  hipError_t err;
+
+  if (!is_fp8) {
+    if (T == 0) return TPMLP_OK;
+    EpiArgs e1{};
+    e1.out = a_saved; e1.ldo = Fs;
+    e1.out2 = h_saved; e1.ldo2 = GFs;
+    e1.bias = d->has_bias ? b1 : nullptr;
+    GemmArgs g1 = make_gemm(x, H, W1, H, T, Fs, H, Fs);
+    err = run_step(kind, swiglu ? FC1_FWD_SWIGLU : FC1_FWD_GELU, g1, e1, s);
+    if (err != hipSuccess) return hip_fail(err);
+    EpiArgs e2{};
+    e2.out = y; e2.ldo = H;
+    GemmArgs g2 = make_gemm(a_saved, Fs, W2, Fs, T, H, Fs, 0);
+    err = run_step(kind, FC2_FWD, g2, e2, s);
+    if (err != hipSuccess) return hip_fail(err);
+    return TPMLP_OK;
+  }
+
+  // e4m3: fc1 (bf16 a + per-workgroup amax) -> quantise a -> fc2
+  char* wsb = static_cast<char*>(ws);
+  void* a_bf16 = wsb;
+  float* parts = reinterpret_cast<float*>(wsb + align_up((size_t)T * (size_t)Fs * 2, 256));
+  const int nparts = fp8_fc1_parts(d);
+  if (T > 0) {
+    EpiArgs e1{};
+    e1.out = a_bf16; e1.ldo = Fs;
+    e1.out2 = h_saved; e1.ldo2 = Fs;
+    e1.bias = d->has_bias ? b1 : nullptr;
+    e1.scale_a = fp8->x_scale_inv; e1.scale_b = fp8->w1_scale_inv;
+    e1.amax_part = parts;
+    GemmArgs g1 = make_gemm(x, H, W1, H, T, Fs, H, Fs);
+    err = run_step(kind, FC1_FWD_GELU, g1, e1, s);
+    if (err != hipSuccess) return hip_fail(err);
+  }
+  err = timed("quantize_a.e4m3", s, [&]() {
+    return quantize_launch(true, a_bf16, T * Fs, static_cast<uint8_t*>(a_saved), parts, nparts,
+                           fp8->a_amax, fp8->a_scale_inv, s);
+  });
+  if (err != hipSuccess) return hip_fail(err);
+  if (T > 0) {
+    EpiArgs e2{};
+    e2.out = y; e2.ldo = H;
+    e2.scale_a = fp8->a_scale_inv; e2.scale_b = fp8->w2_scale_inv;
+    GemmArgs g2 = make_gemm(a_saved, Fs, W2, Fs, T, H, Fs, 0);
+    err = run_step(kind, FC2_FWD, g2, e2, s);
+    if (err != hipSuccess) return hip_fail(err);
+  }
+  return TPMLP_OK;
+}
+
+tpmlp_status tpmlp_bwd_dgrad(const tpmlp_desc* d, const void* dy, const void* W1,
+                             const void* W2, const void* h_saved, void* dH, void* dx,
+                             void* ws, size_t ws_bytes, hipStream_t s) {
+  tpmlp_status st = check_desc(d);
+  if (st != TPMLP_OK) return st;
+  if (d->dtype == TPMLP_E4M3) return TPMLP_E_UNSUPPORTED;
+  if ((st = check_ptrs({dy, W1, W2, h_saved, dH, dx})) != TPMLP_OK) return st;
+  if ((st = check_workspace(d, TPMLP_CALL_DGRAD, ws, ws_bytes)) != TPMLP_OK) return st;
+  const int64_t T = d->tokens, H = d->hidden, Fs = d->ffn_shard;
+  if (T == 0) return TPMLP_OK;
+  const bool swiglu = d->act == TPMLP_ACT_SWIGLU;
+  const int64_t GFs = swiglu ? 2 * Fs : Fs;
+  const Kind kind = d->dtype == TPMLP_F32 ? KIND_F32 : KIND_BF16;
+  // fc2 dgrad: dA = dy . W2 (W2 [H, Fs] read as [K=H][N=Fs]), activation derivative fused
+  EpiArgs e1{};
+  e1.out = dH; e1.ldo = GFs;
+  e1.aux = h_saved; e1.ldaux = GFs;
+  GemmArgs g1 = make_gemm(dy, H, W2, Fs, T, Fs, H, Fs);
+  hipError_t err = run_step(kind, swiglu ? FC2_DGRAD_SWIGLU : FC2_DGRAD_GELU, g1, e1, s);
+  if (err != hipSuccess) return hip_fail(err);
+  // fc1 dgrad: dx = dH . W1 (W1 [GFs, H] read as [K=GFs][N=H])
+  EpiArgs e2{};
+  e2.out = dx; e2.ldo = H;
+  GemmArgs g2 = make_gemm(dH, GFs, W1, H, T, H, GFs, 0);
+  err = run_step(kind, FC1_DGRAD, g2, e2, s);
+  if (err != hipSuccess) return hip_fail(err);
+  return TPMLP_OK;
+}
+
+tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* d, const void* dy, const void* x,
+                             const void* a_saved, const void* dH, float* dW1, float* db1,
+                             float* dW2, int32_t accumulate, void* ws, size_t ws_bytes,
+                             hipStream_t s) {
+  tpmlp_status st = check_desc(d);
+  if (st != TPMLP_OK) return st;
+  if (d->dtype == TPMLP_E4M3) return TPMLP_E_UNSUPPORTED;
+  if (accumulate != 0 && accumulate != 1) return TPMLP_E_DTYPE;
+  if ((st = check_ptrs({dy, x, a_saved, dH, dW1, dW2})) != TPMLP_OK) return st;
+  if (d->has_bias && (st = check_ptrs({db1})) != TPMLP_OK) return st;
+  if ((st = check_workspace(d, TPMLP_CALL_WGRAD, ws, ws_bytes)) != TPMLP_OK) return st;
+  const int64_t T = d->tokens, H = d->hidden, Fs = d->ffn_shard;
+  if (T == 0 && accumulate) return TPMLP_OK;  // adding nothing
+  const bool swiglu = d->act == TPMLP_ACT_SWIGLU;
+  const int64_t GFs = swiglu ? 2 * Fs : Fs;
+  const Kind kind = d->dtype == TPMLP_F32 ? KIND_F32 : KIND_BF16;
+  // dW2 [H, Fs] = dy^T . a : A = dy as [K=T][M=H], B = a as [K=T][N=Fs]
+  EpiArgs e1{};
+  e1.out = dW2; e1.ldo = Fs; e1.accumulate = accumulate;
+  GemmArgs g1 = make_gemm(dy, H, a_saved, Fs, H, Fs, T, 0);
+  hipError_t err = run_step(kind, WGRAD, g1, e1, s);
+  if (err != hipSuccess) return hip_fail(err);
+  // dW1 [GFs, H] = dH^T . x (+ db1 = column sums of dH)
+  EpiArgs e2{};
+  e2.out = dW1; e2.ldo = H; e2.accumulate = accumulate;
+  e2.colsum = d->has_bias ? db1 : nullptr;
+  GemmArgs g2 = make_gemm(dH, GFs, x, H, GFs, H, T, 0);
+  err = run_step(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, g2, e2, s);
+  if (err != hipSuccess) return hip_fail(err);
+  return TPMLP_OK;
+}
+
+size_t tpmlp_quantize_workspace_size(int64_t n) {
+  if (n < 0) return 0;
+  return align_up((size_t)quant_parts(n) * 4, 256);
+}
+
+tpmlp_status tpmlp_quantize_e4m3(int32_t src_dtype, const void* src, int64_t n, uint8_t* dst,
+                                 float* amax_out, float* scale_inv_out, void* ws,
+                                 size_t ws_bytes, hipStream_t s) {
+  if (src_dtype != TPMLP_F32 && src_dtype != TPMLP_BF16) return TPMLP_E_DTYPE;
+  if (n < 0) return TPMLP_E_SHAPE;
+  if (!amax_out || !scale_inv_out) return TPMLP_E_NULL;
+  if (n > 0) {
+    tpmlp_status st = check_ptrs({src, dst});
+    if (st != TPMLP_OK) return st;
+  }
+  if (!ws || ws_bytes < tpmlp_quantize_workspace_size(n)) return TPMLP_E_WORKSPACE;
+  if (!aligned16(ws)) return TPMLP_E_ALIGN;
+  const bool bf = src_dtype == TPMLP_BF16;
+  const int nparts = quant_parts(n);
+  float* parts = static_cast<float*>(ws);
+  hipError_t err = timed("amax_partial", s, [&]() {
+    return amax_partial_launch(bf, src, n, parts, nparts, s);
+  });
+  if (err != hipSuccess) return hip_fail(err);
+  err = timed("quantize", s, [&]() {
+    return quantize_launch(bf, src, n, dst, parts, nparts, amax_out, scale_inv_out, s);
+  });
+  if (err != hipSuccess) return hip_fail(err);
+  return TPMLP_OK;
+}
+
+tpmlp_status tpmlp_timing_enable(int32_t enable, const char* name_filter) {
+  for (auto& r : g_recs) {
+    g_pool.push_back(r.start);
+    g_pool.push_back(r.stop);
+  }
+  g_recs.clear();
+  g_timing = enable != 0;
+  g_filter = (enable && name_filter) ? name_filter : "";
+  return TPMLP_OK;
+}
+
+int32_t tpmlp_timing_collect(const char** names, int64_t* counts, double* total_ms, int32_t cap) {
+  std::vector<const char*> keys;
+  std::vector<int64_t> cnt;
+  std::vector<double> tot;
+  for (auto& r : g_recs) {
+    if (hipEventSynchronize(r.stop) != hipSuccess) return -1;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return -1;
+    size_t i = 0;
+    while (i < keys.size() && strcmp(keys[i], r.name) != 0) ++i;
+    if (i == keys.size()) {
+      keys.push_back(r.name);
+      cnt.push_back(0);
+      tot.push_back(0.0);
+    }
+    cnt[i] += 1;
+    tot[i] += ms;
+  }
+  for (size_t i = 0; i < keys.size() && (int32_t)i < cap; ++i) {
+    if (names) names[i] = keys[i];
+    if (counts) counts[i] = cnt[i];
+    if (total_ms) total_ms[i] = tot[i];
+  }
+  return (int32_t)keys.size();
+}
+
+}  // extern "C"

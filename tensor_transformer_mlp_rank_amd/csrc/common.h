@@ -1,0 +1,126 @@
+// Device-side building blocks shared by the libtpmlp kernels (gfx950 / CDNA4).
+//
+// * vector types for MFMA operands and accumulators;
+// * buffer-resource loads: the hardware range check turns every access past a
+//   tensor's end into a zero, which gives ragged tiles for free;
+// * fp32 <-> bf16 and fp32 -> OCP E4M3 conversions (round to nearest even);
+// * the activation functions of the MLP block and their derivatives in fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpmlp {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef uint16_t bf16_t;  // bfloat16 storage
+typedef uint8_t e4m3_t;   // OCP E4M3 storage
+
+#define TPMLP_LDS __attribute__((address_space(3)))
+
+// ---------------------------------------------------------------- buffer loads
+// Resource word 3 for gfx9-family raw buffers (32-bit data format, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
+// Offsets at or beyond this value are always outside a resource (records are
+// capped below it), so loads from them return zero.
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  if (bytes < 0) bytes = 0;
+  if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferFlags);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf2f(bf16_t u) {
+  return __uint_as_float(((uint32_t)u) << 16);
+}
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  __bf16 h = (__bf16)f;  // round to nearest even (hardware cvt on gfx950)
+  return __builtin_bit_cast(bf16_t, h);
+}
+__device__ __forceinline__ float round_bf16(float f) { return bf2f(f2bf(f)); }
+
+// Two floats to two E4M3 codes (low byte = a). Inputs are clamped to +-448
+// first: the conversion instruction rounds to nearest even in OCP E4M3 but
+// yields NaN (not the largest finite value) above 448.
+__device__ __forceinline__ uint32_t f2e4m3x2(float a, float b) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
+  b = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kBytes = 4;
+  __device__ __forceinline__ static float load(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+  __device__ __forceinline__ static void store(void* p, int64_t i, float v) {
+    static_cast<float*>(p)[i] = v;
+  }
+  __device__ __forceinline__ static float round(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float load(const void* p, int64_t i) {
+    return bf2f(static_cast<const bf16_t*>(p)[i]);
+  }
+  __device__ __forceinline__ static void store(void* p, int64_t i, float v) {
+    static_cast<bf16_t*>(p)[i] = f2bf(v);
+  }
+  __device__ __forceinline__ static float round(float v) { return round_bf16(v); }
+};
+
+// ---------------------------------------------------------------- activations
+// GELU, tanh form: gelu(z) = z/2 (1 + tanh u), u = sqrt(2/pi)(z + 0.044715 z^3).
+// Since (1 + tanh u)/2 = sigmoid(2u), gelu(z) = z * sigmoid(2u), and
+// gelu'(z) = s + 2 z s (1 - s) u'(z) with s = sigmoid(2u),
+// u'(z) = sqrt(2/pi)(1 + 3 * 0.044715 z^2).
+// sigmoid(t) = 1 / (1 + 2^(-t log2 e)) from the hardware exp2 and reciprocal.
+constexpr float kSqrt2OverPi = 0.7978845608028654f;
+constexpr float kGeluCubic = 0.044715f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float sigmoid_f(float t) {
+  float e = __builtin_amdgcn_exp2f(-t * kLog2e);  // +inf for very negative t
+  return __builtin_amdgcn_rcpf(1.0f + e);          // rcp(+inf) = 0
+}
+__device__ __forceinline__ float gelu_f(float z) {
+  float u = kSqrt2OverPi * (z + kGeluCubic * z * z * z);
+  return z * sigmoid_f(2.0f * u);
+}
+__device__ __forceinline__ float gelu_grad_f(float z) {
+  float z2 = z * z;
+  float u = kSqrt2OverPi * (z + kGeluCubic * z2 * z);
+  float du = kSqrt2OverPi * (1.0f + 3.0f * kGeluCubic * z2);
+  float s = sigmoid_f(2.0f * u);
+  return s + 2.0f * z * s * (1.0f - s) * du;
+}
+// SiLU: silu(g) = g sigmoid(g); silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))).
+__device__ __forceinline__ float silu_f(float g) { return g * sigmoid_f(g); }
+__device__ __forceinline__ float silu_grad_f(float g) {
+  float s = sigmoid_f(g);
+  return s * (1.0f + g * (1.0f - s));
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace tpmlp

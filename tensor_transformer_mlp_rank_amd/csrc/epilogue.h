@@ -1,0 +1,92 @@
+// Per-element epilogues of the MLP block's GEMMs, shared by the MFMA (bf16,
+// e4m3) and the VALU (fp32) tile kernels. Each takes one fp32 accumulator
+// value of C at (row, col) and writes the block's tensors:
+//
+//   EPI_STORE     out = alpha * acc                   (y_partial, dx_partial)
+//   EPI_F32       out = acc (+ out if accumulate)     (dW1, dW2, fp32)
+//   EPI_BIAS_GELU h = alpha * acc + b1[col]; out2 = h; out = gelu(h)
+//   EPI_SWIGLU    (gate, up) pair: out2 = [g | u]; out = silu(g) * u
+//   EPI_DGELU     out = acc * gelu'(h[row, col])      (dH)
+//   EPI_DSWIGLU   out[col] = acc * u * silu'(g); out[col + Fs] = acc * silu(g)
+//
+// The activation is evaluated on h as stored (rounded to the activation type),
+// so the backward pass, which reads the stored h, differentiates exactly the
+// function whose value the forward produced.
+#pragma once
+
+#include "common.h"
+
+namespace tpmlp {
+
+enum EpiKind : int {
+  EPI_STORE = 0,
+  EPI_F32 = 1,
+  EPI_BIAS_GELU = 2,
+  EPI_SWIGLU = 3,
+  EPI_DGELU = 4,
+  EPI_DSWIGLU = 5,
+};
+
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  int64_t lda, ldb;
+  int M, N, K;     // N: output columns (for the gated fc1: the Fs pair columns)
+  int pair_off;    // gated blocks: Fs (offset between gate and up rows/columns)
+  int tiles_m, tiles_n, group_m;
+};
+
+struct EpiArgs {
+  void* out;          int64_t ldo;    // primary output
+  void* out2;         int64_t ldo2;   // saved pre-activation h (may be null)
+  const void* bias;                   // b1 (may be null)
+  const void* aux;    int64_t ldaux;  // saved h read by the dgrad epilogues
+  const float* scale_a;               // e4m3: dequantisation factors (device)
+  const float* scale_b;
+  float* amax_part;                   // e4m3 fc1: per-workgroup max |bf16(a)|
+  float* colsum;                      // fc1 wgrad: db1 (sum over k of A), or null
+  int accumulate;                     // EPI_F32 and colsum: add into outputs
+};
+
+// Non-paired kinds. `bias` is b1[col] (0 when absent). For IS_FP8 the
+// activation is written as bf16 and its rounded magnitude folded into amax.
+template <int EPI, typename OutT, bool IS_FP8>
+__device__ __forceinline__ void epi_one(const EpiArgs& e, int pair_off, int row, int col,
+                                        float v, float alpha, float bias, float& amax) {
+  const int64_t o = (int64_t)row * e.ldo + col;
+  if constexpr (EPI == EPI_STORE) {
+    Elem<OutT>::store(e.out, o, v * alpha);
+  } else if constexpr (EPI == EPI_F32) {
+    float* out = static_cast<float*>(e.out);
+    out[o] = e.accumulate ? out[o] + v : v;
+  } else if constexpr (EPI == EPI_BIAS_GELU) {
+    const float h = v * alpha + bias;
+    if (e.out2) Elem<OutT>::store(e.out2, (int64_t)row * e.ldo2 + col, h);
+    const float a = gelu_f(Elem<OutT>::round(h));
+    if constexpr (IS_FP8) amax = __builtin_fmaxf(amax, __builtin_fabsf(round_bf16(a)));
+    Elem<OutT>::store(e.out, o, a);
+  } else if constexpr (EPI == EPI_DGELU) {
+    const float h = Elem<OutT>::load(e.aux, (int64_t)row * e.ldaux + col);
+    Elem<OutT>::store(e.out, o, v * gelu_grad_f(h));
+  } else if constexpr (EPI == EPI_DSWIGLU) {
+    const int64_t ho = (int64_t)row * e.ldaux + col;
+    const float gt = Elem<OutT>::load(e.aux, ho);
+    const float up = Elem<OutT>::load(e.aux, ho + pair_off);
+    Elem<OutT>::store(e.out, o, v * up * silu_grad_f(gt));
+    Elem<OutT>::store(e.out, o + pair_off, v * silu_f(gt));
+  }
+}
+
+// Gated fc1: gate and up accumulators of pair column `col`.
+template <typename OutT>
+__device__ __forceinline__ void epi_pair(const EpiArgs& e, int pair_off, int row, int col,
+                                         float gt, float up) {
+  if (e.out2) {
+    Elem<OutT>::store(e.out2, (int64_t)row * e.ldo2 + col, gt);
+    Elem<OutT>::store(e.out2, (int64_t)row * e.ldo2 + pair_off + col, up);
+  }
+  const float gr = Elem<OutT>::round(gt), ur = Elem<OutT>::round(up);
+  Elem<OutT>::store(e.out, (int64_t)row * e.ldo + col, silu_f(gr) * ur);
+}
+
+}  // namespace tpmlp

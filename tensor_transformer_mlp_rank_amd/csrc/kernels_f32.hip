@@ -1,0 +1,79 @@
+// Instantiations and launchers of the fp32 (VALU) tile kernel and of the
+// E4M3 quantiser.
+#include "gemm_f32.h"
+#include "launch.h"
+#include "quant.h"
+
+namespace tpmlp {
+
+namespace {
+
+template <bool A_K, bool B_K, int EPI, bool COLSUM>
+hipError_t launch_f32(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  const int nb = g.tiles_m * g.tiles_n;
+  hipLaunchKernelGGL((gemm_f32_kernel<A_K, B_K, EPI, COLSUM>), dim3(nb), dim3(kF32Threads), 0, s,
+                     g, e);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int f32_grid(Step step, GemmArgs& g) {
+  const bool pair = (step == FC1_FWD_SWIGLU);
+  g.tiles_m = (g.M + kF32Tile - 1) / kF32Tile;
+  const int bn = pair ? kF32Tile / 2 : kF32Tile;
+  g.tiles_n = (g.N + bn - 1) / bn;
+  g.group_m = 1;
+  if (g.M <= 0 || g.N <= 0) return 0;
+  return g.tiles_m * g.tiles_n;
+}
+
+hipError_t f32_launch(Step step, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  switch (step) {
+    case FC1_FWD_GELU: return launch_f32<true, true, EPI_BIAS_GELU, false>(g, e, s);
+    case FC1_FWD_SWIGLU: return launch_f32<true, true, EPI_SWIGLU, false>(g, e, s);
+    case FC2_FWD: return launch_f32<true, true, EPI_STORE, false>(g, e, s);
+    case FC2_DGRAD_GELU: return launch_f32<true, false, EPI_DGELU, false>(g, e, s);
+    case FC2_DGRAD_SWIGLU: return launch_f32<true, false, EPI_DSWIGLU, false>(g, e, s);
+    case FC1_DGRAD: return launch_f32<true, false, EPI_STORE, false>(g, e, s);
+    case WGRAD: return launch_f32<false, false, EPI_F32, false>(g, e, s);
+    case WGRAD_COLSUM: return launch_f32<false, false, EPI_F32, true>(g, e, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int quant_parts(int64_t n) {
+  int64_t per = (int64_t)kQuantThreads * kQuantVec * 4;  // ~4 iterations per thread
+  int64_t p = (n + per - 1) / per;
+  if (p < 1) p = 1;
+  if (p > kQuantMaxParts) p = kQuantMaxParts;
+  return (int)p;
+}
+
+hipError_t amax_partial_launch(bool src_bf16, const void* src, int64_t n, float* partial,
+                               int nparts, hipStream_t s) {
+  if (src_bf16)
+    hipLaunchKernelGGL(amax_partial_kernel<bf16_t>, dim3(nparts), dim3(kQuantThreads), 0, s,
+                       static_cast<const bf16_t*>(src), n, partial);
+  else
+    hipLaunchKernelGGL(amax_partial_kernel<float>, dim3(nparts), dim3(kQuantThreads), 0, s,
+                       static_cast<const float*>(src), n, partial);
+  return hipGetLastError();
+}
+
+hipError_t quantize_launch(bool src_bf16, const void* src, int64_t n, uint8_t* dst,
+                           const float* partial, int nparts, float* amax_out,
+                           float* scale_inv_out, hipStream_t s) {
+  const int nb = quant_parts(n) * 4 > 4096 ? 4096 : quant_parts(n) * 4;
+  if (src_bf16)
+    hipLaunchKernelGGL(quantize_kernel<bf16_t>, dim3(nb), dim3(kQuantThreads), 0, s,
+                       static_cast<const bf16_t*>(src), n, dst, partial, nparts, amax_out,
+                       scale_inv_out);
+  else
+    hipLaunchKernelGGL(quantize_kernel<float>, dim3(nb), dim3(kQuantThreads), 0, s,
+                       static_cast<const float*>(src), n, dst, partial, nparts, amax_out,
+                       scale_inv_out);
+  return hipGetLastError();
+}
+
+}  // namespace tpmlp

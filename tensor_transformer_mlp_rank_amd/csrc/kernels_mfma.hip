@@ -1,0 +1,62 @@
+// Instantiations and launchers of the MFMA tile kernel (bf16 and e4m3).
+#include "gemm_mfma.h"
+#include "launch.h"
+
+namespace tpmlp {
+
+namespace {
+
+template <bool IS_FP8, bool A_K, bool B_K, int EPI, bool COLSUM>
+hipError_t launch_one(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  auto* k = &gemm_mfma_kernel<IS_FP8, A_K, B_K, EPI, bf16_t, COLSUM>;
+  // the LDS allowance is raised once per instantiation and device
+  static bool attr_set[64] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!attr_set[dev]) {
+    err = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
+    if (err != hipSuccess) return err;
+    attr_set[dev] = true;
+  }
+  const int nb = g.tiles_m * g.tiles_n;
+  hipLaunchKernelGGL(k, dim3(nb), dim3(kThreads), kSmemBytes, s, g, e);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int mfma_grid(Step step, GemmArgs& g) {
+  const bool pair = (step == FC1_FWD_SWIGLU);
+  g.tiles_m = (g.M + kBM - 1) / kBM;
+  const int bn = pair ? kBN / 2 : kBN;
+  g.tiles_n = (g.N + bn - 1) / bn;
+  g.group_m = 8;
+  if (g.M <= 0 || g.N <= 0) return 0;
+  return g.tiles_m * g.tiles_n;
+}
+
+hipError_t mfma_launch(bool fp8, Step step, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  if (fp8) {
+    switch (step) {
+      case FC1_FWD_GELU: return launch_one<true, true, true, EPI_BIAS_GELU, false>(g, e, s);
+      case FC2_FWD: return launch_one<true, true, true, EPI_STORE, false>(g, e, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (step) {
+    case FC1_FWD_GELU: return launch_one<false, true, true, EPI_BIAS_GELU, false>(g, e, s);
+    case FC1_FWD_SWIGLU: return launch_one<false, true, true, EPI_SWIGLU, false>(g, e, s);
+    case FC2_FWD: return launch_one<false, true, true, EPI_STORE, false>(g, e, s);
+    case FC2_DGRAD_GELU: return launch_one<false, true, false, EPI_DGELU, false>(g, e, s);
+    case FC2_DGRAD_SWIGLU: return launch_one<false, true, false, EPI_DSWIGLU, false>(g, e, s);
+    case FC1_DGRAD: return launch_one<false, true, false, EPI_STORE, false>(g, e, s);
+    case WGRAD: return launch_one<false, false, false, EPI_F32, false>(g, e, s);
+    case WGRAD_COLSUM: return launch_one<false, false, false, EPI_F32, true>(g, e, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tpmlp

@@ -1,0 +1,44 @@
+// Host-side launchers of the libtpmlp kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "epilogue.h"
+
+namespace tpmlp {
+
+// The GEMM steps of the block; each maps to one kernel instantiation per
+// element type.
+enum Step : int {
+  FC1_FWD_GELU = 0,   // x . W1^T, bias + GELU, saves h, writes a
+  FC1_FWD_SWIGLU,     // x . W1^T (gate/up pairs), SiLU(g) * u, saves h, writes a
+  FC2_FWD,            // a . W2^T -> y_partial
+  FC2_DGRAD_GELU,     // dy . W2, times gelu'(h) -> dH
+  FC2_DGRAD_SWIGLU,   // dy . W2, SwiGLU derivative -> dH (both halves)
+  FC1_DGRAD,          // dH . W1 -> dx_partial
+  WGRAD,              // A^T . B over tokens -> fp32 (dW2, or dW1 without bias)
+  WGRAD_COLSUM,       // same, plus column sums of A (dW1 and db1)
+  kNumSteps
+};
+
+enum Kind : int { KIND_F32 = 0, KIND_BF16 = 1, KIND_E4M3 = 2 };
+
+// Fill the grid fields of `g` (tiles_m, tiles_n, group_m) for the step and
+// return the number of workgroups (0: nothing to launch).
+int mfma_grid(Step step, GemmArgs& g);
+int f32_grid(Step step, GemmArgs& g);
+
+// Enqueue one GEMM step; `g` must have its grid fields filled.
+hipError_t mfma_launch(bool fp8, Step step, const GemmArgs& g, const EpiArgs& e,
+                       hipStream_t stream);
+hipError_t f32_launch(Step step, const GemmArgs& g, const EpiArgs& e, hipStream_t stream);
+
+// Quantiser passes. src_bf16 selects the source type (bf16 or f32).
+int quant_parts(int64_t n);
+hipError_t amax_partial_launch(bool src_bf16, const void* src, int64_t n, float* partial,
+                               int nparts, hipStream_t stream);
+hipError_t quantize_launch(bool src_bf16, const void* src, int64_t n, uint8_t* dst,
+                           const float* partial, int nparts, float* amax_out,
+                           float* scale_inv_out, hipStream_t stream);
+
+}  // namespace tpmlp

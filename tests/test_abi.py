@@ -1,0 +1,149 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/tpmlp.h, and rejects invalid arguments with the documented
+status codes before any HIP call (fake device addresses are never touched,
+because validation fails first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tensor_transformer_mlp_rank_amd as tp
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tpmlp.h")
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_UNSUP, E_WS, E_HIP = range(8)
+P = 0x100000          # fake, 16-byte aligned "device" address (never dereferenced)
+MIS = 0x100008        # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tpmlp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"tpmlp_fwd", "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad"} <= set(names)
+    for n in names:
+        assert hasattr(tp.lib, n), n
+
+
+def test_version_and_strings():
+    assert tp.lib.tpmlp_abi_version() == 1
+    for s in range(8):
+        assert len(tp.lib.tpmlp_strerror(s)) > 5
+    assert tp.lib.tpmlp_last_hip_error() == b""
+
+
+def fwd(desc, x=P, W1=P, b1=P, W2=P, y=P, h=P, a=P, fp8=None, ws=None, nbytes=0):
+    d = None if desc is None else ctypes.byref(desc)
+    sc = None if fp8 is None else ctypes.byref(fp8)
+    return tp.lib.tpmlp_fwd(d, x, W1, b1, W2, y, h, a, sc, ws, nbytes, None)
+
+
+def dgrad(desc, dy=P, W1=P, W2=P, h=P, dH=P, dx=P):
+    return tp.lib.tpmlp_bwd_dgrad(ctypes.byref(desc), dy, W1, W2, h, dH, dx, None, 0, None)
+
+
+def wgrad(desc, dy=P, x=P, a=P, dH=P, dW1=P, db1=P, dW2=P, acc=0):
+    return tp.lib.tpmlp_bwd_wgrad(ctypes.byref(desc), dy, x, a, dH, dW1, db1, dW2, acc, None, 0,
+                                  None)
+
+
+def D(**kw):
+    base = dict(tokens=64, hidden=256, ffn_shard=128, act="gelu", dtype="bf16", has_bias=True)
+    base.update(kw)
+    return tp.make_desc(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tokens=-1), E_SHAPE), (dict(hidden=0), E_SHAPE), (dict(ffn_shard=-16), E_SHAPE),
+    (dict(hidden=264), E_SHAPE), (dict(ffn_shard=136), E_SHAPE), (dict(hidden=1 << 23), E_SHAPE),
+    (dict(ffn_shard=(1 << 22) - 16 + 32, act="swiglu", has_bias=False), E_SHAPE),
+    (dict(dtype=9), E_DTYPE), (dict(act=4), E_DTYPE),
+    (dict(act="swiglu", has_bias=True), E_UNSUP), (dict(act="swiglu", dtype="e4m3", has_bias=False), E_UNSUP),
+])
+def test_desc_validation(kw, code):
+    assert fwd(D(**kw)) == code
+
+
+def test_desc_null_and_reserved_and_flags():
+    assert fwd(None) == E_NULL
+    d = D()
+    d.reserved = 1
+    assert fwd(d) == E_DTYPE
+    d = D()
+    d.has_bias = 2
+    assert fwd(d) == E_DTYPE
+
+
+@pytest.mark.parametrize("name", ["x", "W1", "W2", "y", "a"])
+def test_fwd_required_pointers(name):
+    assert fwd(D(), **{name: None}) == E_NULL
+    assert fwd(D(), **{name: MIS}) == E_ALIGN
+
+
+def test_fwd_bias_and_h_rules():
+    assert fwd(D(has_bias=True), b1=None) == E_NULL
+    assert fwd(D(has_bias=True), b1=MIS) == E_ALIGN
+    assert fwd(D(), h=MIS) == E_ALIGN
+
+
+def test_fp8_rules():
+    d8 = D(dtype="e4m3")
+    sc = tp.Fp8Scales(P, P, P, P, P)
+    assert fwd(d8) == E_NULL                           # scales required
+    assert fwd(D(), fp8=sc) == E_DTYPE                 # scales only for e4m3
+    assert fwd(d8, fp8=tp.Fp8Scales(P, None, P, P, P)) == E_NULL
+    need = tp.workspace_size(d8, tp.CALL_FWD)
+    assert need >= 64 * 128 * 2
+    assert fwd(d8, fp8=sc) == E_WS
+    assert fwd(d8, fp8=sc, ws=P, nbytes=need - 1) == E_WS
+    assert fwd(d8, fp8=sc, ws=MIS, nbytes=need) == E_ALIGN
+    assert dgrad(d8) == E_UNSUP
+    assert wgrad(d8) == E_UNSUP
+
+
+def test_workspace_sizes():
+    assert tp.workspace_size(D(), tp.CALL_FWD) == 0
+    assert tp.workspace_size(D(), tp.CALL_DGRAD) == 0
+    assert tp.workspace_size(D(), tp.CALL_WGRAD) == 0
+    assert tp.workspace_size(D(hidden=3), tp.CALL_FWD) == 0      # invalid desc
+    assert tp.workspace_size(D(dtype="e4m3"), 7) == 0            # invalid call
+
+
+@pytest.mark.parametrize("name", ["dy", "W1", "W2", "h", "dH", "dx"])
+def test_dgrad_pointers(name):
+    assert dgrad(D(), **{name: None}) == E_NULL
+    assert dgrad(D(), **{name: MIS}) == E_ALIGN
+
+
+@pytest.mark.parametrize("name", ["dy", "x", "a", "dH", "dW1", "dW2"])
+def test_wgrad_pointers(name):
+    assert wgrad(D(), **{name: None}) == E_NULL
+    assert wgrad(D(), **{name: MIS}) == E_ALIGN
+
+
+def test_wgrad_bias_and_flag():
+    assert wgrad(D(has_bias=True), db1=None) == E_NULL
+    assert wgrad(D(), acc=2) == E_DTYPE
+
+
+def test_quantize_validation():
+    q = tp.lib.tpmlp_quantize_e4m3
+    ws = int(tp.lib.tpmlp_quantize_workspace_size(1000))
+    assert ws >= 4
+    assert q(5, P, 1000, P, P, P, P, ws, None) == E_DTYPE
+    assert q(tp.BF16, P, -1, P, P, P, P, ws, None) == E_SHAPE
+    assert q(tp.BF16, P, 1000, P, None, P, P, ws, None) == E_NULL
+    assert q(tp.BF16, None, 1000, P, P, P, P, ws, None) == E_NULL
+    assert q(tp.BF16, MIS, 1000, P, P, P, P, ws, None) == E_ALIGN
+    assert q(tp.BF16, P, 1000, P, P, P, None, ws, None) == E_WS
+    assert q(tp.BF16, P, 1000, P, P, P, P, ws - 1, None) == E_WS
+
+
+def test_timing_facility_without_records():
+    assert tp.lib.tpmlp_timing_enable(1, b"fc1") == 0
+    assert tp.timing_collect() == {}
+    assert tp.lib.tpmlp_timing_enable(0, None) == 0

@@ -1,0 +1,164 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, on the
+same seeded inputs, element by element (small and ragged shapes spanning
+several tiles) or on sampled outputs (full per-rank shapes).
+
+Tolerance per output tensor, max|gpu - oracle| / max|oracle|:
+fp32 1e-5, bf16 inputs with fp32 accumulation 2e-2, e4m3 with per-tensor
+scales 6e-2."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _gpu_helpers import (TOL, check, gpu_block, oracle_block, rel_err, require_gpu,
+                          sample_gpu, sampled_reference, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+ALL = ("y", "h", "a", "dH", "dx", "dW1", "db1", "dW2")
+
+
+@pytest.fixture(scope="module")
+def tp():
+    require_gpu()
+    import tensor_transformer_mlp_rank_amd as m
+    return m
+
+
+# ------------------------------------------------------------------ tiny fp32, simulated TP=2
+@pytest.mark.parametrize("bias_std", [0.0, 0.3])
+def test_tiny_fp32_two_simulated_shards(tp, bias_std):
+    """Tiny fp32 GELU block (T=128, H=256, F=1024) split into two shards:
+    each rank runs on the GPU; the sum of the partial outputs must match the
+    unsharded oracle block, and every per-rank tensor its oracle shard."""
+    w = synth.WORKLOADS[1]
+    full = synth.make_unsharded_inputs(w, b1_std=bias_std)
+    ref_full = oracle.unsharded_backward(full["x"], full["W1"], full["b1"], full["W2"], full["dy"],
+                                         "gelu")
+    ys, dxs = [], []
+    for r in range(w.tp):
+        W1r, b1r, W2r = oracle.shard_rank(oracle.to_f64(full["W1"]), oracle.to_f64(full["b1"]),
+                                          oracle.to_f64(full["W2"]), w.tp, r, "gelu")
+        inp = {"x": full["x"], "dy": full["dy"],
+               "W1": torch.from_numpy(W1r).float(), "b1": torch.from_numpy(b1r).float(),
+               "W2": torch.from_numpy(W2r).float()}
+        say(f"rank {r} of {w.tp}")
+        gpu = gpu_block(tp, inp, "gelu", "f32", True)
+        ref = oracle_block(inp, "gelu", True)
+        check(gpu, ref, "f32", ALL)
+        ys.append(oracle.to_f64(gpu["y"]))
+        dxs.append(oracle.to_f64(gpu["dx"]))
+    assert rel_err(sum(ys), ref_full["y"]) <= TOL["f32"]
+    assert rel_err(sum(dxs), ref_full["dx"]) <= TOL["f32"]
+
+
+# ------------------------------------------------------------------ small and ragged shapes
+SHAPES = [
+    # (T, H, Fs): several tiles of every GEMM and ragged tails in T, H and Fs
+    (300, 528, 272),
+    (513, 256, 256),
+    (64, 1040, 400),
+    (1, 16, 16),
+    (37, 48, 32),
+]
+
+
+@pytest.mark.parametrize("T,H,Fs", SHAPES)
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_small_and_ragged(tp, T, H, Fs, act, dtype):
+    w = synth.WORKLOADS[4 if act == "swiglu" else 2]
+    inp = synth.make_rank_inputs(w, tokens=T, hidden=H, ffn_shard=Fs, dtype=dtype,
+                                 seed_base=100 + T % 97)
+    has_bias = act == "gelu"
+    gpu = gpu_block(tp, inp, act, dtype, has_bias)
+    ref = oracle_block(inp, act, has_bias)
+    check(gpu, ref, dtype, ALL)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_wgrad_accumulate(tp, dtype, act):
+    """accumulate=1 adds into seeded nonzero fp32 buffers."""
+    T, H, Fs = 200, 272, 144
+    w = synth.WORKLOADS[4 if act == "swiglu" else 2]
+    inp = synth.make_rank_inputs(w, tokens=T, hidden=H, ffn_shard=Fs, dtype=dtype, seed_base=77)
+    has_bias = act == "gelu"
+    G = 2 if act == "swiglu" else 1
+    prior = {"dW1": synth.grad_init(77, (G * Fs, H), 1) * 100,
+             "db1": synth.grad_init(77, (G * Fs,), 2) * 100 if has_bias else None,
+             "dW2": synth.grad_init(77, (H, Fs), 3) * 100}
+    gpu = gpu_block(tp, inp, act, dtype, has_bias, accumulate_into=prior)
+    ref = oracle_block(inp, act, has_bias, prior=prior)
+    check(gpu, ref, dtype, ("dW1", "db1", "dW2"))
+
+
+def test_zero_tokens(tp):
+    """T = 0: forward and dgrad enqueue nothing; wgrad overwrites with zeros
+    (accumulate = 0) or leaves the buffers alone (accumulate = 1)."""
+    H, Fs = 64, 32
+    desc = tp.make_desc(0, H, Fs, act="gelu", dtype="bf16", has_bias=True)
+    e = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    W1 = torch.zeros((Fs, H), dtype=torch.bfloat16, device="cuda")
+    b1 = torch.zeros((Fs,), dtype=torch.bfloat16, device="cuda")
+    W2 = torch.zeros((H, Fs), dtype=torch.bfloat16, device="cuda")
+    # zero-sized tensors may have no storage: pass a valid aligned pointer instead
+    anyp = W1
+    tp.tpmlp_fwd(desc, anyp, W1, b1, W2, anyp, anyp, anyp)
+    tp.tpmlp_bwd_dgrad(desc, anyp, W1, W2, anyp, anyp, anyp)
+    dW1 = torch.full((Fs, H), 7.0, device="cuda")
+    db1 = torch.full((Fs,), 7.0, device="cuda")
+    dW2 = torch.full((H, Fs), 7.0, device="cuda")
+    tp.tpmlp_bwd_wgrad(desc, anyp, anyp, anyp, anyp, dW1, db1, dW2, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.all(dW1 == 7) and torch.all(db1 == 7) and torch.all(dW2 == 7)
+    tp.tpmlp_bwd_wgrad(desc, anyp, anyp, anyp, anyp, dW1, db1, dW2, accumulate=False)
+    torch.cuda.synchronize()
+    assert torch.all(dW1 == 0) and torch.all(db1 == 0) and torch.all(dW2 == 0)
+    del e
+
+
+def test_deterministic(tp):
+    """Two runs on the same inputs are bitwise identical (no atomics)."""
+    inp = synth.make_rank_inputs(synth.WORKLOADS[2], tokens=520, hidden=512, ffn_shard=384,
+                                 seed_base=5)
+    a = gpu_block(tp, inp, "gelu", "bf16", True)
+    b = gpu_block(tp, inp, "gelu", "bf16", True)
+    for k in ALL:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_swiglu_h_layout(tp):
+    """The saved pre-activation of the gated block is [gate | up]: the gate
+    half is x . W1[:Fs]^T and the up half x . W1[Fs:]^T (checked separately so a
+    swapped half cannot pass through a symmetric check)."""
+    T, H, Fs = 96, 160, 80
+    inp = synth.make_rank_inputs(synth.WORKLOADS[4], tokens=T, hidden=H, ffn_shard=Fs,
+                                 seed_base=9)
+    gpu = gpu_block(tp, inp, "swiglu", "bf16", False, calls=("fwd",))
+    x = oracle.to_f64(inp["x"])
+    W1 = oracle.to_f64(inp["W1"])
+    assert rel_err(gpu["h"][:, :Fs], x @ W1[:Fs].T) <= TOL["bf16"]
+    assert rel_err(gpu["h"][:, Fs:], x @ W1[Fs:].T) <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ full per-rank shapes
+ROWS = np.array([0, 1, 255, 256, 4097, 8191])
+COLS = np.array([0, 1, 127, 128, 1000, 2047])
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_full_size_sampled(tp, cfg):
+    """Full per-rank workload in the configuration the benchmark times; the
+    oracle checks sampled token rows (y, h, a, dH, dx) and sampled features
+    (dW2 columns, dW1 rows, db1 entries)."""
+    w = synth.WORKLOADS[cfg]
+    say(f"config {cfg} {w.name}: generating inputs")
+    inp = synth.make_rank_inputs(w)
+    has_bias = w.has_bias
+    gpu = gpu_block(tp, inp, w.act, w.dtype, has_bias)
+    cols = COLS[COLS < w.ffn_shard]
+    ref = sampled_reference(inp, w.act, has_bias, ROWS, cols)
+    got = sample_gpu(gpu, w.act, w.ffn_shard, ROWS, cols)
+    check(got, ref, w.dtype, ALL)
