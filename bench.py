@@ -1,0 +1,207 @@
+"""Benchmark: one tensor-parallel rank's column->row MLP block, forward +
+backward (dgrad + wgrad), bf16 inputs with fp32 accumulation, on one MI355X.
+
+One step = tpmlp_fwd + tpmlp_bwd_dgrad + tpmlp_bwd_wgrad over one batch of
+synthetic per-rank inputs (default workload: T = 8192 tokens (4 x 2048),
+H = 8192, F = 32768 at TP = 8, i.e. Fs = 4096). Inputs and all output
+buffers are resident in HBM before the timed region.
+
+Prints one JSON line: TFLOP/s of the whole step (algorithmic FLOPs
+6*T*H*Fs*(G+1) over the measured time), the dominant kernel's roofline
+(its average launch time from HIP events recorded on its launch stream during
+the timed steps) and the CPU oracle's throughput on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK = {"bf16": 2516.6, "f32": 157.3, "e4m3": 5033.2}
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["gemm_mfma.h", "epilogue.h", "common.h", "kernels_mfma.hip"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tensor_transformer_mlp_rank_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    runs, or None when absent or when the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != kernel_source_sha():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(w, tokens: int) -> dict:
+    """The CPU oracle (fp64 NumPy, as it stands) on the first `tokens` tokens
+    of the same per-rank shard: forward, dgrad and wgrad."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 0) for p in threadpool_info()
+                     if p.get("internal_api") in ("openblas", "mkl", "blis")), default=0)
+    except Exception:  # threadpoolctl missing: report the affinity count
+        cores = 0
+    if not cores:
+        cores = len(os.sched_getaffinity(0))
+    inp = synth.make_rank_inputs(w, tokens=tokens)
+    x, W1, W2, dy = (oracle.to_f64(inp[k]) for k in ("x", "W1", "W2", "dy"))
+    b1 = oracle.to_f64(inp["b1"]) if w.has_bias else None
+    t0 = time.perf_counter()
+    f = oracle.rank_forward(x, W1, b1, W2, w.act)
+    g = oracle.rank_dgrad(dy, W1, W2, f["h"], w.act)
+    oracle.rank_wgrad(dy, x, f["a"], g["dH"], w.has_bias)
+    dt = time.perf_counter() - t0
+    flops = w.flops(tokens=tokens)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"fwd+dgrad+wgrad of the first {tokens} of {w.tokens} tokens of the "
+                      f"{w.name} shard in fp64 NumPy ({flops / 1e12:.3f} TFLOP, {dt:.2f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, help="workload id (3: H=8192 TP=8 shard)")
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="tokens in the CPU oracle sample (0: skip)")
+    ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
+                         "kernel for scaling HBM byte counters)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "launches": 5}))
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the library computes one tensor-parallel rank's "
+              "share and has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import tensor_transformer_mlp_rank_amd as tp
+
+    w = synth.WORKLOADS[args.workload]
+    if "dgrad" not in w.calls:
+        raise SystemExit("the benchmark times forward + backward; pick a workload with backward")
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    inp = synth.make_rank_inputs(w)
+    d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    T, H, Fs, G = w.tokens, w.hidden, w.ffn_shard, w.gate_mult
+    desc = tp.make_desc(T, H, Fs, act=w.act, dtype=w.dtype, has_bias=w.has_bias)
+    at = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    buf = {
+        "y": torch.empty((T, H), dtype=at, device=dev),
+        "h": torch.empty((T, G * Fs), dtype=at, device=dev),
+        "a": torch.empty((T, Fs), dtype=at, device=dev),
+        "dH": torch.empty((T, G * Fs), dtype=at, device=dev),
+        "dx": torch.empty((T, H), dtype=at, device=dev),
+        "dW1": torch.zeros((G * Fs, H), dtype=torch.float32, device=dev),
+        "db1": torch.zeros((G * Fs,), dtype=torch.float32, device=dev) if w.has_bias else None,
+        "dW2": torch.zeros((H, Fs), dtype=torch.float32, device=dev),
+    }
+    stream = torch.cuda.current_stream()
+
+    def step():
+        tp.tpmlp_fwd(desc, d["x"], d["W1"], d["b1"], d["W2"], buf["y"], buf["h"], buf["a"],
+                     stream=stream)
+        tp.tpmlp_bwd_dgrad(desc, d["dy"], d["W1"], d["W2"], buf["h"], buf["dH"], buf["dx"],
+                           stream=stream)
+        tp.tpmlp_bwd_wgrad(desc, d["dy"], d["x"], buf["a"], buf["dH"], buf["dW1"], buf["db1"],
+                           buf["dW2"], accumulate=True, stream=stream)
+
+    # warm-up, timing every kernel to find the dominant one
+    tp.timing_enable(True)
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    per = tp.timing_collect()
+    tp.timing_enable(False)
+    dominant = max(per, key=lambda k: per[k][1])
+    breakdown = {k: round(v[1] / v[0], 4) for k, v in per.items()}
+    if args.breakdown:
+        print("per-kernel ms (warm-up):", json.dumps(breakdown), file=sys.stderr)
+
+    # timed region: live events around the dominant kernel only
+    tp.timing_enable(True, dominant)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dom = tp.timing_collect()[dominant]
+    tp.timing_enable(False)
+
+    ms = (t1 - t0) * 1e3 / args.steps
+    flops = w.flops()
+    value = flops / (ms * 1e-3) / 1e12
+    # fc1's three GEMMs have T*H*G*Fs multiply-adds each, fc2's T*H*Fs
+    per_gemm_flops = 2.0 * T * H * Fs * (G if dominant.startswith("fc1") else 1)
+    dom_ms = dom[1] / dom[0]
+    achieved = per_gemm_flops / (dom_ms * 1e-3) / 1e12
+    traffic = measured_traffic(dominant)
+    line = {
+        "metric": "TFLOP/s per-rank TP-MLP fwd+bwd (bf16) and % of MFMA peak, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded PCG64 normals; per-rank shard shapes)",
+        "config": {"workload": w.name, "tokens": T, "batch": w.batch, "seq_len": w.seq,
+                   "hidden": H, "ffn": w.ffn, "tp": w.tp, "ffn_shard": Fs, "act": w.act,
+                   "parallelism": "one TP rank's shard on one GPU"},
+        "pct_of_peak": round(100 * value / PEAK[w.dtype], 2),
+        "roofline": {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
+                     "peak": PEAK[w.dtype], "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK[w.dtype], 4), "traffic": traffic,
+                     "launches": dom[0], "avg_ms": round(dom_ms, 4)},
+        "kernel_ms": breakdown,
+    }
+    if args.cpu_tokens > 0:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -116,24 +116,26 @@ tpmlp_status check_workspace(const tpmlp_desc* d, int32_t call, void* ws, size_t
 }
 
 // ---------------------------------------------------------------- GEMM step dispatch
-const char* step_name(Kind kind, Step step) {
-  static const char* names[3][kNumSteps] = {
-      {"fc1_fwd_gelu.f32", "fc1_fwd_swiglu.f32", "fc2_fwd.f32", "fc2_dgrad_gelu.f32",
-       "fc2_dgrad_swiglu.f32", "fc1_dgrad.f32", "wgrad.f32", "wgrad_colsum.f32"},
-      {"fc1_fwd_gelu.bf16", "fc1_fwd_swiglu.bf16", "fc2_fwd.bf16", "fc2_dgrad_gelu.bf16",
-       "fc2_dgrad_swiglu.bf16", "fc1_dgrad.bf16", "wgrad.bf16", "wgrad_colsum.bf16"},
-      {"fc1_fwd_gelu.e4m3", "fc1_fwd_swiglu.e4m3", "fc2_fwd.e4m3", "fc2_dgrad_gelu.e4m3",
-       "fc2_dgrad_swiglu.e4m3", "fc1_dgrad.e4m3", "wgrad.e4m3", "wgrad_colsum.e4m3"}};
-  return names[kind][step];
-}
-
-hipError_t run_step(Kind kind, Step step, GemmArgs g, const EpiArgs& e, hipStream_t s) {
+// `label` names the launch for the timing facility (e.g. "fc1_fwd.bf16").
+hipError_t run_step(Kind kind, Step step, const char* label, GemmArgs g, const EpiArgs& e,
+                    hipStream_t s) {
   const int nb = (kind == KIND_F32) ? f32_grid(step, g) : mfma_grid(step, g);
   if (nb == 0) return hipSuccess;
-  return timed(step_name(kind, step), s, [&]() {
+  return timed(label, s, [&]() {
     return kind == KIND_F32 ? f32_launch(step, g, e, s)
                             : mfma_launch(kind == KIND_E4M3, step, g, e, s);
   });
+}
+
+const char* label(Kind kind, int which) {
+  // which: 0 fc1_fwd, 1 fc2_fwd, 2 fc2_dgrad, 3 fc1_dgrad, 4 fc2_wgrad, 5 fc1_wgrad
+  static const char* names[3][6] = {
+      {"fc1_fwd.f32", "fc2_fwd.f32", "fc2_dgrad.f32", "fc1_dgrad.f32", "fc2_wgrad.f32", "fc1_wgrad.f32"},
+      {"fc1_fwd.bf16", "fc2_fwd.bf16", "fc2_dgrad.bf16", "fc1_dgrad.bf16", "fc2_wgrad.bf16",
+       "fc1_wgrad.bf16"},
+      {"fc1_fwd.e4m3", "fc2_fwd.e4m3", "fc2_dgrad.e4m3", "fc1_dgrad.e4m3", "fc2_wgrad.e4m3",
+       "fc1_wgrad.e4m3"}};
+  return names[kind][which];
 }
 
 GemmArgs make_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
@@ -207,12 +209,12 @@ tpmlp_status tpmlp_fwd(const tpmlp_desc* d, const void* x, const void* W1, const
     e1.out2 = h_saved; e1.ldo2 = GFs;
     e1.bias = d->has_bias ? b1 : nullptr;
     GemmArgs g1 = make_gemm(x, H, W1, H, T, Fs, H, Fs);
-    err = run_step(kind, swiglu ? FC1_FWD_SWIGLU : FC1_FWD_GELU, g1, e1, s);
+    err = run_step(kind, swiglu ? FC1_FWD_SWIGLU : FC1_FWD_GELU, label(kind, 0), g1, e1, s);
     if (err != hipSuccess) return hip_fail(err);
     EpiArgs e2{};
     e2.out = y; e2.ldo = H;
     GemmArgs g2 = make_gemm(a_saved, Fs, W2, Fs, T, H, Fs, 0);
-    err = run_step(kind, FC2_FWD, g2, e2, s);
+    err = run_step(kind, FC2_FWD, label(kind, 1), g2, e2, s);
     if (err != hipSuccess) return hip_fail(err);
     return TPMLP_OK;
   }
@@ -230,7 +232,7 @@ tpmlp_status tpmlp_fwd(const tpmlp_desc* d, const void* x, const void* W1, const
     e1.scale_a = fp8->x_scale_inv; e1.scale_b = fp8->w1_scale_inv;
     e1.amax_part = parts;
     GemmArgs g1 = make_gemm(x, H, W1, H, T, Fs, H, Fs);
-    err = run_step(kind, FC1_FWD_GELU, g1, e1, s);
+    err = run_step(kind, FC1_FWD_GELU, label(kind, 0), g1, e1, s);
     if (err != hipSuccess) return hip_fail(err);
   }
   err = timed("quantize_a.e4m3", s, [&]() {
@@ -243,7 +245,7 @@ tpmlp_status tpmlp_fwd(const tpmlp_desc* d, const void* x, const void* W1, const
     e2.out = y; e2.ldo = H;
     e2.scale_a = fp8->a_scale_inv; e2.scale_b = fp8->w2_scale_inv;
     GemmArgs g2 = make_gemm(a_saved, Fs, W2, Fs, T, H, Fs, 0);
-    err = run_step(kind, FC2_FWD, g2, e2, s);
+    err = run_step(kind, FC2_FWD, label(kind, 1), g2, e2, s);
     if (err != hipSuccess) return hip_fail(err);
   }
   return TPMLP_OK;
@@ -267,13 +269,14 @@ tpmlp_status tpmlp_bwd_dgrad(const tpmlp_desc* d, const void* dy, const void* W1
   e1.out = dH; e1.ldo = GFs;
   e1.aux = h_saved; e1.ldaux = GFs;
   GemmArgs g1 = make_gemm(dy, H, W2, Fs, T, Fs, H, Fs);
-  hipError_t err = run_step(kind, swiglu ? FC2_DGRAD_SWIGLU : FC2_DGRAD_GELU, g1, e1, s);
+  hipError_t err =
+      run_step(kind, swiglu ? FC2_DGRAD_SWIGLU : FC2_DGRAD_GELU, label(kind, 2), g1, e1, s);
   if (err != hipSuccess) return hip_fail(err);
   // fc1 dgrad: dx = dH . W1 (W1 [GFs, H] read as [K=GFs][N=H])
   EpiArgs e2{};
   e2.out = dx; e2.ldo = H;
   GemmArgs g2 = make_gemm(dH, GFs, W1, H, T, H, GFs, 0);
-  err = run_step(kind, FC1_DGRAD, g2, e2, s);
+  err = run_step(kind, FC1_DGRAD, label(kind, 3), g2, e2, s);
   if (err != hipSuccess) return hip_fail(err);
   return TPMLP_OK;
 }
@@ -298,14 +301,14 @@ tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* d, const void* dy, const void* x,
   EpiArgs e1{};
   e1.out = dW2; e1.ldo = Fs; e1.accumulate = accumulate;
   GemmArgs g1 = make_gemm(dy, H, a_saved, Fs, H, Fs, T, 0);
-  hipError_t err = run_step(kind, WGRAD, g1, e1, s);
+  hipError_t err = run_step(kind, WGRAD, label(kind, 4), g1, e1, s);
   if (err != hipSuccess) return hip_fail(err);
   // dW1 [GFs, H] = dH^T . x (+ db1 = column sums of dH)
   EpiArgs e2{};
   e2.out = dW1; e2.ldo = H; e2.accumulate = accumulate;
   e2.colsum = d->has_bias ? db1 : nullptr;
   GemmArgs g2 = make_gemm(dH, GFs, x, H, GFs, H, T, 0);
-  err = run_step(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, g2, e2, s);
+  err = run_step(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, label(kind, 5), g2, e2, s);
   if (err != hipSuccess) return hip_fail(err);
   return TPMLP_OK;
 }

@@ -66,6 +66,17 @@ __device__ __forceinline__ uint32_t f2e4m3x2(float a, float b) {
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static constexpr int kBytes = 4;
+  // 8 consecutive elements at index i (i a multiple of 8, 32-byte aligned)
+  __device__ __forceinline__ static void load8(const void* p, int64_t i, float (&v)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i + 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { v[q] = a[q]; v[q + 4] = b[q]; }
+  }
+  __device__ __forceinline__ static void store8(void* p, int64_t i, const float (&v)[8]) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(p) + i) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(static_cast<float*>(p) + i + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  }
   __device__ __forceinline__ static float load(const void* p, int64_t i) {
     return static_cast<const float*>(p)[i];
   }
@@ -76,6 +87,20 @@ template <> struct Elem<float> {
 };
 template <> struct Elem<bf16_t> {
   static constexpr int kBytes = 2;
+  __device__ __forceinline__ static void load8(const void* p, int64_t i, float (&v)[8]) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(p) + i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static void store8(void* p, int64_t i, const float (&v)[8]) {
+    u32x4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = (uint32_t)f2bf(v[2 * q]) | ((uint32_t)f2bf(v[2 * q + 1]) << 16);
+    *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(p) + i) = w;
+  }
   __device__ __forceinline__ static float load(const void* p, int64_t i) {
     return bf2f(static_cast<const bf16_t*>(p)[i]);
   }

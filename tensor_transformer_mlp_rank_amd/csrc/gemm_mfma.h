@@ -16,32 +16,41 @@
 //   fc2 wgrad dy^T . a                A MN-major, B MN-major (K = T)
 //   fc1 wgrad dH^T . x                A MN-major, B MN-major (K = T)
 //
-// Work decomposition (512 threads = 8 waves of 64 lanes):
-//   * workgroup tile 256 (M) x 256 (N), K step of 128 bytes per row
-//     (64 bf16 or 128 e4m3 elements), two LDS stages of 2 x 32 KiB;
-//   * waves in a 2 x 4 grid, each owning a 128 x 64 sub-tile held as 4 x 2
-//     accumulators of the 32x32 MFMA (v_mfma_f32_32x32x16_bf16, or
-//     v_mfma_f32_32x32x64_f8f6f4 for e4m3): 128 fp32 registers per lane;
-//   * global -> registers -> LDS with 16-byte loads coalesced along the
-//     contiguous dimension; loads for step k+1 are in flight while step k's
-//     MFMAs run; one barrier per step.
+// Work decomposition: 256 threads = 4 waves in a 2 x 2 grid, one wave per
+// SIMD. Each wave owns a 128 x 128 sub-tile held as 4 x 4 accumulators of the
+// 32x32 MFMA (v_mfma_f32_32x32x16_bf16, or v_mfma_f32_32x32x64_f8f6f4 for
+// e4m3): 256 fp32 accumulator registers per lane (AGPRs). Per FLOP this reads
+// half the LDS bytes of a 128 x 64 wave tile.
 //
-// LDS layouts (bank-conflict-free for the access patterns used):
-//   * K-major operand: [256 rows][128 B]; 16-byte chunk c of row r is stored at
-//     chunk c ^ (r & 7). Fragment reads are ds_read_b128 (one 32x32x16 bf16
-//     operand = 8 consecutive k of one row).
-//   * MN-major operand: [64 k-rows][256 elements] (512 B); chunk c of k-row r
-//     is stored at chunk c ^ 2(r & 3). Fragment reads use the CDNA4 transpose
+// Pipeline: K advances 64 bytes per row per stage (32 bf16 / 64 e4m3
+// elements); a stage holds a 16 KiB A tile and a 16 KiB B tile; four stages
+// (128 KiB of the 160 KiB LDS) rotate. Tiles go from HBM straight into LDS
+// with buffer_load_dwordx4 ... lds (no staging registers, no LDS store
+// instructions); the buffer resource's range check turns reads past a
+// tensor's end into zeros. Loads for stage k+3 are issued right after the
+// barrier that opens stage k, so each load has three compute stages to land.
+// The barrier is a plain s_barrier preceded by an explicit wait on this
+// wave's own loads of stage k (vmcnt) and its LDS reads of stage k-1: a full
+// __syncthreads would drain all loads in flight and serialise the pipeline.
+//
+// LDS layouts (direct-to-LDS loads write 64 lanes x 16 B = 1 KiB linearly per
+// instruction, so swizzles are applied by choosing which global chunk each
+// lane fetches):
+//   * K-major tile: [256 rows][64 B]; 16-byte chunk c of row r lives at chunk
+//     c ^ ((r >> 1) & 3). Any 8 consecutive rows then put a given chunk in 8
+//     distinct 16-byte slots of a 128-byte bank window, so the fragment reads
+//     (ds_read_b128, 8 consecutive k of one row per lane) are conflict-free.
+//   * MN-major tile: [32 k-rows][256 elements = 512 B]; chunk c of k-row r
+//     lives at chunk c ^ 2(r & 3). Fragments are read with the CDNA4 transpose
 //     read ds_read_b64_tr_b16: in each group of 16 lanes, lane j receives
 //     element j%4 of the 8-byte chunks addressed by lanes 4q + j/4 (q = 0..3),
 //     so pointing lane i at k-row k0 + i/4, elements m0 + 4(i%4) .. +3 hands
 //     lane j the four k values k0..k0+3 of element m0 + j -- the MFMA operand
-//     layout, read straight from the un-transposed tile.
+//     layout, read straight from the untransposed tile.
 //
-// Gated fc1 (SwiGLU): the B tile holds 128 gate rows and the 128 matching up
-// rows of W1, interleaved in blocks of 32 so that each wave's two N
-// accumulators are a (gate, up) pair for the same 32 output features; the
-// epilogue then forms silu(gate) * up in registers.
+// Gated fc1 (SwiGLU): each wave's four N accumulators hold gate features
+// (fn = 0, 1) and the matching up features (fn = 2, 3) of the same 64 output
+// features, so the epilogue forms silu(gate) * up in registers.
 //
 // Workgroup order: blockIdx.x is first remapped so that the workgroups the
 // hardware places on one XCD (ids congruent mod 8) get consecutive tile ids,
@@ -49,14 +58,19 @@
 // resident on an XCD share A and B tiles in that XCD's L2.
 #pragma once
 
+#include <type_traits>
+
 #include "epilogue.h"
 
 namespace tpmlp {
 
-constexpr int kBM = 256, kBN = 256, kBKB = 128;  // tile rows, cols, K bytes per step
-constexpr int kThreads = 512;
-constexpr int kTileBytes = 256 * kBKB;             // 32 KiB per operand per stage
-constexpr int kSmemBytes = 2 * 2 * kTileBytes;     // 128 KiB
+constexpr int kBM = 256, kBN = 256;
+constexpr int kThreads = 256;
+constexpr int kRowBytes = 64;                      // per tile row per stage
+constexpr int kStages = 4;
+constexpr int kTileBytes = 256 * kRowBytes;        // 16 KiB
+constexpr int kStageBytes = 2 * kTileBytes;        // A + B
+constexpr int kSmemBytes = kStages * kStageBytes;  // 128 KiB
 
 __device__ __forceinline__ void tile_coords(const GemmArgs& g, int bid, int& bm, int& bn) {
   const int nb = g.tiles_m * g.tiles_n;
@@ -75,73 +89,88 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& g, int bid, int& bm,
   bn = in / gsz;
 }
 
-// --------------------------------------------------------------- tile loaders
-// K-major: 256 rows x 8 chunks; thread t loads chunk t&7 of rows (t>>3) + 64i.
-// row_map gives each tile row's rsrc (0: rs0, 1: rs1) and local row index.
-struct KMajorLoader {
-  __amdgpu_buffer_rsrc_t rs0, rs1;
-  int64_t ld_bytes;
-  uint32_t kbytes;       // K * element size (row length in bytes)
-  uint32_t row_off[4];   // byte offset of the row start within its rsrc (or kOOB)
-  bool use1[4];
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, char* lds_wave_base,
+                                          uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TPMLP_LDS void*)lds_wave_base, 16, voff, 0, 0, 0);
+}
 
-  __device__ __forceinline__ void load(u32x4 (&r)[4], int tid, uint32_t k0b) const {
-    const uint32_t cb = k0b + (uint32_t)((tid & 7) << 4);
-    const bool kin = cb < kbytes;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t off = (kin && row_off[i] != kOOB) ? row_off[i] + cb : kOOB;
-      r[i] = use1[i] ? buf_load16(rs1, off) : buf_load16(rs0, off);
-    }
+// --------------------------------------------------------------- tile loaders
+// Each wave issues 4 instructions per tile per stage; instruction i of wave w
+// fills LDS bytes [(4w + i) KiB, +1 KiB) of the tile.
+//
+// K-major: instruction (w, i) covers rows 16(4w+i) .. +15; lane l fetches row
+// 16(4w+i) + l/4, logical chunk (l%4) ^ swz(row).
+// For the gated fc1 the tile rows of instruction (w, i) all come from one
+// half of W1 (gate: rs0, up: base1); which one depends on (w, i) only, so the
+// choice is wave-uniform and the resource stays in scalar registers.
+template <bool PAIR>
+struct KMajorLoader {
+  __amdgpu_buffer_rsrc_t rs0;
+  const char* base1;              // gated fc1: start of the up half's rows
+  int64_t bytes1;
+  uint32_t voff[4];               // row*ld + chunk*16 within its resource, or kOOB
+  uint32_t chunk_b[4];            // chunk*16 (for the K-range mask)
+  uint32_t kbytes;                // row length K * element size
+
+  __device__ __forceinline__ static bool up_half(int wave, int i) {
+    return (((wave * 4 + i) >> 1) & 3) >= 2;  // fragment (row / 32) % 4 of these rows
   }
-  __device__ __forceinline__ static void store(char* lds, const u32x4 (&r)[4], int tid) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 3) + 64 * i;
-      const int c = (tid & 7) ^ (row & 7);
-      *reinterpret_cast<u32x4*>(lds + row * kBKB + (c << 4)) = r[i];
+  __device__ __forceinline__ void issue_one(char* tile, int wave, uint32_t k0b, int i) const {
+    const uint32_t off = (voff[i] != kOOB && k0b + chunk_b[i] < kbytes) ? voff[i] + k0b : kOOB;
+    if constexpr (PAIR) {
+      if (up_half(wave, i))
+        lds_dma16(make_rsrc(base1, bytes1), tile + ((wave * 4 + i) << 10), off);
+      else
+        lds_dma16(rs0, tile + ((wave * 4 + i) << 10), off);
+    } else {
+      lds_dma16(rs0, tile + ((wave * 4 + i) << 10), off);
     }
   }
 };
 
-// MN-major (bf16 only): 64 k-rows x 32 chunks; thread t loads chunk t&31 of
-// k-rows (t>>5) + 16i. The resource is rebased to k-row k0 each step.
+// MN-major (bf16 only): instruction (w, i) covers k-rows 2(4w+i), +1; lane l
+// fetches k-row 2(4w+i) + l/32, logical chunk (l%32) ^ 2(krow&3). The
+// resource is rebased to the stage's first k-row.
 struct MNMajorLoader {
   const char* base;      // element (k=0, m=tile start)
   int64_t ld_bytes;
   int64_t total_bytes;   // bytes from `base` to the end of the tensor
-  uint32_t col_ok;       // chunk t&31 lies inside the M (or N) extent
+  uint32_t voff[4];
 
-  __device__ __forceinline__ void load(u32x4 (&r)[4], int tid, int k0) const {
+  __device__ __forceinline__ void issue_one(char* tile, int wave, int k0, int i) const {
     const int64_t kofs = (int64_t)k0 * ld_bytes;
-    __amdgpu_buffer_rsrc_t rs = make_rsrc(base + kofs, total_bytes - kofs);
-    const uint32_t cb = (uint32_t)((tid & 31) << 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kr = (tid >> 5) + 16 * i;
-      uint32_t off = col_ok ? (uint32_t)(kr * ld_bytes) + cb : kOOB;
-      r[i] = buf_load16(rs, off);
-    }
-  }
-  __device__ __forceinline__ static void store(char* lds, const u32x4 (&r)[4], int tid) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kr = (tid >> 5) + 16 * i;
-      const int c = (tid & 31) ^ ((kr & 3) << 1);
-      *reinterpret_cast<u32x4*>(lds + kr * 512 + (c << 4)) = r[i];
-    }
+    lds_dma16(make_rsrc(base + kofs, total_bytes - kofs), tile + ((wave * 4 + i) << 10), voff[i]);
   }
 };
 
 // --------------------------------------------------------------- fragment reads
-// bf16, K-major tile: lane l takes row (l&31) of the 32-row block starting at
-// `row0`, k elements 16*ks + 8*(l>>5) .. +7.
+__device__ __forceinline__ int kswz(int row) { return (row >> 1) & 3; }
+
+// bf16, K-major tile: lane l takes row row0 + (l&31), k elements
+// 16*ks + 8*(l>>5) .. +7 of the stage.
 __device__ __forceinline__ bf16x8 frag_k_bf16(const char* lds, int row0, int ks, int lane) {
   const int row = row0 + (lane & 31);
-  const int c = ((ks << 1) | (lane >> 5)) ^ (row & 7);
-  return *reinterpret_cast<const bf16x8*>(lds + row * kBKB + (c << 4));
+  const int c = ((ks << 1) | (lane >> 5)) ^ kswz(row);
+  return *reinterpret_cast<const bf16x8*>(lds + row * kRowBytes + (c << 4));
 }
-// bf16, MN-major tile: same operand through two transpose reads.
+// The transpose read is issued through inline asm: the compiler's builtin
+// for it carries no memory-operand information, so the compiler would make
+// it wait for every LDS-bound global load in flight (vmcnt(0)) and drain the
+// pipeline. The asm result is not tracked by the compiler's wait counters:
+// every use of it below follows an explicit lgkmcnt(0) wait (the stage
+// barrier, or wait_lds at the top of a stage).
+__device__ __forceinline__ i16x4 ds_read_tr16(const char* p) {
+  i16x4 r;
+  const uint32_t a = (uint32_t)(uintptr_t)(const TPMLP_LDS char*)p;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
+  return r;
+}
+__device__ __forceinline__ void wait_lds() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
+  __builtin_amdgcn_sched_barrier(0);
+}
+// bf16, MN-major tile: the same operand through two transpose reads.
 __device__ __forceinline__ bf16x8 frag_mn_bf16(const char* lds, int col0, int ks, int lane) {
   const int g = lane >> 4, i = lane & 15;
   const int m = col0 + ((g & 1) << 4) + ((i & 3) << 2);
@@ -152,255 +181,350 @@ __device__ __forceinline__ bf16x8 frag_mn_bf16(const char* lds, int col0, int ks
     const int kr = kb + 4 * r;
     const int c = (m >> 3) ^ ((kr & 3) << 1);
     const char* p = lds + kr * 512 + (c << 4) + ((m & 7) << 1);
-    i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPMLP_LDS i16x4*)(p));
-    v[r] = __builtin_bit_cast(bf16x4, t);
+    v[r] = __builtin_bit_cast(bf16x4, ds_read_tr16(p));
   }
   return __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
 }
-// e4m3, K-major tile: lane l takes row (l&31), bytes 64*ks + 32*(l>>5) .. +31.
-__device__ __forceinline__ i32x8 frag_k_e4m3(const char* lds, int row0, int ks, int lane) {
+// e4m3, K-major tile: lane l takes row (l&31), bytes 32*(l>>5) .. +31.
+__device__ __forceinline__ i32x8 frag_k_e4m3(const char* lds, int row0, int lane) {
   const int row = row0 + (lane & 31);
-  const int c0 = ((ks << 2) | ((lane >> 5) << 1));
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + row * kBKB + (((c0) ^ (row & 7)) << 4));
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(lds + row * kBKB + (((c0 + 1) ^ (row & 7)) << 4));
+  const int c0 = (lane >> 5) << 1;
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + row * kRowBytes + ((c0 ^ kswz(row)) << 4));
+  const u32x4 hi =
+      *reinterpret_cast<const u32x4*>(lds + row * kRowBytes + (((c0 + 1) ^ kswz(row)) << 4));
   i32x8 r;
   r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
   r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
   return r;
 }
 
+// Wait until at most N of this wave's vector-memory loads are in flight and
+// all its LDS reads are done, then barrier. The wait is the s_waitcnt builtin
+// (so the compiler's own wait tracking knows about it) with vmcnt = N,
+// expcnt and lgkmcnt = 0 (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[5:4] at bits 15:14). The empty asm statements keep
+// the compiler from moving memory accesses across the barrier, the
+// scheduling barriers keep the instruction scheduler from moving anything
+// (MFMAs included) across it.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  constexpr int imm = (N & 15) | (7 << 4) | ((N >> 4) << 14);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(imm);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // --------------------------------------------------------------- the kernel
 // IS_FP8: operands are e4m3 (both K-major). A_K / B_K: operand layouts.
 // EPI: epilogue kind. OutT: element type of EPI_STORE's output and of the
 // activation tensors (h, a, dH). COLSUM: also reduce A over k into e.colsum
-// (workgroups with tile column 0 only).
+// (workgroups with tile column 0 only; A must be MN-major).
 template <bool IS_FP8, bool A_K, bool B_K, int EPI, typename OutT, bool COLSUM>
 __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g, const EpiArgs e) {
   static_assert(!COLSUM || !A_K, "the fused column sum reads an MN-major A tile");
   static_assert(!IS_FP8 || (A_K && B_K), "e4m3 operands are K-major");
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
   constexpr bool kPair = (EPI == EPI_SWIGLU);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  constexpr int esz = IS_FP8 ? 1 : 2;
+  constexpr int kStep = kRowBytes / esz;  // k elements per stage
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
   int bm, bn;
   tile_coords(g, blockIdx.x, bm, bn);
   const int m0 = bm * kBM;
   const int n0 = bn * (kPair ? kBN / 2 : kBN);
-  constexpr int esz = IS_FP8 ? 1 : 2;
-  const int kelems_per_step = kBKB / esz;
-  const int nk = (g.K + kelems_per_step - 1) / kelems_per_step;
+  const int nk = (g.K + kStep - 1) / kStep;
 
   // ---- operand A loader
-  KMajorLoader la{};
+  KMajorLoader<false> la{};
   MNMajorLoader lma{};
   if constexpr (A_K) {
-    const char* base = static_cast<const char*>(g.A) + (int64_t)m0 * g.lda * esz;
-    la.rs0 = make_rsrc(base, (int64_t)(g.M - m0) * g.lda * esz);
-    la.rs1 = la.rs0;
-    la.ld_bytes = g.lda * esz;
+    const int64_t ldb_ = g.lda * esz;
+    la.rs0 = make_rsrc(static_cast<const char*>(g.A) + (int64_t)m0 * ldb_,
+                       (int64_t)(g.M - m0) * ldb_);
     la.kbytes = (uint32_t)(g.K * esz);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 3) + 64 * i;
-      la.row_off[i] = (m0 + row < g.M) ? (uint32_t)(row * la.ld_bytes) : kOOB;
-      la.use1[i] = false;
+      const int row = 16 * (wave * 4 + i) + (lane >> 2);
+      const int c = (lane & 3) ^ kswz(row);
+      la.chunk_b[i] = (uint32_t)(c << 4);
+      la.voff[i] = (m0 + row < g.M) ? (uint32_t)(row * ldb_) + (uint32_t)(c << 4) : kOOB;
     }
   } else {
     lma.base = static_cast<const char*>(g.A) + (int64_t)m0 * esz;
     lma.ld_bytes = g.lda * esz;
     lma.total_bytes = (int64_t)g.K * g.lda * esz - (int64_t)m0 * esz;
-    lma.col_ok = (m0 + ((tid & 31) << 3)) < g.M;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kr = 2 * (wave * 4 + i) + (lane >> 5);
+      const int c = (lane & 31) ^ ((kr & 3) << 1);
+      lma.voff[i] = (m0 + (c << 3) < g.M) ? (uint32_t)(kr * lma.ld_bytes) + (uint32_t)(c << 4) : kOOB;
+    }
   }
   // ---- operand B loader
-  KMajorLoader lb{};
+  KMajorLoader<kPair> lb{};
   MNMajorLoader lmb{};
   if constexpr (B_K) {
-    lb.ld_bytes = g.ldb * esz;
+    const int64_t ldb_ = g.ldb * esz;
     lb.kbytes = (uint32_t)(g.K * esz);
     if constexpr (kPair) {
-      // rows 64w + 32f + i  ->  gate (f = 0) or up (f = 1) row n0 + 32w + i
-      const char* gate = static_cast<const char*>(g.B) + (int64_t)n0 * g.ldb * esz;
-      const char* up = static_cast<const char*>(g.B) + (int64_t)(g.pair_off + n0) * g.ldb * esz;
-      const int64_t rem = (int64_t)(g.pair_off - n0) * g.ldb * esz;
-      lb.rs0 = make_rsrc(gate, rem);
-      lb.rs1 = make_rsrc(up, rem);
+      // tile row r: wave half wn = r/128, fragment f = (r/32)%4; f < 2 gate,
+      // f >= 2 up; feature n0 + 64 wn + 32 (f%2) + r%32
+      const int64_t rem = (int64_t)(g.pair_off - n0) * ldb_;
+      lb.rs0 = make_rsrc(static_cast<const char*>(g.B) + (int64_t)n0 * ldb_, rem);
+      lb.base1 = static_cast<const char*>(g.B) + (int64_t)(g.pair_off + n0) * ldb_;
+      lb.bytes1 = rem;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = (tid >> 3) + 64 * i;
-        const int lr = ((row >> 6) << 5) + (row & 31);
-        lb.row_off[i] = (n0 + lr < g.N) ? (uint32_t)(lr * lb.ld_bytes) : kOOB;
-        lb.use1[i] = (row >> 5) & 1;
+        const int row = 16 * (wave * 4 + i) + (lane >> 2);
+        const int c = (lane & 3) ^ kswz(row);
+        const int f = (row >> 5) & 3;
+        const int lr = ((row >> 7) << 6) + ((f & 1) << 5) + (row & 31);
+        lb.chunk_b[i] = (uint32_t)(c << 4);
+        lb.voff[i] = (n0 + lr < g.N) ? (uint32_t)(lr * ldb_) + (uint32_t)(c << 4) : kOOB;
       }
     } else {
-      const char* base = static_cast<const char*>(g.B) + (int64_t)n0 * g.ldb * esz;
-      lb.rs0 = make_rsrc(base, (int64_t)(g.N - n0) * g.ldb * esz);
-      lb.rs1 = lb.rs0;
+      lb.rs0 = make_rsrc(static_cast<const char*>(g.B) + (int64_t)n0 * ldb_,
+                         (int64_t)(g.N - n0) * ldb_);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = (tid >> 3) + 64 * i;
-        lb.row_off[i] = (n0 + row < g.N) ? (uint32_t)(row * lb.ld_bytes) : kOOB;
-        lb.use1[i] = false;
+        const int row = 16 * (wave * 4 + i) + (lane >> 2);
+        const int c = (lane & 3) ^ kswz(row);
+        lb.chunk_b[i] = (uint32_t)(c << 4);
+        lb.voff[i] = (n0 + row < g.N) ? (uint32_t)(row * ldb_) + (uint32_t)(c << 4) : kOOB;
       }
     }
   } else {
     lmb.base = static_cast<const char*>(g.B) + (int64_t)n0 * esz;
     lmb.ld_bytes = g.ldb * esz;
     lmb.total_bytes = (int64_t)g.K * g.ldb * esz - (int64_t)n0 * esz;
-    lmb.col_ok = (n0 + ((tid & 31) << 3)) < g.N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kr = 2 * (wave * 4 + i) + (lane >> 5);
+      const int c = (lane & 31) ^ ((kr & 3) << 1);
+      lmb.voff[i] = (n0 + (c << 3) < g.N) ? (uint32_t)(kr * lmb.ld_bytes) + (uint32_t)(c << 4) : kOOB;
+    }
   }
 
+  // DMA instruction j of stage kt: j = 0..3 fill the A tile, 4..7 the B tile.
+  auto issue_one = [&](int kt, int j) __attribute__((always_inline)) {
+    char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
+    char* sb = sa + kTileBytes;
+    if (j < 4) {
+      if constexpr (A_K) la.issue_one(sa, wave, (uint32_t)(kt * kRowBytes), j);
+      else lma.issue_one(sa, wave, kt * kStep, j);
+    } else {
+      if constexpr (B_K) lb.issue_one(sb, wave, (uint32_t)(kt * kRowBytes), j - 4);
+      else lmb.issue_one(sb, wave, kt * kStep, j - 4);
+    }
+  };
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) issue_one(kt, j);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // fused column sum: thread t owns 8 columns (chunk t%32) of k-rows t/32 + 8j
   const bool do_colsum = COLSUM && (bn == 0) && (e.colsum != nullptr);
   float csum[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) csum[j] = 0.f;
 
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int kt) {
-    if constexpr (A_K) la.load(ra, tid, (uint32_t)(kt * kBKB));
-    else lma.load(ra, tid, kt * kelems_per_step);
-    if constexpr (B_K) lb.load(rb, tid, (uint32_t)(kt * kBKB));
-    else lmb.load(rb, tid, kt * kelems_per_step);
+  // Fragment registers, double-buffered: while the MFMAs of one half-stage
+  // run, the LDS reads of the next half-stage are in flight.
+  using Frag = typename std::conditional<IS_FP8, i32x8, bf16x8>::type;
+  Frag pa[4], pb[4], qa[4], qb[4];
+  auto frag_a = [&](int kt, int ks, int f) __attribute__((always_inline)) -> Frag {
+    const char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
+    if constexpr (IS_FP8) return frag_k_e4m3(sa, 128 * wm + 32 * f, lane);
+    else if constexpr (A_K) return frag_k_bf16(sa, 128 * wm + 32 * f, ks, lane);
+    else return frag_mn_bf16(sa, 128 * wm + 32 * f, ks, lane);
   };
-  auto sstore = [&](int stage) {
-    char* sa = smem + stage * (2 * kTileBytes);
-    char* sb = sa + kTileBytes;
-    if constexpr (A_K) KMajorLoader::store(sa, ra, tid);
-    else MNMajorLoader::store(sa, ra, tid);
-    if constexpr (B_K) KMajorLoader::store(sb, rb, tid);
-    else MNMajorLoader::store(sb, rb, tid);
+  auto frag_b = [&](int kt, int ks, int f) __attribute__((always_inline)) -> Frag {
+    const char* sb = smem + (kt & (kStages - 1)) * kStageBytes + kTileBytes;
+    if constexpr (IS_FP8) return frag_k_e4m3(sb, 128 * wn + 32 * f, lane);
+    else if constexpr (B_K) return frag_k_bf16(sb, 128 * wn + 32 * f, ks, lane);
+    else return frag_mn_bf16(sb, 128 * wn + 32 * f, ks, lane);
+  };
+  auto mma = [&](int fm, int fn, const Frag& fa, const Frag& fb) __attribute__((always_inline)) {
+    if constexpr (IS_FP8)
+      acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[fm][fn], 0, 0, 0,
+                                                                    0, 0, 0);
+    else
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[fm][fn], 0, 0, 0);
+  };
+  auto colsum_part = [&](int kt, int j) __attribute__((always_inline)) {
     if constexpr (COLSUM) {
       if (do_colsum) {
+        const char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
+        const int c = tid & 31;
+        const int kr = (tid >> 5) + 8 * j;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sa + kr * 512 + ((c ^ ((kr & 3) << 1)) << 4));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            csum[2 * w] += bf2f((bf16_t)(ra[i][w] & 0xffffu));
-            csum[2 * w + 1] += bf2f((bf16_t)(ra[i][w] >> 16));
-          }
+        for (int w = 0; w < 4; ++w) {
+          csum[2 * w] += bf2f((bf16_t)(v[w] & 0xffffu));
+          csum[2 * w + 1] += bf2f((bf16_t)(v[w] >> 16));
+        }
       }
     }
   };
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  // Every stage index is issued, also those past the end of K: their offsets
+  // fall outside the resources, so they cost no memory traffic and load
+  // zeros, and the number of loads in flight stays uniform -- every wait below
+  // is the same vmcnt and the loop body has no branches.
+  //
+  // The half-stages below pin their instruction order (a scheduling barrier
+  // after every slot): slot i issues MFMA i, then its share of the LDS reads
+  // for the next half-stage, then (in the second half) its share of the DMA
+  // loads, so neither the LDS nor the vector-memory queue ever holds up the
+  // MFMA issue for long.
+  //
+  // prologue: stages 0..3 in flight; stage 0's first fragments in registers
+#pragma unroll
+  for (int s = 0; s < kStages; ++s) issue(s);
+  wait_and_barrier<24>();
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    pa[f] = frag_a(0, 0, f);
+    pb[f] = frag_b(0, 0, f);
+  }
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const char* sa = smem + stage * (2 * kTileBytes);
-    const char* sb = sa + kTileBytes;
-    if constexpr (!IS_FP8) {
+  if constexpr (!IS_FP8) {
+    // stage kt: [MFMAs (kt, ks0) | reads (kt, ks1)]
+    //           barrier: stage kt+1 has landed; every wave holds stage kt
+    //           [MFMAs (kt, ks1) | reads (kt+1, ks0) | DMA stage kt+4 into kt's buffer]
+    for (int kt = 0; kt < nk; ++kt) {
+      if constexpr (!A_K || !B_K) wait_lds();  // transpose reads of (kt, ks0) done
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        bf16x8 af[4], bfr[2];
-#pragma unroll
-        for (int fm = 0; fm < 4; ++fm) {
-          if constexpr (A_K) af[fm] = frag_k_bf16(sa, 128 * wm + 32 * fm, ks, lane);
-          else af[fm] = frag_mn_bf16(sa, 128 * wm + 32 * fm, ks, lane);
+      for (int i = 0; i < 16; ++i) {
+        mma(i >> 2, i & 3, pa[i >> 2], pb[i & 3]);
+        if (i < 8) {
+          if (i & 1) qb[i >> 1] = frag_b(kt, 1, i >> 1);
+          else qa[i >> 1] = frag_a(kt, 1, i >> 1);
+        } else if (i < 12) {
+          colsum_part(kt, i - 8);
         }
-#pragma unroll
-        for (int fn = 0; fn < 2; ++fn) {
-          if constexpr (B_K) bfr[fn] = frag_k_bf16(sb, 64 * wn + 32 * fn, ks, lane);
-          else bfr[fn] = frag_mn_bf16(sb, 64 * wn + 32 * fn, ks, lane);
-        }
-#pragma unroll
-        for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < 2; ++fn)
-            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    } else {
+      wait_and_barrier<16>();
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        i32x8 af[4], bfr[2];
-#pragma unroll
-        for (int fm = 0; fm < 4; ++fm) af[fm] = frag_k_e4m3(sa, 128 * wm + 32 * fm, ks, lane);
-#pragma unroll
-        for (int fn = 0; fn < 2; ++fn) bfr[fn] = frag_k_e4m3(sb, 64 * wn + 32 * fn, ks, lane);
-#pragma unroll
-        for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < 2; ++fn)
-            acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[fm], bfr[fn], acc[fm][fn], 0, 0, 0, 0, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        mma(i >> 2, i & 3, qa[i >> 2], qb[i & 3]);
+        if (i < 8) {
+          if (i & 1) pb[i >> 1] = frag_b(kt + 1, 0, i >> 1);
+          else pa[i >> 1] = frag_a(kt + 1, 0, i >> 1);
+        }
+        if (i & 1) issue_one(kt + kStages, i >> 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (kt + 1 < nk) sstore(stage ^ 1);
-    __syncthreads();
+  } else {
+    // e4m3: one MFMA k-step per stage. [MFMAs fm 0-1] barrier [MFMAs fm 2-3 |
+    // reads of stage kt+1 | DMA stage kt+4]; the copy at the end is register
+    // renaming.
+    for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mma(i >> 2, i & 3, pa[i >> 2], pb[i & 3]);
+      wait_and_barrier<16>();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        mma(2 + (i >> 2), i & 3, pa[2 + (i >> 2)], pb[i & 3]);
+        if (i & 1) qb[i >> 1] = frag_b(kt + 1, 0, i >> 1);
+        else qa[i >> 1] = frag_a(kt + 1, 0, i >> 1);
+        issue_one(kt + kStages, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int f = 0; f < 4; ++f) { pa[f] = qa[f]; pb[f] = qb[f]; }
+    }
   }
 
   // ---- fused column sum of A (db1 = sum over tokens of dH)
   if constexpr (COLSUM) {
     if (do_colsum) {
-      // threads t and t + 32j (j = 0..15) hold the same 8 columns
-      float* red = reinterpret_cast<float*>(smem);  // 16 x 256 floats
+      __syncthreads();  // all waves are done with the stage buffers
+      float* red = reinterpret_cast<float*>(smem);  // 8 x 256 floats
 #pragma unroll
       for (int j = 0; j < 8; ++j) red[(tid >> 5) * 256 + ((tid & 31) << 3) + j] = csum[j];
       __syncthreads();
-      if (tid < 256) {
-        float s = 0.f;
-        for (int q = 0; q < 16; ++q) s += red[q * 256 + tid];
-        const int m = m0 + tid;
-        if (m < g.M) e.colsum[m] = e.accumulate ? e.colsum[m] + s : s;
-      }
+      const int m = m0 + tid;
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += red[q * 256 + tid];
+      if (m < g.M) e.colsum[m] = e.accumulate ? e.colsum[m] + s : s;
     }
   }
 
   // ---- epilogue. acc[fm][fn][j] is C at
-  //   row m0 + 128 wm + 32 fm + 8 (j/4) + 4 (lane/32) + j%4,
-  //   col n0 + 64 wn + 32 fn + lane%32          (pair tiles: see below)
+  //   row 128 wm + 32 fm + 8 (j/4) + 4 (lane/32) + j%4 of the tile,
+  //   col 128 wn + 32 fn + lane%32                  (pair tiles: see above).
+  // Each wave stages one 32-row slab (fm) at a time through its own 17 KiB of
+  // LDS as fp32 [32][136] (8 floats of padding put the two row groups a
+  // 32x32 result writes per instruction in different banks), then every lane
+  // takes 8 consecutive columns of a row: 16-byte loads and stores, each row
+  // segment written by consecutive lanes.
+  __syncthreads();  // every wave is done reading the stage buffers
   float alpha = 1.0f;
   if constexpr (IS_FP8) alpha = (*e.scale_a) * (*e.scale_b);
   float amax = 0.f;
-  const int rbase = m0 + 128 * wm + 4 * (lane >> 5);
-  if constexpr (kPair) {
-    const int col = n0 + 32 * wn + (lane & 31);
-    if (col < g.N) {
+  constexpr int kLd = 136;
+  float* wl = reinterpret_cast<float*>(smem + wave * 32768);
 #pragma unroll
-      for (int fm = 0; fm < 4; ++fm)
+  for (int fm = 0; fm < 4; ++fm) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int row = rbase + 32 * fm + 8 * (j >> 2) + (j & 3);
-          if (row < g.M)
-            epi_pair<OutT>(e, g.pair_off, row, col, acc[fm][0][j] * alpha, acc[fm][1][j] * alpha);
-        }
-    }
-  } else {
+    for (int fn = 0; fn < 4; ++fn)
 #pragma unroll
-    for (int fn = 0; fn < 2; ++fn) {
-      const int col = n0 + 64 * wn + 32 * fn + (lane & 31);
-      if (col >= g.N) continue;
-      float bias = 0.f;
-      if constexpr (EPI == EPI_BIAS_GELU) {
-        if (e.bias) bias = Elem<OutT>::load(e.bias, col);
+      for (int j = 0; j < 16; ++j)
+        wl[(8 * (j >> 2) + 4 * (lane >> 5) + (j & 3)) * kLd + 32 * fn + (lane & 31)] = acc[fm][fn][j];
+    const int row0 = m0 + 128 * wm + 32 * fm;
+    if constexpr (kPair) {
+      // slab columns [0, 64) gate and [64, 128) up of the wave's 64 features
+#pragma unroll 2
+      for (int t = 0; t < 4; ++t) {
+        const int q = lane + 64 * t;
+        const int r = q >> 3, cg = q & 7;
+        const int row = row0 + r, col = n0 + 64 * wn + 8 * cg;
+        float gt[8], up[8];
+        const float* src = wl + r * kLd + 8 * cg;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) { gt[u] = src[u]; up[u] = src[64 + u]; }
+        if (row < g.M && col < g.N) epi_pair8<OutT>(e, g.pair_off, row, col, gt, up, alpha);
       }
+    } else {
+#pragma unroll 2
+      for (int t = 0; t < 8; ++t) {
+        const int q = lane + 64 * t;
+        const int r = q >> 4, cg = q & 15;
+        const int row = row0 + r, col = n0 + 128 * wn + 8 * cg;
+        float v[8];
+        const float* src = wl + r * kLd + 8 * cg;
 #pragma unroll
-      for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int row = rbase + 32 * fm + 8 * (j >> 2) + (j & 3);
-          if (row < g.M)
-            epi_one<EPI, OutT, IS_FP8>(e, g.pair_off, row, col, acc[fm][fn][j], alpha, bias, amax);
-        }
+        for (int u = 0; u < 8; ++u) v[u] = src[u];
+        if (row < g.M && col < g.N) epi_group8<EPI, OutT, IS_FP8>(e, g.pair_off, row, col, v, alpha, amax);
+      }
     }
   }
   if constexpr (IS_FP8 && EPI == EPI_BIAS_GELU) {
     amax = wave_max(amax);
-    __shared__ float wmax[8];
+    __shared__ float wmax[4];
     if (lane == 0) wmax[wave] = amax;
     __syncthreads();
     if (tid == 0) {
       float m = 0.f;
-      for (int w = 0; w < 8; ++w) m = __builtin_fmaxf(m, wmax[w]);
+      for (int w = 0; w < 4; ++w) m = __builtin_fmaxf(m, wmax[w]);
       e.amax_part[blockIdx.x] = m;
     }
   }
