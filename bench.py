@@ -53,7 +53,7 @@ def measured_traffic(kernel: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
-def cpu_baseline(w, tokens: int) -> dict:
+def cpu_baseline(w, tokens: int, repeats: int = 3) -> dict:
     """The CPU oracle (fp64 NumPy, as it stands) on the first `tokens` tokens
     of the same per-rank shard: forward, dgrad and wgrad."""
     import numpy as np
@@ -70,16 +70,21 @@ def cpu_baseline(w, tokens: int) -> dict:
     inp = synth.make_rank_inputs(w, tokens=tokens)
     x, W1, W2, dy = (oracle.to_f64(inp[k]) for k in ("x", "W1", "W2", "dy"))
     b1 = oracle.to_f64(inp["b1"]) if w.has_bias else None
-    t0 = time.perf_counter()
-    f = oracle.rank_forward(x, W1, b1, W2, w.act)
-    g = oracle.rank_dgrad(dy, W1, W2, f["h"], w.act)
-    oracle.rank_wgrad(dy, x, f["a"], g["dH"], w.has_bias)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        f = oracle.rank_forward(x, W1, b1, W2, w.act)
+        g = oracle.rank_dgrad(dy, W1, W2, f["h"], w.act)
+        oracle.rank_wgrad(dy, x, f["a"], g["dH"], w.has_bias)
+        times.append(time.perf_counter() - t0)
+        del f, g
+    dt = sorted(times)[len(times) // 2]
     flops = w.flops(tokens=tokens)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"fwd+dgrad+wgrad of the first {tokens} of {w.tokens} tokens of the "
-                      f"{w.name} shard in fp64 NumPy ({flops / 1e12:.3f} TFLOP, {dt:.2f} s)"}
+                      f"{w.name} shard in fp64 NumPy, median of {repeats} runs "
+                      f"({flops / 1e12:.3f} TFLOP per run, {dt:.2f} s, {sum(times):.1f} s total)"}
 
 
 def main():
@@ -88,7 +93,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3, help="workload id (3: H=8192 TP=8 shard)")
-    ap.add_argument("--cpu-tokens", type=int, default=2048,
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens in the CPU oracle sample (0: skip)")
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
     ap.add_argument("--copy-calibration", action="store_true",

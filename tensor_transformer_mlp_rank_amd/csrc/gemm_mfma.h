@@ -37,11 +37,14 @@
 // instruction, so swizzles are applied by choosing which global chunk each
 // lane fetches):
 //   * K-major tile: [256 rows][64 B]; 16-byte chunk c of row r lives at chunk
-//     c ^ ((r >> 1) & 3). Any 8 consecutive rows then put a given chunk in 8
-//     distinct 16-byte slots of a 128-byte bank window, so the fragment reads
-//     (ds_read_b128, 8 consecutive k of one row per lane) are conflict-free.
+//     c ^ (((r >> 1) ^ (r >> 2)) & 3). Any 16 consecutive rows then put a given
+//     chunk in 16 distinct 16-byte slots of a 256-byte bank window, so the
+//     fragment reads (ds_read_b128, 8 consecutive k of one row per lane) are
+//     conflict-free.
 //   * MN-major tile: [32 k-rows][256 elements = 512 B]; chunk c of k-row r
-//     lives at chunk c ^ 2(r & 3). Fragments are read with the CDNA4 transpose
+//     lives at chunk c ^ {0, 4, 10, 14}[r % 4], which spreads the 32 lanes of
+//     a transpose read over 32 distinct 8-byte slots of a 256-byte bank window.
+//     Fragments are read with the CDNA4 transpose
 //     read ds_read_b64_tr_b16: in each group of 16 lanes, lane j receives
 //     element j%4 of the 8-byte chunks addressed by lanes 4q + j/4 (q = 0..3),
 //     so pointing lane i at k-row k0 + i/4, elements m0 + 4(i%4) .. +3 hands
@@ -144,7 +147,11 @@ struct MNMajorLoader {
 };
 
 // --------------------------------------------------------------- fragment reads
-__device__ __forceinline__ int kswz(int row) { return (row >> 1) & 3; }
+// Swizzles (measured conflict-free on gfx950, whose LDS serves 256 bytes per
+// cycle): K-major rows put chunk c at c ^ kswz(row); MN-major k-rows put chunk
+// c at c ^ mnswz(krow), mnswz = 0, 4, 10, 14 for krow % 4 = 0..3.
+__device__ __forceinline__ int kswz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+__device__ __forceinline__ int mnswz(int kr) { return (0xEA40 >> ((kr & 3) << 2)) & 15; }
 
 // bf16, K-major tile: lane l takes row row0 + (l&31), k elements
 // 16*ks + 8*(l>>5) .. +7 of the stage.
@@ -179,7 +186,7 @@ __device__ __forceinline__ bf16x8 frag_mn_bf16(const char* lds, int col0, int ks
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int kr = kb + 4 * r;
-    const int c = (m >> 3) ^ ((kr & 3) << 1);
+    const int c = (m >> 3) ^ mnswz(kr);
     const char* p = lds + kr * 512 + (c << 4) + ((m & 7) << 1);
     v[r] = __builtin_bit_cast(bf16x4, ds_read_tr16(p));
   }
@@ -262,7 +269,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int kr = 2 * (wave * 4 + i) + (lane >> 5);
-      const int c = (lane & 31) ^ ((kr & 3) << 1);
+      const int c = (lane & 31) ^ mnswz(kr);
       lma.voff[i] = (m0 + (c << 3) < g.M) ? (uint32_t)(kr * lma.ld_bytes) + (uint32_t)(c << 4) : kOOB;
     }
   }
@@ -306,7 +313,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int kr = 2 * (wave * 4 + i) + (lane >> 5);
-      const int c = (lane & 31) ^ ((kr & 3) << 1);
+      const int c = (lane & 31) ^ mnswz(kr);
       lmb.voff[i] = (n0 + (c << 3) < g.N) ? (uint32_t)(kr * lmb.ld_bytes) + (uint32_t)(c << 4) : kOOB;
     }
   }
@@ -371,7 +378,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
         const char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
         const int c = tid & 31;
         const int kr = (tid >> 5) + 8 * j;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(sa + kr * 512 + ((c ^ ((kr & 3) << 1)) << 4));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sa + kr * 512 + ((c ^ mnswz(kr)) << 4));
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           csum[2 * w] += bf2f((bf16_t)(v[w] & 0xffffu));
@@ -472,15 +479,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   //   row 128 wm + 32 fm + 8 (j/4) + 4 (lane/32) + j%4 of the tile,
   //   col 128 wn + 32 fn + lane%32                  (pair tiles: see above).
   // Each wave stages one 32-row slab (fm) at a time through its own 17 KiB of
-  // LDS as fp32 [32][136] (8 floats of padding put the two row groups a
-  // 32x32 result writes per instruction in different banks), then every lane
+  // LDS as fp32 [32][132] (4 floats of padding: measured conflict-free for
+  // both the scattered writes and the row-segment reads), then every lane
   // takes 8 consecutive columns of a row: 16-byte loads and stores, each row
   // segment written by consecutive lanes.
   __syncthreads();  // every wave is done reading the stage buffers
   float alpha = 1.0f;
   if constexpr (IS_FP8) alpha = (*e.scale_a) * (*e.scale_b);
   float amax = 0.f;
-  constexpr int kLd = 136;
+  constexpr int kLd = 132;
   float* wl = reinterpret_cast<float*>(smem + wave * 32768);
 #pragma unroll
   for (int fm = 0; fm < 4; ++fm) {
