@@ -69,9 +69,9 @@ namespace tpmlp {
 
 constexpr int kBM = 256, kBN = 256;
 constexpr int kThreads = 256;
-constexpr int kRowBytes = 64;                      // per tile row per stage
-constexpr int kStages = 4;
-constexpr int kTileBytes = 256 * kRowBytes;        // 16 KiB
+constexpr int kRowBytes = 128;                     // per tile row per stage
+constexpr int kStages = 2;
+constexpr int kTileBytes = 256 * kRowBytes;        // 32 KiB
 constexpr int kStageBytes = 2 * kTileBytes;        // A + B
 constexpr int kSmemBytes = kStages * kStageBytes;  // 128 KiB
 
@@ -98,59 +98,63 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, char* lds_w
 }
 
 // --------------------------------------------------------------- tile loaders
-// Each wave issues 4 instructions per tile per stage; instruction i of wave w
-// fills LDS bytes [(4w + i) KiB, +1 KiB) of the tile.
+// A tile is filled by 32 load instructions of 1 KiB; instruction ii fills LDS
+// bytes [ii KiB, +1 KiB). Wave w issues instructions 8w .. 8w+7 of each tile.
 //
-// K-major: instruction (w, i) covers rows 16(4w+i) .. +15; lane l fetches row
-// 16(4w+i) + l/4, logical chunk (l%4) ^ swz(row).
-// For the gated fc1 the tile rows of instruction (w, i) all come from one
-// half of W1 (gate: rs0, up: base1); which one depends on (w, i) only, so the
+// K-major: instruction ii covers rows 8 ii .. +7 (a full 128-byte row each, so
+// every request is a whole cache line); lane l fetches row 8 ii + l/8,
+// logical chunk (l%8) ^ kswz(row).
+// For the gated fc1 the rows of one instruction all come from one half of W1
+// (gate: rs0, up: base1); which one depends on the instruction only, so the
 // choice is wave-uniform and the resource stays in scalar registers.
 template <bool PAIR>
 struct KMajorLoader {
   __amdgpu_buffer_rsrc_t rs0;
   const char* base1;              // gated fc1: start of the up half's rows
   int64_t bytes1;
-  uint32_t voff[4];               // row*ld + chunk*16 within its resource, or kOOB
-  uint32_t chunk_b[4];            // chunk*16 (for the K-range mask)
+  uint32_t voff[8];               // row*ld + chunk*16 within its resource, or kOOB
+  uint32_t chunk_b[8];            // chunk*16 (for the K-range mask)
   uint32_t kbytes;                // row length K * element size
 
-  __device__ __forceinline__ static bool up_half(int wave, int i) {
-    return (((wave * 4 + i) >> 1) & 3) >= 2;  // fragment (row / 32) % 4 of these rows
+  __device__ __forceinline__ static bool up_half(int ii) {
+    return ((ii >> 2) & 3) >= 2;  // fragment (row / 32) % 4 of these rows
   }
   __device__ __forceinline__ void issue_one(char* tile, int wave, uint32_t k0b, int i) const {
+    const int ii = 8 * wave + i;
     const uint32_t off = (voff[i] != kOOB && k0b + chunk_b[i] < kbytes) ? voff[i] + k0b : kOOB;
     if constexpr (PAIR) {
-      if (up_half(wave, i))
-        lds_dma16(make_rsrc(base1, bytes1), tile + ((wave * 4 + i) << 10), off);
+      if (up_half(ii))
+        lds_dma16(make_rsrc(base1, bytes1), tile + (ii << 10), off);
       else
-        lds_dma16(rs0, tile + ((wave * 4 + i) << 10), off);
+        lds_dma16(rs0, tile + (ii << 10), off);
     } else {
-      lds_dma16(rs0, tile + ((wave * 4 + i) << 10), off);
+      lds_dma16(rs0, tile + (ii << 10), off);
     }
   }
 };
 
-// MN-major (bf16 only): instruction (w, i) covers k-rows 2(4w+i), +1; lane l
-// fetches k-row 2(4w+i) + l/32, logical chunk (l%32) ^ 2(krow&3). The
-// resource is rebased to the stage's first k-row.
+// MN-major (bf16 only): instruction ii covers k-rows 2 ii, +1; lane l fetches
+// k-row 2 ii + l/32, logical chunk (l%32) ^ mnswz(krow). The resource is
+// rebased to the stage's first k-row.
 struct MNMajorLoader {
   const char* base;      // element (k=0, m=tile start)
   int64_t ld_bytes;
   int64_t total_bytes;   // bytes from `base` to the end of the tensor
-  uint32_t voff[4];
+  uint32_t voff[8];
 
   __device__ __forceinline__ void issue_one(char* tile, int wave, int k0, int i) const {
     const int64_t kofs = (int64_t)k0 * ld_bytes;
-    lds_dma16(make_rsrc(base + kofs, total_bytes - kofs), tile + ((wave * 4 + i) << 10), voff[i]);
+    lds_dma16(make_rsrc(base + kofs, total_bytes - kofs), tile + ((8 * wave + i) << 10), voff[i]);
   }
 };
 
 // --------------------------------------------------------------- fragment reads
-// Swizzles (measured conflict-free on gfx950, whose LDS serves 256 bytes per
-// cycle): K-major rows put chunk c at c ^ kswz(row); MN-major k-rows put chunk
-// c at c ^ mnswz(krow), mnswz = 0, 4, 10, 14 for krow % 4 = 0..3.
-__device__ __forceinline__ int kswz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+// Swizzles (gfx950's LDS serves 256 bytes per cycle): K-major 128-byte rows
+// put chunk c at c ^ ((row >> 1) & 7), so 16 consecutive rows put a given
+// chunk in 16 distinct 16-byte slots of a 256-byte window; MN-major k-rows put
+// chunk c at c ^ mnswz(krow), mnswz = 0, 4, 10, 14 for krow % 4 = 0..3
+// (measured conflict-free).
+__device__ __forceinline__ int kswz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int mnswz(int kr) { return (0xEA40 >> ((kr & 3) << 2)) & 15; }
 
 // bf16, K-major tile: lane l takes row row0 + (l&31), k elements
@@ -192,10 +196,10 @@ __device__ __forceinline__ bf16x8 frag_mn_bf16(const char* lds, int col0, int ks
   }
   return __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
 }
-// e4m3, K-major tile: lane l takes row (l&31), bytes 32*(l>>5) .. +31.
-__device__ __forceinline__ i32x8 frag_k_e4m3(const char* lds, int row0, int lane) {
+// e4m3, K-major tile: lane l takes row (l&31), bytes 64*ks + 32*(l>>5) .. +31.
+__device__ __forceinline__ i32x8 frag_k_e4m3(const char* lds, int row0, int ks, int lane) {
   const int row = row0 + (lane & 31);
-  const int c0 = (lane >> 5) << 1;
+  const int c0 = (ks << 2) | ((lane >> 5) << 1);
   const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + row * kRowBytes + ((c0 ^ kswz(row)) << 4));
   const u32x4 hi =
       *reinterpret_cast<const u32x4*>(lds + row * kRowBytes + (((c0 + 1) ^ kswz(row)) << 4));
@@ -215,7 +219,7 @@ __device__ __forceinline__ i32x8 frag_k_e4m3(const char* lds, int row0, int lane
 // (MFMAs included) across it.
 template <int N>
 __device__ __forceinline__ void wait_and_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
+  static_assert(N >= 0 && N <= 63, "vmcnt range (63: no wait on loads)");
   constexpr int imm = (N & 15) | (7 << 4) | ((N >> 4) << 14);
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
@@ -256,9 +260,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
                        (int64_t)(g.M - m0) * ldb_);
     la.kbytes = (uint32_t)(g.K * esz);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * (wave * 4 + i) + (lane >> 2);
-      const int c = (lane & 3) ^ kswz(row);
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * (wave * 8 + i) + (lane >> 3);
+      const int c = (lane & 7) ^ kswz(row);
       la.chunk_b[i] = (uint32_t)(c << 4);
       la.voff[i] = (m0 + row < g.M) ? (uint32_t)(row * ldb_) + (uint32_t)(c << 4) : kOOB;
     }
@@ -267,8 +271,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     lma.ld_bytes = g.lda * esz;
     lma.total_bytes = (int64_t)g.K * g.lda * esz - (int64_t)m0 * esz;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kr = 2 * (wave * 4 + i) + (lane >> 5);
+    for (int i = 0; i < 8; ++i) {
+      const int kr = 2 * (wave * 8 + i) + (lane >> 5);
       const int c = (lane & 31) ^ mnswz(kr);
       lma.voff[i] = (m0 + (c << 3) < g.M) ? (uint32_t)(kr * lma.ld_bytes) + (uint32_t)(c << 4) : kOOB;
     }
@@ -287,9 +291,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
       lb.base1 = static_cast<const char*>(g.B) + (int64_t)(g.pair_off + n0) * ldb_;
       lb.bytes1 = rem;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * (wave * 4 + i) + (lane >> 2);
-        const int c = (lane & 3) ^ kswz(row);
+      for (int i = 0; i < 8; ++i) {
+        const int row = 8 * (wave * 8 + i) + (lane >> 3);
+        const int c = (lane & 7) ^ kswz(row);
         const int f = (row >> 5) & 3;
         const int lr = ((row >> 7) << 6) + ((f & 1) << 5) + (row & 31);
         lb.chunk_b[i] = (uint32_t)(c << 4);
@@ -299,9 +303,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
       lb.rs0 = make_rsrc(static_cast<const char*>(g.B) + (int64_t)n0 * ldb_,
                          (int64_t)(g.N - n0) * ldb_);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * (wave * 4 + i) + (lane >> 2);
-        const int c = (lane & 3) ^ kswz(row);
+      for (int i = 0; i < 8; ++i) {
+        const int row = 8 * (wave * 8 + i) + (lane >> 3);
+        const int c = (lane & 7) ^ kswz(row);
         lb.chunk_b[i] = (uint32_t)(c << 4);
         lb.voff[i] = (n0 + row < g.N) ? (uint32_t)(row * ldb_) + (uint32_t)(c << 4) : kOOB;
       }
@@ -311,28 +315,29 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     lmb.ld_bytes = g.ldb * esz;
     lmb.total_bytes = (int64_t)g.K * g.ldb * esz - (int64_t)n0 * esz;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kr = 2 * (wave * 4 + i) + (lane >> 5);
+    for (int i = 0; i < 8; ++i) {
+      const int kr = 2 * (wave * 8 + i) + (lane >> 5);
       const int c = (lane & 31) ^ mnswz(kr);
       lmb.voff[i] = (n0 + (c << 3) < g.N) ? (uint32_t)(kr * lmb.ld_bytes) + (uint32_t)(c << 4) : kOOB;
     }
   }
 
-  // DMA instruction j of stage kt: j = 0..3 fill the A tile, 4..7 the B tile.
+  // This wave's load instruction j of stage kt: j = 0..7 fill its part of
+  // the A tile, 8..15 of the B tile.
   auto issue_one = [&](int kt, int j) __attribute__((always_inline)) {
     char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
     char* sb = sa + kTileBytes;
-    if (j < 4) {
+    if (j < 8) {
       if constexpr (A_K) la.issue_one(sa, wave, (uint32_t)(kt * kRowBytes), j);
       else lma.issue_one(sa, wave, kt * kStep, j);
     } else {
-      if constexpr (B_K) lb.issue_one(sb, wave, (uint32_t)(kt * kRowBytes), j - 4);
-      else lmb.issue_one(sb, wave, kt * kStep, j - 4);
+      if constexpr (B_K) lb.issue_one(sb, wave, (uint32_t)(kt * kRowBytes), j - 8);
+      else lmb.issue_one(sb, wave, kt * kStep, j - 8);
     }
   };
   auto issue = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) issue_one(kt, j);
+    for (int j = 0; j < 16; ++j) issue_one(kt, j);
   };
 
   f32x16 acc[4][4];
@@ -349,29 +354,41 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
 #pragma unroll
   for (int j = 0; j < 8; ++j) csum[j] = 0.f;
 
-  // Fragment registers, double-buffered: while the MFMAs of one half-stage
-  // run, the LDS reads of the next half-stage are in flight.
+  // A stage has kKs MFMA k-steps (4 for bf16: 16 elements each; 2 for e4m3:
+  // 64 each) of 16 MFMAs. The fragments of k-step ks live in register slot
+  // ks (A rows 128 wm + 32 f, B rows 128 wn + 32 f, f = 0..3).
+  constexpr int kKs = IS_FP8 ? 2 : 4;
   using Frag = typename std::conditional<IS_FP8, i32x8, bf16x8>::type;
-  Frag pa[4], pb[4], qa[4], qb[4];
+  Frag fa[kKs][4], fb[kKs][4];
   auto frag_a = [&](int kt, int ks, int f) __attribute__((always_inline)) -> Frag {
     const char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
-    if constexpr (IS_FP8) return frag_k_e4m3(sa, 128 * wm + 32 * f, lane);
+    if constexpr (IS_FP8) return frag_k_e4m3(sa, 128 * wm + 32 * f, ks, lane);
     else if constexpr (A_K) return frag_k_bf16(sa, 128 * wm + 32 * f, ks, lane);
     else return frag_mn_bf16(sa, 128 * wm + 32 * f, ks, lane);
   };
   auto frag_b = [&](int kt, int ks, int f) __attribute__((always_inline)) -> Frag {
     const char* sb = smem + (kt & (kStages - 1)) * kStageBytes + kTileBytes;
-    if constexpr (IS_FP8) return frag_k_e4m3(sb, 128 * wn + 32 * f, lane);
+    if constexpr (IS_FP8) return frag_k_e4m3(sb, 128 * wn + 32 * f, ks, lane);
     else if constexpr (B_K) return frag_k_bf16(sb, 128 * wn + 32 * f, ks, lane);
     else return frag_mn_bf16(sb, 128 * wn + 32 * f, ks, lane);
   };
-  auto mma = [&](int fm, int fn, const Frag& fa, const Frag& fb) __attribute__((always_inline)) {
-    if constexpr (IS_FP8)
-      acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[fm][fn], 0, 0, 0,
-                                                                    0, 0, 0);
-    else
-      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[fm][fn], 0, 0, 0);
+  // fragment j (0..7) of k-step ks of stage kt: A0..3, then B0..3
+  auto read_one = [&](int kt, int ks, int j) __attribute__((always_inline)) {
+    if (j & 4) fb[ks][j & 3] = frag_b(kt, ks, j & 3);
+    else fa[ks][j & 3] = frag_a(kt, ks, j & 3);
   };
+  auto mma = [&](int i) __attribute__((always_inline)) {
+    // MFMA i of a stage: k-step i/16, row block (i/4)%4, column block i%4
+    const int ks = i >> 4, fm = (i >> 2) & 3, fn = i & 3;
+    if constexpr (IS_FP8)
+      acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[ks][fm], fb[ks][fn],
+                                                                    acc[fm][fn], 0, 0, 0, 0, 0, 0);
+    else
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][fm], fb[ks][fn], acc[fm][fn],
+                                                            0, 0, 0);
+  };
+  // column sums of the A tile of stage kt: thread t adds chunk t%32 of k-rows
+  // t/32 + 8j (j = 0..7)
   auto colsum_part = [&](int kt, int j) __attribute__((always_inline)) {
     if constexpr (COLSUM) {
       if (do_colsum) {
@@ -390,74 +407,82 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
 
   // Every stage index is issued, also those past the end of K: their offsets
   // fall outside the resources, so they cost no memory traffic and load
-  // zeros, and the number of loads in flight stays uniform -- every wait below
-  // is the same vmcnt and the loop body has no branches.
+  // zeros (which also makes the fused column sum of those stages zero), and
+  // the number of loads in flight stays uniform: one wait count, no branches.
   //
-  // The half-stages below pin their instruction order (a scheduling barrier
-  // after every slot): slot i issues MFMA i, then its share of the LDS reads
-  // for the next half-stage, then (in the second half) its share of the DMA
-  // loads, so neither the LDS nor the vector-memory queue ever holds up the
-  // MFMA issue for long.
-  //
-  // prologue: stages 0..3 in flight; stage 0's first fragments in registers
+  // Stage kt (kMma MFMAs issued from registers; a scheduling barrier after
+  // every slot pins the interleave):
+  //   first quarter   MFMAs of k-step 0; reads of the stage's second half of
+  //                   k-steps (and its column sums)
+  //   barrier A       every wave has finished reading stage kt: its buffer
+  //                   is free
+  //   middle half     MFMAs; the 16 loads of stage kt+2 into that buffer, one
+  //                   per two slots (one per slot for e4m3)
+  //   barrier B       stage kt+1 has landed (this wave's loads: vmcnt(16),
+  //                   every wave's: the barrier)
+  //   last quarter    MFMAs of the last k-step; reads of stage kt+1's first
+  //                   half of k-steps
+  constexpr int kMma = 16 * kKs;
+  constexpr int kQ = kMma / 4;           // slots per quarter
+  constexpr int kHalfKs = kKs / 2;       // k-steps read per quarter
+  constexpr int kReadsQ = 8 * kHalfKs;   // fragments read per quarter
+  constexpr int kDmaEvery = (kMma / 2) / 16;
+  auto stage_iter = [&](int kt) __attribute__((always_inline)) {
+    // transpose reads (asm, not tracked by the compiler) of the previous last
+    // quarter must have landed before their first use here
+    if constexpr (!A_K || !B_K) wait_lds();
 #pragma unroll
-  for (int s = 0; s < kStages; ++s) issue(s);
-  wait_and_barrier<24>();
+    for (int i = 0; i < kQ; ++i) {
+      mma(i);
+      // kReadsQ fragments over kQ slots
+      if (kReadsQ >= kQ) {
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    pa[f] = frag_a(0, 0, f);
-    pb[f] = frag_b(0, 0, f);
-  }
+        for (int r = 0; r < kReadsQ / kQ; ++r) {
+          const int j = i * (kReadsQ / kQ) + r;
+          read_one(kt, kHalfKs + j / 8, j & 7);
+        }
+      } else if (i % (kQ / kReadsQ) == 0) {
+        const int j = i / (kQ / kReadsQ);
+        read_one(kt, kHalfKs + j / 8, j & 7);
+      }
+      if (COLSUM && (i & 1)) colsum_part(kt, (i >> 1) & 7);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_and_barrier<63>();  // A: LDS reads done everywhere
+#pragma unroll
+    for (int i = kQ; i < 3 * kQ; ++i) {
+      mma(i);
+      if ((i - kQ) % kDmaEvery == kDmaEvery - 1) issue_one(kt + kStages, (i - kQ) / kDmaEvery);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_and_barrier<16>();  // B: stage kt+1 landed
+#pragma unroll
+    for (int i = 3 * kQ; i < kMma; ++i) {
+      mma(i);
+      const int q = i - 3 * kQ;
+      if (kReadsQ >= kQ) {
+#pragma unroll
+        for (int r = 0; r < kReadsQ / kQ; ++r) {
+          const int j = q * (kReadsQ / kQ) + r;
+          read_one(kt + 1, j / 8, j & 7);
+        }
+      } else if (q % (kQ / kReadsQ) == 0) {
+        const int j = q / (kQ / kReadsQ);
+        read_one(kt + 1, j / 8, j & 7);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
-  if constexpr (!IS_FP8) {
-    // stage kt: [MFMAs (kt, ks0) | reads (kt, ks1)]
-    //           barrier: stage kt+1 has landed; every wave holds stage kt
-    //           [MFMAs (kt, ks1) | reads (kt+1, ks0) | DMA stage kt+4 into kt's buffer]
-    for (int kt = 0; kt < nk; ++kt) {
-      if constexpr (!A_K || !B_K) wait_lds();  // transpose reads of (kt, ks0) done
+  // prologue: stages 0 and 1 in flight; stage 0's first half of k-steps in
+  // registers
+  issue(0);
+  issue(1);
+  wait_and_barrier<16>();
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        mma(i >> 2, i & 3, pa[i >> 2], pb[i & 3]);
-        if (i < 8) {
-          if (i & 1) qb[i >> 1] = frag_b(kt, 1, i >> 1);
-          else qa[i >> 1] = frag_a(kt, 1, i >> 1);
-        } else if (i < 12) {
-          colsum_part(kt, i - 8);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      wait_and_barrier<16>();
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        mma(i >> 2, i & 3, qa[i >> 2], qb[i & 3]);
-        if (i < 8) {
-          if (i & 1) pb[i >> 1] = frag_b(kt + 1, 0, i >> 1);
-          else pa[i >> 1] = frag_a(kt + 1, 0, i >> 1);
-        }
-        if (i & 1) issue_one(kt + kStages, i >> 1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  } else {
-    // e4m3: one MFMA k-step per stage. [MFMAs fm 0-1] barrier [MFMAs fm 2-3 |
-    // reads of stage kt+1 | DMA stage kt+4]; the copy at the end is register
-    // renaming.
-    for (int kt = 0; kt < nk; ++kt) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mma(i >> 2, i & 3, pa[i >> 2], pb[i & 3]);
-      wait_and_barrier<16>();
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        mma(2 + (i >> 2), i & 3, pa[2 + (i >> 2)], pb[i & 3]);
-        if (i & 1) qb[i >> 1] = frag_b(kt + 1, 0, i >> 1);
-        else qa[i >> 1] = frag_a(kt + 1, 0, i >> 1);
-        issue_one(kt + kStages, i);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int f = 0; f < 4; ++f) { pa[f] = qa[f]; pb[f] = qb[f]; }
-    }
-  }
+  for (int j = 0; j < kReadsQ; ++j) read_one(0, j / 8, j & 7);
+
+  for (int kt = 0; kt < nk; ++kt) stage_iter(kt);
 
   // ---- fused column sum of A (db1 = sum over tokens of dH)
   if constexpr (COLSUM) {
