@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 1
+#define TPMLP_ABI_VERSION 2
 
 typedef enum {
   TPMLP_OK = 0,
@@ -100,7 +100,12 @@ typedef struct tpmlp_fp8_scales {
   float* a_scale_inv;         /* out: 1 / (448 / a_amax) in float32, as used by fc2 */
 } tpmlp_fp8_scales;
 
-/* Bytes of workspace the call needs (0 if none). Returns 0 for an invalid desc. */
+/*
+ * Bytes of workspace the call needs (0 if none). Returns 0 for an invalid desc.
+ * Non-zero for: the E4M3 forward (the bfloat16 activation before
+ * quantisation and per-workgroup amax partials) and the BF16 weight gradient
+ * with bias (per-tile-column partial sums of db1, added up in a fixed order).
+ */
 size_t tpmlp_workspace_size(const tpmlp_desc* desc, int32_t call);
 
 /*
@@ -136,7 +141,9 @@ tpmlp_status tpmlp_bwd_dgrad(const tpmlp_desc* desc, const void* dy, const void*
  *   dW2 = dy^T . a_saved;  dW1 = dH^T . x;  db1 = column sums of dH (if has_bias).
  * accumulate = 0 overwrites the outputs; accumulate = 1 adds into them
  * (gradient accumulation across micro-batches). db1 may be NULL only when
- * has_bias = 0. F32 or BF16 only.
+ * has_bias = 0. F32 or BF16 only. Workspace: tpmlp_workspace_size(desc,
+ * TPMLP_CALL_WGRAD) bytes (BF16 with bias). Results are reproducible bit for
+ * bit: every sum is taken in a fixed order, no atomics.
  */
 tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* desc, const void* dy, const void* x,
                              const void* a_saved, const void* dH, float* dW1, float* db1,

@@ -205,8 +205,10 @@ def bwd_wgrad(desc, dy, x, a, dH, accumulate_into=None, stream=None):
         out = {"dW1": _empty((G * Fs, H), torch.float32, dev),
                "db1": _empty((G * Fs,), torch.float32, dev) if desc.has_bias else None,
                "dW2": _empty((H, Fs), torch.float32, dev)}
+    n = workspace_size(desc, CALL_WGRAD)
+    ws = _empty((n,), torch.uint8, dev) if n else None
     tpmlp_bwd_wgrad(desc, dy, x, a, dH, out["dW1"], out.get("db1"), out["dW2"],
-                    accumulate=accumulate_into is not None, stream=stream)
+                    accumulate=accumulate_into is not None, workspace=ws, stream=stream)
     return out
 
 

@@ -98,11 +98,25 @@ int fp8_fc1_parts(const tpmlp_desc* d) {
   return mfma_grid(FC1_FWD_GELU, g);
 }
 
+// bf16 fc1 wgrad with bias: tile columns of dW1 = dH^T . x (N = H), each of
+// which writes one row of db1 partial sums
+int colsum_parts(const tpmlp_desc* d) {
+  GemmArgs g{};
+  g.M = (int)(d->act == TPMLP_ACT_SWIGLU ? 2 * d->ffn_shard : d->ffn_shard);
+  g.N = (int)d->hidden;
+  mfma_grid(WGRAD_COLSUM, g);
+  return g.tiles_n;
+}
+
 size_t workspace_bytes(const tpmlp_desc* d, int32_t call) {
   if (call == TPMLP_CALL_FWD && d->dtype == TPMLP_E4M3) {
     const size_t a_bytes = align_up((size_t)d->tokens * (size_t)d->ffn_shard * 2, 256);
     const size_t parts = align_up((size_t)fp8_fc1_parts(d) * 4 + 4, 256);
     return a_bytes + parts;
+  }
+  if (call == TPMLP_CALL_WGRAD && d->dtype == TPMLP_BF16 && d->has_bias) {
+    const size_t gfs = (size_t)(d->act == TPMLP_ACT_SWIGLU ? 2 : 1) * (size_t)d->ffn_shard;
+    return align_up((size_t)colsum_parts(d) * gfs * 4, 256);
   }
   return 0;
 }
@@ -303,13 +317,23 @@ tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* d, const void* dy, const void* x,
   GemmArgs g1 = make_gemm(dy, H, a_saved, Fs, H, Fs, T, 0);
   hipError_t err = run_step(kind, WGRAD, label(kind, 4), g1, e1, s);
   if (err != hipSuccess) return hip_fail(err);
-  // dW1 [GFs, H] = dH^T . x (+ db1 = column sums of dH)
+  // dW1 [GFs, H] = dH^T . x (+ db1 = column sums of dH). The fp32 kernel
+  // writes db1 itself; the MFMA kernel writes per-tile-column partial sums
+  // into the workspace, which a second pass adds up into db1.
+  const bool split = d->has_bias && kind == KIND_BF16;
   EpiArgs e2{};
   e2.out = dW1; e2.ldo = H; e2.accumulate = accumulate;
-  e2.colsum = d->has_bias ? db1 : nullptr;
+  e2.colsum = d->has_bias ? (split ? static_cast<float*>(ws) : db1) : nullptr;
   GemmArgs g2 = make_gemm(dH, GFs, x, H, GFs, H, T, 0);
   err = run_step(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, label(kind, 5), g2, e2, s);
   if (err != hipSuccess) return hip_fail(err);
+  if (split) {
+    err = timed("db1_reduce.bf16", s, [&]() {
+      return colsum_reduce_launch(static_cast<const float*>(ws), colsum_parts(d), (int)GFs, db1,
+                                  accumulate, s);
+    });
+    if (err != hipSuccess) return hip_fail(err);
+  }
   return TPMLP_OK;
 }
 

@@ -110,30 +110,56 @@ template <> struct Elem<bf16_t> {
   __device__ __forceinline__ static float round(float v) { return round_bf16(v); }
 };
 
+// 8 consecutive elements as 16 (bf16) or 32 (fp32) bytes <-> 8 floats.
+__device__ __forceinline__ void unpack_bf16x8(const u32x4 w, float (&v)[8]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = __uint_as_float(w[q] << 16);
+    v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ u32x4 pack_bf16x8(const float (&v)[8]) {
+  u32x4 w;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) w[q] = (uint32_t)f2bf(v[2 * q]) | ((uint32_t)f2bf(v[2 * q + 1]) << 16);
+  return w;
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
 // ---------------------------------------------------------------- activations
 // GELU, tanh form: gelu(z) = z/2 (1 + tanh u), u = sqrt(2/pi)(z + 0.044715 z^3).
-// Since (1 + tanh u)/2 = sigmoid(2u), gelu(z) = z * sigmoid(2u), and
-// gelu'(z) = s + 2 z s (1 - s) u'(z) with s = sigmoid(2u),
-// u'(z) = sqrt(2/pi)(1 + 3 * 0.044715 z^2).
-// sigmoid(t) = 1 / (1 + 2^(-t log2 e)) from the hardware exp2 and reciprocal.
-constexpr float kSqrt2OverPi = 0.7978845608028654f;
-constexpr float kGeluCubic = 0.044715f;
-constexpr float kLog2e = 1.4426950408889634f;
+// Since (1 + tanh u)/2 = sigmoid(2u), gelu(z) = z * s with s = sigmoid(2u),
+// and gelu'(z) = s + 2 z s (1 - s) u'(z), u'(z) = sqrt(2/pi)(1 + 3 * 0.044715 z^2).
+// sigmoid(2u) = 1 / (1 + 2^(-2u log2 e)) from the hardware exp2 and
+// reciprocal, with -2u log2 e = z (k0 + k1 z^2) folded into two constants.
+constexpr double kSqrt2OverPi = 0.7978845608028654;
+constexpr double kGeluCubic = 0.044715;
+constexpr double kLog2eD = 1.4426950408889634;
+constexpr float kLog2e = (float)kLog2eD;
+constexpr float kGeluK0 = (float)(-2.0 * kSqrt2OverPi * kLog2eD);
+constexpr float kGeluK1 = (float)(-2.0 * kSqrt2OverPi * kLog2eD * kGeluCubic);
+// 2 u'(z) = m0 + m1 z^2
+constexpr float kGeluM0 = (float)(2.0 * kSqrt2OverPi);
+constexpr float kGeluM1 = (float)(6.0 * kSqrt2OverPi * kGeluCubic);
 
 __device__ __forceinline__ float sigmoid_f(float t) {
   float e = __builtin_amdgcn_exp2f(-t * kLog2e);  // +inf for very negative t
   return __builtin_amdgcn_rcpf(1.0f + e);          // rcp(+inf) = 0
 }
-__device__ __forceinline__ float gelu_f(float z) {
-  float u = kSqrt2OverPi * (z + kGeluCubic * z * z * z);
-  return z * sigmoid_f(2.0f * u);
+// sigmoid(2u(z)) for GELU
+__device__ __forceinline__ float gelu_sig_f(float z, float z2) {
+  const float e = __builtin_amdgcn_exp2f(z * __builtin_fmaf(kGeluK1, z2, kGeluK0));
+  return __builtin_amdgcn_rcpf(1.0f + e);
 }
+__device__ __forceinline__ float gelu_f(float z) { return z * gelu_sig_f(z, z * z); }
 __device__ __forceinline__ float gelu_grad_f(float z) {
-  float z2 = z * z;
-  float u = kSqrt2OverPi * (z + kGeluCubic * z2 * z);
-  float du = kSqrt2OverPi * (1.0f + 3.0f * kGeluCubic * z2);
-  float s = sigmoid_f(2.0f * u);
-  return s + 2.0f * z * s * (1.0f - s) * du;
+  const float z2 = z * z;
+  const float s = gelu_sig_f(z, z2);
+  const float q = __builtin_fmaf(kGeluM1, z2, kGeluM0);  // 2 u'(z)
+  // s + z s (1 - s) 2u', grouped so that s = 0 gives 0 for any finite z
+  return __builtin_fmaf(s * z, (1.0f - s) * q, s);
 }
 // SiLU: silu(g) = g sigmoid(g); silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))).
 __device__ __forceinline__ float silu_f(float g) { return g * sigmoid_f(g); }

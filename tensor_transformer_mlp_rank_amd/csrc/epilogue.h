@@ -1,6 +1,7 @@
-// Per-element epilogues of the MLP block's GEMMs, shared by the MFMA (bf16,
-// e4m3) and the VALU (fp32) tile kernels. Each takes one fp32 accumulator
-// value of C at (row, col) and writes the block's tensors:
+// Epilogues of the MLP block's GEMMs. The per-element forms below serve the
+// VALU (fp32) tile kernel; the MFMA kernel applies the same formulas to eight
+// consecutive columns at a time. Each takes the fp32 accumulator value of C
+// at (row, col) and writes the block's tensors:
 //
 //   EPI_STORE     out = alpha * acc                   (y_partial, dx_partial)
 //   EPI_F32       out = acc (+ out if accumulate)     (dW1, dW2, fp32)
@@ -44,7 +45,10 @@ struct EpiArgs {
   const float* scale_a;               // e4m3: dequantisation factors (device)
   const float* scale_b;
   float* amax_part;                   // e4m3 fc1: per-workgroup max |bf16(a)|
-  float* colsum;                      // fc1 wgrad: db1 (sum over k of A), or null
+  float* colsum;                      // fc1 wgrad: column sums of A over k, or null:
+                                      //   VALU kernel: db1 itself (written by tile
+                                      //   column 0); MFMA kernel: a [tiles_n][M]
+                                      //   array of per-tile-column partial sums
   int accumulate;                     // EPI_F32 and colsum: add into outputs
 };
 
@@ -87,78 +91,6 @@ __device__ __forceinline__ void epi_pair(const EpiArgs& e, int pair_off, int row
   }
   const float gr = Elem<OutT>::round(gt), ur = Elem<OutT>::round(up);
   Elem<OutT>::store(e.out, (int64_t)row * e.ldo + col, silu_f(gr) * ur);
-}
-
-// Vector form used by the MFMA kernel: 8 consecutive columns col..col+7 of
-// one row (col a multiple of 8; all 8 inside the output), one 16-byte access
-// per tensor and row segment.
-template <int EPI, typename OutT, bool IS_FP8>
-__device__ __forceinline__ void epi_group8(const EpiArgs& e, int pair_off, int row, int col,
-                                           float (&v)[8], float alpha, float& amax) {
-  const int64_t o = (int64_t)row * e.ldo + col;
-  if constexpr (EPI == EPI_STORE) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] *= alpha;
-    Elem<OutT>::store8(e.out, o, v);
-  } else if constexpr (EPI == EPI_F32) {
-    if (e.accumulate) {
-      float old[8];
-      Elem<float>::load8(e.out, o, old);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] += old[q];
-    }
-    Elem<float>::store8(e.out, o, v);
-  } else if constexpr (EPI == EPI_BIAS_GELU) {
-    float b[8];
-    if (e.bias) {
-      Elem<OutT>::load8(e.bias, col, b);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) b[q] = 0.f;
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = v[q] * alpha + b[q];
-    if (e.out2) Elem<OutT>::store8(e.out2, (int64_t)row * e.ldo2 + col, v);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      v[q] = gelu_f(Elem<OutT>::round(v[q]));
-      if constexpr (IS_FP8) amax = __builtin_fmaxf(amax, __builtin_fabsf(round_bf16(v[q])));
-    }
-    Elem<OutT>::store8(e.out, o, v);
-  } else if constexpr (EPI == EPI_DGELU) {
-    float h[8];
-    Elem<OutT>::load8(e.aux, (int64_t)row * e.ldaux + col, h);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] *= gelu_grad_f(h[q]);
-    Elem<OutT>::store8(e.out, o, v);
-  } else if constexpr (EPI == EPI_DSWIGLU) {
-    const int64_t ho = (int64_t)row * e.ldaux + col;
-    float gt[8], up[8], dg[8];
-    Elem<OutT>::load8(e.aux, ho, gt);
-    Elem<OutT>::load8(e.aux, ho + pair_off, up);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      dg[q] = v[q] * up[q] * silu_grad_f(gt[q]);
-      v[q] = v[q] * silu_f(gt[q]);
-    }
-    Elem<OutT>::store8(e.out, o, dg);
-    Elem<OutT>::store8(e.out, o + pair_off, v);
-  }
-}
-
-// Gated fc1, vector form: gate and up accumulators of pair columns col..col+7.
-template <typename OutT>
-__device__ __forceinline__ void epi_pair8(const EpiArgs& e, int pair_off, int row, int col,
-                                          float (&gt)[8], float (&up)[8], float alpha) {
-#pragma unroll
-  for (int q = 0; q < 8; ++q) { gt[q] *= alpha; up[q] *= alpha; }
-  if (e.out2) {
-    Elem<OutT>::store8(e.out2, (int64_t)row * e.ldo2 + col, gt);
-    Elem<OutT>::store8(e.out2, (int64_t)row * e.ldo2 + pair_off + col, up);
-  }
-#pragma unroll
-  for (int q = 0; q < 8; ++q) gt[q] = silu_f(Elem<OutT>::round(gt[q])) * Elem<OutT>::round(up[q]);
-  Elem<OutT>::store8(e.out, (int64_t)row * e.ldo + col, gt);
 }
 
 }  // namespace tpmlp

@@ -229,6 +229,193 @@ __device__ __forceinline__ void wait_and_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// --------------------------------------------------------------- epilogue
+// acc[fm][fn][j] is C at
+//   row 128 wm + 32 fm + 8 (j/4) + 4 (lane/32) + j%4 of the tile,
+//   col 128 wn + 32 fn + lane%32                  (pair tiles: see above).
+// Each wave stages one 32-row slab (fm) at a time through its own 17 KiB of
+// LDS as fp32 [32][132] (4 floats of padding: measured conflict-free for both
+// the scattered writes and the row-segment reads). Then every lane takes 8
+// consecutive columns (group cg) of the rows rl, rl + kRowStep, ... of the
+// slab, so each row segment is covered by consecutive lanes with 16-byte
+// accesses. Global accesses are buffer loads and stores on a resource per
+// slab: the range check drops the rows past the tensor's end, and column
+// groups past N get an offset outside the resource. No branches, so all
+// loads of a slab can be in flight together.
+//
+// LOADS: the epilogue reads global memory per element (h for the activation
+// derivative, the old dW when accumulating). Those loads are issued for two
+// slabs at a time, before the slabs are staged, and waited for once: one
+// counter tracks both loads and stores, so a wait for a load issued after a
+// store also waits for the store, and per-group load/use pairs would
+// serialise the epilogue on memory latency.
+template <bool IS_FP8, int EPI, typename OutT, bool LOADS>
+__device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e,
+                                           f32x16 (&acc)[4][4], char* smem, int wave, int lane,
+                                           int m0, int n0, float& amax) {
+  static_assert(std::is_same<OutT, bf16_t>::value, "MFMA activations and outputs are bf16");
+  constexpr bool kPair = (EPI == EPI_SWIGLU);
+  constexpr int kLd = 132;
+  constexpr int kT = kPair ? 4 : 8;         // row groups per lane and slab
+  constexpr int kRowStep = kPair ? 8 : 4;   // rows between them
+  constexpr int kPre = (EPI == EPI_F32 || EPI == EPI_DSWIGLU) ? 2 : 1;  // 16 B loads per group
+  constexpr int kOes = (EPI == EPI_F32) ? 4 : 2;  // primary output element bytes
+  constexpr uint32_t kBf = 2;
+  const int wm = wave >> 1, wn = wave & 1;
+  float* wl = reinterpret_cast<float*>(smem + wave * 32768);
+  const int cg = kPair ? (lane & 7) : (lane & 15);
+  const int rl = kPair ? (lane >> 3) : (lane >> 4);
+  const int wrow = m0 + 128 * wm;
+  const int wcol = kPair ? n0 + 64 * wn : n0 + 128 * wn;
+  // or-ed into every offset of a column group past N: puts it outside any
+  // resource (offsets inside a slab stay below 2^31)
+  const uint32_t oob = (wcol + 8 * cg < g.N) ? 0u : kOOB;
+  float alpha = 1.0f;
+  if constexpr (IS_FP8) alpha = (*e.scale_a) * (*e.scale_b);
+
+  // byte offset of group t in a slab resource with `ld` elements of `es` bytes per row
+  auto goff = [&](int64_t ld, uint32_t es, int t) __attribute__((always_inline)) -> uint32_t {
+    return ((uint32_t)(rl + kRowStep * t) * (uint32_t)(ld * es) + (uint32_t)(8 * cg) * es) | oob;
+  };
+  // rows [row0, M) of a row-major tensor, from column wcol of slab fm's first
+  // row; an empty range for a null tensor (its stores are dropped)
+  auto slab_rsrc = [&](const void* p, int64_t ld, int64_t es, int fm)
+      __attribute__((always_inline)) {
+    const int row0 = wrow + 32 * fm;
+    const int64_t bytes = p ? ((int64_t)(g.M - row0) * ld - wcol) * es : 0;
+    return make_rsrc(static_cast<const char*>(p) + ((int64_t)row0 * ld + wcol) * es, bytes);
+  };
+
+  u32x4 pre[2][kT][kPre];
+  auto load_slabs = [&](int fm0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if constexpr (EPI == EPI_F32) {
+        const auto rs = slab_rsrc(e.out, e.ldo, 4, fm0 + s);
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+          const uint32_t o = goff(e.ldo, 4, t);
+          pre[s][t][0] = buf_load16(rs, o);
+          pre[s][t][kPre - 1] = buf_load16(rs, o + 16);
+        }
+      } else {
+        const auto rs = slab_rsrc(e.aux, e.ldaux, 2, fm0 + s);
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+          const uint32_t o = goff(e.ldaux, kBf, t);
+          pre[s][t][0] = buf_load16(rs, o);
+          if constexpr (EPI == EPI_DSWIGLU)
+            pre[s][t][kPre - 1] = buf_load16(rs, o + (uint32_t)g.pair_off * kBf);
+        }
+      }
+    }
+  };
+
+  float bias[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) bias[q] = 0.f;
+  if constexpr (EPI == EPI_BIAS_GELU) {
+    if (e.bias) {
+      const auto rb = make_rsrc(e.bias, (int64_t)g.N * 2);
+      unpack_bf16x8(buf_load16(rb, ((uint32_t)(wcol + 8 * cg) * kBf) | oob), bias);
+    }
+  }
+
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm) {
+    if constexpr (LOADS) {
+      if ((fm & 1) == 0) load_slabs(fm);
+    }
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        wl[(8 * (j >> 2) + 4 * (lane >> 5) + (j & 3)) * kLd + 32 * fn + (lane & 31)] = acc[fm][fn][j];
+    if constexpr (LOADS) {
+      if ((fm & 1) == 0) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));  // vmcnt(0)
+      }
+    }
+    const int s = fm & 1;
+    const auto ro = slab_rsrc(e.out, e.ldo, kOes, fm);
+#pragma unroll
+    for (int t = 0; t < kT; ++t) {
+      const float* src = wl + (rl + kRowStep * t) * kLd + 8 * cg;
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = src[u] * alpha;
+      if constexpr (EPI == EPI_STORE) {
+        buf_store16(ro, goff(e.ldo, kOes, t), pack_bf16x8(v));
+      } else if constexpr (EPI == EPI_F32) {
+        if constexpr (LOADS) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            v[u] += __uint_as_float(pre[s][t][0][u]);
+            v[u + 4] += __uint_as_float(pre[s][t][1][u]);
+          }
+        }
+        const uint32_t o = goff(e.ldo, kOes, t);
+        buf_store16(ro, o, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                 __float_as_uint(v[2]), __float_as_uint(v[3])});
+        buf_store16(ro, o + 16, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]),
+                                      __float_as_uint(v[6]), __float_as_uint(v[7])});
+      } else if constexpr (EPI == EPI_BIAS_GELU) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] += bias[u];
+        const u32x4 hw = pack_bf16x8(v);
+        buf_store16(slab_rsrc(e.out2, e.ldo2, 2, fm), goff(e.ldo2, kBf, t), hw);  // h, if saved
+        unpack_bf16x8(hw, v);  // the activation is taken of h as stored
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = gelu_f(v[u]);
+        const u32x4 aw = pack_bf16x8(v);
+        if constexpr (IS_FP8) {
+          // rows past M hold gelu(b1), not activations: leave them out
+          if (oob == 0u && wrow + 32 * fm + rl + kRowStep * t < g.M) {
+            float ar[8];
+            unpack_bf16x8(aw, ar);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) amax = __builtin_fmaxf(amax, __builtin_fabsf(ar[u]));
+          }
+        }
+        buf_store16(ro, goff(e.ldo, kBf, t), aw);
+      } else if constexpr (EPI == EPI_SWIGLU) {
+        float up[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) up[u] = src[64 + u] * alpha;
+        const u32x4 gw = pack_bf16x8(v), uw = pack_bf16x8(up);
+        const auto r2 = slab_rsrc(e.out2, e.ldo2, 2, fm);  // h, if saved
+        const uint32_t o2 = goff(e.ldo2, kBf, t);
+        buf_store16(r2, o2, gw);
+        buf_store16(r2, o2 + (uint32_t)g.pair_off * kBf, uw);
+        unpack_bf16x8(gw, v);
+        unpack_bf16x8(uw, up);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = silu_f(v[u]) * up[u];
+        buf_store16(ro, goff(e.ldo, kBf, t), pack_bf16x8(v));
+      } else if constexpr (EPI == EPI_DGELU) {
+        float h[8];
+        unpack_bf16x8(pre[s][t][0], h);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] *= gelu_grad_f(h[u]);
+        buf_store16(ro, goff(e.ldo, kBf, t), pack_bf16x8(v));
+      } else if constexpr (EPI == EPI_DSWIGLU) {
+        float gt[8], up[8], dg[8];
+        unpack_bf16x8(pre[s][t][0], gt);
+        unpack_bf16x8(pre[s][t][1], up);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          dg[u] = v[u] * up[u] * silu_grad_f(gt[u]);
+          v[u] = v[u] * silu_f(gt[u]);
+        }
+        const uint32_t o = goff(e.ldo, kBf, t);
+        buf_store16(ro, o, pack_bf16x8(dg));
+        buf_store16(ro, o + (uint32_t)g.pair_off * kBf, pack_bf16x8(v));
+      }
+    }
+  }
+}
+
 // --------------------------------------------------------------- the kernel
 // IS_FP8: operands are e4m3 (both K-major). A_K / B_K: operand layouts.
 // EPI: epilogue kind. OutT: element type of EPI_STORE's output and of the
@@ -348,8 +535,12 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // fused column sum: thread t owns 8 columns (chunk t%32) of k-rows t/32 + 8j
-  const bool do_colsum = COLSUM && (bn == 0) && (e.colsum != nullptr);
+  // fused column sum: thread t owns 8 columns (chunk t%32) of k-rows t/32 + 8j.
+  // The k-stages are shared out over the tile columns: the workgroup in tile
+  // column bn sums stages bn, bn + tiles_n, ... and writes its partial sums to
+  // row bn of e.colsum ([tiles_n][M]); a second pass adds up the rows.
+  const bool do_colsum = COLSUM && (e.colsum != nullptr);
+  int cs_next = bn;  // the next stage this workgroup sums
   float csum[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) csum[j] = 0.f;
@@ -389,9 +580,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   };
   // column sums of the A tile of stage kt: thread t adds chunk t%32 of k-rows
   // t/32 + 8j (j = 0..7)
-  auto colsum_part = [&](int kt, int j) __attribute__((always_inline)) {
+  auto colsum_part = [&](int kt, int j, bool on) __attribute__((always_inline)) {
     if constexpr (COLSUM) {
-      if (do_colsum) {
+      if (on) {
         const char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
         const int c = tid & 31;
         const int kr = (tid >> 5) + 8 * j;
@@ -431,6 +622,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     // transpose reads (asm, not tracked by the compiler) of the previous last
     // quarter must have landed before their first use here
     if constexpr (!A_K || !B_K) wait_lds();
+    const bool cs_on = do_colsum && kt == cs_next;
+    if (cs_on) cs_next += g.tiles_n;
 #pragma unroll
     for (int i = 0; i < kQ; ++i) {
       mma(i);
@@ -445,7 +638,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
         const int j = i / (kQ / kReadsQ);
         read_one(kt, kHalfKs + j / 8, j & 7);
       }
-      if (COLSUM && (i & 1)) colsum_part(kt, (i >> 1) & 7);
+      if (COLSUM && (i & 1)) colsum_part(kt, (i >> 1) & 7, cs_on);
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_and_barrier<63>();  // A: LDS reads done everywhere
@@ -484,7 +677,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
 
   for (int kt = 0; kt < nk; ++kt) stage_iter(kt);
 
-  // ---- fused column sum of A (db1 = sum over tokens of dH)
+  // ---- fused column sum of A: this workgroup's share of the k-stages
   if constexpr (COLSUM) {
     if (do_colsum) {
       __syncthreads();  // all waves are done with the stage buffers
@@ -496,58 +689,20 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
       float s = 0.f;
 #pragma unroll
       for (int q = 0; q < 8; ++q) s += red[q * 256 + tid];
-      if (m < g.M) e.colsum[m] = e.accumulate ? e.colsum[m] + s : s;
+      if (m < g.M) e.colsum[(int64_t)bn * g.M + m] = s;
     }
   }
 
-  // ---- epilogue. acc[fm][fn][j] is C at
-  //   row 128 wm + 32 fm + 8 (j/4) + 4 (lane/32) + j%4 of the tile,
-  //   col 128 wn + 32 fn + lane%32                  (pair tiles: see above).
-  // Each wave stages one 32-row slab (fm) at a time through its own 17 KiB of
-  // LDS as fp32 [32][132] (4 floats of padding: measured conflict-free for
-  // both the scattered writes and the row-segment reads), then every lane
-  // takes 8 consecutive columns of a row: 16-byte loads and stores, each row
-  // segment written by consecutive lanes.
   __syncthreads();  // every wave is done reading the stage buffers
-  float alpha = 1.0f;
-  if constexpr (IS_FP8) alpha = (*e.scale_a) * (*e.scale_b);
   float amax = 0.f;
-  constexpr int kLd = 132;
-  float* wl = reinterpret_cast<float*>(smem + wave * 32768);
-#pragma unroll
-  for (int fm = 0; fm < 4; ++fm) {
-#pragma unroll
-    for (int fn = 0; fn < 4; ++fn)
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        wl[(8 * (j >> 2) + 4 * (lane >> 5) + (j & 3)) * kLd + 32 * fn + (lane & 31)] = acc[fm][fn][j];
-    const int row0 = m0 + 128 * wm + 32 * fm;
-    if constexpr (kPair) {
-      // slab columns [0, 64) gate and [64, 128) up of the wave's 64 features
-#pragma unroll 2
-      for (int t = 0; t < 4; ++t) {
-        const int q = lane + 64 * t;
-        const int r = q >> 3, cg = q & 7;
-        const int row = row0 + r, col = n0 + 64 * wn + 8 * cg;
-        float gt[8], up[8];
-        const float* src = wl + r * kLd + 8 * cg;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) { gt[u] = src[u]; up[u] = src[64 + u]; }
-        if (row < g.M && col < g.N) epi_pair8<OutT>(e, g.pair_off, row, col, gt, up, alpha);
-      }
-    } else {
-#pragma unroll 2
-      for (int t = 0; t < 8; ++t) {
-        const int q = lane + 64 * t;
-        const int r = q >> 4, cg = q & 15;
-        const int row = row0 + r, col = n0 + 128 * wn + 8 * cg;
-        float v[8];
-        const float* src = wl + r * kLd + 8 * cg;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = src[u];
-        if (row < g.M && col < g.N) epi_group8<EPI, OutT, IS_FP8>(e, g.pair_off, row, col, v, alpha, amax);
-      }
-    }
+  if constexpr (EPI == EPI_F32) {
+    if (e.accumulate)
+      store_tile<IS_FP8, EPI, OutT, true>(g, e, acc, smem, wave, lane, m0, n0, amax);
+    else
+      store_tile<IS_FP8, EPI, OutT, false>(g, e, acc, smem, wave, lane, m0, n0, amax);
+  } else {
+    constexpr bool kLoads = (EPI == EPI_DGELU || EPI == EPI_DSWIGLU);
+    store_tile<IS_FP8, EPI, OutT, kLoads>(g, e, acc, smem, wave, lane, m0, n0, amax);
   }
   if constexpr (IS_FP8 && EPI == EPI_BIAS_GELU) {
     amax = wave_max(amax);

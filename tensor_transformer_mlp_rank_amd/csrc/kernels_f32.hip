@@ -1,5 +1,6 @@
-// Instantiations and launchers of the fp32 (VALU) tile kernel and of the
-// E4M3 quantiser.
+// Instantiations and launchers of the fp32 (VALU) tile kernel, of the
+// E4M3 quantiser and of the reduction of the MFMA kernel's column-sum
+// partials.
 #include "gemm_f32.h"
 #include "launch.h"
 #include "quant.h"
@@ -16,7 +17,28 @@ hipError_t launch_f32(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
   return hipGetLastError();
 }
 
+// out[m] = (out[m] if accumulate) + sum over r of part[r][m], rows added in
+// order r = 0, 1, ... (fixed order: reproducible bit for bit).
+__global__ void __launch_bounds__(256) colsum_reduce_kernel(const float* __restrict__ part,
+                                                            int nparts, int M,
+                                                            float* __restrict__ out,
+                                                            int accumulate) {
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m >= M) return;
+  float s = 0.f;
+  for (int r = 0; r < nparts; ++r) s += part[(int64_t)r * M + m];
+  out[m] = accumulate ? out[m] + s : s;
+}
+
 }  // namespace
+
+hipError_t colsum_reduce_launch(const float* part, int nparts, int M, float* out, int accumulate,
+                                hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((M + 255) / 256), dim3(256), 0, s, part, nparts,
+                     M, out, accumulate);
+  return hipGetLastError();
+}
 
 int f32_grid(Step step, GemmArgs& g) {
   const bool pair = (step == FC1_FWD_SWIGLU);

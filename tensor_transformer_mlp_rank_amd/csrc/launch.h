@@ -33,6 +33,10 @@ hipError_t mfma_launch(bool fp8, Step step, const GemmArgs& g, const EpiArgs& e,
                        hipStream_t stream);
 hipError_t f32_launch(Step step, const GemmArgs& g, const EpiArgs& e, hipStream_t stream);
 
+// db1 from the MFMA kernel's [nparts][M] column-sum partials.
+hipError_t colsum_reduce_launch(const float* part, int nparts, int M, float* out, int accumulate,
+                                hipStream_t stream);
+
 // Quantiser passes. src_bf16 selects the source type (bf16 or f32).
 int quant_parts(int64_t n);
 hipError_t amax_partial_launch(bool src_bf16, const void* src, int64_t n, float* partial,

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert tp.lib.tpmlp_abi_version() == 1
+    assert tp.lib.tpmlp_abi_version() == 2
     for s in range(8):
         assert len(tp.lib.tpmlp_strerror(s)) > 5
     assert tp.lib.tpmlp_last_hip_error() == b""
@@ -108,7 +108,12 @@ def test_fp8_rules():
 def test_workspace_sizes():
     assert tp.workspace_size(D(), tp.CALL_FWD) == 0
     assert tp.workspace_size(D(), tp.CALL_DGRAD) == 0
-    assert tp.workspace_size(D(), tp.CALL_WGRAD) == 0
+    # bf16 wgrad with bias: one fp32 row of db1 partials per 256-column tile of H
+    assert tp.workspace_size(D(), tp.CALL_WGRAD) == 1 * 128 * 4
+    assert tp.workspace_size(D(hidden=4096, ffn_shard=1000 - 1000 % 16), tp.CALL_WGRAD) == \
+        (16 * 992 * 4 + 255) // 256 * 256
+    assert tp.workspace_size(D(has_bias=False), tp.CALL_WGRAD) == 0
+    assert tp.workspace_size(D(dtype="f32"), tp.CALL_WGRAD) == 0
     assert tp.workspace_size(D(hidden=3), tp.CALL_FWD) == 0      # invalid desc
     assert tp.workspace_size(D(dtype="e4m3"), 7) == 0            # invalid call
 
@@ -128,6 +133,14 @@ def test_wgrad_pointers(name):
 def test_wgrad_bias_and_flag():
     assert wgrad(D(has_bias=True), db1=None) == E_NULL
     assert wgrad(D(), acc=2) == E_DTYPE
+
+
+def test_wgrad_workspace():
+    need = tp.workspace_size(D(), tp.CALL_WGRAD)
+    args = (ctypes.byref(D()), P, P, P, P, P, P, P, 0)
+    assert tp.lib.tpmlp_bwd_wgrad(*args, None, 0, None) == E_WS
+    assert tp.lib.tpmlp_bwd_wgrad(*args, P, need - 1, None) == E_WS
+    assert tp.lib.tpmlp_bwd_wgrad(*args, MIS, need, None) == E_ALIGN
 
 
 def test_quantize_validation():

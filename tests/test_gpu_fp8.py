@@ -125,3 +125,28 @@ def test_fp8_forward_full_size_sampled(tp):
     e_h = rel_err(gpu["h"][rows], ref["h"])
     say(f"  rel errors y={e_y:.2e} h={e_h:.2e}")
     assert e_y <= TOL["e4m3"] and e_h <= TOL["bf16"]
+
+
+def test_fp8_amax_leaves_out_padding_rows(tp):
+    """T = 300 is not a multiple of the 256-row tile: the rows past T in the
+    last tile hold h = b1, not activations. Here every real h is -3 (tiny
+    |gelu|) while gelu(b1) = 29, so amax must stay near |gelu(-3)|."""
+    T, H, Fs = 300, 32, 16
+    x = torch.ones((T, H), dtype=torch.bfloat16)
+    W1 = -torch.ones((Fs, H), dtype=torch.bfloat16)
+    W2 = torch.ones((H, Fs), dtype=torch.bfloat16)
+    b1 = torch.full((Fs,), 29.0, dtype=torch.bfloat16)
+    q = {}
+    for k, v in (("x", x), ("W1", W1), ("W2", W2)):
+        codes, _, sinv = tp.quantize_e4m3(v.cuda())
+        q[k] = (codes, sinv)
+    desc = tp.make_desc(T, H, Fs, act="gelu", dtype="e4m3", has_bias=True)
+    out = tp.fwd(desc, q["x"][0], q["W1"][0], b1.cuda(), q["W2"][0],
+                 fp8_in_scales=(q["x"][1], q["W1"][1], q["W2"][1]))
+    torch.cuda.synchronize()
+    ref = oracle.rank_forward(oracle.to_f64(x), oracle.to_f64(W1), oracle.to_f64(b1),
+                              oracle.to_f64(W2), "gelu")
+    amax_ref = float(np.max(np.abs(ref["a"])))
+    amax = float(out["a_amax"].cpu()[0])
+    say(f"  amax gpu {amax:.6g} oracle {amax_ref:.6g}")
+    assert abs(amax - amax_ref) <= TOL["bf16"] * amax_ref

@@ -110,10 +110,13 @@ def test_zero_tokens(tp):
     dW1 = torch.full((Fs, H), 7.0, device="cuda")
     db1 = torch.full((Fs,), 7.0, device="cuda")
     dW2 = torch.full((H, Fs), 7.0, device="cuda")
-    tp.tpmlp_bwd_wgrad(desc, anyp, anyp, anyp, anyp, dW1, db1, dW2, accumulate=True)
+    ws = torch.empty(tp.workspace_size(desc, tp.CALL_WGRAD), dtype=torch.uint8, device="cuda")
+    tp.tpmlp_bwd_wgrad(desc, anyp, anyp, anyp, anyp, dW1, db1, dW2, accumulate=True,
+                       workspace=ws)
     torch.cuda.synchronize()
     assert torch.all(dW1 == 7) and torch.all(db1 == 7) and torch.all(dW2 == 7)
-    tp.tpmlp_bwd_wgrad(desc, anyp, anyp, anyp, anyp, dW1, db1, dW2, accumulate=False)
+    tp.tpmlp_bwd_wgrad(desc, anyp, anyp, anyp, anyp, dW1, db1, dW2, accumulate=False,
+                       workspace=ws)
     torch.cuda.synchronize()
     assert torch.all(dW1 == 0) and torch.all(db1 == 0) and torch.all(dW2 == 0)
     del e
