@@ -28,14 +28,21 @@ if ROOT not in sys.path:
 PEAK = {"bf16": 2516.6, "f32": 157.3, "e4m3": 5033.2}
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 1 << 30  # the calibration copy
 KERNEL_SOURCES = ["gemm_mfma.h", "epilogue.h", "common.h", "kernels_mfma.hip"]
 
 
 def kernel_source_sha() -> str:
+    """Hash of the GEMM kernel's code (comments and whitespace left out, so
+    that only a change of the code itself marks the counters stale)."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "tensor_transformer_mlp_rank_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "tensor_transformer_mlp_rank_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -51,6 +58,69 @@ def measured_traffic(kernel: str):
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
+
+
+def step_labels(w) -> list:
+    """The library's launches in one step (forward, dgrad, wgrad), in order,
+    under the names its timing facility gives them."""
+    sfx = "." + w.dtype
+    seq = ["fc1_fwd", "fc2_fwd", "fc2_dgrad", "fc1_dgrad", "fc2_wgrad", "fc1_wgrad"]
+    if w.has_bias and w.dtype == "bf16":
+        seq.append("db1_reduce")  # adds up the fused column-sum partials
+    return [k + sfx for k in seq]
+
+
+def _counter_rows(d: str) -> list:
+    import csv
+    with open(os.path.join(d, "run_counter_collection.csv")) as fh:
+        return sorted(csv.DictReader(fh), key=lambda r: int(r["Dispatch_Id"]))
+
+
+def write_traffic(w, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands) -> dict:
+    """HBM bytes per launch of each kernel of the step, from rocprofv3 --pmc
+    FETCH_SIZE and WRITE_SIZE runs of this script (KiB per dispatch), each
+    scaled by what the same counter reads for the plain 1 GiB device copy of
+    --copy-calibration. Dispatches of the library are matched to step labels
+    by launch order."""
+    import statistics
+    copy_bytes = float(COPY_BYTES)
+
+    def copy_kib(d):
+        v = [float(r["Counter_Value"]) for r in _counter_rows(d) if "copyBuffer" in r["Kernel_Name"]]
+        if not v:
+            raise SystemExit(f"no copy kernel dispatch in {d}")
+        return statistics.median(v)
+
+    scale = {"FETCH_SIZE": copy_bytes / (copy_kib(copy_fetch_dir) * 1024.0),
+             "WRITE_SIZE": copy_bytes / (copy_kib(copy_write_dir) * 1024.0)}
+    seq = step_labels(w)
+    per = {}
+    for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        rows = [r for r in _counter_rows(d)
+                if "tpmlp::" in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        if not rows or len(rows) % len(seq):
+            raise SystemExit(f"{d}: {len(rows)} library dispatches, not whole steps of {len(seq)}")
+        for i, r in enumerate(rows):
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+            k = per.setdefault(seq[i % len(seq)], {"kernel": name})
+            if k["kernel"] != name:
+                raise SystemExit(f"dispatch order does not match the step: {r['Kernel_Name']}")
+            k.setdefault(counter, []).append(float(r["Counter_Value"]) * 1024.0 * scale[counter])
+    kernels = {}
+    for label, k in per.items():
+        fetch = statistics.mean(k["FETCH_SIZE"])
+        write = statistics.mean(k["WRITE_SIZE"])
+        kernels[label] = {"kernel": k["kernel"], "dispatches": len(k["FETCH_SIZE"]),
+                          "fetch_bytes": round(fetch), "write_bytes": round(write),
+                          "bytes_per_launch": round(fetch + write)}
+    out = {"source_sha": kernel_source_sha(), "workload": w.name,
+           "scale": {"FETCH_SIZE": round(scale["FETCH_SIZE"], 4),
+                     "WRITE_SIZE": round(scale["WRITE_SIZE"], 4)},
+           "commands": commands, "kernels": kernels}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    return out
 
 
 def cpu_baseline(w, tokens: int, repeats: int = 3) -> dict:
@@ -99,10 +169,21 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
                          "kernel for scaling HBM byte counters)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="no GPU: write profiles/traffic.json from four rocprofv3 --pmc output "
+                         "folders (FETCH_SIZE and WRITE_SIZE of this benchmark, then of "
+                         "--copy-calibration)")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --write-traffic: the commands that made the folders (recorded)")
     args = ap.parse_args()
+    if args.write_traffic:
+        import synth
+        out = write_traffic(synth.WORKLOADS[args.workload], *args.write_traffic, args.command)
+        print(json.dumps(out["kernels"], indent=1))
+        return
     if args.copy_calibration:
         import torch
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(5):
             dst.copy_(src)
@@ -163,6 +244,8 @@ def main():
     torch.cuda.synchronize()
     per = tp.timing_collect()
     tp.timing_enable(False)
+    if list(per) != step_labels(w):
+        raise SystemExit(f"unexpected launch sequence {list(per)}")
     dominant = max(per, key=lambda k: per[k][1])
     breakdown = {k: round(v[1] / v[0], 4) for k, v in per.items()}
     if args.breakdown:
@@ -207,6 +290,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
                      "peak": PEAK[w.dtype], "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK[w.dtype], 4), "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-calibrated)",
                      "launches": dom[0], "avg_ms": round(dom_ms, 4)},
         "kernel_ms": breakdown,
     }

@@ -22,26 +22,28 @@
 // e4m3): 256 fp32 accumulator registers per lane (AGPRs). Per FLOP this reads
 // half the LDS bytes of a 128 x 64 wave tile.
 //
-// Pipeline: K advances 64 bytes per row per stage (32 bf16 / 64 e4m3
-// elements); a stage holds a 16 KiB A tile and a 16 KiB B tile; four stages
-// (128 KiB of the 160 KiB LDS) rotate. Tiles go from HBM straight into LDS
-// with buffer_load_dwordx4 ... lds (no staging registers, no LDS store
-// instructions); the buffer resource's range check turns reads past a
-// tensor's end into zeros. Loads for stage k+3 are issued right after the
-// barrier that opens stage k, so each load has three compute stages to land.
-// The barrier is a plain s_barrier preceded by an explicit wait on this
-// wave's own loads of stage k (vmcnt) and its LDS reads of stage k-1: a full
-// __syncthreads would drain all loads in flight and serialise the pipeline.
+// Pipeline: K advances 128 bytes per row per stage (64 bf16 / 128 e4m3
+// elements, whole cache lines per request); a stage holds a 32 KiB A tile and
+// a 32 KiB B tile; two stages (128 KiB of the 160 KiB LDS) alternate. Tiles go
+// from HBM straight into LDS with buffer_load_dwordx4 ... lds (no staging
+// registers, no LDS store instructions); the buffer resource's range check
+// turns reads past a tensor's end into zeros. Within a stage (see
+// stage_iter) the MFMAs run from registers while the LDS reads for the next
+// k-steps and the loads of stage k+2 are interleaved between them; two
+// barriers per stage hand the buffers over. Each barrier is a plain s_barrier
+// preceded by an explicit wait (vmcnt for this wave's loads, lgkmcnt for its
+// LDS reads): a full __syncthreads would drain all loads in flight and
+// serialise the pipeline.
 //
 // LDS layouts (direct-to-LDS loads write 64 lanes x 16 B = 1 KiB linearly per
 // instruction, so swizzles are applied by choosing which global chunk each
 // lane fetches):
-//   * K-major tile: [256 rows][64 B]; 16-byte chunk c of row r lives at chunk
-//     c ^ (((r >> 1) ^ (r >> 2)) & 3). Any 16 consecutive rows then put a given
-//     chunk in 16 distinct 16-byte slots of a 256-byte bank window, so the
-//     fragment reads (ds_read_b128, 8 consecutive k of one row per lane) are
+//   * K-major tile: [256 rows][128 B]; 16-byte chunk c of row r lives at
+//     chunk c ^ ((r >> 1) & 7). Any 16 consecutive rows then put a given chunk
+//     in 16 distinct 16-byte slots of a 256-byte bank window, so the fragment
+//     reads (ds_read_b128, 8 consecutive k of one row per lane) are
 //     conflict-free.
-//   * MN-major tile: [32 k-rows][256 elements = 512 B]; chunk c of k-row r
+//   * MN-major tile: [64 k-rows][256 elements = 512 B]; chunk c of k-row r
 //     lives at chunk c ^ {0, 4, 10, 14}[r % 4], which spreads the 32 lanes of
 //     a transpose read over 32 distinct 8-byte slots of a 256-byte bank window.
 //     Fragments are read with the CDNA4 transpose

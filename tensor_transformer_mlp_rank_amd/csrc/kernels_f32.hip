@@ -17,17 +17,35 @@ hipError_t launch_f32(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
   return hipGetLastError();
 }
 
-// out[m] = (out[m] if accumulate) + sum over r of part[r][m], rows added in
-// order r = 0, 1, ... (fixed order: reproducible bit for bit).
+// out[m] = (out[m] if accumulate) + sum over r of part[r][m]. A workgroup
+// takes 64 columns; its four waves each add every fourth row (r = w, w + 4,
+// ...), loads issued eight at a time, and wave 0 adds the four sums in wave
+// order: a fixed order, so the result is reproducible bit for bit.
 __global__ void __launch_bounds__(256) colsum_reduce_kernel(const float* __restrict__ part,
                                                             int nparts, int M,
                                                             float* __restrict__ out,
                                                             int accumulate) {
-  const int m = blockIdx.x * 256 + threadIdx.x;
-  if (m >= M) return;
+  __shared__ float red[4][64];
+  const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int m = blockIdx.x * 64 + c;
   float s = 0.f;
-  for (int r = 0; r < nparts; ++r) s += part[(int64_t)r * M + m];
-  out[m] = accumulate ? out[m] + s : s;
+  if (m < M) {
+    int r = w;
+    for (; r + 28 < nparts; r += 32) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = part[(int64_t)(r + 4 * i) * M + m];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[i];
+    }
+    for (; r < nparts; r += 4) s += part[(int64_t)r * M + m];
+  }
+  red[w][c] = s;
+  __syncthreads();
+  if (w == 0 && m < M) {
+    const float t = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+    out[m] = accumulate ? out[m] + t : t;
+  }
 }
 
 }  // namespace
@@ -35,8 +53,8 @@ __global__ void __launch_bounds__(256) colsum_reduce_kernel(const float* __restr
 hipError_t colsum_reduce_launch(const float* part, int nparts, int M, float* out, int accumulate,
                                 hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((M + 255) / 256), dim3(256), 0, s, part, nparts,
-                     M, out, accumulate);
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((M + 63) / 64), dim3(256), 0, s, part, nparts, M,
+                     out, accumulate);
   return hipGetLastError();
 }
 
