@@ -118,10 +118,16 @@ __device__ __forceinline__ void unpack_bf16x8(const u32x4 w, float (&v)[8]) {
     v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
   }
 }
+// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
 __device__ __forceinline__ u32x4 pack_bf16x8(const float (&v)[8]) {
   u32x4 w;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) w[q] = (uint32_t)f2bf(v[2 * q]) | ((uint32_t)f2bf(v[2 * q + 1]) << 16);
+  for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
   return w;
 }
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {

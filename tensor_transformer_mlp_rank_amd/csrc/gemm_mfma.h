@@ -603,18 +603,19 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // zeros (which also makes the fused column sum of those stages zero), and
   // the number of loads in flight stays uniform: one wait count, no branches.
   //
-  // Stage kt (kMma MFMAs issued from registers; a scheduling barrier after
-  // every slot pins the interleave):
+  // Stage kt with two K-major operands (kMma MFMAs issued from registers; a
+  // scheduling barrier after every slot pins the interleave):
   //   first quarter   MFMAs of k-step 0; reads of the stage's second half of
   //                   k-steps (and its column sums)
-  //   barrier A       every wave has finished reading stage kt: its buffer
-  //                   is free
-  //   middle half     MFMAs; the 16 loads of stage kt+2 into that buffer, one
-  //                   per two slots (one per slot for e4m3)
-  //   barrier B       stage kt+1 has landed (this wave's loads: vmcnt(16),
-  //                   every wave's: the barrier)
+  //   barrier         every wave has finished reading stage kt, so its
+  //                   buffer is free, and stage kt+1 has landed (this wave's
+  //                   loads: vmcnt(0); every wave's: the barrier)
+  //   middle half     MFMAs; the 16 loads of stage kt+2 into stage kt's
+  //                   buffer, one per two slots (one per slot for e4m3)
   //   last quarter    MFMAs of the last k-step; reads of stage kt+1's first
   //                   half of k-steps
+  // One barrier per stage: the loads of stage kt+1 have the last quarter of
+  // stage kt-1 and the first quarter of stage kt to land.
   constexpr int kMma = 16 * kKs;
   constexpr int kQ = kMma / 4;           // slots per quarter
   constexpr int kHalfKs = kKs / 2;       // k-steps read per quarter
@@ -643,14 +644,16 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
       if (COLSUM && (i & 1)) colsum_part(kt, (i >> 1) & 7, cs_on);
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_and_barrier<63>();  // A: LDS reads done everywhere
+    // the stage's one barrier: every wave is done reading stage kt (its
+    // buffer is free) and has stage kt+1 in LDS (its loads, issued in the
+    // middle half of stage kt-1, are the only ones in flight: vmcnt(0))
+    wait_and_barrier<0>();
 #pragma unroll
     for (int i = kQ; i < 3 * kQ; ++i) {
       mma(i);
       if ((i - kQ) % kDmaEvery == kDmaEvery - 1) issue_one(kt + kStages, (i - kQ) / kDmaEvery);
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_and_barrier<16>();  // B: stage kt+1 landed
 #pragma unroll
     for (int i = 3 * kQ; i < kMma; ++i) {
       mma(i);
@@ -669,15 +672,55 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     }
   };
 
-  // prologue: stages 0 and 1 in flight; stage 0's first half of k-steps in
-  // registers
+  // bf16 stage kt with an MN-major operand (64 slots in four groups of 16,
+  // group q issuing the MFMAs of k-step q): the 8 fragments of a k-step are read right after the
+  // previous stage's MFMAs of that k-step have released their registers, one
+  // every two slots, so the LDS reads are spread evenly over the stage
+  // instead of coming in two bursts:
+  //   group 0   reads of stage kt's k-step 3 (and its column sums)
+  //   barrier   every wave has finished reading stage kt, and stage kt+1
+  //             has landed (vmcnt(0))
+  //   group 1   reads of stage kt+1's k-step 0; loads 0..7 of stage kt+2
+  //   group 2   reads of stage kt+1's k-step 1; loads 8..15 of stage kt+2
+  //   group 3   reads of stage kt+1's k-step 2
+  auto stage_iter_rolling = [&](int kt) __attribute__((always_inline)) {
+    // transpose reads (asm, not tracked by the compiler) of the previous
+    // stage must have landed before their first use here
+    if constexpr (!A_K || !B_K) wait_lds();
+    const bool cs_on = do_colsum && kt == cs_next;
+    if (cs_on) cs_next += g.tiles_n;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      mma(i);
+      const int grp = i >> 4, r = i & 15;
+      if ((r & 1) == 0) {
+        if (grp == 0) read_one(kt, 3, r >> 1);
+        else read_one(kt + 1, grp - 1, r >> 1);
+      }
+      if (COLSUM && grp == 0 && (i & 1)) colsum_part(kt, (i >> 1) & 7, cs_on);
+      if ((grp == 1 || grp == 2) && (r & 1)) issue_one(kt + kStages, (i - 16) >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i == 15) wait_and_barrier<0>();
+    }
+  };
+
+  // prologue: stages 0 and 1 in flight; stage 0's first k-steps in registers
   issue(0);
   issue(1);
   wait_and_barrier<16>();
+  // The rolling schedule pays off where a transpose-read operand makes the
+  // reads costly (twice the read instructions); with two K-major operands
+  // the quarter schedule measured slightly faster.
+  constexpr bool kRolling = !IS_FP8 && (!A_K || !B_K);
+  if constexpr (!kRolling) {
 #pragma unroll
-  for (int j = 0; j < kReadsQ; ++j) read_one(0, j / 8, j & 7);
-
-  for (int kt = 0; kt < nk; ++kt) stage_iter(kt);
+    for (int j = 0; j < kReadsQ; ++j) read_one(0, j / 8, j & 7);
+    for (int kt = 0; kt < nk; ++kt) stage_iter(kt);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 24; ++j) read_one(0, j / 8, j & 7);
+    for (int kt = 0; kt < nk; ++kt) stage_iter_rolling(kt);
+  }
 
   // ---- fused column sum of A: this workgroup's share of the k-stages
   if constexpr (COLSUM) {

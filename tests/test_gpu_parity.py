@@ -77,6 +77,27 @@ def test_block_small_and_ragged(tp, T, H, Fs, act, dtype):
     check(gpu, ref, dtype, ALL)
 
 
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_block_more_tiles_than_workgroups(tp, act):
+    """bf16 block whose GEMMs have 289 (SwiGLU fc1: 561) 256-wide tiles, more
+    than the persistent kernel's workgroups (one per CU): workgroups run
+    several tiles in a row, and every GEMM has ragged edges in M, N and K.
+    Compared element by element, with accumulation into prior gradients."""
+    T, H, Fs = 4200, 4208, 4112
+    w = synth.WORKLOADS[4 if act == "swiglu" else 2]
+    say(f"  T={T} H={H} Fs={Fs} {act}: generating inputs")
+    inp = synth.make_rank_inputs(w, tokens=T, hidden=H, ffn_shard=Fs, seed_base=313)
+    has_bias = act == "gelu"
+    G = 2 if act == "swiglu" else 1
+    prior = {"dW1": synth.grad_init(313, (G * Fs, H), 1),
+             "db1": synth.grad_init(313, (G * Fs,), 2) if has_bias else None,
+             "dW2": synth.grad_init(313, (H, Fs), 3)}
+    gpu = gpu_block(tp, inp, act, "bf16", has_bias, accumulate_into=prior)
+    say("  oracle")
+    ref = oracle_block(inp, act, has_bias, prior=prior)
+    check(gpu, ref, "bf16", ALL)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("act", ["gelu", "swiglu"])
 def test_wgrad_accumulate(tp, dtype, act):
