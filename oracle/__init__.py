@@ -17,8 +17,9 @@ written as the definitions stated by the pages:
   (all-reduce forward, identity backward) that fix which tensors are
   replicated and which are partial -- "Megatron-LM / Megatron-Core" concept
   note, section "Key math / How it works";
-* FP8 (per-tensor current scaling into OCP E4M3) for the forward pass --
-  code tour, "Honest Limits"; concept note, "Key math / How it works".
+* FP8 (OCP E4M3 for the forward tensors, OCP E5M2 for the gradients;
+  per-tensor current or delayed scaling) -- code tour, "Honest Limits";
+  concept note, "Key math / How it works".
 
 Where the pages are silent (activation formulas, gated layout, scaling
 recipe) the readings are the textbook ones and are recorded in the design doc.
@@ -30,13 +31,18 @@ differences, the shard-sum invariant, brute force, the OCP E4M3 table).
 from .activations import gelu_tanh, gelu_tanh_grad, silu, silu_grad, sigmoid
 from .block import (shard_rank, select_features, rank_forward, rank_dgrad, rank_wgrad,
                     unsharded_forward, unsharded_backward, block_loss, to_f64)
-from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, current_scale, quantize_e4m3,
-                  dequantize_e4m3)
+from .fp8 import (E4M3_MAX, E5M2_MAX, FMAX, e4m3_decode, e4m3_encode, e5m2_decode, e5m2_encode,
+                  current_scale, quantize_e4m3, dequantize_e4m3, quantize, dequantize,
+                  delayed_update)
+from .fp8_block import rank_forward_fp8, rank_dgrad_fp8, rank_wgrad_fp8
 
 __all__ = [
     "gelu_tanh", "gelu_tanh_grad", "silu", "silu_grad", "sigmoid",
     "shard_rank", "select_features", "rank_forward", "rank_dgrad", "rank_wgrad",
     "unsharded_forward", "unsharded_backward", "block_loss", "to_f64",
-    "E4M3_MAX", "e4m3_decode", "e4m3_encode", "current_scale", "quantize_e4m3",
+    "E4M3_MAX", "E5M2_MAX", "FMAX", "e4m3_decode", "e4m3_encode", "e5m2_decode", "e5m2_encode",
+    "quantize", "dequantize", "delayed_update",
+    "rank_forward_fp8", "rank_dgrad_fp8", "rank_wgrad_fp8",
+    "current_scale", "quantize_e4m3",
     "dequantize_e4m3",
 ]

@@ -1,0 +1,66 @@
+"""The per-rank GELU block with FP8 operands, forward and backward, float64.
+
+Test infrastructure (see the package header). The inputs are the
+dequantised FP8 tensors the device consumes: x, W1, W2 from E4M3 codes and
+dy from E5M2 codes, each decode(code) * scale_inv. The block is then the
+plain one (column-parallel fc1, bias + GELU, row-parallel fc2, its data and
+weight gradients -- Megatron-LM code tour, "The Tensor-Parallel Primitives"
+and "The Transformer Stack"), with the two tensors that the block itself
+produces and feeds to a later product quantised on the way, at the scale
+the call is given (delayed scaling, see oracle.fp8):
+
+* the activation a, to E4M3, before fc2 and the fc2 weight gradient;
+* the gradient dH = dA * gelu'(h), to E5M2, before the fc1 data and weight
+  gradients and the bias gradient.
+
+Everything else is float64 on those values.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .activations import gelu_tanh, gelu_tanh_grad
+from .fp8 import dequantize, quantize
+
+
+def _inv(scale) -> np.float32:
+    return np.float32(np.float32(1.0) / np.float32(scale))
+
+
+def rank_forward_fp8(x, W1, b1, W2, a_scale) -> dict:
+    """h = x W1^T + b1; a = gelu(h); a quantised to E4M3 at a_scale (codes,
+    and a_q = decode(code) / a_scale); y = a_q W2^T. amax = max |a|."""
+    h = x @ W1.T + (0.0 if b1 is None else b1)
+    a = gelu_tanh(h)
+    codes = quantize(a, "e4m3", a_scale)
+    a_q = dequantize(codes, "e4m3", _inv(a_scale))
+    y = a_q @ W2.T
+    amax = float(np.max(np.abs(a))) if a.size else 0.0
+    return {"h": h, "a": a, "a_codes": codes, "a_q": a_q, "y": y, "amax": amax}
+
+
+def rank_dgrad_fp8(dy, W1, W2, h, dH_scale) -> dict:
+    """dA = dy W2; dH = dA * gelu'(h); dH quantised to E5M2 at dH_scale
+    (codes, and dH_q); dx = dH_q W1. amax = max |dH|."""
+    dA = dy @ W2
+    dH = dA * gelu_tanh_grad(h)
+    codes = quantize(dH, "e5m2", dH_scale)
+    dH_q = dequantize(codes, "e5m2", _inv(dH_scale))
+    dx = dH_q @ W1
+    amax = float(np.max(np.abs(dH))) if dH.size else 0.0
+    return {"dA": dA, "dH": dH, "dH_codes": codes, "dH_q": dH_q, "dx": dx, "amax": amax}
+
+
+def rank_wgrad_fp8(dy, x, a_q, dH_q, dW1_in=None, db1_in=None, dW2_in=None) -> dict:
+    """dW2 = dy^T a_q; dW1 = dH_q^T x; db1 = column sums of dH_q; each added
+    to the given prior value when one is given (accumulation)."""
+    dW2 = dy.T @ a_q
+    dW1 = dH_q.T @ x
+    db1 = dH_q.sum(axis=0)
+    if dW2_in is not None:
+        dW2 = np.asarray(dW2_in, dtype=np.float64) + dW2
+    if dW1_in is not None:
+        dW1 = np.asarray(dW1_in, dtype=np.float64) + dW1
+    if db1_in is not None:
+        db1 = np.asarray(db1_in, dtype=np.float64) + db1
+    return {"dW1": dW1, "db1": db1, "dW2": dW2}

@@ -348,6 +348,145 @@ def test_current_scaling_recipe():
     assert amax0 == 0 and s0 == 1.0 and np.all(z == 0)
 
 
+# ---------------------------------------------------------------- E5M2
+def _torch_e5m2_codes(v):
+    t = torch.from_numpy(np.clip(np.asarray(v, np.float32), -57344.0, 57344.0))
+    return t.to(torch.float8_e5m2).view(torch.uint8).numpy()
+
+
+def test_e5m2_golden_points_from_ocp_table():
+    with open(os.path.join(GOLDEN, "e5m2_ocp_points.txt")) as fh:
+        rows = [ln.split()[:2] for ln in fh if ln.strip() and not ln.startswith("#")]
+    assert len(rows) == 13
+    for code_s, val_s in rows:
+        code = int(code_s, 16)
+        dec = oracle.e5m2_decode(np.array([code], np.uint8))[0]
+        if val_s == "nan":
+            assert np.isnan(dec)
+        elif val_s in ("inf", "-inf"):
+            assert dec == float(val_s)
+            # saturating conversion: infinities become the largest finite value
+            assert oracle.e5m2_encode(np.array([float(val_s)]))[0] == (0x7B | (code & 0x80))
+        else:
+            val = float(val_s)
+            assert dec == val and math.copysign(1.0, dec) == math.copysign(1.0, val)
+            assert oracle.e5m2_encode(np.array([val]))[0] == code
+
+
+def test_e5m2_decode_table_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    ours = oracle.e5m2_decode(codes)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+    assert np.nanmax(ours[np.isfinite(ours)]) == 57344.0
+
+
+def test_e5m2_encode_matches_torch_cast_and_round_trips():
+    rng = np.random.default_rng(321)
+    vals = [rng.standard_normal(200000).astype(np.float32) * s for s in (1e-4, 0.01, 1, 300, 20000)]
+    grid = oracle.e5m2_decode(np.arange(256, dtype=np.uint8))
+    grid = np.unique(grid[np.isfinite(grid)])
+    mids = ((grid[1:] + grid[:-1]) / 2).astype(np.float32)
+    near = np.concatenate([np.nextafter(mids, np.float32(np.inf)),
+                           np.nextafter(mids, np.float32(-np.inf))])
+    v = np.concatenate(vals + [grid.astype(np.float32), mids, near])
+    assert np.array_equal(oracle.e5m2_encode(v), _torch_e5m2_codes(v))
+    finite = np.arange(256, dtype=np.uint8)
+    finite = finite[np.isfinite(oracle.e5m2_decode(finite))]
+    back = oracle.e5m2_encode(oracle.e5m2_decode(finite))
+    assert np.array_equal(back, finite)
+
+
+def test_e5m2_ties_round_to_even_and_saturate():
+    # 1.125 lies halfway between 1.0 (mantissa 0) and 1.25 (mantissa 1): to even
+    assert oracle.e5m2_encode(np.array([1.125]))[0] == 0x3C
+    # 1.375 between 1.25 (odd) and 1.5 (even): up
+    assert oracle.e5m2_encode(np.array([1.375]))[0] == 0x3E
+    for big in (57345.0, 60000.0, 61440.0, 1e30, np.inf):
+        assert oracle.e5m2_encode(np.array([big]))[0] == 0x7B
+        assert oracle.e5m2_encode(np.array([-big]))[0] == 0xFB
+    assert oracle.e5m2_encode(np.array([np.nan]))[0] & 0x7F == 0x7F
+
+
+def test_quantize_error_bounds_both_formats():
+    rng = np.random.default_rng(9)
+    v = (rng.standard_normal(5000) * 3).astype(np.float32)
+    for fmt, mant, sub in (("e4m3", 3, 2.0 ** -9), ("e5m2", 2, 2.0 ** -16)):
+        s = np.float32(oracle.FMAX[fmt] / np.max(np.abs(v)))
+        deq = oracle.dequantize(oracle.quantize(v, fmt, s), fmt, np.float32(1) / s)
+        # half a unit in the last place in the scaled domain
+        bound = np.maximum(np.abs(v) * 2.0 ** -(mant + 1), sub / 2 / float(s)) * (1 + 1e-6)
+        assert np.all(np.abs(deq - v) <= bound), fmt
+        assert np.max(np.abs(deq)) <= np.max(np.abs(v)) * (1 + 2.0 ** -(mant + 1))
+
+
+def test_delayed_scaling_steps():
+    # a history of 4, e4m3: hand-worked steps
+    h = np.zeros(4, np.float32)
+    s = np.float32(1.0)
+    h, s2, sinv = oracle.delayed_update(h, np.float32(2.0), s, "e4m3")
+    assert list(h) == [2, 0, 0, 0] and s2 == np.float32(224.0) and sinv == 1.0
+    h, s3, sinv = oracle.delayed_update(h, np.float32(8.0), s2, "e4m3")
+    assert list(h) == [8, 2, 0, 0] and s3 == np.float32(56.0)
+    assert sinv == np.float32(np.float32(1) / np.float32(224))
+    h, s4, _ = oracle.delayed_update(h, np.float32(1.0), s3, "e4m3")
+    assert list(h) == [1, 8, 2, 0] and s4 == np.float32(56.0)   # the max is still 8
+    h, s5, _ = oracle.delayed_update(h, np.float32(1.0), s4, "e4m3")
+    h, s6, _ = oracle.delayed_update(h, np.float32(1.0), s5, "e4m3")
+    assert list(h) == [1, 1, 1, 8] and s6 == np.float32(56.0)
+    h, s7, _ = oracle.delayed_update(h, np.float32(1.0), s6, "e4m3")
+    assert list(h) == [1, 1, 1, 1] and s7 == np.float32(448.0)  # 8 has left the window
+    # e5m2 uses its own largest finite value
+    _, s8, _ = oracle.delayed_update(np.zeros(2, np.float32), np.float32(4.0), s, "e5m2")
+    assert s8 == np.float32(14336.0)
+    # a zero or non-finite history keeps the previous scale
+    _, s9, _ = oracle.delayed_update(np.zeros(3, np.float32), np.float32(0.0), np.float32(7), "e4m3")
+    assert s9 == np.float32(7)
+    _, s10, _ = oracle.delayed_update(np.zeros(3, np.float32), np.float32(np.inf), np.float32(7), "e4m3")
+    assert s10 == np.float32(7)
+
+
+def test_fp8_block_is_the_plain_block_within_quantisation_bounds():
+    """The FP8 block's unquantised intermediates are the plain block's; its
+    outputs differ from the plain block by no more than the rounding bound
+    of the quantised intermediates (a in E4M3, dH in E5M2) carried through
+    the following products."""
+    rng = np.random.default_rng(17)
+    T, H, Fs = 24, 40, 32
+    x = rng.standard_normal((T, H))
+    W1 = rng.standard_normal((Fs, H)) * 0.2
+    b1 = rng.standard_normal(Fs) * 0.1
+    W2 = rng.standard_normal((H, Fs)) * 0.2
+    dy = rng.standard_normal((T, H))
+    f = ob.rank_forward(x, W1, b1, W2, "gelu")
+    a_scale = np.float32(448.0 / np.max(np.abs(f["a"])))
+    q = oracle.rank_forward_fp8(x, W1, b1, W2, a_scale)
+    assert np.allclose(q["h"], f["h"], rtol=0, atol=1e-13)
+    assert np.allclose(q["a"], f["a"], rtol=0, atol=1e-13)
+    da = np.maximum(np.abs(f["a"]) * 2.0 ** -4, 2.0 ** -10 / float(a_scale)) * (1 + 1e-6)
+    assert np.all(np.abs(q["a_q"] - f["a"]) <= da)
+    assert np.all(np.abs(q["y"] - f["y"]) <= da @ np.abs(W2.T) + 1e-12)
+    assert np.any(q["a_q"] != f["a"])               # the quantisation is not a no-op
+    g = ob.rank_dgrad(dy, W1, W2, f["h"], "gelu")
+    dH_scale = np.float32(57344.0 / np.max(np.abs(g["dH"])) / 4)
+    p = oracle.rank_dgrad_fp8(dy, W1, W2, f["h"], dH_scale)
+    assert np.allclose(p["dH"], g["dH"], rtol=0, atol=1e-12)
+    dh = np.maximum(np.abs(g["dH"]) * 2.0 ** -3, 2.0 ** -17 / float(dH_scale)) * (1 + 1e-6)
+    assert np.all(np.abs(p["dH_q"] - g["dH"]) <= dh)
+    assert np.all(np.abs(p["dx"] - g["dx"]) <= dh @ np.abs(W1) + 1e-12)
+    w = oracle.rank_wgrad_fp8(dy, x, q["a_q"], p["dH_q"])
+    ref = ob.rank_wgrad(dy, x, f["a"], g["dH"], True)
+    assert np.all(np.abs(w["dW2"] - ref["dW2"]) <= np.abs(dy.T) @ da + 1e-12)
+    assert np.all(np.abs(w["dW1"] - ref["dW1"]) <= dh.T @ np.abs(x) + 1e-12)
+    assert np.all(np.abs(w["db1"] - ref["db1"]) <= dh.sum(axis=0) + 1e-12)
+    # with every intermediate exactly representable the FP8 block is the plain one:
+    # an all-zero gradient quantises exactly
+    z = oracle.rank_dgrad_fp8(np.zeros((T, H)), W1, W2, f["h"], dH_scale)
+    assert np.all(z["dH_codes"] & 0x7F == 0) and np.all(z["dx"] == 0)
+
+
 # ---------------------------------------------------------------- inputs
 def test_synth_is_deterministic_and_shaped():
     w = synth.WORKLOADS[2]
