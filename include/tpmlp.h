@@ -33,11 +33,19 @@
  *   TPMLP_F32  : everything float32.
  *   TPMLP_BF16 : x, W1, b1, W2, dy, h, a, dH, y_partial, dx_partial bfloat16;
  *                products accumulate in float32.
- *   TPMLP_E4M3 : forward only, GELU only. x, W1, W2 are OCP E4M3 codes with
- *                per-tensor float32 dequantisation factors (scale_inv);
- *                b1, h_saved and y_partial are bfloat16; a_saved receives the
- *                E4M3 codes of the activation, quantised with per-tensor
- *                current scaling (scale = 448 / amax(a), amax 0 -> scale 1).
+ *   TPMLP_E4M3 : GELU only. FP8 with per-tensor float32 dequantisation
+ *                factors (scale_inv): forward tensors in OCP E4M3, gradients
+ *                in OCP E5M2 (Transformer Engine's default "hybrid" format;
+ *                the pages name FP8 through Transformer Engine, code tour
+ *                "Honest Limits", concept note "Key math / How it works").
+ *                x, W1, W2, a_saved: E4M3 codes. dy, dH: E5M2 codes.
+ *                b1, h_saved, y_partial, dx_partial: bfloat16. dW1, db1,
+ *                dW2: float32. The block quantises the two tensors it
+ *                produces and reuses: a (E4M3, forward) with current scaling
+ *                (scale = 448 / amax(a), amax 0 -> scale 1) or delayed
+ *                scaling (tpmlp_fp8_history), and dH (E5M2, dgrad) with
+ *                delayed scaling. Codes saturate at the largest finite value
+ *                (448, 57344) and are rounded to nearest even.
  *
  * Ownership: the caller allocates and frees every buffer, the workspace too
  * (size from tpmlp_workspace_size). Pointers are device pointers unless noted.
@@ -62,7 +70,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 2
+#define TPMLP_ABI_VERSION 3
 
 typedef enum {
   TPMLP_OK = 0,
@@ -70,7 +78,7 @@ typedef enum {
   TPMLP_E_SHAPE = 2,       /* T < 0, H <= 0, Fs <= 0, H or Fs not a multiple of 16, or too large */
   TPMLP_E_DTYPE = 3,       /* unknown dtype or activation code */
   TPMLP_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
-  TPMLP_E_UNSUPPORTED = 5, /* valid but not provided (E4M3 backward, E4M3 SwiGLU, SwiGLU bias) */
+  TPMLP_E_UNSUPPORTED = 5, /* valid but not provided (E4M3 SwiGLU, SwiGLU bias) */
   TPMLP_E_WORKSPACE = 6,   /* workspace NULL or smaller than tpmlp_workspace_size */
   TPMLP_E_HIP = 7          /* a HIP runtime call failed while enqueuing */
 } tpmlp_status;
@@ -91,20 +99,48 @@ typedef struct tpmlp_desc {
   int32_t reserved;   /* must be 0 */
 } tpmlp_desc;
 
-/* FP8 forward scales (host struct holding device pointers to single floats). */
+/*
+ * Delayed scaling state of one tensor that the block quantises itself (a in
+ * the forward, dH in dgrad): a host struct holding device pointers, owned by
+ * the caller and updated by each call (Transformer Engine's delayed scaling
+ * with margin 0). The call quantises with *scale; afterwards the tensor's
+ * amax (max |value| over the tensor) enters the history, newest first, the
+ * oldest entry dropping out; *scale_inv = 1 / (the factor the call used),
+ * which is what consumers of the codes dequantise with; and *scale =
+ * fmax / max(history) for the next call (fmax 448 for E4M3, 57344 for E5M2),
+ * unchanged while that maximum is 0 or not finite. All float32.
+ */
+typedef struct tpmlp_fp8_history {
+  float* amax_history;  /* [len] device floats, newest first (start with zeros) */
+  float* scale;         /* device float: in, the factor this call uses; out, the next one */
+  float* scale_inv;     /* device float: out, 1 / (the factor this call used) */
+  int32_t len;          /* 1 .. 4096 */
+  int32_t reserved;     /* must be 0 */
+} tpmlp_fp8_history;
+
+/* FP8 scales (host struct holding device pointers to single floats); the
+   fields a call does not use are ignored. */
 typedef struct tpmlp_fp8_scales {
-  const float* x_scale_inv;   /* in: dequantisation factor of x */
-  const float* w1_scale_inv;  /* in: of W1_shard */
-  const float* w2_scale_inv;  /* in: of W2_shard */
-  float* a_amax;              /* out: max |a| over the bfloat16-rounded activation */
-  float* a_scale_inv;         /* out: 1 / (448 / a_amax) in float32, as used by fc2 */
+  const float* x_scale_inv;   /* fwd, wgrad: dequantisation factor of x (E4M3) */
+  const float* w1_scale_inv;  /* fwd, dgrad: of W1_shard (E4M3) */
+  const float* w2_scale_inv;  /* fwd, dgrad: of W2_shard (E4M3) */
+  float* a_amax;              /* fwd with current scaling: out, max |a| of the bfloat16-rounded a */
+  float* a_scale_inv;         /* fwd with current scaling: out, 1 / (448 / a_amax), as used by fc2;
+                                 wgrad: in, the factor of a_saved (with delayed scaling: the
+                                 a_history->scale_inv the forward wrote) */
+  const tpmlp_fp8_history* a_history;   /* fwd: delayed scaling of a; NULL: current scaling */
+  const float* dy_scale_inv;  /* dgrad, wgrad: of dy (E5M2) */
+  const tpmlp_fp8_history* dH_history;  /* dgrad: delayed scaling of dH (E5M2), required */
+  const float* dH_scale_inv;  /* wgrad: of dH (the dH_history->scale_inv dgrad wrote) */
 } tpmlp_fp8_scales;
 
 /*
  * Bytes of workspace the call needs (0 if none). Returns 0 for an invalid desc.
- * Non-zero for: the E4M3 forward (the bfloat16 activation before
- * quantisation and per-workgroup amax partials) and the BF16 weight gradient
- * with bias (per-tile-column partial sums of db1, added up in a fixed order).
+ * Non-zero for: the E4M3 forward (per-workgroup amax partials of a and,
+ * with current scaling, the bfloat16 activation before quantisation; the
+ * size covers both modes), the E4M3 dgrad (amax partials of dH), and the
+ * BF16 or E4M3 weight gradient with bias (per-tile-column partial sums of
+ * db1, added up in a fixed order).
  */
 size_t tpmlp_workspace_size(const tpmlp_desc* desc, int32_t call);
 
@@ -112,8 +148,11 @@ size_t tpmlp_workspace_size(const tpmlp_desc* desc, int32_t call);
  * Forward (fc1 -> activation -> fc2), enqueued on `stream`:
  *   h = x . W1_shard^T (+ b1_shard);  a = act(h);  y_partial = a . W2_shard^T.
  * For E4M3 the fc1 accumulator is multiplied by x_scale_inv * w1_scale_inv
- * before the bias; `a` is rounded to bfloat16, its amax taken, quantised to
- * E4M3 into a_saved; fc2's accumulator is multiplied by a_scale_inv *
+ * before the bias; `a` is rounded to bfloat16 and quantised to E4M3 into
+ * a_saved: with current scaling (fp8->a_history NULL) from its own amax,
+ * through a bfloat16 copy in the workspace and a second pass; with delayed
+ * scaling directly in fc1's epilogue at a_history->scale, after which the
+ * history is updated. fc2's accumulator is multiplied by (1 / a's scale) *
  * w2_scale_inv. h_saved may be NULL (inference: nothing saved for backward).
  * a_saved is required. b1_shard is required iff desc->has_bias. fp8 must be
  * non-NULL iff dtype is E4M3.
@@ -129,26 +168,35 @@ tpmlp_status tpmlp_fwd(const tpmlp_desc* desc, const void* x, const void* W1_sha
  *   GELU:   dH = dA * gelu'(h)
  *   SwiGLU: dH = [dA * up * silu'(gate) | dA * silu(gate)]  (gate, up = halves of h)
  *   dx_partial = dH . W1_shard.
- * dH is written (the caller keeps it for tpmlp_bwd_wgrad). F32 or BF16 only.
+ * dH is written (the caller keeps it for tpmlp_bwd_wgrad). For E4M3 (GELU):
+ * dy is E5M2 codes; dA is the accumulator times dy_scale_inv * w2_scale_inv;
+ * dH is quantised to E5M2 in the epilogue at fp8->dH_history->scale and the
+ * history updated; dx_partial = dH_codes . W1_codes times
+ * dH_history->scale_inv * w1_scale_inv. fp8 must be non-NULL iff dtype is
+ * E4M3. Workspace: tpmlp_workspace_size(desc, TPMLP_CALL_DGRAD) bytes.
  */
 tpmlp_status tpmlp_bwd_dgrad(const tpmlp_desc* desc, const void* dy, const void* W1_shard,
                              const void* W2_shard, const void* h_saved, void* dH,
-                             void* dx_partial, void* workspace, size_t workspace_bytes,
-                             hipStream_t stream);
+                             void* dx_partial, const tpmlp_fp8_scales* fp8, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Weight gradients, float32 results:
  *   dW2 = dy^T . a_saved;  dW1 = dH^T . x;  db1 = column sums of dH (if has_bias).
  * accumulate = 0 overwrites the outputs; accumulate = 1 adds into them
  * (gradient accumulation across micro-batches). db1 may be NULL only when
- * has_bias = 0. F32 or BF16 only. Workspace: tpmlp_workspace_size(desc,
- * TPMLP_CALL_WGRAD) bytes (BF16 with bias). Results are reproducible bit for
- * bit: every sum is taken in a fixed order, no atomics.
+ * has_bias = 0. For E4M3 the operands are FP8 codes (dy, dH: E5M2; x, a: E4M3)
+ * and each product is scaled by its two operands' dequantisation factors
+ * from fp8 (dy_scale_inv, a_scale_inv, dH_scale_inv, x_scale_inv); db1 is
+ * the column sums of the dequantised dH. fp8 must be non-NULL iff dtype is
+ * E4M3. Workspace: tpmlp_workspace_size(desc, TPMLP_CALL_WGRAD) bytes (with
+ * bias). Results are reproducible bit for bit: every sum is taken in a
+ * fixed order, no atomics.
  */
 tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* desc, const void* dy, const void* x,
                              const void* a_saved, const void* dH, float* dW1, float* db1,
-                             float* dW2, int32_t accumulate, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream);
+                             float* dW2, int32_t accumulate, const tpmlp_fp8_scales* fp8,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Per-tensor current-scaling quantiser (the FP8 recipe used for `a` inside
@@ -161,6 +209,11 @@ tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* desc, const void* dy, const void*
  */
 size_t tpmlp_quantize_workspace_size(int64_t n);
 tpmlp_status tpmlp_quantize_e4m3(int32_t src_dtype, const void* src, int64_t n, uint8_t* dst,
+                                 float* amax_out, float* scale_inv_out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+/* The same recipe into OCP E5M2 (for gradients such as dy): scale = 57344 /
+   amax, codes saturate at +-57344. Same arguments and workspace. */
+tpmlp_status tpmlp_quantize_e5m2(int32_t src_dtype, const void* src, int64_t n, uint8_t* dst,
                                  float* amax_out, float* scale_inv_out, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
 

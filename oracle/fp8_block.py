@@ -14,6 +14,13 @@ the call is given (delayed scaling, see oracle.fp8):
   gradients and the bias gradient.
 
 Everything else is float64 on those values.
+
+Where the device's rounding decides a code, the oracle takes the same
+steps, so that both sides decide in the same precision (the pages fix none):
+fc1's output h leaves the block as bfloat16 (its storage type at the
+boundary), and the activation, forward and backward, is taken of h as
+stored: a = gelu(bf16(h)), dH = dA * gelu'(bf16(h)). The value handed to
+the quantiser is then rounded to float32 once, as the device's is.
 """
 from __future__ import annotations
 
@@ -27,21 +34,35 @@ def _inv(scale) -> np.float32:
     return np.float32(np.float32(1.0) / np.float32(scale))
 
 
+def round_bf16(v) -> np.ndarray:
+    """bfloat16 value of fl32(v), round to nearest even, as float64: the top
+    16 bits of the float32 pattern after adding half of the dropped range
+    (0x7fff, plus 1 when the kept part is odd). Finite inputs only."""
+    b = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def rank_forward_fp8(x, W1, b1, W2, a_scale) -> dict:
-    """h = x W1^T + b1; a = gelu(h); a quantised to E4M3 at a_scale (codes,
-    and a_q = decode(code) / a_scale); y = a_q W2^T. amax = max |a|."""
-    h = x @ W1.T + (0.0 if b1 is None else b1)
+    """h = x W1^T + b1, stored as bf16; a = gelu(h as stored); a quantised
+    to E4M3 at a_scale (codes, and a_q = decode(code) / a_scale);
+    y = a_q W2^T. amax = max |a|. Returns h as stored (bf16 values) and,
+    as h_exact, before that rounding."""
+    h_exact = x @ W1.T + (0.0 if b1 is None else b1)
+    h = round_bf16(h_exact)
     a = gelu_tanh(h)
     codes = quantize(a, "e4m3", a_scale)
     a_q = dequantize(codes, "e4m3", _inv(a_scale))
     y = a_q @ W2.T
     amax = float(np.max(np.abs(a))) if a.size else 0.0
-    return {"h": h, "a": a, "a_codes": codes, "a_q": a_q, "y": y, "amax": amax}
+    return {"h_exact": h_exact, "h": h, "a": a, "a_codes": codes, "a_q": a_q, "y": y,
+            "amax": amax}
 
 
 def rank_dgrad_fp8(dy, W1, W2, h, dH_scale) -> dict:
-    """dA = dy W2; dH = dA * gelu'(h); dH quantised to E5M2 at dH_scale
-    (codes, and dH_q); dx = dH_q W1. amax = max |dH|."""
+    """dA = dy W2; dH = dA * gelu'(h), h as the forward stored it (bf16);
+    dH quantised to E5M2 at dH_scale (codes, and dH_q); dx = dH_q W1.
+    amax = max |dH|."""
     dA = dy @ W2
     dH = dA * gelu_tanh_grad(h)
     codes = quantize(dH, "e5m2", dH_scale)

@@ -8,7 +8,7 @@ HIP stream; every step of the block runs in the library's HIP kernels
 this module raises on import -- there is no fallback path.
 
 The C entry points keep their names here (``tpmlp_fwd``, ``tpmlp_bwd_dgrad``,
-``tpmlp_bwd_wgrad``, ``tpmlp_quantize_e4m3``) and take preallocated output
+``tpmlp_bwd_wgrad``, ``tpmlp_quantize_e4m3``, ``tpmlp_quantize_e5m2``) and take preallocated output
 tensors; ``fwd``, ``bwd_dgrad`` and ``bwd_wgrad`` are conveniences that
 allocate the outputs with torch and call them. Layouts are those of
 ``include/tpmlp.h``.
@@ -42,10 +42,44 @@ class Desc(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class Fp8History(ctypes.Structure):
+    _fields_ = [("amax_history", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("scale_inv", ctypes.c_void_p), ("len", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 class Fp8Scales(ctypes.Structure):
     _fields_ = [("x_scale_inv", ctypes.c_void_p), ("w1_scale_inv", ctypes.c_void_p),
                 ("w2_scale_inv", ctypes.c_void_p), ("a_amax", ctypes.c_void_p),
-                ("a_scale_inv", ctypes.c_void_p)]
+                ("a_scale_inv", ctypes.c_void_p), ("a_history", ctypes.POINTER(Fp8History)),
+                ("dy_scale_inv", ctypes.c_void_p), ("dH_history", ctypes.POINTER(Fp8History)),
+                ("dH_scale_inv", ctypes.c_void_p)]
+
+
+class DelayedScaling:
+    """Device state of one tensor under delayed scaling (tpmlp_fp8_history):
+    an amax history of ``length`` floats (newest first), the scale the next
+    call quantises with and the 1/scale of the last call."""
+
+    def __init__(self, length: int, device="cuda", scale: float = 1.0):
+        self.amax_history = torch.zeros(length, dtype=torch.float32, device=device)
+        self.scale = torch.full((1,), float(scale), dtype=torch.float32, device=device)
+        self.scale_inv = torch.zeros(1, dtype=torch.float32, device=device)
+        self.struct = Fp8History(_ptr(self.amax_history), _ptr(self.scale), _ptr(self.scale_inv),
+                                 int(length), 0)
+
+
+def fp8_scales(x_scale_inv=None, w1_scale_inv=None, w2_scale_inv=None, a_amax=None,
+               a_scale_inv=None, a_history: DelayedScaling | None = None, dy_scale_inv=None,
+               dH_history: DelayedScaling | None = None, dH_scale_inv=None) -> Fp8Scales:
+    """tpmlp_fp8_scales from one-element float32 device tensors (None: NULL)."""
+    sc = Fp8Scales(_ptr(x_scale_inv), _ptr(w1_scale_inv), _ptr(w2_scale_inv), _ptr(a_amax),
+                   _ptr(a_scale_inv), None if a_history is None else ctypes.pointer(a_history.struct),
+                   _ptr(dy_scale_inv),
+                   None if dH_history is None else ctypes.pointer(dH_history.struct),
+                   _ptr(dH_scale_inv))
+    sc._keep = (a_history, dH_history)
+    return sc
 
 
 class TpmlpError(RuntimeError):
@@ -65,15 +99,17 @@ def _load():
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     pdesc = ctypes.POINTER(Desc)
     L.tpmlp_fwd.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Fp8Scales), vp, sz, vp]
-    L.tpmlp_bwd_dgrad.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    L.tpmlp_bwd_wgrad.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    psc = ctypes.POINTER(Fp8Scales)
+    L.tpmlp_bwd_dgrad.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, psc, vp, sz, vp]
+    L.tpmlp_bwd_wgrad.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, i32, psc, vp, sz, vp]
     L.tpmlp_quantize_e4m3.argtypes = [i32, vp, i64, vp, vp, vp, vp, sz, vp]
+    L.tpmlp_quantize_e5m2.argtypes = [i32, vp, i64, vp, vp, vp, vp, sz, vp]
     L.tpmlp_quantize_workspace_size.argtypes = [i64]
     L.tpmlp_quantize_workspace_size.restype = sz
     L.tpmlp_workspace_size.argtypes = [pdesc, i32]
     L.tpmlp_workspace_size.restype = sz
     for f in ("tpmlp_fwd", "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad", "tpmlp_quantize_e4m3",
-              "tpmlp_timing_enable"):
+              "tpmlp_quantize_e5m2", "tpmlp_timing_enable"):
         getattr(L, f).restype = i32
     L.tpmlp_strerror.argtypes = [i32]
     L.tpmlp_strerror.restype = ctypes.c_char_p
@@ -132,27 +168,38 @@ def tpmlp_fwd(desc, x, W1, b1, W2, y, h, a, fp8=None, workspace=None, stream=Non
                          _ptr(h), _ptr(a), sc, ws, nbytes, _stream(stream)), "tpmlp_fwd")
 
 
-def tpmlp_bwd_dgrad(desc, dy, W1, W2, h, dH, dx, workspace=None, stream=None):
+def tpmlp_bwd_dgrad(desc, dy, W1, W2, h, dH, dx, fp8=None, workspace=None, stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sc = None if fp8 is None else ctypes.byref(fp8)
     _check(lib.tpmlp_bwd_dgrad(ctypes.byref(desc), _ptr(dy), _ptr(W1), _ptr(W2), _ptr(h),
-                               _ptr(dH), _ptr(dx), _ptr(workspace), nbytes, _stream(stream)),
+                               _ptr(dH), _ptr(dx), sc, _ptr(workspace), nbytes, _stream(stream)),
            "tpmlp_bwd_dgrad")
 
 
-def tpmlp_bwd_wgrad(desc, dy, x, a, dH, dW1, db1, dW2, accumulate=False, workspace=None,
-                    stream=None):
+def tpmlp_bwd_wgrad(desc, dy, x, a, dH, dW1, db1, dW2, accumulate=False, fp8=None,
+                    workspace=None, stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sc = None if fp8 is None else ctypes.byref(fp8)
     _check(lib.tpmlp_bwd_wgrad(ctypes.byref(desc), _ptr(dy), _ptr(x), _ptr(a), _ptr(dH),
-                               _ptr(dW1), _ptr(db1), _ptr(dW2), int(bool(accumulate)),
+                               _ptr(dW1), _ptr(db1), _ptr(dW2), int(bool(accumulate)), sc,
                                _ptr(workspace), nbytes, _stream(stream)), "tpmlp_bwd_wgrad")
 
 
-def tpmlp_quantize_e4m3(src, dst, amax, scale_inv, workspace, stream=None):
+def _quantize(fn, name, src, dst, amax, scale_inv, workspace, stream):
     dt = BF16 if src.dtype == torch.bfloat16 else F32 if src.dtype == torch.float32 else -1
     nbytes = workspace.numel() * workspace.element_size()
-    _check(lib.tpmlp_quantize_e4m3(dt, _ptr(src), src.numel(), _ptr(dst), _ptr(amax),
-                                   _ptr(scale_inv), _ptr(workspace), nbytes, _stream(stream)),
-           "tpmlp_quantize_e4m3")
+    _check(fn(dt, _ptr(src), src.numel(), _ptr(dst), _ptr(amax), _ptr(scale_inv),
+              _ptr(workspace), nbytes, _stream(stream)), name)
+
+
+def tpmlp_quantize_e4m3(src, dst, amax, scale_inv, workspace, stream=None):
+    _quantize(lib.tpmlp_quantize_e4m3, "tpmlp_quantize_e4m3", src, dst, amax, scale_inv,
+              workspace, stream)
+
+
+def tpmlp_quantize_e5m2(src, dst, amax, scale_inv, workspace, stream=None):
+    _quantize(lib.tpmlp_quantize_e5m2, "tpmlp_quantize_e5m2", src, dst, amax, scale_inv,
+              workspace, stream)
 
 
 # ------------------------------------------------------------------ conveniences
@@ -160,10 +207,11 @@ def _empty(shape, dtype, device):
     return torch.empty(shape, dtype=dtype, device=device)
 
 
-def fwd(desc, x, W1, b1, W2, save_h=True, fp8_in_scales=None, stream=None):
+def fwd(desc, x, W1, b1, W2, save_h=True, fp8_in_scales=None, a_history=None, stream=None):
     """Run the forward; returns dict y, h (or None), a, and for E4M3 a_amax,
     a_scale_inv. ``fp8_in_scales`` = (x_scale_inv, w1_scale_inv, w2_scale_inv)
-    one-element fp32 device tensors."""
+    one-element fp32 device tensors. With ``a_history`` (DelayedScaling), a
+    is quantised with delayed scaling and a_scale_inv is the history's."""
     dev = x.device
     T, H, Fs = desc.tokens, desc.hidden, desc.ffn_shard
     G = 2 if desc.act == SWIGLU else 1
@@ -173,29 +221,41 @@ def fwd(desc, x, W1, b1, W2, save_h=True, fp8_in_scales=None, stream=None):
            "a": _empty((T, Fs), torch.uint8 if desc.dtype == E4M3 else act_t, dev)}
     sc = None
     if desc.dtype == E4M3:
-        out["a_amax"] = torch.zeros(1, dtype=torch.float32, device=dev)
-        out["a_scale_inv"] = torch.zeros(1, dtype=torch.float32, device=dev)
         xs, w1s, w2s = fp8_in_scales
-        sc = Fp8Scales(_ptr(xs), _ptr(w1s), _ptr(w2s), _ptr(out["a_amax"]), _ptr(out["a_scale_inv"]))
+        if a_history is None:
+            out["a_amax"] = torch.zeros(1, dtype=torch.float32, device=dev)
+            out["a_scale_inv"] = torch.zeros(1, dtype=torch.float32, device=dev)
+            sc = fp8_scales(xs, w1s, w2s, out["a_amax"], out["a_scale_inv"])
+        else:
+            out["a_scale_inv"] = a_history.scale_inv
+            sc = fp8_scales(xs, w1s, w2s, a_history=a_history)
     n = workspace_size(desc, CALL_FWD)
     ws = _empty((max(n, 1),), torch.uint8, dev) if n else None
     tpmlp_fwd(desc, x, W1, b1, W2, out["y"], out["h"], out["a"], sc, ws, stream)
     return out
 
 
-def bwd_dgrad(desc, dy, W1, W2, h, stream=None):
+def bwd_dgrad(desc, dy, W1, W2, h, fp8=None, stream=None):
+    """dH and dx_partial. For E4M3, ``fp8`` = dict dy_scale_inv, w1_scale_inv,
+    w2_scale_inv (device tensors) and dH_history (DelayedScaling); dH is
+    E5M2 codes and dx_partial bfloat16."""
     dev = dy.device
     T, H, Fs = desc.tokens, desc.hidden, desc.ffn_shard
     G = 2 if desc.act == SWIGLU else 1
     t = _TORCH[desc.dtype]
-    out = {"dH": _empty((T, G * Fs), t, dev), "dx": _empty((T, H), t, dev)}
-    tpmlp_bwd_dgrad(desc, dy, W1, W2, h, out["dH"], out["dx"], None, stream)
+    out = {"dH": _empty((T, G * Fs), t, dev),
+           "dx": _empty((T, H), torch.bfloat16 if desc.dtype == E4M3 else t, dev)}
+    sc = None if fp8 is None else fp8_scales(**fp8)
+    n = workspace_size(desc, CALL_DGRAD)
+    ws = _empty((n,), torch.uint8, dev) if n else None
+    tpmlp_bwd_dgrad(desc, dy, W1, W2, h, out["dH"], out["dx"], sc, ws, stream)
     return out
 
 
-def bwd_wgrad(desc, dy, x, a, dH, accumulate_into=None, stream=None):
+def bwd_wgrad(desc, dy, x, a, dH, accumulate_into=None, fp8=None, stream=None):
     """fp32 weight gradients. ``accumulate_into`` = dict dW1, db1, dW2 of
-    existing fp32 buffers to add into (accumulate mode)."""
+    existing fp32 buffers to add into (accumulate mode). For E4M3, ``fp8`` =
+    dict dy_scale_inv, x_scale_inv, a_scale_inv, dH_scale_inv."""
     dev = dy.device
     H, Fs = desc.hidden, desc.ffn_shard
     G = 2 if desc.act == SWIGLU else 1
@@ -207,21 +267,27 @@ def bwd_wgrad(desc, dy, x, a, dH, accumulate_into=None, stream=None):
                "dW2": _empty((H, Fs), torch.float32, dev)}
     n = workspace_size(desc, CALL_WGRAD)
     ws = _empty((n,), torch.uint8, dev) if n else None
+    sc = None if fp8 is None else fp8_scales(**fp8)
     tpmlp_bwd_wgrad(desc, dy, x, a, dH, out["dW1"], out.get("db1"), out["dW2"],
-                    accumulate=accumulate_into is not None, workspace=ws, stream=stream)
+                    accumulate=accumulate_into is not None, fp8=sc, workspace=ws, stream=stream)
     return out
 
 
-def quantize_e4m3(src, stream=None):
-    """E4M3 codes (uint8, same shape) plus one-element amax and scale_inv."""
+def quantize_e4m3(src, stream=None, e5m2=False):
+    """E4M3 (or E5M2) codes (uint8, same shape) plus one-element amax and
+    scale_inv, per-tensor current scaling."""
     dev = src.device
     dst = _empty(src.shape, torch.uint8, dev)
     amax = torch.zeros(1, dtype=torch.float32, device=dev)
     sinv = torch.zeros(1, dtype=torch.float32, device=dev)
     n = int(lib.tpmlp_quantize_workspace_size(src.numel()))
     ws = _empty((max(n, 256),), torch.uint8, dev)
-    tpmlp_quantize_e4m3(src, dst, amax, sinv, ws, stream)
+    (tpmlp_quantize_e5m2 if e5m2 else tpmlp_quantize_e4m3)(src, dst, amax, sinv, ws, stream)
     return dst, amax, sinv
+
+
+def quantize_e5m2(src, stream=None):
+    return quantize_e4m3(src, stream, e5m2=True)
 
 
 # ------------------------------------------------------------------ timing
@@ -239,7 +305,8 @@ def timing_collect(cap: int = 64) -> dict:
     return {names[i].decode(): (int(counts[i]), float(tot[i])) for i in range(min(n, cap))}
 
 
-__all__ = ["Desc", "Fp8Scales", "TpmlpError", "make_desc", "workspace_size", "tpmlp_fwd",
-           "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad", "tpmlp_quantize_e4m3", "fwd", "bwd_dgrad",
-           "bwd_wgrad", "quantize_e4m3", "timing_enable", "timing_collect", "lib", "LIB_PATH",
+__all__ = ["Desc", "Fp8Scales", "Fp8History", "DelayedScaling", "fp8_scales", "TpmlpError",
+           "make_desc", "workspace_size", "tpmlp_fwd", "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad",
+           "tpmlp_quantize_e4m3", "tpmlp_quantize_e5m2", "fwd", "bwd_dgrad", "bwd_wgrad",
+           "quantize_e4m3", "quantize_e5m2", "timing_enable", "timing_collect", "lib", "LIB_PATH",
            "F32", "BF16", "E4M3", "GELU", "SWIGLU"]

@@ -91,15 +91,21 @@ tpmlp_status check_ptrs(std::initializer_list<const void*> req) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-int fp8_fc1_parts(const tpmlp_desc* d) {
+// workgroups of the MFMA kernel for an M x N product (one per 256 x 256 tile)
+int gemm_tiles(int64_t M, int64_t N) {
   GemmArgs g{};
-  g.M = (int)d->tokens;
-  g.N = (int)d->ffn_shard;
-  return mfma_grid(FC1_FWD_GELU, g);
+  g.M = (int)M;
+  g.N = (int)N;
+  return mfma_grid(FC2_FWD, g);
 }
 
-// bf16 fc1 wgrad with bias: tile columns of dW1 = dH^T . x (N = H), each of
-// which writes one row of db1 partial sums
+// e4m3 forward: fc1's workgroups, one amax partial each
+int fp8_fc1_parts(const tpmlp_desc* d) { return gemm_tiles(d->tokens, d->ffn_shard); }
+// e4m3 dgrad: fc2 dgrad's workgroups (M = T, N = Fs), one amax partial of dH each
+int fp8_dgrad_parts(const tpmlp_desc* d) { return gemm_tiles(d->tokens, d->ffn_shard); }
+
+// fc1 wgrad with bias: tile columns of dW1 = dH^T . x (N = H), each of which
+// writes one row of db1 partial sums
 int colsum_parts(const tpmlp_desc* d) {
   GemmArgs g{};
   g.M = (int)(d->act == TPMLP_ACT_SWIGLU ? 2 * d->ffn_shard : d->ffn_shard);
@@ -109,16 +115,26 @@ int colsum_parts(const tpmlp_desc* d) {
 }
 
 size_t workspace_bytes(const tpmlp_desc* d, int32_t call) {
-  if (call == TPMLP_CALL_FWD && d->dtype == TPMLP_E4M3) {
+  const bool fp8 = d->dtype == TPMLP_E4M3;
+  if (call == TPMLP_CALL_FWD && fp8) {
+    // current scaling: bf16 a, then the partials; delayed scaling: partials only
     const size_t a_bytes = align_up((size_t)d->tokens * (size_t)d->ffn_shard * 2, 256);
     const size_t parts = align_up((size_t)fp8_fc1_parts(d) * 4 + 4, 256);
     return a_bytes + parts;
   }
-  if (call == TPMLP_CALL_WGRAD && d->dtype == TPMLP_BF16 && d->has_bias) {
+  if (call == TPMLP_CALL_DGRAD && fp8) return align_up((size_t)fp8_dgrad_parts(d) * 4 + 4, 256);
+  if (call == TPMLP_CALL_WGRAD && d->dtype != TPMLP_F32 && d->has_bias) {
     const size_t gfs = (size_t)(d->act == TPMLP_ACT_SWIGLU ? 2 : 1) * (size_t)d->ffn_shard;
     return align_up((size_t)colsum_parts(d) * gfs * 4, 256);
   }
   return 0;
+}
+
+// A delayed-scaling state: pointers present, length in range.
+tpmlp_status check_history(const tpmlp_fp8_history* h) {
+  if (!h || !h->amax_history || !h->scale || !h->scale_inv) return TPMLP_E_NULL;
+  if (h->reserved != 0 || h->len < 1 || h->len > kMaxHistoryLen) return TPMLP_E_SHAPE;
+  return TPMLP_OK;
 }
 
 tpmlp_status check_workspace(const tpmlp_desc* d, int32_t call, void* ws, size_t ws_bytes) {
@@ -177,7 +193,7 @@ const char* tpmlp_strerror(tpmlp_status s) {
     case TPMLP_E_SHAPE: return "invalid sizes (T >= 0; H, Fs > 0 and multiples of 16; within limits)";
     case TPMLP_E_DTYPE: return "unknown dtype, activation or flag value";
     case TPMLP_E_ALIGN: return "a pointer is not 16-byte aligned";
-    case TPMLP_E_UNSUPPORTED: return "combination not provided (E4M3 backward, E4M3 SwiGLU, SwiGLU bias)";
+    case TPMLP_E_UNSUPPORTED: return "combination not provided (E4M3 SwiGLU, SwiGLU bias)";
     case TPMLP_E_WORKSPACE: return "workspace missing or too small";
     case TPMLP_E_HIP: return "HIP runtime error while enqueuing (see tpmlp_last_hip_error)";
   }
@@ -205,9 +221,11 @@ tpmlp_status tpmlp_fwd(const tpmlp_desc* d, const void* x, const void* W1, const
   if (h_saved && !aligned16(h_saved)) return TPMLP_E_ALIGN;
   const bool is_fp8 = d->dtype == TPMLP_E4M3;
   if (is_fp8 != (fp8 != nullptr)) return is_fp8 ? TPMLP_E_NULL : TPMLP_E_DTYPE;
-  if (is_fp8 && (!fp8->x_scale_inv || !fp8->w1_scale_inv || !fp8->w2_scale_inv ||
-                 !fp8->a_amax || !fp8->a_scale_inv))
+  const bool delayed = is_fp8 && fp8->a_history != nullptr;
+  if (is_fp8 && (!fp8->x_scale_inv || !fp8->w1_scale_inv || !fp8->w2_scale_inv))
     return TPMLP_E_NULL;
+  if (is_fp8 && !delayed && (!fp8->a_amax || !fp8->a_scale_inv)) return TPMLP_E_NULL;
+  if (delayed && (st = check_history(fp8->a_history)) != TPMLP_OK) return st;
   if ((st = check_workspace(d, TPMLP_CALL_FWD, ws, ws_bytes)) != TPMLP_OK) return st;
 
   const int64_t T = d->tokens, H = d->hidden, Fs = d->ffn_shard;
@@ -233,7 +251,38 @@ tpmlp_status tpmlp_fwd(const tpmlp_desc* d, const void* x, const void* W1, const
     return TPMLP_OK;
   }
 
-  // e4m3: fc1 (bf16 a + per-workgroup amax) -> quantise a -> fc2
+  if (delayed) {
+    // e4m3, delayed scaling: fc1 quantises a at a_history->scale in its
+    // epilogue (+ per-workgroup amax) -> history update -> fc2
+    const tpmlp_fp8_history* ah = fp8->a_history;
+    if (T == 0) return TPMLP_OK;
+    float* parts = static_cast<float*>(ws);
+    const int nparts = fp8_fc1_parts(d);
+    EpiArgs e1{};
+    e1.out = a_saved; e1.ldo = Fs;
+    e1.out2 = h_saved; e1.ldo2 = Fs;
+    e1.bias = d->has_bias ? b1 : nullptr;
+    e1.scale_a = fp8->x_scale_inv; e1.scale_b = fp8->w1_scale_inv;
+    e1.q_scale = ah->scale;
+    e1.amax_part = parts;
+    GemmArgs g1 = make_gemm(x, H, W1, H, T, Fs, H, Fs);
+    err = run_step(kind, FC1_FWD_GELU_Q, label(kind, 0), g1, e1, s);
+    if (err != hipSuccess) return hip_fail(err);
+    err = timed("a_scale_update.e4m3", s, [&]() {
+      return delayed_update_launch(parts, nparts, ah->amax_history, ah->len, ah->scale,
+                                   ah->scale_inv, false, s);
+    });
+    if (err != hipSuccess) return hip_fail(err);
+    EpiArgs e2{};
+    e2.out = y; e2.ldo = H;
+    e2.scale_a = ah->scale_inv; e2.scale_b = fp8->w2_scale_inv;
+    GemmArgs g2 = make_gemm(a_saved, Fs, W2, Fs, T, H, Fs, 0);
+    err = run_step(kind, FC2_FWD, label(kind, 1), g2, e2, s);
+    if (err != hipSuccess) return hip_fail(err);
+    return TPMLP_OK;
+  }
+
+  // e4m3, current scaling: fc1 (bf16 a + per-workgroup amax) -> quantise a -> fc2
   char* wsb = static_cast<char*>(ws);
   void* a_bf16 = wsb;
   float* parts = reinterpret_cast<float*>(wsb + align_up((size_t)T * (size_t)Fs * 2, 256));
@@ -267,28 +316,52 @@ tpmlp_status tpmlp_fwd(const tpmlp_desc* d, const void* x, const void* W1, const
 
 tpmlp_status tpmlp_bwd_dgrad(const tpmlp_desc* d, const void* dy, const void* W1,
                              const void* W2, const void* h_saved, void* dH, void* dx,
-                             void* ws, size_t ws_bytes, hipStream_t s) {
+                             const tpmlp_fp8_scales* fp8, void* ws, size_t ws_bytes,
+                             hipStream_t s) {
   tpmlp_status st = check_desc(d);
   if (st != TPMLP_OK) return st;
-  if (d->dtype == TPMLP_E4M3) return TPMLP_E_UNSUPPORTED;
   if ((st = check_ptrs({dy, W1, W2, h_saved, dH, dx})) != TPMLP_OK) return st;
+  const bool is_fp8 = d->dtype == TPMLP_E4M3;
+  if (is_fp8 != (fp8 != nullptr)) return is_fp8 ? TPMLP_E_NULL : TPMLP_E_DTYPE;
+  if (is_fp8) {
+    if (!fp8->dy_scale_inv || !fp8->w1_scale_inv || !fp8->w2_scale_inv) return TPMLP_E_NULL;
+    if ((st = check_history(fp8->dH_history)) != TPMLP_OK) return st;
+  }
   if ((st = check_workspace(d, TPMLP_CALL_DGRAD, ws, ws_bytes)) != TPMLP_OK) return st;
   const int64_t T = d->tokens, H = d->hidden, Fs = d->ffn_shard;
   if (T == 0) return TPMLP_OK;
   const bool swiglu = d->act == TPMLP_ACT_SWIGLU;
   const int64_t GFs = swiglu ? 2 * Fs : Fs;
-  const Kind kind = d->dtype == TPMLP_F32 ? KIND_F32 : KIND_BF16;
+  const Kind kind = d->dtype == TPMLP_F32 ? KIND_F32 : d->dtype == TPMLP_BF16 ? KIND_BF16 : KIND_E4M3;
+  hipError_t err;
   // fc2 dgrad: dA = dy . W2 (W2 [H, Fs] read as [K=H][N=Fs]), activation derivative fused
   EpiArgs e1{};
   e1.out = dH; e1.ldo = GFs;
   e1.aux = h_saved; e1.ldaux = GFs;
   GemmArgs g1 = make_gemm(dy, H, W2, Fs, T, Fs, H, Fs);
-  hipError_t err =
-      run_step(kind, swiglu ? FC2_DGRAD_SWIGLU : FC2_DGRAD_GELU, label(kind, 2), g1, e1, s);
-  if (err != hipSuccess) return hip_fail(err);
+  if (!is_fp8) {
+    err = run_step(kind, swiglu ? FC2_DGRAD_SWIGLU : FC2_DGRAD_GELU, label(kind, 2), g1, e1, s);
+    if (err != hipSuccess) return hip_fail(err);
+  } else {
+    // dH quantised to e5m2 at dH_history->scale in the epilogue, then the
+    // history update (which also writes the factor fc1 dgrad dequantises with)
+    const tpmlp_fp8_history* hh = fp8->dH_history;
+    float* parts = static_cast<float*>(ws);
+    e1.scale_a = fp8->dy_scale_inv; e1.scale_b = fp8->w2_scale_inv;
+    e1.q_scale = hh->scale;
+    e1.amax_part = parts;
+    err = run_step(kind, FC2_DGRAD_GELU_Q, label(kind, 2), g1, e1, s);
+    if (err != hipSuccess) return hip_fail(err);
+    err = timed("dH_scale_update.e4m3", s, [&]() {
+      return delayed_update_launch(parts, fp8_dgrad_parts(d), hh->amax_history, hh->len,
+                                   hh->scale, hh->scale_inv, true, s);
+    });
+    if (err != hipSuccess) return hip_fail(err);
+  }
   // fc1 dgrad: dx = dH . W1 (W1 [GFs, H] read as [K=GFs][N=H])
   EpiArgs e2{};
   e2.out = dx; e2.ldo = H;
+  if (is_fp8) { e2.scale_a = fp8->dH_history->scale_inv; e2.scale_b = fp8->w1_scale_inv; }
   GemmArgs g2 = make_gemm(dH, GFs, W1, H, T, H, GFs, 0);
   err = run_step(kind, FC1_DGRAD, label(kind, 3), g2, e2, s);
   if (err != hipSuccess) return hip_fail(err);
@@ -297,38 +370,44 @@ tpmlp_status tpmlp_bwd_dgrad(const tpmlp_desc* d, const void* dy, const void* W1
 
 tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* d, const void* dy, const void* x,
                              const void* a_saved, const void* dH, float* dW1, float* db1,
-                             float* dW2, int32_t accumulate, void* ws, size_t ws_bytes,
-                             hipStream_t s) {
+                             float* dW2, int32_t accumulate, const tpmlp_fp8_scales* fp8,
+                             void* ws, size_t ws_bytes, hipStream_t s) {
   tpmlp_status st = check_desc(d);
   if (st != TPMLP_OK) return st;
-  if (d->dtype == TPMLP_E4M3) return TPMLP_E_UNSUPPORTED;
   if (accumulate != 0 && accumulate != 1) return TPMLP_E_DTYPE;
   if ((st = check_ptrs({dy, x, a_saved, dH, dW1, dW2})) != TPMLP_OK) return st;
   if (d->has_bias && (st = check_ptrs({db1})) != TPMLP_OK) return st;
+  const bool is_fp8 = d->dtype == TPMLP_E4M3;
+  if (is_fp8 != (fp8 != nullptr)) return is_fp8 ? TPMLP_E_NULL : TPMLP_E_DTYPE;
+  if (is_fp8 && (!fp8->dy_scale_inv || !fp8->x_scale_inv || !fp8->a_scale_inv ||
+                 !fp8->dH_scale_inv))
+    return TPMLP_E_NULL;
   if ((st = check_workspace(d, TPMLP_CALL_WGRAD, ws, ws_bytes)) != TPMLP_OK) return st;
   const int64_t T = d->tokens, H = d->hidden, Fs = d->ffn_shard;
   if (T == 0 && accumulate) return TPMLP_OK;  // adding nothing
   const bool swiglu = d->act == TPMLP_ACT_SWIGLU;
   const int64_t GFs = swiglu ? 2 * Fs : Fs;
-  const Kind kind = d->dtype == TPMLP_F32 ? KIND_F32 : KIND_BF16;
+  const Kind kind = d->dtype == TPMLP_F32 ? KIND_F32 : d->dtype == TPMLP_BF16 ? KIND_BF16 : KIND_E4M3;
   // dW2 [H, Fs] = dy^T . a : A = dy as [K=T][M=H], B = a as [K=T][N=Fs]
   EpiArgs e1{};
   e1.out = dW2; e1.ldo = Fs; e1.accumulate = accumulate;
+  if (is_fp8) { e1.scale_a = fp8->dy_scale_inv; e1.scale_b = fp8->a_scale_inv; }
   GemmArgs g1 = make_gemm(dy, H, a_saved, Fs, H, Fs, T, 0);
   hipError_t err = run_step(kind, WGRAD, label(kind, 4), g1, e1, s);
   if (err != hipSuccess) return hip_fail(err);
   // dW1 [GFs, H] = dH^T . x (+ db1 = column sums of dH). The fp32 kernel
   // writes db1 itself; the MFMA kernel writes per-tile-column partial sums
   // into the workspace, which a second pass adds up into db1.
-  const bool split = d->has_bias && kind == KIND_BF16;
+  const bool split = d->has_bias && kind != KIND_F32;
   EpiArgs e2{};
   e2.out = dW1; e2.ldo = H; e2.accumulate = accumulate;
   e2.colsum = d->has_bias ? (split ? static_cast<float*>(ws) : db1) : nullptr;
+  if (is_fp8) { e2.scale_a = fp8->dH_scale_inv; e2.scale_b = fp8->x_scale_inv; }
   GemmArgs g2 = make_gemm(dH, GFs, x, H, GFs, H, T, 0);
   err = run_step(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, label(kind, 5), g2, e2, s);
   if (err != hipSuccess) return hip_fail(err);
   if (split) {
-    err = timed("db1_reduce.bf16", s, [&]() {
+    err = timed(is_fp8 ? "db1_reduce.e4m3" : "db1_reduce.bf16", s, [&]() {
       return colsum_reduce_launch(static_cast<const float*>(ws), colsum_parts(d), (int)GFs, db1,
                                   accumulate, s);
     });
@@ -342,9 +421,12 @@ size_t tpmlp_quantize_workspace_size(int64_t n) {
   return align_up((size_t)quant_parts(n) * 4, 256);
 }
 
-tpmlp_status tpmlp_quantize_e4m3(int32_t src_dtype, const void* src, int64_t n, uint8_t* dst,
-                                 float* amax_out, float* scale_inv_out, void* ws,
-                                 size_t ws_bytes, hipStream_t s) {
+}  // extern "C"
+
+namespace {
+tpmlp_status quantize_fp8(int32_t src_dtype, const void* src, int64_t n, uint8_t* dst,
+                          float* amax_out, float* scale_inv_out, void* ws, size_t ws_bytes,
+                          hipStream_t s, bool e5m2) {
   if (src_dtype != TPMLP_F32 && src_dtype != TPMLP_BF16) return TPMLP_E_DTYPE;
   if (n < 0) return TPMLP_E_SHAPE;
   if (!amax_out || !scale_inv_out) return TPMLP_E_NULL;
@@ -362,10 +444,25 @@ tpmlp_status tpmlp_quantize_e4m3(int32_t src_dtype, const void* src, int64_t n, 
   });
   if (err != hipSuccess) return hip_fail(err);
   err = timed("quantize", s, [&]() {
-    return quantize_launch(bf, src, n, dst, parts, nparts, amax_out, scale_inv_out, s);
+    return quantize_launch(bf, src, n, dst, parts, nparts, amax_out, scale_inv_out, s, e5m2);
   });
   if (err != hipSuccess) return hip_fail(err);
   return TPMLP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+tpmlp_status tpmlp_quantize_e4m3(int32_t src_dtype, const void* src, int64_t n, uint8_t* dst,
+                                 float* amax_out, float* scale_inv_out, void* ws,
+                                 size_t ws_bytes, hipStream_t s) {
+  return quantize_fp8(src_dtype, src, n, dst, amax_out, scale_inv_out, ws, ws_bytes, s, false);
+}
+
+tpmlp_status tpmlp_quantize_e5m2(int32_t src_dtype, const void* src, int64_t n, uint8_t* dst,
+                                 float* amax_out, float* scale_inv_out, void* ws,
+                                 size_t ws_bytes, hipStream_t s) {
+  return quantize_fp8(src_dtype, src, n, dst, amax_out, scale_inv_out, ws, ws_bytes, s, true);
 }
 
 tpmlp_status tpmlp_timing_enable(int32_t enable, const char* name_filter) {

@@ -63,6 +63,27 @@ __device__ __forceinline__ uint32_t f2e4m3x2(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
 }
 
+// Floats to OCP E5M2 codes, as f2e4m3x2: clamped to +-57344 first (the
+// conversion rounds to nearest even but gives infinity past the largest
+// finite value).
+__device__ __forceinline__ uint32_t f2e5m2x2(float a, float b) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -57344.0f), 57344.0f);
+  b = __builtin_fminf(__builtin_fmaxf(b, -57344.0f), 57344.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false) & 0xffffu;
+}
+// 8 floats to 8 FP8 codes (E4M3, or E5M2 if E5), byte u = code of v[u]
+template <bool E5>
+__device__ __forceinline__ u32x2 pack_fp8x8(const float (&v)[8]) {
+  u32x2 w;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t lo = E5 ? f2e5m2x2(v[4 * q], v[4 * q + 1]) : f2e4m3x2(v[4 * q], v[4 * q + 1]);
+    const uint32_t hi = E5 ? f2e5m2x2(v[4 * q + 2], v[4 * q + 3]) : f2e4m3x2(v[4 * q + 2], v[4 * q + 3]);
+    w[q] = lo | (hi << 16);
+  }
+  return w;
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static constexpr int kBytes = 4;
@@ -132,6 +153,9 @@ __device__ __forceinline__ u32x4 pack_bf16x8(const float (&v)[8]) {
 }
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
 }
 
 // ---------------------------------------------------------------- activations

@@ -9,6 +9,10 @@
 //   EPI_SWIGLU    (gate, up) pair: out2 = [g | u]; out = silu(g) * u
 //   EPI_DGELU     out = acc * gelu'(h[row, col])      (dH)
 //   EPI_DSWIGLU   out[col] = acc * u * silu'(g); out[col + Fs] = acc * silu(g)
+//   EPI_BIAS_GELU_Q  as EPI_BIAS_GELU; out = E4M3 codes of bf16(a) * q_scale
+//   EPI_DGELU_Q   as EPI_DGELU; out = E5M2 codes of dH * q_scale
+// (FP8 codes saturate at the format's largest finite value; the quantising
+// epilogues also fold max |value| into a per-workgroup amax.)
 //
 // The activation is evaluated on h as stored (rounded to the activation type),
 // so the backward pass, which reads the stored h, differentiates exactly the
@@ -26,6 +30,8 @@ enum EpiKind : int {
   EPI_SWIGLU = 3,
   EPI_DGELU = 4,
   EPI_DSWIGLU = 5,
+  EPI_BIAS_GELU_Q = 6,  // EPI_BIAS_GELU, a quantised to E4M3 at *q_scale
+  EPI_DGELU_Q = 7,      // EPI_DGELU, dH quantised to E5M2 at *q_scale
 };
 
 struct GemmArgs {
@@ -44,7 +50,8 @@ struct EpiArgs {
   const void* aux;    int64_t ldaux;  // saved h read by the dgrad epilogues
   const float* scale_a;               // e4m3: dequantisation factors (device)
   const float* scale_b;
-  float* amax_part;                   // e4m3 fc1: per-workgroup max |bf16(a)|
+  float* amax_part;                   // e4m3 fc1 (a) / fc2 dgrad (dH): per-workgroup amax
+  const float* q_scale;               // quantising epilogues: the factor codes are taken at
   float* colsum;                      // fc1 wgrad: column sums of A over k, or null:
                                       //   VALU kernel: db1 itself (written by tile
                                       //   column 0); MFMA kernel: a [tiles_n][M]

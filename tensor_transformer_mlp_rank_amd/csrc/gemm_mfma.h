@@ -135,8 +135,10 @@ struct KMajorLoader {
   }
 };
 
-// MN-major (bf16 only): instruction ii covers k-rows 2 ii, +1; lane l fetches
-// k-row 2 ii + l/32, logical chunk (l%32) ^ mnswz(krow). The resource is
+// MN-major: bf16 instruction ii covers k-rows 2 ii, +1 (512 bytes each); lane
+// l fetches k-row 2 ii + l/32, logical chunk (l%32) ^ mnswz(krow). FP8
+// instruction ii covers k-rows 4 ii .. +3 (256 bytes each); lane l fetches
+// k-row 4 ii + l/16, logical chunk (l%16) ^ mnswz8(krow). The resource is
 // rebased to the stage's first k-row.
 struct MNMajorLoader {
   const char* base;      // element (k=0, m=tile start)
@@ -158,6 +160,10 @@ struct MNMajorLoader {
 // (measured conflict-free).
 __device__ __forceinline__ int kswz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int mnswz(int kr) { return (0xEA40 >> ((kr & 3) << 2)) & 15; }
+// FP8 MN-major k-rows (256 bytes) put chunk c at c ^ 2 (krow % 8): a transpose
+// read takes one 16-byte chunk pair (c, c+1), c even, from 8 consecutive
+// k-rows per half-wave, which land in 16 distinct 16-byte slots.
+__device__ __forceinline__ int mnswz8(int kr) { return (kr & 7) << 1; }
 
 // bf16, K-major tile: lane l takes row row0 + (l&31), k elements
 // 16*ks + 8*(l>>5) .. +7 of the stage.
@@ -211,6 +217,34 @@ __device__ __forceinline__ i32x8 frag_k_e4m3(const char* lds, int row0, int ks, 
   return r;
 }
 
+// FP8 (either format), MN-major tile [128 k-rows][256 bytes]: the operand
+// of frag_k_e4m3 (lane l: column col0 + l%32, k 64 ks + 32 (l/32) .. +31)
+// through four 8-bit transpose reads. ds_read_b64_tr_b8 gives lane j of each
+// 16-lane group byte j%8 of the 8-byte chunks addressed by lanes 2q + j/8
+// (q = 0..7, output byte q), so pointing lane i at k-row kb + i/2, bytes
+// col + 8 (i%2) .. +7 hands lane j the 8 k values kb .. kb+7 of column
+// col + j. Issued through inline asm for the same reason as ds_read_tr16.
+__device__ __forceinline__ u32x2 ds_read_tr8(const char* p) {
+  u32x2 r;
+  const uint32_t a = (uint32_t)(uintptr_t)(const TPMLP_LDS char*)p;
+  asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(r) : "v"(a));
+  return r;
+}
+__device__ __forceinline__ i32x8 frag_mn_fp8(const char* lds, int col0, int ks, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int m = col0 + ((g & 1) << 4);               // 16-byte aligned column of the group
+  i32x8 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int kr = (ks << 6) + ((g >> 1) << 5) + (q << 3) + (i >> 1);
+    const int c = (m >> 4) ^ mnswz8(kr);
+    const u32x2 v = ds_read_tr8(lds + kr * 256 + (c << 4) + ((i & 1) << 3));
+    r[2 * q] = (int)v[0];
+    r[2 * q + 1] = (int)v[1];
+  }
+  return r;
+}
+
 // Wait until at most N of this wave's vector-memory loads are in flight and
 // all its LDS reads are done, then barrier. The wait is the s_waitcnt builtin
 // (so the compiler's own wait tracking knows about it) with vmcnt = N,
@@ -261,7 +295,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e,
   constexpr int kT = kPair ? 4 : 8;         // row groups per lane and slab
   constexpr int kRowStep = kPair ? 8 : 4;   // rows between them
   constexpr int kPre = (EPI == EPI_F32 || EPI == EPI_DSWIGLU) ? 2 : 1;  // 16 B loads per group
-  constexpr int kOes = (EPI == EPI_F32) ? 4 : 2;  // primary output element bytes
+  constexpr bool kQ8 = (EPI == EPI_BIAS_GELU_Q || EPI == EPI_DGELU_Q);  // FP8 codes out
+  constexpr int kOes = (EPI == EPI_F32) ? 4 : kQ8 ? 1 : 2;  // primary output element bytes
   constexpr uint32_t kBf = 2;
   const int wm = wave >> 1, wn = wave & 1;
   float* wl = reinterpret_cast<float*>(smem + wave * 32768);
@@ -274,6 +309,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e,
   const uint32_t oob = (wcol + 8 * cg < g.N) ? 0u : kOOB;
   float alpha = 1.0f;
   if constexpr (IS_FP8) alpha = (*e.scale_a) * (*e.scale_b);
+  float qs = 1.0f;
+  if constexpr (kQ8) qs = *e.q_scale;
 
   // byte offset of group t in a slab resource with `ld` elements of `es` bytes per row
   auto goff = [&](int64_t ld, uint32_t es, int t) __attribute__((always_inline)) -> uint32_t {
@@ -316,7 +353,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e,
   float bias[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) bias[q] = 0.f;
-  if constexpr (EPI == EPI_BIAS_GELU) {
+  if constexpr (EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_Q) {
     if (e.bias) {
       const auto rb = make_rsrc(e.bias, (int64_t)g.N * 2);
       unpack_bf16x8(buf_load16(rb, ((uint32_t)(wcol + 8 * cg) * kBf) | oob), bias);
@@ -362,7 +399,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e,
                                  __float_as_uint(v[2]), __float_as_uint(v[3])});
         buf_store16(ro, o + 16, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]),
                                       __float_as_uint(v[6]), __float_as_uint(v[7])});
-      } else if constexpr (EPI == EPI_BIAS_GELU) {
+      } else if constexpr (EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_Q) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) v[u] += bias[u];
         const u32x4 hw = pack_bf16x8(v);
@@ -370,17 +407,30 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e,
         unpack_bf16x8(hw, v);  // the activation is taken of h as stored
 #pragma unroll
         for (int u = 0; u < 8; ++u) v[u] = gelu_f(v[u]);
-        const u32x4 aw = pack_bf16x8(v);
-        if constexpr (IS_FP8) {
-          // rows past M hold gelu(b1), not activations: leave them out
-          if (oob == 0u && wrow + 32 * fm + rl + kRowStep * t < g.M) {
+        // rows past M hold gelu(b1), not activations: the amax leaves them out
+        const bool row_ok = oob == 0u && wrow + 32 * fm + rl + kRowStep * t < g.M;
+        if constexpr (kQ8) {
+          // codes straight from the fp32 activation, amax of the same values
+          if (row_ok) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[u]));
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] *= qs;
+          buf_store8(ro, goff(e.ldo, 1, t), pack_fp8x8<false>(v));
+        } else {
+          const u32x4 aw = pack_bf16x8(v);
+          if constexpr (IS_FP8) {
+            // amax of a as stored in bf16, the values the quantiser reads
             float ar[8];
             unpack_bf16x8(aw, ar);
+            if (row_ok) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) amax = __builtin_fmaxf(amax, __builtin_fabsf(ar[u]));
+              for (int u = 0; u < 8; ++u) amax = __builtin_fmaxf(amax, __builtin_fabsf(ar[u]));
+            }
           }
+          buf_store16(ro, goff(e.ldo, kBf, t), aw);
         }
-        buf_store16(ro, goff(e.ldo, kBf, t), aw);
       } else if constexpr (EPI == EPI_SWIGLU) {
         float up[8];
 #pragma unroll
@@ -395,12 +445,22 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e,
 #pragma unroll
         for (int u = 0; u < 8; ++u) v[u] = silu_f(v[u]) * up[u];
         buf_store16(ro, goff(e.ldo, kBf, t), pack_bf16x8(v));
-      } else if constexpr (EPI == EPI_DGELU) {
+      } else if constexpr (EPI == EPI_DGELU || EPI == EPI_DGELU_Q) {
         float h[8];
         unpack_bf16x8(pre[s][t][0], h);
 #pragma unroll
         for (int u = 0; u < 8; ++u) v[u] *= gelu_grad_f(h[u]);
-        buf_store16(ro, goff(e.ldo, kBf, t), pack_bf16x8(v));
+        if constexpr (kQ8) {
+          if (oob == 0u && wrow + 32 * fm + rl + kRowStep * t < g.M) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[u]));
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] *= qs;
+          buf_store8(ro, goff(e.ldo, 1, t), pack_fp8x8<true>(v));
+        } else {
+          buf_store16(ro, goff(e.ldo, kBf, t), pack_bf16x8(v));
+        }
       } else if constexpr (EPI == EPI_DSWIGLU) {
         float gt[8], up[8], dg[8];
         unpack_bf16x8(pre[s][t][0], gt);
@@ -419,14 +479,15 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e,
 }
 
 // --------------------------------------------------------------- the kernel
-// IS_FP8: operands are e4m3 (both K-major). A_K / B_K: operand layouts.
-// EPI: epilogue kind. OutT: element type of EPI_STORE's output and of the
-// activation tensors (h, a, dH). COLSUM: also reduce A over k into e.colsum
-// (workgroups with tile column 0 only; A must be MN-major).
-template <bool IS_FP8, bool A_K, bool B_K, int EPI, typename OutT, bool COLSUM>
+// IS_FP8: FP8 operands, A in E5M2 if FMT & 1 else E4M3, B in E5M2 if FMT & 2
+// else E4M3. A_K / B_K: operand layouts. EPI: epilogue kind. OutT: element
+// type of EPI_STORE's output and of the activation tensors (h, a, dH).
+// COLSUM: also reduce A over k into the per-tile-column partial sums
+// e.colsum (A must be MN-major; FP8 sums are scaled by *e.scale_a).
+template <bool IS_FP8, bool A_K, bool B_K, int EPI, typename OutT, bool COLSUM, int FMT = 0>
 __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g, const EpiArgs e) {
   static_assert(!COLSUM || !A_K, "the fused column sum reads an MN-major A tile");
-  static_assert(!IS_FP8 || (A_K && B_K), "e4m3 operands are K-major");
+  static_assert(IS_FP8 || FMT == 0, "formats select FP8 encodings");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   constexpr bool kPair = (EPI == EPI_SWIGLU);
   constexpr int esz = IS_FP8 ? 1 : 2;
@@ -461,9 +522,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     lma.total_bytes = (int64_t)g.K * g.lda * esz - (int64_t)m0 * esz;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int kr = 2 * (wave * 8 + i) + (lane >> 5);
-      const int c = (lane & 31) ^ mnswz(kr);
-      lma.voff[i] = (m0 + (c << 3) < g.M) ? (uint32_t)(kr * lma.ld_bytes) + (uint32_t)(c << 4) : kOOB;
+      // chunk c holds 16 bytes: columns 8c .. (bf16) or 16c .. (FP8)
+      const int kr = IS_FP8 ? 4 * (wave * 8 + i) + (lane >> 4) : 2 * (wave * 8 + i) + (lane >> 5);
+      const int c = IS_FP8 ? (lane & 15) ^ mnswz8(kr) : (lane & 31) ^ mnswz(kr);
+      lma.voff[i] = (m0 + (c << (IS_FP8 ? 4 : 3)) < g.M)
+                        ? (uint32_t)(kr * lma.ld_bytes) + (uint32_t)(c << 4) : kOOB;
     }
   }
   // ---- operand B loader
@@ -505,9 +568,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     lmb.total_bytes = (int64_t)g.K * g.ldb * esz - (int64_t)n0 * esz;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int kr = 2 * (wave * 8 + i) + (lane >> 5);
-      const int c = (lane & 31) ^ mnswz(kr);
-      lmb.voff[i] = (n0 + (c << 3) < g.N) ? (uint32_t)(kr * lmb.ld_bytes) + (uint32_t)(c << 4) : kOOB;
+      const int kr = IS_FP8 ? 4 * (wave * 8 + i) + (lane >> 4) : 2 * (wave * 8 + i) + (lane >> 5);
+      const int c = IS_FP8 ? (lane & 15) ^ mnswz8(kr) : (lane & 31) ^ mnswz(kr);
+      lmb.voff[i] = (n0 + (c << (IS_FP8 ? 4 : 3)) < g.N)
+                        ? (uint32_t)(kr * lmb.ld_bytes) + (uint32_t)(c << 4) : kOOB;
     }
   }
 
@@ -543,9 +607,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // row bn of e.colsum ([tiles_n][M]); a second pass adds up the rows.
   const bool do_colsum = COLSUM && (e.colsum != nullptr);
   int cs_next = bn;  // the next stage this workgroup sums
-  float csum[8];
+  constexpr int kCs = IS_FP8 ? 16 : 8;  // columns per thread
+  float csum[kCs];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) csum[j] = 0.f;
+  for (int j = 0; j < kCs; ++j) csum[j] = 0.f;
 
   // A stage has kKs MFMA k-steps (4 for bf16: 16 elements each; 2 for e4m3:
   // 64 each) of 16 MFMAs. The fragments of k-step ks live in register slot
@@ -555,13 +620,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   Frag fa[kKs][4], fb[kKs][4];
   auto frag_a = [&](int kt, int ks, int f) __attribute__((always_inline)) -> Frag {
     const char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
-    if constexpr (IS_FP8) return frag_k_e4m3(sa, 128 * wm + 32 * f, ks, lane);
+    if constexpr (IS_FP8 && A_K) return frag_k_e4m3(sa, 128 * wm + 32 * f, ks, lane);
+    else if constexpr (IS_FP8) return frag_mn_fp8(sa, 128 * wm + 32 * f, ks, lane);
     else if constexpr (A_K) return frag_k_bf16(sa, 128 * wm + 32 * f, ks, lane);
     else return frag_mn_bf16(sa, 128 * wm + 32 * f, ks, lane);
   };
   auto frag_b = [&](int kt, int ks, int f) __attribute__((always_inline)) -> Frag {
     const char* sb = smem + (kt & (kStages - 1)) * kStageBytes + kTileBytes;
-    if constexpr (IS_FP8) return frag_k_e4m3(sb, 128 * wn + 32 * f, ks, lane);
+    if constexpr (IS_FP8 && B_K) return frag_k_e4m3(sb, 128 * wn + 32 * f, ks, lane);
+    else if constexpr (IS_FP8) return frag_mn_fp8(sb, 128 * wn + 32 * f, ks, lane);
     else if constexpr (B_K) return frag_k_bf16(sb, 128 * wn + 32 * f, ks, lane);
     else return frag_mn_bf16(sb, 128 * wn + 32 * f, ks, lane);
   };
@@ -574,25 +641,43 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     // MFMA i of a stage: k-step i/16, row block (i/4)%4, column block i%4
     const int ks = i >> 4, fm = (i >> 2) & 3, fn = i & 3;
     if constexpr (IS_FP8)
-      acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[ks][fm], fb[ks][fn],
-                                                                    acc[fm][fn], 0, 0, 0, 0, 0, 0);
+      acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          fa[ks][fm], fb[ks][fn], acc[fm][fn], FMT & 1, (FMT >> 1) & 1, 0, 0, 0, 0);
     else
       acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][fm], fb[ks][fn], acc[fm][fn],
                                                             0, 0, 0);
   };
-  // column sums of the A tile of stage kt: thread t adds chunk t%32 of k-rows
-  // t/32 + 8j (j = 0..7)
+  // column sums of the A tile of stage kt: bf16, thread t adds chunk t%32 (8
+  // columns) of k-rows t/32 + 8j; FP8, chunk t%16 (16 columns) of k-rows
+  // t/16 + 16j (j = 0..7); FP8 codes are decoded to floats exactly
   auto colsum_part = [&](int kt, int j, bool on) __attribute__((always_inline)) {
     if constexpr (COLSUM) {
       if (on) {
         const char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
-        const int c = tid & 31;
-        const int kr = (tid >> 5) + 8 * j;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(sa + kr * 512 + ((c ^ mnswz(kr)) << 4));
+        if constexpr (IS_FP8) {
+          const int c = tid & 15;
+          const int kr = (tid >> 4) + 16 * j;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sa + kr * 256 + ((c ^ mnswz8(kr)) << 4));
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          csum[2 * w] += bf2f((bf16_t)(v[w] & 0xffffu));
-          csum[2 * w + 1] += bf2f((bf16_t)(v[w] >> 16));
+          for (int w = 0; w < 4; ++w) {
+            const auto lo = (FMT & 1) ? __builtin_amdgcn_cvt_pk_f32_bf8((int)v[w], false)
+                                      : __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], false);
+            const auto hi = (FMT & 1) ? __builtin_amdgcn_cvt_pk_f32_bf8((int)v[w], true)
+                                      : __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], true);
+            csum[4 * w] += lo[0];
+            csum[4 * w + 1] += lo[1];
+            csum[4 * w + 2] += hi[0];
+            csum[4 * w + 3] += hi[1];
+          }
+        } else {
+          const int c = tid & 31;
+          const int kr = (tid >> 5) + 8 * j;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sa + kr * 512 + ((c ^ mnswz(kr)) << 4));
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            csum[2 * w] += bf2f((bf16_t)(v[w] & 0xffffu));
+            csum[2 * w + 1] += bf2f((bf16_t)(v[w] >> 16));
+          }
         }
       }
     }
@@ -683,6 +768,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   //   group 1   reads of stage kt+1's k-step 0; loads 0..7 of stage kt+2
   //   group 2   reads of stage kt+1's k-step 1; loads 8..15 of stage kt+2
   //   group 3   reads of stage kt+1's k-step 2
+  // FP8 (two k-steps of 64): group 0 reads stage kt's k-step 1; group 1
+  // reads stage kt+1's k-step 0 and issues the 16 loads of stage kt+2.
+  constexpr int kDmaStride = IS_FP8 ? 1 : 2;  // slots per load from slot 16 on
   auto stage_iter_rolling = [&](int kt) __attribute__((always_inline)) {
     // transpose reads (asm, not tracked by the compiler) of the previous
     // stage must have landed before their first use here
@@ -690,15 +778,16 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     const bool cs_on = do_colsum && kt == cs_next;
     if (cs_on) cs_next += g.tiles_n;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
+    for (int i = 0; i < kMma; ++i) {
       mma(i);
       const int grp = i >> 4, r = i & 15;
       if ((r & 1) == 0) {
-        if (grp == 0) read_one(kt, 3, r >> 1);
+        if (grp == 0) read_one(kt, kKs - 1, r >> 1);
         else read_one(kt + 1, grp - 1, r >> 1);
       }
       if (COLSUM && grp == 0 && (i & 1)) colsum_part(kt, (i >> 1) & 7, cs_on);
-      if ((grp == 1 || grp == 2) && (r & 1)) issue_one(kt + kStages, (i - 16) >> 1);
+      if (i >= 16 && i < 16 + 16 * kDmaStride && (i - 16) % kDmaStride == kDmaStride - 1)
+        issue_one(kt + kStages, (i - 16) / kDmaStride);
       __builtin_amdgcn_sched_barrier(0);
       if (i == 15) wait_and_barrier<0>();
     }
@@ -709,16 +798,16 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   issue(1);
   wait_and_barrier<16>();
   // The rolling schedule pays off where a transpose-read operand makes the
-  // reads costly (twice the read instructions); with two K-major operands
-  // the quarter schedule measured slightly faster.
-  constexpr bool kRolling = !IS_FP8 && (!A_K || !B_K);
+  // reads costly (twice the read instructions per byte); with two K-major
+  // operands the quarter schedule measured slightly faster.
+  constexpr bool kRolling = !A_K || !B_K;
   if constexpr (!kRolling) {
 #pragma unroll
     for (int j = 0; j < kReadsQ; ++j) read_one(0, j / 8, j & 7);
     for (int kt = 0; kt < nk; ++kt) stage_iter(kt);
   } else {
 #pragma unroll
-    for (int j = 0; j < 24; ++j) read_one(0, j / 8, j & 7);
+    for (int j = 0; j < 8 * (kKs - 1); ++j) read_one(0, j / 8, j & 7);
     for (int kt = 0; kt < nk; ++kt) stage_iter_rolling(kt);
   }
 
@@ -726,14 +815,18 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   if constexpr (COLSUM) {
     if (do_colsum) {
       __syncthreads();  // all waves are done with the stage buffers
-      float* red = reinterpret_cast<float*>(smem);  // 8 x 256 floats
+      // 8 (bf16) or 16 (FP8) groups of 256 column sums
+      constexpr int kGroups = IS_FP8 ? 16 : 8;
+      float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) red[(tid >> 5) * 256 + ((tid & 31) << 3) + j] = csum[j];
+      for (int j = 0; j < kCs; ++j)
+        red[(tid / (256 / kGroups)) * 256 + (tid % (256 / kGroups)) * kCs + j] = csum[j];
       __syncthreads();
       const int m = m0 + tid;
       float s = 0.f;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) s += red[q * 256 + tid];
+      for (int q = 0; q < kGroups; ++q) s += red[q * 256 + tid];
+      if constexpr (IS_FP8) s *= *e.scale_a;
       if (m < g.M) e.colsum[(int64_t)bn * g.M + m] = s;
     }
   }
@@ -746,10 +839,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     else
       store_tile<IS_FP8, EPI, OutT, false>(g, e, acc, smem, wave, lane, m0, n0, amax);
   } else {
-    constexpr bool kLoads = (EPI == EPI_DGELU || EPI == EPI_DSWIGLU);
+    constexpr bool kLoads = (EPI == EPI_DGELU || EPI == EPI_DSWIGLU || EPI == EPI_DGELU_Q);
     store_tile<IS_FP8, EPI, OutT, kLoads>(g, e, acc, smem, wave, lane, m0, n0, amax);
   }
-  if constexpr (IS_FP8 && EPI == EPI_BIAS_GELU) {
+  if constexpr (IS_FP8 && (EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_Q || EPI == EPI_DGELU_Q)) {
     amax = wave_max(amax);
     __shared__ float wmax[4];
     if (lane == 0) wmax[wave] = amax;

@@ -103,16 +103,26 @@ hipError_t amax_partial_launch(bool src_bf16, const void* src, int64_t n, float*
 
 hipError_t quantize_launch(bool src_bf16, const void* src, int64_t n, uint8_t* dst,
                            const float* partial, int nparts, float* amax_out,
-                           float* scale_inv_out, hipStream_t s) {
+                           float* scale_inv_out, hipStream_t s, bool e5m2) {
   const int nb = quant_parts(n) * 4 > 4096 ? 4096 : quant_parts(n) * 4;
-  if (src_bf16)
-    hipLaunchKernelGGL(quantize_kernel<bf16_t>, dim3(nb), dim3(kQuantThreads), 0, s,
-                       static_cast<const bf16_t*>(src), n, dst, partial, nparts, amax_out,
-                       scale_inv_out);
-  else
-    hipLaunchKernelGGL(quantize_kernel<float>, dim3(nb), dim3(kQuantThreads), 0, s,
-                       static_cast<const float*>(src), n, dst, partial, nparts, amax_out,
-                       scale_inv_out);
+  auto go = [&](auto kernel, const auto* p) {
+    hipLaunchKernelGGL(kernel, dim3(nb), dim3(kQuantThreads), 0, s, p, n, dst, partial, nparts,
+                       amax_out, scale_inv_out);
+  };
+  if (src_bf16) {
+    const bf16_t* p = static_cast<const bf16_t*>(src);
+    if (e5m2) go(quantize_kernel<bf16_t, true>, p); else go(quantize_kernel<bf16_t, false>, p);
+  } else {
+    const float* p = static_cast<const float*>(src);
+    if (e5m2) go(quantize_kernel<float, true>, p); else go(quantize_kernel<float, false>, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t delayed_update_launch(const float* partial, int nparts, float* history, int len,
+                                 float* scale, float* scale_inv, bool e5m2, hipStream_t s) {
+  hipLaunchKernelGGL(delayed_update_kernel, dim3(1), dim3(kQuantThreads), 0, s, partial, nparts,
+                     history, len, scale, scale_inv, e5m2 ? 57344.0f : 448.0f);
   return hipGetLastError();
 }
 

@@ -6,9 +6,9 @@ namespace tpmlp {
 
 namespace {
 
-template <bool IS_FP8, bool A_K, bool B_K, int EPI, bool COLSUM>
+template <bool IS_FP8, bool A_K, bool B_K, int EPI, bool COLSUM, int FMT = 0>
 hipError_t launch_one(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
-  auto* k = &gemm_mfma_kernel<IS_FP8, A_K, B_K, EPI, bf16_t, COLSUM>;
+  auto* k = &gemm_mfma_kernel<IS_FP8, A_K, B_K, EPI, bf16_t, COLSUM, FMT>;
   // the LDS allowance is raised once per instantiation and device
   static bool attr_set[64] = {};
   int dev = 0;
@@ -40,9 +40,17 @@ int mfma_grid(Step step, GemmArgs& g) {
 
 hipError_t mfma_launch(bool fp8, Step step, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
   if (fp8) {
+    // forward: e4m3 x e4m3; backward: e5m2 gradient (A) x e4m3 (B)
+    constexpr int kA5 = 1;
     switch (step) {
       case FC1_FWD_GELU: return launch_one<true, true, true, EPI_BIAS_GELU, false>(g, e, s);
+      case FC1_FWD_GELU_Q: return launch_one<true, true, true, EPI_BIAS_GELU_Q, false>(g, e, s);
       case FC2_FWD: return launch_one<true, true, true, EPI_STORE, false>(g, e, s);
+      case FC2_DGRAD_GELU_Q:
+        return launch_one<true, true, false, EPI_DGELU_Q, false, kA5>(g, e, s);
+      case FC1_DGRAD: return launch_one<true, true, false, EPI_STORE, false, kA5>(g, e, s);
+      case WGRAD: return launch_one<true, false, false, EPI_F32, false, kA5>(g, e, s);
+      case WGRAD_COLSUM: return launch_one<true, false, false, EPI_F32, true, kA5>(g, e, s);
       default: return hipErrorInvalidValue;
     }
   }

@@ -10,7 +10,7 @@ namespace tpmlp {
 // The GEMM steps of the block; each maps to one kernel instantiation per
 // element type.
 enum Step : int {
-  FC1_FWD_GELU = 0,   // x . W1^T, bias + GELU, saves h, writes a
+  FC1_FWD_GELU = 0,   // x . W1^T, bias + GELU, saves h, writes a (e4m3: bf16 a + amax)
   FC1_FWD_SWIGLU,     // x . W1^T (gate/up pairs), SiLU(g) * u, saves h, writes a
   FC2_FWD,            // a . W2^T -> y_partial
   FC2_DGRAD_GELU,     // dy . W2, times gelu'(h) -> dH
@@ -18,6 +18,8 @@ enum Step : int {
   FC1_DGRAD,          // dH . W1 -> dx_partial
   WGRAD,              // A^T . B over tokens -> fp32 (dW2, or dW1 without bias)
   WGRAD_COLSUM,       // same, plus column sums of A (dW1 and db1)
+  FC1_FWD_GELU_Q,     // e4m3: as FC1_FWD_GELU, a quantised to e4m3 in the epilogue
+  FC2_DGRAD_GELU_Q,   // e4m3 weights, e5m2 dy: dH quantised to e5m2 in the epilogue
   kNumSteps
 };
 
@@ -43,6 +45,11 @@ hipError_t amax_partial_launch(bool src_bf16, const void* src, int64_t n, float*
                                int nparts, hipStream_t stream);
 hipError_t quantize_launch(bool src_bf16, const void* src, int64_t n, uint8_t* dst,
                            const float* partial, int nparts, float* amax_out,
-                           float* scale_inv_out, hipStream_t stream);
+                           float* scale_inv_out, hipStream_t stream, bool e5m2 = false);
+// One step of delayed scaling from per-workgroup amax partials (E4M3 or E5M2
+// largest finite value); history has len entries, newest first.
+constexpr int kMaxHistoryLen = 4096;
+hipError_t delayed_update_launch(const float* partial, int nparts, float* history, int len,
+                                 float* scale, float* scale_inv, bool e5m2, hipStream_t stream);
 
 }  // namespace tpmlp

@@ -65,11 +65,13 @@ __global__ void __launch_bounds__(kQuantThreads) amax_partial_kernel(const SrcT*
   }
 }
 
-template <typename SrcT>
+// E5: quantise to OCP E5M2 (largest finite 57344) instead of E4M3 (448).
+template <typename SrcT, bool E5>
 __global__ void __launch_bounds__(kQuantThreads) quantize_kernel(const SrcT* src, int64_t n,
                                                                  uint8_t* dst, const float* partial,
                                                                  int nparts, float* amax_out,
                                                                  float* scale_inv_out) {
+  constexpr float kFmax = E5 ? 57344.0f : 448.0f;
   // every workgroup reduces the partials identically
   float m = 0.f;
   for (int p = threadIdx.x; p < nparts; p += kQuantThreads) m = __builtin_fmaxf(m, partial[p]);
@@ -79,7 +81,7 @@ __global__ void __launch_bounds__(kQuantThreads) quantize_kernel(const SrcT* src
   __syncthreads();
   float amax = 0.f;
   for (int w = 0; w < kQuantThreads / 64; ++w) amax = __builtin_fmaxf(amax, wm[w]);
-  const float scale = (amax > 0.f && amax <= 3.4028234663852886e38f) ? 448.0f / amax : 1.0f;
+  const float scale = (amax > 0.f && amax <= 3.4028234663852886e38f) ? kFmax / amax : 1.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     *amax_out = amax;
     *scale_inv_out = 1.0f / scale;
@@ -89,14 +91,58 @@ __global__ void __launch_bounds__(kQuantThreads) quantize_kernel(const SrcT* src
        i += stride) {
     float v[8];
     load8(src, i, n, v);
-    uint32_t lo = f2e4m3x2(v[0] * scale, v[1] * scale) | (f2e4m3x2(v[2] * scale, v[3] * scale) << 16);
-    uint32_t hi = f2e4m3x2(v[4] * scale, v[5] * scale) | (f2e4m3x2(v[6] * scale, v[7] * scale) << 16);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] *= scale;
+    const u32x2 w = pack_fp8x8<E5>(v);
+    const uint32_t lo = w[0], hi = w[1];
     if (i + 8 <= n) {
       *reinterpret_cast<u32x2*>(dst + i) = u32x2{lo, hi};
     } else {
       for (int q = 0; q < 8 && i + q < n; ++q)
         dst[i + q] = (uint8_t)(((q < 4 ? lo : hi) >> (8 * (q & 3))) & 0xffu);
     }
+  }
+}
+
+// One step of delayed scaling of a tensor whose per-workgroup amaxes are in
+// partial[0 .. nparts): amax = their maximum; history <- [amax, history[0 ..
+// len-2]] (newest first); *scale_inv = 1 / *scale (the factor the tensor was
+// quantised with); *scale <- fmax / max(history), kept while that maximum is
+// 0 or not finite. One workgroup, all float32; max is exact, so the result
+// does not depend on the order of the partials.
+constexpr int kMaxHistory = 4096;
+__global__ void __launch_bounds__(kQuantThreads) delayed_update_kernel(const float* partial,
+                                                                       int nparts, float* history,
+                                                                       int len, float* scale,
+                                                                       float* scale_inv,
+                                                                       float fmax) {
+  __shared__ float old[kMaxHistory];
+  __shared__ float wm[kQuantThreads / 64];
+  float m = 0.f;
+  for (int p = threadIdx.x; p < nparts; p += kQuantThreads) m = __builtin_fmaxf(m, partial[p]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  for (int i = threadIdx.x; i < len; i += kQuantThreads) old[i] = history[i];
+  __syncthreads();
+  float amax = 0.f;
+  for (int w = 0; w < kQuantThreads / 64; ++w) amax = __builtin_fmaxf(amax, wm[w]);
+  __syncthreads();  // every wave has read wm
+  float hm = 0.f;
+  for (int i = threadIdx.x; i < len; i += kQuantThreads) {
+    const float v = i == 0 ? amax : old[i - 1];
+    history[i] = v;
+    hm = __builtin_fmaxf(hm, v);
+  }
+  // max |.| of a history that may hold infinities: fmax ignores NaN only
+  hm = wave_max(hm);
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = hm;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float hmax = 0.f;
+    for (int w = 0; w < kQuantThreads / 64; ++w) hmax = __builtin_fmaxf(hmax, wm[w]);
+    const float used = *scale;
+    *scale_inv = 1.0f / used;
+    *scale = (hmax > 0.f && hmax <= 3.4028234663852886e38f) ? fmax / hmax : used;
   }
 }
 

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert tp.lib.tpmlp_abi_version() == 2
+    assert tp.lib.tpmlp_abi_version() == 3
     for s in range(8):
         assert len(tp.lib.tpmlp_strerror(s)) > 5
     assert tp.lib.tpmlp_last_hip_error() == b""
@@ -42,13 +42,15 @@ def fwd(desc, x=P, W1=P, b1=P, W2=P, y=P, h=P, a=P, fp8=None, ws=None, nbytes=0)
     return tp.lib.tpmlp_fwd(d, x, W1, b1, W2, y, h, a, sc, ws, nbytes, None)
 
 
-def dgrad(desc, dy=P, W1=P, W2=P, h=P, dH=P, dx=P):
-    return tp.lib.tpmlp_bwd_dgrad(ctypes.byref(desc), dy, W1, W2, h, dH, dx, None, 0, None)
+def dgrad(desc, dy=P, W1=P, W2=P, h=P, dH=P, dx=P, fp8=None, ws=None, nbytes=0):
+    sc = None if fp8 is None else ctypes.byref(fp8)
+    return tp.lib.tpmlp_bwd_dgrad(ctypes.byref(desc), dy, W1, W2, h, dH, dx, sc, ws, nbytes, None)
 
 
-def wgrad(desc, dy=P, x=P, a=P, dH=P, dW1=P, db1=P, dW2=P, acc=0):
-    return tp.lib.tpmlp_bwd_wgrad(ctypes.byref(desc), dy, x, a, dH, dW1, db1, dW2, acc, None, 0,
-                                  None)
+def wgrad(desc, dy=P, x=P, a=P, dH=P, dW1=P, db1=P, dW2=P, acc=0, fp8=None, ws=None, nbytes=0):
+    sc = None if fp8 is None else ctypes.byref(fp8)
+    return tp.lib.tpmlp_bwd_wgrad(ctypes.byref(desc), dy, x, a, dH, dW1, db1, dW2, acc, sc, ws,
+                                  nbytes, None)
 
 
 def D(**kw):
@@ -96,18 +98,59 @@ def test_fp8_rules():
     assert fwd(d8) == E_NULL                           # scales required
     assert fwd(D(), fp8=sc) == E_DTYPE                 # scales only for e4m3
     assert fwd(d8, fp8=tp.Fp8Scales(P, None, P, P, P)) == E_NULL
+    assert fwd(d8, fp8=tp.Fp8Scales(P, P, P, None, P)) == E_NULL   # current scaling: amax out
     need = tp.workspace_size(d8, tp.CALL_FWD)
     assert need >= 64 * 128 * 2
     assert fwd(d8, fp8=sc) == E_WS
     assert fwd(d8, fp8=sc, ws=P, nbytes=need - 1) == E_WS
     assert fwd(d8, fp8=sc, ws=MIS, nbytes=need) == E_ALIGN
-    assert dgrad(d8) == E_UNSUP
-    assert wgrad(d8) == E_UNSUP
+    assert dgrad(d8) == E_NULL                         # fp8 scales required
+    assert wgrad(d8) == E_NULL
+    assert dgrad(D(), fp8=sc) == E_DTYPE
+    assert wgrad(D(), fp8=sc) == E_DTYPE
+    assert fwd(D(dtype="e4m3", act="swiglu", has_bias=False), fp8=sc) == E_UNSUP
+
+
+def _hist(length=4, reserved=0, ptrs=True):
+    return tp.Fp8History(P if ptrs else None, P, P, length, reserved)
+
+
+def test_fp8_delayed_and_backward_rules():
+    d8 = D(dtype="e4m3")
+    h = _hist()
+    # forward with delayed scaling: no amax output needed; the history is checked
+    ok_fwd = tp.Fp8Scales(P, P, P, None, None, ctypes.pointer(h))
+    need = tp.workspace_size(d8, tp.CALL_FWD)
+    assert fwd(d8, fp8=ok_fwd) == E_WS                 # passes validation up to the workspace
+    for bad in (_hist(0), _hist(4097), _hist(4, reserved=1)):
+        sc = tp.Fp8Scales(P, P, P, None, None, ctypes.pointer(bad))
+        assert fwd(d8, fp8=sc, ws=P, nbytes=need) == E_SHAPE
+    sc = tp.Fp8Scales(P, P, P, None, None, ctypes.pointer(_hist(ptrs=False)))
+    assert fwd(d8, fp8=sc, ws=P, nbytes=need) == E_NULL
+    # dgrad: dy, W1, W2 scales and the dH history are required; workspace = amax partials
+    need_d = tp.workspace_size(d8, tp.CALL_DGRAD)
+    assert need_d >= 4
+    full = dict(x_scale_inv=None, w1_scale_inv=P, w2_scale_inv=P, a_amax=None, a_scale_inv=None,
+                a_history=None, dy_scale_inv=P, dH_history=ctypes.pointer(h), dH_scale_inv=None)
+    assert dgrad(d8, fp8=tp.Fp8Scales(**full)) == E_WS
+    assert dgrad(d8, fp8=tp.Fp8Scales(**full), ws=P, nbytes=need_d - 1) == E_WS
+    for k in ("w1_scale_inv", "w2_scale_inv", "dy_scale_inv", "dH_history"):
+        assert dgrad(d8, fp8=tp.Fp8Scales(**dict(full, **{k: None})), ws=P, nbytes=need_d) == E_NULL
+    bad = ctypes.pointer(_hist(0))
+    assert dgrad(d8, fp8=tp.Fp8Scales(**dict(full, dH_history=bad)), ws=P, nbytes=need_d) == E_SHAPE
+    # wgrad: dy, x, a, dH scales are required
+    need_w = tp.workspace_size(d8, tp.CALL_WGRAD)
+    assert need_w == 1 * 128 * 4                       # db1 partials, as for bf16
+    wfull = dict(x_scale_inv=P, a_scale_inv=P, dy_scale_inv=P, dH_scale_inv=P)
+    assert wgrad(d8, fp8=tp.Fp8Scales(**wfull)) == E_WS
+    for k in wfull:
+        assert wgrad(d8, fp8=tp.Fp8Scales(**dict(wfull, **{k: None})), ws=P, nbytes=need_w) == E_NULL
 
 
 def test_workspace_sizes():
     assert tp.workspace_size(D(), tp.CALL_FWD) == 0
     assert tp.workspace_size(D(), tp.CALL_DGRAD) == 0
+    assert tp.workspace_size(D(dtype="e4m3"), tp.CALL_DGRAD) == 256  # one amax partial, padded
     # bf16 wgrad with bias: one fp32 row of db1 partials per 256-column tile of H
     assert tp.workspace_size(D(), tp.CALL_WGRAD) == 1 * 128 * 4
     assert tp.workspace_size(D(hidden=4096, ffn_shard=1000 - 1000 % 16), tp.CALL_WGRAD) == \
@@ -137,7 +180,7 @@ def test_wgrad_bias_and_flag():
 
 def test_wgrad_workspace():
     need = tp.workspace_size(D(), tp.CALL_WGRAD)
-    args = (ctypes.byref(D()), P, P, P, P, P, P, P, 0)
+    args = (ctypes.byref(D()), P, P, P, P, P, P, P, 0, None)
     assert tp.lib.tpmlp_bwd_wgrad(*args, None, 0, None) == E_WS
     assert tp.lib.tpmlp_bwd_wgrad(*args, P, need - 1, None) == E_WS
     assert tp.lib.tpmlp_bwd_wgrad(*args, MIS, need, None) == E_ALIGN

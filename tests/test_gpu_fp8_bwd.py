@@ -1,0 +1,298 @@
+"""GPU parity of the FP8 backward and of delayed scaling (OCP E4M3 forward
+tensors, OCP E5M2 gradients).
+
+* The E5M2 quantiser is bit-exact against the oracle's encoder (same float32
+  product v * scale decides the code).
+* Delayed scaling: the history rolls, the call quantises with the scale it
+  was given and reports 1 / that scale, and the next scale follows
+  fmax / max(history).
+* The FP8 block forward + dgrad + wgrad runs through the C ABI on codes the
+  GPU quantiser produced (first checked equal to the oracle's own) and is
+  compared with the oracle's FP8 block on the dequantised inputs, which
+  quantises a (E4M3) and dH (E5M2) at the same given scales.
+
+The codes of a and dH are decided by floating point on both sides, from a
+float32 product sum on the device and a float64 one in the oracle, so a
+value that falls within that difference of a rounding boundary may take
+either neighbour. Such codes are checked for validity: every device code
+must be the rounding of some value within delta of the oracle's exact
+value, delta being a bound on the device's arithmetic error (for a product
+sum, 1.5e-4 of the largest |sum|: the FP8 matrix instructions do not sum
+exactly in float32); every code whose value is not that close to a boundary
+is then equal to the oracle's. The same holds for h at bf16. Tensors computed from
+identical FP8 inputs (the weight gradients given the oracle's codes) are
+held to 1e-4 of max |oracle| (float32 accumulation only); tensors after a
+quantised intermediate to 6e-2."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _gpu_helpers import TOL, rel_err, require_gpu, say
+from oracle.fp8_block import round_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tp():
+    require_gpu()
+    import tensor_transformer_mlp_rank_amd as m
+    return m
+
+
+def _f32(x):
+    return np.float32(x)
+
+
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [1, 1000, 65537, 2 * 1024 * 1024 + 3])
+def test_e5m2_quantizer_bit_exact(tp, src, n):
+    rng = np.random.default_rng(n + 11)
+    v = (rng.standard_normal(n) * rng.choice([1e-4, 0.05, 30.0], size=n)).astype(np.float32)
+    if n > 5000:
+        # grid points, ties and their neighbours in the scaled domain
+        grid = oracle.e5m2_decode(np.arange(256, dtype=np.uint8))
+        grid = np.unique(grid[np.isfinite(grid)])
+        mids = ((grid[1:] + grid[:-1]) / 2).astype(np.float32)
+        sp = np.concatenate([grid.astype(np.float32), mids, np.nextafter(mids, np.float32(np.inf))])
+        v[: sp.size] = (sp / 57344.0 * float(np.max(np.abs(v)))).astype(np.float32)
+    t = torch.from_numpy(v)
+    if src == "bf16":
+        t = t.to(torch.bfloat16)
+    say(f"quantize e5m2 src={src} n={n}")
+    codes, amax, sinv = tp.quantize_e5m2(t.cuda())
+    torch.cuda.synchronize()
+    vv = t.float().numpy()
+    ramax = _f32(np.max(np.abs(vv)))
+    rs = _f32(_f32(57344.0) / ramax)
+    assert float(amax.cpu()[0]) == float(ramax)
+    assert float(sinv.cpu()[0]) == float(_f32(_f32(1.0) / rs))
+    rc = oracle.quantize(vv, "e5m2", rs)
+    got = codes.cpu().numpy()
+    mism = np.nonzero(got != rc)[0]
+    assert mism.size == 0, f"{mism.size} codes differ, first at {mism[:5]}"
+
+
+def _quantized_inputs(tp, inp, with_dy=True):
+    """GPU codes of x, W1, W2 (E4M3) and dy (E5M2), each checked equal to the
+    oracle's; returns (device codes and scale_inv tensors, dequantised f64)."""
+    dev, deq = {}, {}
+    fmts = {"x": "e4m3", "W1": "e4m3", "W2": "e4m3"}
+    if with_dy:
+        fmts["dy"] = "e5m2"
+    for k, fmt in fmts.items():
+        v = inp[k].float()
+        codes, amax, sinv = tp.quantize_e4m3(v.cuda(), e5m2=(fmt == "e5m2"))
+        vv = v.numpy()
+        s = _f32(_f32(oracle.FMAX[fmt]) / _f32(np.max(np.abs(vv))))
+        rc = oracle.quantize(vv, fmt, s)
+        torch.cuda.synchronize()
+        assert np.array_equal(codes.cpu().numpy(), rc), k
+        assert float(sinv.cpu()[0]) == float(_f32(_f32(1.0) / s)), k
+        dev[k] = (codes, sinv)
+        deq[k] = oracle.dequantize(rc, fmt, _f32(_f32(1.0) / s))
+    return dev, deq
+
+
+def _scale_for(amax, fmt):
+    return _f32(_f32(oracle.FMAX[fmt]) / _f32(amax))
+
+
+# Error bounds for device results that decide a rounding. The FP8 matrix
+# instructions do not sum their products exactly in float32: measured against
+# exact sums, their results carry errors up to about 3e-5 of the largest
+# |result| of a product (5e-5 with heavy-tailed inputs), some hundred float32
+# ulps, so the bound on a product sum is 1.5e-4 of the largest |sum| in its
+# tensor; on the float32 activation arithmetic after it, 1e-5 of the value.
+SUM_ERR, REL_ERR = 1.5e-4, 1e-5
+EXACT_TOL = 1e-4     # products of identical FP8 inputs, against max |oracle|
+
+
+def _valid_rounding(got, t, d, rnd):
+    """got lies between rnd(t - d) and rnd(t + d): the rounding (monotone)
+    of some value within d of t."""
+    return (got >= rnd(t - d)) & (got <= rnd(t + d))
+
+
+def _check_codes(name, codes_dev, t, d, fmt, ref_codes):
+    """Device FP8 codes against the exact scaled values t (float64) within
+    delta d; reports how many differ from the oracle's own codes."""
+    got = oracle.dequantize(codes_dev.cpu().numpy(), fmt, 1.0)
+    rnd = lambda v: oracle.dequantize(oracle.quantize(v, fmt, 1.0), fmt, 1.0)
+    ok = _valid_rounding(got, t, d, rnd)
+    n_diff = int(np.count_nonzero(codes_dev.cpu().numpy() != ref_codes))
+    say(f"    {name}: {n_diff} of {ref_codes.size} codes are the other neighbour")
+    bad = np.argwhere(~ok)
+    assert bad.size == 0, (name, bad[:5].tolist(), got[~ok][:5], t[~ok][:5])
+    assert n_diff <= max(8, ref_codes.size // 20), (name, n_diff)
+
+
+def _amax(v):
+    return float(np.max(np.abs(v), initial=0.0))
+
+
+def _check_h(h_dev, h_exact):
+    """Stored h (bf16) against the oracle's exact h; returns the bf16 values
+    either side of the oracle's range [lo, hi], for the next tolerance."""
+    d = REL_ERR * np.abs(h_exact) + SUM_ERR * _amax(h_exact)
+    lo, hi = round_bf16(h_exact - d), round_bf16(h_exact + d)
+    got = oracle.to_f64(h_dev.cpu())
+    ok = (got >= lo) & (got <= hi)
+    assert np.all(ok), (np.argwhere(~ok)[:5].tolist(), got[~ok][:5], h_exact[~ok][:5])
+    return lo, hi
+
+
+def _a_delta(rf, lo, hi):
+    """delta for a (unscaled): float32 error of gelu and, where h may take
+    another bf16 value in [lo, hi], gelu's change across them (|gelu'| <
+    1.13)."""
+    a = rf["a"]
+    return REL_ERR * np.abs(a) + 1e-6 * _amax(a) + 1.13 * (hi - lo)
+
+
+def _dH_delta(rg, lo, hi):
+    """delta for dH (unscaled): the product sum dA's error through gelu'
+    (|gelu'| < 1.13), the float32 error of the product, and, where h may
+    take another bf16 value in [lo, hi], gelu' across them."""
+    dA = rg["dA"]
+    d = REL_ERR * np.abs(rg["dH"]) + 1.13 * SUM_ERR * _amax(dA)
+    return d + np.abs(dA) * np.abs(oracle.gelu_tanh_grad(hi) - oracle.gelu_tanh_grad(lo))
+
+
+def test_delayed_scaling_forward_two_calls(tp):
+    """Two forward calls with a history of 3: each quantises a at the scale it
+    is given, reports 1 / that scale, rolls the history and sets the next
+    scale from it; outputs match the oracle's FP8 block at those scales."""
+    T, H, Fs = 300, 528, 272
+    w = synth.WORKLOADS[5]
+    inp = synth.make_rank_inputs(w, tokens=T, hidden=H, ffn_shard=Fs, seed_base=710)
+    dev, deq = _quantized_inputs(tp, inp, with_dy=False)
+    b1 = oracle.to_f64(inp["b1"])
+    ref0 = oracle.rank_forward(deq["x"], deq["W1"], b1, deq["W2"], "gelu")
+    amax_ref = float(np.max(np.abs(ref0["a"])))
+    hist = tp.DelayedScaling(3, scale=float(_scale_for(amax_ref, "e4m3") / 2))
+    prior = np.array([0.5, 0.25, 0.125], np.float32)          # earlier amaxes
+    hist.amax_history.copy_(torch.from_numpy(prior))
+    desc = tp.make_desc(T, H, Fs, act="gelu", dtype="e4m3", has_bias=True)
+    scales = (dev["x"][1], dev["W1"][1], dev["W2"][1])
+    for call in range(2):
+        s_in = _f32(hist.scale.cpu()[0])
+        h_before = hist.amax_history.cpu().numpy().copy()
+        say(f"  delayed forward call {call}: scale {float(s_in):.6g}")
+        out = tp.fwd(desc, dev["x"][0], dev["W1"][0], inp["b1"].cuda(), dev["W2"][0],
+                     fp8_in_scales=scales, a_history=hist)
+        torch.cuda.synchronize()
+        h_after = hist.amax_history.cpu().numpy()
+        s_out = _f32(hist.scale.cpu()[0])
+        sinv = _f32(hist.scale_inv.cpu()[0])
+        ref = oracle.rank_forward_fp8(deq["x"], deq["W1"], b1, deq["W2"], s_in)
+        # the history rolled and took this call's amax
+        assert np.array_equal(h_after[1:], h_before[:-1])
+        # 1 / the factor used; the next factor from the whole history
+        assert sinv == _f32(_f32(1.0) / s_in)
+        assert s_out == _f32(_f32(448.0) / _f32(np.max(h_after)))
+        lo, hi = _check_h(out["h"], ref["h_exact"])
+        da = _a_delta(ref, lo, hi)
+        _check_codes("a", out["a"], ref["a"] * float(s_in), da * float(s_in), "e4m3", ref["a_codes"])
+        assert abs(float(h_after[0]) - ref["amax"]) <= float(np.max(da))
+        e_y = rel_err(out["y"].cpu(), ref["y"])
+        say(f"    rel error y={e_y:.2e}")
+        assert e_y <= TOL["e4m3"]
+
+
+def _fp8_block(tp, T, H, Fs, seed, prior=False):
+    """Each entry point on the oracle's own inputs (forward on the quantised
+    x, W1, W2; dgrad also on the oracle's stored h; wgrad on the oracle's
+    codes of a and dH), then the three chained on the device's own outputs,
+    as a training step runs them."""
+    w = synth.WORKLOADS[5]
+    inp = synth.make_rank_inputs(w, tokens=T, hidden=H, ffn_shard=Fs, seed_base=seed)
+    dev, deq = _quantized_inputs(tp, inp)
+    b1 = oracle.to_f64(inp["b1"])
+    # the scales a and dH are quantised with (given to both sides): from the
+    # plain block's amaxes, halved, so that the test also covers codes that
+    # are not at the top of the range
+    f0 = oracle.rank_forward(deq["x"], deq["W1"], b1, deq["W2"], "gelu")
+    g0 = oracle.rank_dgrad(deq["dy"], deq["W1"], deq["W2"], f0["h"], "gelu")
+    a_scale = _f32(_scale_for(np.max(np.abs(f0["a"])), "e4m3") / 2)
+    dH_scale = _f32(_scale_for(np.max(np.abs(g0["dH"])), "e5m2") / 2)
+    a_sinv, dH_sinv = _f32(_f32(1.0) / a_scale), _f32(_f32(1.0) / dH_scale)
+    rf = oracle.rank_forward_fp8(deq["x"], deq["W1"], b1, deq["W2"], a_scale)
+    rg = oracle.rank_dgrad_fp8(deq["dy"], deq["W1"], deq["W2"], rf["h"], dH_scale)
+    pr = None
+    if prior:
+        pr = {"dW1": synth.grad_init(5, (Fs, H), 1), "db1": synth.grad_init(5, (Fs,), 2),
+              "dW2": synth.grad_init(5, (H, Fs), 3)}
+    prior_args = () if pr is None else tuple(pr[k].double().numpy() for k in ("dW1", "db1", "dW2"))
+    rw = oracle.rank_wgrad_fp8(deq["dy"], deq["x"], rf["a_q"], rg["dH_q"], *prior_args)
+    desc = tp.make_desc(T, H, Fs, act="gelu", dtype="e4m3", has_bias=True)
+    fp8_fwd = (dev["x"][1], dev["W1"][1], dev["W2"][1])
+    fp8_dgrad = lambda hist: dict(dy_scale_inv=dev["dy"][1], w1_scale_inv=dev["W1"][1],
+                                  w2_scale_inv=dev["W2"][1], dH_history=hist)
+    cu = lambda v: torch.tensor([float(v)], dtype=torch.float32, device="cuda")
+    fp8_wgrad = lambda a_si, dH_si: dict(dy_scale_inv=dev["dy"][1], x_scale_inv=dev["x"][1],
+                                         a_scale_inv=a_si, dH_scale_inv=dH_si)
+    acc = lambda: None if pr is None else {k: v.cuda() for k, v in pr.items()}
+    say(f"  e4m3 block T={T} H={H} Fs={Fs}")
+
+    # forward
+    ah = tp.DelayedScaling(2, scale=float(a_scale))
+    f = tp.fwd(desc, dev["x"][0], dev["W1"][0], inp["b1"].cuda(), dev["W2"][0],
+               fp8_in_scales=fp8_fwd, a_history=ah)
+    torch.cuda.synchronize()
+    lo, hi = _check_h(f["h"], rf["h_exact"])
+    da = _a_delta(rf, lo, hi)
+    _check_codes("a", f["a"], rf["a"] * float(a_scale), da * float(a_scale), "e4m3", rf["a_codes"])
+    assert float(ah.scale_inv.cpu()[0]) == float(a_sinv)
+    assert abs(float(ah.amax_history.cpu()[0]) - rf["amax"]) <= float(np.max(da))
+    errs = {"y": rel_err(f["y"].cpu(), rf["y"])}
+
+    # dgrad on the oracle's stored h
+    h_or = torch.from_numpy(rf["h"].astype(np.float32)).to(torch.bfloat16).cuda()
+    dh = tp.DelayedScaling(2, scale=float(dH_scale))
+    g = tp.bwd_dgrad(desc, dev["dy"][0], dev["W1"][0], dev["W2"][0], h_or, fp8=fp8_dgrad(dh))
+    torch.cuda.synchronize()
+    ddH = _dH_delta(rg, rf["h"], rf["h"])
+    _check_codes("dH", g["dH"], rg["dH"] * float(dH_scale), ddH * float(dH_scale), "e5m2",
+                 rg["dH_codes"])
+    assert float(dh.scale_inv.cpu()[0]) == float(dH_sinv)
+    assert abs(float(dh.amax_history.cpu()[0]) - rg["amax"]) <= float(np.max(ddH))
+    errs["dx"] = rel_err(g["dx"].cpu(), rg["dx"])
+
+    # wgrad on the oracle's codes: identical FP8 inputs
+    wg = tp.bwd_wgrad(desc, dev["dy"][0], dev["x"][0],
+                      torch.from_numpy(rf["a_codes"]).cuda(), torch.from_numpy(rg["dH_codes"]).cuda(),
+                      accumulate_into=acc(), fp8=fp8_wgrad(cu(a_sinv), cu(dH_sinv)))
+    torch.cuda.synchronize()
+    exact = {k: rel_err(wg[k].cpu(), rw[k]) for k in ("dW1", "db1", "dW2")}
+    say("    given codes: " + " ".join(f"{k}={v:.2e}" for k, v in exact.items()))
+    for k, v in exact.items():
+        assert v <= EXACT_TOL, (k, v)
+
+    # the chain, on the device's own h, a and dH
+    dh2 = tp.DelayedScaling(2, scale=float(dH_scale))
+    g2 = tp.bwd_dgrad(desc, dev["dy"][0], dev["W1"][0], dev["W2"][0], f["h"], fp8=fp8_dgrad(dh2))
+    wg2 = tp.bwd_wgrad(desc, dev["dy"][0], dev["x"][0], f["a"], g2["dH"], accumulate_into=acc(),
+                       fp8=fp8_wgrad(ah.scale_inv, dh2.scale_inv))
+    torch.cuda.synchronize()
+    _check_codes("dH (chain)", g2["dH"], rg["dH"] * float(dH_scale),
+                 _dH_delta(rg, lo, hi) * float(dH_scale), "e5m2", rg["dH_codes"])
+    errs["dx (chain)"] = rel_err(g2["dx"].cpu(), rg["dx"])
+    for k in ("dW1", "db1", "dW2"):
+        errs[k + " (chain)"] = rel_err(wg2[k].cpu(), rw[k])
+    say("    rel errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL["e4m3"], (k, v)
+
+
+@pytest.mark.parametrize("T,H,Fs", [(300, 528, 272), (64, 256, 512), (37, 48, 32), (513, 1040, 400)])
+def test_fp8_block_small_and_ragged(tp, T, H, Fs):
+    _fp8_block(tp, T, H, Fs, seed=900 + T)
+
+
+def test_fp8_block_accumulate_and_more_tiles_than_cus(tp):
+    """accumulate = 1 into prior fp32 gradients, at a size whose GEMMs have
+    more than 256 tiles (ragged in every dimension)."""
+    _fp8_block(tp, 4200, 4208, 4112, seed=917, prior=True)
