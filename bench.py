@@ -10,6 +10,13 @@ Prints one JSON line: TFLOP/s of the whole step (algorithmic FLOPs
 6*T*H*Fs*(G+1) over the measured time), the dominant kernel's roofline
 (its average launch time from HIP events recorded on its launch stream during
 the timed steps) and the CPU oracle's throughput on a bounded sample.
+
+FP8 (e4m3) steps: x, W1, W2 are E4M3 codes and dy E5M2 codes, quantised
+once before the timed region (per-tensor current scaling); inside it the
+block quantises a (E4M3) and dH (E5M2) with delayed scaling, the history
+update included. ``--calls`` picks the entry points of a step (the 12288-
+hidden FP8 shard is forward only unless asked for more); ``--dtype``
+overrides the workload's dtype.
 """
 from __future__ import annotations
 
@@ -27,7 +34,12 @@ if ROOT not in sys.path:
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
 PEAK = {"bf16": 2516.6, "f32": 157.3, "e4m3": 5033.2}
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+HISTORY_LEN = 1024  # delayed-scaling amax history (the common default length)
+
+
+def traffic_file(w) -> str:
+    return os.path.join(TRAFFIC_DIR, f"traffic_{w.name}.json")
 COPY_BYTES = 1 << 30  # the calibration copy
 KERNEL_SOURCES = ["gemm_mfma.h", "epilogue.h", "common.h", "kernels_mfma.hip"]
 
@@ -46,27 +58,36 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
+def measured_traffic(w, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    runs, or None when absent or when the kernel source changed since."""
+    runs of workload `w`, or None when absent or when the kernel source
+    changed since."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(traffic_file(w)) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != kernel_source_sha():
+    if t.get("source_sha") != kernel_source_sha() or t.get("workload") != w.name:
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
 
 
-def step_labels(w) -> list:
-    """The library's launches in one step (forward, dgrad, wgrad), in order,
-    under the names its timing facility gives them."""
+def step_labels(w, calls) -> list:
+    """The library's launches in one step (the given entry points among
+    forward, dgrad, wgrad), in order, under the names its timing facility
+    gives them."""
     sfx = "." + w.dtype
-    seq = ["fc1_fwd", "fc2_fwd", "fc2_dgrad", "fc1_dgrad", "fc2_wgrad", "fc1_wgrad"]
-    if w.has_bias and w.dtype == "bf16":
-        seq.append("db1_reduce")  # adds up the fused column-sum partials
+    fp8 = w.dtype == "e4m3"
+    seq = []
+    if "fwd" in calls:
+        seq += ["fc1_fwd", "a_scale_update", "fc2_fwd"] if fp8 else ["fc1_fwd", "fc2_fwd"]
+    if "dgrad" in calls:
+        seq += ["fc2_dgrad", "dH_scale_update", "fc1_dgrad"] if fp8 else ["fc2_dgrad", "fc1_dgrad"]
+    if "wgrad" in calls:
+        seq += ["fc2_wgrad", "fc1_wgrad"]
+        if w.has_bias and w.dtype != "f32":
+            seq.append("db1_reduce")  # adds up the fused column-sum partials
     return [k + sfx for k in seq]
 
 
@@ -76,7 +97,7 @@ def _counter_rows(d: str) -> list:
         return sorted(csv.DictReader(fh), key=lambda r: int(r["Dispatch_Id"]))
 
 
-def write_traffic(w, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands) -> dict:
+def write_traffic(w, calls, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands) -> dict:
     """HBM bytes per launch of each kernel of the step, from rocprofv3 --pmc
     FETCH_SIZE and WRITE_SIZE runs of this script (KiB per dispatch), each
     scaled by what the same counter reads for the plain 1 GiB device copy of
@@ -93,7 +114,7 @@ def write_traffic(w, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, comma
 
     scale = {"FETCH_SIZE": copy_bytes / (copy_kib(copy_fetch_dir) * 1024.0),
              "WRITE_SIZE": copy_bytes / (copy_kib(copy_write_dir) * 1024.0)}
-    seq = step_labels(w)
+    seq = step_labels(w, calls)
     per = {}
     for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         rows = [r for r in _counter_rows(d)
@@ -113,19 +134,20 @@ def write_traffic(w, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, comma
         kernels[label] = {"kernel": k["kernel"], "dispatches": len(k["FETCH_SIZE"]),
                           "fetch_bytes": round(fetch), "write_bytes": round(write),
                           "bytes_per_launch": round(fetch + write)}
-    out = {"source_sha": kernel_source_sha(), "workload": w.name,
+    out = {"source_sha": kernel_source_sha(), "workload": w.name, "calls": list(calls),
            "scale": {"FETCH_SIZE": round(scale["FETCH_SIZE"], 4),
                      "WRITE_SIZE": round(scale["WRITE_SIZE"], 4)},
            "commands": commands, "kernels": kernels}
-    with open(TRAFFIC_FILE, "w") as fh:
+    with open(traffic_file(w), "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
     return out
 
 
-def cpu_baseline(w, tokens: int, repeats: int = 3) -> dict:
+def cpu_baseline(w, calls, tokens: int, repeats: int = 3) -> dict:
     """The CPU oracle (fp64 NumPy, as it stands) on the first `tokens` tokens
-    of the same per-rank shard: forward, dgrad and wgrad."""
+    of the same per-rank shard: the step's entry points (for e4m3, the
+    oracle's FP8 block on the dequantised codes)."""
     import numpy as np
     import oracle
     import synth
@@ -140,19 +162,43 @@ def cpu_baseline(w, tokens: int, repeats: int = 3) -> dict:
     inp = synth.make_rank_inputs(w, tokens=tokens)
     x, W1, W2, dy = (oracle.to_f64(inp[k]) for k in ("x", "W1", "W2", "dy"))
     b1 = oracle.to_f64(inp["b1"]) if w.has_bias else None
+    fp8 = w.dtype == "e4m3"
+    if fp8:
+        # the codes the device is given, dequantised; the scales of a and dH
+        # as delayed scaling would settle on them (from the plain block's amaxes)
+        def deq(v, fmt):
+            amax = np.float32(np.max(np.abs(v)))
+            s = np.float32(np.float32(oracle.FMAX[fmt]) / amax)
+            return oracle.dequantize(oracle.quantize(v, fmt, s), fmt, np.float32(1.0) / s)
+        x, W1, W2 = deq(x, "e4m3"), deq(W1, "e4m3"), deq(W2, "e4m3")
+        dy = deq(dy, "e5m2")
+        f0 = oracle.rank_forward(x, W1, b1, W2, w.act)
+        a_scale = np.float32(448.0 / np.max(np.abs(f0["a"])))
+        dH_scale = np.float32(57344.0 / np.max(np.abs(
+            oracle.rank_dgrad(dy, W1, W2, f0["h"], w.act)["dH"]))) if "dgrad" in calls else None
+        del f0
     times = []
     for _ in range(repeats):
         t0 = time.perf_counter()
-        f = oracle.rank_forward(x, W1, b1, W2, w.act)
-        g = oracle.rank_dgrad(dy, W1, W2, f["h"], w.act)
-        oracle.rank_wgrad(dy, x, f["a"], g["dH"], w.has_bias)
+        if fp8:
+            f = oracle.rank_forward_fp8(x, W1, b1, W2, a_scale)
+            if "dgrad" in calls:
+                g = oracle.rank_dgrad_fp8(dy, W1, W2, f["h"], dH_scale)
+                if "wgrad" in calls:
+                    oracle.rank_wgrad_fp8(dy, x, f["a_q"], g["dH_q"])
+        else:
+            f = oracle.rank_forward(x, W1, b1, W2, w.act)
+            if "dgrad" in calls:
+                g = oracle.rank_dgrad(dy, W1, W2, f["h"], w.act)
+                if "wgrad" in calls:
+                    oracle.rank_wgrad(dy, x, f["a"], g["dH"], w.has_bias)
         times.append(time.perf_counter() - t0)
-        del f, g
+        f = g = None
     dt = sorted(times)[len(times) // 2]
-    flops = w.flops(tokens=tokens)
+    flops = w.flops(tokens=tokens, calls=calls)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"fwd+dgrad+wgrad of the first {tokens} of {w.tokens} tokens of the "
+            "sample": f"{'+'.join(calls)} of the first {tokens} of {w.tokens} tokens of the "
                       f"{w.name} shard in fp64 NumPy, median of {repeats} runs "
                       f"({flops / 1e12:.3f} TFLOP per run, {dt:.2f} s, {sum(times):.1f} s total)"}
 
@@ -163,6 +209,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3, help="workload id (3: H=8192 TP=8 shard)")
+    ap.add_argument("--calls", default=None,
+                    help="entry points of a step, comma-separated among fwd,dgrad,wgrad "
+                         "(default: the workload's)")
+    ap.add_argument("--dtype", default=None, choices=["f32", "bf16", "e4m3"],
+                    help="override the workload's dtype")
     ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens in the CPU oracle sample (0: skip)")
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
@@ -170,15 +221,23 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
                          "kernel for scaling HBM byte counters)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
-                    help="no GPU: write profiles/traffic.json from four rocprofv3 --pmc output "
+                    help="no GPU: write profiles/traffic_<workload>.json from four rocprofv3 --pmc output "
                          "folders (FETCH_SIZE and WRITE_SIZE of this benchmark, then of "
                          "--copy-calibration)")
     ap.add_argument("--command", action="append", default=[],
                     help="with --write-traffic: the commands that made the folders (recorded)")
     args = ap.parse_args()
+    import dataclasses
+    import synth
+    w = synth.WORKLOADS[args.workload]
+    if args.dtype and args.dtype != w.dtype:
+        w = dataclasses.replace(w, dtype=args.dtype, name=w.name.replace(w.dtype, args.dtype))
+    calls = tuple(args.calls.split(",")) if args.calls else w.calls
+    if not calls or any(c not in ("fwd", "dgrad", "wgrad") for c in calls) or calls[0] != "fwd" \
+            or ("wgrad" in calls and "dgrad" not in calls):
+        raise SystemExit("--calls: fwd, then optionally dgrad, then optionally wgrad")
     if args.write_traffic:
-        import synth
-        out = write_traffic(synth.WORKLOADS[args.workload], *args.write_traffic, args.command)
+        out = write_traffic(w, calls, *args.write_traffic, args.command)
         print(json.dumps(out["kernels"], indent=1))
         return
     if args.copy_calibration:
@@ -197,40 +256,57 @@ def main():
         sys.exit(2)
 
     import torch
-    import synth
     import tensor_transformer_mlp_rank_amd as tp
 
-    w = synth.WORKLOADS[args.workload]
-    if "dgrad" not in w.calls:
-        raise SystemExit("the benchmark times forward + backward; pick a workload with backward")
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     inp = synth.make_rank_inputs(w)
     d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
     T, H, Fs, G = w.tokens, w.hidden, w.ffn_shard, w.gate_mult
     desc = tp.make_desc(T, H, Fs, act=w.act, dtype=w.dtype, has_bias=w.has_bias)
-    at = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    fp8 = w.dtype == "e4m3"
+    at = torch.bfloat16 if w.dtype in ("bf16", "e4m3") else torch.float32
+    qt = torch.uint8 if fp8 else at  # a and dH: FP8 codes in the e4m3 step
     buf = {
         "y": torch.empty((T, H), dtype=at, device=dev),
         "h": torch.empty((T, G * Fs), dtype=at, device=dev),
-        "a": torch.empty((T, Fs), dtype=at, device=dev),
-        "dH": torch.empty((T, G * Fs), dtype=at, device=dev),
+        "a": torch.empty((T, Fs), dtype=qt, device=dev),
+        "dH": torch.empty((T, G * Fs), dtype=qt, device=dev),
         "dx": torch.empty((T, H), dtype=at, device=dev),
         "dW1": torch.zeros((G * Fs, H), dtype=torch.float32, device=dev),
         "db1": torch.zeros((G * Fs,), dtype=torch.float32, device=dev) if w.has_bias else None,
         "dW2": torch.zeros((H, Fs), dtype=torch.float32, device=dev),
     }
-    ws_n = tp.workspace_size(desc, tp.CALL_WGRAD)
-    wgrad_ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    ws = {}
+    for c, code in (("fwd", tp.CALL_FWD), ("dgrad", tp.CALL_DGRAD), ("wgrad", tp.CALL_WGRAD)):
+        n = tp.workspace_size(desc, code)
+        ws[c] = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+    sc = {"fwd": None, "dgrad": None, "wgrad": None}
+    if fp8:
+        # inputs as FP8 codes (current scaling, once); a and dH under delayed scaling
+        sinv = {}
+        for k, e5 in (("x", False), ("W1", False), ("W2", False), ("dy", True)):
+            codes, _, sinv[k] = tp.quantize_e4m3(d[k], stream=torch.cuda.current_stream(), e5m2=e5)
+            d[k] = codes
+        a_hist, dH_hist = tp.DelayedScaling(HISTORY_LEN), tp.DelayedScaling(HISTORY_LEN)
+        sc["fwd"] = tp.fp8_scales(sinv["x"], sinv["W1"], sinv["W2"], a_history=a_hist)
+        sc["dgrad"] = tp.fp8_scales(w1_scale_inv=sinv["W1"], w2_scale_inv=sinv["W2"],
+                                    dy_scale_inv=sinv["dy"], dH_history=dH_hist)
+        sc["wgrad"] = tp.fp8_scales(x_scale_inv=sinv["x"], a_scale_inv=a_hist.scale_inv,
+                                    dy_scale_inv=sinv["dy"], dH_scale_inv=dH_hist.scale_inv)
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     def step():
         tp.tpmlp_fwd(desc, d["x"], d["W1"], d["b1"], d["W2"], buf["y"], buf["h"], buf["a"],
-                     stream=stream)
-        tp.tpmlp_bwd_dgrad(desc, d["dy"], d["W1"], d["W2"], buf["h"], buf["dH"], buf["dx"],
-                           stream=stream)
-        tp.tpmlp_bwd_wgrad(desc, d["dy"], d["x"], buf["a"], buf["dH"], buf["dW1"], buf["db1"],
-                           buf["dW2"], accumulate=True, workspace=wgrad_ws, stream=stream)
+                     fp8=sc["fwd"], workspace=ws["fwd"], stream=stream)
+        if "dgrad" in calls:
+            tp.tpmlp_bwd_dgrad(desc, d["dy"], d["W1"], d["W2"], buf["h"], buf["dH"], buf["dx"],
+                               fp8=sc["dgrad"], workspace=ws["dgrad"], stream=stream)
+        if "wgrad" in calls:
+            tp.tpmlp_bwd_wgrad(desc, d["dy"], d["x"], buf["a"], buf["dH"], buf["dW1"], buf["db1"],
+                               buf["dW2"], accumulate=True, fp8=sc["wgrad"],
+                               workspace=ws["wgrad"], stream=stream)
 
     # warm-up; its last (up to three) steps time every kernel, to find the
     # dominant one (the first step, with its one-off costs, only if it is the
@@ -244,7 +320,7 @@ def main():
     torch.cuda.synchronize()
     per = tp.timing_collect()
     tp.timing_enable(False)
-    if list(per) != step_labels(w):
+    if list(per) != step_labels(w, calls):
         raise SystemExit(f"unexpected launch sequence {list(per)}")
     dominant = max(per, key=lambda k: per[k][1])
     breakdown = {k: round(v[1] / v[0], 4) for k, v in per.items()}
@@ -263,15 +339,16 @@ def main():
     tp.timing_enable(False)
 
     ms = (t1 - t0) * 1e3 / args.steps
-    flops = w.flops()
+    flops = w.flops(calls=calls)
     value = flops / (ms * 1e-3) / 1e12
     # fc1's three GEMMs have T*H*G*Fs multiply-adds each, fc2's T*H*Fs
     per_gemm_flops = 2.0 * T * H * Fs * (G if dominant.startswith("fc1") else 1)
     dom_ms = dom[1] / dom[0]
     achieved = per_gemm_flops / (dom_ms * 1e-3) / 1e12
-    traffic = measured_traffic(dominant)
+    traffic = measured_traffic(w, dominant)
+    what = "fwd+bwd" if calls == ("fwd", "dgrad", "wgrad") else "+".join(calls)
     line = {
-        "metric": "TFLOP/s per-rank TP-MLP fwd+bwd (bf16) and % of MFMA peak, 1 MI355X",
+        "metric": f"TFLOP/s per-rank TP-MLP {what} ({w.dtype}) and % of MFMA peak, 1 MI355X",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -296,7 +373,7 @@ def main():
         "kernel_ms": breakdown,
     }
     if args.cpu_tokens > 0:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+        line["cpu_baseline"] = cpu_baseline(w, calls, args.cpu_tokens)
     print(json.dumps(line), flush=True)
 
 
