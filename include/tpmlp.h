@@ -108,7 +108,11 @@ typedef struct tpmlp_desc {
  * oldest entry dropping out; *scale_inv = 1 / (the factor the call used),
  * which is what consumers of the codes dequantise with; and *scale =
  * fmax / max(history) for the next call (fmax 448 for E4M3, 57344 for E5M2),
- * unchanged while that maximum is 0 or not finite. All float32.
+ * unchanged while that maximum is 0 or not finite. All float32. The amax is
+ * taken over the tensor's float32 values before scaling (NaN elements, which
+ * finite inputs do not produce, are left out). A call with no tokens still
+ * updates the state, with an amax of 0. Calls that share one state must be
+ * ordered on one stream.
  */
 typedef struct tpmlp_fp8_history {
   float* amax_history;  /* [len] device floats, newest first (start with zeros) */

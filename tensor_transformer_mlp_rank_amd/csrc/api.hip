@@ -254,25 +254,29 @@ tpmlp_status tpmlp_fwd(const tpmlp_desc* d, const void* x, const void* W1, const
   if (delayed) {
     // e4m3, delayed scaling: fc1 quantises a at a_history->scale in its
     // epilogue (+ per-workgroup amax) -> history update -> fc2
+    // (no tokens: no products; the call still enters an amax of 0 and rolls
+    // the history, one entry per call)
     const tpmlp_fp8_history* ah = fp8->a_history;
-    if (T == 0) return TPMLP_OK;
     float* parts = static_cast<float*>(ws);
-    const int nparts = fp8_fc1_parts(d);
-    EpiArgs e1{};
-    e1.out = a_saved; e1.ldo = Fs;
-    e1.out2 = h_saved; e1.ldo2 = Fs;
-    e1.bias = d->has_bias ? b1 : nullptr;
-    e1.scale_a = fp8->x_scale_inv; e1.scale_b = fp8->w1_scale_inv;
-    e1.q_scale = ah->scale;
-    e1.amax_part = parts;
-    GemmArgs g1 = make_gemm(x, H, W1, H, T, Fs, H, Fs);
-    err = run_step(kind, FC1_FWD_GELU_Q, label(kind, 0), g1, e1, s);
-    if (err != hipSuccess) return hip_fail(err);
+    const int nparts = T > 0 ? fp8_fc1_parts(d) : 0;
+    if (T > 0) {
+      EpiArgs e1{};
+      e1.out = a_saved; e1.ldo = Fs;
+      e1.out2 = h_saved; e1.ldo2 = Fs;
+      e1.bias = d->has_bias ? b1 : nullptr;
+      e1.scale_a = fp8->x_scale_inv; e1.scale_b = fp8->w1_scale_inv;
+      e1.q_scale = ah->scale;
+      e1.amax_part = parts;
+      GemmArgs g1 = make_gemm(x, H, W1, H, T, Fs, H, Fs);
+      err = run_step(kind, FC1_FWD_GELU_Q, label(kind, 0), g1, e1, s);
+      if (err != hipSuccess) return hip_fail(err);
+    }
     err = timed("a_scale_update.e4m3", s, [&]() {
       return delayed_update_launch(parts, nparts, ah->amax_history, ah->len, ah->scale,
                                    ah->scale_inv, false, s);
     });
     if (err != hipSuccess) return hip_fail(err);
+    if (T == 0) return TPMLP_OK;
     EpiArgs e2{};
     e2.out = y; e2.ldo = H;
     e2.scale_a = ah->scale_inv; e2.scale_b = fp8->w2_scale_inv;
@@ -329,7 +333,16 @@ tpmlp_status tpmlp_bwd_dgrad(const tpmlp_desc* d, const void* dy, const void* W1
   }
   if ((st = check_workspace(d, TPMLP_CALL_DGRAD, ws, ws_bytes)) != TPMLP_OK) return st;
   const int64_t T = d->tokens, H = d->hidden, Fs = d->ffn_shard;
-  if (T == 0) return TPMLP_OK;
+  if (T == 0) {
+    // no products; with FP8 the call still enters an amax of 0 into dH's history
+    if (!is_fp8) return TPMLP_OK;
+    const tpmlp_fp8_history* hh = fp8->dH_history;
+    hipError_t err = timed("dH_scale_update.e4m3", s, [&]() {
+      return delayed_update_launch(static_cast<float*>(ws), 0, hh->amax_history, hh->len,
+                                   hh->scale, hh->scale_inv, true, s);
+    });
+    return err == hipSuccess ? TPMLP_OK : hip_fail(err);
+  }
   const bool swiglu = d->act == TPMLP_ACT_SWIGLU;
   const int64_t GFs = swiglu ? 2 * Fs : Fs;
   const Kind kind = d->dtype == TPMLP_F32 ? KIND_F32 : d->dtype == TPMLP_BF16 ? KIND_BF16 : KIND_E4M3;

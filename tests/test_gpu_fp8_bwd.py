@@ -296,3 +296,45 @@ def test_fp8_block_accumulate_and_more_tiles_than_cus(tp):
     """accumulate = 1 into prior fp32 gradients, at a size whose GEMMs have
     more than 256 tiles (ragged in every dimension)."""
     _fp8_block(tp, 4200, 4208, 4112, seed=917, prior=True)
+
+
+def test_fp8_zero_tokens_still_step_the_histories(tp):
+    """T = 0: no products, but each call enters an amax of 0 into its
+    history (one entry per call), reports 1 / the factor it was given and
+    sets the next factor as the oracle's delayed update does; wgrad without
+    accumulation writes zeros."""
+    H, Fs = 48, 32
+    desc = tp.make_desc(0, H, Fs, act="gelu", dtype="e4m3", has_bias=True)
+    one = lambda: torch.ones(1, dtype=torch.float32, device="cuda")
+    W1 = torch.zeros((Fs, H), dtype=torch.uint8, device="cuda")
+    W2 = torch.zeros((H, Fs), dtype=torch.uint8, device="cuda")
+    b1 = torch.zeros((Fs,), dtype=torch.bfloat16, device="cuda")
+    anyp = W1  # zero-sized tensors may have no storage: a valid aligned pointer instead
+    ws = {c: torch.empty(max(tp.workspace_size(desc, c), 1), dtype=torch.uint8, device="cuda")
+          for c in (tp.CALL_FWD, tp.CALL_DGRAD, tp.CALL_WGRAD)}
+    for prior in (np.array([3.0, 0.0, 5.0], np.float32), np.zeros(3, np.float32)):
+        ah = tp.DelayedScaling(3, scale=2.0)
+        dh = tp.DelayedScaling(3, scale=4.0)
+        ah.amax_history.copy_(torch.from_numpy(prior))
+        dh.amax_history.copy_(torch.from_numpy(prior))
+        say(f"  zero tokens, prior history {prior.tolist()}")
+        tp.tpmlp_fwd(desc, anyp, W1, b1, W2, anyp, anyp, anyp,
+                     fp8=tp.fp8_scales(one(), one(), one(), a_history=ah), workspace=ws[tp.CALL_FWD])
+        tp.tpmlp_bwd_dgrad(desc, anyp, W1, W2, anyp, anyp, anyp,
+                           fp8=tp.fp8_scales(w1_scale_inv=one(), w2_scale_inv=one(),
+                                             dy_scale_inv=one(), dH_history=dh),
+                           workspace=ws[tp.CALL_DGRAD])
+        dW1 = torch.full((Fs, H), 7.0, device="cuda")
+        db1 = torch.full((Fs,), 7.0, device="cuda")
+        dW2 = torch.full((H, Fs), 7.0, device="cuda")
+        tp.tpmlp_bwd_wgrad(desc, anyp, anyp, anyp, anyp, dW1, db1, dW2, accumulate=False,
+                           fp8=tp.fp8_scales(x_scale_inv=one(), a_scale_inv=one(),
+                                             dy_scale_inv=one(), dH_scale_inv=one()),
+                           workspace=ws[tp.CALL_WGRAD])
+        torch.cuda.synchronize()
+        for hist, s_in, fmt in ((ah, 2.0, "e4m3"), (dh, 4.0, "e5m2")):
+            want_h, want_s, want_si = oracle.delayed_update(prior, np.float32(0.0), np.float32(s_in), fmt)
+            assert np.array_equal(hist.amax_history.cpu().numpy(), want_h), fmt
+            assert float(hist.scale.cpu()[0]) == float(want_s), fmt
+            assert float(hist.scale_inv.cpu()[0]) == float(want_si), fmt
+        assert torch.all(dW1 == 0) and torch.all(db1 == 0) and torch.all(dW2 == 0)
