@@ -221,6 +221,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens in the CPU oracle sample (0: skip)")
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time the steps with caches flushed before each (a 512 MiB buffer "
+                         "is written between steps, outside the timed spans)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
                          "kernel for scaling HBM byte counters)")
@@ -301,16 +304,46 @@ def main():
         torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def step():
+    def fwd():
         tp.tpmlp_fwd(desc, d["x"], d["W1"], d["b1"], d["W2"], buf["y"], buf["h"], buf["a"],
                      fp8=sc["fwd"], workspace=ws["fwd"], stream=stream)
-        if "dgrad" in calls:
-            tp.tpmlp_bwd_dgrad(desc, d["dy"], d["W1"], d["W2"], buf["h"], buf["dH"], buf["dx"],
-                               fp8=sc["dgrad"], workspace=ws["dgrad"], stream=stream)
-        if "wgrad" in calls:
-            tp.tpmlp_bwd_wgrad(desc, d["dy"], d["x"], buf["a"], buf["dH"], buf["dW1"], buf["db1"],
-                               buf["dW2"], accumulate=True, fp8=sc["wgrad"],
-                               workspace=ws["wgrad"], stream=stream)
+
+    def dgrad():
+        tp.tpmlp_bwd_dgrad(desc, d["dy"], d["W1"], d["W2"], buf["h"], buf["dH"], buf["dx"],
+                           fp8=sc["dgrad"], workspace=ws["dgrad"], stream=stream)
+
+    def wgrad():
+        tp.tpmlp_bwd_wgrad(desc, d["dy"], d["x"], buf["a"], buf["dH"], buf["dW1"], buf["db1"],
+                           buf["dW2"], accumulate=True, fp8=sc["wgrad"], workspace=ws["wgrad"],
+                           stream=stream)
+
+    fns = [{"fwd": fwd, "dgrad": dgrad, "wgrad": wgrad}[c] for c in calls]
+
+    def step(ev=None):
+        # ev: events recorded on the launch stream before the first call and
+        # after each call (they add no work to the step)
+        if ev is not None:
+            ev[0].record(stream)
+        for j, f in enumerate(fns):
+            f()
+            if ev is not None:
+                ev[j + 1].record(stream)
+
+    def new_events():
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+                for _ in range(args.steps)]
+
+    def span_stats(ev) -> dict:
+        """median / p10 / p90 of the step and the median of each call, in ms"""
+        import statistics
+        def q(v, f):
+            v = sorted(v)
+            return round(v[min(len(v) - 1, int(f * len(v)))], 4)
+        st = [e[0].elapsed_time(e[-1]) for e in ev]
+        return {"step_ms": {"median": round(statistics.median(st), 4), "p10": q(st, 0.1),
+                            "p90": q(st, 0.9)},
+                "call_ms": {c: round(statistics.median(e[j].elapsed_time(e[j + 1]) for e in ev), 4)
+                            for j, c in enumerate(calls)}}
 
     # warm-up; its last (up to three) steps time every kernel, to find the
     # dominant one (the first step, with its one-off costs, only if it is the
@@ -334,13 +367,27 @@ def main():
     # timed region: live events around the dominant kernel only
     tp.timing_enable(True, dominant)
     torch.cuda.synchronize()
+    ev = new_events()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(ev[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     dom = tp.timing_collect()[dominant]
     tp.timing_enable(False)
+    spans = span_stats(ev)
+    cold = None
+    if args.cold:
+        # caches flushed before each step: 512 MiB written (more than the 256 MB
+        # MALL and the 8 x 4 MB L2), outside the event spans
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cev = new_events()
+        for i in range(args.steps):
+            flush.fill_(i & 0xFF)
+            step(cev[i])
+        torch.cuda.synchronize()
+        cold = span_stats(cev)
+        del flush
 
     ms = (t1 - t0) * 1e3 / args.steps
     flops = w.flops(calls=calls)
@@ -375,7 +422,10 @@ def main():
                                      "copy-calibrated)",
                      "launches": dom[0], "avg_ms": round(dom_ms, 4)},
         "kernel_ms": breakdown,
+        "spans": spans,
     }
+    if cold is not None:
+        line["spans_cold"] = cold
     if args.cpu_tokens > 0:
         line["cpu_baseline"] = cpu_baseline(w, calls, args.cpu_tokens)
     print(json.dumps(line), flush=True)

@@ -19,14 +19,20 @@ written as the definitions stated by the pages:
   note, section "Key math / How it works";
 * FP8 (OCP E4M3 for the forward tensors, OCP E5M2 for the gradients;
   per-tensor current or delayed scaling) -- code tour, "Honest Limits";
-  concept note, "Key math / How it works".
+  concept note, "Key math / How it works";
+* the attention projections (``attention``): the packed QKV projection,
+  column-parallel, and the row-parallel output projection, split by heads --
+  code tour, "The Transformer Stack"; concept note, "Key math / How it
+  works".
 
 Where the pages are silent (activation formulas, gated layout, scaling
-recipe) the readings are the textbook ones and are recorded in the design doc.
+recipe) the readings are the textbook ones, each stated in the header of the
+module that takes it.
 
 Parity status: every function here is pinned by the CPU tests in
-``tests/test_oracle.py`` (library routines, closed forms, finite
-differences, the shard-sum invariant, brute force, the OCP E4M3 table).
+``tests/test_oracle.py`` and ``tests/test_oracle_attention.py`` (library
+routines, closed forms, finite differences, the shard-sum invariant of the
+MLP and of the attention block, brute force, the OCP E4M3 and E5M2 tables).
 """
 from .activations import gelu_tanh, gelu_tanh_grad, silu, silu_grad, sigmoid
 from .block import (shard_rank, select_features, rank_forward, rank_dgrad, rank_wgrad,
@@ -35,6 +41,7 @@ from .fp8 import (E4M3_MAX, E5M2_MAX, FMAX, e4m3_decode, e4m3_encode, e5m2_decod
                   current_scale, quantize_e4m3, dequantize_e4m3, quantize, dequantize,
                   delayed_update)
 from .fp8_block import rank_forward_fp8, rank_dgrad_fp8, rank_wgrad_fp8
+from . import attention
 
 __all__ = [
     "gelu_tanh", "gelu_tanh_grad", "silu", "silu_grad", "sigmoid",
@@ -44,5 +51,5 @@ __all__ = [
     "quantize", "dequantize", "delayed_update",
     "rank_forward_fp8", "rank_dgrad_fp8", "rank_wgrad_fp8",
     "current_scale", "quantize_e4m3",
-    "dequantize_e4m3",
+    "dequantize_e4m3", "attention",
 ]

@@ -32,7 +32,7 @@ def rel_err(gpu, ref) -> float:
 
 
 def require_gpu():
-    assert torch.cuda.is_available(), "GPU tests need an MI355X; run them with -m gpu on the GPU box"
+    assert torch.cuda.is_available(), "GPU tests need an MI355X (run them with -m gpu on a machine that has one)"
 
 
 def to_dev(d: dict) -> dict:
