@@ -38,8 +38,8 @@ TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 HISTORY_LEN = 1024  # delayed-scaling amax history (the common default length)
 
 
-def traffic_file(w) -> str:
-    return os.path.join(TRAFFIC_DIR, f"traffic_{w.name}.json")
+def traffic_file(name: str) -> str:
+    return os.path.join(TRAFFIC_DIR, f"traffic_{name}.json")
 COPY_BYTES = 1 << 30  # the calibration copy
 KERNEL_SOURCES = ["gemm_mfma.h", "epilogue.h", "common.h", "kernels_mfma.hip"]
 
@@ -58,16 +58,16 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(w, kernel: str):
+def measured_traffic(name: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    runs of workload `w`, or None when absent or when the kernel source
+    runs of workload `name`, or None when absent or when the kernel source
     changed since."""
     try:
-        with open(traffic_file(w)) as fh:
+        with open(traffic_file(name)) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != kernel_source_sha() or t.get("workload") != w.name:
+    if t.get("source_sha") != kernel_source_sha() or t.get("workload") != name:
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
@@ -97,7 +97,8 @@ def _counter_rows(d: str) -> list:
         return sorted(csv.DictReader(fh), key=lambda r: int(r["Dispatch_Id"]))
 
 
-def write_traffic(w, calls, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands) -> dict:
+def write_traffic(name, labels, setup, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir,
+                  commands) -> dict:
     """HBM bytes per launch of each kernel of the step, from rocprofv3 --pmc
     FETCH_SIZE and WRITE_SIZE runs of this script (KiB per dispatch), each
     scaled by what the same counter reads for the plain 1 GiB device copy of
@@ -114,14 +115,12 @@ def write_traffic(w, calls, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir
 
     scale = {"FETCH_SIZE": copy_bytes / (copy_kib(copy_fetch_dir) * 1024.0),
              "WRITE_SIZE": copy_bytes / (copy_kib(copy_write_dir) * 1024.0)}
-    seq = step_labels(w, calls)
+    seq = labels
     per = {}
     for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         rows = [r for r in _counter_rows(d)
                 if "tpmlp::" in r["Kernel_Name"] and r["Counter_Name"] == counter]
-        # the FP8 step's one-off set-up (quantising its inputs) comes first
-        setup = 8 if w.dtype == "e4m3" else 0
-        rows = rows[setup:]
+        rows = rows[setup:]  # one-off set-up launches (the FP8 step quantises its inputs)
         if not rows or len(rows) % len(seq):
             raise SystemExit(f"{d}: {len(rows)} library dispatches after the set-up, not whole "
                              f"steps of {len(seq)}")
@@ -138,14 +137,25 @@ def write_traffic(w, calls, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir
         kernels[label] = {"kernel": k["kernel"], "dispatches": len(k["FETCH_SIZE"]),
                           "fetch_bytes": round(fetch), "write_bytes": round(write),
                           "bytes_per_launch": round(fetch + write)}
-    out = {"source_sha": kernel_source_sha(), "workload": w.name, "calls": list(calls),
+    out = {"source_sha": kernel_source_sha(), "workload": name, "labels": list(labels),
            "scale": {"FETCH_SIZE": round(scale["FETCH_SIZE"], 4),
                      "WRITE_SIZE": round(scale["WRITE_SIZE"], 4)},
            "commands": commands, "kernels": kernels}
-    with open(traffic_file(w), "w") as fh:
+    with open(traffic_file(name), "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
     return out
+
+
+def _cpu_cores() -> int:
+    """Threads of the BLAS the oracle runs on (else the affinity count)."""
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 0) for p in threadpool_info()
+                     if p.get("internal_api") in ("openblas", "mkl", "blis")), default=0)
+    except Exception:  # threadpoolctl missing: report the affinity count
+        cores = 0
+    return cores or len(os.sched_getaffinity(0))
 
 
 def cpu_baseline(w, calls, tokens: int, repeats: int = 3) -> dict:
@@ -155,14 +165,7 @@ def cpu_baseline(w, calls, tokens: int, repeats: int = 3) -> dict:
     import numpy as np
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 0) for p in threadpool_info()
-                     if p.get("internal_api") in ("openblas", "mkl", "blis")), default=0)
-    except Exception:  # threadpoolctl missing: report the affinity count
-        cores = 0
-    if not cores:
-        cores = len(os.sched_getaffinity(0))
+    cores = _cpu_cores()
     inp = synth.make_rank_inputs(w, tokens=tokens)
     x, W1, W2, dy = (oracle.to_f64(inp[k]) for k in ("x", "W1", "W2", "dy"))
     b1 = oracle.to_f64(inp["b1"]) if w.has_bias else None
@@ -207,66 +210,46 @@ def cpu_baseline(w, calls, tokens: int, repeats: int = 3) -> dict:
                       f"({flops / 1e12:.3f} TFLOP per run, {dt:.2f} s, {sum(times):.1f} s total)"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3, help="workload id (3: H=8192 TP=8 shard)")
-    ap.add_argument("--calls", default=None,
-                    help="entry points of a step, comma-separated among fwd,dgrad,wgrad "
-                         "(default: the workload's)")
-    ap.add_argument("--dtype", default=None, choices=["f32", "bf16", "e4m3"],
-                    help="override the workload's dtype")
-    ap.add_argument("--cpu-tokens", type=int, default=8192,
-                    help="tokens in the CPU oracle sample (0: skip)")
-    ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time the steps with caches flushed before each (a 512 MiB buffer "
-                         "is written between steps, outside the timed spans)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
-                         "kernel for scaling HBM byte counters)")
-    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
-                    help="no GPU: write profiles/traffic_<workload>.json from four rocprofv3 --pmc output "
-                         "folders (FETCH_SIZE and WRITE_SIZE of this benchmark, then of "
-                         "--copy-calibration)")
-    ap.add_argument("--command", action="append", default=[],
-                    help="with --write-traffic: the commands that made the folders (recorded)")
-    args = ap.parse_args()
-    import dataclasses
+def attn_cpu_baseline(w, tokens: int, repeats: int = 3) -> dict:
+    """The CPU oracle's per-rank attention projections (fp64 NumPy, as it
+    stands) on the first `tokens` tokens: the six products of a step."""
+    import oracle
     import synth
-    w = synth.WORKLOADS[args.workload]
-    if args.dtype and args.dtype != w.dtype:
-        w = dataclasses.replace(w, dtype=args.dtype, name=w.name.replace(w.dtype, args.dtype))
-    calls = tuple(args.calls.split(",")) if args.calls else w.calls
-    if not calls or any(c not in ("fwd", "dgrad", "wgrad") for c in calls) or calls[0] != "fwd" \
-            or ("wgrad" in calls and "dgrad" not in calls):
-        raise SystemExit("--calls: fwd, then optionally dgrad, then optionally wgrad")
-    if args.write_traffic:
-        out = write_traffic(w, calls, *args.write_traffic, args.command)
-        print(json.dumps(out["kernels"], indent=1))
-        return
-    if args.copy_calibration:
-        import torch
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
-                          "launches": 5}))
-        return
-    if args.gpus != 1:
-        print("bench.py measures one GPU: the library computes one tensor-parallel rank's "
-              "share and has no multi-GPU path; run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+    from oracle import attention as oa
+    cores = _cpu_cores()
+    inp = synth.make_attn_inputs(w, tokens=tokens)
+    x, W, Wo, dy, ctx, dqkv = (oracle.to_f64(inp[k]) for k in ("x", "Wqkv", "Wo", "dy", "ctx", "dqkv"))
+    b = oracle.to_f64(inp["bqkv"]) if inp["bqkv"] is not None else None
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oa.qkv_forward(x, W, b)
+        oa.out_forward(ctx, Wo)
+        oa.out_dgrad(dy, Wo)
+        oa.out_wgrad(dy, ctx)
+        oa.qkv_dgrad(dqkv, W)
+        oa.qkv_wgrad(dqkv, x, has_bias=b is not None)
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
+    flops = w.flops(tokens=tokens)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"the six projection products of the first {tokens} of {w.tokens} tokens of "
+                      f"the {w.name} shard in fp64 NumPy, median of {repeats} runs "
+                      f"({flops / 1e12:.3f} TFLOP per run, {dt:.2f} s, {sum(times):.1f} s total)"}
 
-    import torch
-    import tensor_transformer_mlp_rank_amd as tp
 
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
+class Job:
+    """One benchmark step: its calls (name, function), the library launches
+    they make in order, algorithmic FLOPs, and what the JSON line reports."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def mlp_job(tp, torch, w, calls, dev) -> Job:
+    """The MLP block: forward, dgrad, wgrad (accumulate) on one rank's shard."""
+    import synth
     inp = synth.make_rank_inputs(w)
     d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
     T, H, Fs, G = w.tokens, w.hidden, w.ffn_shard, w.gate_mult
@@ -317,25 +300,176 @@ def main():
                            buf["dW2"], accumulate=True, fp8=sc["wgrad"], workspace=ws["wgrad"],
                            stream=stream)
 
-    fns = [{"fwd": fwd, "dgrad": dgrad, "wgrad": wgrad}[c] for c in calls]
+    what = "fwd+bwd" if calls == ("fwd", "dgrad", "wgrad") else "+".join(calls)
+    return Job(
+        name=w.name, dtype=w.dtype, stream=stream,
+        fns=[(c, {"fwd": fwd, "dgrad": dgrad, "wgrad": wgrad}[c]) for c in calls],
+        labels=step_labels(w, calls), flops=w.flops(calls=calls),
+        # fc1's GEMMs have T*H*G*Fs multiply-adds each, fc2's T*H*Fs
+        gemm_flops=lambda lab: 2.0 * T * H * Fs * (G if lab.startswith("fc1") else 1),
+        metric=f"TFLOP/s per-rank TP-MLP {what} ({w.dtype}) and % of MFMA peak, 1 MI355X",
+        config={"workload": w.name, "tokens": T, "batch": w.batch, "seq_len": w.seq,
+                "hidden": H, "ffn": w.ffn, "tp": w.tp, "ffn_shard": Fs, "act": w.act,
+                "parallelism": "one TP rank's shard on one GPU"},
+        cpu=lambda n: cpu_baseline(w, calls, n))
+
+
+def attn_job(tp, torch, w, dev) -> Job:
+    """The attention block's two projections, forward and backward, on one
+    rank's shard: packed QKV, output projection, their dgrads and wgrads
+    (accumulate). The core attention between them is not the library's and
+    is not run; its output ctx and input gradient dqkv are synthetic."""
+    import synth
+    inp = synth.make_attn_inputs(w)
+    d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    T, H, N, D = w.tokens, w.hidden, w.nqkv, w.d
+    has_bias = w.b_std is not None
+    desc = tp.make_attn_desc(T, H, w.q_heads_rank, w.kv_heads_rank, w.head_dim, dtype=w.dtype,
+                             has_bias=has_bias)
+    at = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    buf = {"qkv": torch.empty((T, N), dtype=at, device=dev),
+           "y": torch.empty((T, H), dtype=at, device=dev),
+           "dctx": torch.empty((T, D), dtype=at, device=dev),
+           "dx": torch.empty((T, H), dtype=at, device=dev),
+           "dWo": torch.zeros((H, D), dtype=torch.float32, device=dev),
+           "dWqkv": torch.zeros((N, H), dtype=torch.float32, device=dev),
+           "dbqkv": torch.zeros((N,), dtype=torch.float32, device=dev) if has_bias else None}
+    n = tp.attn_workspace_size(desc)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        tp.tpmlp_attn_qkv_fwd(desc, d["x"], d["Wqkv"], d["bqkv"], buf["qkv"], stream=stream)
+        tp.tpmlp_attn_out_fwd(desc, d["ctx"], d["Wo"], buf["y"], stream=stream)
+
+    def bwd():
+        tp.tpmlp_attn_out_bwd_dgrad(desc, d["dy"], d["Wo"], buf["dctx"], stream=stream)
+        tp.tpmlp_attn_out_bwd_wgrad(desc, d["dy"], d["ctx"], buf["dWo"], True, stream=stream)
+        tp.tpmlp_attn_qkv_bwd_dgrad(desc, d["dqkv"], d["Wqkv"], buf["dx"], stream=stream)
+        tp.tpmlp_attn_qkv_bwd_wgrad(desc, d["dqkv"], d["x"], buf["dWqkv"], buf["dbqkv"], True,
+                                    ws, stream=stream)
+
+    sfx = "." + w.dtype
+    labels = [k + sfx for k in ("qkv_fwd", "out_fwd", "out_dgrad", "out_wgrad", "qkv_dgrad",
+                                "qkv_wgrad")]
+    if has_bias and w.dtype != "f32":
+        labels.append("dbqkv_reduce" + sfx)
+    return Job(
+        name=w.name, dtype=w.dtype, stream=stream, fns=[("fwd", fwd), ("bwd", bwd)],
+        labels=labels, flops=w.flops(),
+        gemm_flops=lambda lab: 2.0 * T * H * (N if lab.startswith("qkv") else D),
+        metric=f"TFLOP/s per-rank TP attention projections fwd+bwd ({w.dtype}) and % of MFMA "
+               f"peak, 1 MI355X",
+        config={"workload": w.name, "tokens": T, "batch": w.batch, "seq_len": w.seq,
+                "hidden": H, "heads": w.heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
+                "tp": w.tp, "qkv_shard": N, "ctx_shard": D,
+                "parallelism": "one TP rank's shard on one GPU"},
+        cpu=lambda n: attn_cpu_baseline(w, n))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3,
+                    help="workload id (3: H=8192 TP=8 MLP shard; 6, 7: attention projections)")
+    ap.add_argument("--calls", default=None,
+                    help="MLP: entry points of a step, comma-separated among fwd,dgrad,wgrad "
+                         "(default: the workload's)")
+    ap.add_argument("--dtype", default=None, choices=["f32", "bf16", "e4m3"],
+                    help="override the workload's dtype")
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
+                    help="tokens in the CPU oracle sample (0: skip)")
+    ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time the steps with caches flushed before each (a 512 MiB buffer "
+                         "is written between steps, outside the timed spans)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
+                         "kernel for scaling HBM byte counters)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="no GPU: write profiles/traffic_<workload>.json from four rocprofv3 "
+                         "--pmc output folders (FETCH_SIZE and WRITE_SIZE of this benchmark, then "
+                         "of --copy-calibration)")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --write-traffic: the commands that made the folders (recorded)")
+    args = ap.parse_args()
+    import dataclasses
+    import synth
+    attn = args.workload in synth.ATTN_WORKLOADS
+    if attn:
+        w = synth.ATTN_WORKLOADS[args.workload]
+        if args.dtype and args.dtype != w.dtype:
+            if args.dtype == "e4m3":
+                raise SystemExit("the attention projections have no FP8 path")
+            w = dataclasses.replace(w, dtype=args.dtype, name=w.name.replace(w.dtype, args.dtype))
+        if args.calls:
+            raise SystemExit("--calls applies to the MLP workloads")
+        calls = ("fwd", "bwd")
+    else:
+        w = synth.WORKLOADS[args.workload]
+        if args.dtype and args.dtype != w.dtype:
+            w = dataclasses.replace(w, dtype=args.dtype, name=w.name.replace(w.dtype, args.dtype))
+        calls = tuple(args.calls.split(",")) if args.calls else w.calls
+        if not calls or any(c not in ("fwd", "dgrad", "wgrad") for c in calls) \
+                or calls[0] != "fwd" or ("wgrad" in calls and "dgrad" not in calls):
+            raise SystemExit("--calls: fwd, then optionally dgrad, then optionally wgrad")
+    if args.write_traffic:
+        if attn:
+            sfx = "." + w.dtype
+            labels = [k + sfx for k in ("qkv_fwd", "out_fwd", "out_dgrad", "out_wgrad",
+                                        "qkv_dgrad", "qkv_wgrad")]
+            if w.b_std is not None and w.dtype != "f32":
+                labels.append("dbqkv_reduce" + sfx)
+            setup = 0
+        else:
+            labels = step_labels(w, calls)
+            setup = 8 if w.dtype == "e4m3" else 0  # the FP8 step quantises its four inputs
+        out = write_traffic(w.name, labels, setup, *args.write_traffic, args.command)
+        print(json.dumps(out["kernels"], indent=1))
+        return
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "launches": 5}))
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the library computes one tensor-parallel rank's "
+              "share and has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tensor_transformer_mlp_rank_amd as tp
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    job = attn_job(tp, torch, w, dev) if attn else mlp_job(tp, torch, w, calls, dev)
+    stream = job.stream
 
     def step(ev=None):
         # ev: events recorded on the launch stream before the first call and
         # after each call (they add no work to the step)
         if ev is not None:
             ev[0].record(stream)
-        for j, f in enumerate(fns):
+        for j, (_, f) in enumerate(job.fns):
             f()
             if ev is not None:
                 ev[j + 1].record(stream)
 
     def new_events():
-        return [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(len(job.fns) + 1)]
                 for _ in range(args.steps)]
 
     def span_stats(ev) -> dict:
         """median / p10 / p90 of the step and the median of each call, in ms"""
         import statistics
+
         def q(v, f):
             v = sorted(v)
             return round(v[min(len(v) - 1, int(f * len(v)))], 4)
@@ -343,7 +477,7 @@ def main():
         return {"step_ms": {"median": round(statistics.median(st), 4), "p10": q(st, 0.1),
                             "p90": q(st, 0.9)},
                 "call_ms": {c: round(statistics.median(e[j].elapsed_time(e[j + 1]) for e in ev), 4)
-                            for j, c in enumerate(calls)}}
+                            for j, (c, _) in enumerate(job.fns)}}
 
     # warm-up; its last (up to three) steps time every kernel, to find the
     # dominant one (the first step, with its one-off costs, only if it is the
@@ -357,7 +491,7 @@ def main():
     torch.cuda.synchronize()
     per = tp.timing_collect()
     tp.timing_enable(False)
-    if list(per) != step_labels(w, calls):
+    if list(per) != job.labels:
         raise SystemExit(f"unexpected launch sequence {list(per)}")
     dominant = max(per, key=lambda k: per[k][1])
     breakdown = {k: round(v[1] / v[0], 4) for k, v in per.items()}
@@ -390,16 +524,12 @@ def main():
         del flush
 
     ms = (t1 - t0) * 1e3 / args.steps
-    flops = w.flops(calls=calls)
-    value = flops / (ms * 1e-3) / 1e12
-    # fc1's three GEMMs have T*H*G*Fs multiply-adds each, fc2's T*H*Fs
-    per_gemm_flops = 2.0 * T * H * Fs * (G if dominant.startswith("fc1") else 1)
+    value = job.flops / (ms * 1e-3) / 1e12
     dom_ms = dom[1] / dom[0]
-    achieved = per_gemm_flops / (dom_ms * 1e-3) / 1e12
-    traffic = measured_traffic(w, dominant)
-    what = "fwd+bwd" if calls == ("fwd", "dgrad", "wgrad") else "+".join(calls)
+    achieved = job.gemm_flops(dominant) / (dom_ms * 1e-3) / 1e12
+    peak = PEAK[job.dtype]
     line = {
-        "metric": f"TFLOP/s per-rank TP-MLP {what} ({w.dtype}) and % of MFMA peak, 1 MI355X",
+        "metric": job.metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -409,15 +539,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": job.dtype,
         "data": "synthetic (seeded PCG64 normals; per-rank shard shapes)",
-        "config": {"workload": w.name, "tokens": T, "batch": w.batch, "seq_len": w.seq,
-                   "hidden": H, "ffn": w.ffn, "tp": w.tp, "ffn_shard": Fs, "act": w.act,
-                   "parallelism": "one TP rank's shard on one GPU"},
-        "pct_of_peak": round(100 * value / PEAK[w.dtype], 2),
+        "config": job.config,
+        "pct_of_peak": round(100 * value / peak, 2),
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
-                     "peak": PEAK[w.dtype], "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK[w.dtype], 4), "traffic": traffic,
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(job.name, dominant),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                      "copy-calibrated)",
                      "launches": dom[0], "avg_ms": round(dom_ms, 4)},
@@ -427,7 +555,7 @@ def main():
     if cold is not None:
         line["spans_cold"] = cold
     if args.cpu_tokens > 0:
-        line["cpu_baseline"] = cpu_baseline(w, calls, args.cpu_tokens)
+        line["cpu_baseline"] = job.cpu(args.cpu_tokens)
     print(json.dumps(line), flush=True)
 
 

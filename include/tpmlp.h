@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 3
+#define TPMLP_ABI_VERSION 4
 
 typedef enum {
   TPMLP_OK = 0,
@@ -220,6 +220,72 @@ tpmlp_status tpmlp_quantize_e4m3(int32_t src_dtype, const void* src, int64_t n, 
 tpmlp_status tpmlp_quantize_e5m2(int32_t src_dtype, const void* src, int64_t n, uint8_t* dst,
                                  float* amax_out, float* scale_inv_out, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ---------------------------------------------------------------- attention
+ * One rank's share of the attention block's two projections, on the same
+ * kernels as the MLP (code tour, "The Transformer Stack" and its SelfAttention
+ * entry: one packed QKV projection, column-parallel, and the output
+ * projection, row-parallel; concept note, "Key math / How it works": heads are
+ * split over the TP ranks). The core attention between them (softmax over
+ * q k^T, times v) is not part of the library; as for the MLP, the caller
+ * all-reduces y_partial and dx_partial.
+ *
+ * Notation and layouts (row-major, contiguous, 16-byte aligned):
+ *   nq query heads and nkv key/value heads on this rank (nkv divides nq;
+ *   query head j uses key/value head j / (nq / nkv)), hn the head size,
+ *   Nqkv = (nq + 2 nkv) hn, D = nq hn.
+ *   x, dy, y_partial, dx_partial : [T, H]
+ *   Wqkv : [Nqkv, H]  this rank's rows stacked [Wq (nq hn rows); Wk (nkv hn);
+ *                     Wv (nkv hn)], each head's rows contiguous ([out, in])
+ *   bqkv : [Nqkv]     the same order (when has_bias)
+ *   qkv, dqkv : [T, Nqkv]  per token [q heads | k heads | v heads]: q is
+ *                     columns [0, D), k [D, D + nkv hn), v the rest, each a
+ *                     [T, heads, hn] view with row stride Nqkv
+ *   ctx, dctx : [T, D]  the core attention's output, heads concatenated
+ *   Wo : [H, D]
+ *   dWqkv [Nqkv, H], dbqkv [Nqkv], dWo [H, D] : float32 always.
+ * Element types: TPMLP_F32 (all float32) or TPMLP_BF16 (everything but the
+ * weight gradients bfloat16, float32 accumulation); E4M3 is not provided
+ * (TPMLP_E_UNSUPPORTED). The output projection's bias is not in the partial
+ * sum: it is added once after the all-reduce. Errors, ownership, asynchrony
+ * and aliasing as for the MLP calls; accumulate as in tpmlp_bwd_wgrad.
+ */
+typedef struct tpmlp_attn_desc {
+  int64_t tokens;     /* T >= 0 */
+  int64_t hidden;     /* H > 0, multiple of 16 */
+  int32_t q_heads;    /* nq > 0 */
+  int32_t kv_heads;   /* nkv > 0, divides nq */
+  int32_t head_dim;   /* hn > 0, multiple of 16 */
+  int32_t dtype;      /* TPMLP_F32 or TPMLP_BF16 */
+  int32_t has_bias;   /* 1: the QKV projection has a bias; 0: none */
+  int32_t reserved;   /* must be 0 */
+} tpmlp_attn_desc;
+
+/* qkv = x . Wqkv^T (+ bqkv). bqkv is required iff has_bias. */
+tpmlp_status tpmlp_attn_qkv_fwd(const tpmlp_attn_desc* desc, const void* x, const void* Wqkv,
+                                const void* bqkv, void* qkv, hipStream_t stream);
+/* y_partial = ctx . Wo^T. */
+tpmlp_status tpmlp_attn_out_fwd(const tpmlp_attn_desc* desc, const void* ctx, const void* Wo,
+                                void* y_partial, hipStream_t stream);
+/* dctx = dy . Wo (dy replicated on every rank). */
+tpmlp_status tpmlp_attn_out_bwd_dgrad(const tpmlp_attn_desc* desc, const void* dy,
+                                      const void* Wo, void* dctx, hipStream_t stream);
+/* dWo (+)= dy^T . ctx, float32. */
+tpmlp_status tpmlp_attn_out_bwd_wgrad(const tpmlp_attn_desc* desc, const void* dy,
+                                      const void* ctx, float* dWo, int32_t accumulate,
+                                      hipStream_t stream);
+/* dx_partial = dqkv . Wqkv. */
+tpmlp_status tpmlp_attn_qkv_bwd_dgrad(const tpmlp_attn_desc* desc, const void* dqkv,
+                                      const void* Wqkv, void* dx_partial, hipStream_t stream);
+/* dWqkv (+)= dqkv^T . x and, when has_bias, dbqkv (+)= column sums of dqkv
+   (dbqkv required iff has_bias); float32. Workspace:
+   tpmlp_attn_workspace_size(desc) bytes (0 for float32 or without bias). */
+size_t tpmlp_attn_workspace_size(const tpmlp_attn_desc* desc);
+tpmlp_status tpmlp_attn_qkv_bwd_wgrad(const tpmlp_attn_desc* desc, const void* dqkv,
+                                      const void* x, float* dWqkv, float* dbqkv,
+                                      int32_t accumulate, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
 
 const char* tpmlp_strerror(tpmlp_status status);
 int32_t tpmlp_abi_version(void);

@@ -25,6 +25,12 @@ GELU block split into two simulated shards, GELU shards at TP=4 and TP=8,
 a gated SwiGLU shard at TP=2 and an fp8 GELU shard at TP=8. The block
 structure (column-parallel fc1, activation, row-parallel fc2) follows the
 Megatron code tour, section "The Transformer Stack".
+
+The attention-projection workloads (``ATTN_WORKLOADS``) use the same rule
+with their own tensor ids: x=1, Wqkv=2, bqkv=3, Wo=4, dy=5, dW_init=6,
+ctx=7 (the core attention's output, the input of the output projection) and
+dqkv=8 (the core attention's input gradient). The per-rank packed weight is
+drawn directly at its shard shape [(nq + 2 nkv) hn, H].
 """
 from __future__ import annotations
 
@@ -34,7 +40,8 @@ import math
 import numpy as np
 import torch
 
-TENSOR_IDS = {"x": 1, "W1": 2, "b1": 3, "W2": 4, "dy": 5, "dW_init": 6}
+TENSOR_IDS = {"x": 1, "W1": 2, "b1": 3, "W2": 4, "dy": 5, "dW_init": 6,
+              "Wqkv": 2, "bqkv": 3, "Wo": 4, "ctx": 7, "dqkv": 8}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -191,3 +198,83 @@ def grad_init(cfg_id: int, shape, salt: int = 0) -> torch.Tensor:
     """Seeded nonzero fp32 buffer used as the prior content of a gradient
     accumulator when testing the accumulate mode."""
     return torch.from_numpy(normal_f32(seed_for(cfg_id, "dW_init") + 7919 * salt, shape, 1e-3))
+
+
+# ---------------------------------------------------------------- attention projections
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    """One rank's share of the attention block's projections."""
+
+    cfg_id: int
+    name: str
+    tokens: int          # T = micro-batch x sequence length
+    batch: int
+    seq: int
+    hidden: int          # H
+    heads: int           # query heads, unsharded
+    kv_heads: int        # key/value heads, unsharded (= heads without grouped queries)
+    head_dim: int        # hn
+    tp: int
+    dtype: str           # "f32" or "bf16"
+    x_std: float
+    w_std: float
+    b_std: float | None  # None: no QKV bias
+
+    @property
+    def q_heads_rank(self) -> int:
+        return self.heads // self.tp
+
+    @property
+    def kv_heads_rank(self) -> int:
+        return self.kv_heads // self.tp
+
+    @property
+    def nqkv(self) -> int:
+        return (self.q_heads_rank + 2 * self.kv_heads_rank) * self.head_dim
+
+    @property
+    def d(self) -> int:
+        return self.q_heads_rank * self.head_dim
+
+    def flops(self, tokens: int | None = None) -> float:
+        """Algorithmic FLOPs of the two projections forward + backward (six GEMMs)."""
+        t = self.tokens if tokens is None else tokens
+        return 3 * 2.0 * t * self.hidden * (self.nqkv + self.d)
+
+
+ATTN_WORKLOADS = {
+    # the pages' example model (hidden 1024, 16 heads, TP 2, micro-batch 2 x seq 2048)
+    6: AttnWorkload(6, "attn_bf16_h1024_tp2", 4096, 2, 2048, 1024, 16, 16, 64, 2, "bf16",
+                    1.0, 0.02, 0.01),
+    # the 8192-hidden shard of the MLP workloads' model: 64 heads of 128, TP 8
+    7: AttnWorkload(7, "attn_bf16_h8192_tp8", 8192, 4, 2048, 8192, 64, 64, 128, 8, "bf16",
+                    1.0, 0.02, 0.01),
+}
+
+
+def make_attn_inputs(w: AttnWorkload, tokens: int | None = None, hidden: int | None = None,
+                     q_heads: int | None = None, kv_heads: int | None = None,
+                     head_dim: int | None = None, dtype: str | None = None,
+                     seed_base: int | None = None) -> dict:
+    """Per-rank inputs of the two projections on the CPU: x, Wqkv, bqkv (or
+    None), Wo, dy, ctx, dqkv. Sizes override the workload's per-rank ones."""
+    dt = w.dtype if dtype is None else dtype
+    cid = w.cfg_id if seed_base is None else seed_base
+    t = w.tokens if tokens is None else tokens
+    h = w.hidden if hidden is None else hidden
+    nq = w.q_heads_rank if q_heads is None else q_heads
+    nkv = w.kv_heads_rank if kv_heads is None else kv_heads
+    hn = w.head_dim if head_dim is None else head_dim
+    nqkv, d = (nq + 2 * nkv) * hn, nq * hn
+    out = {
+        "x": _cast(normal_f32(seed_for(cid, "x"), (t, h), w.x_std), dt),
+        "Wqkv": _cast(normal_f32(seed_for(cid, "Wqkv"), (nqkv, h), w.w_std), dt),
+        "Wo": _cast(normal_f32(seed_for(cid, "Wo"), (h, d), w.w_std), dt),
+        "dy": _cast(normal_f32(seed_for(cid, "dy"), (t, h), 1.0), dt),
+        "ctx": _cast(normal_f32(seed_for(cid, "ctx"), (t, d), 1.0), dt),
+        "dqkv": _cast(normal_f32(seed_for(cid, "dqkv"), (t, nqkv), 1.0), dt),
+        "bqkv": None,
+    }
+    if w.b_std is not None:
+        out["bqkv"] = _cast(normal_f32(seed_for(cid, "bqkv"), (nqkv,), w.b_std), dt)
+    return out

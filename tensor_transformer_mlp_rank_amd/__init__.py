@@ -8,10 +8,11 @@ HIP stream; every step of the block runs in the library's HIP kernels
 this module raises on import -- there is no fallback path.
 
 The C entry points keep their names here (``tpmlp_fwd``, ``tpmlp_bwd_dgrad``,
-``tpmlp_bwd_wgrad``, ``tpmlp_quantize_e4m3``, ``tpmlp_quantize_e5m2``) and take preallocated output
-tensors; ``fwd``, ``bwd_dgrad`` and ``bwd_wgrad`` are conveniences that
-allocate the outputs with torch and call them. Layouts are those of
-``include/tpmlp.h``.
+``tpmlp_bwd_wgrad``, ``tpmlp_quantize_e4m3``, ``tpmlp_quantize_e5m2``, and the
+attention projections ``tpmlp_attn_*``) and take preallocated output
+tensors; ``fwd``, ``bwd_dgrad``, ``bwd_wgrad`` and ``attn_*`` are
+conveniences that allocate the outputs with torch and call them. Layouts are
+those of ``include/tpmlp.h``.
 """
 from __future__ import annotations
 
@@ -40,6 +41,21 @@ class Desc(ctypes.Structure):
                 ("ffn_shard", ctypes.c_int64), ("act", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("has_bias", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
+                ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("has_bias", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+    @property
+    def nqkv(self) -> int:
+        return (self.q_heads + 2 * self.kv_heads) * self.head_dim
+
+    @property
+    def d(self) -> int:
+        return self.q_heads * self.head_dim
 
 
 class Fp8History(ctypes.Structure):
@@ -108,8 +124,19 @@ def _load():
     L.tpmlp_quantize_workspace_size.restype = sz
     L.tpmlp_workspace_size.argtypes = [pdesc, i32]
     L.tpmlp_workspace_size.restype = sz
+    pa = ctypes.POINTER(AttnDesc)
+    L.tpmlp_attn_qkv_fwd.argtypes = [pa, vp, vp, vp, vp, vp]
+    L.tpmlp_attn_out_fwd.argtypes = [pa, vp, vp, vp, vp]
+    L.tpmlp_attn_out_bwd_dgrad.argtypes = [pa, vp, vp, vp, vp]
+    L.tpmlp_attn_out_bwd_wgrad.argtypes = [pa, vp, vp, vp, i32, vp]
+    L.tpmlp_attn_qkv_bwd_dgrad.argtypes = [pa, vp, vp, vp, vp]
+    L.tpmlp_attn_qkv_bwd_wgrad.argtypes = [pa, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.tpmlp_attn_workspace_size.argtypes = [pa]
+    L.tpmlp_attn_workspace_size.restype = sz
     for f in ("tpmlp_fwd", "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad", "tpmlp_quantize_e4m3",
-              "tpmlp_quantize_e5m2", "tpmlp_timing_enable"):
+              "tpmlp_quantize_e5m2", "tpmlp_timing_enable", "tpmlp_attn_qkv_fwd",
+              "tpmlp_attn_out_fwd", "tpmlp_attn_out_bwd_dgrad", "tpmlp_attn_out_bwd_wgrad",
+              "tpmlp_attn_qkv_bwd_dgrad", "tpmlp_attn_qkv_bwd_wgrad"):
         getattr(L, f).restype = i32
     L.tpmlp_strerror.argtypes = [i32]
     L.tpmlp_strerror.restype = ctypes.c_char_p
@@ -131,6 +158,13 @@ def make_desc(tokens: int, hidden: int, ffn_shard: int, act="gelu", dtype="bf16"
     a = _ACT_CODES[act] if isinstance(act, str) else int(act)
     d = _DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
     return Desc(int(tokens), int(hidden), int(ffn_shard), a, d, int(bool(has_bias)), 0)
+
+
+def make_attn_desc(tokens: int, hidden: int, q_heads: int, kv_heads: int, head_dim: int,
+                   dtype="bf16", has_bias: bool = True) -> AttnDesc:
+    d = _DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
+    return AttnDesc(int(tokens), int(hidden), int(q_heads), int(kv_heads), int(head_dim), d,
+                    int(bool(has_bias)), 0)
 
 
 def _ptr(t) -> int | None:
@@ -291,6 +325,89 @@ def quantize_e5m2(src, stream=None):
 
 
 # ------------------------------------------------------------------ timing
+# ------------------------------------------------------------------ attention projections
+def attn_workspace_size(desc: AttnDesc) -> int:
+    return int(lib.tpmlp_attn_workspace_size(ctypes.byref(desc)))
+
+
+def tpmlp_attn_qkv_fwd(desc, x, Wqkv, bqkv, qkv, stream=None):
+    _check(lib.tpmlp_attn_qkv_fwd(ctypes.byref(desc), _ptr(x), _ptr(Wqkv), _ptr(bqkv), _ptr(qkv),
+                                  _stream(stream)), "tpmlp_attn_qkv_fwd")
+
+
+def tpmlp_attn_out_fwd(desc, ctx, Wo, y, stream=None):
+    _check(lib.tpmlp_attn_out_fwd(ctypes.byref(desc), _ptr(ctx), _ptr(Wo), _ptr(y),
+                                  _stream(stream)), "tpmlp_attn_out_fwd")
+
+
+def tpmlp_attn_out_bwd_dgrad(desc, dy, Wo, dctx, stream=None):
+    _check(lib.tpmlp_attn_out_bwd_dgrad(ctypes.byref(desc), _ptr(dy), _ptr(Wo), _ptr(dctx),
+                                        _stream(stream)), "tpmlp_attn_out_bwd_dgrad")
+
+
+def tpmlp_attn_out_bwd_wgrad(desc, dy, ctx, dWo, accumulate=False, stream=None):
+    _check(lib.tpmlp_attn_out_bwd_wgrad(ctypes.byref(desc), _ptr(dy), _ptr(ctx), _ptr(dWo),
+                                        int(bool(accumulate)), _stream(stream)),
+           "tpmlp_attn_out_bwd_wgrad")
+
+
+def tpmlp_attn_qkv_bwd_dgrad(desc, dqkv, Wqkv, dx, stream=None):
+    _check(lib.tpmlp_attn_qkv_bwd_dgrad(ctypes.byref(desc), _ptr(dqkv), _ptr(Wqkv), _ptr(dx),
+                                        _stream(stream)), "tpmlp_attn_qkv_bwd_dgrad")
+
+
+def tpmlp_attn_qkv_bwd_wgrad(desc, dqkv, x, dWqkv, dbqkv, accumulate=False, workspace=None,
+                             stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.tpmlp_attn_qkv_bwd_wgrad(ctypes.byref(desc), _ptr(dqkv), _ptr(x), _ptr(dWqkv),
+                                        _ptr(dbqkv), int(bool(accumulate)), _ptr(workspace),
+                                        nbytes, _stream(stream)), "tpmlp_attn_qkv_bwd_wgrad")
+
+
+def _act_t(desc):
+    return torch.float32 if desc.dtype == F32 else torch.bfloat16
+
+
+def attn_qkv_fwd(desc, x, Wqkv, bqkv=None, stream=None):
+    """Packed projection; returns (qkv, q, k, v), q/k/v column views of qkv."""
+    qkv = _empty((desc.tokens, desc.nqkv), _act_t(desc), x.device)
+    tpmlp_attn_qkv_fwd(desc, x, Wqkv, bqkv, qkv, stream)
+    a, b = desc.d, desc.d + desc.kv_heads * desc.head_dim
+    return qkv, qkv[:, :a], qkv[:, a:b], qkv[:, b:]
+
+
+def attn_out_fwd(desc, ctx, Wo, stream=None):
+    y = _empty((desc.tokens, desc.hidden), _act_t(desc), ctx.device)
+    tpmlp_attn_out_fwd(desc, ctx, Wo, y, stream)
+    return y
+
+
+def attn_out_bwd(desc, dy, Wo, ctx, dWo=None, stream=None):
+    """(dctx, dWo); with a given dWo the gradient is added into it."""
+    dctx = _empty((desc.tokens, desc.d), _act_t(desc), dy.device)
+    tpmlp_attn_out_bwd_dgrad(desc, dy, Wo, dctx, stream)
+    acc = dWo is not None
+    if not acc:
+        dWo = _empty((desc.hidden, desc.d), torch.float32, dy.device)
+    tpmlp_attn_out_bwd_wgrad(desc, dy, ctx, dWo, acc, stream)
+    return dctx, dWo
+
+
+def attn_qkv_bwd(desc, dqkv, Wqkv, x, dWqkv=None, dbqkv=None, stream=None):
+    """(dx_partial, dWqkv, dbqkv or None); with given dWqkv (and dbqkv) the
+    gradients are added into them."""
+    dx = _empty((desc.tokens, desc.hidden), _act_t(desc), dqkv.device)
+    tpmlp_attn_qkv_bwd_dgrad(desc, dqkv, Wqkv, dx, stream)
+    acc = dWqkv is not None
+    if not acc:
+        dWqkv = _empty((desc.nqkv, desc.hidden), torch.float32, dqkv.device)
+        dbqkv = _empty((desc.nqkv,), torch.float32, dqkv.device) if desc.has_bias else None
+    n = attn_workspace_size(desc)
+    ws = _empty((n,), torch.uint8, dqkv.device) if n else None
+    tpmlp_attn_qkv_bwd_wgrad(desc, dqkv, x, dWqkv, dbqkv, acc, ws, stream)
+    return dx, dWqkv, dbqkv
+
+
 def timing_enable(enable: bool, name_filter: str | None = None):
     lib.tpmlp_timing_enable(int(bool(enable)), None if name_filter is None else name_filter.encode())
 
@@ -309,4 +426,8 @@ __all__ = ["Desc", "Fp8Scales", "Fp8History", "DelayedScaling", "fp8_scales", "T
            "make_desc", "workspace_size", "tpmlp_fwd", "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad",
            "tpmlp_quantize_e4m3", "tpmlp_quantize_e5m2", "fwd", "bwd_dgrad", "bwd_wgrad",
            "quantize_e4m3", "quantize_e5m2", "timing_enable", "timing_collect", "lib", "LIB_PATH",
-           "F32", "BF16", "E4M3", "GELU", "SWIGLU"]
+           "F32", "BF16", "E4M3", "GELU", "SWIGLU",
+           "AttnDesc", "make_attn_desc", "attn_workspace_size", "tpmlp_attn_qkv_fwd",
+           "tpmlp_attn_out_fwd", "tpmlp_attn_out_bwd_dgrad", "tpmlp_attn_out_bwd_wgrad",
+           "tpmlp_attn_qkv_bwd_dgrad", "tpmlp_attn_qkv_bwd_wgrad", "attn_qkv_fwd",
+           "attn_out_fwd", "attn_out_bwd", "attn_qkv_bwd"]

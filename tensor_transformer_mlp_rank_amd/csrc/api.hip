@@ -168,6 +168,52 @@ const char* label(Kind kind, int which) {
   return names[kind][which];
 }
 
+// ---------------------------------------------------------------- attention
+tpmlp_status check_attn_desc(const tpmlp_attn_desc* d) {
+  if (!d) return TPMLP_E_NULL;
+  if (d->reserved != 0) return TPMLP_E_DTYPE;
+  if (d->dtype == TPMLP_E4M3) return TPMLP_E_UNSUPPORTED;
+  if (d->dtype != TPMLP_F32 && d->dtype != TPMLP_BF16) return TPMLP_E_DTYPE;
+  if (d->has_bias != 0 && d->has_bias != 1) return TPMLP_E_DTYPE;
+  if (d->tokens < 0 || d->hidden <= 0 || d->q_heads <= 0 || d->kv_heads <= 0 ||
+      d->head_dim <= 0)
+    return TPMLP_E_SHAPE;
+  if (d->hidden % 16 != 0 || d->head_dim % 16 != 0 || d->q_heads % d->kv_heads != 0)
+    return TPMLP_E_SHAPE;
+  const int64_t nqkv = ((int64_t)d->q_heads + 2 * (int64_t)d->kv_heads) * d->head_dim;
+  if (d->hidden > kMaxDim || nqkv > kMaxDim || d->tokens > kMaxTokens) return TPMLP_E_SHAPE;
+  return TPMLP_OK;
+}
+int64_t attn_nqkv(const tpmlp_attn_desc* d) {
+  return ((int64_t)d->q_heads + 2 * (int64_t)d->kv_heads) * d->head_dim;
+}
+int64_t attn_d(const tpmlp_attn_desc* d) { return (int64_t)d->q_heads * d->head_dim; }
+Kind attn_kind(const tpmlp_attn_desc* d) { return d->dtype == TPMLP_F32 ? KIND_F32 : KIND_BF16; }
+
+// which: 0 qkv_fwd, 1 out_fwd, 2 out_dgrad, 3 out_wgrad, 4 qkv_dgrad, 5 qkv_wgrad, 6 dbqkv_reduce
+const char* attn_label(Kind kind, int which) {
+  static const char* names[2][7] = {
+      {"qkv_fwd.f32", "out_fwd.f32", "out_dgrad.f32", "out_wgrad.f32", "qkv_dgrad.f32",
+       "qkv_wgrad.f32", "dbqkv_reduce.f32"},
+      {"qkv_fwd.bf16", "out_fwd.bf16", "out_dgrad.bf16", "out_wgrad.bf16", "qkv_dgrad.bf16",
+       "qkv_wgrad.bf16", "dbqkv_reduce.bf16"}};
+  return names[kind == KIND_F32 ? 0 : 1][which];
+}
+
+// qkv wgrad with bias on the MFMA kernel: one row of dbqkv partials per tile
+// column of dWqkv = dqkv^T . x (N = H)
+int attn_colsum_parts(const tpmlp_attn_desc* d) {
+  GemmArgs g{};
+  g.M = (int)attn_nqkv(d);
+  g.N = (int)d->hidden;
+  mfma_grid(WGRAD_COLSUM, g);
+  return g.tiles_n;
+}
+size_t attn_workspace_bytes(const tpmlp_attn_desc* d) {
+  if (d->dtype == TPMLP_F32 || !d->has_bias) return 0;
+  return align_up((size_t)attn_colsum_parts(d) * (size_t)attn_nqkv(d) * 4, 256);
+}
+
 GemmArgs make_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
                    int64_t K, int64_t pair_off) {
   GemmArgs g{};
@@ -190,10 +236,13 @@ const char* tpmlp_strerror(tpmlp_status s) {
   switch (s) {
     case TPMLP_OK: return "success";
     case TPMLP_E_NULL: return "a required pointer is NULL";
-    case TPMLP_E_SHAPE: return "invalid sizes (T >= 0; H, Fs > 0 and multiples of 16; within limits)";
+    case TPMLP_E_SHAPE:
+      return "invalid sizes (T >= 0; H, Fs, head size > 0 and multiples of 16; kv heads divide "
+             "query heads; within limits)";
     case TPMLP_E_DTYPE: return "unknown dtype, activation or flag value";
     case TPMLP_E_ALIGN: return "a pointer is not 16-byte aligned";
-    case TPMLP_E_UNSUPPORTED: return "combination not provided (E4M3 SwiGLU, SwiGLU bias)";
+    case TPMLP_E_UNSUPPORTED:
+      return "combination not provided (E4M3 SwiGLU, SwiGLU bias, E4M3 attention projections)";
     case TPMLP_E_WORKSPACE: return "workspace missing or too small";
     case TPMLP_E_HIP: return "HIP runtime error while enqueuing (see tpmlp_last_hip_error)";
   }
@@ -423,6 +472,127 @@ tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* d, const void* dy, const void* x,
     err = timed(is_fp8 ? "db1_reduce.e4m3" : "db1_reduce.bf16", s, [&]() {
       return colsum_reduce_launch(static_cast<const float*>(ws), colsum_parts(d), (int)GFs, db1,
                                   accumulate, s);
+    });
+    if (err != hipSuccess) return hip_fail(err);
+  }
+  return TPMLP_OK;
+}
+
+// ---------------------------------------------------------------- attention
+size_t tpmlp_attn_workspace_size(const tpmlp_attn_desc* d) {
+  if (check_attn_desc(d) != TPMLP_OK) return 0;
+  return attn_workspace_bytes(d);
+}
+
+tpmlp_status tpmlp_attn_qkv_fwd(const tpmlp_attn_desc* d, const void* x, const void* Wqkv,
+                                const void* bqkv, void* qkv, hipStream_t s) {
+  tpmlp_status st = check_attn_desc(d);
+  if (st != TPMLP_OK) return st;
+  if ((st = check_ptrs({x, Wqkv, qkv})) != TPMLP_OK) return st;
+  if (d->has_bias && (st = check_ptrs({bqkv})) != TPMLP_OK) return st;
+  const int64_t T = d->tokens, H = d->hidden, N = attn_nqkv(d);
+  if (T == 0) return TPMLP_OK;
+  const Kind kind = attn_kind(d);
+  EpiArgs e{};
+  e.out = qkv; e.ldo = N;
+  e.bias = d->has_bias ? bqkv : nullptr;
+  GemmArgs g = make_gemm(x, H, Wqkv, H, T, N, H, 0);
+  // without a bias the plain store epilogue serves
+  hipError_t err = run_step(kind, d->has_bias ? QKV_FWD_BIAS : FC2_FWD, attn_label(kind, 0), g,
+                            e, s);
+  return err == hipSuccess ? TPMLP_OK : hip_fail(err);
+}
+
+tpmlp_status tpmlp_attn_out_fwd(const tpmlp_attn_desc* d, const void* ctx, const void* Wo,
+                                void* y, hipStream_t s) {
+  tpmlp_status st = check_attn_desc(d);
+  if (st != TPMLP_OK) return st;
+  if ((st = check_ptrs({ctx, Wo, y})) != TPMLP_OK) return st;
+  const int64_t T = d->tokens, H = d->hidden, D = attn_d(d);
+  if (T == 0) return TPMLP_OK;
+  const Kind kind = attn_kind(d);
+  EpiArgs e{};
+  e.out = y; e.ldo = H;
+  GemmArgs g = make_gemm(ctx, D, Wo, D, T, H, D, 0);
+  hipError_t err = run_step(kind, FC2_FWD, attn_label(kind, 1), g, e, s);
+  return err == hipSuccess ? TPMLP_OK : hip_fail(err);
+}
+
+tpmlp_status tpmlp_attn_out_bwd_dgrad(const tpmlp_attn_desc* d, const void* dy, const void* Wo,
+                                      void* dctx, hipStream_t s) {
+  tpmlp_status st = check_attn_desc(d);
+  if (st != TPMLP_OK) return st;
+  if ((st = check_ptrs({dy, Wo, dctx})) != TPMLP_OK) return st;
+  const int64_t T = d->tokens, H = d->hidden, D = attn_d(d);
+  if (T == 0) return TPMLP_OK;
+  const Kind kind = attn_kind(d);
+  // dctx = dy . Wo: A = dy [T, H] K-major, B = Wo [H, D] read as [K=H][N=D]
+  EpiArgs e{};
+  e.out = dctx; e.ldo = D;
+  GemmArgs g = make_gemm(dy, H, Wo, D, T, D, H, 0);
+  hipError_t err = run_step(kind, FC1_DGRAD, attn_label(kind, 2), g, e, s);
+  return err == hipSuccess ? TPMLP_OK : hip_fail(err);
+}
+
+tpmlp_status tpmlp_attn_out_bwd_wgrad(const tpmlp_attn_desc* d, const void* dy, const void* ctx,
+                                      float* dWo, int32_t accumulate, hipStream_t s) {
+  tpmlp_status st = check_attn_desc(d);
+  if (st != TPMLP_OK) return st;
+  if (accumulate != 0 && accumulate != 1) return TPMLP_E_DTYPE;
+  if ((st = check_ptrs({dy, ctx, dWo})) != TPMLP_OK) return st;
+  const int64_t T = d->tokens, H = d->hidden, D = attn_d(d);
+  if (T == 0 && accumulate) return TPMLP_OK;  // adding nothing
+  const Kind kind = attn_kind(d);
+  // dWo [H, D] = dy^T . ctx: A = dy as [K=T][M=H], B = ctx as [K=T][N=D]
+  EpiArgs e{};
+  e.out = dWo; e.ldo = D; e.accumulate = accumulate;
+  GemmArgs g = make_gemm(dy, H, ctx, D, H, D, T, 0);
+  hipError_t err = run_step(kind, WGRAD, attn_label(kind, 3), g, e, s);
+  return err == hipSuccess ? TPMLP_OK : hip_fail(err);
+}
+
+tpmlp_status tpmlp_attn_qkv_bwd_dgrad(const tpmlp_attn_desc* d, const void* dqkv,
+                                      const void* Wqkv, void* dx, hipStream_t s) {
+  tpmlp_status st = check_attn_desc(d);
+  if (st != TPMLP_OK) return st;
+  if ((st = check_ptrs({dqkv, Wqkv, dx})) != TPMLP_OK) return st;
+  const int64_t T = d->tokens, H = d->hidden, N = attn_nqkv(d);
+  if (T == 0) return TPMLP_OK;
+  const Kind kind = attn_kind(d);
+  // dx = dqkv . Wqkv: A = dqkv [T, Nqkv] K-major, B = Wqkv [Nqkv, H] read as [K=Nqkv][N=H]
+  EpiArgs e{};
+  e.out = dx; e.ldo = H;
+  GemmArgs g = make_gemm(dqkv, N, Wqkv, H, T, H, N, 0);
+  hipError_t err = run_step(kind, FC1_DGRAD, attn_label(kind, 4), g, e, s);
+  return err == hipSuccess ? TPMLP_OK : hip_fail(err);
+}
+
+tpmlp_status tpmlp_attn_qkv_bwd_wgrad(const tpmlp_attn_desc* d, const void* dqkv, const void* x,
+                                      float* dWqkv, float* dbqkv, int32_t accumulate, void* ws,
+                                      size_t ws_bytes, hipStream_t s) {
+  tpmlp_status st = check_attn_desc(d);
+  if (st != TPMLP_OK) return st;
+  if (accumulate != 0 && accumulate != 1) return TPMLP_E_DTYPE;
+  if ((st = check_ptrs({dqkv, x, dWqkv})) != TPMLP_OK) return st;
+  if (d->has_bias && (st = check_ptrs({dbqkv})) != TPMLP_OK) return st;
+  const size_t need = attn_workspace_bytes(d);
+  if (need && (!ws || ws_bytes < need)) return TPMLP_E_WORKSPACE;
+  if (need && !aligned16(ws)) return TPMLP_E_ALIGN;
+  const int64_t T = d->tokens, H = d->hidden, N = attn_nqkv(d);
+  if (T == 0 && accumulate) return TPMLP_OK;
+  const Kind kind = attn_kind(d);
+  // dWqkv [Nqkv, H] = dqkv^T . x (+ dbqkv = column sums of dqkv), as fc1's wgrad
+  const bool split = d->has_bias && kind != KIND_F32;
+  EpiArgs e{};
+  e.out = dWqkv; e.ldo = H; e.accumulate = accumulate;
+  e.colsum = d->has_bias ? (split ? static_cast<float*>(ws) : dbqkv) : nullptr;
+  GemmArgs g = make_gemm(dqkv, N, x, H, N, H, T, 0);
+  hipError_t err = run_step(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, attn_label(kind, 5), g, e, s);
+  if (err != hipSuccess) return hip_fail(err);
+  if (split) {
+    err = timed(attn_label(kind, 6), s, [&]() {
+      return colsum_reduce_launch(static_cast<const float*>(ws), attn_colsum_parts(d), (int)N,
+                                  dbqkv, accumulate, s);
     });
     if (err != hipSuccess) return hip_fail(err);
   }

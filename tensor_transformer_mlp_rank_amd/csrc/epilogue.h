@@ -11,6 +11,7 @@
 //   EPI_DSWIGLU   out[col] = acc * u * silu'(g); out[col + Fs] = acc * silu(g)
 //   EPI_BIAS_GELU_Q  as EPI_BIAS_GELU; out = E4M3 codes of bf16(a) * q_scale
 //   EPI_DGELU_Q   as EPI_DGELU; out = E5M2 codes of dH * q_scale
+//   EPI_BIAS      out = alpha * acc + bias[col]        (packed q, k, v)
 // (FP8 codes saturate at the format's largest finite value; the quantising
 // epilogues also fold max |value| into a per-workgroup amax.)
 //
@@ -32,6 +33,7 @@ enum EpiKind : int {
   EPI_DSWIGLU = 5,
   EPI_BIAS_GELU_Q = 6,  // EPI_BIAS_GELU, a quantised to E4M3 at *q_scale
   EPI_DGELU_Q = 7,      // EPI_DGELU, dH quantised to E5M2 at *q_scale
+  EPI_BIAS = 8,         // bias added, no activation (attention's QKV projection)
 };
 
 struct GemmArgs {
@@ -46,7 +48,7 @@ struct GemmArgs {
 struct EpiArgs {
   void* out;          int64_t ldo;    // primary output
   void* out2;         int64_t ldo2;   // saved pre-activation h (may be null)
-  const void* bias;                   // b1 (may be null)
+  const void* bias;                   // b1, or the QKV bias (may be null)
   const void* aux;    int64_t ldaux;  // saved h read by the dgrad epilogues
   const float* scale_a;               // e4m3: dequantisation factors (device)
   const float* scale_b;
@@ -67,6 +69,8 @@ __device__ __forceinline__ void epi_one(const EpiArgs& e, int pair_off, int row,
   const int64_t o = (int64_t)row * e.ldo + col;
   if constexpr (EPI == EPI_STORE) {
     Elem<OutT>::store(e.out, o, v * alpha);
+  } else if constexpr (EPI == EPI_BIAS) {
+    Elem<OutT>::store(e.out, o, v * alpha + bias);
   } else if constexpr (EPI == EPI_F32) {
     float* out = static_cast<float*>(e.out);
     out[o] = e.accumulate ? out[o] + v : v;

@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(kF32Threads) gemm_f32_kernel(const GemmArgs g,
         const int col = n0 + tx + 16 * j;
         if (col >= g.N) continue;
         float bias = 0.f;
-        if constexpr (EPI == EPI_BIAS_GELU) {
+        if constexpr (EPI == EPI_BIAS_GELU || EPI == EPI_BIAS) {
           if (e.bias) bias = static_cast<const float*>(e.bias)[col];
         }
         epi_one<EPI, float, false>(e, g.pair_off, row, col, acc[i][j], 1.0f, bias, amax);

@@ -353,7 +353,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e,
   float bias[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) bias[q] = 0.f;
-  if constexpr (EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_Q) {
+  if constexpr (EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_Q || EPI == EPI_BIAS) {
     if (e.bias) {
       const auto rb = make_rsrc(e.bias, (int64_t)g.N * 2);
       unpack_bf16x8(buf_load16(rb, ((uint32_t)(wcol + 8 * cg) * kBf) | oob), bias);
@@ -385,6 +385,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e,
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = src[u] * alpha;
       if constexpr (EPI == EPI_STORE) {
+        buf_store16(ro, goff(e.ldo, kOes, t), pack_bf16x8(v));
+      } else if constexpr (EPI == EPI_BIAS) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] += bias[u];
         buf_store16(ro, goff(e.ldo, kOes, t), pack_bf16x8(v));
       } else if constexpr (EPI == EPI_F32) {
         if constexpr (LOADS) {

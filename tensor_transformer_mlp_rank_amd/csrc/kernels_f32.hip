@@ -78,6 +78,7 @@ hipError_t f32_launch(Step step, const GemmArgs& g, const EpiArgs& e, hipStream_
     case FC1_DGRAD: return launch_f32<true, false, EPI_STORE, false>(g, e, s);
     case WGRAD: return launch_f32<false, false, EPI_F32, false>(g, e, s);
     case WGRAD_COLSUM: return launch_f32<false, false, EPI_F32, true>(g, e, s);
+    case QKV_FWD_BIAS: return launch_f32<true, true, EPI_BIAS, false>(g, e, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -63,6 +63,7 @@ hipError_t mfma_launch(bool fp8, Step step, const GemmArgs& g, const EpiArgs& e,
     case FC1_DGRAD: return launch_one<false, true, false, EPI_STORE, false>(g, e, s);
     case WGRAD: return launch_one<false, false, false, EPI_F32, false>(g, e, s);
     case WGRAD_COLSUM: return launch_one<false, false, false, EPI_F32, true>(g, e, s);
+    case QKV_FWD_BIAS: return launch_one<false, true, true, EPI_BIAS, false>(g, e, s);
     default: return hipErrorInvalidValue;
   }
 }

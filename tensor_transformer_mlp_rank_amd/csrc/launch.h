@@ -20,6 +20,7 @@ enum Step : int {
   WGRAD_COLSUM,       // same, plus column sums of A (dW1 and db1)
   FC1_FWD_GELU_Q,     // e4m3: as FC1_FWD_GELU, a quantised to e4m3 in the epilogue
   FC2_DGRAD_GELU_Q,   // e4m3 weights, e5m2 dy: dH quantised to e5m2 in the epilogue
+  QKV_FWD_BIAS,       // attention: x . Wqkv^T + bias -> packed q, k, v
   kNumSteps
 };
 

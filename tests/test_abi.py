@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert tp.lib.tpmlp_abi_version() == 3
+    assert tp.lib.tpmlp_abi_version() == 4
     for s in range(8):
         assert len(tp.lib.tpmlp_strerror(s)) > 5
     assert tp.lib.tpmlp_last_hip_error() == b""
@@ -203,3 +203,76 @@ def test_timing_facility_without_records():
     assert tp.lib.tpmlp_timing_enable(1, b"fc1") == 0
     assert tp.timing_collect() == {}
     assert tp.lib.tpmlp_timing_enable(0, None) == 0
+
+
+# ------------------------------------------------------------------ attention projections
+def A(**kw):
+    base = dict(tokens=64, hidden=256, q_heads=8, kv_heads=2, head_dim=64, dtype="bf16",
+                has_bias=True)
+    base.update(kw)
+    return tp.make_attn_desc(**base)
+
+
+def attn_calls(d, p=P, acc=0, ws=None, nbytes=0, bias=P):
+    """status of each of the six attention calls with every pointer = p"""
+    b = ctypes.byref(d) if d is not None else None
+    L = tp.lib
+    return [L.tpmlp_attn_qkv_fwd(b, p, p, bias, p, None),
+            L.tpmlp_attn_out_fwd(b, p, p, p, None),
+            L.tpmlp_attn_out_bwd_dgrad(b, p, p, p, None),
+            L.tpmlp_attn_out_bwd_wgrad(b, p, p, p, acc, None),
+            L.tpmlp_attn_qkv_bwd_dgrad(b, p, p, p, None),
+            L.tpmlp_attn_qkv_bwd_wgrad(b, p, p, p, bias, acc, ws, nbytes, None)]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tokens=-1), E_SHAPE), (dict(hidden=0), E_SHAPE), (dict(hidden=264), E_SHAPE),
+    (dict(q_heads=0), E_SHAPE), (dict(kv_heads=0), E_SHAPE), (dict(kv_heads=3), E_SHAPE),
+    (dict(head_dim=72), E_SHAPE), (dict(head_dim=-16), E_SHAPE),
+    (dict(q_heads=1 << 16, kv_heads=1 << 16), E_SHAPE), (dict(hidden=1 << 23), E_SHAPE),
+    (dict(dtype=9), E_DTYPE), (dict(dtype="e4m3"), E_UNSUP),
+])
+def test_attn_desc_validation(kw, code):
+    assert attn_calls(A(**kw)) == [code] * 6
+
+
+def test_attn_null_reserved_pointers_alignment():
+    assert attn_calls(None) == [E_NULL] * 6
+    d = A()
+    d.reserved = 1
+    assert attn_calls(d) == [E_DTYPE] * 6
+    d = A()
+    d.has_bias = 2
+    assert attn_calls(d) == [E_DTYPE] * 6
+    assert attn_calls(A(), p=None) == [E_NULL] * 6
+    assert attn_calls(A(), p=MIS) == [E_ALIGN] * 6
+
+
+# Each case below fails validation; calls that would pass it are never made
+# (their fake addresses must not reach a kernel).
+def test_attn_bias_and_accumulate_rules():
+    L, d = tp.lib, A()
+    b = ctypes.byref(d)
+    # the bias pointer is required with has_bias
+    assert L.tpmlp_attn_qkv_fwd(b, P, P, None, P, None) == E_NULL
+    assert L.tpmlp_attn_qkv_bwd_wgrad(b, P, P, P, None, 0, P, 1 << 20, None) == E_NULL
+    assert L.tpmlp_attn_qkv_fwd(b, P, P, MIS, P, None) == E_ALIGN
+    # accumulate is 0 or 1
+    assert L.tpmlp_attn_out_bwd_wgrad(b, P, P, P, 2, None) == E_DTYPE
+    assert L.tpmlp_attn_qkv_bwd_wgrad(b, P, P, P, P, -1, P, 1 << 20, None) == E_DTYPE
+
+
+def test_attn_workspace():
+    d = A(tokens=1000, hidden=512, q_heads=8, kv_heads=8, head_dim=64)
+    n = tp.attn_workspace_size(d)
+    nqkv = (8 + 16) * 64
+    tiles_n = (512 + 255) // 256
+    assert n == ((tiles_n * nqkv * 4 + 255) // 256) * 256
+    assert tp.attn_workspace_size(A(has_bias=False)) == 0
+    assert tp.attn_workspace_size(A(dtype="f32")) == 0
+    assert tp.attn_workspace_size(A(hidden=7)) == 0
+    # qkv wgrad with bias: missing or short workspace, misaligned workspace
+    L, b = tp.lib, ctypes.byref(d)
+    assert L.tpmlp_attn_qkv_bwd_wgrad(b, P, P, P, P, 0, None, 0, None) == E_WS
+    assert L.tpmlp_attn_qkv_bwd_wgrad(b, P, P, P, P, 0, P, n - 1, None) == E_WS
+    assert L.tpmlp_attn_qkv_bwd_wgrad(b, P, P, P, P, 0, MIS, n, None) == E_ALIGN
