@@ -23,14 +23,18 @@ written as the definitions stated by the pages:
 * the attention projections (``attention``): the packed QKV projection,
   column-parallel, and the row-parallel output projection, split by heads --
   code tour, "The Transformer Stack"; concept note, "Key math / How it
-  works".
+  works";
+* the expert MLPs of a mixture-of-experts layer over ragged token groups
+  (``moe``) -- onegen.ai overview, "Key Features"; concept note, "Key math /
+  How it works".
 
 Where the pages are silent (activation formulas, gated layout, scaling
 recipe) the readings are the textbook ones, each stated in the header of the
 module that takes it.
 
 Parity status: every function here is pinned by the CPU tests in
-``tests/test_oracle.py`` and ``tests/test_oracle_attention.py`` (library
+``tests/test_oracle.py``, ``tests/test_oracle_attention.py`` and
+``tests/test_oracle_moe.py`` (library
 routines, closed forms, finite differences, the shard-sum invariant of the
 MLP and of the attention block, brute force, the OCP E4M3 and E5M2 tables).
 """
@@ -42,6 +46,7 @@ from .fp8 import (E4M3_MAX, E5M2_MAX, FMAX, e4m3_decode, e4m3_encode, e5m2_decod
                   delayed_update)
 from .fp8_block import rank_forward_fp8, rank_dgrad_fp8, rank_wgrad_fp8
 from . import attention
+from . import moe
 
 __all__ = [
     "gelu_tanh", "gelu_tanh_grad", "silu", "silu_grad", "sigmoid",
@@ -51,5 +56,5 @@ __all__ = [
     "quantize", "dequantize", "delayed_update",
     "rank_forward_fp8", "rank_dgrad_fp8", "rank_wgrad_fp8",
     "current_scale", "quantize_e4m3",
-    "dequantize_e4m3", "attention",
+    "dequantize_e4m3", "attention", "moe",
 ]

@@ -31,6 +31,15 @@ with their own tensor ids: x=1, Wqkv=2, bqkv=3, Wo=4, dy=5, dW_init=6,
 ctx=7 (the core attention's output, the input of the output projection) and
 dqkv=8 (the core attention's input gradient). The per-rank packed weight is
 drawn directly at its shard shape [(nq + 2 nkv) hn, H].
+
+The mixture-of-experts workloads (``MOE_WORKLOADS``) draw the per-expert
+token counts from a seeded synthetic routing (``moe_counts``): router logits
+N(0, 1) per token and expert plus a per-expert offset N(0, 0.5) (so the
+experts are unevenly loaded, as trained routers are), each token sent to its
+top-k experts; the counts are the histogram of those choices. The grouped
+rows themselves (x, dy) are drawn directly at [sum(counts), H] with tensor
+ids x=1, W1=2, b1=3, W2=4, dy=5, dW_init=6, routing=9; expert weights are
+[E, ...] stacks.
 """
 from __future__ import annotations
 
@@ -41,7 +50,7 @@ import numpy as np
 import torch
 
 TENSOR_IDS = {"x": 1, "W1": 2, "b1": 3, "W2": 4, "dy": 5, "dW_init": 6,
-              "Wqkv": 2, "bqkv": 3, "Wo": 4, "ctx": 7, "dqkv": 8}
+              "Wqkv": 2, "bqkv": 3, "Wo": 4, "ctx": 7, "dqkv": 8, "routing": 9}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -277,4 +286,83 @@ def make_attn_inputs(w: AttnWorkload, tokens: int | None = None, hidden: int | N
     }
     if w.b_std is not None:
         out["bqkv"] = _cast(normal_f32(seed_for(cid, "bqkv"), (nqkv,), w.b_std), dt)
+    return out
+
+
+# ---------------------------------------------------------------- mixture of experts
+@dataclasses.dataclass(frozen=True)
+class MoeWorkload:
+    """One rank's local experts of a mixture-of-experts layer."""
+
+    cfg_id: int
+    name: str
+    tokens: int          # tokens entering the layer (batch x sequence)
+    batch: int
+    seq: int
+    hidden: int          # H
+    experts: int         # local experts E
+    topk: int            # experts per token
+    ffn_shard: int       # Fs per expert (its expert-tensor-parallel share)
+    act: str             # "gelu" or "swiglu"
+    dtype: str
+    x_std: float
+    w_std: float
+    b1_std: float | None
+
+    @property
+    def gate_mult(self) -> int:
+        return 2 if self.act == "swiglu" else 1
+
+    @property
+    def has_bias(self) -> bool:
+        return self.b1_std is not None
+
+    def flops(self, rows: int) -> float:
+        """Algorithmic FLOPs of forward + backward over `rows` routed rows."""
+        return 3 * 2.0 * rows * self.hidden * self.ffn_shard * (self.gate_mult + 1)
+
+
+MOE_WORKLOADS = {
+    # Mixtral-style: 8 experts, top-2, SwiGLU, hidden 4096, expert ffn 14336 (all local)
+    8: MoeWorkload(8, "moe_swiglu_bf16_h4096_e8", 4096, 1, 4096, 4096, 8, 2, 14336, "swiglu",
+                   "bf16", 1.0, 0.02, None),
+    # fine-grained: 64 experts, top-6, GELU with bias, hidden 2048, expert ffn 1408
+    9: MoeWorkload(9, "moe_gelu_bf16_h2048_e64", 4096, 1, 4096, 2048, 64, 6, 1408, "gelu",
+                   "bf16", 1.0, 0.02, 0.01),
+}
+
+
+def moe_counts(w: MoeWorkload, tokens: int | None = None, seed_base: int | None = None) -> np.ndarray:
+    """Rows per local expert (int32 [E]) from a seeded synthetic top-k routing."""
+    t = w.tokens if tokens is None else tokens
+    cid = w.cfg_id if seed_base is None else seed_base
+    rng = np.random.Generator(np.random.PCG64(seed_for(cid, "routing")))
+    bias = rng.standard_normal(w.experts).astype(np.float32) * np.float32(0.5)
+    logits = rng.standard_normal((t, w.experts), dtype=np.float32) + bias
+    top = np.argpartition(-logits, w.topk - 1, axis=1)[:, :w.topk]
+    return np.bincount(top.reshape(-1), minlength=w.experts).astype(np.int32)
+
+
+def make_moe_inputs(w: MoeWorkload, counts, hidden: int | None = None,
+                    ffn_shard: int | None = None, experts: int | None = None,
+                    dtype: str | None = None, seed_base: int | None = None) -> dict:
+    """Grouped rows and expert stacks on the CPU: x, dy [sum(counts), H];
+    W1 [E, G*Fs, H], b1 [E, G*Fs] or None, W2 [E, H, Fs]; counts (int32)."""
+    dt = w.dtype if dtype is None else dtype
+    cid = w.cfg_id if seed_base is None else seed_base
+    h = w.hidden if hidden is None else hidden
+    fs = w.ffn_shard if ffn_shard is None else ffn_shard
+    e = w.experts if experts is None else experts
+    rows = int(np.sum(counts))
+    g = w.gate_mult
+    out = {
+        "counts": torch.from_numpy(np.asarray(counts, dtype=np.int32)),
+        "x": _cast(normal_f32(seed_for(cid, "x"), (rows, h), w.x_std), dt),
+        "W1": _cast(normal_f32(seed_for(cid, "W1"), (e, g * fs, h), w.w_std), dt),
+        "W2": _cast(normal_f32(seed_for(cid, "W2"), (e, h, fs), w.w_std), dt),
+        "dy": _cast(normal_f32(seed_for(cid, "dy"), (rows, h), 1.0), dt),
+        "b1": None,
+    }
+    if w.has_bias:
+        out["b1"] = _cast(normal_f32(seed_for(cid, "b1"), (e, g * fs), w.b1_std), dt)
     return out
