@@ -367,13 +367,109 @@ def attn_job(tp, torch, w, dev) -> Job:
         cpu=lambda n: attn_cpu_baseline(w, n))
 
 
+def moe_labels(w) -> list:
+    labels = ["moe_fc1_fwd", "moe_fc2_fwd", "moe_fc2_dgrad", "moe_fc1_dgrad", "moe_fc2_wgrad",
+              "moe_fc1_wgrad"]
+    if w.has_bias:
+        labels.append("moe_db1_reduce")
+    return [k + "." + w.dtype for k in labels]
+
+
+def moe_job(tp, torch, w, dev) -> Job:
+    """The local experts of a mixture-of-experts layer: grouped forward,
+    dgrad, wgrad (accumulate) over the rows of a seeded synthetic routing.
+    The dispatch and combine around them are not the library's and are not
+    run."""
+    import synth
+    import numpy as np
+    counts = synth.moe_counts(w)
+    inp = synth.make_moe_inputs(w, counts)
+    d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    T, H, Fs, G, E = int(counts.sum()), w.hidden, w.ffn_shard, w.gate_mult, w.experts
+    desc = tp.make_moe_desc(T, H, Fs, E, act=w.act, dtype=w.dtype, has_bias=w.has_bias)
+    bf = torch.bfloat16
+    buf = {"y": torch.empty((T, H), dtype=bf, device=dev),
+           "h": torch.empty((T, G * Fs), dtype=bf, device=dev),
+           "a": torch.empty((T, Fs), dtype=bf, device=dev),
+           "dH": torch.empty((T, G * Fs), dtype=bf, device=dev),
+           "dx": torch.empty((T, H), dtype=bf, device=dev),
+           "dW1": torch.zeros((E, G * Fs, H), dtype=torch.float32, device=dev),
+           "db1": torch.zeros((E, G * Fs), dtype=torch.float32, device=dev) if w.has_bias else None,
+           "dW2": torch.zeros((E, H, Fs), dtype=torch.float32, device=dev)}
+    n = tp.moe_workspace_size(desc)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+    stream = torch.cuda.current_stream()
+    c = d["counts"]
+
+    def fwd():
+        tp.tpmlp_moe_fwd(desc, c, d["x"], d["W1"], d["b1"], d["W2"], buf["y"], buf["h"], buf["a"],
+                         stream=stream)
+
+    def dgrad():
+        tp.tpmlp_moe_bwd_dgrad(desc, c, d["dy"], d["W1"], d["W2"], buf["h"], buf["dH"], buf["dx"],
+                               stream=stream)
+
+    def wgrad():
+        tp.tpmlp_moe_bwd_wgrad(desc, c, d["dy"], d["x"], buf["a"], buf["dH"], buf["dW1"],
+                               buf["db1"], buf["dW2"], True, ws, stream=stream)
+
+    return Job(
+        name=w.name, dtype=w.dtype, stream=stream,
+        fns=[("fwd", fwd), ("dgrad", dgrad), ("wgrad", wgrad)], labels=moe_labels(w),
+        flops=w.flops(T),
+        gemm_flops=lambda lab: 2.0 * T * H * Fs * (G if lab.startswith("moe_fc1") else 1),
+        metric=f"TFLOP/s per-rank MoE expert MLPs fwd+bwd ({w.dtype}) and % of MFMA peak, "
+               f"1 MI355X",
+        config={"workload": w.name, "tokens": w.tokens, "routed_rows": T, "experts": E,
+                "topk": w.topk, "hidden": H, "expert_ffn_shard": Fs, "act": w.act,
+                "rows_per_expert_min": int(np.min(counts)),
+                "rows_per_expert_max": int(np.max(counts)),
+                "parallelism": "one rank's local experts on one GPU"},
+        cpu=lambda nt: moe_cpu_baseline(w, counts, nt))
+
+
+def moe_cpu_baseline(w, counts, rows: int, repeats: int = 3) -> dict:
+    """The CPU oracle's grouped block (fp64 NumPy, as it stands) on the
+    first `rows` routed rows (the leading experts' groups, the last one cut)."""
+    import numpy as np
+    import oracle
+    import synth
+    from oracle import moe as om
+    cores = _cpu_cores()
+    cum = np.cumsum(counts)
+    sub = [int(min(c, max(rows - (s - c), 0))) for c, s in zip(counts, cum)]
+    k = max(i + 1 for i, c in enumerate(sub) if c > 0) if any(sub) else 1
+    sub = sub[:k]  # the experts the sample reaches
+    inp = synth.make_moe_inputs(w, counts)
+    n = sum(sub)
+    x, dy = oracle.to_f64(inp["x"][:n]), oracle.to_f64(inp["dy"][:n])
+    W1, W2 = oracle.to_f64(inp["W1"][:k]), oracle.to_f64(inp["W2"][:k])
+    b1 = oracle.to_f64(inp["b1"][:k]) if w.has_bias else None
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        f = om.grouped_forward(x, sub, W1, b1, W2, w.act)
+        g = om.grouped_dgrad(dy, sub, W1, W2, f["h"], w.act)
+        om.grouped_wgrad(dy, x, f["a"], g["dH"], sub, w.has_bias)
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
+    flops = w.flops(n)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"fwd+dgrad+wgrad of the first {n} of {int(np.sum(counts))} routed rows "
+                      f"(experts 0..{k - 1}) of the {w.name} layer in fp64 NumPy, median of "
+                      f"{repeats} runs "
+                      f"({flops / 1e12:.3f} TFLOP per run, {dt:.2f} s, {sum(times):.1f} s total)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3,
-                    help="workload id (3: H=8192 TP=8 MLP shard; 6, 7: attention projections)")
+                    help="workload id (3: H=8192 TP=8 MLP shard; 6, 7: attention projections; "
+                         "8, 9: mixture-of-experts expert MLPs)")
     ap.add_argument("--calls", default=None,
                     help="MLP: entry points of a step, comma-separated among fwd,dgrad,wgrad "
                          "(default: the workload's)")
@@ -398,7 +494,13 @@ def main():
     import dataclasses
     import synth
     attn = args.workload in synth.ATTN_WORKLOADS
-    if attn:
+    moe = args.workload in synth.MOE_WORKLOADS
+    if moe:
+        w = synth.MOE_WORKLOADS[args.workload]
+        if (args.dtype and args.dtype != w.dtype) or args.calls:
+            raise SystemExit("the expert workloads run bf16 forward + backward")
+        calls = ("fwd", "dgrad", "wgrad")
+    elif attn:
         w = synth.ATTN_WORKLOADS[args.workload]
         if args.dtype and args.dtype != w.dtype:
             if args.dtype == "e4m3":
@@ -416,7 +518,9 @@ def main():
                 or calls[0] != "fwd" or ("wgrad" in calls and "dgrad" not in calls):
             raise SystemExit("--calls: fwd, then optionally dgrad, then optionally wgrad")
     if args.write_traffic:
-        if attn:
+        if moe:
+            labels, setup = moe_labels(w), 0
+        elif attn:
             sfx = "." + w.dtype
             labels = [k + sfx for k in ("qkv_fwd", "out_fwd", "out_dgrad", "out_wgrad",
                                         "qkv_dgrad", "qkv_wgrad")]
@@ -449,7 +553,12 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    job = attn_job(tp, torch, w, dev) if attn else mlp_job(tp, torch, w, calls, dev)
+    if moe:
+        job = moe_job(tp, torch, w, dev)
+    elif attn:
+        job = attn_job(tp, torch, w, dev)
+    else:
+        job = mlp_job(tp, torch, w, calls, dev)
     stream = job.stream
 
     def step(ev=None):

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 4
+#define TPMLP_ABI_VERSION 5
 
 typedef enum {
   TPMLP_OK = 0,
@@ -286,6 +286,56 @@ tpmlp_status tpmlp_attn_qkv_bwd_wgrad(const tpmlp_attn_desc* desc, const void* d
                                       const void* x, float* dWqkv, float* dbqkv,
                                       int32_t accumulate, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ---------------------------------------------------------------- mixture of experts
+ * The expert MLPs of a mixture-of-experts layer: this rank's E local experts,
+ * each the per-rank block above with its own weights, over the token rows
+ * already grouped by expert (onegen.ai overview, "Key Features"; concept
+ * note, "Key math / How it works": expert parallelism, whose all-to-all
+ * dispatch and combine, routing and permutation stay with the caller). Each
+ * call is one launch per product covering every expert (grouped GEMM).
+ *
+ *   counts : [E] int32, device: rows of each expert in expert order; expert e
+ *            owns rows [off_e, off_e + counts[e]) of x, y, h, a, dy, dH, dx,
+ *            off_e = counts[0] + ... + counts[e-1]. The kernels read them on
+ *            the device (no host copy needed). Negative counts count as 0 and
+ *            the running total is capped at `tokens`, so no row outside
+ *            [0, tokens) is read or written; rows past the sum of the counts
+ *            are left as they are (and add nothing to the weight gradients).
+ *   x, dy, y, dx : [tokens, H]; h, dH : [tokens, G*Fs]; a : [tokens, Fs]
+ *   W1 : [E, G*Fs, H]; b1 : [E, G*Fs] (GELU only); W2 : [E, H, Fs]
+ *   dW1 [E, G*Fs, H], db1 [E, G*Fs], dW2 [E, H, Fs] : float32.
+ * dtype TPMLP_BF16 only (other dtypes: TPMLP_E_UNSUPPORTED). Layouts,
+ * ownership, errors, asynchrony, aliasing and accumulate as for the
+ * per-rank block; counts must stay unchanged until the calls reading them
+ * have run.
+ */
+typedef struct tpmlp_moe_desc {
+  int64_t tokens;     /* rows of the grouped tensors, >= 0 */
+  int64_t hidden;     /* H > 0, multiple of 16 */
+  int64_t ffn_shard;  /* Fs per expert > 0, multiple of 16 */
+  int32_t experts;    /* E, 1 .. 1024 */
+  int32_t act;        /* tpmlp_act */
+  int32_t dtype;      /* TPMLP_BF16 */
+  int32_t has_bias;   /* GELU only */
+  int32_t reserved0;  /* must be 0 */
+  int32_t reserved1;  /* must be 0 */
+} tpmlp_moe_desc;
+
+tpmlp_status tpmlp_moe_fwd(const tpmlp_moe_desc* desc, const int32_t* counts, const void* x,
+                           const void* W1, const void* b1, const void* W2, void* y,
+                           void* h_saved, void* a_saved, hipStream_t stream);
+tpmlp_status tpmlp_moe_bwd_dgrad(const tpmlp_moe_desc* desc, const int32_t* counts,
+                                 const void* dy, const void* W1, const void* W2,
+                                 const void* h_saved, void* dH, void* dx, hipStream_t stream);
+/* Workspace: tpmlp_moe_workspace_size(desc) bytes (0 without bias). */
+size_t tpmlp_moe_workspace_size(const tpmlp_moe_desc* desc);
+tpmlp_status tpmlp_moe_bwd_wgrad(const tpmlp_moe_desc* desc, const int32_t* counts,
+                                 const void* dy, const void* x, const void* a_saved,
+                                 const void* dH, float* dW1, float* db1, float* dW2,
+                                 int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 const char* tpmlp_strerror(tpmlp_status status);
 int32_t tpmlp_abi_version(void);

@@ -9,7 +9,8 @@ this module raises on import -- there is no fallback path.
 
 The C entry points keep their names here (``tpmlp_fwd``, ``tpmlp_bwd_dgrad``,
 ``tpmlp_bwd_wgrad``, ``tpmlp_quantize_e4m3``, ``tpmlp_quantize_e5m2``, and the
-attention projections ``tpmlp_attn_*``) and take preallocated output
+attention projections ``tpmlp_attn_*`` and the expert MLPs ``tpmlp_moe_*``) and
+take preallocated output
 tensors; ``fwd``, ``bwd_dgrad``, ``bwd_wgrad`` and ``attn_*`` are
 conveniences that allocate the outputs with torch and call them. Layouts are
 those of ``include/tpmlp.h``.
@@ -56,6 +57,13 @@ class AttnDesc(ctypes.Structure):
     @property
     def d(self) -> int:
         return self.q_heads * self.head_dim
+
+
+class MoeDesc(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
+                ("ffn_shard", ctypes.c_int64), ("experts", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("dtype", ctypes.c_int32), ("has_bias", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32), ("reserved1", ctypes.c_int32)]
 
 
 class Fp8History(ctypes.Structure):
@@ -133,10 +141,17 @@ def _load():
     L.tpmlp_attn_qkv_bwd_wgrad.argtypes = [pa, vp, vp, vp, vp, i32, vp, sz, vp]
     L.tpmlp_attn_workspace_size.argtypes = [pa]
     L.tpmlp_attn_workspace_size.restype = sz
+    pm = ctypes.POINTER(MoeDesc)
+    L.tpmlp_moe_fwd.argtypes = [pm, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.tpmlp_moe_bwd_dgrad.argtypes = [pm, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.tpmlp_moe_bwd_wgrad.argtypes = [pm, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.tpmlp_moe_workspace_size.argtypes = [pm]
+    L.tpmlp_moe_workspace_size.restype = sz
     for f in ("tpmlp_fwd", "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad", "tpmlp_quantize_e4m3",
               "tpmlp_quantize_e5m2", "tpmlp_timing_enable", "tpmlp_attn_qkv_fwd",
               "tpmlp_attn_out_fwd", "tpmlp_attn_out_bwd_dgrad", "tpmlp_attn_out_bwd_wgrad",
-              "tpmlp_attn_qkv_bwd_dgrad", "tpmlp_attn_qkv_bwd_wgrad"):
+              "tpmlp_attn_qkv_bwd_dgrad", "tpmlp_attn_qkv_bwd_wgrad", "tpmlp_moe_fwd",
+              "tpmlp_moe_bwd_dgrad", "tpmlp_moe_bwd_wgrad"):
         getattr(L, f).restype = i32
     L.tpmlp_strerror.argtypes = [i32]
     L.tpmlp_strerror.restype = ctypes.c_char_p
@@ -165,6 +180,14 @@ def make_attn_desc(tokens: int, hidden: int, q_heads: int, kv_heads: int, head_d
     d = _DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
     return AttnDesc(int(tokens), int(hidden), int(q_heads), int(kv_heads), int(head_dim), d,
                     int(bool(has_bias)), 0)
+
+
+def make_moe_desc(tokens: int, hidden: int, ffn_shard: int, experts: int, act="gelu",
+                  dtype="bf16", has_bias: bool = True) -> MoeDesc:
+    a = _ACT_CODES[act] if isinstance(act, str) else int(act)
+    d = _DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
+    return MoeDesc(int(tokens), int(hidden), int(ffn_shard), int(experts), a, d,
+                   int(bool(has_bias)), 0, 0)
 
 
 def _ptr(t) -> int | None:
@@ -408,6 +431,75 @@ def attn_qkv_bwd(desc, dqkv, Wqkv, x, dWqkv=None, dbqkv=None, stream=None):
     return dx, dWqkv, dbqkv
 
 
+# ------------------------------------------------------------------ mixture of experts
+def moe_workspace_size(desc: MoeDesc) -> int:
+    return int(lib.tpmlp_moe_workspace_size(ctypes.byref(desc)))
+
+
+def _counts(counts):
+    if counts.dtype != torch.int32:
+        raise ValueError("counts must be an int32 device tensor")
+    return counts
+
+
+def tpmlp_moe_fwd(desc, counts, x, W1, b1, W2, y, h, a, stream=None):
+    _check(lib.tpmlp_moe_fwd(ctypes.byref(desc), _ptr(_counts(counts)), _ptr(x), _ptr(W1),
+                             _ptr(b1), _ptr(W2), _ptr(y), _ptr(h), _ptr(a), _stream(stream)),
+           "tpmlp_moe_fwd")
+
+
+def tpmlp_moe_bwd_dgrad(desc, counts, dy, W1, W2, h, dH, dx, stream=None):
+    _check(lib.tpmlp_moe_bwd_dgrad(ctypes.byref(desc), _ptr(_counts(counts)), _ptr(dy), _ptr(W1),
+                                   _ptr(W2), _ptr(h), _ptr(dH), _ptr(dx), _stream(stream)),
+           "tpmlp_moe_bwd_dgrad")
+
+
+def tpmlp_moe_bwd_wgrad(desc, counts, dy, x, a, dH, dW1, db1, dW2, accumulate=False,
+                        workspace=None, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.tpmlp_moe_bwd_wgrad(ctypes.byref(desc), _ptr(_counts(counts)), _ptr(dy), _ptr(x),
+                                   _ptr(a), _ptr(dH), _ptr(dW1), _ptr(db1), _ptr(dW2),
+                                   int(bool(accumulate)), _ptr(workspace), nbytes,
+                                   _stream(stream)), "tpmlp_moe_bwd_wgrad")
+
+
+def moe_fwd(desc, counts, x, W1, b1, W2, stream=None):
+    """dict y, h, a of the grouped rows (rows past the sum of counts unset)."""
+    G = 2 if desc.act == SWIGLU else 1
+    T, H, Fs = desc.tokens, desc.hidden, desc.ffn_shard
+    out = {"y": _empty((T, H), torch.bfloat16, x.device),
+           "h": _empty((T, G * Fs), torch.bfloat16, x.device),
+           "a": _empty((T, Fs), torch.bfloat16, x.device)}
+    tpmlp_moe_fwd(desc, counts, x, W1, b1, W2, out["y"], out["h"], out["a"], stream)
+    return out
+
+
+def moe_bwd_dgrad(desc, counts, dy, W1, W2, h, stream=None):
+    G = 2 if desc.act == SWIGLU else 1
+    T, H, Fs = desc.tokens, desc.hidden, desc.ffn_shard
+    out = {"dH": _empty((T, G * Fs), torch.bfloat16, dy.device),
+           "dx": _empty((T, H), torch.bfloat16, dy.device)}
+    tpmlp_moe_bwd_dgrad(desc, counts, dy, W1, W2, h, out["dH"], out["dx"], stream)
+    return out
+
+
+def moe_bwd_wgrad(desc, counts, dy, x, a, dH, accumulate_into=None, stream=None):
+    """Per-expert fp32 dW1 [E, G*Fs, H], db1 [E, G*Fs], dW2 [E, H, Fs]."""
+    G = 2 if desc.act == SWIGLU else 1
+    E, H, Fs = desc.experts, desc.hidden, desc.ffn_shard
+    if accumulate_into is not None:
+        out = accumulate_into
+    else:
+        out = {"dW1": _empty((E, G * Fs, H), torch.float32, dy.device),
+               "db1": _empty((E, G * Fs), torch.float32, dy.device) if desc.has_bias else None,
+               "dW2": _empty((E, H, Fs), torch.float32, dy.device)}
+    n = moe_workspace_size(desc)
+    ws = _empty((n,), torch.uint8, dy.device) if n else None
+    tpmlp_moe_bwd_wgrad(desc, counts, dy, x, a, dH, out["dW1"], out.get("db1"), out["dW2"],
+                        accumulate_into is not None, ws, stream)
+    return out
+
+
 def timing_enable(enable: bool, name_filter: str | None = None):
     lib.tpmlp_timing_enable(int(bool(enable)), None if name_filter is None else name_filter.encode())
 
@@ -430,4 +522,7 @@ __all__ = ["Desc", "Fp8Scales", "Fp8History", "DelayedScaling", "fp8_scales", "T
            "AttnDesc", "make_attn_desc", "attn_workspace_size", "tpmlp_attn_qkv_fwd",
            "tpmlp_attn_out_fwd", "tpmlp_attn_out_bwd_dgrad", "tpmlp_attn_out_bwd_wgrad",
            "tpmlp_attn_qkv_bwd_dgrad", "tpmlp_attn_qkv_bwd_wgrad", "attn_qkv_fwd",
-           "attn_out_fwd", "attn_out_bwd", "attn_qkv_bwd"]
+           "attn_out_fwd", "attn_out_bwd", "attn_qkv_bwd",
+           "MoeDesc", "make_moe_desc", "moe_workspace_size", "tpmlp_moe_fwd",
+           "tpmlp_moe_bwd_dgrad", "tpmlp_moe_bwd_wgrad", "moe_fwd", "moe_bwd_dgrad",
+           "moe_bwd_wgrad"]

@@ -61,7 +61,9 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
 // ---------------------------------------------------------------- validation
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int64_t kMaxDim = int64_t(1) << 22;     // H and G*Fs (row length bound)
+// Row length bound for H, G*Fs and the attention widths: 256 rows of a
+// K-major tile stay within one buffer resource's 2 GiB range.
+constexpr int64_t kMaxDim = int64_t(1) << 21;
 constexpr int64_t kMaxTokens = int64_t(1) << 30;
 
 tpmlp_status check_desc(const tpmlp_desc* d) {
@@ -212,6 +214,61 @@ int attn_colsum_parts(const tpmlp_attn_desc* d) {
 size_t attn_workspace_bytes(const tpmlp_attn_desc* d) {
   if (d->dtype == TPMLP_F32 || !d->has_bias) return 0;
   return align_up((size_t)attn_colsum_parts(d) * (size_t)attn_nqkv(d) * 4, 256);
+}
+
+// ---------------------------------------------------------------- mixture of experts
+constexpr int32_t kMaxExperts = 1024;
+
+tpmlp_status check_moe_desc(const tpmlp_moe_desc* d) {
+  if (!d) return TPMLP_E_NULL;
+  if (d->reserved0 != 0 || d->reserved1 != 0) return TPMLP_E_DTYPE;
+  if (d->dtype < TPMLP_F32 || d->dtype > TPMLP_E4M3) return TPMLP_E_DTYPE;
+  if (d->act != TPMLP_ACT_GELU_TANH && d->act != TPMLP_ACT_SWIGLU) return TPMLP_E_DTYPE;
+  if (d->has_bias != 0 && d->has_bias != 1) return TPMLP_E_DTYPE;
+  if (d->tokens < 0 || d->hidden <= 0 || d->ffn_shard <= 0 || d->experts <= 0) return TPMLP_E_SHAPE;
+  if (d->hidden % 16 != 0 || d->ffn_shard % 16 != 0 || d->experts > kMaxExperts)
+    return TPMLP_E_SHAPE;
+  const int64_t g = d->act == TPMLP_ACT_SWIGLU ? 2 : 1;
+  if (d->hidden > kMaxDim || g * d->ffn_shard > kMaxDim || d->tokens > kMaxTokens)
+    return TPMLP_E_SHAPE;
+  // the grouped grid, (ceil(tokens / 256) + E) M-tiles by the widest N, fits one launch
+  const int64_t widest = d->hidden > g * d->ffn_shard ? d->hidden : g * d->ffn_shard;
+  if (((d->tokens + 255) / 256 + d->experts) * ((widest + 255) / 256) >= (int64_t(1) << 31))
+    return TPMLP_E_SHAPE;
+  if ((int64_t)d->experts * ((widest + 255) / 256) * ((widest + 255) / 256) >= (int64_t(1) << 31))
+    return TPMLP_E_SHAPE;
+  if (d->dtype != TPMLP_BF16) return TPMLP_E_UNSUPPORTED;
+  if (d->act == TPMLP_ACT_SWIGLU && d->has_bias) return TPMLP_E_UNSUPPORTED;
+  return TPMLP_OK;
+}
+
+const char* moe_label(int which) {
+  static const char* names[7] = {"moe_fc1_fwd.bf16",   "moe_fc2_fwd.bf16",   "moe_fc2_dgrad.bf16",
+                                 "moe_fc1_dgrad.bf16", "moe_fc2_wgrad.bf16", "moe_fc1_wgrad.bf16",
+                                 "moe_db1_reduce.bf16"};
+  return names[which];
+}
+
+// fc1 wgrad with bias: tile columns of each expert's dW1 (N = H); every
+// expert writes that many rows of db1 partial sums
+int moe_colsum_parts(const tpmlp_moe_desc* d) {
+  GemmArgs g{};
+  g.M = (int)((d->act == TPMLP_ACT_SWIGLU ? 2 : 1) * d->ffn_shard);
+  g.N = (int)d->hidden;
+  mfma_grid(WGRAD_COLSUM, g);
+  return g.tiles_n;
+}
+size_t moe_workspace_bytes(const tpmlp_moe_desc* d) {
+  if (!d->has_bias) return 0;
+  const size_t gfs = (size_t)(d->act == TPMLP_ACT_SWIGLU ? 2 : 1) * (size_t)d->ffn_shard;
+  return align_up((size_t)d->experts * (size_t)moe_colsum_parts(d) * gfs * 4, 256);
+}
+
+hipError_t run_group_step(Step step, int group, const char* label, const GemmArgs& g,
+                          const EpiArgs& e, hipStream_t s) {
+  GemmArgs gg = g;
+  if (mfma_group_grid(step, group, gg) <= 0) return hipSuccess;
+  return timed(label, s, [&]() { return mfma_group_launch(step, group, g, e, s); });
 }
 
 GemmArgs make_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
@@ -593,6 +650,125 @@ tpmlp_status tpmlp_attn_qkv_bwd_wgrad(const tpmlp_attn_desc* d, const void* dqkv
     err = timed(attn_label(kind, 6), s, [&]() {
       return colsum_reduce_launch(static_cast<const float*>(ws), attn_colsum_parts(d), (int)N,
                                   dbqkv, accumulate, s);
+    });
+    if (err != hipSuccess) return hip_fail(err);
+  }
+  return TPMLP_OK;
+}
+
+// ---------------------------------------------------------------- mixture of experts
+size_t tpmlp_moe_workspace_size(const tpmlp_moe_desc* d) {
+  if (check_moe_desc(d) != TPMLP_OK) return 0;
+  return moe_workspace_bytes(d);
+}
+
+namespace {
+void set_groups(GemmArgs& g, const tpmlp_moe_desc* d, const int32_t* counts) {
+  g.counts = counts;
+  g.groups = d->experts;
+  g.rows = (int)d->tokens;
+}
+}  // namespace
+
+tpmlp_status tpmlp_moe_fwd(const tpmlp_moe_desc* d, const int32_t* counts, const void* x,
+                           const void* W1, const void* b1, const void* W2, void* y,
+                           void* h_saved, void* a_saved, hipStream_t s) {
+  tpmlp_status st = check_moe_desc(d);
+  if (st != TPMLP_OK) return st;
+  if ((st = check_ptrs({counts, x, W1, W2, y, a_saved})) != TPMLP_OK) return st;
+  if (d->has_bias && (st = check_ptrs({b1})) != TPMLP_OK) return st;
+  if (h_saved && !aligned16(h_saved)) return TPMLP_E_ALIGN;
+  const int64_t T = d->tokens, H = d->hidden, Fs = d->ffn_shard;
+  if (T == 0) return TPMLP_OK;
+  const bool swiglu = d->act == TPMLP_ACT_SWIGLU;
+  const int64_t GFs = swiglu ? 2 * Fs : Fs;
+  EpiArgs e1{};
+  e1.out = a_saved; e1.ldo = Fs;
+  e1.out2 = h_saved; e1.ldo2 = GFs;
+  e1.bias = d->has_bias ? b1 : nullptr;
+  GemmArgs g1 = make_gemm(x, H, W1, H, T, Fs, H, Fs);
+  set_groups(g1, d, counts);
+  g1.b_gstride = GFs * H;
+  g1.bias_gstride = GFs;
+  hipError_t err = run_group_step(swiglu ? FC1_FWD_SWIGLU : FC1_FWD_GELU, GROUP_M, moe_label(0),
+                                  g1, e1, s);
+  if (err != hipSuccess) return hip_fail(err);
+  EpiArgs e2{};
+  e2.out = y; e2.ldo = H;
+  GemmArgs g2 = make_gemm(a_saved, Fs, W2, Fs, T, H, Fs, 0);
+  set_groups(g2, d, counts);
+  g2.b_gstride = H * Fs;
+  err = run_group_step(FC2_FWD, GROUP_M, moe_label(1), g2, e2, s);
+  return err == hipSuccess ? TPMLP_OK : hip_fail(err);
+}
+
+tpmlp_status tpmlp_moe_bwd_dgrad(const tpmlp_moe_desc* d, const int32_t* counts, const void* dy,
+                                 const void* W1, const void* W2, const void* h_saved, void* dH,
+                                 void* dx, hipStream_t s) {
+  tpmlp_status st = check_moe_desc(d);
+  if (st != TPMLP_OK) return st;
+  if ((st = check_ptrs({counts, dy, W1, W2, h_saved, dH, dx})) != TPMLP_OK) return st;
+  const int64_t T = d->tokens, H = d->hidden, Fs = d->ffn_shard;
+  if (T == 0) return TPMLP_OK;
+  const bool swiglu = d->act == TPMLP_ACT_SWIGLU;
+  const int64_t GFs = swiglu ? 2 * Fs : Fs;
+  // fc2 dgrad per expert: dA = dy . W2[e], activation derivative fused
+  EpiArgs e1{};
+  e1.out = dH; e1.ldo = GFs;
+  e1.aux = h_saved; e1.ldaux = GFs;
+  GemmArgs g1 = make_gemm(dy, H, W2, Fs, T, Fs, H, Fs);
+  set_groups(g1, d, counts);
+  g1.b_gstride = H * Fs;
+  hipError_t err = run_group_step(swiglu ? FC2_DGRAD_SWIGLU : FC2_DGRAD_GELU, GROUP_M,
+                                  moe_label(2), g1, e1, s);
+  if (err != hipSuccess) return hip_fail(err);
+  // fc1 dgrad per expert: dx = dH . W1[e]
+  EpiArgs e2{};
+  e2.out = dx; e2.ldo = H;
+  GemmArgs g2 = make_gemm(dH, GFs, W1, H, T, H, GFs, 0);
+  set_groups(g2, d, counts);
+  g2.b_gstride = GFs * H;
+  err = run_group_step(FC1_DGRAD, GROUP_M, moe_label(3), g2, e2, s);
+  return err == hipSuccess ? TPMLP_OK : hip_fail(err);
+}
+
+tpmlp_status tpmlp_moe_bwd_wgrad(const tpmlp_moe_desc* d, const int32_t* counts, const void* dy,
+                                 const void* x, const void* a_saved, const void* dH, float* dW1,
+                                 float* db1, float* dW2, int32_t accumulate, void* ws,
+                                 size_t ws_bytes, hipStream_t s) {
+  tpmlp_status st = check_moe_desc(d);
+  if (st != TPMLP_OK) return st;
+  if (accumulate != 0 && accumulate != 1) return TPMLP_E_DTYPE;
+  if ((st = check_ptrs({counts, dy, x, a_saved, dH, dW1, dW2})) != TPMLP_OK) return st;
+  if (d->has_bias && (st = check_ptrs({db1})) != TPMLP_OK) return st;
+  const size_t need = moe_workspace_bytes(d);
+  if (need && (!ws || ws_bytes < need)) return TPMLP_E_WORKSPACE;
+  if (need && !aligned16(ws)) return TPMLP_E_ALIGN;
+  const int64_t T = d->tokens, H = d->hidden, Fs = d->ffn_shard;
+  if (T == 0 && accumulate) return TPMLP_OK;  // adding nothing
+  const bool swiglu = d->act == TPMLP_ACT_SWIGLU;
+  const int64_t GFs = swiglu ? 2 * Fs : Fs;
+  // dW2[e] [H, Fs] = dy_e^T . a_e over expert e's rows
+  EpiArgs e1{};
+  e1.out = dW2; e1.ldo = Fs; e1.accumulate = accumulate;
+  GemmArgs g1 = make_gemm(dy, H, a_saved, Fs, H, Fs, T, 0);
+  set_groups(g1, d, counts);
+  g1.out_gstride = H * Fs;
+  hipError_t err = run_group_step(WGRAD, GROUP_K, moe_label(4), g1, e1, s);
+  if (err != hipSuccess) return hip_fail(err);
+  // dW1[e] [GFs, H] = dH_e^T . x_e (+ per-expert column-sum partials of dH_e)
+  EpiArgs e2{};
+  e2.out = dW1; e2.ldo = H; e2.accumulate = accumulate;
+  e2.colsum = d->has_bias ? static_cast<float*>(ws) : nullptr;
+  GemmArgs g2 = make_gemm(dH, GFs, x, H, GFs, H, T, 0);
+  set_groups(g2, d, counts);
+  g2.out_gstride = GFs * H;
+  err = run_group_step(d->has_bias ? WGRAD_COLSUM : WGRAD, GROUP_K, moe_label(5), g2, e2, s);
+  if (err != hipSuccess) return hip_fail(err);
+  if (d->has_bias) {
+    err = timed(moe_label(6), s, [&]() {
+      return colsum_reduce_launch(static_cast<const float*>(ws), moe_colsum_parts(d), (int)GFs,
+                                  db1, accumulate, s, d->experts);
     });
     if (err != hipSuccess) return hip_fail(err);
   }

@@ -36,6 +36,17 @@ enum EpiKind : int {
   EPI_BIAS = 8,         // bias added, no activation (attention's QKV projection)
 };
 
+// Grouped products (the expert MLPs of a mixture-of-experts layer): group e
+// owns the rows [off_e, off_e + c_e) of the token-major tensors, off_e the
+// sum of the counts before it, and its own block of each per-group tensor.
+//   GROUP_M: the tokens are M (forward, data gradients): A and the outputs
+//            are token-major; B (the weight) and the bias are per group.
+//   GROUP_K: the tokens are K (weight gradients): A and B are token-major;
+//            the output and the column-sum partials are per group.
+// Counts are read on the device and clamped (negative as 0, prefix sums
+// saturated at `rows`), so no row outside [0, rows) is touched.
+enum GroupKind : int { GROUP_NONE = 0, GROUP_M = 1, GROUP_K = 2 };
+
 struct GemmArgs {
   const void* A;
   const void* B;
@@ -43,6 +54,13 @@ struct GemmArgs {
   int M, N, K;     // N: output columns (for the gated fc1: the Fs pair columns)
   int pair_off;    // gated blocks: Fs (offset between gate and up rows/columns)
   int tiles_m, tiles_n, group_m;
+  // grouped products only
+  const int* counts;       // [groups] rows per group (device)
+  int groups;
+  int rows;                // rows of the token-major tensors
+  int64_t b_gstride;       // GROUP_M: elements between groups' B blocks
+  int64_t out_gstride;     // GROUP_K: elements between groups' output blocks
+  int64_t bias_gstride;    // GROUP_M: elements between groups' biases
 };
 
 struct EpiArgs {

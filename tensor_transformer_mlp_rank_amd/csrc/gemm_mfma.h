@@ -77,21 +77,107 @@ constexpr int kTileBytes = 256 * kRowBytes;        // 32 KiB
 constexpr int kStageBytes = 2 * kTileBytes;        // A + B
 constexpr int kSmemBytes = kStages * kStageBytes;  // 128 KiB
 
-__device__ __forceinline__ void tile_coords(const GemmArgs& g, int bid, int& bm, int& bn) {
-  const int nb = g.tiles_m * g.tiles_n;
-  // XCD remap: hardware sends workgroup b to XCD b % 8.
+// XCD remap: hardware sends workgroup b to XCD b % 8; this gives the
+// workgroups of one XCD consecutive ids out of nb.
+__device__ __forceinline__ int xcd_remap(int bid, int nb) {
   const int xcd = bid & 7, local = bid >> 3;
   const int q = nb >> 3, r = nb & 7;
-  const int id = xcd * q + (xcd < r ? xcd : r) + local;
-  // grouped walk over M-tiles
-  const int per_group = g.group_m * g.tiles_n;
+  return xcd * q + (xcd < r ? xcd : r) + local;
+}
+// Walk over the tiles in groups of group_m M-tiles (all N-tiles of a group
+// before the next), so consecutive ids share A and B panels in L2.
+__device__ __forceinline__ void tile_walk(int id, int tiles_m, int tiles_n, int group_m, int& bm,
+                                          int& bn) {
+  const int per_group = group_m * tiles_n;
   const int grp = id / per_group;
-  const int first_m = grp * g.group_m;
-  int gsz = g.tiles_m - first_m;
-  if (gsz > g.group_m) gsz = g.group_m;
+  const int first_m = grp * group_m;
+  int gsz = tiles_m - first_m;
+  if (gsz > group_m) gsz = group_m;
   const int in = id - grp * per_group;
   bm = first_m + in % gsz;
   bn = in / gsz;
+}
+__device__ __forceinline__ void tile_coords(const GemmArgs& g, int bid, int& bm, int& bn) {
+  tile_walk(xcd_remap(bid, g.tiles_m * g.tiles_n), g.tiles_m, g.tiles_n, g.group_m, bm, bn);
+}
+
+// Grouped products. Each wave scans the group counts 64 groups per pass with
+// a saturating prefix sum (every wave of a workgroup gets the same, uniform
+// results). GROUP_M: group e has ceil(c_e / 256) M-tiles times tiles_n;
+// GROUP_K: every group has tiles_m x tiles_n tiles.
+// group_scan returns the total number of tiles; with target >= 0 it also
+// fills `hit` with the group holding tile `target`, its first row, its row
+// count and the tile's index within the group (hit.e = -1: none).
+struct GroupHit {
+  int e, local, off, cnt;
+};
+template <int GROUP>
+__device__ __forceinline__ int group_scan(const GemmArgs& g, int target, int lane, GroupHit& hit) {
+  const uint32_t R = (uint32_t)g.rows;
+  const int per = g.tiles_m * g.tiles_n;
+  const int want = (GROUP == GROUP_K && target >= 0) ? target / per : -1;
+  hit.e = -1;
+  uint32_t row_base = 0;
+  int tile_base = 0;
+  for (int p0 = 0; p0 < g.groups; p0 += 64) {
+    const int j = p0 + lane;
+    const int c = (j < g.groups) ? g.counts[j] : 0;
+    uint32_t cu = c > 0 ? (uint32_t)c : 0u;
+    if (cu > R) cu = R;
+    uint32_t incl = cu;  // saturating inclusive prefix within the pass
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = (uint32_t)__shfl_up((int)incl, d, 64);
+      if (lane >= d) incl = (incl + o > R) ? R : incl + o;
+    }
+    uint32_t excl = (uint32_t)__shfl_up((int)incl, 1, 64);
+    if (lane == 0) excl = 0;
+    uint32_t start = row_base + excl, end = row_base + incl;
+    if (start > R) start = R;
+    if (end > R) end = R;
+    const int cnt = (int)(end - start);
+    int tiles = 0, t_incl = 0;
+    if constexpr (GROUP == GROUP_M) {
+      tiles = (j < g.groups) ? ((cnt + kBM - 1) / kBM) * g.tiles_n : 0;
+      t_incl = tiles;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(t_incl, d, 64);
+        if (lane >= d) t_incl += o;
+      }
+    }
+    const int t_start = tile_base + t_incl - tiles;
+    if (target >= 0 && hit.e < 0) {
+      const bool mine = (GROUP == GROUP_M)
+                            ? (tiles > 0 && target >= t_start && target < t_start + tiles)
+                            : (j == want);
+      const uint64_t bal = __ballot(mine);
+      if (bal) {
+        const int src = __builtin_ctzll(bal);
+        hit.e = p0 + src;
+        hit.off = __builtin_amdgcn_readlane((int)start, src);
+        hit.cnt = __builtin_amdgcn_readlane(cnt, src);
+        hit.local = (GROUP == GROUP_M) ? target - __builtin_amdgcn_readlane(t_start, src)
+                                       : target % per;
+        if (GROUP == GROUP_K) return g.groups * per;
+      }
+    }
+    row_base += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    if (row_base > R) row_base = R;
+    tile_base += __builtin_amdgcn_readlane(t_incl, 63);
+  }
+  return (GROUP == GROUP_K) ? g.groups * per : tile_base;
+}
+// The tile of workgroup `bid`: the launch has an upper bound of workgroups
+// (GROUP_M) or exactly the tiles (GROUP_K); ids past the real total exit.
+// The XCD remap runs over the real total, so each XCD gets a contiguous run
+// of tiles and the surplus workgroups are spread over all XCDs.
+template <int GROUP>
+__device__ __forceinline__ bool find_group(const GemmArgs& g, int bid, int lane, GroupHit& hit) {
+  const int total = group_scan<GROUP>(g, -1, lane, hit);
+  if (bid >= total) return false;
+  group_scan<GROUP>(g, xcd_remap(bid, total), lane, hit);
+  return hit.e >= 0;
 }
 
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, char* lds_wave_base,
@@ -488,10 +574,13 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e,
 // type of EPI_STORE's output and of the activation tensors (h, a, dH).
 // COLSUM: also reduce A over k into the per-tile-column partial sums
 // e.colsum (A must be MN-major; FP8 sums are scaled by *e.scale_a).
-template <bool IS_FP8, bool A_K, bool B_K, int EPI, typename OutT, bool COLSUM, int FMT = 0>
-__global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g, const EpiArgs e) {
+template <bool IS_FP8, bool A_K, bool B_K, int EPI, typename OutT, bool COLSUM, int FMT = 0,
+          int GROUP = GROUP_NONE>
+__global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g_in,
+                                                                const EpiArgs e_in) {
   static_assert(!COLSUM || !A_K, "the fused column sum reads an MN-major A tile");
   static_assert(IS_FP8 || FMT == 0, "formats select FP8 encodings");
+  static_assert(GROUP == GROUP_NONE || !IS_FP8, "grouped products are bf16");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   constexpr bool kPair = (EPI == EPI_SWIGLU);
   constexpr int esz = IS_FP8 ? 1 : 2;
@@ -499,8 +588,33 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  GemmArgs g = g_in;
+  EpiArgs e = e_in;
   int bm, bn;
-  tile_coords(g, blockIdx.x, bm, bn);
+  if constexpr (GROUP == GROUP_NONE) {
+    tile_coords(g, blockIdx.x, bm, bn);
+  } else {
+    GroupHit hit;
+    if (!find_group<GROUP>(g, blockIdx.x, lane, hit)) return;
+    // rebase every tensor on the group's rows or on its own block
+    constexpr int64_t kOut = (EPI == EPI_F32) ? 4 : 2;  // output element bytes
+    g.A = static_cast<const char*>(g.A) + (int64_t)hit.off * g.lda * esz;
+    if constexpr (GROUP == GROUP_M) {
+      g.M = hit.cnt;
+      g.tiles_m = (hit.cnt + kBM - 1) / kBM;
+      g.B = static_cast<const char*>(g.B) + (int64_t)hit.e * g.b_gstride * esz;
+      e.out = static_cast<char*>(e.out) + (int64_t)hit.off * e.ldo * kOut;
+      if (e.out2) e.out2 = static_cast<char*>(e.out2) + (int64_t)hit.off * e.ldo2 * 2;
+      if (e.aux) e.aux = static_cast<const char*>(e.aux) + (int64_t)hit.off * e.ldaux * 2;
+      if (e.bias) e.bias = static_cast<const char*>(e.bias) + (int64_t)hit.e * g.bias_gstride * 2;
+    } else {
+      g.K = hit.cnt;
+      g.B = static_cast<const char*>(g.B) + (int64_t)hit.off * g.ldb * esz;
+      e.out = static_cast<char*>(e.out) + (int64_t)hit.e * g.out_gstride * kOut;
+      if (e.colsum) e.colsum += (int64_t)hit.e * g.tiles_n * g.M;
+    }
+    tile_walk(hit.local, g.tiles_m, g.tiles_n, g.group_m, bm, bn);
+  }
   const int m0 = bm * kBM;
   const int n0 = bn * (kPair ? kBN / 2 : kBN);
   const int nk = (g.K + kStep - 1) / kStep;

@@ -21,11 +21,15 @@ hipError_t launch_f32(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
 // takes 64 columns; its four waves each add every fourth row (r = w, w + 4,
 // ...), loads issued eight at a time, and wave 0 adds the four sums in wave
 // order: a fixed order, so the result is reproducible bit for bit.
+// Groups (blockIdx.y) are independent: group y reads part + y * nparts * M
+// and writes out + y * M.
 __global__ void __launch_bounds__(256) colsum_reduce_kernel(const float* __restrict__ part,
                                                             int nparts, int M,
                                                             float* __restrict__ out,
                                                             int accumulate) {
   __shared__ float red[4][64];
+  part += (int64_t)blockIdx.y * nparts * M;
+  out += (int64_t)blockIdx.y * M;
   const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int m = blockIdx.x * 64 + c;
   float s = 0.f;
@@ -51,10 +55,10 @@ __global__ void __launch_bounds__(256) colsum_reduce_kernel(const float* __restr
 }  // namespace
 
 hipError_t colsum_reduce_launch(const float* part, int nparts, int M, float* out, int accumulate,
-                                hipStream_t s) {
-  if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((M + 63) / 64), dim3(256), 0, s, part, nparts, M,
-                     out, accumulate);
+                                hipStream_t s, int groups) {
+  if (M <= 0 || groups <= 0) return hipSuccess;
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((M + 63) / 64, groups), dim3(256), 0, s, part,
+                     nparts, M, out, accumulate);
   return hipGetLastError();
 }
 

@@ -6,9 +6,10 @@ namespace tpmlp {
 
 namespace {
 
-template <bool IS_FP8, bool A_K, bool B_K, int EPI, bool COLSUM, int FMT = 0>
-hipError_t launch_one(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
-  auto* k = &gemm_mfma_kernel<IS_FP8, A_K, B_K, EPI, bf16_t, COLSUM, FMT>;
+template <bool IS_FP8, bool A_K, bool B_K, int EPI, bool COLSUM, int FMT = 0,
+          int GROUP = GROUP_NONE>
+hipError_t launch_one(const GemmArgs& g, const EpiArgs& e, hipStream_t s, int64_t nb = -1) {
+  auto* k = &gemm_mfma_kernel<IS_FP8, A_K, B_K, EPI, bf16_t, COLSUM, FMT, GROUP>;
   // the LDS allowance is raised once per instantiation and device
   static bool attr_set[64] = {};
   int dev = 0;
@@ -21,8 +22,8 @@ hipError_t launch_one(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
     if (err != hipSuccess) return err;
     attr_set[dev] = true;
   }
-  const int nb = g.tiles_m * g.tiles_n;
-  hipLaunchKernelGGL(k, dim3(nb), dim3(kThreads), kSmemBytes, s, g, e);
+  if (nb < 0) nb = (int64_t)g.tiles_m * g.tiles_n;
+  hipLaunchKernelGGL(k, dim3((unsigned)nb), dim3(kThreads), kSmemBytes, s, g, e);
   return hipGetLastError();
 }
 
@@ -36,6 +37,50 @@ int mfma_grid(Step step, GemmArgs& g) {
   g.group_m = 8;
   if (g.M <= 0 || g.N <= 0) return 0;
   return g.tiles_m * g.tiles_n;
+}
+
+int64_t mfma_group_grid(Step step, int group, GemmArgs& g) {
+  mfma_grid(step, g);  // tiles_n (and tiles_m of one group for GROUP_K)
+  if (g.groups <= 0 || g.N <= 0) return 0;
+  if (group == GROUP_M) {
+    // at most ceil(rows / 256) + groups M-tiles over all groups
+    if (g.rows <= 0) return 0;
+    return ((int64_t)(g.rows + kBM - 1) / kBM + g.groups) * g.tiles_n;
+  }
+  if (g.M <= 0) return 0;
+  return (int64_t)g.groups * g.tiles_m * g.tiles_n;
+}
+
+hipError_t mfma_group_launch(Step step, int group, const GemmArgs& g0, const EpiArgs& e,
+                             hipStream_t s) {
+  GemmArgs g = g0;
+  const int64_t nb = mfma_group_grid(step, group, g);
+  if (nb <= 0) return hipSuccess;
+  if (group == GROUP_M) {
+    switch (step) {
+      case FC1_FWD_GELU:
+        return launch_one<false, true, true, EPI_BIAS_GELU, false, 0, GROUP_M>(g, e, s, nb);
+      case FC1_FWD_SWIGLU:
+        return launch_one<false, true, true, EPI_SWIGLU, false, 0, GROUP_M>(g, e, s, nb);
+      case FC2_FWD: return launch_one<false, true, true, EPI_STORE, false, 0, GROUP_M>(g, e, s, nb);
+      case FC2_DGRAD_GELU:
+        return launch_one<false, true, false, EPI_DGELU, false, 0, GROUP_M>(g, e, s, nb);
+      case FC2_DGRAD_SWIGLU:
+        return launch_one<false, true, false, EPI_DSWIGLU, false, 0, GROUP_M>(g, e, s, nb);
+      case FC1_DGRAD:
+        return launch_one<false, true, false, EPI_STORE, false, 0, GROUP_M>(g, e, s, nb);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (group == GROUP_K) {
+    switch (step) {
+      case WGRAD: return launch_one<false, false, false, EPI_F32, false, 0, GROUP_K>(g, e, s, nb);
+      case WGRAD_COLSUM:
+        return launch_one<false, false, false, EPI_F32, true, 0, GROUP_K>(g, e, s, nb);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t mfma_launch(bool fp8, Step step, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {

@@ -34,11 +34,20 @@ int f32_grid(Step step, GemmArgs& g);
 // Enqueue one GEMM step; `g` must have its grid fields filled.
 hipError_t mfma_launch(bool fp8, Step step, const GemmArgs& g, const EpiArgs& e,
                        hipStream_t stream);
+
+// Grouped (bf16) GEMM steps. `g` carries the per-group tile grid (tiles_m,
+// tiles_n of one group; for GROUP_M tiles_m is that of the largest possible
+// group) and the group fields; the launch covers every group's tiles.
+// Returns the number of workgroups launched (0: nothing to launch).
+int64_t mfma_group_grid(Step step, int group, GemmArgs& g);
+hipError_t mfma_group_launch(Step step, int group, const GemmArgs& g, const EpiArgs& e,
+                             hipStream_t stream);
 hipError_t f32_launch(Step step, const GemmArgs& g, const EpiArgs& e, hipStream_t stream);
 
-// db1 from the MFMA kernel's [nparts][M] column-sum partials.
+// db1 from the MFMA kernel's [nparts][M] column-sum partials ([groups] of
+// them, one output row of M each).
 hipError_t colsum_reduce_launch(const float* part, int nparts, int M, float* out, int accumulate,
-                                hipStream_t stream);
+                                hipStream_t stream, int groups = 1);
 
 // Quantiser passes. src_bf16 selects the source type (bf16 or f32).
 int quant_parts(int64_t n);

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert tp.lib.tpmlp_abi_version() == 4
+    assert tp.lib.tpmlp_abi_version() == 5
     for s in range(8):
         assert len(tp.lib.tpmlp_strerror(s)) > 5
     assert tp.lib.tpmlp_last_hip_error() == b""
@@ -276,3 +276,64 @@ def test_attn_workspace():
     assert L.tpmlp_attn_qkv_bwd_wgrad(b, P, P, P, P, 0, None, 0, None) == E_WS
     assert L.tpmlp_attn_qkv_bwd_wgrad(b, P, P, P, P, 0, P, n - 1, None) == E_WS
     assert L.tpmlp_attn_qkv_bwd_wgrad(b, P, P, P, P, 0, MIS, n, None) == E_ALIGN
+
+
+# ------------------------------------------------------------------ mixture of experts
+def Mo(**kw):
+    base = dict(tokens=1000, hidden=256, ffn_shard=128, experts=8, act="gelu", dtype="bf16",
+                has_bias=True)
+    base.update(kw)
+    return tp.make_moe_desc(**base)
+
+
+def moe_calls(d, p=P, acc=0, ws=None, nbytes=0, bias=P, counts=P):
+    b = ctypes.byref(d) if d is not None else None
+    L = tp.lib
+    return [L.tpmlp_moe_fwd(b, counts, p, p, bias, p, p, p, p, None),
+            L.tpmlp_moe_bwd_dgrad(b, counts, p, p, p, p, p, p, None),
+            L.tpmlp_moe_bwd_wgrad(b, counts, p, p, p, p, p, bias, p, acc, ws, nbytes, None)]
+
+
+def test_moe_desc_struct_layout():
+    assert ctypes.sizeof(tp.MoeDesc) == 48
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tokens=-1), E_SHAPE), (dict(hidden=0), E_SHAPE), (dict(ffn_shard=24), E_SHAPE),
+    (dict(experts=0), E_SHAPE), (dict(experts=1025), E_SHAPE), (dict(hidden=1 << 22), E_SHAPE),
+    (dict(tokens=1 << 30, hidden=1 << 21, experts=1024), E_SHAPE),
+    (dict(dtype=9), E_DTYPE), (dict(act=5), E_DTYPE),
+    (dict(dtype="f32"), E_UNSUP), (dict(dtype="e4m3"), E_UNSUP),
+    (dict(act="swiglu", has_bias=True), E_UNSUP),
+])
+def test_moe_desc_validation(kw, code):
+    assert moe_calls(Mo(**kw)) == [code] * 3
+
+
+def test_moe_null_reserved_pointers():
+    assert moe_calls(None) == [E_NULL] * 3
+    for f in ("reserved0", "reserved1", "has_bias"):
+        d = Mo()
+        setattr(d, f, 2)
+        assert moe_calls(d) == [E_DTYPE] * 3, f
+    assert moe_calls(Mo(), counts=None) == [E_NULL] * 3
+    assert moe_calls(Mo(), p=None) == [E_NULL] * 3
+    assert moe_calls(Mo(), p=MIS) == [E_ALIGN] * 3
+    assert moe_calls(Mo(), counts=MIS) == [E_ALIGN] * 3
+
+
+def test_moe_bias_accumulate_workspace():
+    L, d = tp.lib, Mo()
+    b = ctypes.byref(d)
+    assert L.tpmlp_moe_fwd(b, P, P, P, None, P, P, P, P, None) == E_NULL
+    n = tp.moe_workspace_size(d)
+    tiles_n = (256 + 255) // 256
+    assert n == ((8 * tiles_n * 128 * 4 + 255) // 256) * 256
+    assert tp.moe_workspace_size(Mo(has_bias=False)) == 0
+    assert tp.moe_workspace_size(Mo(act="swiglu", has_bias=False)) == 0
+    assert tp.moe_workspace_size(Mo(dtype="f32")) == 0
+    assert L.tpmlp_moe_bwd_wgrad(b, P, P, P, P, P, P, None, P, 0, P, n, None) == E_NULL
+    assert L.tpmlp_moe_bwd_wgrad(b, P, P, P, P, P, P, P, P, 2, P, n, None) == E_DTYPE
+    assert L.tpmlp_moe_bwd_wgrad(b, P, P, P, P, P, P, P, P, 0, None, 0, None) == E_WS
+    assert L.tpmlp_moe_bwd_wgrad(b, P, P, P, P, P, P, P, P, 0, P, n - 1, None) == E_WS
+    assert L.tpmlp_moe_bwd_wgrad(b, P, P, P, P, P, P, P, P, 0, MIS, n, None) == E_ALIGN
