@@ -343,8 +343,8 @@ def attn_job(tp, torch, w, dev) -> Job:
         tp.tpmlp_attn_out_fwd(desc, d["ctx"], d["Wo"], buf["y"], stream=stream)
 
     def bwd():
-        tp.tpmlp_attn_out_bwd_dgrad(desc, d["dy"], d["Wo"], buf["dctx"], stream=stream)
-        tp.tpmlp_attn_out_bwd_wgrad(desc, d["dy"], d["ctx"], buf["dWo"], True, stream=stream)
+        tp.tpmlp_attn_out_bwd_dgrad(desc, d["dy"], d["Wo"], buf["dctx"], ws, stream=stream)
+        tp.tpmlp_attn_out_bwd_wgrad(desc, d["dy"], d["ctx"], buf["dWo"], True, ws, stream=stream)
         tp.tpmlp_attn_qkv_bwd_dgrad(desc, d["dqkv"], d["Wqkv"], buf["dx"], stream=stream)
         tp.tpmlp_attn_qkv_bwd_wgrad(desc, d["dqkv"], d["x"], buf["dWqkv"], buf["dbqkv"], True,
                                     ws, stream=stream)

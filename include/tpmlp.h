@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 5
+#define TPMLP_ABI_VERSION 6
 
 typedef enum {
   TPMLP_OK = 0,
@@ -139,12 +139,16 @@ typedef struct tpmlp_fp8_scales {
 } tpmlp_fp8_scales;
 
 /*
- * Bytes of workspace the call needs (0 if none). Returns 0 for an invalid desc.
+ * Bytes of workspace for the call (0 if none). Returns 0 for an invalid desc.
  * Non-zero for: the E4M3 forward (per-workgroup amax partials of a and,
  * with current scaling, the bfloat16 activation before quantisation; the
  * size covers both modes), the E4M3 dgrad (amax partials of dH), and the
- * BF16 or E4M3 weight gradient with bias (per-tile-column partial sums of
- * db1, added up in a fixed order).
+ * weight gradient: with bias, per-tile-column partial sums of db1 (needed),
+ * and for BF16 products whose tile grid would leave compute units idle, the
+ * fp32 partial sums of a split along K (optional: with fewer bytes the
+ * products run unsplit, and the call needs only the db1 partials). Split
+ * products are summed in a fixed order, so results stay reproducible, but
+ * differ in rounding from unsplit ones.
  */
 size_t tpmlp_workspace_size(const tpmlp_desc* desc, int32_t call);
 
@@ -193,9 +197,10 @@ tpmlp_status tpmlp_bwd_dgrad(const tpmlp_desc* desc, const void* dy, const void*
  * and each product is scaled by its two operands' dequantisation factors
  * from fp8 (dy_scale_inv, a_scale_inv, dH_scale_inv, x_scale_inv); db1 is
  * the column sums of the dequantised dH. fp8 must be non-NULL iff dtype is
- * E4M3. Workspace: tpmlp_workspace_size(desc, TPMLP_CALL_WGRAD) bytes (with
- * bias). Results are reproducible bit for bit: every sum is taken in a
- * fixed order, no atomics.
+ * E4M3. Workspace: tpmlp_workspace_size(desc, TPMLP_CALL_WGRAD) bytes (the
+ * db1 partials are required with bias; the split-K part is optional).
+ * Results are reproducible bit for bit: every sum is taken in a fixed order,
+ * no atomics.
  */
 tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* desc, const void* dy, const void* x,
                              const void* a_saved, const void* dH, float* dW1, float* db1,
@@ -268,19 +273,29 @@ tpmlp_status tpmlp_attn_qkv_fwd(const tpmlp_attn_desc* desc, const void* x, cons
 /* y_partial = ctx . Wo^T. */
 tpmlp_status tpmlp_attn_out_fwd(const tpmlp_attn_desc* desc, const void* ctx, const void* Wo,
                                 void* y_partial, hipStream_t stream);
-/* dctx = dy . Wo (dy replicated on every rank). */
+/* dctx = dy . Wo (dy replicated on every rank). The workspace (may be NULL)
+   enables split-K, see tpmlp_attn_workspace_size. */
 tpmlp_status tpmlp_attn_out_bwd_dgrad(const tpmlp_attn_desc* desc, const void* dy,
-                                      const void* Wo, void* dctx, hipStream_t stream);
-/* dWo (+)= dy^T . ctx, float32. */
+                                      const void* Wo, void* dctx, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+/* dWo (+)= dy^T . ctx, float32. Workspace as for tpmlp_attn_out_bwd_dgrad. */
 tpmlp_status tpmlp_attn_out_bwd_wgrad(const tpmlp_attn_desc* desc, const void* dy,
                                       const void* ctx, float* dWo, int32_t accumulate,
+                                      void* workspace, size_t workspace_bytes,
                                       hipStream_t stream);
 /* dx_partial = dqkv . Wqkv. */
 tpmlp_status tpmlp_attn_qkv_bwd_dgrad(const tpmlp_attn_desc* desc, const void* dqkv,
                                       const void* Wqkv, void* dx_partial, hipStream_t stream);
 /* dWqkv (+)= dqkv^T . x and, when has_bias, dbqkv (+)= column sums of dqkv
-   (dbqkv required iff has_bias); float32. Workspace:
-   tpmlp_attn_workspace_size(desc) bytes (0 for float32 or without bias). */
+   (dbqkv required iff has_bias); float32.
+   Workspace of the three backward calls that take one: with
+   tpmlp_attn_workspace_size(desc) bytes (the same buffer serves all three,
+   one call at a time) a bf16 product whose tile grid would leave compute
+   units idle is split along K into fp32 partial sums that a second pass adds
+   up in a fixed order (results do not depend on timing, but differ in
+   rounding from the unsplit product). A smaller workspace (or NULL) runs
+   unsplit; the qkv wgrad with bias in bf16 still needs the bytes of its
+   column-sum partials (TPMLP_E_WORKSPACE otherwise). */
 size_t tpmlp_attn_workspace_size(const tpmlp_attn_desc* desc);
 tpmlp_status tpmlp_attn_qkv_bwd_wgrad(const tpmlp_attn_desc* desc, const void* dqkv,
                                       const void* x, float* dWqkv, float* dbqkv,

@@ -135,8 +135,8 @@ def _load():
     pa = ctypes.POINTER(AttnDesc)
     L.tpmlp_attn_qkv_fwd.argtypes = [pa, vp, vp, vp, vp, vp]
     L.tpmlp_attn_out_fwd.argtypes = [pa, vp, vp, vp, vp]
-    L.tpmlp_attn_out_bwd_dgrad.argtypes = [pa, vp, vp, vp, vp]
-    L.tpmlp_attn_out_bwd_wgrad.argtypes = [pa, vp, vp, vp, i32, vp]
+    L.tpmlp_attn_out_bwd_dgrad.argtypes = [pa, vp, vp, vp, vp, sz, vp]
+    L.tpmlp_attn_out_bwd_wgrad.argtypes = [pa, vp, vp, vp, i32, vp, sz, vp]
     L.tpmlp_attn_qkv_bwd_dgrad.argtypes = [pa, vp, vp, vp, vp]
     L.tpmlp_attn_qkv_bwd_wgrad.argtypes = [pa, vp, vp, vp, vp, i32, vp, sz, vp]
     L.tpmlp_attn_workspace_size.argtypes = [pa]
@@ -363,14 +363,20 @@ def tpmlp_attn_out_fwd(desc, ctx, Wo, y, stream=None):
                                   _stream(stream)), "tpmlp_attn_out_fwd")
 
 
-def tpmlp_attn_out_bwd_dgrad(desc, dy, Wo, dctx, stream=None):
+def _nbytes(workspace):
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
+def tpmlp_attn_out_bwd_dgrad(desc, dy, Wo, dctx, workspace=None, stream=None):
     _check(lib.tpmlp_attn_out_bwd_dgrad(ctypes.byref(desc), _ptr(dy), _ptr(Wo), _ptr(dctx),
-                                        _stream(stream)), "tpmlp_attn_out_bwd_dgrad")
+                                        _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "tpmlp_attn_out_bwd_dgrad")
 
 
-def tpmlp_attn_out_bwd_wgrad(desc, dy, ctx, dWo, accumulate=False, stream=None):
+def tpmlp_attn_out_bwd_wgrad(desc, dy, ctx, dWo, accumulate=False, workspace=None, stream=None):
     _check(lib.tpmlp_attn_out_bwd_wgrad(ctypes.byref(desc), _ptr(dy), _ptr(ctx), _ptr(dWo),
-                                        int(bool(accumulate)), _stream(stream)),
+                                        int(bool(accumulate)), _ptr(workspace),
+                                        _nbytes(workspace), _stream(stream)),
            "tpmlp_attn_out_bwd_wgrad")
 
 
@@ -405,14 +411,20 @@ def attn_out_fwd(desc, ctx, Wo, stream=None):
     return y
 
 
+def _attn_ws(desc, device):
+    n = attn_workspace_size(desc)
+    return _empty((n,), torch.uint8, device) if n else None
+
+
 def attn_out_bwd(desc, dy, Wo, ctx, dWo=None, stream=None):
     """(dctx, dWo); with a given dWo the gradient is added into it."""
     dctx = _empty((desc.tokens, desc.d), _act_t(desc), dy.device)
-    tpmlp_attn_out_bwd_dgrad(desc, dy, Wo, dctx, stream)
+    ws = _attn_ws(desc, dy.device)
+    tpmlp_attn_out_bwd_dgrad(desc, dy, Wo, dctx, ws, stream)
     acc = dWo is not None
     if not acc:
         dWo = _empty((desc.hidden, desc.d), torch.float32, dy.device)
-    tpmlp_attn_out_bwd_wgrad(desc, dy, ctx, dWo, acc, stream)
+    tpmlp_attn_out_bwd_wgrad(desc, dy, ctx, dWo, acc, ws, stream)
     return dctx, dWo
 
 
@@ -425,9 +437,7 @@ def attn_qkv_bwd(desc, dqkv, Wqkv, x, dWqkv=None, dbqkv=None, stream=None):
     if not acc:
         dWqkv = _empty((desc.nqkv, desc.hidden), torch.float32, dqkv.device)
         dbqkv = _empty((desc.nqkv,), torch.float32, dqkv.device) if desc.has_bias else None
-    n = attn_workspace_size(desc)
-    ws = _empty((n,), torch.uint8, dqkv.device) if n else None
-    tpmlp_attn_qkv_bwd_wgrad(desc, dqkv, x, dWqkv, dbqkv, acc, ws, stream)
+    tpmlp_attn_qkv_bwd_wgrad(desc, dqkv, x, dWqkv, dbqkv, acc, _attn_ws(desc, dqkv.device), stream)
     return dx, dWqkv, dbqkv
 
 

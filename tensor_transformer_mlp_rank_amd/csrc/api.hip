@@ -1,7 +1,9 @@
 // libtpmlp C ABI: argument validation, kernel selection and launch, and the
 // kernel timing facility. The interface is documented in include/tpmlp.h.
+#include <math.h>
 #include <string.h>
 
+#include <cmath>
 #include <initializer_list>
 
 #include <string>
@@ -93,6 +95,44 @@ tpmlp_status check_ptrs(std::initializer_list<const void*> req) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// ---------------------------------------------------------------- split-K
+// Splits of K for a bf16 product whose tile grid leaves CUs idle (1 = none).
+// The estimate of s splits: rounds of tiles over the 256 CUs times one tile's
+// share of K (at an assumed 4.7 TFLOP/s per CU), plus writing and reading the
+// s fp32 partial planes (at an assumed 4 TB/s). The best s in 2..4 is taken
+// if it saves at least 10% and every split keeps 8 stages or more.
+int plan_splits(Kind kind, Step step, int64_t M, int64_t N, int64_t K) {
+  if (kind != KIND_BF16) return 1;
+  if (step != FC2_FWD && step != QKV_FWD_BIAS && step != FC1_DGRAD && step != WGRAD &&
+      step != WGRAD_COLSUM)
+    return 1;
+  if (M <= 0 || N <= 0 || K <= 0) return 1;
+  const double tiles = (double)((M + 255) / 256) * (double)((N + 255) / 256);
+  const int64_t stages = (K + 63) / 64;
+  auto est = [&](int sp) {
+    const double rounds = std::ceil(tiles * sp / 256.0);
+    const double t_tile = 2.0 * 256 * 256 * 64.0 * (double)((stages + sp - 1) / sp) / 4.7e12;
+    const double t_red = sp > 1 ? 2.0 * sp * (double)M * (double)N * 4 / 4e12 : 0.0;
+    return rounds * t_tile + t_red;
+  };
+  const double t1 = est(1);
+  int best = 1;
+  double tb = 0.9 * t1;
+  for (int sp = 2; sp <= 4; ++sp) {
+    if (stages < 8 * sp) break;
+    const double t = est(sp);
+    if (t < tb) {
+      tb = t;
+      best = sp;
+    }
+  }
+  return best;
+}
+size_t split_bytes(int sp, int64_t M, int64_t N) {
+  return sp > 1 ? align_up((size_t)sp * (size_t)M * (size_t)N * 4, 256) : 0;
+}
+
+
 // workgroups of the MFMA kernel for an M x N product (one per 256 x 256 tile)
 int gemm_tiles(int64_t M, int64_t N) {
   GemmArgs g{};
@@ -116,6 +156,29 @@ int colsum_parts(const tpmlp_desc* d) {
   return g.tiles_n;
 }
 
+// The MLP wgrad's split plans (fc2's dW2, fc1's dW1) and its workspace: the
+// db1 partial rows of the column sums (sp1 * tiles_n of them), then the
+// partial planes of the larger split product.
+struct WgradPlan {
+  int sp2, sp1;
+  size_t colsum, planes;
+};
+WgradPlan wgrad_plan(const tpmlp_desc* d, bool split_ok) {
+  const Kind kind = d->dtype == TPMLP_F32 ? KIND_F32 : d->dtype == TPMLP_BF16 ? KIND_BF16 : KIND_E4M3;
+  const int64_t gfs = (d->act == TPMLP_ACT_SWIGLU ? 2 : 1) * d->ffn_shard;
+  WgradPlan p{1, 1, 0, 0};
+  if (split_ok) {
+    p.sp2 = plan_splits(kind, WGRAD, d->hidden, d->ffn_shard, d->tokens);
+    p.sp1 = plan_splits(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, gfs, d->hidden, d->tokens);
+  }
+  if (d->has_bias && kind != KIND_F32)
+    p.colsum = align_up((size_t)p.sp1 * (size_t)colsum_parts(d) * (size_t)gfs * 4, 256);
+  const size_t a = split_bytes(p.sp2, d->hidden, d->ffn_shard);
+  const size_t b = split_bytes(p.sp1, gfs, d->hidden);
+  p.planes = a > b ? a : b;
+  return p;
+}
+
 size_t workspace_bytes(const tpmlp_desc* d, int32_t call) {
   const bool fp8 = d->dtype == TPMLP_E4M3;
   if (call == TPMLP_CALL_FWD && fp8) {
@@ -125,11 +188,17 @@ size_t workspace_bytes(const tpmlp_desc* d, int32_t call) {
     return a_bytes + parts;
   }
   if (call == TPMLP_CALL_DGRAD && fp8) return align_up((size_t)fp8_dgrad_parts(d) * 4 + 4, 256);
-  if (call == TPMLP_CALL_WGRAD && d->dtype != TPMLP_F32 && d->has_bias) {
-    const size_t gfs = (size_t)(d->act == TPMLP_ACT_SWIGLU ? 2 : 1) * (size_t)d->ffn_shard;
-    return align_up((size_t)colsum_parts(d) * gfs * 4, 256);
+  if (call == TPMLP_CALL_WGRAD) {
+    const WgradPlan p = wgrad_plan(d, true);
+    return p.colsum + p.planes;
   }
   return 0;
+}
+// The part of the workspace a call cannot run without (the rest only enables
+// split-K).
+size_t workspace_min_bytes(const tpmlp_desc* d, int32_t call) {
+  if (call == TPMLP_CALL_WGRAD) return wgrad_plan(d, false).colsum;
+  return workspace_bytes(d, call);
 }
 
 // A delayed-scaling state: pointers present, length in range.
@@ -140,7 +209,7 @@ tpmlp_status check_history(const tpmlp_fp8_history* h) {
 }
 
 tpmlp_status check_workspace(const tpmlp_desc* d, int32_t call, void* ws, size_t ws_bytes) {
-  const size_t need = workspace_bytes(d, call);
+  const size_t need = workspace_min_bytes(d, call);
   if (need == 0) return TPMLP_OK;
   if (!ws || ws_bytes < need) return TPMLP_E_WORKSPACE;
   if (!aligned16(ws)) return TPMLP_E_ALIGN;
@@ -156,6 +225,29 @@ hipError_t run_step(Kind kind, Step step, const char* label, GemmArgs g, const E
   return timed(label, s, [&]() {
     return kind == KIND_F32 ? f32_launch(step, g, e, s)
                             : mfma_launch(kind == KIND_E4M3, step, g, e, s);
+  });
+}
+
+// One product: split-K when `sp` > 1 (the caller checked that `part` holds
+// the sp partial planes), else the plain kernel. The timing facility brackets
+// the product and its reduce together under `label`. A fused column sum then
+// writes sp * tiles_n partial rows.
+hipError_t run_gemm(Kind kind, Step step, const char* label, GemmArgs g, const EpiArgs& e,
+                    hipStream_t s, int sp, float* part) {
+  if (sp < 2) return run_step(kind, step, label, g, e, s);
+  if (mfma_grid(step, g) == 0) return hipSuccess;
+  g.k_splits = sp;
+  g.split_stages = (int)(((g.K + 63) / 64 + sp - 1) / sp);
+  EpiArgs ep = e;
+  ep.out = part;
+  ep.ldo = g.N;
+  ep.accumulate = 0;
+  const bool out_bf16 = step != WGRAD && step != WGRAD_COLSUM;
+  return timed(label, s, [&]() {
+    hipError_t err = mfma_split_launch(step, g, ep, s);
+    if (err != hipSuccess) return err;
+    return splitk_reduce_launch(part, sp, g.M, g.N, e.out, out_bf16,
+                                step == QKV_FWD_BIAS ? e.bias : nullptr, e.accumulate, s);
   });
 }
 
@@ -211,9 +303,47 @@ int attn_colsum_parts(const tpmlp_attn_desc* d) {
   mfma_grid(WGRAD_COLSUM, g);
   return g.tiles_n;
 }
+// Split plans of the attention backward's products and the workspace each
+// call needs: the qkv wgrad's dbqkv partial rows first, then partial planes.
+struct AttnPlan {
+  int sp_od, sp_ow, sp_qw;
+  size_t colsum;  // qkv wgrad's dbqkv partial rows
+};
+AttnPlan attn_plan(const tpmlp_attn_desc* d, bool split_ok) {
+  const Kind kind = attn_kind(d);
+  AttnPlan p{1, 1, 1, 0};
+  if (split_ok) {
+    p.sp_od = plan_splits(kind, FC1_DGRAD, d->tokens, attn_d(d), d->hidden);
+    p.sp_ow = plan_splits(kind, WGRAD, d->hidden, attn_d(d), d->tokens);
+    p.sp_qw = plan_splits(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, attn_nqkv(d), d->hidden,
+                          d->tokens);
+  }
+  if (d->has_bias && kind != KIND_F32)
+    p.colsum = align_up((size_t)p.sp_qw * (size_t)attn_colsum_parts(d) * (size_t)attn_nqkv(d) * 4,
+                        256);
+  return p;
+}
+// which: 0 out dgrad, 1 out wgrad, 2 qkv wgrad
+size_t attn_call_bytes(const tpmlp_attn_desc* d, const AttnPlan& p, int which) {
+  if (which == 0) return split_bytes(p.sp_od, d->tokens, attn_d(d));
+  if (which == 1) return split_bytes(p.sp_ow, d->hidden, attn_d(d));
+  return p.colsum + split_bytes(p.sp_qw, attn_nqkv(d), d->hidden);
+}
 size_t attn_workspace_bytes(const tpmlp_attn_desc* d) {
-  if (d->dtype == TPMLP_F32 || !d->has_bias) return 0;
-  return align_up((size_t)attn_colsum_parts(d) * (size_t)attn_nqkv(d) * 4, 256);
+  const AttnPlan p = attn_plan(d, true);
+  size_t m = 0;
+  for (int w = 0; w < 3; ++w) {
+    const size_t b = attn_call_bytes(d, p, w);
+    if (b > m) m = b;
+  }
+  return m;
+}
+// the plan a call runs with: split-K if the workspace holds the full plan's
+// bytes for this call, else none (which needs only the column-sum rows)
+AttnPlan attn_plan_for(const tpmlp_attn_desc* d, int which, const void* ws, size_t ws_bytes) {
+  const AttnPlan full = attn_plan(d, true);
+  if (ws && ws_bytes >= attn_call_bytes(d, full, which)) return full;
+  return attn_plan(d, false);
 }
 
 // ---------------------------------------------------------------- mixture of experts
@@ -507,28 +637,34 @@ tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* d, const void* dy, const void* x,
   const bool swiglu = d->act == TPMLP_ACT_SWIGLU;
   const int64_t GFs = swiglu ? 2 * Fs : Fs;
   const Kind kind = d->dtype == TPMLP_F32 ? KIND_F32 : d->dtype == TPMLP_BF16 ? KIND_BF16 : KIND_E4M3;
+  // split-K for grids that leave CUs idle, when the workspace has room for it
+  const WgradPlan full = wgrad_plan(d, true);
+  const WgradPlan p = (ws && ws_bytes >= full.colsum + full.planes) ? full : wgrad_plan(d, false);
+  float* planes = reinterpret_cast<float*>(static_cast<char*>(ws) + p.colsum);
   // dW2 [H, Fs] = dy^T . a : A = dy as [K=T][M=H], B = a as [K=T][N=Fs]
   EpiArgs e1{};
   e1.out = dW2; e1.ldo = Fs; e1.accumulate = accumulate;
   if (is_fp8) { e1.scale_a = fp8->dy_scale_inv; e1.scale_b = fp8->a_scale_inv; }
   GemmArgs g1 = make_gemm(dy, H, a_saved, Fs, H, Fs, T, 0);
-  hipError_t err = run_step(kind, WGRAD, label(kind, 4), g1, e1, s);
+  hipError_t err = run_gemm(kind, WGRAD, label(kind, 4), g1, e1, s, p.sp2, planes);
   if (err != hipSuccess) return hip_fail(err);
   // dW1 [GFs, H] = dH^T . x (+ db1 = column sums of dH). The fp32 kernel
   // writes db1 itself; the MFMA kernel writes per-tile-column partial sums
-  // into the workspace, which a second pass adds up into db1.
-  const bool split = d->has_bias && kind != KIND_F32;
+  // (per split and tile column) into the workspace, which a second pass adds
+  // up into db1.
+  const bool parts = d->has_bias && kind != KIND_F32;
   EpiArgs e2{};
   e2.out = dW1; e2.ldo = H; e2.accumulate = accumulate;
-  e2.colsum = d->has_bias ? (split ? static_cast<float*>(ws) : db1) : nullptr;
+  e2.colsum = d->has_bias ? (parts ? static_cast<float*>(ws) : db1) : nullptr;
   if (is_fp8) { e2.scale_a = fp8->dH_scale_inv; e2.scale_b = fp8->x_scale_inv; }
   GemmArgs g2 = make_gemm(dH, GFs, x, H, GFs, H, T, 0);
-  err = run_step(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, label(kind, 5), g2, e2, s);
+  err = run_gemm(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, label(kind, 5), g2, e2, s, p.sp1,
+                 planes);
   if (err != hipSuccess) return hip_fail(err);
-  if (split) {
+  if (parts) {
     err = timed(is_fp8 ? "db1_reduce.e4m3" : "db1_reduce.bf16", s, [&]() {
-      return colsum_reduce_launch(static_cast<const float*>(ws), colsum_parts(d), (int)GFs, db1,
-                                  accumulate, s);
+      return colsum_reduce_launch(static_cast<const float*>(ws), p.sp1 * colsum_parts(d),
+                                  (int)GFs, db1, accumulate, s);
     });
     if (err != hipSuccess) return hip_fail(err);
   }
@@ -576,35 +712,42 @@ tpmlp_status tpmlp_attn_out_fwd(const tpmlp_attn_desc* d, const void* ctx, const
 }
 
 tpmlp_status tpmlp_attn_out_bwd_dgrad(const tpmlp_attn_desc* d, const void* dy, const void* Wo,
-                                      void* dctx, hipStream_t s) {
+                                      void* dctx, void* ws, size_t ws_bytes, hipStream_t s) {
   tpmlp_status st = check_attn_desc(d);
   if (st != TPMLP_OK) return st;
   if ((st = check_ptrs({dy, Wo, dctx})) != TPMLP_OK) return st;
+  if (ws && !aligned16(ws)) return TPMLP_E_ALIGN;
   const int64_t T = d->tokens, H = d->hidden, D = attn_d(d);
   if (T == 0) return TPMLP_OK;
   const Kind kind = attn_kind(d);
+  const AttnPlan p = attn_plan_for(d, 0, ws, ws_bytes);
   // dctx = dy . Wo: A = dy [T, H] K-major, B = Wo [H, D] read as [K=H][N=D]
   EpiArgs e{};
   e.out = dctx; e.ldo = D;
   GemmArgs g = make_gemm(dy, H, Wo, D, T, D, H, 0);
-  hipError_t err = run_step(kind, FC1_DGRAD, attn_label(kind, 2), g, e, s);
+  hipError_t err = run_gemm(kind, FC1_DGRAD, attn_label(kind, 2), g, e, s, p.sp_od,
+                            static_cast<float*>(ws));
   return err == hipSuccess ? TPMLP_OK : hip_fail(err);
 }
 
 tpmlp_status tpmlp_attn_out_bwd_wgrad(const tpmlp_attn_desc* d, const void* dy, const void* ctx,
-                                      float* dWo, int32_t accumulate, hipStream_t s) {
+                                      float* dWo, int32_t accumulate, void* ws, size_t ws_bytes,
+                                      hipStream_t s) {
   tpmlp_status st = check_attn_desc(d);
   if (st != TPMLP_OK) return st;
   if (accumulate != 0 && accumulate != 1) return TPMLP_E_DTYPE;
   if ((st = check_ptrs({dy, ctx, dWo})) != TPMLP_OK) return st;
+  if (ws && !aligned16(ws)) return TPMLP_E_ALIGN;
   const int64_t T = d->tokens, H = d->hidden, D = attn_d(d);
   if (T == 0 && accumulate) return TPMLP_OK;  // adding nothing
   const Kind kind = attn_kind(d);
+  const AttnPlan p = attn_plan_for(d, 1, ws, ws_bytes);
   // dWo [H, D] = dy^T . ctx: A = dy as [K=T][M=H], B = ctx as [K=T][N=D]
   EpiArgs e{};
   e.out = dWo; e.ldo = D; e.accumulate = accumulate;
   GemmArgs g = make_gemm(dy, H, ctx, D, H, D, T, 0);
-  hipError_t err = run_step(kind, WGRAD, attn_label(kind, 3), g, e, s);
+  hipError_t err = run_gemm(kind, WGRAD, attn_label(kind, 3), g, e, s, p.sp_ow,
+                            static_cast<float*>(ws));
   return err == hipSuccess ? TPMLP_OK : hip_fail(err);
 }
 
@@ -632,24 +775,27 @@ tpmlp_status tpmlp_attn_qkv_bwd_wgrad(const tpmlp_attn_desc* d, const void* dqkv
   if (accumulate != 0 && accumulate != 1) return TPMLP_E_DTYPE;
   if ((st = check_ptrs({dqkv, x, dWqkv})) != TPMLP_OK) return st;
   if (d->has_bias && (st = check_ptrs({dbqkv})) != TPMLP_OK) return st;
-  const size_t need = attn_workspace_bytes(d);
+  const size_t need = attn_plan(d, false).colsum;
   if (need && (!ws || ws_bytes < need)) return TPMLP_E_WORKSPACE;
-  if (need && !aligned16(ws)) return TPMLP_E_ALIGN;
+  if (ws && !aligned16(ws)) return TPMLP_E_ALIGN;
   const int64_t T = d->tokens, H = d->hidden, N = attn_nqkv(d);
   if (T == 0 && accumulate) return TPMLP_OK;
   const Kind kind = attn_kind(d);
+  const AttnPlan p = attn_plan_for(d, 2, ws, ws_bytes);
+  float* planes = reinterpret_cast<float*>(static_cast<char*>(ws) + p.colsum);
   // dWqkv [Nqkv, H] = dqkv^T . x (+ dbqkv = column sums of dqkv), as fc1's wgrad
-  const bool split = d->has_bias && kind != KIND_F32;
+  const bool parts = d->has_bias && kind != KIND_F32;
   EpiArgs e{};
   e.out = dWqkv; e.ldo = H; e.accumulate = accumulate;
-  e.colsum = d->has_bias ? (split ? static_cast<float*>(ws) : dbqkv) : nullptr;
+  e.colsum = d->has_bias ? (parts ? static_cast<float*>(ws) : dbqkv) : nullptr;
   GemmArgs g = make_gemm(dqkv, N, x, H, N, H, T, 0);
-  hipError_t err = run_step(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, attn_label(kind, 5), g, e, s);
+  hipError_t err = run_gemm(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, attn_label(kind, 5), g, e,
+                            s, p.sp_qw, planes);
   if (err != hipSuccess) return hip_fail(err);
-  if (split) {
+  if (parts) {
     err = timed(attn_label(kind, 6), s, [&]() {
-      return colsum_reduce_launch(static_cast<const float*>(ws), attn_colsum_parts(d), (int)N,
-                                  dbqkv, accumulate, s);
+      return colsum_reduce_launch(static_cast<const float*>(ws), p.sp_qw * attn_colsum_parts(d),
+                                  (int)N, dbqkv, accumulate, s);
     });
     if (err != hipSuccess) return hip_fail(err);
   }

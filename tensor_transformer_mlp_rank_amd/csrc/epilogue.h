@@ -61,6 +61,12 @@ struct GemmArgs {
   int64_t b_gstride;       // GROUP_M: elements between groups' B blocks
   int64_t out_gstride;     // GROUP_K: elements between groups' output blocks
   int64_t bias_gstride;    // GROUP_M: elements between groups' biases
+  // split-K (ungrouped products only): k_splits > 1 workgroups share a tile,
+  // split s taking stages [s * split_stages, (s + 1) * split_stages) and
+  // writing an fp32 partial plane at out + s * M * ldo (EPI_F32, no
+  // accumulate); a reduce pass forms the result
+  int k_splits;
+  int split_stages;
 };
 
 struct EpiArgs {

@@ -591,8 +591,22 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   GemmArgs g = g_in;
   EpiArgs e = e_in;
   int bm, bn;
+  int kt0 = 0;                              // first stage of this workgroup's K range
+  int nk = (g.K + kStep - 1) / kStep;       // its number of stages
+  int split = 0;
   if constexpr (GROUP == GROUP_NONE) {
-    tile_coords(g, blockIdx.x, bm, bn);
+    if (g.k_splits > 1) {
+      // ids split-major: the workgroups of one XCD share a split's panels
+      const int tiles = g.tiles_m * g.tiles_n;
+      const int id = xcd_remap(blockIdx.x, tiles * g.k_splits);
+      split = id / tiles;
+      tile_walk(id - split * tiles, g.tiles_m, g.tiles_n, g.group_m, bm, bn);
+      kt0 = split * g.split_stages;
+      nk = nk - kt0 < g.split_stages ? nk - kt0 : g.split_stages;
+      e.out = static_cast<char*>(e.out) + (int64_t)split * g.M * e.ldo * 4;
+    } else {
+      tile_coords(g, blockIdx.x, bm, bn);
+    }
   } else {
     GroupHit hit;
     if (!find_group<GROUP>(g, blockIdx.x, lane, hit)) return;
@@ -617,7 +631,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   }
   const int m0 = bm * kBM;
   const int n0 = bn * (kPair ? kBN / 2 : kBN);
-  const int nk = (g.K + kStep - 1) / kStep;
+  if constexpr (GROUP != GROUP_NONE) nk = (g.K + kStep - 1) / kStep;
 
   // ---- operand A loader
   KMajorLoader<false> la{};
@@ -699,11 +713,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
     char* sb = sa + kTileBytes;
     if (j < 8) {
-      if constexpr (A_K) la.issue_one(sa, wave, (uint32_t)(kt * kRowBytes), j);
-      else lma.issue_one(sa, wave, kt * kStep, j);
+      if constexpr (A_K) la.issue_one(sa, wave, (uint32_t)((kt0 + kt) * kRowBytes), j);
+      else lma.issue_one(sa, wave, (kt0 + kt) * kStep, j);
     } else {
-      if constexpr (B_K) lb.issue_one(sb, wave, (uint32_t)(kt * kRowBytes), j - 8);
-      else lmb.issue_one(sb, wave, kt * kStep, j - 8);
+      if constexpr (B_K) lb.issue_one(sb, wave, (uint32_t)((kt0 + kt) * kRowBytes), j - 8);
+      else lmb.issue_one(sb, wave, (kt0 + kt) * kStep, j - 8);
     }
   };
   auto issue = [&](int kt) __attribute__((always_inline)) {
@@ -723,8 +737,12 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // The k-stages are shared out over the tile columns: the workgroup in tile
   // column bn sums stages bn, bn + tiles_n, ... and writes its partial sums to
   // row bn of e.colsum ([tiles_n][M]); a second pass adds up the rows.
+  // Under split-K the share is taken within the split's own stages (global
+  // stage index congruent to bn modulo tiles_n) and written to partial row
+  // split * tiles_n + bn.
   const bool do_colsum = COLSUM && (e.colsum != nullptr);
-  int cs_next = bn;  // the next stage this workgroup sums
+  int cs_next = ((bn - kt0) % g.tiles_n + g.tiles_n) % g.tiles_n;  // next (local) stage summed
+  const int cs_row = split * g.tiles_n + bn;
   constexpr int kCs = IS_FP8 ? 16 : 8;  // columns per thread
   float csum[kCs];
 #pragma unroll
@@ -945,7 +963,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
 #pragma unroll
       for (int q = 0; q < kGroups; ++q) s += red[q * 256 + tid];
       if constexpr (IS_FP8) s *= *e.scale_a;
-      if (m < g.M) e.colsum[(int64_t)bn * g.M + m] = s;
+      if (m < g.M) e.colsum[(int64_t)cs_row * g.M + m] = s;
     }
   }
 

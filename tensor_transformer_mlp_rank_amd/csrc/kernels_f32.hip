@@ -52,7 +52,55 @@ __global__ void __launch_bounds__(256) colsum_reduce_kernel(const float* __restr
   }
 }
 
+// Split-K: the sum of the fp32 partial planes part[s][M][N] in split order,
+// then the product's own epilogue: bf16 out = sum (+ bias[col]), or fp32 out
+// = sum (+ the old out when accumulating). Eight consecutive elements per
+// thread (N is a multiple of 16).
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part,
+                                                            int splits, int64_t plane, int N,
+                                                            void* __restrict__ out, int out_bf16,
+                                                            const bf16_t* __restrict__ bias,
+                                                            int accumulate) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= plane) return;
+  float v[8];
+  Elem<float>::load8(part, i, v);
+  for (int s = 1; s < splits; ++s) {
+    float w[8];
+    Elem<float>::load8(part + (int64_t)s * plane, i, w);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] += w[u];
+  }
+  if (out_bf16) {
+    if (bias) {
+      const int col = (int)(i % N);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] += bf2f(bias[col + u]);
+    }
+    Elem<bf16_t>::store8(out, i, v);
+  } else {
+    if (accumulate) {
+      float o[8];
+      Elem<float>::load8(out, i, o);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] += o[u];
+    }
+    Elem<float>::store8(out, i, v);
+  }
+}
+
 }  // namespace
+
+hipError_t splitk_reduce_launch(const float* part, int splits, int64_t M, int64_t N, void* out,
+                                bool out_bf16, const void* bias, int accumulate, hipStream_t s) {
+  const int64_t plane = M * N;
+  if (plane <= 0) return hipSuccess;
+  const int64_t blocks = (plane / 8 + 255) / 256;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, part, splits,
+                     plane, (int)N, out, out_bf16 ? 1 : 0, static_cast<const bf16_t*>(bias),
+                     accumulate);
+  return hipGetLastError();
+}
 
 hipError_t colsum_reduce_launch(const float* part, int nparts, int M, float* out, int accumulate,
                                 hipStream_t s, int groups) {

@@ -83,6 +83,19 @@ hipError_t mfma_group_launch(Step step, int group, const GemmArgs& g0, const Epi
   return hipErrorInvalidValue;
 }
 
+hipError_t mfma_split_launch(Step step, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  if (g.k_splits < 2) return hipErrorInvalidValue;
+  const int64_t nb = (int64_t)g.tiles_m * g.tiles_n * g.k_splits;
+  switch (step) {
+    case FC2_FWD:
+    case QKV_FWD_BIAS: return launch_one<false, true, true, EPI_F32, false>(g, e, s, nb);
+    case FC1_DGRAD: return launch_one<false, true, false, EPI_F32, false>(g, e, s, nb);
+    case WGRAD: return launch_one<false, false, false, EPI_F32, false>(g, e, s, nb);
+    case WGRAD_COLSUM: return launch_one<false, false, false, EPI_F32, true>(g, e, s, nb);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t mfma_launch(bool fp8, Step step, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
   if (fp8) {
     // forward: e4m3 x e4m3; backward: e5m2 gradient (A) x e4m3 (B)

@@ -40,6 +40,15 @@ hipError_t mfma_launch(bool fp8, Step step, const GemmArgs& g, const EpiArgs& e,
 // group) and the group fields; the launch covers every group's tiles.
 // Returns the number of workgroups launched (0: nothing to launch).
 int64_t mfma_group_grid(Step step, int group, GemmArgs& g);
+
+// Split-K form of a bf16 step whose epilogue is a plain store, a bias, or an
+// fp32 store/accumulate (FC2_FWD, QKV_FWD_BIAS, FC1_DGRAD, WGRAD,
+// WGRAD_COLSUM): g.k_splits workgroups per tile write fp32 partial planes to
+// e.out (k_splits x M x N floats); splitk_reduce_launch then forms the output.
+hipError_t mfma_split_launch(Step step, const GemmArgs& g, const EpiArgs& e, hipStream_t stream);
+hipError_t splitk_reduce_launch(const float* part, int splits, int64_t M, int64_t N, void* out,
+                                bool out_bf16, const void* bias, int accumulate,
+                                hipStream_t stream);
 hipError_t mfma_group_launch(Step step, int group, const GemmArgs& g, const EpiArgs& e,
                              hipStream_t stream);
 hipError_t f32_launch(Step step, const GemmArgs& g, const EpiArgs& e, hipStream_t stream);

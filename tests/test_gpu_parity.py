@@ -153,6 +153,49 @@ def test_deterministic(tp):
         assert torch.equal(a[k], b[k]), k
 
 
+@pytest.mark.parametrize("act,bias", [("gelu", True), ("swiglu", False)])
+def test_wgrad_split_k(tp, act, bias):
+    """Weight gradients whose tile grid leaves most CUs idle (a few 256 x 256
+    tiles, many tokens) are split along K when the workspace has room for the
+    partial sums: the result matches the oracle like the unsplit product (a
+    workspace with only the db1 partials), and two split runs are bitwise
+    identical (the partials are added in a fixed order)."""
+    T, H, Fs = 4104, 512, 496
+    w = synth.WORKLOADS[2 if act == "gelu" else 4]
+    inp = synth.make_rank_inputs(w, tokens=T, hidden=H, ffn_shard=Fs, seed_base=77)
+    G = 2 if act == "swiglu" else 1
+    desc = tp.make_desc(T, H, Fs, act=act, dtype="bf16", has_bias=bias)
+    dv = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    f = tp.fwd(desc, dv["x"], dv["W1"], dv["b1"] if bias else None, dv["W2"])
+    g = tp.bwd_dgrad(desc, dv["dy"], dv["W1"], dv["W2"], f["h"])
+    full = tp.workspace_size(desc, tp.CALL_WGRAD)
+    tiles_n = (H + 255) // 256
+    minimum = ((tiles_n * G * Fs * 4 + 255) // 256) * 256 if bias else 0
+    assert full > minimum  # this shape is split
+    say(f"  wgrad split-K act={act} bias={bias}: workspace {full} bytes, {minimum} unsplit")
+
+    def run(nbytes):
+        out = {"dW1": torch.empty((G * Fs, H), device="cuda"),
+               "db1": torch.empty((G * Fs,), device="cuda") if bias else None,
+               "dW2": torch.empty((H, Fs), device="cuda")}
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+        tp.tpmlp_bwd_wgrad(desc, dv["dy"], dv["x"], f["a"], g["dH"], out["dW1"], out["db1"],
+                           out["dW2"], accumulate=False, workspace=ws[:nbytes] if nbytes else None)
+        torch.cuda.synchronize()
+        return {k: (None if v is None else v.cpu()) for k, v in out.items()}
+
+    split1, split2, plain = run(full), run(full), run(minimum)
+    ref = oracle_block(inp, act, bias)
+    names = ("dW1", "db1", "dW2") if bias else ("dW1", "dW2")
+    check(split1, ref, "bf16", names)
+    check(plain, ref, "bf16", names)
+    for k in names:
+        assert torch.equal(split1[k], split2[k]), k
+    # the two orders of summation differ only by fp32 rounding
+    for k in names:
+        assert rel_err(split1[k], plain[k]) <= 1e-5, k
+
+
 def test_swiglu_h_layout(tp):
     """The saved pre-activation of the gated block is [gate | up]: the gate
     half is x . W1[:Fs]^T and the up half x . W1[Fs:]^T (checked separately so a
