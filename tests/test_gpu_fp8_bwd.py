@@ -338,3 +338,58 @@ def test_fp8_zero_tokens_still_step_the_histories(tp):
             assert float(hist.scale.cpu()[0]) == float(want_s), fmt
             assert float(hist.scale_inv.cpu()[0]) == float(want_si), fmt
         assert torch.all(dW1 == 0) and torch.all(db1 == 0) and torch.all(dW2 == 0)
+
+
+def test_fp8_block_full_size_sampled(tp):
+    """The 12288-hidden TP=8 FP8 shard, forward + backward as the benchmark
+    runs it (delayed scaling for a and dH): sampled token rows (y, dx, and
+    the codes of a and dH) and sampled features (dW1 rows, db1 entries, dW2
+    columns), each computed by the oracle from the full inputs."""
+    from oracle import block as ob
+    w = synth.WORKLOADS[5]
+    say("config 5 forward + backward: generating and quantising inputs")
+    inp = synth.make_rank_inputs(w)
+    dev, deq = _quantized_inputs(tp, inp)
+    b1 = oracle.to_f64(inp["b1"])
+    rows = np.array([0, 1, 255, 4097, 8191])
+    feats = np.array([0, 1, 255, 256, 6143])
+    # scales for a and dH from the sampled rows' values, with headroom (both
+    # sides quantise at these same factors)
+    f0 = oracle.rank_forward(deq["x"][rows], deq["W1"], b1, deq["W2"], "gelu")
+    g0 = oracle.rank_dgrad(deq["dy"][rows], deq["W1"], deq["W2"], f0["h"], "gelu")
+    a_scale = _scale_for(4 * np.max(np.abs(f0["a"])), "e4m3")
+    dH_scale = _scale_for(4 * np.max(np.abs(g0["dH"])), "e5m2")
+    T, H, Fs = w.tokens, w.hidden, w.ffn_shard
+    desc = tp.make_desc(T, H, Fs, act="gelu", dtype="e4m3", has_bias=True)
+    ah = tp.DelayedScaling(16, scale=float(a_scale))
+    dh = tp.DelayedScaling(16, scale=float(dH_scale))
+    say(f"  e4m3 block T={T} H={H} Fs={Fs}")
+    f = tp.fwd(desc, dev["x"][0], dev["W1"][0], inp["b1"].cuda(), dev["W2"][0],
+               fp8_in_scales=(dev["x"][1], dev["W1"][1], dev["W2"][1]), a_history=ah)
+    g = tp.bwd_dgrad(desc, dev["dy"][0], dev["W1"][0], dev["W2"][0], f["h"],
+                     fp8=dict(dy_scale_inv=dev["dy"][1], w1_scale_inv=dev["W1"][1],
+                              w2_scale_inv=dev["W2"][1], dH_history=dh))
+    wg = tp.bwd_wgrad(desc, dev["dy"][0], dev["x"][0], f["a"], g["dH"],
+                      fp8=dict(dy_scale_inv=dev["dy"][1], x_scale_inv=dev["x"][1],
+                               a_scale_inv=ah.scale_inv, dH_scale_inv=dh.scale_inv))
+    torch.cuda.synchronize()
+    # sampled rows
+    rf = oracle.rank_forward_fp8(deq["x"][rows], deq["W1"], b1, deq["W2"], a_scale)
+    rg = oracle.rank_dgrad_fp8(deq["dy"][rows], deq["W1"], deq["W2"], rf["h"], dH_scale)
+    lo, hi = _check_h(f["h"][rows], rf["h_exact"])
+    _check_codes("a rows", f["a"][rows], rf["a"] * float(a_scale),
+                 _a_delta(rf, lo, hi) * float(a_scale), "e4m3", rf["a_codes"])
+    _check_codes("dH rows", g["dH"][rows], rg["dH"] * float(dH_scale),
+                 _dH_delta(rg, lo, hi) * float(dH_scale), "e5m2", rg["dH_codes"])
+    errs = {"y": rel_err(f["y"][rows].cpu(), rf["y"]), "dx": rel_err(g["dx"][rows].cpu(), rg["dx"])}
+    # sampled features over all tokens
+    W1s, b1s, W2s = ob.select_features(deq["W1"], b1, deq["W2"], feats, "gelu")
+    cf = oracle.rank_forward_fp8(deq["x"], W1s, b1s, W2s, a_scale)
+    cg = oracle.rank_dgrad_fp8(deq["dy"], W1s, W2s, cf["h"], dH_scale)
+    cw = oracle.rank_wgrad_fp8(deq["dy"], deq["x"], cf["a_q"], cg["dH_q"])
+    errs["dW1"] = rel_err(wg["dW1"][feats].cpu(), cw["dW1"])
+    errs["db1"] = rel_err(wg["db1"][feats].cpu(), cw["db1"])
+    errs["dW2"] = rel_err(wg["dW2"][:, feats].cpu(), cw["dW2"])
+    say("    rel errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL["e4m3"], (k, v)
