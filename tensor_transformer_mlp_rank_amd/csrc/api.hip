@@ -68,6 +68,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int64_t kMaxDim = int64_t(1) << 21;
 constexpr int64_t kMaxTokens = int64_t(1) << 30;
 
+// Every product of a call launches at most ceil(T / 64) x ceil(widest / 64)
+// workgroups (the fp32 kernel's 64 x 64 tiles; the MFMA kernel's are larger):
+// tile ids must stay below 2^31.
+bool grid_fits(int64_t tokens, int64_t widest) {
+  return ((tokens + 63) / 64 + 1) * ((widest + 63) / 64 + 1) < (int64_t(1) << 31);
+}
+
 tpmlp_status check_desc(const tpmlp_desc* d) {
   if (!d) return TPMLP_E_NULL;
   if (d->reserved != 0) return TPMLP_E_DTYPE;
@@ -78,6 +85,8 @@ tpmlp_status check_desc(const tpmlp_desc* d) {
   if (d->hidden % 16 != 0 || d->ffn_shard % 16 != 0) return TPMLP_E_SHAPE;
   const int64_t g = d->act == TPMLP_ACT_SWIGLU ? 2 : 1;
   if (d->hidden > kMaxDim || g * d->ffn_shard > kMaxDim || d->tokens > kMaxTokens)
+    return TPMLP_E_SHAPE;
+  if (!grid_fits(d->tokens, d->hidden > g * d->ffn_shard ? d->hidden : g * d->ffn_shard))
     return TPMLP_E_SHAPE;
   if (d->act == TPMLP_ACT_SWIGLU && d->has_bias) return TPMLP_E_UNSUPPORTED;
   if (d->dtype == TPMLP_E4M3 && d->act != TPMLP_ACT_GELU_TANH) return TPMLP_E_UNSUPPORTED;
@@ -276,6 +285,7 @@ tpmlp_status check_attn_desc(const tpmlp_attn_desc* d) {
     return TPMLP_E_SHAPE;
   const int64_t nqkv = ((int64_t)d->q_heads + 2 * (int64_t)d->kv_heads) * d->head_dim;
   if (d->hidden > kMaxDim || nqkv > kMaxDim || d->tokens > kMaxTokens) return TPMLP_E_SHAPE;
+  if (!grid_fits(d->tokens, d->hidden > nqkv ? d->hidden : nqkv)) return TPMLP_E_SHAPE;
   return TPMLP_OK;
 }
 int64_t attn_nqkv(const tpmlp_attn_desc* d) {

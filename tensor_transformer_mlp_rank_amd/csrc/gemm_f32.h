@@ -18,6 +18,7 @@
 namespace tpmlp {
 
 constexpr int kF32Tile = 64, kF32BK = 16, kF32Threads = 256;
+constexpr int kF32Fold = 256;  // k values per block of the two-level summation
 
 template <bool A_K, bool B_K, int EPI, bool COLSUM>
 __global__ void __launch_bounds__(kF32Threads) gemm_f32_kernel(const GemmArgs g, const EpiArgs e) {
@@ -34,11 +35,16 @@ __global__ void __launch_bounds__(kF32Threads) gemm_f32_kernel(const GemmArgs g,
   const bool do_colsum = COLSUM && bn == 0 && e.colsum != nullptr;
   float csum = 0.f;
 
-  float acc[4][4];
+  // Two-level summation: each block of kF32Fold k values is summed on its
+  // own, then folded into the running total, so the rounding error grows
+  // with K / kF32Fold + kF32Fold rather than with K (long token sums of the
+  // weight gradients).
+  float acc[4][4], blk[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int j = 0; j < 4; ++j) acc[i][j] = blk[i][j] = 0.f;
+  float cblk = 0.f;
 
   for (int k0 = 0; k0 < g.K; k0 += kF32BK) {
 #pragma unroll
@@ -72,7 +78,7 @@ __global__ void __launch_bounds__(kF32Threads) gemm_f32_kernel(const GemmArgs g,
     if constexpr (COLSUM) {
       if (do_colsum && tid < kF32Tile) {
 #pragma unroll
-        for (int k = 0; k < kF32BK; ++k) csum += As[k][tid];
+        for (int k = 0; k < kF32BK; ++k) cblk += As[k][tid];
       }
     }
 #pragma unroll
@@ -85,9 +91,20 @@ __global__ void __launch_bounds__(kF32Threads) gemm_f32_kernel(const GemmArgs g,
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) blk[i][j] = __builtin_fmaf(a[i], b[j], blk[i][j]);
     }
     __syncthreads();
+    if ((k0 + kF32BK) % kF32Fold == 0 || k0 + kF32BK >= g.K) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] += blk[i][j];
+          blk[i][j] = 0.f;
+        }
+      csum += cblk;
+      cblk = 0.f;
+    }
   }
 
   if constexpr (COLSUM) {

@@ -62,6 +62,7 @@ def D(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(tokens=-1), E_SHAPE), (dict(hidden=0), E_SHAPE), (dict(ffn_shard=-16), E_SHAPE),
     (dict(hidden=264), E_SHAPE), (dict(ffn_shard=136), E_SHAPE), (dict(hidden=1 << 23), E_SHAPE),
+    (dict(tokens=1 << 30, hidden=1 << 21), E_SHAPE),   # a tile grid past 2^31 workgroups
     (dict(ffn_shard=(1 << 22) - 16 + 32, act="swiglu", has_bias=False), E_SHAPE),
     (dict(dtype=9), E_DTYPE), (dict(act=4), E_DTYPE),
     (dict(act="swiglu", has_bias=True), E_UNSUP), (dict(act="swiglu", dtype="e4m3", has_bias=False), E_UNSUP),
@@ -230,6 +231,7 @@ def attn_calls(d, p=P, acc=0, ws=None, nbytes=0, bias=P):
     (dict(q_heads=0), E_SHAPE), (dict(kv_heads=0), E_SHAPE), (dict(kv_heads=3), E_SHAPE),
     (dict(head_dim=72), E_SHAPE), (dict(head_dim=-16), E_SHAPE),
     (dict(q_heads=1 << 16, kv_heads=1 << 16), E_SHAPE), (dict(hidden=1 << 23), E_SHAPE),
+    (dict(tokens=1 << 30, hidden=1 << 21, q_heads=16, kv_heads=16, head_dim=64), E_SHAPE),
     (dict(dtype=9), E_DTYPE), (dict(dtype="e4m3"), E_UNSUP),
 ])
 def test_attn_desc_validation(kw, code):

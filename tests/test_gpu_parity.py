@@ -196,6 +196,23 @@ def test_wgrad_split_k(tp, act, bias):
         assert rel_err(split1[k], plain[k]) <= 1e-5, k
 
 
+@pytest.mark.parametrize("T,H,Fs,dtype", [
+    (1 << 20, 64, 64, "bf16"),       # a million tokens: 4096 M-tiles, weight gradients over K = 2^20
+    (256, 1 << 16, 256, "bf16"),     # a 65536-wide hidden dimension: K = 2^16 for fc1 and dgrad
+    (1 << 18, 64, 48, "f32"),        # the fp32 kernel over many tokens
+])
+def test_extreme_shapes(tp, T, H, Fs, dtype):
+    """Very long token counts and very wide rows (64-bit offsets, large tile
+    grids, long K loops, split-K over a million tokens), every output
+    compared with the oracle in full."""
+    w = synth.WORKLOADS[1 if dtype == "f32" else 2]
+    inp = synth.make_rank_inputs(w, tokens=T, hidden=H, ffn_shard=Fs, seed_base=123)
+    say(f"  extreme shape T={T} H={H} Fs={Fs} {dtype}")
+    gpu = gpu_block(tp, inp, "gelu", dtype, True)
+    ref = oracle_block(inp, "gelu", True)
+    check(gpu, ref, dtype, ALL)
+
+
 def test_swiglu_h_layout(tp):
     """The saved pre-activation of the gated block is [gate | up]: the gate
     half is x . W1[:Fs]^T and the up half x . W1[Fs:]^T (checked separately so a
