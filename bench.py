@@ -103,7 +103,7 @@ def write_traffic(name, labels, setup, fetch_dir, write_dir, copy_fetch_dir, cop
     FETCH_SIZE and WRITE_SIZE runs of this script (KiB per dispatch), each
     scaled by what the same counter reads for the plain 1 GiB device copy of
     --copy-calibration. Dispatches of the library are matched to step labels
-    by launch order."""
+    by launch order; a split-K product's reduce pass counts with its GEMM."""
     import statistics
     copy_bytes = float(COPY_BYTES)
 
@@ -113,28 +113,47 @@ def write_traffic(name, labels, setup, fetch_dir, write_dir, copy_fetch_dir, cop
             raise SystemExit(f"no copy kernel dispatch in {d}")
         return statistics.median(v)
 
+    def kname(r):
+        return r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+
     scale = {"FETCH_SIZE": copy_bytes / (copy_kib(copy_fetch_dir) * 1024.0),
              "WRITE_SIZE": copy_bytes / (copy_kib(copy_write_dir) * 1024.0)}
-    seq = labels
     per = {}
     for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         rows = [r for r in _counter_rows(d)
                 if "tpmlp::" in r["Kernel_Name"] and r["Counter_Name"] == counter]
         rows = rows[setup:]  # one-off set-up launches (the FP8 step quantises its inputs)
-        if not rows or len(rows) % len(seq):
+        li, step, cur, first = 0, 0, None, True
+        sums = {}
+        for r in rows:
+            kn = kname(r)
+            if "splitk_reduce" in kn and cur is not None:
+                lab = cur  # the reduce pass of the product just launched
+            else:
+                first = step == 0  # the first step records each label's kernels
+                lab = labels[li]
+                li += 1
+                if li == len(labels):
+                    li, step = 0, step + 1
+                cur = lab
+            k = per.setdefault(lab, {"kernels": []})
+            if first:
+                if kn not in k["kernels"]:
+                    k["kernels"].append(kn)
+            elif kn not in k["kernels"]:
+                raise SystemExit(f"dispatch order does not match the step: {kn} as {lab}")
+            sums.setdefault(lab, []).append(float(r["Counter_Value"]) * 1024.0 * scale[counter])
+        if li != 0 or step == 0:
             raise SystemExit(f"{d}: {len(rows)} library dispatches after the set-up, not whole "
-                             f"steps of {len(seq)}")
-        for i, r in enumerate(rows):
-            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
-            k = per.setdefault(seq[i % len(seq)], {"kernel": name})
-            if k["kernel"] != name:
-                raise SystemExit(f"dispatch order does not match the step: {r['Kernel_Name']}")
-            k.setdefault(counter, []).append(float(r["Counter_Value"]) * 1024.0 * scale[counter])
+                             f"steps of {labels}")
+        for lab, v in sums.items():
+            per[lab][counter] = sum(v) / step
+            per[lab]["steps"] = step
     kernels = {}
-    for label, k in per.items():
-        fetch = statistics.mean(k["FETCH_SIZE"])
-        write = statistics.mean(k["WRITE_SIZE"])
-        kernels[label] = {"kernel": k["kernel"], "dispatches": len(k["FETCH_SIZE"]),
+    for label in labels:
+        k = per[label]
+        fetch, write = k["FETCH_SIZE"], k["WRITE_SIZE"]
+        kernels[label] = {"kernel": " + ".join(k["kernels"]), "dispatches": k["steps"],
                           "fetch_bytes": round(fetch), "write_bytes": round(write),
                           "bytes_per_launch": round(fetch + write)}
     out = {"source_sha": kernel_source_sha(), "workload": name, "labels": list(labels),
@@ -145,7 +164,6 @@ def write_traffic(name, labels, setup, fetch_dir, write_dir, copy_fetch_dir, cop
         json.dump(out, fh, indent=1)
         fh.write("\n")
     return out
-
 
 def _cpu_cores() -> int:
     """Threads of the BLAS the oracle runs on (else the affinity count)."""
