@@ -168,12 +168,23 @@ __device__ __forceinline__ int group_scan(const GemmArgs& g, int target, int lan
   }
   return (GROUP == GROUP_K) ? g.groups * per : tile_base;
 }
-// The tile of workgroup `bid`: the launch has an upper bound of workgroups
-// (GROUP_M) or exactly the tiles (GROUP_K); ids past the real total exit.
-// The XCD remap runs over the real total, so each XCD gets a contiguous run
-// of tiles and the surplus workgroups are spread over all XCDs.
+// The tile of workgroup `bid`.
+// GROUP_M: the launch has an upper bound of workgroups; ids past the real total
+// exit. The XCD remap runs over the real total, so each XCD gets a contiguous
+// run of tiles (all of equal work) and the surplus workgroups are spread over
+// all XCDs.
+// GROUP_K: exactly the tiles are launched, every group with the same tile
+// grid but its own K. A contiguous run per XCD would hand whole groups to
+// single XCDs, and group sizes vary by orders of magnitude. So ids stay in
+// hardware order, round-robin over the XCDs: each XCD gets every eighth tile
+// of every group (within a group, its tiles of one M-tile row and thus that
+// row's A panel).
 template <int GROUP>
 __device__ __forceinline__ bool find_group(const GemmArgs& g, int bid, int lane, GroupHit& hit) {
+  if constexpr (GROUP == GROUP_K) {
+    group_scan<GROUP>(g, bid, lane, hit);
+    return hit.e >= 0;
+  }
   const int total = group_scan<GROUP>(g, -1, lane, hit);
   if (bid >= total) return false;
   group_scan<GROUP>(g, xcd_remap(bid, total), lane, hit);
