@@ -156,12 +156,13 @@ size_t tpmlp_workspace_size(const tpmlp_desc* desc, int32_t call);
  * Forward (fc1 -> activation -> fc2), enqueued on `stream`:
  *   h = x . W1_shard^T (+ b1_shard);  a = act(h);  y_partial = a . W2_shard^T.
  * For E4M3 the fc1 accumulator is multiplied by x_scale_inv * w1_scale_inv
- * before the bias; `a` is rounded to bfloat16 and quantised to E4M3 into
- * a_saved: with current scaling (fp8->a_history NULL) from its own amax,
- * through a bfloat16 copy in the workspace and a second pass; with delayed
- * scaling directly in fc1's epilogue at a_history->scale, after which the
- * history is updated. fc2's accumulator is multiplied by (1 / a's scale) *
- * w2_scale_inv. h_saved may be NULL (inference: nothing saved for backward).
+ * before the bias, and h is stored in bfloat16; a = gelu(h as stored) is
+ * quantised to E4M3 into a_saved. With current scaling (fp8->a_history
+ * NULL) it goes through a bfloat16 copy of a in the workspace, and the scale
+ * comes from that copy's amax (a second pass). With delayed scaling it is
+ * quantised from its fp32 value directly in fc1's epilogue at
+ * a_history->scale, after which the history is updated. fc2's accumulator is
+ * multiplied by (1 / a's scale) * w2_scale_inv. h_saved may be NULL (inference: nothing saved for backward).
  * a_saved is required. b1_shard is required iff desc->has_bias. fp8 must be
  * non-NULL iff dtype is E4M3.
  */

@@ -9,7 +9,7 @@
 //   EPI_SWIGLU    (gate, up) pair: out2 = [g | u]; out = silu(g) * u
 //   EPI_DGELU     out = acc * gelu'(h[row, col])      (dH)
 //   EPI_DSWIGLU   out[col] = acc * u * silu'(g); out[col + Fs] = acc * silu(g)
-//   EPI_BIAS_GELU_Q  as EPI_BIAS_GELU; out = E4M3 codes of bf16(a) * q_scale
+//   EPI_BIAS_GELU_Q  as EPI_BIAS_GELU; out = E4M3 codes of a * q_scale (a in fp32)
 //   EPI_DGELU_Q   as EPI_DGELU; out = E5M2 codes of dH * q_scale
 //   EPI_BIAS      out = alpha * acc + bias[col]        (packed q, k, v)
 // (FP8 codes saturate at the format's largest finite value; the quantising

@@ -18,9 +18,10 @@
 //
 // Work decomposition: 256 threads = 4 waves in a 2 x 2 grid, one wave per
 // SIMD. Each wave owns a 128 x 128 sub-tile held as 4 x 4 accumulators of the
-// 32x32 MFMA (v_mfma_f32_32x32x16_bf16, or v_mfma_f32_32x32x64_f8f6f4 for
-// e4m3): 256 fp32 accumulator registers per lane (AGPRs). Per FLOP this reads
-// half the LDS bytes of a 128 x 64 wave tile.
+// 32x32 MFMA (v_mfma_f32_32x32x16_bf16, or v_mfma_scale_f32_32x32x64_f8f6f4
+// with unit scales for FP8, its format bits choosing E4M3 or E5M2 per
+// operand): 256 fp32 accumulator registers per lane (AGPRs). Per FLOP this
+// reads half the LDS bytes of a 128 x 64 wave tile.
 //
 // Pipeline: K advances 128 bytes per row per stage (64 bf16 / 128 e4m3
 // elements, whole cache lines per request); a stage holds a 32 KiB A tile and
@@ -28,12 +29,17 @@
 // from HBM straight into LDS with buffer_load_dwordx4 ... lds (no staging
 // registers, no LDS store instructions); the buffer resource's range check
 // turns reads past a tensor's end into zeros. Within a stage (see
-// stage_iter) the MFMAs run from registers while the LDS reads for the next
-// k-steps and the loads of stage k+2 are interleaved between them; two
-// barriers per stage hand the buffers over. Each barrier is a plain s_barrier
-// preceded by an explicit wait (vmcnt for this wave's loads, lgkmcnt for its
-// LDS reads): a full __syncthreads would drain all loads in flight and
-// serialise the pipeline.
+// stage_iter and stage_iter_rolling) the MFMAs run from registers while the
+// LDS reads for the next k-steps and the loads of stage k+2 are interleaved
+// between them; one barrier per stage hands the buffers over. It is a plain
+// s_barrier preceded by an explicit wait (vmcnt for this wave's loads,
+// lgkmcnt for its LDS reads): a full __syncthreads would drain all loads in
+// flight and serialise the pipeline.
+//
+// Tile mappings besides the plain grid: grouped products (the experts of a
+// mixture-of-experts layer, see find_group) and split-K (GemmArgs::k_splits),
+// where the workgroups of a tile take consecutive K ranges and write fp32
+// partial planes that a reduce pass adds up.
 //
 // LDS layouts (direct-to-LDS loads write 64 lanes x 16 B = 1 KiB linearly per
 // instruction, so swizzles are applied by choosing which global chunk each
