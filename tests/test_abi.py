@@ -162,6 +162,36 @@ def test_workspace_sizes():
     assert tp.workspace_size(D(dtype="e4m3"), 7) == 0            # invalid call
 
 
+def _colsum_bytes(H, GFs, splits=1):
+    return ((splits * ((H + 255) // 256) * GFs * 4 + 255) // 256) * 256
+
+
+def test_split_k_plans_through_workspace_sizes():
+    """The wgrad workspace adds split-K partial planes exactly where the tile
+    grid would leave CUs idle: the 2048-hidden TP=4 shard (64 tiles of
+    256 x 256 over K = 8192 tokens) splits four ways; the 8192-hidden TP=8
+    shard (512 tiles, two full rounds) does not; FP8 and fp32 never do."""
+    H = Fs = 2048
+    got = tp.workspace_size(D(tokens=8192, hidden=H, ffn_shard=Fs), tp.CALL_WGRAD)
+    planes = 4 * H * Fs * 4                      # four fp32 partial planes of the larger product
+    assert got == _colsum_bytes(H, Fs, 4) + planes
+    big = D(tokens=8192, hidden=8192, ffn_shard=4096)
+    assert tp.workspace_size(big, tp.CALL_WGRAD) == _colsum_bytes(8192, 4096)
+    assert tp.workspace_size(D(tokens=8192, hidden=H, ffn_shard=Fs, dtype="e4m3"),
+                             tp.CALL_WGRAD) == _colsum_bytes(H, Fs)
+    assert tp.workspace_size(D(tokens=8192, hidden=H, ffn_shard=Fs, dtype="f32"),
+                             tp.CALL_WGRAD) == 0
+    # too few stages to split (K = 512 tokens): the colsum rows only
+    assert tp.workspace_size(D(tokens=512, hidden=H, ffn_shard=Fs), tp.CALL_WGRAD) == \
+        _colsum_bytes(H, Fs)
+    # without bias the planes alone
+    assert tp.workspace_size(D(tokens=8192, hidden=H, ffn_shard=Fs, has_bias=False),
+                             tp.CALL_WGRAD) == planes
+    # the attention out-projection backward at the 8192-hidden shard (128 tiles) splits in two
+    a = tp.make_attn_desc(8192, 8192, 8, 8, 128, dtype="bf16", has_bias=True)
+    assert tp.attn_workspace_size(a) >= 2 * 8192 * 1024 * 4
+
+
 @pytest.mark.parametrize("name", ["dy", "W1", "W2", "h", "dH", "dx"])
 def test_dgrad_pointers(name):
     assert dgrad(D(), **{name: None}) == E_NULL
