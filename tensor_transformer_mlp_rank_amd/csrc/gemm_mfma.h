@@ -287,9 +287,21 @@ __device__ __forceinline__ i16x4 ds_read_tr16(const char* p) {
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
   return r;
 }
+// A 16-byte LDS read whose result the compiler does not wait for: the
+// caller waits (lgkmcnt) before using it.
+__device__ __forceinline__ u32x4 ds_read_b128_async(const char* p) {
+  u32x4 r;
+  const uint32_t a = (uint32_t)(uintptr_t)(const TPMLP_LDS char*)p;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(a));
+  return r;
+}
+// Wait until at most N of this wave's LDS reads are in flight (they
+// complete in order).
+template <int N = 0>
 __device__ __forceinline__ void wait_lds() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (N << 8) | (3 << 14));  // lgkmcnt(N) only
   __builtin_amdgcn_sched_barrier(0);
 }
 // bf16, MN-major tile: the same operand through two transpose reads.
@@ -802,40 +814,43 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   };
   // column sums of the A tile of stage kt: bf16, thread t adds chunk t%32 (8
   // columns) of k-rows t/32 + 8j; FP8, chunk t%16 (16 columns) of k-rows
-  // t/16 + 16j (j = 0..7); FP8 codes are decoded to floats exactly
-  auto colsum_part = [&](int kt, int j, bool on) __attribute__((always_inline)) {
-    if constexpr (COLSUM) {
-      if (on) {
-        const char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
-        if constexpr (IS_FP8) {
-          const int c = tid & 15;
-          const int kr = (tid >> 4) + 16 * j;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(sa + kr * 256 + ((c ^ mnswz8(kr)) << 4));
+  // t/16 + 16j (j = 0..7); FP8 codes are decoded to floats exactly.
+  // colsum_issue reads part j without waiting for it; colsum_add adds it
+  // once a wait has covered the read.
+  auto colsum_issue = [&](int kt, int j) __attribute__((always_inline)) -> u32x4 {
+    const char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
+    if constexpr (IS_FP8) {
+      const int c = tid & 15;
+      const int kr = (tid >> 4) + 16 * j;
+      return ds_read_b128_async(sa + kr * 256 + ((c ^ mnswz8(kr)) << 4));
+    } else {
+      const int c = tid & 31;
+      const int kr = (tid >> 5) + 8 * j;
+      return ds_read_b128_async(sa + kr * 512 + ((c ^ mnswz(kr)) << 4));
+    }
+  };
+  auto colsum_add = [&](u32x4 v) __attribute__((always_inline)) {
+    asm volatile("" : "+v"(v));  // keeps the adds after the wait before them
+    if constexpr (IS_FP8) {
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const auto lo = (FMT & 1) ? __builtin_amdgcn_cvt_pk_f32_bf8((int)v[w], false)
-                                      : __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], false);
-            const auto hi = (FMT & 1) ? __builtin_amdgcn_cvt_pk_f32_bf8((int)v[w], true)
-                                      : __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], true);
-            csum[4 * w] += lo[0];
-            csum[4 * w + 1] += lo[1];
-            csum[4 * w + 2] += hi[0];
-            csum[4 * w + 3] += hi[1];
-          }
-        } else {
-          const int c = tid & 31;
-          const int kr = (tid >> 5) + 8 * j;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(sa + kr * 512 + ((c ^ mnswz(kr)) << 4));
+      for (int w = 0; w < 4; ++w) {
+        const auto lo = (FMT & 1) ? __builtin_amdgcn_cvt_pk_f32_bf8((int)v[w], false)
+                                  : __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], false);
+        const auto hi = (FMT & 1) ? __builtin_amdgcn_cvt_pk_f32_bf8((int)v[w], true)
+                                  : __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], true);
+        csum[4 * w] += lo[0];
+        csum[4 * w + 1] += lo[1];
+        csum[4 * w + 2] += hi[0];
+        csum[4 * w + 3] += hi[1];
+      }
+    } else {
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            csum[2 * w] += bf2f((bf16_t)(v[w] & 0xffffu));
-            csum[2 * w + 1] += bf2f((bf16_t)(v[w] >> 16));
-          }
-        }
+      for (int w = 0; w < 4; ++w) {
+        csum[2 * w] += bf2f((bf16_t)(v[w] & 0xffffu));
+        csum[2 * w + 1] += bf2f((bf16_t)(v[w] >> 16));
       }
     }
   };
-
   // Every stage index is issued, also those past the end of K: their offsets
   // fall outside the resources, so they cost no memory traffic and load
   // zeros (which also makes the fused column sum of those stages zero), and
@@ -863,8 +878,6 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     // transpose reads (asm, not tracked by the compiler) of the previous last
     // quarter must have landed before their first use here
     if constexpr (!A_K || !B_K) wait_lds();
-    const bool cs_on = do_colsum && kt == cs_next;
-    if (cs_on) cs_next += g.tiles_n;
 #pragma unroll
     for (int i = 0; i < kQ; ++i) {
       mma(i);
@@ -879,7 +892,6 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
         const int j = i / (kQ / kReadsQ);
         read_one(kt, kHalfKs + j / 8, j & 7);
       }
-      if (COLSUM && (i & 1)) colsum_part(kt, (i >> 1) & 7, cs_on);
       __builtin_amdgcn_sched_barrier(0);
     }
     // the stage's one barrier: every wave is done reading stage kt (its
@@ -915,21 +927,34 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // previous stage's MFMAs of that k-step have released their registers, one
   // every two slots, so the LDS reads are spread evenly over the stage
   // instead of coming in two bursts:
-  //   group 0   reads of stage kt's k-step 3 (and its column sums)
+  //   group 0   reads of stage kt's k-step 3 (and of its column-sum parts)
   //   barrier   every wave has finished reading stage kt, and stage kt+1
   //             has landed (vmcnt(0))
-  //   group 1   reads of stage kt+1's k-step 0; loads 0..7 of stage kt+2
+  //   group 1   reads of stage kt+1's k-step 0; loads 0..7 of stage kt+2;
+  //             the column-sum parts are added
   //   group 2   reads of stage kt+1's k-step 1; loads 8..15 of stage kt+2
   //   group 3   reads of stage kt+1's k-step 2
   // FP8 (two k-steps of 64): group 0 reads stage kt's k-step 1; group 1
   // reads stage kt+1's k-step 0 and issues the 16 loads of stage kt+2.
   constexpr int kDmaStride = IS_FP8 ? 1 : 2;  // slots per load from slot 16 on
+  // Column sums: in a stage whose sums are this workgroup's share, slot 1
+  // reads the eight parts; slot 1 of the next stage adds them (the waits at
+  // the barrier and at the top of the stage cover the reads). One uniform
+  // branch per stage, laid out for the common case of no column sums.
+  u32x4 cs_buf[8];
+  int cs_pending = 0;
   auto stage_iter_rolling = [&](int kt) __attribute__((always_inline)) {
     // transpose reads (asm, not tracked by the compiler) of the previous
     // stage must have landed before their first use here
     if constexpr (!A_K || !B_K) wait_lds();
-    const bool cs_on = do_colsum && kt == cs_next;
-    if (cs_on) cs_next += g.tiles_n;
+    // 1: add the parts read in the previous stage; 2: read this stage's
+    int cs_mode = 0;
+    if constexpr (COLSUM) {
+      const int on = (do_colsum && kt == cs_next) ? 1 : 0;
+      cs_next += on * g.tiles_n;
+      cs_mode = __builtin_amdgcn_readfirstlane(cs_pending | (on << 1));
+      cs_pending = on;
+    }
 #pragma unroll
     for (int i = 0; i < kMma; ++i) {
       mma(i);
@@ -938,7 +963,18 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
         if (grp == 0) read_one(kt, kKs - 1, r >> 1);
         else read_one(kt + 1, grp - 1, r >> 1);
       }
-      if (COLSUM && grp == 0 && (i & 1)) colsum_part(kt, (i >> 1) & 7, cs_on);
+      if (COLSUM && i == 1) {
+        if (__builtin_expect(cs_mode != 0, 0)) {
+          if (cs_mode & 1) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) colsum_add(cs_buf[j]);
+          }
+          if (cs_mode & 2) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) cs_buf[j] = colsum_issue(kt, j);
+          }
+        }
+      }
       if (i >= 16 && i < 16 + 16 * kDmaStride && (i - 16) % kDmaStride == kDmaStride - 1)
         issue_one(kt + kStages, (i - 16) / kDmaStride);
       __builtin_amdgcn_sched_barrier(0);
@@ -962,6 +998,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
 #pragma unroll
     for (int j = 0; j < 8 * (kKs - 1); ++j) read_one(0, j / 8, j & 7);
     for (int kt = 0; kt < nk; ++kt) stage_iter_rolling(kt);
+  }
+  // The last stage's transpose reads ahead (asm: the compiler does not know
+  // they are in flight) must land before their registers are reused.
+  wait_lds();
+  if constexpr (COLSUM) {
+    if (cs_pending) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) colsum_add(cs_buf[j]);
+    }
   }
 
   // ---- fused column sum of A: this workgroup's share of the k-stages
