@@ -217,16 +217,23 @@ struct KMajorLoader {
   __amdgpu_buffer_rsrc_t rs0;
   const char* base1;              // gated fc1: start of the up half's rows
   int64_t bytes1;
-  uint32_t voff[8];               // row*ld + chunk*16 within its resource, or kOOB
-  uint32_t chunk_b[8];            // chunk*16 (for the K-range mask)
+  uint32_t voff[8];               // row*ld + chunk*16 within its resource
+  uint32_t klim[8];               // the chunk is inside K for stage offsets below this
+                                  // (0 for rows past the tensor's end)
   uint32_t kbytes;                // row length K * element size
+
+  __device__ __forceinline__ static uint32_t k_limit(bool row_ok, uint32_t kbytes,
+                                                     uint32_t chunk_b) {
+    return (row_ok && kbytes > chunk_b) ? kbytes - chunk_b : 0u;
+  }
 
   __device__ __forceinline__ static bool up_half(int ii) {
     return ((ii >> 2) & 3) >= 2;  // fragment (row / 32) % 4 of these rows
   }
   __device__ __forceinline__ void issue_one(char* tile, int wave, uint32_t k0b, int i) const {
     const int ii = 8 * wave + i;
-    const uint32_t off = (voff[i] != kOOB && k0b + chunk_b[i] < kbytes) ? voff[i] + k0b : kOOB;
+    // one compare and one select: no per-lane branch around the load
+    const uint32_t off = (k0b < klim[i]) ? voff[i] + k0b : kOOB;
     if constexpr (PAIR) {
       if (up_half(ii))
         lds_dma16(make_rsrc(base1, bytes1), tile + (ii << 10), off);
@@ -674,8 +681,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     for (int i = 0; i < 8; ++i) {
       const int row = 8 * (wave * 8 + i) + (lane >> 3);
       const int c = (lane & 7) ^ kswz(row);
-      la.chunk_b[i] = (uint32_t)(c << 4);
-      la.voff[i] = (m0 + row < g.M) ? (uint32_t)(row * ldb_) + (uint32_t)(c << 4) : kOOB;
+      la.klim[i] = la.k_limit(m0 + row < g.M, la.kbytes, (uint32_t)(c << 4));
+      la.voff[i] = (uint32_t)(row * ldb_) + (uint32_t)(c << 4);
     }
   } else {
     lma.base = static_cast<const char*>(g.A) + (int64_t)m0 * esz;
@@ -709,8 +716,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
         const int c = (lane & 7) ^ kswz(row);
         const int f = (row >> 5) & 3;
         const int lr = ((row >> 7) << 6) + ((f & 1) << 5) + (row & 31);
-        lb.chunk_b[i] = (uint32_t)(c << 4);
-        lb.voff[i] = (n0 + lr < g.N) ? (uint32_t)(lr * ldb_) + (uint32_t)(c << 4) : kOOB;
+        lb.klim[i] = lb.k_limit(n0 + lr < g.N, lb.kbytes, (uint32_t)(c << 4));
+        lb.voff[i] = (uint32_t)(lr * ldb_) + (uint32_t)(c << 4);
       }
     } else {
       lb.rs0 = make_rsrc(static_cast<const char*>(g.B) + (int64_t)n0 * ldb_,
@@ -719,8 +726,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
       for (int i = 0; i < 8; ++i) {
         const int row = 8 * (wave * 8 + i) + (lane >> 3);
         const int c = (lane & 7) ^ kswz(row);
-        lb.chunk_b[i] = (uint32_t)(c << 4);
-        lb.voff[i] = (n0 + row < g.N) ? (uint32_t)(row * ldb_) + (uint32_t)(c << 4) : kOOB;
+        lb.klim[i] = lb.k_limit(n0 + row < g.N, lb.kbytes, (uint32_t)(c << 4));
+        lb.voff[i] = (uint32_t)(row * ldb_) + (uint32_t)(c << 4);
       }
     }
   } else {
