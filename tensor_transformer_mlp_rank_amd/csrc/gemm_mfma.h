@@ -70,10 +70,24 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "epilogue.h"
 
 namespace tpmlp {
+
+// Compile-time loops: f(IC<i>{}) for i = 0 .. N-1. The index is a constant
+// expression inside f, so it can pick registers and instruction offsets.
+template <int V>
+using IC = std::integral_constant<int, V>;
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, Is...>) {
+  (f(IC<Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 constexpr int kBM = 256, kBN = 256;
 constexpr int kThreads = 256;
@@ -282,18 +296,13 @@ __device__ __forceinline__ bf16x8 frag_k_bf16(const char* lds, int row0, int ks,
   const int c = ((ks << 1) | (lane >> 5)) ^ kswz(row);
   return *reinterpret_cast<const bf16x8*>(lds + row * kRowBytes + (c << 4));
 }
-// The transpose read is issued through inline asm: the compiler's builtin
-// for it carries no memory-operand information, so the compiler would make
-// it wait for every LDS-bound global load in flight (vmcnt(0)) and drain the
-// pipeline. The asm result is not tracked by the compiler's wait counters:
-// every use of it below follows an explicit lgkmcnt(0) wait (the stage
-// barrier, or wait_lds at the top of a stage).
-__device__ __forceinline__ i16x4 ds_read_tr16(const char* p) {
-  i16x4 r;
-  const uint32_t a = (uint32_t)(uintptr_t)(const TPMLP_LDS char*)p;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
-  return r;
-}
+// The transpose reads (ds_read_tr16_at, ds_read_tr8_at below) are issued
+// through inline asm: the compiler's builtin for them carries no
+// memory-operand information, so the compiler would make them wait for every
+// LDS-bound global load in flight (vmcnt(0)) and drain the pipeline. The asm
+// results are not tracked by the compiler's wait counters: every use of them
+// follows an explicit lgkmcnt wait (the stage barrier, or wait_lds at the
+// top of a stage).
 // A 16-byte LDS read whose result the compiler does not wait for: the
 // caller waits (lgkmcnt) before using it.
 __device__ __forceinline__ u32x4 ds_read_b128_async(const char* p) {
@@ -311,20 +320,40 @@ __device__ __forceinline__ void wait_lds() {
   __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (N << 8) | (3 << 14));  // lgkmcnt(N) only
   __builtin_amdgcn_sched_barrier(0);
 }
-// bf16, MN-major tile: the same operand through two transpose reads.
-__device__ __forceinline__ bf16x8 frag_mn_bf16(const char* lds, int col0, int ks, int lane) {
+// Transpose reads at a constant byte offset from a per-lane base address:
+// the offset goes into the instruction's 16-bit offset field, so the k-step,
+// the part of the fragment and the tile (A or B) cost no address arithmetic.
+template <int OFF>
+__device__ __forceinline__ i16x4 ds_read_tr16_at(uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
+  i16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr8_at(uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF));
+  return r;
+}
+
+// bf16, MN-major tile: the same operand through two transpose reads. `stage`
+// is the stage buffer and T the tile's offset in it (0: A, kTileBytes: B).
+// Read r takes k-row kr = 16 ks + 8 (g/2) + i/4 + 4 r; the swizzle depends
+// on kr % 4 = (i/4) % 4 only, so the address is a per-lane part plus
+// ks * 8192 + r * 2048, which goes into the offset field.
+template <int T, int KS>
+__device__ __forceinline__ bf16x8 frag_mn_bf16(const char* stage, int col0, int lane) {
   const int g = lane >> 4, i = lane & 15;
   const int m = col0 + ((g & 1) << 4) + ((i & 3) << 2);
-  const int kb = (ks << 4) + ((g >> 1) << 3) + (i >> 2);
-  bf16x4 v[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int kr = kb + 4 * r;
-    const int c = (m >> 3) ^ mnswz(kr);
-    const char* p = lds + kr * 512 + (c << 4) + ((m & 7) << 1);
-    v[r] = __builtin_bit_cast(bf16x4, ds_read_tr16(p));
-  }
-  return __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  const int kr0 = ((g >> 1) << 3) + (i >> 2);
+  const int c = (m >> 3) ^ mnswz(kr0);
+  const uint32_t a = (uint32_t)(uintptr_t)(const TPMLP_LDS char*)stage + kr0 * 512 + (c << 4) +
+                     ((m & 7) << 1);
+  const bf16x4 v0 = __builtin_bit_cast(bf16x4, ds_read_tr16_at<T + KS * 8192>(a));
+  const bf16x4 v1 = __builtin_bit_cast(bf16x4, ds_read_tr16_at<T + KS * 8192 + 2048>(a));
+  return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 // e4m3, K-major tile: lane l takes row (l&31), bytes 64*ks + 32*(l>>5) .. +31.
 __device__ __forceinline__ i32x8 frag_k_e4m3(const char* lds, int row0, int ks, int lane) {
@@ -345,25 +374,25 @@ __device__ __forceinline__ i32x8 frag_k_e4m3(const char* lds, int row0, int ks, 
 // 16-lane group byte j%8 of the 8-byte chunks addressed by lanes 2q + j/8
 // (q = 0..7, output byte q), so pointing lane i at k-row kb + i/2, bytes
 // col + 8 (i%2) .. +7 hands lane j the 8 k values kb .. kb+7 of column
-// col + j. Issued through inline asm for the same reason as ds_read_tr16.
-__device__ __forceinline__ u32x2 ds_read_tr8(const char* p) {
-  u32x2 r;
-  const uint32_t a = (uint32_t)(uintptr_t)(const TPMLP_LDS char*)p;
-  asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(r) : "v"(a));
-  return r;
-}
-__device__ __forceinline__ i32x8 frag_mn_fp8(const char* lds, int col0, int ks, int lane) {
+// col + j.
+// Read q takes k-row kr = 64 ks + 32 (g/2) + 8 q + i/2; the swizzle depends
+// on kr % 8 = (i/2) % 8 only, so the address is a per-lane part plus
+// ks * 16384 + q * 2048, which goes into the offset field.
+template <int T, int KS>
+__device__ __forceinline__ i32x8 frag_mn_fp8(const char* stage, int col0, int lane) {
   const int g = lane >> 4, i = lane & 15;
-  const int m = col0 + ((g & 1) << 4);               // 16-byte aligned column of the group
+  const int m = col0 + ((g & 1) << 4);  // 16-byte aligned column of the group
+  const int kr0 = ((g >> 1) << 5) + (i >> 1);
+  const int c = (m >> 4) ^ mnswz8(kr0);
+  const uint32_t a = (uint32_t)(uintptr_t)(const TPMLP_LDS char*)stage + kr0 * 256 + (c << 4) +
+                     ((i & 1) << 3);
   i32x8 r;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int kr = (ks << 6) + ((g >> 1) << 5) + (q << 3) + (i >> 1);
-    const int c = (m >> 4) ^ mnswz8(kr);
-    const u32x2 v = ds_read_tr8(lds + kr * 256 + (c << 4) + ((i & 1) << 3));
+  static_for<4>([&](auto Q) {
+    constexpr int q = decltype(Q)::value;
+    const u32x2 v = ds_read_tr8_at<T + KS * 16384 + q * 2048>(a);
     r[2 * q] = (int)v[0];
     r[2 * q + 1] = (int)v[1];
-  }
+  });
   return r;
 }
 
@@ -790,24 +819,23 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   constexpr int kKs = IS_FP8 ? 2 : 4;
   using Frag = typename std::conditional<IS_FP8, i32x8, bf16x8>::type;
   Frag fa[kKs][4], fb[kKs][4];
-  auto frag_a = [&](int kt, int ks, int f) __attribute__((always_inline)) -> Frag {
-    const char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
-    if constexpr (IS_FP8 && A_K) return frag_k_e4m3(sa, 128 * wm + 32 * f, ks, lane);
-    else if constexpr (IS_FP8) return frag_mn_fp8(sa, 128 * wm + 32 * f, ks, lane);
-    else if constexpr (A_K) return frag_k_bf16(sa, 128 * wm + 32 * f, ks, lane);
-    else return frag_mn_bf16(sa, 128 * wm + 32 * f, ks, lane);
-  };
-  auto frag_b = [&](int kt, int ks, int f) __attribute__((always_inline)) -> Frag {
-    const char* sb = smem + (kt & (kStages - 1)) * kStageBytes + kTileBytes;
-    if constexpr (IS_FP8 && B_K) return frag_k_e4m3(sb, 128 * wn + 32 * f, ks, lane);
-    else if constexpr (IS_FP8) return frag_mn_fp8(sb, 128 * wn + 32 * f, ks, lane);
-    else if constexpr (B_K) return frag_k_bf16(sb, 128 * wn + 32 * f, ks, lane);
-    else return frag_mn_bf16(sb, 128 * wn + 32 * f, ks, lane);
-  };
-  // fragment j (0..7) of k-step ks of stage kt: A0..3, then B0..3
-  auto read_one = [&](int kt, int ks, int j) __attribute__((always_inline)) {
-    if (j & 4) fb[ks][j & 3] = frag_b(kt, ks, j & 3);
-    else fa[ks][j & 3] = frag_a(kt, ks, j & 3);
+  // fragment J (0..7) of k-step KS of stage kt: A0..3, then B0..3 (KS and J
+  // are compile-time constants: they select registers and offsets)
+  auto read_one = [&](int kt, auto KS, auto J) __attribute__((always_inline)) {
+    constexpr int ks = decltype(KS)::value, j = decltype(J)::value, f = j & 3;
+    const char* st = smem + (kt & (kStages - 1)) * kStageBytes;
+    if constexpr (j < 4) {
+      if constexpr (IS_FP8 && A_K) fa[ks][f] = frag_k_e4m3(st, 128 * wm + 32 * f, ks, lane);
+      else if constexpr (IS_FP8) fa[ks][f] = frag_mn_fp8<0, ks>(st, 128 * wm + 32 * f, lane);
+      else if constexpr (A_K) fa[ks][f] = frag_k_bf16(st, 128 * wm + 32 * f, ks, lane);
+      else fa[ks][f] = frag_mn_bf16<0, ks>(st, 128 * wm + 32 * f, lane);
+    } else {
+      const char* sb = st + kTileBytes;
+      if constexpr (IS_FP8 && B_K) fb[ks][f] = frag_k_e4m3(sb, 128 * wn + 32 * f, ks, lane);
+      else if constexpr (IS_FP8) fb[ks][f] = frag_mn_fp8<kTileBytes, ks>(st, 128 * wn + 32 * f, lane);
+      else if constexpr (B_K) fb[ks][f] = frag_k_bf16(sb, 128 * wn + 32 * f, ks, lane);
+      else fb[ks][f] = frag_mn_bf16<kTileBytes, ks>(st, 128 * wn + 32 * f, lane);
+    }
   };
   auto mma = [&](int i) __attribute__((always_inline)) {
     // MFMA i of a stage: k-step i/16, row block (i/4)%4, column block i%4
@@ -885,48 +913,40 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     // transpose reads (asm, not tracked by the compiler) of the previous last
     // quarter must have landed before their first use here
     if constexpr (!A_K || !B_K) wait_lds();
-#pragma unroll
-    for (int i = 0; i < kQ; ++i) {
-      mma(i);
-      // kReadsQ fragments over kQ slots
-      if (kReadsQ >= kQ) {
-#pragma unroll
-        for (int r = 0; r < kReadsQ / kQ; ++r) {
-          const int j = i * (kReadsQ / kQ) + r;
-          read_one(kt, kHalfKs + j / 8, j & 7);
-        }
-      } else if (i % (kQ / kReadsQ) == 0) {
-        const int j = i / (kQ / kReadsQ);
-        read_one(kt, kHalfKs + j / 8, j & 7);
+    // reads of quarter slot q (kReadsQ fragments over kQ slots) of k-steps
+    // ks0, ks0 + 1
+    auto reads_at = [&](int kt_r, auto Q, auto KS0) __attribute__((always_inline)) {
+      constexpr int q = decltype(Q)::value, ks0 = decltype(KS0)::value;
+      if constexpr (kReadsQ >= kQ) {
+        static_for<kReadsQ / kQ>([&](auto R) {
+          constexpr int j = q * (kReadsQ / kQ) + decltype(R)::value;
+          read_one(kt_r, IC<ks0 + j / 8>{}, IC<j & 7>{});
+        });
+      } else if constexpr (q % (kQ / kReadsQ) == 0) {
+        constexpr int j = q / (kQ / kReadsQ);
+        read_one(kt_r, IC<ks0 + j / 8>{}, IC<j & 7>{});
       }
+    };
+    static_for<kQ>([&](auto I) {
+      mma(decltype(I)::value);
+      reads_at(kt, I, IC<kHalfKs>{});
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     // the stage's one barrier: every wave is done reading stage kt (its
     // buffer is free) and has stage kt+1 in LDS (its loads, issued in the
     // middle half of stage kt-1, are the only ones in flight: vmcnt(0))
     wait_and_barrier<0>();
-#pragma unroll
-    for (int i = kQ; i < 3 * kQ; ++i) {
+    static_for<2 * kQ>([&](auto I) {
+      constexpr int i = kQ + decltype(I)::value;
       mma(i);
-      if ((i - kQ) % kDmaEvery == kDmaEvery - 1) issue_one(kt + kStages, (i - kQ) / kDmaEvery);
+      if constexpr ((i - kQ) % kDmaEvery == kDmaEvery - 1) issue_one(kt + kStages, (i - kQ) / kDmaEvery);
       __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int i = 3 * kQ; i < kMma; ++i) {
-      mma(i);
-      const int q = i - 3 * kQ;
-      if (kReadsQ >= kQ) {
-#pragma unroll
-        for (int r = 0; r < kReadsQ / kQ; ++r) {
-          const int j = q * (kReadsQ / kQ) + r;
-          read_one(kt + 1, j / 8, j & 7);
-        }
-      } else if (q % (kQ / kReadsQ) == 0) {
-        const int j = q / (kQ / kReadsQ);
-        read_one(kt + 1, j / 8, j & 7);
-      }
+    });
+    static_for<kQ>([&](auto Q) {
+      mma(3 * kQ + decltype(Q)::value);
+      reads_at(kt + 1, Q, IC<0>{});
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   };
 
   // bf16 stage kt with an MN-major operand (64 slots in four groups of 16,
@@ -962,15 +982,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
       cs_mode = __builtin_amdgcn_readfirstlane(cs_pending | (on << 1));
       cs_pending = on;
     }
-#pragma unroll
-    for (int i = 0; i < kMma; ++i) {
+    static_for<kMma>([&](auto I) {
+      constexpr int i = decltype(I)::value;
       mma(i);
-      const int grp = i >> 4, r = i & 15;
-      if ((r & 1) == 0) {
-        if (grp == 0) read_one(kt, kKs - 1, r >> 1);
-        else read_one(kt + 1, grp - 1, r >> 1);
+      constexpr int grp = i >> 4, r = i & 15;
+      if constexpr ((r & 1) == 0) {
+        if constexpr (grp == 0) read_one(kt, IC<kKs - 1>{}, IC<(r >> 1)>{});
+        else read_one(kt + 1, IC<grp - 1>{}, IC<(r >> 1)>{});
       }
-      if (COLSUM && i == 1) {
+      if constexpr (COLSUM && i == 1) {
         if (__builtin_expect(cs_mode != 0, 0)) {
           if (cs_mode & 1) {
 #pragma unroll
@@ -982,11 +1002,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
           }
         }
       }
-      if (i >= 16 && i < 16 + 16 * kDmaStride && (i - 16) % kDmaStride == kDmaStride - 1)
+      if constexpr (i >= 16 && i < 16 + 16 * kDmaStride && (i - 16) % kDmaStride == kDmaStride - 1)
         issue_one(kt + kStages, (i - 16) / kDmaStride);
       __builtin_amdgcn_sched_barrier(0);
-      if (i == 15) wait_and_barrier<0>();
-    }
+      if constexpr (i == 15) wait_and_barrier<0>();
+    });
   };
 
   // prologue: stages 0 and 1 in flight; stage 0's first k-steps in registers
@@ -998,12 +1018,16 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // operands the quarter schedule measured slightly faster.
   constexpr bool kRolling = !A_K || !B_K;
   if constexpr (!kRolling) {
-#pragma unroll
-    for (int j = 0; j < kReadsQ; ++j) read_one(0, j / 8, j & 7);
+    static_for<kReadsQ>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      read_one(0, IC<j / 8>{}, IC<j & 7>{});
+    });
     for (int kt = 0; kt < nk; ++kt) stage_iter(kt);
   } else {
-#pragma unroll
-    for (int j = 0; j < 8 * (kKs - 1); ++j) read_one(0, j / 8, j & 7);
+    static_for<8 * (kKs - 1)>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      read_one(0, IC<j / 8>{}, IC<j & 7>{});
+    });
     for (int kt = 0; kt < nk; ++kt) stage_iter_rolling(kt);
   }
   // The last stage's transpose reads ahead (asm: the compiler does not know
