@@ -212,8 +212,9 @@ __device__ __forceinline__ bool find_group(const GemmArgs& g, int bid, int lane,
 }
 
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, char* lds_wave_base,
-                                          uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TPMLP_LDS void*)lds_wave_base, 16, voff, 0, 0, 0);
+                                          uint32_t voff, uint32_t soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TPMLP_LDS void*)lds_wave_base, 16, voff, soff, 0,
+                                           0);
 }
 
 // --------------------------------------------------------------- tile loaders
@@ -246,15 +247,17 @@ struct KMajorLoader {
   }
   __device__ __forceinline__ void issue_one(char* tile, int wave, uint32_t k0b, int i) const {
     const int ii = 8 * wave + i;
-    // one compare and one select: no per-lane branch around the load
-    const uint32_t off = (k0b < klim[i]) ? voff[i] + k0b : kOOB;
+    // one compare and one select, no per-lane branch; the stage's k offset
+    // is the instruction's scalar offset (a lane past the end keeps an
+    // offset of at least kOOB, beyond any resource)
+    const uint32_t off = (k0b < klim[i]) ? voff[i] : kOOB;
     if constexpr (PAIR) {
       if (up_half(ii))
-        lds_dma16(make_rsrc(base1, bytes1), tile + (ii << 10), off);
+        lds_dma16(make_rsrc(base1, bytes1), tile + (ii << 10), off, k0b);
       else
-        lds_dma16(rs0, tile + (ii << 10), off);
+        lds_dma16(rs0, tile + (ii << 10), off, k0b);
     } else {
-      lds_dma16(rs0, tile + (ii << 10), off);
+      lds_dma16(rs0, tile + (ii << 10), off, k0b);
     }
   }
 };
@@ -291,10 +294,21 @@ __device__ __forceinline__ int mnswz8(int kr) { return (kr & 7) << 1; }
 
 // bf16, K-major tile: lane l takes row row0 + (l&31), k elements
 // 16*ks + 8*(l>>5) .. +7 of the stage.
-__device__ __forceinline__ bf16x8 frag_k_bf16(const char* lds, int row0, int ks, int lane) {
-  const int row = row0 + (lane & 31);
-  const int c = ((ks << 1) | (lane >> 5)) ^ kswz(row);
-  return *reinterpret_cast<const bf16x8*>(lds + row * kRowBytes + (c << 4));
+// Issued through inline asm like the transpose reads below (its result is
+// untracked: the stage barrier and the wait at the top of a stage cover it),
+// so that the tile T and the 32-row block F go into the offset field. The
+// swizzle depends on (lane & 31) only, since 128 wrow and 32 F are multiples
+// of 16 rows.
+template <int T, int KS, int F>
+__device__ __forceinline__ bf16x8 frag_k_bf16(const char* stage, int wrow, int lane) {
+  const int row = wrow + (lane & 31);
+  const int c = ((KS << 1) | (lane >> 5)) ^ kswz(row);
+  const uint32_t a = (uint32_t)(uintptr_t)(const TPMLP_LDS char*)stage + row * kRowBytes + (c << 4);
+  constexpr int kOff = T + F * 32 * kRowBytes;
+  static_assert(kOff >= 0 && kOff < 65536, "DS offset field");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(kOff));
+  return __builtin_bit_cast(bf16x8, r);
 }
 // The transpose reads (ds_read_tr16_at, ds_read_tr8_at below) are issued
 // through inline asm: the compiler's builtin for them carries no
@@ -827,13 +841,13 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     if constexpr (j < 4) {
       if constexpr (IS_FP8 && A_K) fa[ks][f] = frag_k_e4m3(st, 128 * wm + 32 * f, ks, lane);
       else if constexpr (IS_FP8) fa[ks][f] = frag_mn_fp8<0, ks>(st, 128 * wm + 32 * f, lane);
-      else if constexpr (A_K) fa[ks][f] = frag_k_bf16(st, 128 * wm + 32 * f, ks, lane);
+      else if constexpr (A_K) fa[ks][f] = frag_k_bf16<0, ks, f>(st, 128 * wm, lane);
       else fa[ks][f] = frag_mn_bf16<0, ks>(st, 128 * wm + 32 * f, lane);
     } else {
       const char* sb = st + kTileBytes;
       if constexpr (IS_FP8 && B_K) fb[ks][f] = frag_k_e4m3(sb, 128 * wn + 32 * f, ks, lane);
       else if constexpr (IS_FP8) fb[ks][f] = frag_mn_fp8<kTileBytes, ks>(st, 128 * wn + 32 * f, lane);
-      else if constexpr (B_K) fb[ks][f] = frag_k_bf16(sb, 128 * wn + 32 * f, ks, lane);
+      else if constexpr (B_K) fb[ks][f] = frag_k_bf16<kTileBytes, ks, f>(st, 128 * wn, lane);
       else fb[ks][f] = frag_mn_bf16<kTileBytes, ks>(st, 128 * wn + 32 * f, lane);
     }
   };
@@ -910,9 +924,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   constexpr int kReadsQ = 8 * kHalfKs;   // fragments read per quarter
   constexpr int kDmaEvery = (kMma / 2) / 16;
   auto stage_iter = [&](int kt) __attribute__((always_inline)) {
-    // transpose reads (asm, not tracked by the compiler) of the previous last
-    // quarter must have landed before their first use here
-    if constexpr (!A_K || !B_K) wait_lds();
+    // bf16 fragment reads are asm (not tracked by the compiler): the previous
+    // last quarter's k-step 0 must have landed (its 8 reads of k-step 1, one
+    // instruction each, may still be in flight)
+    if constexpr (!IS_FP8) wait_lds<8>();
     // reads of quarter slot q (kReadsQ fragments over kQ slots) of k-steps
     // ks0, ks0 + 1
     auto reads_at = [&](int kt_r, auto Q, auto KS0) __attribute__((always_inline)) {
