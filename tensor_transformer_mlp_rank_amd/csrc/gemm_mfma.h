@@ -370,12 +370,18 @@ __device__ __forceinline__ bf16x8 frag_mn_bf16(const char* stage, int col0, int 
   return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 // e4m3, K-major tile: lane l takes row (l&31), bytes 64*ks + 32*(l>>5) .. +31.
-__device__ __forceinline__ i32x8 frag_k_e4m3(const char* lds, int row0, int ks, int lane) {
-  const int row = row0 + (lane & 31);
-  const int c0 = (ks << 2) | ((lane >> 5) << 1);
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + row * kRowBytes + ((c0 ^ kswz(row)) << 4));
-  const u32x4 hi =
-      *reinterpret_cast<const u32x4*>(lds + row * kRowBytes + (((c0 + 1) ^ kswz(row)) << 4));
+template <int T, int KS, int F>
+__device__ __forceinline__ i32x8 frag_k_e4m3(const char* stage, int wrow, int lane) {
+  // as frag_k_bf16: asm reads, the tile and 32-row block in the offset field
+  const int row = wrow + (lane & 31);
+  const int c0 = (KS << 2) | ((lane >> 5) << 1);
+  const uint32_t base = (uint32_t)(uintptr_t)(const TPMLP_LDS char*)stage + row * kRowBytes;
+  const uint32_t a0 = base + ((c0 ^ kswz(row)) << 4), a1 = base + (((c0 + 1) ^ kswz(row)) << 4);
+  constexpr int kOff = T + F * 32 * kRowBytes;
+  static_assert(kOff >= 0 && kOff < 65536, "DS offset field");
+  u32x4 lo, hi;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(lo) : "v"(a0), "i"(kOff));
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(hi) : "v"(a1), "i"(kOff));
   i32x8 r;
   r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
   r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
@@ -839,13 +845,13 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     constexpr int ks = decltype(KS)::value, j = decltype(J)::value, f = j & 3;
     const char* st = smem + (kt & (kStages - 1)) * kStageBytes;
     if constexpr (j < 4) {
-      if constexpr (IS_FP8 && A_K) fa[ks][f] = frag_k_e4m3(st, 128 * wm + 32 * f, ks, lane);
+      if constexpr (IS_FP8 && A_K) fa[ks][f] = frag_k_e4m3<0, ks, f>(st, 128 * wm, lane);
       else if constexpr (IS_FP8) fa[ks][f] = frag_mn_fp8<0, ks>(st, 128 * wm + 32 * f, lane);
       else if constexpr (A_K) fa[ks][f] = frag_k_bf16<0, ks, f>(st, 128 * wm, lane);
       else fa[ks][f] = frag_mn_bf16<0, ks>(st, 128 * wm + 32 * f, lane);
     } else {
       const char* sb = st + kTileBytes;
-      if constexpr (IS_FP8 && B_K) fb[ks][f] = frag_k_e4m3(sb, 128 * wn + 32 * f, ks, lane);
+      if constexpr (IS_FP8 && B_K) fb[ks][f] = frag_k_e4m3<kTileBytes, ks, f>(st, 128 * wn, lane);
       else if constexpr (IS_FP8) fb[ks][f] = frag_mn_fp8<kTileBytes, ks>(st, 128 * wn + 32 * f, lane);
       else if constexpr (B_K) fb[ks][f] = frag_k_bf16<kTileBytes, ks, f>(st, 128 * wn, lane);
       else fb[ks][f] = frag_mn_bf16<kTileBytes, ks>(st, 128 * wn + 32 * f, lane);
@@ -924,9 +930,13 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   constexpr int kReadsQ = 8 * kHalfKs;   // fragments read per quarter
   constexpr int kDmaEvery = (kMma / 2) / 16;
   auto stage_iter = [&](int kt) __attribute__((always_inline)) {
-    // bf16 fragment reads are asm (not tracked by the compiler): the previous
+    // Fragment reads are asm (not tracked by the compiler). bf16: the previous
     // last quarter's k-step 0 must have landed (its 8 reads of k-step 1, one
-    // instruction each, may still be in flight)
+    // instruction each, may still be in flight). FP8 (two k-steps, two
+    // instructions per fragment): the last quarter read all of k-step 0,
+    // A0..3 then B0..3; MFMA i < 4 needs B_i, followed by three fragment reads
+    // (six instructions, counting this quarter's reads issued since), so a
+    // wait for at most 6 in flight precedes each of the first four MFMAs.
     if constexpr (!IS_FP8) wait_lds<8>();
     // reads of quarter slot q (kReadsQ fragments over kQ slots) of k-steps
     // ks0, ks0 + 1
@@ -943,6 +953,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
       }
     };
     static_for<kQ>([&](auto I) {
+      if constexpr (IS_FP8 && decltype(I)::value < 4) wait_lds<6>();
       mma(decltype(I)::value);
       reads_at(kt, I, IC<kHalfKs>{});
       __builtin_amdgcn_sched_barrier(0);
