@@ -286,7 +286,9 @@ struct MNMajorLoader {
 // chunk c at c ^ mnswz(krow), mnswz = 0, 4, 10, 14 for krow % 4 = 0..3
 // (measured conflict-free).
 __device__ __forceinline__ int kswz(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int mnswz(int kr) { return (0xEA40 >> ((kr & 3) << 2)) & 15; }
+__device__ __forceinline__ int mnswz(int kr) {
+  return ((0xEA40 >> ((kr & 3) << 2)) & 15) ^ ((kr >> 2) & 2);
+}
 // FP8 MN-major k-rows (256 bytes) put chunk c at c ^ 2 (krow % 8): a transpose
 // read takes one 16-byte chunk pair (c, c+1), c even, from 8 consecutive
 // k-rows per half-wave, which land in 16 distinct 16-byte slots.
@@ -294,17 +296,19 @@ __device__ __forceinline__ int mnswz8(int kr) { return (kr & 7) << 1; }
 
 // bf16, K-major tile: lane l takes row row0 + (l&31), k elements
 // 16*ks + 8*(l>>5) .. +7 of the stage.
-// Issued through inline asm like the transpose reads below (its result is
-// untracked: the stage barrier and the wait at the top of a stage cover it),
-// so that the tile T and the 32-row block F go into the offset field. The
-// swizzle depends on (lane & 31) only, since 128 wrow and 32 F are multiples
-// of 16 rows.
-template <int T, int KS, int F>
+// bf16, K-major tile, operand of the 16x16x32 MFMA: lane l takes row
+// wrow + 16 R + (l & 15), k elements 32 KS + 8 (l >> 4) .. +7 (16 bytes,
+// chunk 4 KS + l / 16). Issued through inline asm like the transpose reads
+// below (its result is untracked: the stage barrier and the wait at the top
+// of a stage cover it). The swizzle depends on (l & 15) only, since wrow and
+// 16 R are multiples of 16 rows, so the tile T and the row block R go into
+// the offset field.
+template <int T, int KS, int R>
 __device__ __forceinline__ bf16x8 frag_k_bf16(const char* stage, int wrow, int lane) {
-  const int row = wrow + (lane & 31);
-  const int c = ((KS << 1) | (lane >> 5)) ^ kswz(row);
+  const int row = wrow + (lane & 15);
+  const int c = ((KS << 2) | (lane >> 4)) ^ kswz(row);
   const uint32_t a = (uint32_t)(uintptr_t)(const TPMLP_LDS char*)stage + row * kRowBytes + (c << 4);
-  constexpr int kOff = T + F * 32 * kRowBytes;
+  constexpr int kOff = T + R * 16 * kRowBytes;
   static_assert(kOff >= 0 && kOff < 65536, "DS offset field");
   u32x4 r;
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(kOff));
@@ -352,21 +356,24 @@ __device__ __forceinline__ u32x2 ds_read_tr8_at(uint32_t a) {
   return r;
 }
 
-// bf16, MN-major tile: the same operand through two transpose reads. `stage`
-// is the stage buffer and T the tile's offset in it (0: A, kTileBytes: B).
-// Read r takes k-row kr = 16 ks + 8 (g/2) + i/4 + 4 r; the swizzle depends
-// on kr % 4 = (i/4) % 4 only, so the address is a per-lane part plus
-// ks * 8192 + r * 2048, which goes into the offset field.
+// bf16, MN-major tile, operand of the 16x16x32 MFMA through two transpose
+// reads. `stage` is the stage buffer and T the tile's offset in it (0: A,
+// kTileBytes: B). In 16-lane group g (k 8g .. 8g+7 of the k-step), lane i
+// points at k-row 32 KS + 8 g + i/4 (+4 for the second read), elements
+// col0 + 4 (i%4) .. +3, so lane j of the group receives the k values of
+// element col0 + j. The swizzle depends on k-row bits 0, 1 and 3 only, which
+// neither KS nor the +4 changes, so KS * 16384 + r * 2048 goes into the
+// offset field.
 template <int T, int KS>
 __device__ __forceinline__ bf16x8 frag_mn_bf16(const char* stage, int col0, int lane) {
   const int g = lane >> 4, i = lane & 15;
-  const int m = col0 + ((g & 1) << 4) + ((i & 3) << 2);
-  const int kr0 = ((g >> 1) << 3) + (i >> 2);
+  const int m = col0 + ((i & 3) << 2);
+  const int kr0 = (g << 3) + (i >> 2);
   const int c = (m >> 3) ^ mnswz(kr0);
   const uint32_t a = (uint32_t)(uintptr_t)(const TPMLP_LDS char*)stage + kr0 * 512 + (c << 4) +
                      ((m & 7) << 1);
-  const bf16x4 v0 = __builtin_bit_cast(bf16x4, ds_read_tr16_at<T + KS * 8192>(a));
-  const bf16x4 v1 = __builtin_bit_cast(bf16x4, ds_read_tr16_at<T + KS * 8192 + 2048>(a));
+  const bf16x4 v0 = __builtin_bit_cast(bf16x4, ds_read_tr16_at<T + KS * 16384>(a));
+  const bf16x4 v1 = __builtin_bit_cast(bf16x4, ds_read_tr16_at<T + KS * 16384 + 2048>(a));
   return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 // e4m3, K-major tile: lane l takes row (l&31), bytes 64*ks + 32*(l>>5) .. +31.
@@ -456,10 +463,10 @@ __device__ __forceinline__ void wait_and_barrier() {
 // counter tracks both loads and stores, so a wait for a load issued after a
 // store also waits for the store, and per-group load/use pairs would
 // serialise the epilogue on memory latency.
-template <bool IS_FP8, int EPI, typename OutT, bool LOADS>
-__device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e,
-                                           f32x16 (&acc)[4][4], char* smem, int wave, int lane,
-                                           int m0, int n0, float& amax) {
+template <bool IS_FP8, int EPI, typename OutT, bool LOADS, typename Acc>
+__device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e, Acc& acc,
+                                           char* smem, int wave, int lane, int m0, int n0,
+                                           float& amax) {
   static_assert(std::is_same<OutT, bf16_t>::value, "MFMA activations and outputs are bf16");
   constexpr bool kPair = (EPI == EPI_SWIGLU);
   constexpr int kLd = 132;
@@ -536,11 +543,26 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e,
     if constexpr (LOADS) {
       if ((fm & 1) == 0) load_slabs(fm);
     }
+    if constexpr (IS_FP8) {
+      // 32x32 blocks: register j of block (fm, fn) is row 8 (j/4) + 4 (l/32)
+      // + j%4, column 32 fn + l%32
 #pragma unroll
-    for (int fn = 0; fn < 4; ++fn)
+      for (int fn = 0; fn < 4; ++fn)
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        wl[(8 * (j >> 2) + 4 * (lane >> 5) + (j & 3)) * kLd + 32 * fn + (lane & 31)] = acc[fm][fn][j];
+        for (int j = 0; j < 16; ++j)
+          wl[(8 * (j >> 2) + 4 * (lane >> 5) + (j & 3)) * kLd + 32 * fn + (lane & 31)] =
+              acc[fm][fn][j];
+    } else {
+      // 16x16 blocks: register q of block (2 fm + h, c) is row 16 h + 4 (l/16)
+      // + q, column 16 c + l%16
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            wl[(16 * h + 4 * (lane >> 4) + q) * kLd + 16 * c + (lane & 15)] = acc[2 * fm + h][c][q];
+    }
     if constexpr (LOADS) {
       if ((fm & 1) == 0) {
         asm volatile("" ::: "memory");
@@ -810,13 +832,17 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     for (int j = 0; j < 16; ++j) issue_one(kt, j);
   };
 
-  f32x16 acc[4][4];
+  // accumulators: bf16, 8 x 8 blocks of the 16x16x32 MFMA (4 registers
+  // each); FP8, 4 x 4 blocks of the 32x32x64 one (16 registers each)
+  constexpr int kAb = IS_FP8 ? 4 : 8;
+  using AccV = typename std::conditional<IS_FP8, f32x16, f32x4>::type;
+  AccV acc[kAb][kAb];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kAb; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kAb; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < (IS_FP8 ? 16 : 4); ++r) acc[i][j][r] = 0.f;
 
   // fused column sum: thread t owns 8 columns (chunk t%32) of k-rows t/32 + 8j.
   // The k-stages are shared out over the tile columns: the workgroup in tile
@@ -833,39 +859,49 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
 #pragma unroll
   for (int j = 0; j < kCs; ++j) csum[j] = 0.f;
 
-  // A stage has kKs MFMA k-steps (4 for bf16: 16 elements each; 2 for e4m3:
-  // 64 each) of 16 MFMAs. The fragments of k-step ks live in register slot
-  // ks (A rows 128 wm + 32 f, B rows 128 wn + 32 f, f = 0..3).
-  constexpr int kKs = IS_FP8 ? 2 : 4;
+  // A stage has two MFMA k-steps (bf16: 32 elements each, 64 MFMAs of
+  // 16x16x32; e4m3: 64 each, 16 MFMAs of 32x32x64). The fragments of k-step
+  // ks live in register slot ks: kFr per operand (bf16: A rows 128 wm + 16 f,
+  // B rows 128 wn + 16 f, f = 0..7; FP8: 32-row blocks, f = 0..3).
+  constexpr int kKs = 2;
+  constexpr int kFr = IS_FP8 ? 4 : 8;
   using Frag = typename std::conditional<IS_FP8, i32x8, bf16x8>::type;
-  Frag fa[kKs][4], fb[kKs][4];
-  // fragment J (0..7) of k-step KS of stage kt: A0..3, then B0..3 (KS and J
+  Frag fa[kKs][kFr], fb[kKs][kFr];
+  // fragment J of k-step KS of stage kt: A0..A(kFr-1), then B0.. (KS and J
   // are compile-time constants: they select registers and offsets)
   auto read_one = [&](int kt, auto KS, auto J) __attribute__((always_inline)) {
-    constexpr int ks = decltype(KS)::value, j = decltype(J)::value, f = j & 3;
+    constexpr int ks = decltype(KS)::value, j = decltype(J)::value, f = j % kFr;
     const char* st = smem + (kt & (kStages - 1)) * kStageBytes;
-    if constexpr (j < 4) {
+    if constexpr (j < kFr) {
       if constexpr (IS_FP8 && A_K) fa[ks][f] = frag_k_e4m3<0, ks, f>(st, 128 * wm, lane);
       else if constexpr (IS_FP8) fa[ks][f] = frag_mn_fp8<0, ks>(st, 128 * wm + 32 * f, lane);
       else if constexpr (A_K) fa[ks][f] = frag_k_bf16<0, ks, f>(st, 128 * wm, lane);
-      else fa[ks][f] = frag_mn_bf16<0, ks>(st, 128 * wm + 32 * f, lane);
+      else fa[ks][f] = frag_mn_bf16<0, ks>(st, 128 * wm + 16 * f, lane);
     } else {
-      const char* sb = st + kTileBytes;
       if constexpr (IS_FP8 && B_K) fb[ks][f] = frag_k_e4m3<kTileBytes, ks, f>(st, 128 * wn, lane);
       else if constexpr (IS_FP8) fb[ks][f] = frag_mn_fp8<kTileBytes, ks>(st, 128 * wn + 32 * f, lane);
       else if constexpr (B_K) fb[ks][f] = frag_k_bf16<kTileBytes, ks, f>(st, 128 * wn, lane);
-      else fb[ks][f] = frag_mn_bf16<kTileBytes, ks>(st, 128 * wn + 32 * f, lane);
+      else fb[ks][f] = frag_mn_bf16<kTileBytes, ks>(st, 128 * wn + 16 * f, lane);
     }
   };
   auto mma = [&](int i) __attribute__((always_inline)) {
-    // MFMA i of a stage: k-step i/16, row block (i/4)%4, column block i%4
-    const int ks = i >> 4, fm = (i >> 2) & 3, fn = i & 3;
-    if constexpr (IS_FP8)
+    if constexpr (IS_FP8) {
+      // MFMA i of a stage: k-step i/16, row block (i/4)%4, column block i%4
+      const int ks = i >> 4, fm = (i >> 2) & 3, fn = i & 3;
       acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
           fa[ks][fm], fb[ks][fn], acc[fm][fn], FMT & 1, (FMT >> 1) & 1, 0, 0, 0, 0);
-    else
-      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][fm], fb[ks][fn], acc[fm][fn],
-                                                            0, 0, 0);
+    } else {
+      // MFMA i of a stage: k-step i/64, row block (i/8)%8, column block i%8.
+      // Inline asm with the accumulator tied in place: with the builtin the
+      // register allocator parked accumulators in VGPRs and moved them
+      // around the loop. An accumulator is reused 64 MFMAs later, far past
+      // the instruction's latency; the wait after the main loop covers the
+      // epilogue's first reads of the results.
+      const int ks = i >> 6, r = (i >> 3) & 7, c = i & 7;
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                   : "+a"(acc[r][c])
+                   : "v"(fa[ks][r]), "v"(fb[ks][c]));
+    }
   };
   // column sums of the A tile of stage kt: bf16, thread t adds chunk t%32 (8
   // columns) of k-rows t/32 + 8j; FP8, chunk t%16 (16 columns) of k-rows
@@ -1035,15 +1071,66 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     });
   };
 
+  // bf16 stage kt (128 slots of one 16x16x32 MFMA each, k-step 0 in slots
+  // 0..63, k-step 1 in 64..127), any operand layouts:
+  //   slots 0..47     read this stage's k-step 1 (16 fragments, one every
+  //                   third slot) into the registers k-step 1 of the last
+  //                   stage has released
+  //   slot 63         the stage's one barrier: every wave has read all of
+  //                   stage kt (its buffer is free) and stage kt+1 has landed
+  //                   (this wave's loads: vmcnt(0))
+  //   slots 64..111   read stage kt+1's k-step 0 into the registers k-step 0
+  //                   of this stage has released
+  //   slots 64..127   the 16 loads of stage kt+2, one every fourth slot
+  // A load has a whole stage to land, and every read has 16 slots before the
+  // wait that covers it (the barrier, or the top of the next stage).
+  auto stage_iter16 = [&](int kt) __attribute__((always_inline)) {
+    wait_lds();  // this stage's k-step 0 (read in slots 64..111 of the last)
+    int cs_mode = 0;
+    if constexpr (COLSUM) {
+      const int on = (do_colsum && kt == cs_next) ? 1 : 0;
+      cs_next += on * g.tiles_n;
+      cs_mode = __builtin_amdgcn_readfirstlane(cs_pending | (on << 1));
+      cs_pending = on;
+    }
+    static_for<128>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      constexpr int h = i >> 6, sl = i & 63;
+      mma(i);
+      if constexpr (sl % 3 == 0 && sl / 3 < 2 * kFr) {
+        if constexpr (h == 0) read_one(kt, IC<1>{}, IC<sl / 3>{});
+        else read_one(kt + 1, IC<0>{}, IC<sl / 3>{});
+      }
+      if constexpr (COLSUM && i == 1) {
+        if (__builtin_expect(cs_mode != 0, 0)) {
+          if (cs_mode & 1) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) colsum_add(cs_buf[j]);
+          }
+          if (cs_mode & 2) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) cs_buf[j] = colsum_issue(kt, j);
+          }
+        }
+      }
+      if constexpr (h == 1 && (sl & 3) == 3) issue_one(kt + kStages, sl >> 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (i == 63) wait_and_barrier<0>();
+    });
+  };
+
   // prologue: stages 0 and 1 in flight; stage 0's first k-steps in registers
   issue(0);
   issue(1);
   wait_and_barrier<16>();
-  // The rolling schedule pays off where a transpose-read operand makes the
-  // reads costly (twice the read instructions per byte); with two K-major
-  // operands the quarter schedule measured slightly faster.
+  // FP8: the rolling schedule pays off where a transpose-read operand makes
+  // the reads costly; with two K-major operands the quarter schedule measured
+  // slightly faster.
   constexpr bool kRolling = !A_K || !B_K;
-  if constexpr (!kRolling) {
+  if constexpr (!IS_FP8) {
+    static_for<2 * kFr>([&](auto J) { read_one(0, IC<0>{}, J); });
+    for (int kt = 0; kt < nk; ++kt) stage_iter16(kt);
+  } else if constexpr (!kRolling) {
     static_for<kReadsQ>([&](auto J) {
       constexpr int j = decltype(J)::value;
       read_one(0, IC<j / 8>{}, IC<j & 7>{});
@@ -1059,6 +1146,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // The last stage's transpose reads ahead (asm: the compiler does not know
   // they are in flight) must land before their registers are reused.
   wait_lds();
+  if constexpr (!IS_FP8) {
+    // the last MFMAs (asm, unseen by the compiler's hazard checks) complete
+    // before any instruction reads their accumulators
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+  }
   if constexpr (COLSUM) {
     if (cs_pending) {
 #pragma unroll
