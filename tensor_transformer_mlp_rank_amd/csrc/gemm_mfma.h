@@ -17,11 +17,14 @@
 //   fc1 wgrad dH^T . x                A MN-major, B MN-major (K = T)
 //
 // Work decomposition: 256 threads = 4 waves in a 2 x 2 grid, one wave per
-// SIMD. Each wave owns a 128 x 128 sub-tile held as 4 x 4 accumulators of the
-// 32x32 MFMA (v_mfma_f32_32x32x16_bf16, or v_mfma_scale_f32_32x32x64_f8f6f4
-// with unit scales for FP8, its format bits choosing E4M3 or E5M2 per
-// operand): 256 fp32 accumulator registers per lane (AGPRs). Per FLOP this
-// reads half the LDS bytes of a 128 x 64 wave tile.
+// SIMD. Each wave owns a 128 x 128 sub-tile: for bf16, 8 x 8 accumulator
+// blocks of the 16x16x32 MFMA (v_mfma_f32_16x16x32_bf16); for FP8, 4 x 4
+// blocks of the 32x32x64 one (v_mfma_scale_f32_32x32x64_f8f6f4 with unit
+// scales, its format bits choosing E4M3 or E5M2 per operand). Either way 256
+// fp32 accumulator registers per lane (AGPRs). Per FLOP this reads half the
+// LDS bytes of a 128 x 64 wave tile. Under the chip's power limit the 16x16
+// bf16 MFMA sustains a higher clock than the 32x32 one (an MFMA-only loop
+// with random operands: 1.97 against 1.76 GHz, 8% more FLOP/s).
 //
 // Pipeline: K advances 128 bytes per row per stage (64 bf16 / 128 e4m3
 // elements, whole cache lines per request); a stage holds a 32 KiB A tile and
@@ -29,9 +32,10 @@
 // from HBM straight into LDS with buffer_load_dwordx4 ... lds (no staging
 // registers, no LDS store instructions); the buffer resource's range check
 // turns reads past a tensor's end into zeros. Within a stage (see
-// stage_iter and stage_iter_rolling) the MFMAs run from registers while the
-// LDS reads for the next k-steps and the loads of stage k+2 are interleaved
-// between them; one barrier per stage hands the buffers over. It is a plain
+// stage_iter16 for bf16, stage_iter and stage_iter_rolling for FP8) the
+// MFMAs run from registers while the LDS reads for the next k-steps and the
+// loads of stage k+2 are interleaved between them; one barrier per stage
+// hands the buffers over. It is a plain
 // s_barrier preceded by an explicit wait (vmcnt for this wave's loads,
 // lgkmcnt for its LDS reads): a full __syncthreads would drain all loads in
 // flight and serialise the pipeline.
@@ -50,18 +54,21 @@
 //     reads (ds_read_b128, 8 consecutive k of one row per lane) are
 //     conflict-free.
 //   * MN-major tile: [64 k-rows][256 elements = 512 B]; chunk c of k-row r
-//     lives at chunk c ^ {0, 4, 10, 14}[r % 4], which spreads the 32 lanes of
-//     a transpose read over 32 distinct 8-byte slots of a 256-byte bank window.
-//     Fragments are read with the CDNA4 transpose
+//     lives at chunk c ^ ({0, 4, 10, 14}[r % 4] ^ 2 (r / 8 % 2)). A
+//     transpose read of the 16x16x32 operand takes k-rows k0..k0+3 in lanes
+//     0-15 and k0+8..k0+11 in lanes 16-31, two chunks each: the swizzle puts
+//     these 16 (k-row, chunk) pairs in 16 distinct 16-byte slots of a
+//     256-byte bank window. Fragments are read with the CDNA4 transpose
 //     read ds_read_b64_tr_b16: in each group of 16 lanes, lane j receives
 //     element j%4 of the 8-byte chunks addressed by lanes 4q + j/4 (q = 0..3),
 //     so pointing lane i at k-row k0 + i/4, elements m0 + 4(i%4) .. +3 hands
 //     lane j the four k values k0..k0+3 of element m0 + j -- the MFMA operand
 //     layout, read straight from the untransposed tile.
 //
-// Gated fc1 (SwiGLU): each wave's four N accumulators hold gate features
-// (fn = 0, 1) and the matching up features (fn = 2, 3) of the same 64 output
-// features, so the epilogue forms silu(gate) * up in registers.
+// Gated fc1 (SwiGLU): the first half of each wave's 128 accumulator columns
+// holds gate features and the second half the matching up features of the
+// same 64 output features, so the epilogue forms silu(gate) * up in
+// registers.
 //
 // Workgroup order: blockIdx.x is first remapped so that the workgroups the
 // hardware places on one XCD (ids congruent mod 8) get consecutive tile ids,
@@ -283,8 +290,9 @@ struct MNMajorLoader {
 // Swizzles (gfx950's LDS serves 256 bytes per cycle): K-major 128-byte rows
 // put chunk c at c ^ ((row >> 1) & 7), so 16 consecutive rows put a given
 // chunk in 16 distinct 16-byte slots of a 256-byte window; MN-major k-rows put
-// chunk c at c ^ mnswz(krow), mnswz = 0, 4, 10, 14 for krow % 4 = 0..3
-// (measured conflict-free).
+// chunk c at c ^ mnswz(krow), mnswz = 0, 4, 10, 14 for krow % 4 = 0..3 (the
+// part measured conflict-free for the 32x32 operand's reads), XOR 2 when
+// krow / 8 is odd (for the 16x16 operand's, which pair k-rows 8 apart).
 __device__ __forceinline__ int kswz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int mnswz(int kr) {
   return ((0xEA40 >> ((kr & 3) << 2)) & 15) ^ ((kr >> 2) & 2);
