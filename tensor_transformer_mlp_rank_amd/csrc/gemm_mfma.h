@@ -1121,9 +1121,17 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
           }
         }
       }
-      if constexpr (h == 1 && (sl & 3) == 3) issue_one(kt + kStages, sl >> 2);
+      // loads of stage kt+2: the A tile's eight once every wave has read A of
+      // stage kt (the barrier after slot 23), one every fifth slot; the B
+      // tile's eight after the stage's main barrier, one every eighth slot
+      if constexpr (i >= 25 && i < 25 + 5 * 8 && (i - 25) % 5 == 0) issue_one(kt + kStages, (i - 25) / 5);
+      if constexpr (h == 1 && (sl & 7) == 3) issue_one(kt + kStages, 8 + (sl >> 3));
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (i == 63) wait_and_barrier<0>();
+      // A's fragments of k-step 1 are read in slots 0..21 (and the column-sum
+      // parts at slot 1): after this barrier A of stage kt is free
+      if constexpr (i == 23) wait_and_barrier<63>();
+      // stage kt+1 has landed: all but this stage's eight A loads are done
+      if constexpr (i == 63) wait_and_barrier<8>();
     });
   };
 
