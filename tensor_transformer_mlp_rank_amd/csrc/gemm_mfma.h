@@ -955,17 +955,16 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // zeros (which also makes the fused column sum of those stages zero), and
   // the number of loads in flight stays uniform: one wait count, no branches.
   //
-  // Stage kt with two K-major operands (kMma MFMAs issued from registers; a
-  // scheduling barrier after every slot pins the interleave):
-  //   first quarter   MFMAs of k-step 0; reads of the stage's second half of
-  //                   k-steps (and its column sums)
+  // FP8 stage kt with two K-major operands (32 MFMAs of 32x32x64 issued from
+  // registers, two k-steps; a scheduling barrier after every slot pins the
+  // interleave):
+  //   first quarter   MFMAs of k-step 0; reads of the stage's k-step 1
   //   barrier         every wave has finished reading stage kt, so its
   //                   buffer is free, and stage kt+1 has landed (this wave's
   //                   loads: vmcnt(0); every wave's: the barrier)
   //   middle half     MFMAs; the 16 loads of stage kt+2 into stage kt's
-  //                   buffer, one per two slots (one per slot for e4m3)
-  //   last quarter    MFMAs of the last k-step; reads of stage kt+1's first
-  //                   half of k-steps
+  //                   buffer, one per slot
+  //   last quarter    MFMAs of k-step 1; reads of stage kt+1's k-step 0
   // One barrier per stage: the loads of stage kt+1 have the last quarter of
   // stage kt-1 and the first quarter of stage kt to land.
   constexpr int kMma = 16 * kKs;
@@ -974,14 +973,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   constexpr int kReadsQ = 8 * kHalfKs;   // fragments read per quarter
   constexpr int kDmaEvery = (kMma / 2) / 16;
   auto stage_iter = [&](int kt) __attribute__((always_inline)) {
-    // Fragment reads are asm (not tracked by the compiler). bf16: the previous
-    // last quarter's k-step 0 must have landed (its 8 reads of k-step 1, one
-    // instruction each, may still be in flight). FP8 (two k-steps, two
-    // instructions per fragment): the last quarter read all of k-step 0,
-    // A0..3 then B0..3; MFMA i < 4 needs B_i, followed by three fragment reads
-    // (six instructions, counting this quarter's reads issued since), so a
-    // wait for at most 6 in flight precedes each of the first four MFMAs.
-    if constexpr (!IS_FP8) wait_lds<8>();
+    // Fragment reads are asm (not tracked by the compiler), two instructions
+    // per fragment. The last quarter read all of k-step 0, A0..3 then B0..3;
+    // MFMA i < 4 needs B_i, followed by three fragment reads (six
+    // instructions, counting this quarter's reads issued since), so a wait for
+    // at most 6 in flight precedes each of the first four MFMAs.
     // reads of quarter slot q (kReadsQ fragments over kQ slots) of k-steps
     // ks0, ks0 + 1
     auto reads_at = [&](int kt_r, auto Q, auto KS0) __attribute__((always_inline)) {
@@ -997,7 +993,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
       }
     };
     static_for<kQ>([&](auto I) {
-      if constexpr (IS_FP8 && decltype(I)::value < 4) wait_lds<6>();
+      if constexpr (decltype(I)::value < 4) wait_lds<6>();
       mma(decltype(I)::value);
       reads_at(kt, I, IC<kHalfKs>{});
       __builtin_amdgcn_sched_barrier(0);
@@ -1019,21 +1015,17 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     });
   };
 
-  // bf16 stage kt with an MN-major operand (64 slots in four groups of 16,
-  // group q issuing the MFMAs of k-step q): the 8 fragments of a k-step are read right after the
-  // previous stage's MFMAs of that k-step have released their registers, one
-  // every two slots, so the LDS reads are spread evenly over the stage
-  // instead of coming in two bursts:
-  //   group 0   reads of stage kt's k-step 3 (and of its column-sum parts)
+  // FP8 stage kt with an MN-major operand (32 slots in two groups of 16,
+  // group q issuing the MFMAs of k-step q): the 8 fragments of a k-step are
+  // read right after the previous stage's MFMAs of that k-step have released
+  // their registers, one every two slots, so the LDS reads are spread over
+  // the stage instead of coming in bursts:
+  //   group 0   reads of stage kt's k-step 1 (and of its column-sum parts)
   //   barrier   every wave has finished reading stage kt, and stage kt+1
   //             has landed (vmcnt(0))
-  //   group 1   reads of stage kt+1's k-step 0; loads 0..7 of stage kt+2;
+  //   group 1   reads of stage kt+1's k-step 0; the 16 loads of stage kt+2;
   //             the column-sum parts are added
-  //   group 2   reads of stage kt+1's k-step 1; loads 8..15 of stage kt+2
-  //   group 3   reads of stage kt+1's k-step 2
-  // FP8 (two k-steps of 64): group 0 reads stage kt's k-step 1; group 1
-  // reads stage kt+1's k-step 0 and issues the 16 loads of stage kt+2.
-  constexpr int kDmaStride = IS_FP8 ? 1 : 2;  // slots per load from slot 16 on
+  constexpr int kDmaStride = 1;  // slots per load from slot 16 on
   // Column sums: in a stage whose sums are this workgroup's share, slot 1
   // reads the eight parts; slot 1 of the next stage adds them (the waits at
   // the barrier and at the top of the stage cover the reads). One uniform
@@ -1041,9 +1033,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   u32x4 cs_buf[8];
   int cs_pending = 0;
   auto stage_iter_rolling = [&](int kt) __attribute__((always_inline)) {
-    // transpose reads (asm, not tracked by the compiler) of the previous
+    // fragment reads (asm, not tracked by the compiler) of the previous
     // stage must have landed before their first use here
-    if constexpr (!A_K || !B_K) wait_lds();
+    wait_lds();
     // 1: add the parts read in the previous stage; 2: read this stage's
     int cs_mode = 0;
     if constexpr (COLSUM) {
