@@ -252,12 +252,23 @@ struct KMajorLoader {
   __device__ __forceinline__ static bool up_half(int ii) {
     return ((ii >> 2) & 3) >= 2;  // fragment (row / 32) % 4 of these rows
   }
+  // For a K that is a whole number of stages, the K-range test only tells
+  // rows past the tensor's end apart: fold that into the offsets once
+  // (kOOB for such rows), and the loads of issue_one<true> need no
+  // per-lane instruction at all. Their stages past the end of K then read
+  // whatever lies behind (the next row, or zeros past the resource), into
+  // stage buffers that no MFMA reads.
+  __device__ __forceinline__ void fold_rows() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) voff[i] = klim[i] ? voff[i] : kOOB;
+  }
+  template <bool FAST>
   __device__ __forceinline__ void issue_one(char* tile, int wave, uint32_t k0b, int i) const {
     const int ii = 8 * wave + i;
     // one compare and one select, no per-lane branch; the stage's k offset
     // is the instruction's scalar offset (a lane past the end keeps an
     // offset of at least kOOB, beyond any resource)
-    const uint32_t off = (k0b < klim[i]) ? voff[i] : kOOB;
+    const uint32_t off = FAST ? voff[i] : (k0b < klim[i]) ? voff[i] : kOOB;
     if constexpr (PAIR) {
       if (up_half(ii))
         lds_dma16(make_rsrc(base1, bytes1), tile + (ii << 10), off, k0b);
@@ -824,20 +835,22 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
 
   // This wave's load instruction j of stage kt: j = 0..7 fill its part of
   // the A tile, 8..15 of the B tile.
-  auto issue_one = [&](int kt, int j) __attribute__((always_inline)) {
+  // FAST (std::true_type): K-major loaders folded (fold_rows), no K-range test
+  auto issue_one = [&](int kt, int j, auto FAST) __attribute__((always_inline)) {
+    constexpr bool fast = decltype(FAST)::value;
     char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
     char* sb = sa + kTileBytes;
     if (j < 8) {
-      if constexpr (A_K) la.issue_one(sa, wave, (uint32_t)((kt0 + kt) * kRowBytes), j);
+      if constexpr (A_K) la.template issue_one<fast>(sa, wave, (uint32_t)((kt0 + kt) * kRowBytes), j);
       else lma.issue_one(sa, wave, (kt0 + kt) * kStep, j);
     } else {
-      if constexpr (B_K) lb.issue_one(sb, wave, (uint32_t)((kt0 + kt) * kRowBytes), j - 8);
+      if constexpr (B_K) lb.template issue_one<fast>(sb, wave, (uint32_t)((kt0 + kt) * kRowBytes), j - 8);
       else lmb.issue_one(sb, wave, (kt0 + kt) * kStep, j - 8);
     }
   };
   auto issue = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) issue_one(kt, j);
+    for (int j = 0; j < 16; ++j) issue_one(kt, j, std::false_type{});
   };
 
   // accumulators: bf16, 8 x 8 blocks of the 16x16x32 MFMA (4 registers
@@ -972,7 +985,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   constexpr int kHalfKs = kKs / 2;       // k-steps read per quarter
   constexpr int kReadsQ = 8 * kHalfKs;   // fragments read per quarter
   constexpr int kDmaEvery = (kMma / 2) / 16;
-  auto stage_iter = [&](int kt) __attribute__((always_inline)) {
+  auto stage_iter = [&](int kt, auto FAST) __attribute__((always_inline)) {
     // Fragment reads are asm (not tracked by the compiler), two instructions
     // per fragment. The last quarter read all of k-step 0, A0..3 then B0..3;
     // MFMA i < 4 needs B_i, followed by three fragment reads (six
@@ -1005,7 +1018,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     static_for<2 * kQ>([&](auto I) {
       constexpr int i = kQ + decltype(I)::value;
       mma(i);
-      if constexpr ((i - kQ) % kDmaEvery == kDmaEvery - 1) issue_one(kt + kStages, (i - kQ) / kDmaEvery);
+      if constexpr ((i - kQ) % kDmaEvery == kDmaEvery - 1) issue_one(kt + kStages, (i - kQ) / kDmaEvery, FAST);
       __builtin_amdgcn_sched_barrier(0);
     });
     static_for<kQ>([&](auto Q) {
@@ -1032,7 +1045,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // branch per stage, laid out for the common case of no column sums.
   u32x4 cs_buf[8];
   int cs_pending = 0;
-  auto stage_iter_rolling = [&](int kt) __attribute__((always_inline)) {
+  auto stage_iter_rolling = [&](int kt, auto FAST) __attribute__((always_inline)) {
     // fragment reads (asm, not tracked by the compiler) of the previous
     // stage must have landed before their first use here
     wait_lds();
@@ -1065,7 +1078,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
         }
       }
       if constexpr (i >= 16 && i < 16 + 16 * kDmaStride && (i - 16) % kDmaStride == kDmaStride - 1)
-        issue_one(kt + kStages, (i - 16) / kDmaStride);
+        issue_one(kt + kStages, (i - 16) / kDmaStride, FAST);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (i == 15) wait_and_barrier<0>();
     });
@@ -1084,7 +1097,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   //   slots 64..127   the 16 loads of stage kt+2, one every fourth slot
   // A load has a whole stage to land, and every read has 16 slots before the
   // wait that covers it (the barrier, or the top of the next stage).
-  auto stage_iter16 = [&](int kt) __attribute__((always_inline)) {
+  auto stage_iter16 = [&](int kt, auto FAST) __attribute__((always_inline)) {
     wait_lds();  // this stage's k-step 0 (read in slots 64..111 of the last)
     int cs_mode = 0;
     if constexpr (COLSUM) {
@@ -1116,8 +1129,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
       // loads of stage kt+2: the A tile's eight once every wave has read A of
       // stage kt (the barrier after slot 23), one every fifth slot; the B
       // tile's eight after the stage's main barrier, one every eighth slot
-      if constexpr (i >= 25 && i < 25 + 5 * 8 && (i - 25) % 5 == 0) issue_one(kt + kStages, (i - 25) / 5);
-      if constexpr (h == 1 && (sl & 7) == 3) issue_one(kt + kStages, 8 + (sl >> 3));
+      if constexpr (i >= 25 && i < 25 + 5 * 8 && (i - 25) % 5 == 0) issue_one(kt + kStages, (i - 25) / 5, FAST);
+      if constexpr (h == 1 && (sl & 7) == 3) issue_one(kt + kStages, 8 + (sl >> 3), FAST);
       __builtin_amdgcn_sched_barrier(0);
       // A's fragments of k-step 1 are read in slots 0..21 (and the column-sum
       // parts at slot 1): after this barrier A of stage kt is free
@@ -1135,21 +1148,33 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // the reads costly; with two K-major operands the quarter schedule measured
   // slightly faster.
   constexpr bool kRolling = !A_K || !B_K;
+  // A K of whole stages (every product at the benchmark shapes) runs the main
+  // loop with folded K-major loaders; a ragged K keeps the per-lane test.
+  const bool kfast = (A_K || B_K) && g.K % kStep == 0;
+  auto main_loop = [&](auto stage) __attribute__((always_inline)) {
+    if (kfast) {
+      if constexpr (A_K) la.fold_rows();
+      if constexpr (B_K) lb.fold_rows();
+      for (int kt = 0; kt < nk; ++kt) stage(kt, std::true_type{});
+    } else {
+      for (int kt = 0; kt < nk; ++kt) stage(kt, std::false_type{});
+    }
+  };
   if constexpr (!IS_FP8) {
     static_for<2 * kFr>([&](auto J) { read_one(0, IC<0>{}, J); });
-    for (int kt = 0; kt < nk; ++kt) stage_iter16(kt);
+    main_loop(stage_iter16);
   } else if constexpr (!kRolling) {
     static_for<kReadsQ>([&](auto J) {
       constexpr int j = decltype(J)::value;
       read_one(0, IC<j / 8>{}, IC<j & 7>{});
     });
-    for (int kt = 0; kt < nk; ++kt) stage_iter(kt);
+    main_loop(stage_iter);
   } else {
     static_for<8 * (kKs - 1)>([&](auto J) {
       constexpr int j = decltype(J)::value;
       read_one(0, IC<j / 8>{}, IC<j & 7>{});
     });
-    for (int kt = 0; kt < nk; ++kt) stage_iter_rolling(kt);
+    main_loop(stage_iter_rolling);
   }
   // The last stage's transpose reads ahead (asm: the compiler does not know
   // they are in flight) must land before their registers are reused.
