@@ -247,6 +247,9 @@ hipError_t run_gemm(Kind kind, Step step, const char* label, GemmArgs g, const E
   if (mfma_grid(step, g) == 0) return hipSuccess;
   g.k_splits = sp;
   g.split_stages = (int)(((g.K + 63) / 64 + sp - 1) / sp);
+  // even, so that every split but the last can take the kernel's loop for
+  // K-major operands without a per-lane K-range test
+  g.split_stages += g.split_stages & 1;
   EpiArgs ep = e;
   ep.out = part;
   ep.ldo = g.N;

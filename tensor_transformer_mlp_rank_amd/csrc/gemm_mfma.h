@@ -103,6 +103,21 @@ constexpr int kStages = 2;
 constexpr int kTileBytes = 256 * kRowBytes;        // 32 KiB
 constexpr int kStageBytes = 2 * kTileBytes;        // A + B
 constexpr int kSmemBytes = kStages * kStageBytes;  // 128 KiB
+// LDS: A of stages 0, 1, then B of stages 0, 1 (32 KiB each). A fragment read
+// adds its stage's offset (0 or 32 KiB) in the instruction's offset field,
+// and the main loop runs two stages per iteration, so the per-lane read
+// addresses stay the same from stage to stage.
+constexpr int kTileB0 = kStages * kTileBytes;      // first B tile
+// A stage's buffer parity: IC<0>/IC<1> where the loop knows it at compile
+// time (then the buffer's offset goes into the reads' offset field), or an int.
+template <typename P>
+struct ParityOffset {
+  static constexpr int value = 0;  // runtime parity: added to the address
+};
+template <int P>
+struct ParityOffset<std::integral_constant<int, P>> {
+  static constexpr int value = P * kTileBytes;
+};
 
 // XCD remap: hardware sends workgroup b to XCD b % 8; this gives the
 // workgroups of one XCD consecutive ids out of nb.
@@ -838,8 +853,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // FAST (std::true_type): K-major loaders folded (fold_rows), no K-range test
   auto issue_one = [&](int kt, int j, auto FAST) __attribute__((always_inline)) {
     constexpr bool fast = decltype(FAST)::value;
-    char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
-    char* sb = sa + kTileBytes;
+    char* sa = smem + (kt & (kStages - 1)) * kTileBytes;
+    char* sb = smem + kTileB0 + (kt & (kStages - 1)) * kTileBytes;
     if (j < 8) {
       if constexpr (A_K) la.template issue_one<fast>(sa, wave, (uint32_t)((kt0 + kt) * kRowBytes), j);
       else lma.issue_one(sa, wave, (kt0 + kt) * kStep, j);
@@ -890,21 +905,32 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   Frag fa[kKs][kFr], fb[kKs][kFr];
   // fragment J of k-step KS of stage kt: A0..A(kFr-1), then B0.. (KS and J
   // are compile-time constants: they select registers and offsets)
-  auto read_one = [&](int kt, auto KS, auto J) __attribute__((always_inline)) {
+  auto read_one = [&](auto PAR, auto KS, auto J) __attribute__((always_inline)) {
     constexpr int ks = decltype(KS)::value, j = decltype(J)::value, f = j % kFr;
-    const char* st = smem + (kt & (kStages - 1)) * kStageBytes;
+    constexpr int po = ParityOffset<decltype(PAR)>::value;  // compile-time stage offset
+    int pr = 0;                                            // runtime stage offset
+    if constexpr (std::is_same<decltype(PAR), int>::value) pr = PAR * kTileBytes;
+    const char* ta = smem + pr;            // A tiles
+    const char* tb = smem + kTileB0 + pr;  // B tiles
     if constexpr (j < kFr) {
-      if constexpr (IS_FP8 && A_K) fa[ks][f] = frag_k_e4m3<0, ks, f>(st, 128 * wm, lane);
-      else if constexpr (IS_FP8) fa[ks][f] = frag_mn_fp8<0, ks>(st, 128 * wm + 32 * f, lane);
-      else if constexpr (A_K) fa[ks][f] = frag_k_bf16<0, ks, f>(st, 128 * wm, lane);
-      else fa[ks][f] = frag_mn_bf16<0, ks>(st, 128 * wm + 16 * f, lane);
+      if constexpr (IS_FP8 && A_K) fa[ks][f] = frag_k_e4m3<po, ks, f>(ta, 128 * wm, lane);
+      else if constexpr (IS_FP8) fa[ks][f] = frag_mn_fp8<po, ks>(ta, 128 * wm + 32 * f, lane);
+      else if constexpr (A_K) fa[ks][f] = frag_k_bf16<po, ks, f>(ta, 128 * wm, lane);
+      else fa[ks][f] = frag_mn_bf16<po, ks>(ta, 128 * wm + 16 * f, lane);
     } else {
-      if constexpr (IS_FP8 && B_K) fb[ks][f] = frag_k_e4m3<kTileBytes, ks, f>(st, 128 * wn, lane);
-      else if constexpr (IS_FP8) fb[ks][f] = frag_mn_fp8<kTileBytes, ks>(st, 128 * wn + 32 * f, lane);
-      else if constexpr (B_K) fb[ks][f] = frag_k_bf16<kTileBytes, ks, f>(st, 128 * wn, lane);
-      else fb[ks][f] = frag_mn_bf16<kTileBytes, ks>(st, 128 * wn + 16 * f, lane);
+      if constexpr (IS_FP8 && B_K) fb[ks][f] = frag_k_e4m3<po, ks, f>(tb, 128 * wn, lane);
+      else if constexpr (IS_FP8) fb[ks][f] = frag_mn_fp8<po, ks>(tb, 128 * wn + 32 * f, lane);
+      else if constexpr (B_K) fb[ks][f] = frag_k_bf16<po, ks, f>(tb, 128 * wn, lane);
+      else fb[ks][f] = frag_mn_bf16<po, ks>(tb, 128 * wn + 16 * f, lane);
     }
   };
+  // the parity of the stage after one of parity P
+  auto next_parity = [](auto P) __attribute__((always_inline)) {
+    if constexpr (std::is_same<decltype(P), int>::value) return P ^ 1;
+    else return IC<1 - decltype(P)::value>{};
+  };
+
+
   auto mma = [&](int i) __attribute__((always_inline)) {
     if constexpr (IS_FP8) {
       // MFMA i of a stage: k-step i/16, row block (i/4)%4, column block i%4
@@ -930,7 +956,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // colsum_issue reads part j without waiting for it; colsum_add adds it
   // once a wait has covered the read.
   auto colsum_issue = [&](int kt, int j) __attribute__((always_inline)) -> u32x4 {
-    const char* sa = smem + (kt & (kStages - 1)) * kStageBytes;
+    const char* sa = smem + (kt & (kStages - 1)) * kTileBytes;
     if constexpr (IS_FP8) {
       const int c = tid & 15;
       const int kr = (tid >> 4) + 16 * j;
@@ -985,7 +1011,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   constexpr int kHalfKs = kKs / 2;       // k-steps read per quarter
   constexpr int kReadsQ = 8 * kHalfKs;   // fragments read per quarter
   constexpr int kDmaEvery = (kMma / 2) / 16;
-  auto stage_iter = [&](int kt, auto FAST) __attribute__((always_inline)) {
+  auto stage_iter = [&](int kt, auto FAST, auto PAR) __attribute__((always_inline)) {
+    const auto PAR1 = next_parity(PAR);  // stage kt+1
     // Fragment reads are asm (not tracked by the compiler), two instructions
     // per fragment. The last quarter read all of k-step 0, A0..3 then B0..3;
     // MFMA i < 4 needs B_i, followed by three fragment reads (six
@@ -993,22 +1020,22 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     // at most 6 in flight precedes each of the first four MFMAs.
     // reads of quarter slot q (kReadsQ fragments over kQ slots) of k-steps
     // ks0, ks0 + 1
-    auto reads_at = [&](int kt_r, auto Q, auto KS0) __attribute__((always_inline)) {
+    auto reads_at = [&](auto PR, auto Q, auto KS0) __attribute__((always_inline)) {
       constexpr int q = decltype(Q)::value, ks0 = decltype(KS0)::value;
       if constexpr (kReadsQ >= kQ) {
         static_for<kReadsQ / kQ>([&](auto R) {
           constexpr int j = q * (kReadsQ / kQ) + decltype(R)::value;
-          read_one(kt_r, IC<ks0 + j / 8>{}, IC<j & 7>{});
+          read_one(PR, IC<ks0 + j / 8>{}, IC<j & 7>{});
         });
       } else if constexpr (q % (kQ / kReadsQ) == 0) {
         constexpr int j = q / (kQ / kReadsQ);
-        read_one(kt_r, IC<ks0 + j / 8>{}, IC<j & 7>{});
+        read_one(PR, IC<ks0 + j / 8>{}, IC<j & 7>{});
       }
     };
     static_for<kQ>([&](auto I) {
       if constexpr (decltype(I)::value < 4) wait_lds<6>();
       mma(decltype(I)::value);
-      reads_at(kt, I, IC<kHalfKs>{});
+      reads_at(PAR, I, IC<kHalfKs>{});
       __builtin_amdgcn_sched_barrier(0);
     });
     // the stage's one barrier: every wave is done reading stage kt (its
@@ -1023,7 +1050,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     });
     static_for<kQ>([&](auto Q) {
       mma(3 * kQ + decltype(Q)::value);
-      reads_at(kt + 1, Q, IC<0>{});
+      reads_at(PAR1, Q, IC<0>{});
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -1040,41 +1067,42 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   //             the column-sum parts are added
   constexpr int kDmaStride = 1;  // slots per load from slot 16 on
   // Column sums: in a stage whose sums are this workgroup's share, slot 1
-  // reads the eight parts; slot 1 of the next stage adds them (the waits at
-  // the barrier and at the top of the stage cover the reads). One uniform
-  // branch per stage, laid out for the common case of no column sums.
-  u32x4 cs_buf[8];
-  int cs_pending = 0;
-  auto stage_iter_rolling = [&](int kt, auto FAST) __attribute__((always_inline)) {
+  // reads the eight parts, and the slot after the stage's first barrier (whose
+  // wait covers the reads) adds them. The parts live within one stage: the
+  // reads are asm, so the compiler takes their registers as written at once,
+  // and a value it kept across stages could be spilled before its data
+  // arrived. One uniform branch at each of the two slots, laid out for the
+  // common case of no column sums.
+  auto stage_iter_rolling = [&](int kt, auto FAST, auto PAR) __attribute__((always_inline)) {
+    const auto PAR1 = next_parity(PAR);  // stage kt+1
     // fragment reads (asm, not tracked by the compiler) of the previous
     // stage must have landed before their first use here
     wait_lds();
-    // 1: add the parts read in the previous stage; 2: read this stage's
-    int cs_mode = 0;
+    int cs_mode = 0;  // this stage's column sums are this workgroup's share
+    u32x4 cs_buf[8];
     if constexpr (COLSUM) {
       const int on = (do_colsum && kt == cs_next) ? 1 : 0;
       cs_next += on * g.tiles_n;
-      cs_mode = __builtin_amdgcn_readfirstlane(cs_pending | (on << 1));
-      cs_pending = on;
+      cs_mode = __builtin_amdgcn_readfirstlane(on);
     }
     static_for<kMma>([&](auto I) {
       constexpr int i = decltype(I)::value;
       mma(i);
       constexpr int grp = i >> 4, r = i & 15;
       if constexpr ((r & 1) == 0) {
-        if constexpr (grp == 0) read_one(kt, IC<kKs - 1>{}, IC<(r >> 1)>{});
-        else read_one(kt + 1, IC<grp - 1>{}, IC<(r >> 1)>{});
+        if constexpr (grp == 0) read_one(PAR, IC<kKs - 1>{}, IC<(r >> 1)>{});
+        else read_one(PAR1, IC<grp - 1>{}, IC<(r >> 1)>{});
       }
       if constexpr (COLSUM && i == 1) {
         if (__builtin_expect(cs_mode != 0, 0)) {
-          if (cs_mode & 1) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) colsum_add(cs_buf[j]);
-          }
-          if (cs_mode & 2) {
+          for (int j = 0; j < 8; ++j) cs_buf[j] = colsum_issue(kt, j);
+        }
+      }
+      if constexpr (COLSUM && i == 16) {
+        if (__builtin_expect(cs_mode != 0, 0)) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) cs_buf[j] = colsum_issue(kt, j);
-          }
+          for (int j = 0; j < 8; ++j) colsum_add(cs_buf[j]);
         }
       }
       if constexpr (i >= 16 && i < 16 + 16 * kDmaStride && (i - 16) % kDmaStride == kDmaStride - 1)
@@ -1097,33 +1125,34 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   //   slots 64..127   the 16 loads of stage kt+2, one every fourth slot
   // A load has a whole stage to land, and every read has 16 slots before the
   // wait that covers it (the barrier, or the top of the next stage).
-  auto stage_iter16 = [&](int kt, auto FAST) __attribute__((always_inline)) {
+  auto stage_iter16 = [&](int kt, auto FAST, auto PAR) __attribute__((always_inline)) {
+    const auto PAR1 = next_parity(PAR);  // stage kt+1
     wait_lds();  // this stage's k-step 0 (read in slots 64..111 of the last)
-    int cs_mode = 0;
+    int cs_mode = 0;  // this stage's column sums are this workgroup's share
+    u32x4 cs_buf[8];
     if constexpr (COLSUM) {
       const int on = (do_colsum && kt == cs_next) ? 1 : 0;
       cs_next += on * g.tiles_n;
-      cs_mode = __builtin_amdgcn_readfirstlane(cs_pending | (on << 1));
-      cs_pending = on;
+      cs_mode = __builtin_amdgcn_readfirstlane(on);
     }
     static_for<128>([&](auto I) {
       constexpr int i = decltype(I)::value;
       constexpr int h = i >> 6, sl = i & 63;
       mma(i);
       if constexpr (sl % 3 == 0 && sl / 3 < 2 * kFr) {
-        if constexpr (h == 0) read_one(kt, IC<1>{}, IC<sl / 3>{});
-        else read_one(kt + 1, IC<0>{}, IC<sl / 3>{});
+        if constexpr (h == 0) read_one(PAR, IC<1>{}, IC<sl / 3>{});
+        else read_one(PAR1, IC<0>{}, IC<sl / 3>{});
       }
       if constexpr (COLSUM && i == 1) {
         if (__builtin_expect(cs_mode != 0, 0)) {
-          if (cs_mode & 1) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) colsum_add(cs_buf[j]);
-          }
-          if (cs_mode & 2) {
+          for (int j = 0; j < 8; ++j) cs_buf[j] = colsum_issue(kt, j);
+        }
+      }
+      if constexpr (COLSUM && i == 24) {
+        if (__builtin_expect(cs_mode != 0, 0)) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) cs_buf[j] = colsum_issue(kt, j);
-          }
+          for (int j = 0; j < 8; ++j) colsum_add(cs_buf[j]);
         }
       }
       // loads of stage kt+2: the A tile's eight once every wave has read A of
@@ -1148,31 +1177,55 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // the reads costly; with two K-major operands the quarter schedule measured
   // slightly faster.
   constexpr bool kRolling = !A_K || !B_K;
-  // A K of whole stages (every product at the benchmark shapes) runs the main
-  // loop with folded K-major loaders; a ragged K keeps the per-lane test.
-  const bool kfast = (A_K || B_K) && g.K % kStep == 0;
+  // The main loop runs two stages per iteration, even ones in buffer 0 and odd
+  // ones in buffer 1, so each read's stage offset is an immediate and the
+  // per-lane read addresses stay the same from stage to stage.
+  //  * Both operands MN-major (the weight gradients): always so. An odd count
+  //    of stages gets one more, whose loads fall past the k-rows of both
+  //    resources and fill the tiles with zeros.
+  //  * A K-major operand: so when K is a whole number of stages and the count
+  //    is even (every product at the benchmark shapes; split-K gives every
+  //    split but the last an even count), with folded loaders (no per-lane K
+  //    test). Otherwise one stage per iteration, with the stage's parity added
+  //    to the read addresses and the K test on every K-major load. A K-major
+  //    load whose lanes are all out of range leaves LDS unwritten, so these
+  //    products cannot pad with a stage of zeros.
+  // (A conditional stage inside or after the paired loop made the compiler
+  // move the accumulators between registers; with both loop forms the column
+  // sum kernels spilled an asm read's destination before the read landed.)
+  auto pair_loop = [&](auto stage, auto FAST, int n) __attribute__((always_inline)) {
+    for (int kt = 0; kt < n; kt += 2) {
+      stage(kt, FAST, IC<0>{});
+      stage(kt + 1, FAST, IC<1>{});
+    }
+  };
   auto main_loop = [&](auto stage) __attribute__((always_inline)) {
-    if (kfast) {
-      if constexpr (A_K) la.fold_rows();
-      if constexpr (B_K) lb.fold_rows();
-      for (int kt = 0; kt < nk; ++kt) stage(kt, std::true_type{});
+    if constexpr (!A_K && !B_K) {
+      pair_loop(stage, std::false_type{}, nk + (nk & 1));
     } else {
-      for (int kt = 0; kt < nk; ++kt) stage(kt, std::false_type{});
+      static_assert(!COLSUM, "the fused column sum reads an MN-major A tile");
+      if ((nk & 1) == 0 && g.K % kStep == 0) {
+        if constexpr (A_K) la.fold_rows();
+        if constexpr (B_K) lb.fold_rows();
+        pair_loop(stage, std::true_type{}, nk);
+      } else {
+        for (int kt = 0; kt < nk; ++kt) stage(kt, std::false_type{}, kt & 1);
+      }
     }
   };
   if constexpr (!IS_FP8) {
-    static_for<2 * kFr>([&](auto J) { read_one(0, IC<0>{}, J); });
+    static_for<2 * kFr>([&](auto J) { read_one(IC<0>{}, IC<0>{}, J); });
     main_loop(stage_iter16);
   } else if constexpr (!kRolling) {
     static_for<kReadsQ>([&](auto J) {
       constexpr int j = decltype(J)::value;
-      read_one(0, IC<j / 8>{}, IC<j & 7>{});
+      read_one(IC<0>{}, IC<j / 8>{}, IC<j & 7>{});
     });
     main_loop(stage_iter);
   } else {
     static_for<8 * (kKs - 1)>([&](auto J) {
       constexpr int j = decltype(J)::value;
-      read_one(0, IC<j / 8>{}, IC<j & 7>{});
+      read_one(IC<0>{}, IC<j / 8>{}, IC<j & 7>{});
     });
     main_loop(stage_iter_rolling);
   }
@@ -1184,13 +1237,6 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     // before any instruction reads their accumulators
     asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
   }
-  if constexpr (COLSUM) {
-    if (cs_pending) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) colsum_add(cs_buf[j]);
-    }
-  }
-
   // ---- fused column sum of A: this workgroup's share of the k-stages
   if constexpr (COLSUM) {
     if (do_colsum) {
