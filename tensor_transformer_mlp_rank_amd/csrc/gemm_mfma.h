@@ -28,15 +28,17 @@
 //
 // Pipeline: K advances 128 bytes per row per stage (64 bf16 / 128 e4m3
 // elements, whole cache lines per request); a stage holds a 32 KiB A tile and
-// a 32 KiB B tile; two stages (128 KiB of the 160 KiB LDS) alternate. Tiles go
-// from HBM straight into LDS with buffer_load_dwordx4 ... lds (no staging
-// registers, no LDS store instructions); the buffer resource's range check
-// turns reads past a tensor's end into zeros. Within a stage (see
-// stage_iter16 for bf16, stage_iter and stage_iter_rolling for FP8) the
-// MFMAs run from registers while the LDS reads for the next k-steps and the
-// loads of stage k+2 are interleaved between them; one barrier per stage
-// hands the buffers over. It is a plain
-// s_barrier preceded by an explicit wait (vmcnt for this wave's loads,
+// a 32 KiB B tile; two stages (128 KiB of the 160 KiB LDS, laid out A0 A1 B0
+// B1) alternate, and the main loop runs them in pairs so that a read's stage
+// offset is an immediate (see main_loop). Tiles go from HBM straight into LDS
+// with buffer_load_dwordx4 ... lds (no staging registers, no LDS store
+// instructions); the buffer resource's range check turns reads past a
+// tensor's end into zeros. Within a stage (see stage_iter16 for bf16,
+// stage_iter and stage_iter_rolling for FP8) the MFMAs run from registers
+// while the LDS reads for the next k-steps and the loads of stage k+2 are
+// interleaved between them; barriers inside the stage hand the buffers over
+// (bf16: one when A is free, one when the next stage has landed). Each is a
+// plain s_barrier preceded by an explicit wait (vmcnt for this wave's loads,
 // lgkmcnt for its LDS reads): a full __syncthreads would drain all loads in
 // flight and serialise the pipeline.
 //
