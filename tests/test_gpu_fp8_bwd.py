@@ -287,7 +287,11 @@ def _fp8_block(tp, T, H, Fs, seed, prior=False):
         assert v <= TOL["e4m3"], (k, v)
 
 
-@pytest.mark.parametrize("T,H,Fs", [(300, 528, 272), (64, 256, 512), (37, 48, 32), (513, 1040, 400)])
+# (200, 384, 272): with 128-element FP8 stages, T=200 ragged with an even
+# number of stages (the weight gradients' paired loop), H=384 a whole but odd
+# number (the one-stage loop)
+@pytest.mark.parametrize("T,H,Fs", [(300, 528, 272), (64, 256, 512), (37, 48, 32), (513, 1040, 400),
+                                    (200, 384, 272)])
 def test_fp8_block_small_and_ragged(tp, T, H, Fs):
     _fp8_block(tp, T, H, Fs, seed=900 + T)
 

@@ -61,6 +61,12 @@ SHAPES = [
     (64, 1040, 400),
     (1, 16, 16),
     (37, 48, 32),
+    # the main loop's forms (64-element stages): H=192 a whole but odd number
+    # of stages, Fs=80 and Fs=208 ragged with an even number, T=100 ragged and
+    # even for the weight gradients' paired loop, T=192 whole and odd (their
+    # padded stage)
+    (100, 192, 80),
+    (192, 320, 208),
 ]
 
 
