@@ -67,6 +67,9 @@ SHAPES = [
     # padded stage)
     (100, 192, 80),
     (192, 320, 208),
+    # one tile, Fs of 17 stages: fc2's forward and fc1's data gradient split K
+    # in two, 10 stages (paired loop) and 7 (one-stage loop)
+    (256, 256, 1088),
 ]
 
 
