@@ -6,10 +6,17 @@ synthetic per-rank inputs (default workload: T = 8192 tokens (4 x 2048),
 H = 8192, F = 32768 at TP = 8, i.e. Fs = 4096). Inputs and all output
 buffers are resident in HBM before the timed region.
 
-Prints one JSON line: TFLOP/s of the whole step (algorithmic FLOPs
-6*T*H*Fs*(G+1) over the measured time), the dominant kernel's roofline
-(its average launch time from HIP events recorded on its launch stream during
-the timed steps) and the CPU oracle's throughput on a bounded sample.
+Parity comes first: one step in the timed steps' launch configuration is
+compared, tensor by tensor, with the CPU oracle on the whole workload
+(max|gpu - oracle| / max|oracle| within 1e-5 for fp32, 2e-2 for bf16, 6e-2
+for e4m3); on a miss the script exits with status 3 and prints no line.
+
+Then prints one JSON line: TFLOP/s of the whole step (algorithmic FLOPs
+6*T*H*Fs*(G+1) over the measured time), its fraction of the vendor peak and
+of the peak at the graphics clock sampled during the timed steps, the parity
+errors, the dominant kernel's roofline (its average launch time from HIP
+events recorded on its launch stream during the timed steps) and the CPU
+oracle's throughput on a bounded sample.
 
 FP8 (e4m3) steps: x, W1, W2 are E4M3 codes and dy E5M2 codes, quantised
 once before the timed region (per-tensor current scaling); inside it the
@@ -33,6 +40,11 @@ if ROOT not in sys.path:
 
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
 PEAK = {"bf16": 2516.6, "f32": 157.3, "e4m3": 5033.2}
+# MFMA FLOP per CU per clock (dense), for the peak at a measured clock
+FLOP_PER_CU_CLK = {"bf16": 4096, "f32": 256, "e4m3": 8192}
+N_CU = 256
+# parity tolerance per output tensor, max|gpu - oracle| / max|oracle|
+TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 6e-2}
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 HISTORY_LEN = 1024  # delayed-scaling amax history (the common default length)
@@ -176,77 +188,163 @@ def _cpu_cores() -> int:
     return cores or len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(w, calls, tokens: int, repeats: int = 3) -> dict:
+def rel_err(got, ref) -> float:
+    """max |gpu - oracle| / max |oracle| over one output tensor (the
+    tolerance metric of the block)."""
+    import numpy as np
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.shape != ref.shape:
+        raise SystemExit(f"parity: shape {got.shape} against the oracle's {ref.shape}")
+    if ref.size == 0:
+        return 0.0
+    den = float(np.max(np.abs(ref)))
+    num = float(np.max(np.abs(got - ref)))
+    return num / den if den > 0 else num
+
+
+def parity_report(gpu: dict, ref: dict, tol: dict) -> dict:
+    """Per-tensor relative errors of the device's parity step against the
+    oracle, and whether every one is within its tolerance."""
+    errs = {k: rel_err(gpu[k], ref[k]) for k in tol if gpu.get(k) is not None
+            and ref.get(k) is not None}
+    bad = {k: v for k, v in errs.items() if not v <= tol[k]}
+    return {"max_rel_err": {k: float(f"{v:.3e}") for k, v in errs.items()},
+            "tol": {k: tol[k] for k in errs}, "pass": not bad}
+
+
+def _mlp_oracle(w, calls, x, W1, b1, W2, dy, fp8, a_scale, dH_scale) -> dict:
+    """The oracle's outputs for the step's entry points (fp8: its FP8 block
+    at the scales the device quantised a and dH with)."""
+    import oracle
+    out = {}
+    if fp8:
+        f = oracle.rank_forward_fp8(x, W1, b1, W2, a_scale)
+        out.update(y=f["y"], h=f["h"], a=f["a"])
+        if "dgrad" in calls:
+            g = oracle.rank_dgrad_fp8(dy, W1, W2, f["h"], dH_scale)
+            out.update(dx=g["dx"])
+            if "wgrad" in calls:
+                out.update(oracle.rank_wgrad_fp8(dy, x, f["a_q"], g["dH_q"]))
+                if not w.has_bias:
+                    out["db1"] = None
+    else:
+        f = oracle.rank_forward(x, W1, b1, W2, w.act)
+        out.update(y=f["y"], h=f["h"], a=f["a"])
+        if "dgrad" in calls:
+            g = oracle.rank_dgrad(dy, W1, W2, f["h"], w.act)
+            out.update(dH=g["dH"], dx=g["dx"])
+            if "wgrad" in calls:
+                out.update(oracle.rank_wgrad(dy, x, f["a"], g["dH"], w.has_bias))
+    return out
+
+
+def cpu_baseline(w, calls, tokens: int, repeats: int = 3, gpu=None) -> dict:
     """The CPU oracle (fp64 NumPy, as it stands) on the first `tokens` tokens
     of the same per-rank shard: the step's entry points (for e4m3, the
-    oracle's FP8 block on the dequantised codes)."""
+    oracle's FP8 block on the dequantised codes). With `gpu` (the outputs of
+    the device's parity step on the whole shard, and for e4m3 the scales it
+    quantised a and dH with), the oracle also runs once on the whole shard and
+    every output is compared with the device's: the result's "parity"."""
     import numpy as np
     import oracle
     import synth
     cores = _cpu_cores()
-    inp = synth.make_rank_inputs(w, tokens=tokens)
-    x, W1, W2, dy = (oracle.to_f64(inp[k]) for k in ("x", "W1", "W2", "dy"))
-    b1 = oracle.to_f64(inp["b1"]) if w.has_bias else None
     fp8 = w.dtype == "e4m3"
+    tol = {"y": TOL[w.dtype], "h": TOL["bf16" if fp8 else w.dtype], "a": TOL[w.dtype],
+           "dH": TOL[w.dtype], "dx": TOL[w.dtype], "dW1": TOL[w.dtype], "db1": TOL[w.dtype],
+           "dW2": TOL[w.dtype]}
     if fp8:
-        # the codes the device is given, dequantised; the scales of a and dH
-        # as delayed scaling would settle on them (from the plain block's amaxes)
-        def deq(v, fmt):
-            amax = np.float32(np.max(np.abs(v)))
-            s = np.float32(np.float32(oracle.FMAX[fmt]) / amax)
-            return oracle.dequantize(oracle.quantize(v, fmt, s), fmt, np.float32(1.0) / s)
-        x, W1, W2 = deq(x, "e4m3"), deq(W1, "e4m3"), deq(W2, "e4m3")
-        dy = deq(dy, "e5m2")
+        tol.pop("dH")  # E5M2 codes: checked through dx, dW1 and db1 (one code step exceeds 6e-2)
+
+    def inputs(n):
+        inp = synth.make_rank_inputs(w, tokens=n)
+        x, W1, W2, dy = (oracle.to_f64(inp[k]) for k in ("x", "W1", "W2", "dy"))
+        b1 = oracle.to_f64(inp["b1"]) if w.has_bias else None
+        if fp8:
+            # the codes the device is given (per-tensor current scaling), dequantised
+            def deq(v, fmt):
+                _, s, s_inv = oracle.current_scale(v, fmt)
+                return oracle.dequantize(oracle.quantize(v, fmt, s), fmt, s_inv)
+            x, W1, W2 = deq(x, "e4m3"), deq(W1, "e4m3"), deq(W2, "e4m3")
+            dy = deq(dy, "e5m2")
+        return x, W1, b1, W2, dy
+
+    parity = None
+    times = []
+    if gpu is not None:
+        full = inputs(w.tokens)
+        t0 = time.perf_counter()
+        ref = _mlp_oracle(w, calls, *full, fp8, gpu.get("a_scale"), gpu.get("dH_scale"))
+        dt_full = time.perf_counter() - t0
+        parity = parity_report(gpu, ref, tol)
+        ref = full = None
+        if tokens == w.tokens:
+            times.append(dt_full)  # the whole shard is also the timed sample
+    if tokens <= 0:
+        return None, parity
+    x, W1, b1, W2, dy = inputs(tokens)
+    a_scale = dH_scale = None
+    if fp8:
+        # the scales of a and dH as delayed scaling would settle on them
         f0 = oracle.rank_forward(x, W1, b1, W2, w.act)
         a_scale = np.float32(448.0 / np.max(np.abs(f0["a"])))
         dH_scale = np.float32(57344.0 / np.max(np.abs(
             oracle.rank_dgrad(dy, W1, W2, f0["h"], w.act)["dH"]))) if "dgrad" in calls else None
         del f0
-    times = []
-    for _ in range(repeats):
+    while len(times) < repeats:
         t0 = time.perf_counter()
-        if fp8:
-            f = oracle.rank_forward_fp8(x, W1, b1, W2, a_scale)
-            if "dgrad" in calls:
-                g = oracle.rank_dgrad_fp8(dy, W1, W2, f["h"], dH_scale)
-                if "wgrad" in calls:
-                    oracle.rank_wgrad_fp8(dy, x, f["a_q"], g["dH_q"])
-        else:
-            f = oracle.rank_forward(x, W1, b1, W2, w.act)
-            if "dgrad" in calls:
-                g = oracle.rank_dgrad(dy, W1, W2, f["h"], w.act)
-                if "wgrad" in calls:
-                    oracle.rank_wgrad(dy, x, f["a"], g["dH"], w.has_bias)
+        _mlp_oracle(w, calls, x, W1, b1, W2, dy, fp8, a_scale, dH_scale)
         times.append(time.perf_counter() - t0)
-        f = g = None
     dt = sorted(times)[len(times) // 2]
     flops = w.flops(tokens=tokens, calls=calls)
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{'+'.join(calls)} of the first {tokens} of {w.tokens} tokens of the "
-                      f"{w.name} shard in fp64 NumPy, median of {repeats} runs "
-                      f"({flops / 1e12:.3f} TFLOP per run, {dt:.2f} s, {sum(times):.1f} s total)"}
+    res = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+           "kind": "oracle",
+           "sample": f"{'+'.join(calls)} of the first {tokens} of {w.tokens} tokens of the "
+                     f"{w.name} shard in fp64 NumPy, median of {repeats} runs "
+                     f"({flops / 1e12:.3f} TFLOP per run, {dt:.2f} s, {sum(times):.1f} s total)"}
+    return res, parity
 
 
-def attn_cpu_baseline(w, tokens: int, repeats: int = 3) -> dict:
+def _attn_oracle(x, W, b, Wo, dy, ctx, dqkv) -> dict:
+    from oracle import attention as oa
+    dWqkv, dbqkv = oa.qkv_wgrad(dqkv, x, has_bias=b is not None)
+    return {"qkv": oa.qkv_forward(x, W, b), "y": oa.out_forward(ctx, Wo),
+            "dctx": oa.out_dgrad(dy, Wo), "dWo": oa.out_wgrad(dy, ctx),
+            "dx": oa.qkv_dgrad(dqkv, W), "dWqkv": dWqkv, "dbqkv": dbqkv}
+
+
+def attn_cpu_baseline(w, tokens: int, repeats: int = 3, gpu=None) -> dict:
     """The CPU oracle's per-rank attention projections (fp64 NumPy, as it
-    stands) on the first `tokens` tokens: the six products of a step."""
+    stands) on the first `tokens` tokens: the six products of a step. With
+    `gpu`, also compared on the whole shard with the device's parity step."""
     import oracle
     import synth
-    from oracle import attention as oa
     cores = _cpu_cores()
-    inp = synth.make_attn_inputs(w, tokens=tokens)
-    x, W, Wo, dy, ctx, dqkv = (oracle.to_f64(inp[k]) for k in ("x", "Wqkv", "Wo", "dy", "ctx", "dqkv"))
-    b = oracle.to_f64(inp["bqkv"]) if inp["bqkv"] is not None else None
-    times = []
-    for _ in range(repeats):
+
+    def inputs(n):
+        inp = synth.make_attn_inputs(w, tokens=n)
+        x, W, Wo, dy, ctx, dqkv = (oracle.to_f64(inp[k])
+                                   for k in ("x", "Wqkv", "Wo", "dy", "ctx", "dqkv"))
+        b = oracle.to_f64(inp["bqkv"]) if inp["bqkv"] is not None else None
+        return x, W, b, Wo, dy, ctx, dqkv
+
+    parity, times = None, []
+    if gpu is not None:
+        full = inputs(w.tokens)
         t0 = time.perf_counter()
-        oa.qkv_forward(x, W, b)
-        oa.out_forward(ctx, Wo)
-        oa.out_dgrad(dy, Wo)
-        oa.out_wgrad(dy, ctx)
-        oa.qkv_dgrad(dqkv, W)
-        oa.qkv_wgrad(dqkv, x, has_bias=b is not None)
+        ref = _attn_oracle(*full)
+        dt_full = time.perf_counter() - t0
+        parity = parity_report(gpu, ref, {k: TOL[w.dtype] for k in ref})
+        ref = full = None
+        if tokens == w.tokens:
+            times.append(dt_full)
+    if tokens <= 0:
+        return None, parity
+    args = inputs(tokens)
+    while len(times) < repeats:
+        t0 = time.perf_counter()
+        _attn_oracle(*args)
         times.append(time.perf_counter() - t0)
     dt = sorted(times)[len(times) // 2]
     flops = w.flops(tokens=tokens)
@@ -254,7 +352,65 @@ def attn_cpu_baseline(w, tokens: int, repeats: int = 3) -> dict:
             "kind": "oracle",
             "sample": f"the six projection products of the first {tokens} of {w.tokens} tokens of "
                       f"the {w.name} shard in fp64 NumPy, median of {repeats} runs "
-                      f"({flops / 1e12:.3f} TFLOP per run, {dt:.2f} s, {sum(times):.1f} s total)"}
+                      f"({flops / 1e12:.3f} TFLOP per run, {dt:.2f} s, {sum(times):.1f} s total)"}, parity
+
+
+class ClockSampler:
+    """The GPU's graphics clock, sampled every `period` seconds on a thread
+    while the timed steps run (amdsmi, the device matched to cuda:0 by its
+    PCI address). `mhz()` gives the median of the samples, or None when
+    amdsmi is unavailable or gave fewer than three."""
+
+    def __init__(self, torch, period: float = 0.002):
+        import threading
+        self.period, self.samples, self.h, self.amdsmi = period, [], None, None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            p = torch.cuda.get_device_properties(0)
+            want = (int(getattr(p, "pci_domain_id", 0)), int(p.pci_bus_id), int(p.pci_device_id))
+            for h in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # dddd:bb:dd.f (hex)
+                dom, bus, rest = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self.h = h
+            self.amdsmi = amdsmi
+            if self.h is not None:
+                self._read()
+        except Exception as exc:  # no amdsmi, no access, or no match: no clock figure
+            print(f"clock sampling unavailable: {exc!r}", file=sys.stderr)
+            self.h = None
+
+    def _read(self) -> float:
+        info = self.amdsmi.amdsmi_get_clock_info(self.h, self.amdsmi.AmdSmiClkType.GFX)
+        return float(info["clk"])
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception:
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        if self.h is not None:
+            import threading
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+
+    def mhz(self):
+        if len(self.samples) < 3:
+            return None
+        import statistics
+        return statistics.median(self.samples)
 
 
 class Job:
@@ -318,10 +474,45 @@ def mlp_job(tp, torch, w, calls, dev) -> Job:
                            buf["dW2"], accumulate=True, fp8=sc["wgrad"], workspace=ws["wgrad"],
                            stream=stream)
 
+    fns = {"fwd": fwd, "dgrad": dgrad, "wgrad": wgrad}
+
+    def parity_step() -> dict:
+        """One step on zeroed gradient buffers (accumulating into zeros is
+        the plain result), in the timed steps' launch configuration; the
+        outputs on the host (FP8 codes of a dequantised, with the scales a
+        and dH were quantised at)."""
+        import numpy as np
+        for k in ("dW1", "db1", "dW2"):
+            if buf[k] is not None:
+                buf[k].zero_()
+        extra = {}
+        if fp8:
+            extra = {"a_scale": np.float32(a_hist.scale.item()),
+                     "dH_scale": np.float32(dH_hist.scale.item())}
+        for c in calls:
+            fns[c]()
+        torch.cuda.synchronize()
+        host = lambda t: t.float().cpu().numpy()
+        out = {"y": host(buf["y"]), "h": host(buf["h"])}
+        if fp8:
+            out["a"] = (buf["a"].view(torch.float8_e4m3fn).float().cpu().numpy().astype(np.float64)
+                        * float(a_hist.scale_inv.item()))
+        else:
+            out["a"] = host(buf["a"])
+        if "dgrad" in calls:
+            out["dx"] = host(buf["dx"])
+            if not fp8:
+                out["dH"] = host(buf["dH"])
+            if "wgrad" in calls:
+                out.update(dW1=host(buf["dW1"]), dW2=host(buf["dW2"]),
+                           db1=None if buf["db1"] is None else host(buf["db1"]))
+        out.update(extra)
+        return out
+
     what = "fwd+bwd" if calls == ("fwd", "dgrad", "wgrad") else "+".join(calls)
     return Job(
         name=w.name, dtype=w.dtype, stream=stream,
-        fns=[(c, {"fwd": fwd, "dgrad": dgrad, "wgrad": wgrad}[c]) for c in calls],
+        fns=[(c, fns[c]) for c in calls], parity_step=parity_step,
         labels=step_labels(w, calls), flops=w.flops(calls=calls),
         # fc1's GEMMs have T*H*G*Fs multiply-adds each, fc2's T*H*Fs
         gemm_flops=lambda lab: 2.0 * T * H * Fs * (G if lab.startswith("fc1") else 1),
@@ -329,7 +520,7 @@ def mlp_job(tp, torch, w, calls, dev) -> Job:
         config={"workload": w.name, "tokens": T, "batch": w.batch, "seq_len": w.seq,
                 "hidden": H, "ffn": w.ffn, "tp": w.tp, "ffn_shard": Fs, "act": w.act,
                 "parallelism": "one TP rank's shard on one GPU"},
-        cpu=lambda n: cpu_baseline(w, calls, n))
+        cpu=lambda n, gpu: cpu_baseline(w, calls, n, gpu=gpu))
 
 
 def attn_job(tp, torch, w, dev) -> Job:
@@ -367,6 +558,17 @@ def attn_job(tp, torch, w, dev) -> Job:
         tp.tpmlp_attn_qkv_bwd_wgrad(desc, d["dqkv"], d["x"], buf["dWqkv"], buf["dbqkv"], True,
                                     ws, stream=stream)
 
+    def parity_step() -> dict:
+        for k in ("dWo", "dWqkv", "dbqkv"):
+            if buf[k] is not None:
+                buf[k].zero_()
+        fwd()
+        bwd()
+        torch.cuda.synchronize()
+        return {k: (None if v is None else v.float().cpu().numpy()) for k, v in
+                (("qkv", buf["qkv"]), ("y", buf["y"]), ("dctx", buf["dctx"]), ("dWo", buf["dWo"]),
+                 ("dx", buf["dx"]), ("dWqkv", buf["dWqkv"]), ("dbqkv", buf["dbqkv"]))}
+
     sfx = "." + w.dtype
     labels = [k + sfx for k in ("qkv_fwd", "out_fwd", "out_dgrad", "out_wgrad", "qkv_dgrad",
                                 "qkv_wgrad")]
@@ -374,6 +576,7 @@ def attn_job(tp, torch, w, dev) -> Job:
         labels.append("dbqkv_reduce" + sfx)
     return Job(
         name=w.name, dtype=w.dtype, stream=stream, fns=[("fwd", fwd), ("bwd", bwd)],
+        parity_step=parity_step,
         labels=labels, flops=w.flops(),
         gemm_flops=lambda lab: 2.0 * T * H * (N if lab.startswith("qkv") else D),
         metric=f"TFLOP/s per-rank TP attention projections fwd+bwd ({w.dtype}) and % of MFMA "
@@ -382,7 +585,7 @@ def attn_job(tp, torch, w, dev) -> Job:
                 "hidden": H, "heads": w.heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
                 "tp": w.tp, "qkv_shard": N, "ctx_shard": D,
                 "parallelism": "one TP rank's shard on one GPU"},
-        cpu=lambda n: attn_cpu_baseline(w, n))
+        cpu=lambda n, gpu: attn_cpu_baseline(w, n, gpu=gpu))
 
 
 def moe_labels(w) -> list:
@@ -431,8 +634,18 @@ def moe_job(tp, torch, w, dev) -> Job:
         tp.tpmlp_moe_bwd_wgrad(desc, c, d["dy"], d["x"], buf["a"], buf["dH"], buf["dW1"],
                                buf["db1"], buf["dW2"], True, ws, stream=stream)
 
+    def parity_step() -> dict:
+        for k in ("dW1", "db1", "dW2"):
+            if buf[k] is not None:
+                buf[k].zero_()
+        fwd()
+        dgrad()
+        wgrad()
+        torch.cuda.synchronize()
+        return {k: (None if v is None else v.float().cpu().numpy()) for k, v in buf.items()}
+
     return Job(
-        name=w.name, dtype=w.dtype, stream=stream,
+        name=w.name, dtype=w.dtype, stream=stream, parity_step=parity_step,
         fns=[("fwd", fwd), ("dgrad", dgrad), ("wgrad", wgrad)], labels=moe_labels(w),
         flops=w.flops(T),
         gemm_flops=lambda lab: 2.0 * T * H * Fs * (G if lab.startswith("moe_fc1") else 1),
@@ -443,16 +656,25 @@ def moe_job(tp, torch, w, dev) -> Job:
                 "rows_per_expert_min": int(np.min(counts)),
                 "rows_per_expert_max": int(np.max(counts)),
                 "parallelism": "one rank's local experts on one GPU"},
-        cpu=lambda nt: moe_cpu_baseline(w, counts, nt))
+        cpu=lambda nt, gpu: moe_cpu_baseline(w, counts, nt, gpu=gpu))
 
 
-def moe_cpu_baseline(w, counts, rows: int, repeats: int = 3) -> dict:
+def _moe_oracle(x, dy, W1, b1, W2, counts, act, has_bias) -> dict:
+    from oracle import moe as om
+    f = om.grouped_forward(x, counts, W1, b1, W2, act)
+    g = om.grouped_dgrad(dy, counts, W1, W2, f["h"], act)
+    wg = om.grouped_wgrad(dy, x, f["a"], g["dH"], counts, has_bias)
+    return {**f, **g, **wg}
+
+
+def moe_cpu_baseline(w, counts, rows: int, repeats: int = 3, gpu=None) -> dict:
     """The CPU oracle's grouped block (fp64 NumPy, as it stands) on the
-    first `rows` routed rows (the leading experts' groups, the last one cut)."""
+    first `rows` routed rows (the leading experts' groups, the last one cut).
+    With `gpu`, also compared on every routed row with the device's parity
+    step."""
     import numpy as np
     import oracle
     import synth
-    from oracle import moe as om
     cores = _cpu_cores()
     cum = np.cumsum(counts)
     sub = [int(min(c, max(rows - (s - c), 0))) for c, s in zip(counts, cum)]
@@ -460,15 +682,25 @@ def moe_cpu_baseline(w, counts, rows: int, repeats: int = 3) -> dict:
     sub = sub[:k]  # the experts the sample reaches
     inp = synth.make_moe_inputs(w, counts)
     n = sum(sub)
+    parity, times = None, []
+    if gpu is not None:
+        full = (oracle.to_f64(inp["x"]), oracle.to_f64(inp["dy"]), oracle.to_f64(inp["W1"]),
+                oracle.to_f64(inp["b1"]) if w.has_bias else None, oracle.to_f64(inp["W2"]))
+        t0 = time.perf_counter()
+        ref = _moe_oracle(*full, counts, w.act, w.has_bias)
+        dt_full = time.perf_counter() - t0
+        parity = parity_report(gpu, ref, {k2: TOL[w.dtype] for k2 in ref})
+        ref = full = None
+        if n == int(np.sum(counts)):
+            times.append(dt_full)
+    if rows <= 0:
+        return None, parity
     x, dy = oracle.to_f64(inp["x"][:n]), oracle.to_f64(inp["dy"][:n])
     W1, W2 = oracle.to_f64(inp["W1"][:k]), oracle.to_f64(inp["W2"][:k])
     b1 = oracle.to_f64(inp["b1"][:k]) if w.has_bias else None
-    times = []
-    for _ in range(repeats):
+    while len(times) < repeats:
         t0 = time.perf_counter()
-        f = om.grouped_forward(x, sub, W1, b1, W2, w.act)
-        g = om.grouped_dgrad(dy, sub, W1, W2, f["h"], w.act)
-        om.grouped_wgrad(dy, x, f["a"], g["dH"], sub, w.has_bias)
+        _moe_oracle(x, dy, W1, b1, W2, sub, w.act, w.has_bias)
         times.append(time.perf_counter() - t0)
     dt = sorted(times)[len(times) // 2]
     flops = w.flops(n)
@@ -477,7 +709,7 @@ def moe_cpu_baseline(w, counts, rows: int, repeats: int = 3) -> dict:
             "sample": f"fwd+dgrad+wgrad of the first {n} of {int(np.sum(counts))} routed rows "
                       f"(experts 0..{k - 1}) of the {w.name} layer in fp64 NumPy, median of "
                       f"{repeats} runs "
-                      f"({flops / 1e12:.3f} TFLOP per run, {dt:.2f} s, {sum(times):.1f} s total)"}
+                      f"({flops / 1e12:.3f} TFLOP per run, {dt:.2f} s, {sum(times):.1f} s total)"}, parity
 
 
 def main():
@@ -494,7 +726,8 @@ def main():
     ap.add_argument("--dtype", default=None, choices=["f32", "bf16", "e4m3"],
                     help="override the workload's dtype")
     ap.add_argument("--cpu-tokens", type=int, default=8192,
-                    help="tokens in the CPU oracle sample (0: skip)")
+                    help="tokens in the CPU oracle's timed sample (0: no cpu_baseline; the "
+                         "parity check on the whole workload runs either way)")
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
     ap.add_argument("--cold", action="store_true",
                     help="also time the steps with caches flushed before each (a 512 MiB buffer "
@@ -579,6 +812,15 @@ def main():
         job = mlp_job(tp, torch, w, calls, dev)
     stream = job.stream
 
+    # parity first: one step in the timed steps' launch configuration, compared
+    # with the oracle on the whole workload; no number is reported without it
+    gpu_out = job.parity_step()
+    baseline, parity = job.cpu(args.cpu_tokens, gpu_out)
+    gpu_out = None
+    if not parity["pass"]:
+        print(json.dumps({"parity_failed": parity, "workload": job.name}), file=sys.stderr)
+        sys.exit(3)
+
     def step(ev=None):
         # ev: events recorded on the launch stream before the first call and
         # after each call (they add no work to the step)
@@ -627,13 +869,16 @@ def main():
 
     # timed region: live events around the dominant kernel only
     tp.timing_enable(True, dominant)
+    clock = ClockSampler(torch)
     torch.cuda.synchronize()
     ev = new_events()
+    clock.start()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(ev[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    clock.stop()
     dom = tp.timing_collect()[dominant]
     tp.timing_enable(False)
     spans = span_stats(ev)
@@ -655,6 +900,9 @@ def main():
     dom_ms = dom[1] / dom[0]
     achieved = job.gemm_flops(dominant) / (dom_ms * 1e-3) / 1e12
     peak = PEAK[job.dtype]
+    mhz = clock.mhz()
+    # the peak at the clock the GPU ran at during the timed steps
+    peak_at_clock = None if mhz is None else N_CU * FLOP_PER_CU_CLK[job.dtype] * mhz * 1e-6
     line = {
         "metric": job.metric,
         "value": round(value, 2),
@@ -670,19 +918,24 @@ def main():
         "data": "synthetic (seeded PCG64 normals; per-rank shard shapes)",
         "config": job.config,
         "pct_of_peak": round(100 * value / peak, 2),
+        "clock_mhz": None if mhz is None else round(mhz, 1),
+        "pct_of_peak_at_clock": None if mhz is None else round(100 * value / peak_at_clock, 2),
+        "parity": parity,
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "frac_at_clock": None if mhz is None else round(achieved / peak_at_clock, 4),
                      "traffic": measured_traffic(job.name, dominant),
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
-                                     "copy-calibrated)",
+                     "traffic_unit": "L2-to-fabric bytes per launch (rocprofv3 FETCH_SIZE + "
+                                     "WRITE_SIZE, copy-calibrated; Infinity Cache hits count "
+                                     "as fetched)",
                      "launches": dom[0], "avg_ms": round(dom_ms, 4)},
         "kernel_ms": breakdown,
         "spans": spans,
     }
     if cold is not None:
         line["spans_cold"] = cold
-    if args.cpu_tokens > 0:
-        line["cpu_baseline"] = job.cpu(args.cpu_tokens)
+    if baseline is not None:
+        line["cpu_baseline"] = baseline
     print(json.dumps(line), flush=True)
 
 

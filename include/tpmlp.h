@@ -42,7 +42,8 @@
  *                b1, h_saved, y_partial, dx_partial: bfloat16. dW1, db1,
  *                dW2: float32. The block quantises the two tensors it
  *                produces and reuses: a (E4M3, forward) with current scaling
- *                (scale = 448 / amax(a), amax 0 -> scale 1) or delayed
+ *                (scale = 448 / amax(a); 1 when amax is 0 or the quotient
+ *                overflows) or delayed
  *                scaling (tpmlp_fp8_history), and dH (E5M2, dgrad) with
  *                delayed scaling. Codes saturate at the largest finite value
  *                (448, 57344) and are rounded to nearest even.
@@ -108,9 +109,10 @@ typedef struct tpmlp_desc {
  * oldest entry dropping out; *scale_inv = 1 / (the factor the call used),
  * which is what consumers of the codes dequantise with; and *scale =
  * fmax / max(history) for the next call (fmax 448 for E4M3, 57344 for E5M2),
- * unchanged while that maximum is 0 or not finite. All float32. The amax is
- * taken over the tensor's float32 values before scaling (NaN elements, which
- * finite inputs do not produce, are left out). A call with no tokens still
+ * unchanged while that maximum is 0 or not finite, or so small that the
+ * quotient overflows float32. All float32. The amax is taken over the
+ * tensor's float32 values before scaling (NaN elements, which finite inputs
+ * do not produce, are left out). A call with no tokens still
  * updates the state, with an amax of 0. Calls that share one state must be
  * ordered on one stream.
  */
@@ -211,7 +213,8 @@ tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* desc, const void* dy, const void*
 /*
  * Per-tensor current-scaling quantiser (the FP8 recipe used for `a` inside
  * tpmlp_fwd, exported so callers can produce E4M3 inputs on the device):
- *   amax = max |src|; scale = 448 / amax in float32 (1 if amax is 0);
+ *   amax = max |src|; scale = 448 / amax in float32 (1 if amax is 0, or so
+ *   small that 448 / amax overflows float32: below about 1.3e-36);
  *   dst[i] = E4M3(clamp(fl32(src[i] * scale), -448, 448)), round to nearest even;
  *   *amax_out = amax; *scale_inv_out = 1 / scale in float32.
  * src_dtype is TPMLP_F32 or TPMLP_BF16; n >= 0 elements; dst n bytes.

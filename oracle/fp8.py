@@ -13,7 +13,8 @@ Limits"; concept note, "Key math / How it works"; the onegen.ai overview,
 * Rounding: round to nearest, ties to even; values beyond 448 in magnitude
   saturate to +-448 (the specification's saturating conversion mode).
 * Scaling: per-tensor current scaling. amax = max |v| over the tensor;
-  scale = 448 / amax computed in float32 (amax = 0 gives scale 1);
+  scale = 448 / amax computed in float32 (amax = 0, or an amax so small
+  that the quotient overflows float32, gives scale 1);
   scale_inv = 1 / scale in float32; code = E4M3(fl32(v * scale));
   the dequantised value is decode(code) * scale_inv.
 
@@ -31,7 +32,7 @@ Limits"; concept note, "Key math / How it works"; the onegen.ai overview,
   before the first code is written. After the call the tensor's own amax
   enters a history (newest first, oldest dropped) and the next scale is
   fmax / max(history), kept unchanged while that maximum is 0 or not
-  finite.
+  finite, or so small that the factor would overflow float32.
 
 The float32 steps (division, reciprocal, product) are taken in float32 on
 purpose: the quantised code is an integer decided by floating point, so both
@@ -93,14 +94,21 @@ def e4m3_encode(v) -> np.ndarray:
     return code.astype(np.uint8)
 
 
-def current_scale(v):
-    """(amax, scale, scale_inv) of a tensor as float32 scalars."""
+def current_scale(v, fmt: str = "e4m3"):
+    """(amax, scale, scale_inv) of a tensor as float32 scalars.
+
+    scale = fmax / amax in float32. An amax of 0 or a non-finite amax gives
+    1, and so does an amax so small that fmax / amax overflows float32 (below
+    about 1.3e-36 for E4M3): a factor of infinity would turn zeros into NaN
+    (0 * inf) and make scale_inv 0."""
     v32 = np.asarray(v, dtype=np.float32)
     amax = np.float32(np.max(np.abs(v32))) if v32.size else np.float32(0.0)
-    if amax == 0.0 or not np.isfinite(amax):
-        scale = np.float32(1.0)
-    else:
-        scale = np.float32(np.float32(E4M3_MAX) / amax)
+    scale = np.float32(1.0)
+    if amax > 0.0 and np.isfinite(amax):
+        with np.errstate(over="ignore"):
+            s = np.float32(np.float32(FMAX[fmt]) / amax)
+        if np.isfinite(s):
+            scale = s
     scale_inv = np.float32(np.float32(1.0) / scale)
     return amax, scale, scale_inv
 
@@ -194,8 +202,10 @@ def delayed_update(history, amax, scale, fmt: str):
     new_h = np.concatenate([np.array([amax], dtype=np.float32), h[:-1]]) if h.size else h
     scale = np.float32(scale)
     m = np.float32(np.max(new_h)) if new_h.size else np.float32(0.0)
+    new_scale = scale
     if m > 0.0 and np.isfinite(m):
-        new_scale = np.float32(np.float32(FMAX[fmt]) / m)
-    else:
-        new_scale = scale
+        with np.errstate(over="ignore"):
+            s = np.float32(np.float32(FMAX[fmt]) / m)
+        if np.isfinite(s):   # a maximum so small that the factor overflows keeps it too
+            new_scale = s
     return new_h, new_scale, np.float32(np.float32(1.0) / scale)

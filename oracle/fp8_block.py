@@ -13,14 +13,16 @@ the call is given (delayed scaling, see oracle.fp8):
 * the gradient dH = dA * gelu'(h), to E5M2, before the fc1 data and weight
   gradients and the bias gradient.
 
-Everything else is float64 on those values.
+Everything else is float64 on those values: h = x W1^T + b1 is kept
+exact and the activation, forward and backward, is taken of it (the plain
+block's reading, with no storage rounding). The device stores h in bfloat16
+and applies the activation to that stored value; the GPU tests bound the
+effect of that rounding on each code they check rather than copying it here.
+The value handed to the quantiser is fl32(fl32(v) * scale), which is the
+scaling recipe's own definition (see oracle.fp8).
 
-Where the device's rounding decides a code, the oracle takes the same
-steps, so that both sides decide in the same precision (the pages fix none):
-fc1's output h leaves the block as bfloat16 (its storage type at the
-boundary), and the activation, forward and backward, is taken of h as
-stored: a = gelu(bf16(h)), dH = dA * gelu'(bf16(h)). The value handed to
-the quantiser is then rounded to float32 once, as the device's is.
+``round_bf16`` (float32 to bfloat16, round to nearest even) is a format
+utility for the tests' validity windows; no result of the block uses it.
 """
 from __future__ import annotations
 
@@ -44,23 +46,22 @@ def round_bf16(v) -> np.ndarray:
 
 
 def rank_forward_fp8(x, W1, b1, W2, a_scale) -> dict:
-    """h = x W1^T + b1, stored as bf16; a = gelu(h as stored); a quantised
-    to E4M3 at a_scale (codes, and a_q = decode(code) / a_scale);
-    y = a_q W2^T. amax = max |a|. Returns h as stored (bf16 values) and,
-    as h_exact, before that rounding."""
-    h_exact = x @ W1.T + (0.0 if b1 is None else b1)
-    h = round_bf16(h_exact)
+    """h = x W1^T + b1; a = gelu(h); a quantised to E4M3 at a_scale (codes,
+    and a_q = decode(code) / a_scale); y = a_q W2^T. amax = max |a|. All
+    float64 except the quantiser's float32 product. "h_exact" is the same
+    array as "h" (the name the tests bound the device's stored h against)."""
+    h = x @ W1.T + (0.0 if b1 is None else b1)
     a = gelu_tanh(h)
     codes = quantize(a, "e4m3", a_scale)
     a_q = dequantize(codes, "e4m3", _inv(a_scale))
     y = a_q @ W2.T
     amax = float(np.max(np.abs(a))) if a.size else 0.0
-    return {"h_exact": h_exact, "h": h, "a": a, "a_codes": codes, "a_q": a_q, "y": y,
+    return {"h_exact": h, "h": h, "a": a, "a_codes": codes, "a_q": a_q, "y": y,
             "amax": amax}
 
 
 def rank_dgrad_fp8(dy, W1, W2, h, dH_scale) -> dict:
-    """dA = dy W2; dH = dA * gelu'(h), h as the forward stored it (bf16);
+    """dA = dy W2; dH = dA * gelu'(h) (h as given: the forward's exact h);
     dH quantised to E5M2 at dH_scale (codes, and dH_q); dx = dH_q W1.
     amax = max |dH|."""
     dA = dy @ W2

@@ -110,12 +110,10 @@ constexpr int kSmemBytes = kStages * kStageBytes;  // 128 KiB
 // and the main loop runs two stages per iteration, so the per-lane read
 // addresses stay the same from stage to stage.
 constexpr int kTileB0 = kStages * kTileBytes;      // first B tile
-// A stage's buffer parity: IC<0>/IC<1> where the loop knows it at compile
-// time (then the buffer's offset goes into the reads' offset field), or an int.
+// A stage's buffer parity is a compile-time IC<0>/IC<1>: the buffer's offset
+// goes into the reads' offset field.
 template <typename P>
-struct ParityOffset {
-  static constexpr int value = 0;  // runtime parity: added to the address
-};
+struct ParityOffset;
 template <int P>
 struct ParityOffset<std::integral_constant<int, P>> {
   static constexpr int value = P * kTileBytes;
@@ -775,6 +773,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   const int m0 = bm * kBM;
   const int n0 = bn * (kPair ? kBN / 2 : kBN);
   if constexpr (GROUP != GROUP_NONE) nk = (g.K + kStep - 1) / kStep;
+  // The main loop runs stages in pairs. An odd count is padded at the front:
+  // loop stage 0 is then a stage of zeros written to LDS by the prologue
+  // (no loads), and loop stage j holds K stage kt0 + j - pad.
+  const int pad = nk & 1;
+  const int kbase = kt0 - pad;  // K stage of loop stage 0
 
   // ---- operand A loader
   KMajorLoader<false> la{};
@@ -858,11 +861,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     char* sa = smem + (kt & (kStages - 1)) * kTileBytes;
     char* sb = smem + kTileB0 + (kt & (kStages - 1)) * kTileBytes;
     if (j < 8) {
-      if constexpr (A_K) la.template issue_one<fast>(sa, wave, (uint32_t)((kt0 + kt) * kRowBytes), j);
-      else lma.issue_one(sa, wave, (kt0 + kt) * kStep, j);
+      if constexpr (A_K) la.template issue_one<fast>(sa, wave, (uint32_t)((kbase + kt) * kRowBytes), j);
+      else lma.issue_one(sa, wave, (kbase + kt) * kStep, j);
     } else {
-      if constexpr (B_K) lb.template issue_one<fast>(sb, wave, (uint32_t)((kt0 + kt) * kRowBytes), j - 8);
-      else lmb.issue_one(sb, wave, (kt0 + kt) * kStep, j - 8);
+      if constexpr (B_K) lb.template issue_one<fast>(sb, wave, (uint32_t)((kbase + kt) * kRowBytes), j - 8);
+      else lmb.issue_one(sb, wave, (kbase + kt) * kStep, j - 8);
     }
   };
   auto issue = [&](int kt) __attribute__((always_inline)) {
@@ -890,7 +893,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // stage index congruent to bn modulo tiles_n) and written to partial row
   // split * tiles_n + bn.
   const bool do_colsum = COLSUM && (e.colsum != nullptr);
-  int cs_next = ((bn - kt0) % g.tiles_n + g.tiles_n) % g.tiles_n;  // next (local) stage summed
+  // next loop stage summed (K stages kt0 + local; the front pad shifts them)
+  int cs_next = ((bn - kt0) % g.tiles_n + g.tiles_n) % g.tiles_n + pad;
   const int cs_row = split * g.tiles_n + bn;
   constexpr int kCs = IS_FP8 ? 16 : 8;  // columns per thread
   float csum[kCs];
@@ -909,11 +913,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // are compile-time constants: they select registers and offsets)
   auto read_one = [&](auto PAR, auto KS, auto J) __attribute__((always_inline)) {
     constexpr int ks = decltype(KS)::value, j = decltype(J)::value, f = j % kFr;
-    constexpr int po = ParityOffset<decltype(PAR)>::value;  // compile-time stage offset
-    int pr = 0;                                            // runtime stage offset
-    if constexpr (std::is_same<decltype(PAR), int>::value) pr = PAR * kTileBytes;
-    const char* ta = smem + pr;            // A tiles
-    const char* tb = smem + kTileB0 + pr;  // B tiles
+    constexpr int po = ParityOffset<decltype(PAR)>::value;  // the stage buffer's offset
+    const char* ta = smem;            // A tiles
+    const char* tb = smem + kTileB0;  // B tiles
     if constexpr (j < kFr) {
       if constexpr (IS_FP8 && A_K) fa[ks][f] = frag_k_e4m3<po, ks, f>(ta, 128 * wm, lane);
       else if constexpr (IS_FP8) fa[ks][f] = frag_mn_fp8<po, ks>(ta, 128 * wm + 32 * f, lane);
@@ -928,8 +930,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   };
   // the parity of the stage after one of parity P
   auto next_parity = [](auto P) __attribute__((always_inline)) {
-    if constexpr (std::is_same<decltype(P), int>::value) return P ^ 1;
-    else return IC<1 - decltype(P)::value>{};
+    return IC<1 - decltype(P)::value>{};
   };
 
 
@@ -991,10 +992,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
       }
     }
   };
-  // Every stage index is issued, also those past the end of K: their offsets
-  // fall outside the resources, so they cost no memory traffic and load
-  // zeros (which also makes the fused column sum of those stages zero), and
-  // the number of loads in flight stays uniform: one wait count, no branches.
+  // Every stage's loads are issued, also those of the two stages past the end
+  // of the loop (into buffers no MFMA and no column sum reads): the number of
+  // loads in flight stays uniform, one wait count and no branches. Their
+  // offsets fall outside the resources (no memory traffic), except for
+  // folded K-major loaders, which read whatever lies behind the rows.
   //
   // FP8 stage kt with two K-major operands (32 MFMAs of 32x32x64 issued from
   // registers, two k-steps; a scheduling barrier after every slot pins the
@@ -1171,8 +1173,20 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     });
   };
 
-  // prologue: stages 0 and 1 in flight; stage 0's first k-steps in registers
-  issue(0);
+  // prologue: stages 0 and 1 in flight; stage 0's first k-steps in registers.
+  // A front pad stage is zeros written here with LDS stores (its A and B
+  // tiles in buffer 0, 256 bytes per thread): no load of it is issued, and
+  // its MFMAs add exact zeros. The barrier's wait covers the stores.
+  if (pad) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int off = (i < 8 ? 0 : kTileB0) + ((i & 7) * kThreads + tid) * 16;
+      *reinterpret_cast<u32x4*>(smem + off) = z;
+    }
+  } else {
+    issue(0);
+  }
   issue(1);
   wait_and_barrier<16>();
   // FP8: the rolling schedule pays off where a transpose-read operand makes
@@ -1181,20 +1195,19 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   constexpr bool kRolling = !A_K || !B_K;
   // The main loop runs two stages per iteration, even ones in buffer 0 and odd
   // ones in buffer 1, so each read's stage offset is an immediate and the
-  // per-lane read addresses stay the same from stage to stage.
-  //  * Both operands MN-major (the weight gradients): always so. An odd count
-  //    of stages gets one more, whose loads fall past the k-rows of both
-  //    resources and fill the tiles with zeros.
-  //  * A K-major operand: so when K is a whole number of stages and the count
-  //    is even (every product at the benchmark shapes; split-K gives every
-  //    split but the last an even count), with folded loaders (no per-lane K
-  //    test). Otherwise one stage per iteration, with the stage's parity added
-  //    to the read addresses and the K test on every K-major load. A K-major
-  //    load whose lanes are all out of range leaves LDS unwritten, so these
-  //    products cannot pad with a stage of zeros.
+  // per-lane read addresses stay the same from stage to stage. An odd count
+  // of stages starts with the zero stage of the prologue (pad). When K is a
+  // whole number of stages (every product at the benchmark shapes; split-K
+  // gives every split whole stages), the K-major loaders are folded (no
+  // per-lane K test: the K-range test only separates rows past the tensor's
+  // end, which get an out-of-range offset once). A ragged K keeps the test on
+  // every K-major load; products with both operands MN-major need none (their
+  // resource is rebased on each stage's first k-row and ends at the tensor's
+  // last one).
   // (A conditional stage inside or after the paired loop made the compiler
-  // move the accumulators between registers; with both loop forms the column
-  // sum kernels spilled an asm read's destination before the read landed.)
+  // move the accumulators between registers; with a second loop form in the
+  // column-sum kernels it spilled an asm read's destination before the read
+  // landed: those kernels have one loop.)
   auto pair_loop = [&](auto stage, auto FAST, int n) __attribute__((always_inline)) {
     for (int kt = 0; kt < n; kt += 2) {
       stage(kt, FAST, IC<0>{});
@@ -1203,15 +1216,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   };
   auto main_loop = [&](auto stage) __attribute__((always_inline)) {
     if constexpr (!A_K && !B_K) {
-      pair_loop(stage, std::false_type{}, nk + (nk & 1));
+      pair_loop(stage, std::false_type{}, nk + pad);
     } else {
       static_assert(!COLSUM, "the fused column sum reads an MN-major A tile");
-      if ((nk & 1) == 0 && g.K % kStep == 0) {
+      if (g.K % kStep == 0) {
         if constexpr (A_K) la.fold_rows();
         if constexpr (B_K) lb.fold_rows();
-        pair_loop(stage, std::true_type{}, nk);
+        pair_loop(stage, std::true_type{}, nk + pad);
       } else {
-        for (int kt = 0; kt < nk; ++kt) stage(kt, std::false_type{}, kt & 1);
+        pair_loop(stage, std::false_type{}, nk + pad);
       }
     }
   };

@@ -1,4 +1,6 @@
 // Instantiations and launchers of the MFMA tile kernel (bf16 and e4m3).
+#include <mutex>
+
 #include "gemm_mfma.h"
 #include "launch.h"
 
@@ -10,18 +12,20 @@ template <bool IS_FP8, bool A_K, bool B_K, int EPI, bool COLSUM, int FMT = 0,
           int GROUP = GROUP_NONE>
 hipError_t launch_one(const GemmArgs& g, const EpiArgs& e, hipStream_t s, int64_t nb = -1) {
   auto* k = &gemm_mfma_kernel<IS_FP8, A_K, B_K, EPI, bf16_t, COLSUM, FMT, GROUP>;
-  // the LDS allowance is raised once per instantiation and device
-  static bool attr_set[64] = {};
+  // the LDS allowance is raised once per instantiation and device; call_once
+  // makes that safe when several host threads launch at once (its result,
+  // success or error, is kept)
+  static std::once_flag once[64];
+  static hipError_t attr_err[64];
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!attr_set[dev]) {
-    err = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
-    if (err != hipSuccess) return err;
-    attr_set[dev] = true;
-  }
+  std::call_once(once[dev], [&]() {
+    attr_err[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
+  });
+  if (attr_err[dev] != hipSuccess) return attr_err[dev];
   if (nb < 0) nb = (int64_t)g.tiles_m * g.tiles_n;
   hipLaunchKernelGGL(k, dim3((unsigned)nb), dim3(kThreads), kSmemBytes, s, g, e);
   return hipGetLastError();

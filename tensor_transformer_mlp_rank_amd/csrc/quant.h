@@ -1,6 +1,7 @@
 // Per-tensor current scaling into OCP E4M3.
 //
-//   amax = max |v|;  scale = 448 / amax (float32; 1 when amax is 0);
+//   amax = max |v|;  scale = 448 / amax (float32; 1 when amax is 0 or so
+//   small that the quotient overflows);
 //   code = E4M3(clamp(fl32(v * scale), -448, 448)), round to nearest even;
 //   scale_inv = 1 / scale (float32).
 //
@@ -81,7 +82,10 @@ __global__ void __launch_bounds__(kQuantThreads) quantize_kernel(const SrcT* src
   __syncthreads();
   float amax = 0.f;
   for (int w = 0; w < kQuantThreads / 64; ++w) amax = __builtin_fmaxf(amax, wm[w]);
-  const float scale = (amax > 0.f && amax <= 3.4028234663852886e38f) ? kFmax / amax : 1.0f;
+  // 1 for an amax of 0 or infinity, and for one so small that kFmax / amax
+  // overflows (a factor of infinity would make zeros NaN and scale_inv 0)
+  float scale = (amax > 0.f && amax <= 3.4028234663852886e38f) ? kFmax / amax : 1.0f;
+  if (!(scale <= 3.4028234663852886e38f)) scale = 1.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     *amax_out = amax;
     *scale_inv_out = 1.0f / scale;
@@ -108,8 +112,9 @@ __global__ void __launch_bounds__(kQuantThreads) quantize_kernel(const SrcT* src
 // partial[0 .. nparts): amax = their maximum; history <- [amax, history[0 ..
 // len-2]] (newest first); *scale_inv = 1 / *scale (the factor the tensor was
 // quantised with); *scale <- fmax / max(history), kept while that maximum is
-// 0 or not finite. One workgroup, all float32; max is exact, so the result
-// does not depend on the order of the partials.
+// 0 or not finite, or so small that the quotient overflows. One workgroup,
+// all float32; max is exact, so the result does not depend on the order of
+// the partials.
 constexpr int kMaxHistory = 4096;
 __global__ void __launch_bounds__(kQuantThreads) delayed_update_kernel(const float* partial,
                                                                        int nparts, float* history,
@@ -142,7 +147,10 @@ __global__ void __launch_bounds__(kQuantThreads) delayed_update_kernel(const flo
     for (int w = 0; w < kQuantThreads / 64; ++w) hmax = __builtin_fmaxf(hmax, wm[w]);
     const float used = *scale;
     *scale_inv = 1.0f / used;
-    *scale = (hmax > 0.f && hmax <= 3.4028234663852886e38f) ? fmax / hmax : used;
+    // kept while the maximum is 0 or infinite, or so small that the next
+    // factor would overflow
+    const float next = (hmax > 0.f && hmax <= 3.4028234663852886e38f) ? fmax / hmax : used;
+    *scale = (next <= 3.4028234663852886e38f) ? next : used;
   }
 }
 

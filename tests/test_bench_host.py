@@ -78,3 +78,45 @@ def test_write_traffic_maps_dispatches_to_labels(tmp_path, monkeypatch):
     with pytest.raises(SystemExit):
         bench.write_traffic("toy2", labels, 1, str(tmp_path / "f2"), str(tmp_path / "w2"),
                             str(tmp_path / "cf"), str(tmp_path / "cw"), [])
+
+
+def _small(cfg, **kw):
+    import dataclasses
+    return dataclasses.replace(synth.WORKLOADS[cfg], **kw)
+
+
+@pytest.mark.parametrize("cfg,dtype", [(2, "bf16"), (4, "bf16"), (5, "e4m3")])
+def test_parity_gate_passes_the_oracle_and_catches_a_wrong_tensor(cfg, dtype):
+    """bench.py's parity gate on a small shard: device outputs equal to the
+    oracle's (rounded to the storage types) pass; one output tensor off by
+    10% fails, naming that tensor. Host only: the 'device' outputs are made
+    here from the oracle."""
+    import numpy as np
+    import oracle
+    w = _small(cfg, tokens=64, hidden=48, ffn=synth.WORKLOADS[cfg].tp * 32)
+    calls = ("fwd", "dgrad", "wgrad")
+    inp = synth.make_rank_inputs(w)
+    f64 = {k: (None if v is None else oracle.to_f64(v)) for k, v in inp.items()}
+    fp8 = dtype == "e4m3"
+    extra = {}
+    if fp8:
+        def deq(v, fmt):
+            _, s, s_inv = oracle.current_scale(v, fmt)
+            return oracle.dequantize(oracle.quantize(v, fmt, s), fmt, s_inv)
+        for k, fmt in (("x", "e4m3"), ("W1", "e4m3"), ("W2", "e4m3"), ("dy", "e5m2")):
+            f64[k] = deq(f64[k], fmt)
+        extra = {"a_scale": np.float32(64.0), "dH_scale": np.float32(2048.0)}
+    ref = bench._mlp_oracle(w, calls, f64["x"], f64["W1"], f64["b1"], f64["W2"], f64["dy"],
+                            fp8, extra.get("a_scale"), extra.get("dH_scale"))
+    import torch
+    bf = lambda v: torch.from_numpy(np.asarray(v, np.float32)).to(torch.bfloat16).float().numpy()
+    gpu = {k: (None if v is None else (bf(v) if k in ("y", "h", "a", "dH", "dx") else
+                                      np.asarray(v, np.float32)))
+           for k, v in ref.items()}
+    gpu.update(extra)
+    base, par = bench.cpu_baseline(w, calls, 0, gpu=gpu)
+    assert base is None and par["pass"], par
+    assert set(par["max_rel_err"]) >= {"y", "dx", "dW1", "dW2"}
+    gpu["dW1"] = gpu["dW1"] * 1.1
+    _, par = bench.cpu_baseline(w, calls, 0, gpu=gpu)
+    assert not par["pass"] and par["max_rel_err"]["dW1"] > par["tol"]["dW1"]

@@ -61,14 +61,16 @@ SHAPES = [
     (64, 1040, 400),
     (1, 16, 16),
     (37, 48, 32),
-    # the main loop's forms (64-element stages): H=192 a whole but odd number
-    # of stages, Fs=80 and Fs=208 ragged with an even number, T=100 ragged and
-    # even for the weight gradients' paired loop, T=192 whole and odd (their
-    # padded stage)
+    # the main loop's forms (64-element stages, run two per iteration; an odd
+    # count starts with a zero stage): H=192 and H=320 a whole but odd number
+    # of stages (folded K-major loads after the zero stage), Fs=80 and Fs=208
+    # ragged with an even number, T=100 ragged and even for the weight
+    # gradients, T=192 whole and odd (their zero stage); (300, 528, 272)
+    # above has ragged odd counts in every product
     (100, 192, 80),
     (192, 320, 208),
     # one tile, Fs of 17 stages: fc2's forward and fc1's data gradient split K
-    # in two, 10 stages (paired loop) and 7 (one-stage loop)
+    # in two, 10 stages and 7 (with the zero stage, 8)
     (256, 256, 1088),
 ]
 
@@ -89,9 +91,9 @@ def test_block_small_and_ragged(tp, T, H, Fs, act, dtype):
 @pytest.mark.parametrize("act", ["gelu", "swiglu"])
 def test_block_more_tiles_than_workgroups(tp, act):
     """bf16 block whose GEMMs have 289 (SwiGLU fc1: 561) 256-wide tiles, more
-    than the persistent kernel's workgroups (one per CU): workgroups run
-    several tiles in a row, and every GEMM has ragged edges in M, N and K.
-    Compared element by element, with accumulation into prior gradients."""
+    than the 256 compute units: a CU runs several workgroups in turn, and
+    every GEMM has ragged edges in M, N and K. Compared element by element,
+    with accumulation into prior gradients."""
     T, H, Fs = 4200, 4208, 4112
     w = synth.WORKLOADS[4 if act == "swiglu" else 2]
     say(f"  T={T} H={H} Fs={Fs} {act}: generating inputs")
@@ -255,3 +257,22 @@ def test_full_size_sampled(tp, cfg):
     ref = sampled_reference(inp, w.act, has_bias, ROWS, cols)
     got = sample_gpu(gpu, w.act, w.ffn_shard, ROWS, cols)
     check(got, ref, w.dtype, ALL)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_full_size_every_element(tp, cfg):
+    """Full per-rank workload in the launch configuration the benchmark times
+    (the whole workspace, so split-K where planned; wgrad accumulating into
+    prior fp32 gradients): every element of y, h, a, dH, dx, dW1, db1 and dW2
+    against one oracle evaluation of the whole shard."""
+    w = synth.WORKLOADS[cfg]
+    say(f"config {cfg} {w.name}: generating inputs")
+    inp = synth.make_rank_inputs(w)
+    G, Fs, H = w.gate_mult, w.ffn_shard, w.hidden
+    prior = {"dW1": synth.grad_init(cfg, (G * Fs, H), 1),
+             "db1": synth.grad_init(cfg, (G * Fs,), 2) if w.has_bias else None,
+             "dW2": synth.grad_init(cfg, (H, Fs), 3)}
+    gpu = gpu_block(tp, inp, w.act, w.dtype, w.has_bias, accumulate_into=prior)
+    say("  oracle on the whole shard")
+    ref = oracle_block(inp, w.act, w.has_bias, prior=prior)
+    check(gpu, ref, w.dtype, ALL)
