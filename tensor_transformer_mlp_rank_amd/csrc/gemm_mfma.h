@@ -1228,25 +1228,49 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
       }
     }
   };
+  // Fragment reads are asm: the compiler takes their results as written when
+  // the read is issued, not when it lands. Outside the loop's own schedule
+  // (whose waits cover every use) two places need a fence, a wait for all LDS
+  // reads followed by an empty asm that takes every fragment register as
+  // read and rewritten, so that the compiler neither copies a fragment nor
+  // reuses its register before the data has landed:
+  //  * after the prologue's reads: where a kernel has two loop forms it may
+  //    copy the fragments into the registers one of them expects (a build
+  //    without the fence did, before the reads landed, and gave NaN);
+  //  * after the loop: the last stage's reads ahead are still in flight, and
+  //    their registers are free for the code that follows (a build without
+  //    the fence set up an epilogue address in one of them).
+  // Both places have reads of k-step 0 fragments only in flight.
+  auto frag_keep = [&](auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
+    auto& ra = fa[0][i];  // named first: an asm operand alone does not make
+    auto& rb = fb[0][i];  // the lambda capture the array
+    asm volatile("" : "+v"(ra), "+v"(rb));
+  };
+  auto frag_fence = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    static_for<kFr>(frag_keep);
+  };
   if constexpr (!IS_FP8) {
     static_for<2 * kFr>([&](auto J) { read_one(IC<0>{}, IC<0>{}, J); });
+    frag_fence();
     main_loop(stage_iter16);
   } else if constexpr (!kRolling) {
     static_for<kReadsQ>([&](auto J) {
       constexpr int j = decltype(J)::value;
       read_one(IC<0>{}, IC<j / 8>{}, IC<j & 7>{});
     });
+    frag_fence();
     main_loop(stage_iter);
   } else {
     static_for<8 * (kKs - 1)>([&](auto J) {
       constexpr int j = decltype(J)::value;
       read_one(IC<0>{}, IC<j / 8>{}, IC<j & 7>{});
     });
+    frag_fence();
     main_loop(stage_iter_rolling);
   }
-  // The last stage's transpose reads ahead (asm: the compiler does not know
-  // they are in flight) must land before their registers are reused.
-  wait_lds();
+  frag_fence();
   if constexpr (!IS_FP8) {
     // the last MFMAs (asm, unseen by the compiler's hazard checks) complete
     // before any instruction reads their accumulators
