@@ -1132,6 +1132,12 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   auto stage_iter16 = [&](int kt, auto FAST, auto PAR) __attribute__((always_inline)) {
     const auto PAR1 = next_parity(PAR);  // stage kt+1
     wait_lds();  // this stage's k-step 0 (read in slots 64..111 of the last)
+    // Two wait states before the first MFMA. The MFMAs are asm, so the
+    // compiler's hazard checks do not see their operands; where a kernel has
+    // two loop forms it may move fragments into the registers one loop
+    // expects with VALU copies just before it, and an MFMA may not read a
+    // VGPR that a VALU instruction wrote fewer than two wait states earlier.
+    asm volatile("s_nop 1");
     int cs_mode = 0;  // this stage's column sums are this workgroup's share
     u32x4 cs_buf[8];
     if constexpr (COLSUM) {
