@@ -356,14 +356,17 @@ def attn_cpu_baseline(w, tokens: int, repeats: int = 3, gpu=None) -> dict:
 
 
 class ClockSampler:
-    """The GPU's graphics clock, sampled every `period` seconds on a thread
-    while the timed steps run (amdsmi, the device matched to cuda:0 by its
-    PCI address). `mhz()` gives the median of the samples, or None when
-    amdsmi is unavailable or gave fewer than three."""
+    """The GPU's graphics clock, sampled on a thread while the timed steps
+    run: amdsmi's GPU metrics of the device matched to cuda:0 by its PCI
+    address, each sample the mean of the per-XCD current clocks. A sample
+    counts only while the metrics show the GPU busy (gfx activity of 50% or
+    more), so a reading of another, idle device or a stale one is not taken
+    for the kernels' clock. `mhz()` gives the median of the counted samples,
+    or None when amdsmi is unavailable or counted fewer than three."""
 
     def __init__(self, torch, period: float = 0.002):
         import threading
-        self.period, self.samples, self.h, self.amdsmi = period, [], None, None
+        self.period, self.samples, self.rejected, self.h, self.amdsmi = period, [], 0, None, None
         self._stop = threading.Event()
         self._thread = None
         try:
@@ -383,16 +386,25 @@ class ClockSampler:
             print(f"clock sampling unavailable: {exc!r}", file=sys.stderr)
             self.h = None
 
-    def _read(self) -> float:
-        info = self.amdsmi.amdsmi_get_clock_info(self.h, self.amdsmi.AmdSmiClkType.GFX)
-        return float(info["clk"])
+    def _read(self):
+        """(clock in MHz, gfx activity in %) from one metrics read."""
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
+        clk = sum(clks) / len(clks) if clks else m.get("current_gfxclk")
+        act = m.get("average_gfx_activity")
+        return (float(clk) if isinstance(clk, (int, float)) else None,
+                float(act) if isinstance(act, (int, float)) else None)
 
     def _run(self):
         while not self._stop.is_set():
             try:
-                self.samples.append(self._read())
+                clk, act = self._read()
             except Exception:
                 return
+            if clk is not None and act is not None and act >= 50.0:
+                self.samples.append(clk)
+            else:
+                self.rejected += 1
             self._stop.wait(self.period)
 
     def start(self):
@@ -408,6 +420,9 @@ class ClockSampler:
 
     def mhz(self):
         if len(self.samples) < 3:
+            if self.h is not None:
+                print(f"clock: {len(self.samples)} busy samples ({self.rejected} idle or "
+                      f"unreadable): no figure", file=sys.stderr)
             return None
         import statistics
         return statistics.median(self.samples)
@@ -919,6 +934,7 @@ def main():
         "config": job.config,
         "pct_of_peak": round(100 * value / peak, 2),
         "clock_mhz": None if mhz is None else round(mhz, 1),
+        "clock_samples": len(clock.samples),
         "pct_of_peak_at_clock": None if mhz is None else round(100 * value / peak_at_clock, 2),
         "parity": parity,
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
