@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 6
+#define TPMLP_ABI_VERSION 7
 
 typedef enum {
   TPMLP_OK = 0,
@@ -81,7 +81,8 @@ typedef enum {
   TPMLP_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   TPMLP_E_UNSUPPORTED = 5, /* valid but not provided (E4M3 SwiGLU, SwiGLU bias) */
   TPMLP_E_WORKSPACE = 6,   /* workspace NULL or smaller than tpmlp_workspace_size */
-  TPMLP_E_HIP = 7          /* a HIP runtime call failed while enqueuing */
+  TPMLP_E_HIP = 7,         /* a HIP runtime call failed while enqueuing */
+  TPMLP_E_SCRATCH = 8      /* too large for the fixed scratch of tpmlp_bwd_wgrad_noalloc */
 } tpmlp_status;
 
 typedef enum { TPMLP_F32 = 0, TPMLP_BF16 = 1, TPMLP_E4M3 = 2 } tpmlp_dtype;
@@ -209,6 +210,28 @@ tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* desc, const void* dy, const void*
                              const void* a_saved, const void* dH, float* dW1, float* db1,
                              float* dW2, int32_t accumulate, const tpmlp_fp8_scales* fp8,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * tpmlp_bwd_wgrad without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, results and errors as
+ * tpmlp_bwd_wgrad given only the workspace it cannot run without: the
+ * products are never split along K, so the results are bit for bit those of
+ * tpmlp_bwd_wgrad with tpmlp_workspace_size(desc, TPMLP_CALL_WGRAD) bytes
+ * whenever that size plans no split. The db1 partial sums (bias, bf16 or
+ * E4M3) go to a fixed device array of TPMLP_SCRATCH_BYTES bytes that every
+ * GPU the library runs on holds until the process ends; its address is
+ * looked up on the call's first use on a device. A problem whose partial sums
+ * need more, (ceil(H / 256) * G * Fs * 4 bytes), returns TPMLP_E_SCRATCH
+ * before anything is enqueued. The call allocates and frees nothing. Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different host threads) race.
+ */
+#define TPMLP_SCRATCH_BYTES ((size_t)8 << 20)
+tpmlp_status tpmlp_bwd_wgrad_noalloc(const tpmlp_desc* desc, const void* dy, const void* x,
+                                     const void* a_saved, const void* dH, float* dW1,
+                                     float* db1, float* dW2, int32_t accumulate,
+                                     const tpmlp_fp8_scales* fp8, hipStream_t stream);
 
 /*
  * Per-tensor current-scaling quantiser (the FP8 recipe used for `a` inside

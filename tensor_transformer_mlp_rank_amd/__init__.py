@@ -30,7 +30,7 @@ GELU, SWIGLU = 0, 1
 CALL_FWD, CALL_DGRAD, CALL_WGRAD = 0, 1, 2
 
 STATUS = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_DTYPE", 4: "E_ALIGN", 5: "E_UNSUPPORTED",
-          6: "E_WORKSPACE", 7: "E_HIP"}
+          6: "E_WORKSPACE", 7: "E_HIP", 8: "E_SCRATCH"}
 
 _DTYPE_CODES = {"f32": F32, "bf16": BF16, "e4m3": E4M3}
 _ACT_CODES = {"gelu": GELU, "swiglu": SWIGLU}
@@ -126,6 +126,7 @@ def _load():
     psc = ctypes.POINTER(Fp8Scales)
     L.tpmlp_bwd_dgrad.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, psc, vp, sz, vp]
     L.tpmlp_bwd_wgrad.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, i32, psc, vp, sz, vp]
+    L.tpmlp_bwd_wgrad_noalloc.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, i32, psc, vp]
     L.tpmlp_quantize_e4m3.argtypes = [i32, vp, i64, vp, vp, vp, vp, sz, vp]
     L.tpmlp_quantize_e5m2.argtypes = [i32, vp, i64, vp, vp, vp, vp, sz, vp]
     L.tpmlp_quantize_workspace_size.argtypes = [i64]
@@ -147,7 +148,8 @@ def _load():
     L.tpmlp_moe_bwd_wgrad.argtypes = [pm, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     L.tpmlp_moe_workspace_size.argtypes = [pm]
     L.tpmlp_moe_workspace_size.restype = sz
-    for f in ("tpmlp_fwd", "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad", "tpmlp_quantize_e4m3",
+    for f in ("tpmlp_fwd", "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad", "tpmlp_bwd_wgrad_noalloc",
+              "tpmlp_quantize_e4m3",
               "tpmlp_quantize_e5m2", "tpmlp_timing_enable", "tpmlp_attn_qkv_fwd",
               "tpmlp_attn_out_fwd", "tpmlp_attn_out_bwd_dgrad", "tpmlp_attn_out_bwd_wgrad",
               "tpmlp_attn_qkv_bwd_dgrad", "tpmlp_attn_qkv_bwd_wgrad", "tpmlp_moe_fwd",
@@ -240,6 +242,17 @@ def tpmlp_bwd_wgrad(desc, dy, x, a, dH, dW1, db1, dW2, accumulate=False, fp8=Non
     _check(lib.tpmlp_bwd_wgrad(ctypes.byref(desc), _ptr(dy), _ptr(x), _ptr(a), _ptr(dH),
                                _ptr(dW1), _ptr(db1), _ptr(dW2), int(bool(accumulate)), sc,
                                _ptr(workspace), nbytes, _stream(stream)), "tpmlp_bwd_wgrad")
+
+
+def tpmlp_bwd_wgrad_noalloc(desc, dy, x, a, dH, dW1, db1, dW2, accumulate=False, fp8=None,
+                            stream=None):
+    sc = None if fp8 is None else ctypes.byref(fp8)
+    _check(lib.tpmlp_bwd_wgrad_noalloc(ctypes.byref(desc), _ptr(dy), _ptr(x), _ptr(a), _ptr(dH),
+                                       _ptr(dW1), _ptr(db1), _ptr(dW2), int(bool(accumulate)), sc,
+                                       _stream(stream)), "tpmlp_bwd_wgrad_noalloc")
+
+
+SCRATCH_BYTES = 8 << 20  # TPMLP_SCRATCH_BYTES
 
 
 def _quantize(fn, name, src, dst, amax, scale_inv, workspace, stream):
@@ -526,6 +539,7 @@ def timing_collect(cap: int = 64) -> dict:
 
 __all__ = ["Desc", "Fp8Scales", "Fp8History", "DelayedScaling", "fp8_scales", "TpmlpError",
            "make_desc", "workspace_size", "tpmlp_fwd", "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad",
+           "tpmlp_bwd_wgrad_noalloc", "SCRATCH_BYTES",
            "tpmlp_quantize_e4m3", "tpmlp_quantize_e5m2", "fwd", "bwd_dgrad", "bwd_wgrad",
            "quantize_e4m3", "quantize_e5m2", "timing_enable", "timing_collect", "lib", "LIB_PATH",
            "F32", "BF16", "E4M3", "GELU", "SWIGLU",

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <initializer_list>
+#include <mutex>
 
 #include <string>
 #include <vector>
@@ -428,6 +429,98 @@ GemmArgs make_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, int64
   return g;
 }
 
+
+// ---------------------------------------------------------------- weight gradients
+// The weight-gradient call's checks that do not involve the workspace.
+tpmlp_status check_wgrad(const tpmlp_desc* d, const void* dy, const void* x, const void* a_saved,
+                         const void* dH, float* dW1, float* db1, float* dW2, int32_t accumulate,
+                         const tpmlp_fp8_scales* fp8) {
+  tpmlp_status st = check_desc(d);
+  if (st != TPMLP_OK) return st;
+  if (accumulate != 0 && accumulate != 1) return TPMLP_E_DTYPE;
+  if ((st = check_ptrs({dy, x, a_saved, dH, dW1, dW2})) != TPMLP_OK) return st;
+  if (d->has_bias && (st = check_ptrs({db1})) != TPMLP_OK) return st;
+  const bool is_fp8 = d->dtype == TPMLP_E4M3;
+  if (is_fp8 != (fp8 != nullptr)) return is_fp8 ? TPMLP_E_NULL : TPMLP_E_DTYPE;
+  if (is_fp8 && (!fp8->dy_scale_inv || !fp8->x_scale_inv || !fp8->a_scale_inv ||
+                 !fp8->dH_scale_inv))
+    return TPMLP_E_NULL;
+  return TPMLP_OK;
+}
+
+// dW2 = dy^T . a, dW1 = dH^T . x, db1; arguments already checked. The
+// products are split along K where the workspace holds the full plan's bytes.
+tpmlp_status run_wgrad(const tpmlp_desc* d, const void* dy, const void* x, const void* a_saved,
+                       const void* dH, float* dW1, float* db1, float* dW2, int32_t accumulate,
+                       const tpmlp_fp8_scales* fp8, void* ws, size_t ws_bytes, hipStream_t s) {
+  const int64_t T = d->tokens, H = d->hidden, Fs = d->ffn_shard;
+  if (T == 0 && accumulate) return TPMLP_OK;  // adding nothing
+  const bool is_fp8 = d->dtype == TPMLP_E4M3;
+  const bool swiglu = d->act == TPMLP_ACT_SWIGLU;
+  const int64_t GFs = swiglu ? 2 * Fs : Fs;
+  const Kind kind = d->dtype == TPMLP_F32 ? KIND_F32 : d->dtype == TPMLP_BF16 ? KIND_BF16 : KIND_E4M3;
+  // split-K for grids that leave CUs idle, when the workspace has room for it
+  const WgradPlan full = wgrad_plan(d, true);
+  const WgradPlan p = (ws && ws_bytes >= full.colsum + full.planes) ? full : wgrad_plan(d, false);
+  float* planes = reinterpret_cast<float*>(static_cast<char*>(ws) + p.colsum);
+  // dW2 [H, Fs] = dy^T . a : A = dy as [K=T][M=H], B = a as [K=T][N=Fs]
+  EpiArgs e1{};
+  e1.out = dW2; e1.ldo = Fs; e1.accumulate = accumulate;
+  if (is_fp8) { e1.scale_a = fp8->dy_scale_inv; e1.scale_b = fp8->a_scale_inv; }
+  GemmArgs g1 = make_gemm(dy, H, a_saved, Fs, H, Fs, T, 0);
+  hipError_t err = run_gemm(kind, WGRAD, label(kind, 4), g1, e1, s, p.sp2, planes);
+  if (err != hipSuccess) return hip_fail(err);
+  // dW1 [GFs, H] = dH^T . x (+ db1 = column sums of dH). The fp32 kernel
+  // writes db1 itself; the MFMA kernel writes per-tile-column partial sums
+  // (per split and tile column) into the workspace, which a second pass adds
+  // up into db1.
+  const bool parts = d->has_bias && kind != KIND_F32;
+  EpiArgs e2{};
+  e2.out = dW1; e2.ldo = H; e2.accumulate = accumulate;
+  e2.colsum = d->has_bias ? (parts ? static_cast<float*>(ws) : db1) : nullptr;
+  if (is_fp8) { e2.scale_a = fp8->dH_scale_inv; e2.scale_b = fp8->x_scale_inv; }
+  GemmArgs g2 = make_gemm(dH, GFs, x, H, GFs, H, T, 0);
+  err = run_gemm(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, label(kind, 5), g2, e2, s, p.sp1,
+                 planes);
+  if (err != hipSuccess) return hip_fail(err);
+  if (parts) {
+    err = timed(is_fp8 ? "db1_reduce.e4m3" : "db1_reduce.bf16", s, [&]() {
+      return colsum_reduce_launch(static_cast<const float*>(ws), p.sp1 * colsum_parts(d),
+                                  (int)GFs, db1, accumulate, s);
+    });
+    if (err != hipSuccess) return hip_fail(err);
+  }
+  return TPMLP_OK;
+}
+
+// ---------------------------------------------------------------- fixed scratch
+// Device memory of the allocation-free weight-gradient call: a fixed array
+// that every GPU the library runs on holds until the process ends. In host
+// code the array's name is a stand-in, not a device address, so the address
+// of each device's copy is looked up once per device, with that device
+// current, and kept; kernels and copies get that address. Every such call on
+// one GPU shares the array, so calls that overlap on one GPU race.
+constexpr size_t kScratchBytes = TPMLP_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  const hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -445,6 +538,9 @@ const char* tpmlp_strerror(tpmlp_status s) {
       return "combination not provided (E4M3 SwiGLU, SwiGLU bias, E4M3 attention projections)";
     case TPMLP_E_WORKSPACE: return "workspace missing or too small";
     case TPMLP_E_HIP: return "HIP runtime error while enqueuing (see tpmlp_last_hip_error)";
+    case TPMLP_E_SCRATCH:
+      return "problem too large for the fixed scratch of the allocation-free call "
+             "(TPMLP_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -634,54 +730,28 @@ tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* d, const void* dy, const void* x,
                              const void* a_saved, const void* dH, float* dW1, float* db1,
                              float* dW2, int32_t accumulate, const tpmlp_fp8_scales* fp8,
                              void* ws, size_t ws_bytes, hipStream_t s) {
-  tpmlp_status st = check_desc(d);
+  tpmlp_status st = check_wgrad(d, dy, x, a_saved, dH, dW1, db1, dW2, accumulate, fp8);
   if (st != TPMLP_OK) return st;
-  if (accumulate != 0 && accumulate != 1) return TPMLP_E_DTYPE;
-  if ((st = check_ptrs({dy, x, a_saved, dH, dW1, dW2})) != TPMLP_OK) return st;
-  if (d->has_bias && (st = check_ptrs({db1})) != TPMLP_OK) return st;
-  const bool is_fp8 = d->dtype == TPMLP_E4M3;
-  if (is_fp8 != (fp8 != nullptr)) return is_fp8 ? TPMLP_E_NULL : TPMLP_E_DTYPE;
-  if (is_fp8 && (!fp8->dy_scale_inv || !fp8->x_scale_inv || !fp8->a_scale_inv ||
-                 !fp8->dH_scale_inv))
-    return TPMLP_E_NULL;
   if ((st = check_workspace(d, TPMLP_CALL_WGRAD, ws, ws_bytes)) != TPMLP_OK) return st;
-  const int64_t T = d->tokens, H = d->hidden, Fs = d->ffn_shard;
-  if (T == 0 && accumulate) return TPMLP_OK;  // adding nothing
-  const bool swiglu = d->act == TPMLP_ACT_SWIGLU;
-  const int64_t GFs = swiglu ? 2 * Fs : Fs;
-  const Kind kind = d->dtype == TPMLP_F32 ? KIND_F32 : d->dtype == TPMLP_BF16 ? KIND_BF16 : KIND_E4M3;
-  // split-K for grids that leave CUs idle, when the workspace has room for it
-  const WgradPlan full = wgrad_plan(d, true);
-  const WgradPlan p = (ws && ws_bytes >= full.colsum + full.planes) ? full : wgrad_plan(d, false);
-  float* planes = reinterpret_cast<float*>(static_cast<char*>(ws) + p.colsum);
-  // dW2 [H, Fs] = dy^T . a : A = dy as [K=T][M=H], B = a as [K=T][N=Fs]
-  EpiArgs e1{};
-  e1.out = dW2; e1.ldo = Fs; e1.accumulate = accumulate;
-  if (is_fp8) { e1.scale_a = fp8->dy_scale_inv; e1.scale_b = fp8->a_scale_inv; }
-  GemmArgs g1 = make_gemm(dy, H, a_saved, Fs, H, Fs, T, 0);
-  hipError_t err = run_gemm(kind, WGRAD, label(kind, 4), g1, e1, s, p.sp2, planes);
-  if (err != hipSuccess) return hip_fail(err);
-  // dW1 [GFs, H] = dH^T . x (+ db1 = column sums of dH). The fp32 kernel
-  // writes db1 itself; the MFMA kernel writes per-tile-column partial sums
-  // (per split and tile column) into the workspace, which a second pass adds
-  // up into db1.
-  const bool parts = d->has_bias && kind != KIND_F32;
-  EpiArgs e2{};
-  e2.out = dW1; e2.ldo = H; e2.accumulate = accumulate;
-  e2.colsum = d->has_bias ? (parts ? static_cast<float*>(ws) : db1) : nullptr;
-  if (is_fp8) { e2.scale_a = fp8->dH_scale_inv; e2.scale_b = fp8->x_scale_inv; }
-  GemmArgs g2 = make_gemm(dH, GFs, x, H, GFs, H, T, 0);
-  err = run_gemm(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, label(kind, 5), g2, e2, s, p.sp1,
-                 planes);
-  if (err != hipSuccess) return hip_fail(err);
-  if (parts) {
-    err = timed(is_fp8 ? "db1_reduce.e4m3" : "db1_reduce.bf16", s, [&]() {
-      return colsum_reduce_launch(static_cast<const float*>(ws), p.sp1 * colsum_parts(d),
-                                  (int)GFs, db1, accumulate, s);
-    });
+  return run_wgrad(d, dy, x, a_saved, dH, dW1, db1, dW2, accumulate, fp8, ws, ws_bytes, s);
+}
+
+tpmlp_status tpmlp_bwd_wgrad_noalloc(const tpmlp_desc* d, const void* dy, const void* x,
+                                     const void* a_saved, const void* dH, float* dW1,
+                                     float* db1, float* dW2, int32_t accumulate,
+                                     const tpmlp_fp8_scales* fp8, hipStream_t s) {
+  tpmlp_status st = check_wgrad(d, dy, x, a_saved, dH, dW1, db1, dW2, accumulate, fp8);
+  if (st != TPMLP_OK) return st;
+  // the part of the workspace the call cannot run without (the db1 partial
+  // sums); split-K is left out, so nothing else is needed
+  const size_t need = workspace_min_bytes(d, TPMLP_CALL_WGRAD);
+  if (need > kScratchBytes) return TPMLP_E_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t err = scratch_address(&ws);
     if (err != hipSuccess) return hip_fail(err);
   }
-  return TPMLP_OK;
+  return run_wgrad(d, dy, x, a_saved, dH, dW1, db1, dW2, accumulate, fp8, ws, need, s);
 }
 
 // ---------------------------------------------------------------- attention

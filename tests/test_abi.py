@@ -11,7 +11,7 @@ import pytest
 import tensor_transformer_mlp_rank_amd as tp
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tpmlp.h")
-OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_UNSUP, E_WS, E_HIP = range(8)
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_UNSUP, E_WS, E_HIP, E_SCRATCH = range(9)
 P = 0x100000          # fake, 16-byte aligned "device" address (never dereferenced)
 MIS = 0x100008        # 8-byte aligned only
 
@@ -30,8 +30,8 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert tp.lib.tpmlp_abi_version() == 6
-    for s in range(8):
+    assert tp.lib.tpmlp_abi_version() == 7
+    for s in range(9):
         assert len(tp.lib.tpmlp_strerror(s)) > 5
     assert tp.lib.tpmlp_last_hip_error() == b""
 
@@ -215,6 +215,36 @@ def test_wgrad_workspace():
     assert tp.lib.tpmlp_bwd_wgrad(*args, None, 0, None) == E_WS
     assert tp.lib.tpmlp_bwd_wgrad(*args, P, need - 1, None) == E_WS
     assert tp.lib.tpmlp_bwd_wgrad(*args, MIS, need, None) == E_ALIGN
+
+
+def wgrad_noalloc(desc, dy=P, x=P, a=P, dH=P, dW1=P, db1=P, dW2=P, acc=0, fp8=None):
+    sc = None if fp8 is None else ctypes.byref(fp8)
+    return tp.lib.tpmlp_bwd_wgrad_noalloc(ctypes.byref(desc), dy, x, a, dH, dW1, db1, dW2, acc,
+                                          sc, None)
+
+
+@pytest.mark.parametrize("name", ["dy", "x", "a", "dH", "dW1", "dW2"])
+def test_wgrad_noalloc_validation(name):
+    """The allocation-free weight gradient checks its arguments as
+    tpmlp_bwd_wgrad does, before anything else."""
+    assert wgrad_noalloc(D(), **{name: None}) == E_NULL
+    assert wgrad_noalloc(D(), **{name: MIS}) == E_ALIGN
+    assert wgrad_noalloc(D(has_bias=True), db1=None) == E_NULL
+    assert wgrad_noalloc(D(), acc=2) == E_DTYPE
+    assert wgrad_noalloc(D(dtype="e4m3")) == E_NULL  # FP8 without scales
+
+
+def test_wgrad_noalloc_rejects_what_the_scratch_cannot_hold():
+    """db1 partial sums of ceil(H / 256) * G * Fs floats beyond
+    TPMLP_SCRATCH_BYTES: TPMLP_E_SCRATCH, before any HIP call."""
+    assert tp.SCRATCH_BYTES == 8 << 20
+    fits = D(tokens=64, hidden=8192, ffn_shard=8192)          # 32 * 8192 * 4 = 1 MiB
+    big = D(tokens=64, hidden=65536, ffn_shard=16384)         # 256 * 16384 * 4 = 16 MiB
+    gated = D(tokens=64, hidden=65536, ffn_shard=4112, act="swiglu", has_bias=False)
+    assert tp.workspace_size(fits, tp.CALL_WGRAD) > 0
+    assert wgrad_noalloc(big) == E_SCRATCH
+    # no bias: no partial sums, no scratch needed (validated like any call)
+    assert wgrad_noalloc(gated, db1=None, dW1=MIS) == E_ALIGN
 
 
 def test_quantize_validation():
