@@ -886,10 +886,13 @@ def main():
     clock = ClockSampler(torch)
     torch.cuda.synchronize()
     ev = new_events()
-    clock.start()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(ev[i])
+    # the clock is sampled while the GPU works through the enqueued steps and
+    # this thread waits in the synchronisation (a sampling thread that ran
+    # while the steps were being enqueued would hold up the launches)
+    clock.start()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     clock.stop()
