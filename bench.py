@@ -356,13 +356,29 @@ def attn_cpu_baseline(w, tokens: int, repeats: int = 3, gpu=None) -> dict:
                       f"({flops / 1e12:.3f} TFLOP per run, {dt:.2f} s, {sum(times):.1f} s total)"}, parity
 
 
+def host_outputs(dev: dict) -> dict:
+    """The parity step's device outputs on the host: arrays, and the scales
+    as float32 scalars."""
+    import numpy as np
+    out = {}
+    for k, v in dev.items():
+        if v is None:
+            out[k] = None
+        elif k.endswith("_scale"):
+            out[k] = np.float32(v.item())
+        else:
+            out[k] = v.cpu().numpy()
+    return out
+
+
 class ClockSampler:
     """The GPU's graphics clock, sampled on a thread while the timed steps
     run: amdsmi's GPU metrics of the device matched to cuda:0 by its PCI
     address, each sample the mean of the per-XCD current clocks. A sample
     counts only while the metrics show the GPU busy (gfx activity of 50% or
-    more), so a reading of another, idle device or a stale one is not taken
-    for the kernels' clock. `mhz()` gives the median of the counted samples,
+    more, or where they give no activity, a socket power of 450 W or more),
+    so a reading of another, idle device or a stale one is not taken for the
+    kernels' clock. `mhz()` gives the median of the counted samples,
     or None when amdsmi is unavailable or counted fewer than three."""
 
     def __init__(self, torch, period: float = 0.002):
@@ -393,19 +409,24 @@ class ClockSampler:
         clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
         clk = sum(clks) / len(clks) if clks else m.get("current_gfxclk")
         act = m.get("average_gfx_activity")
-        return (float(clk) if isinstance(clk, (int, float)) else None,
-                float(act) if isinstance(act, (int, float)) else None)
+        pw = m.get("current_socket_power")
+        num = lambda v: float(v) if isinstance(v, (int, float)) else None
+        return num(clk), num(act), num(pw)
 
     def _run(self):
         while not self._stop.is_set():
             try:
-                clk, act = self._read()
+                clk, act, pw = self._read()
             except Exception:
                 return
-            if clk is not None and act is not None and act >= 50.0:
+            # busy: the activity figure, or where the metrics give none, a
+            # socket power above a third of the board's 1.4 kW
+            busy = (act >= 50.0) if act is not None else (pw is not None and pw >= 450.0)
+            if clk is not None and busy:
                 self.samples.append(clk)
             else:
                 self.rejected += 1
+                self.last_rejected = (clk, act, pw)
             self._stop.wait(self.period)
 
     def start(self):
@@ -423,7 +444,8 @@ class ClockSampler:
         if len(self.samples) < 3:
             if self.h is not None:
                 print(f"clock: {len(self.samples)} busy samples ({self.rejected} idle or "
-                      f"unreadable): no figure", file=sys.stderr)
+                      f"unreadable, last (MHz, %, W) {getattr(self, 'last_rejected', None)}): "
+                      f"no figure", file=sys.stderr)
             return None
         import statistics
         return statistics.median(self.samples)
@@ -494,35 +516,30 @@ def mlp_job(tp, torch, w, calls, dev) -> Job:
 
     def parity_step() -> dict:
         """One step on zeroed gradient buffers (accumulating into zeros is
-        the plain result), in the timed steps' launch configuration; the
-        outputs on the host (FP8 codes of a dequantised, with the scales a
-        and dH were quantised at)."""
-        import numpy as np
+        the plain result), in the timed steps' launch configuration; float32
+        copies of its outputs on the device (the FP8 codes of a dequantised,
+        and the scales a and dH were quantised at), for host_outputs() after
+        the timed steps."""
         for k in ("dW1", "db1", "dW2"):
             if buf[k] is not None:
                 buf[k].zero_()
-        extra = {}
+        out = {}
         if fp8:
-            extra = {"a_scale": np.float32(a_hist.scale.item()),
-                     "dH_scale": np.float32(dH_hist.scale.item())}
+            out = {"a_scale": a_hist.scale.clone(), "dH_scale": dH_hist.scale.clone()}
         for c in calls:
             fns[c]()
-        torch.cuda.synchronize()
-        host = lambda t: t.float().cpu().numpy()
-        out = {"y": host(buf["y"]), "h": host(buf["h"])}
+        dev32 = lambda t: None if t is None else t.float().clone()
+        out.update(y=dev32(buf["y"]), h=dev32(buf["h"]))
         if fp8:
-            out["a"] = (buf["a"].view(torch.float8_e4m3fn).float().cpu().numpy().astype(np.float64)
-                        * float(a_hist.scale_inv.item()))
+            out["a"] = buf["a"].view(torch.float8_e4m3fn).float() * a_hist.scale_inv
         else:
-            out["a"] = host(buf["a"])
+            out["a"] = dev32(buf["a"])
         if "dgrad" in calls:
-            out["dx"] = host(buf["dx"])
+            out["dx"] = dev32(buf["dx"])
             if not fp8:
-                out["dH"] = host(buf["dH"])
+                out["dH"] = dev32(buf["dH"])
             if "wgrad" in calls:
-                out.update(dW1=host(buf["dW1"]), dW2=host(buf["dW2"]),
-                           db1=None if buf["db1"] is None else host(buf["db1"]))
-        out.update(extra)
+                out.update(dW1=dev32(buf["dW1"]), dW2=dev32(buf["dW2"]), db1=dev32(buf["db1"]))
         return out
 
     what = "fwd+bwd" if calls == ("fwd", "dgrad", "wgrad") else "+".join(calls)
@@ -580,8 +597,7 @@ def attn_job(tp, torch, w, dev) -> Job:
                 buf[k].zero_()
         fwd()
         bwd()
-        torch.cuda.synchronize()
-        return {k: (None if v is None else v.float().cpu().numpy()) for k, v in
+        return {k: (None if v is None else v.float().clone()) for k, v in
                 (("qkv", buf["qkv"]), ("y", buf["y"]), ("dctx", buf["dctx"]), ("dWo", buf["dWo"]),
                  ("dx", buf["dx"]), ("dWqkv", buf["dWqkv"]), ("dbqkv", buf["dbqkv"]))}
 
@@ -657,8 +673,7 @@ def moe_job(tp, torch, w, dev) -> Job:
         fwd()
         dgrad()
         wgrad()
-        torch.cuda.synchronize()
-        return {k: (None if v is None else v.float().cpu().numpy()) for k, v in buf.items()}
+        return {k: (None if v is None else v.float().clone()) for k, v in buf.items()}
 
     return Job(
         name=w.name, dtype=w.dtype, stream=stream, parity_step=parity_step,
@@ -833,6 +848,7 @@ def main():
     # workload after the timed steps (so that the GPU does not sit idle for the
     # oracle's seconds of CPU work right before them), and no number is
     # reported unless every tensor is within its tolerance.
+    clock = ClockSampler(torch)
     gpu_out = job.parity_step()
 
     def step(ev=None):
@@ -883,7 +899,6 @@ def main():
 
     # timed region: live events around the dominant kernel only
     tp.timing_enable(True, dominant)
-    clock = ClockSampler(torch)
     torch.cuda.synchronize()
     ev = new_events()
     t0 = time.perf_counter()
@@ -954,7 +969,7 @@ def main():
         line["spans_cold"] = cold
     st = [e[0].elapsed_time(e[-1]) for e in ev]
     print("step ms: " + " ".join(f"{v:.3f}" for v in st), file=sys.stderr)
-    baseline, parity = job.cpu(args.cpu_tokens, gpu_out)
+    baseline, parity = job.cpu(args.cpu_tokens, host_outputs(gpu_out))
     gpu_out = None
     if not parity["pass"]:
         print(json.dumps({"parity_failed": parity, "workload": job.name}), file=sys.stderr)
