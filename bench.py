@@ -14,7 +14,7 @@ miss the script exits with status 3 and prints no line.
 
 Then prints one JSON line: TFLOP/s of the whole step (algorithmic FLOPs
 6*T*H*Fs*(G+1) over the measured time), its fraction of the vendor peak and
-of the peak at the graphics clock sampled during the timed steps, the parity
+of the peak at the shader clock the kernels measured themselves, the parity
 errors, the dominant kernel's roofline (its average launch time from HIP
 events recorded on its launch stream during the timed steps) and the CPU
 oracle's throughput on a bounded sample.
@@ -369,86 +369,6 @@ def host_outputs(dev: dict) -> dict:
         else:
             out[k] = v.cpu().numpy()
     return out
-
-
-class ClockSampler:
-    """The GPU's graphics clock, sampled on a thread while the timed steps
-    run: amdsmi's GPU metrics of the device matched to cuda:0 by its PCI
-    address, each sample the mean of the per-XCD current clocks. A sample
-    counts only while the metrics show the GPU busy (gfx activity of 50% or
-    more, or where they give no activity, a socket power of 450 W or more),
-    so a reading of another, idle device or a stale one is not taken for the
-    kernels' clock. `mhz()` gives the median of the counted samples,
-    or None when amdsmi is unavailable or counted fewer than three."""
-
-    def __init__(self, torch, period: float = 0.002):
-        import threading
-        self.period, self.samples, self.rejected, self.h, self.amdsmi = period, [], 0, None, None
-        self._stop = threading.Event()
-        self._thread = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            p = torch.cuda.get_device_properties(0)
-            want = (int(getattr(p, "pci_domain_id", 0)), int(p.pci_bus_id), int(p.pci_device_id))
-            for h in amdsmi.amdsmi_get_processor_handles():
-                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # dddd:bb:dd.f (hex)
-                dom, bus, rest = bdf.split(":")
-                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
-                    self.h = h
-            self.amdsmi = amdsmi
-            if self.h is not None:
-                self._read()
-        except Exception as exc:  # no amdsmi, no access, or no match: no clock figure
-            print(f"clock sampling unavailable: {exc!r}", file=sys.stderr)
-            self.h = None
-
-    def _read(self):
-        """(clock in MHz, gfx activity in %) from one metrics read."""
-        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
-        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
-        clk = sum(clks) / len(clks) if clks else m.get("current_gfxclk")
-        act = m.get("average_gfx_activity")
-        pw = m.get("current_socket_power")
-        num = lambda v: float(v) if isinstance(v, (int, float)) else None
-        return num(clk), num(act), num(pw)
-
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                clk, act, pw = self._read()
-            except Exception:
-                return
-            # busy: the activity figure, or where the metrics give none, a
-            # socket power above a third of the board's 1.4 kW
-            busy = (act >= 50.0) if act is not None else (pw is not None and pw >= 450.0)
-            if clk is not None and busy:
-                self.samples.append(clk)
-            else:
-                self.rejected += 1
-                self.last_rejected = (clk, act, pw)
-            self._stop.wait(self.period)
-
-    def start(self):
-        if self.h is not None:
-            import threading
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
-
-    def stop(self):
-        if self._thread is not None:
-            self._stop.set()
-            self._thread.join()
-
-    def mhz(self):
-        if len(self.samples) < 3:
-            if self.h is not None:
-                print(f"clock: {len(self.samples)} busy samples ({self.rejected} idle or "
-                      f"unreadable, last (MHz, %, W) {getattr(self, 'last_rejected', None)}): "
-                      f"no figure", file=sys.stderr)
-            return None
-        import statistics
-        return statistics.median(self.samples)
 
 
 class Job:
@@ -848,7 +768,6 @@ def main():
     # workload after the timed steps (so that the GPU does not sit idle for the
     # oracle's seconds of CPU work right before them), and no number is
     # reported unless every tensor is within its tolerance.
-    clock = ClockSampler(torch)
     gpu_out = job.parity_step()
 
     def step(ev=None):
@@ -889,6 +808,7 @@ def main():
         step()
     torch.cuda.synchronize()
     per = tp.timing_collect()
+    probe_mhz = {k: round(tp.timing_clock_mhz(k), 1) for k in per}
     tp.timing_enable(False)
     if list(per) != job.labels:
         raise SystemExit(f"unexpected launch sequence {list(per)}")
@@ -904,14 +824,10 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(ev[i])
-    # the clock is sampled while the GPU works through the enqueued steps and
-    # this thread waits in the synchronisation (a sampling thread that ran
-    # while the steps were being enqueued would hold up the launches)
-    clock.start()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    clock.stop()
     dom = tp.timing_collect()[dominant]
+    dom_mhz = tp.timing_clock_mhz(dominant)
     tp.timing_enable(False)
     spans = span_stats(ev)
     cold = None
@@ -932,9 +848,13 @@ def main():
     dom_ms = dom[1] / dom[0]
     achieved = job.gemm_flops(dominant) / (dom_ms * 1e-3) / 1e12
     peak = PEAK[job.dtype]
-    mhz = clock.mhz()
-    # the peak at the clock the GPU ran at during the timed steps
-    peak_at_clock = None if mhz is None else N_CU * FLOP_PER_CU_CLK[job.dtype] * mhz * 1e-6
+    # measured shader clocks (the library's workgroups read the clock and
+    # real-time counters): each GEMM kernel's in the warm-up probe, weighted
+    # by its time, for the step; the dominant kernel's over the timed steps
+    gemm_ms = {k: v[1] for k, v in per.items() if probe_mhz.get(k, 0) > 0}
+    step_mhz = (sum(probe_mhz[k] * t for k, t in gemm_ms.items()) / sum(gemm_ms.values())
+                if gemm_ms else None)
+    at_clock = lambda mhz: None if not mhz else N_CU * FLOP_PER_CU_CLK[job.dtype] * mhz * 1e-6
     line = {
         "metric": job.metric,
         "value": round(value, 2),
@@ -950,13 +870,16 @@ def main():
         "data": "synthetic (seeded PCG64 normals; per-rank shard shapes)",
         "config": job.config,
         "pct_of_peak": round(100 * value / peak, 2),
-        "clock_mhz": None if mhz is None else round(mhz, 1),
-        "clock_samples": len(clock.samples),
-        "pct_of_peak_at_clock": None if mhz is None else round(100 * value / peak_at_clock, 2),
+        "clock_mhz": {"step": None if step_mhz is None else round(step_mhz, 1),
+                      "dominant_kernel": round(dom_mhz, 1) if dom_mhz else None,
+                      "per_kernel_warmup": probe_mhz,
+                      "source": "shader clock counter over the 100 MHz real-time counter, "
+                                "per workgroup of the GEMM kernels"},
+        "pct_of_peak_at_clock": None if step_mhz is None else round(100 * value / at_clock(step_mhz), 2),
         "parity": None,
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "frac_at_clock": None if mhz is None else round(achieved / peak_at_clock, 4),
+                     "frac_at_clock": None if not dom_mhz else round(achieved / at_clock(dom_mhz), 4),
                      "traffic": measured_traffic(job.name, dominant),
                      "traffic_unit": "L2-to-fabric bytes per launch (rocprofv3 FETCH_SIZE + "
                                      "WRITE_SIZE, copy-calibrated; Infinity Cache hits count "

@@ -163,6 +163,8 @@ def _load():
     L.tpmlp_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(i64),
                                        ctypes.POINTER(ctypes.c_double), i32]
     L.tpmlp_timing_collect.restype = i32
+    L.tpmlp_timing_clock_mhz.argtypes = [ctypes.c_char_p]
+    L.tpmlp_timing_clock_mhz.restype = ctypes.c_double
     return L
 
 
@@ -524,7 +526,15 @@ def moe_bwd_wgrad(desc, counts, dy, x, a, dH, accumulate_into=None, stream=None)
 
 
 def timing_enable(enable: bool, name_filter: str | None = None):
-    lib.tpmlp_timing_enable(int(bool(enable)), None if name_filter is None else name_filter.encode())
+    _check(lib.tpmlp_timing_enable(int(bool(enable)),
+                                   None if name_filter is None else name_filter.encode()),
+           "tpmlp_timing_enable")
+
+
+def timing_clock_mhz(name: str) -> float:
+    """Mean shader clock (MHz) of the GEMM launches `name` timed before the
+    last timing_collect(); 0.0 if none."""
+    return float(lib.tpmlp_timing_clock_mhz(name.encode()))
 
 
 def timing_collect(cap: int = 64) -> dict:
@@ -541,7 +551,8 @@ __all__ = ["Desc", "Fp8Scales", "Fp8History", "DelayedScaling", "fp8_scales", "T
            "make_desc", "workspace_size", "tpmlp_fwd", "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad",
            "tpmlp_bwd_wgrad_noalloc", "SCRATCH_BYTES",
            "tpmlp_quantize_e4m3", "tpmlp_quantize_e5m2", "fwd", "bwd_dgrad", "bwd_wgrad",
-           "quantize_e4m3", "quantize_e5m2", "timing_enable", "timing_collect", "lib", "LIB_PATH",
+           "quantize_e4m3", "quantize_e5m2", "timing_enable", "timing_collect", "timing_clock_mhz",
+           "lib", "LIB_PATH",
            "F32", "BF16", "E4M3", "GELU", "SWIGLU",
            "AttnDesc", "make_attn_desc", "attn_workspace_size", "tpmlp_attn_qkv_fwd",
            "tpmlp_attn_out_fwd", "tpmlp_attn_out_bwd_dgrad", "tpmlp_attn_out_bwd_wgrad",

@@ -44,6 +44,38 @@ hipError_t take_event(hipEvent_t* ev) {
   return hipEventCreate(ev);
 }
 
+// Clock capture of the MFMA GEMM launches the facility times: each workgroup
+// writes (shader clock counter, real-time counter) at its start and end into
+// 4 slots of this array (one range of workgroups per launch, handed out in
+// launch order until the array is full). tpmlp_timing_collect turns them into
+// each kernel's mean shader clock: the sum of its workgroups' cycles over the
+// sum of their real-time ticks, at the counter's 100 MHz.
+constexpr int kClockSlots = 32768;
+__device__ __align__(256) unsigned long long clock_slots[4 * kClockSlots];
+struct ClockRec {
+  const char* name;
+  int off, n;
+};
+unsigned long long* g_clk_dev = nullptr;  // the current device's array, while timing
+int g_clk_used = 0;
+std::vector<ClockRec> g_clk_recs;
+std::vector<std::pair<std::string, double>> g_clk_mhz;  // from the last collect
+
+bool timing_selects(const char* name) {
+  return g_timing && (g_filter.empty() || strstr(name, g_filter.c_str()) != nullptr);
+}
+
+// Points the launch's clock capture at the next free slots (or leaves it off).
+void clock_attach(const char* name, GemmArgs& g, int64_t nb) {
+  g.clk = nullptr;
+  g.clk_slots = 0;
+  if (!timing_selects(name) || !g_clk_dev || nb <= 0 || g_clk_used + nb > kClockSlots) return;
+  g.clk = g_clk_dev + 4 * (int64_t)g_clk_used;
+  g.clk_slots = (int)nb;
+  g_clk_recs.push_back({name, g_clk_used, (int)nb});
+  g_clk_used += (int)nb;
+}
+
 template <class F>
 hipError_t timed(const char* name, hipStream_t s, F&& launch) {
   if (!g_timing || (!g_filter.empty() && strstr(name, g_filter.c_str()) == nullptr))
@@ -232,6 +264,7 @@ hipError_t run_step(Kind kind, Step step, const char* label, GemmArgs g, const E
                     hipStream_t s) {
   const int nb = (kind == KIND_F32) ? f32_grid(step, g) : mfma_grid(step, g);
   if (nb == 0) return hipSuccess;
+  if (kind != KIND_F32) clock_attach(label, g, nb);
   return timed(label, s, [&]() {
     return kind == KIND_F32 ? f32_launch(step, g, e, s)
                             : mfma_launch(kind == KIND_E4M3, step, g, e, s);
@@ -251,6 +284,7 @@ hipError_t run_gemm(Kind kind, Step step, const char* label, GemmArgs g, const E
   // even, so that every split but the last can take the kernel's loop for
   // K-major operands without a per-lane K-range test
   g.split_stages += g.split_stages & 1;
+  clock_attach(label, g, (int64_t)g.tiles_m * g.tiles_n * sp);
   EpiArgs ep = e;
   ep.out = part;
   ep.ldo = g.N;
@@ -411,8 +445,11 @@ size_t moe_workspace_bytes(const tpmlp_moe_desc* d) {
 hipError_t run_group_step(Step step, int group, const char* label, const GemmArgs& g,
                           const EpiArgs& e, hipStream_t s) {
   GemmArgs gg = g;
-  if (mfma_group_grid(step, group, gg) <= 0) return hipSuccess;
-  return timed(label, s, [&]() { return mfma_group_launch(step, group, g, e, s); });
+  const int64_t nb = mfma_group_grid(step, group, gg);
+  if (nb <= 0) return hipSuccess;
+  GemmArgs ga = g;
+  clock_attach(label, ga, nb);
+  return timed(label, s, [&]() { return mfma_group_launch(step, group, ga, e, s); });
 }
 
 GemmArgs make_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
@@ -1059,9 +1096,27 @@ tpmlp_status tpmlp_timing_enable(int32_t enable, const char* name_filter) {
     g_pool.push_back(r.stop);
   }
   g_recs.clear();
+  g_clk_recs.clear();
+  g_clk_used = 0;
+  g_clk_dev = nullptr;
   g_timing = enable != 0;
   g_filter = (enable && name_filter) ? name_filter : "";
+  if (g_timing) {
+    // the clock slots of the current device, cleared (unwritten slots read
+    // 0); without a device the facility times with events only
+    void* p = nullptr;
+    hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(clock_slots));
+    if (err == hipSuccess) err = hipMemset(p, 0, sizeof(unsigned long long) * 4 * kClockSlots);
+    if (err == hipSuccess) g_clk_dev = static_cast<unsigned long long*>(p);
+    else (void)hipGetLastError();
+  }
   return TPMLP_OK;
+}
+
+double tpmlp_timing_clock_mhz(const char* name) {
+  for (auto& kv : g_clk_mhz)
+    if (name && kv.first == name) return kv.second;
+  return 0.0;
 }
 
 int32_t tpmlp_timing_collect(const char** names, int64_t* counts, double* total_ms, int32_t cap) {
@@ -1086,6 +1141,34 @@ int32_t tpmlp_timing_collect(const char** names, int64_t* counts, double* total_
     if (names) names[i] = keys[i];
     if (counts) counts[i] = cnt[i];
     if (total_ms) total_ms[i] = tot[i];
+  }
+  // mean shader clock per kernel name from the workgroups' counters (the
+  // events above have completed, so have the launches)
+  g_clk_mhz.clear();
+  if (g_clk_dev && g_clk_used > 0) {
+    std::vector<unsigned long long> h((size_t)4 * g_clk_used);
+    if (hipMemcpy(h.data(), g_clk_dev, h.size() * sizeof(unsigned long long),
+                  hipMemcpyDeviceToHost) != hipSuccess)
+      return -1;
+    std::vector<std::pair<std::string, std::pair<double, double>>> acc;
+    for (auto& r : g_clk_recs) {
+      double cyc = 0, tick = 0;
+      for (int i = r.off; i < r.off + r.n; ++i) {
+        const unsigned long long* q = &h[(size_t)4 * i];
+        // a workgroup that exited early (surplus ids of a grouped launch) has no end
+        if (q[2] > q[0] && q[3] > q[1]) {
+          cyc += (double)(q[2] - q[0]);
+          tick += (double)(q[3] - q[1]);
+        }
+      }
+      size_t j = 0;
+      while (j < acc.size() && acc[j].first != r.name) ++j;
+      if (j == acc.size()) acc.push_back({r.name, {0.0, 0.0}});
+      acc[j].second.first += cyc;
+      acc[j].second.second += tick;
+    }
+    for (auto& a : acc)
+      if (a.second.second > 0) g_clk_mhz.push_back({a.first, 100.0 * a.second.first / a.second.second});
   }
   return (int32_t)keys.size();
 }

@@ -67,6 +67,11 @@ struct GemmArgs {
   // accumulate); a reduce pass forms the result
   int k_splits;
   int split_stages;
+  // clock capture (the timing facility), or null: each workgroup writes
+  // (shader clock, real-time counter) at its start and end to
+  // clk[4 * blockIdx.x .. +3] while blockIdx.x < clk_slots
+  unsigned long long* clk;
+  int clk_slots;
 };
 
 struct EpiArgs {

@@ -731,6 +731,12 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   const int wm = wave >> 1, wn = wave & 1;
   GemmArgs g = g_in;
   EpiArgs e = e_in;
+  // clock capture: stored at once (nothing held in registers across the loop)
+  const bool clk_on = g.clk != nullptr && (int)blockIdx.x < g.clk_slots;
+  if (clk_on && tid == 0) {
+    g.clk[4 * blockIdx.x] = __builtin_amdgcn_s_memtime();
+    g.clk[4 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+  }
   int bm, bn;
   int kt0 = 0;                              // first stage of this workgroup's K range
   int nk = (g.K + kStep - 1) / kStep;       // its number of stages
@@ -1323,6 +1329,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
       for (int w = 0; w < 4; ++w) m = __builtin_fmaxf(m, wmax[w]);
       e.amax_part[blockIdx.x] = m;
     }
+  }
+  if (clk_on && tid == 0) {
+    g_in.clk[4 * blockIdx.x + 2] = __builtin_amdgcn_s_memtime();
+    g_in.clk[4 * blockIdx.x + 3] = __builtin_amdgcn_s_memrealtime();
   }
 }
 
