@@ -102,7 +102,11 @@ def fp8_scales(x_scale_inv=None, w1_scale_inv=None, w2_scale_inv=None, a_amax=No
                    _ptr(dy_scale_inv),
                    None if dH_history is None else ctypes.pointer(dH_history.struct),
                    _ptr(dH_scale_inv))
-    sc._keep = (a_history, dH_history)
+    # the struct holds raw device pointers: keep the tensors they point into
+    # alive as long as the struct (a freed scale tensor's memory would be
+    # handed to the next allocation and the call would read that instead)
+    sc._keep = (x_scale_inv, w1_scale_inv, w2_scale_inv, a_amax, a_scale_inv, a_history,
+                dy_scale_inv, dH_history, dH_scale_inv)
     return sc
 
 

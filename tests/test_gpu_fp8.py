@@ -150,3 +150,43 @@ def test_fp8_amax_leaves_out_padding_rows(tp):
     amax = float(out["a_amax"].cpu()[0])
     say(f"  amax gpu {amax:.6g} oracle {amax_ref:.6g}")
     assert abs(amax - amax_ref) <= TOL["bf16"] * amax_ref
+
+
+def test_fp8_scales_struct_keeps_its_tensors_alive(tp):
+    """A tpmlp_fp8_scales struct built from scale tensors that nothing else
+    references: the struct keeps them alive, so new allocations made before
+    the call cannot take their memory (regression: the benchmark's FP8 step
+    once read a freed x_scale_inv slot holding another tensor's 1.0)."""
+    T, H, Fs = 256, 512, 256
+    w = synth.WORKLOADS[5]
+    inp = synth.make_rank_inputs(w, tokens=T, hidden=H, ffn_shard=Fs, seed_base=77)
+    desc = tp.make_desc(T, H, Fs, act="gelu", dtype="e4m3", has_bias=True)
+    codes = {}
+
+    def scales():
+        sinv = {}
+        for k in ("x", "W1", "W2"):
+            codes[k], _, sinv[k] = tp.quantize_e4m3(inp[k].cuda())
+        return tp.fp8_scales(sinv["x"], sinv["W1"], sinv["W2"], a_history=tp.DelayedScaling(2))
+
+    sc = scales()
+    torch.cuda.synchronize()
+    import gc
+    gc.collect()
+    junk = [torch.full((1,), 1.0, device="cuda") for _ in range(64)]   # reuse freed slots
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    h = torch.empty((T, Fs), dtype=torch.bfloat16, device="cuda")
+    a = torch.empty((T, Fs), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(tp.workspace_size(desc, tp.CALL_FWD), dtype=torch.uint8, device="cuda")
+    tp.tpmlp_fwd(desc, codes["x"], codes["W1"], inp["b1"].cuda(), codes["W2"], y, h, a, fp8=sc,
+                 workspace=ws)
+    torch.cuda.synchronize()
+    deq = {}
+    for k in ("x", "W1", "W2"):
+        rc, _, _, rsinv = oracle.quantize_e4m3(inp[k].numpy())
+        deq[k] = oracle.dequantize_e4m3(rc, rsinv)
+    ref = oracle.rank_forward(deq["x"], deq["W1"], oracle.to_f64(inp["b1"]), deq["W2"], "gelu")
+    e_h = rel_err(h.cpu(), ref["h"])
+    say(f"  rel error h={e_h:.2e}")
+    assert e_h <= TOL["bf16"]
+    del junk
