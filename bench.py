@@ -827,7 +827,10 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     dom = tp.timing_collect()[dominant]
-    dom_mhz = tp.timing_clock_mhz(dominant)
+    # every GEMM kernel's clock over the timed steps (the clock capture covers
+    # all of them; events bracket the dominant kernel only)
+    timed_mhz = {k: round(tp.timing_clock_mhz(k), 1) for k in per}
+    dom_mhz = timed_mhz.get(dominant, 0.0)
     tp.timing_enable(False)
     spans = span_stats(ev)
     cold = None
@@ -849,10 +852,10 @@ def main():
     achieved = job.gemm_flops(dominant) / (dom_ms * 1e-3) / 1e12
     peak = PEAK[job.dtype]
     # measured shader clocks (the library's workgroups read the clock and
-    # real-time counters): each GEMM kernel's in the warm-up probe, weighted
-    # by its time, for the step; the dominant kernel's over the timed steps
-    gemm_ms = {k: v[1] for k, v in per.items() if probe_mhz.get(k, 0) > 0}
-    step_mhz = (sum(probe_mhz[k] * t for k, t in gemm_ms.items()) / sum(gemm_ms.values())
+    # real-time counters) over the timed steps: the step's is each GEMM
+    # kernel's weighted by its share of the step's time (from the warm-up)
+    gemm_ms = {k: v[1] for k, v in per.items() if timed_mhz.get(k, 0) > 0}
+    step_mhz = (sum(timed_mhz[k] * t for k, t in gemm_ms.items()) / sum(gemm_ms.values())
                 if gemm_ms else None)
     at_clock = lambda mhz: None if not mhz else N_CU * FLOP_PER_CU_CLK[job.dtype] * mhz * 1e-6
     line = {
@@ -872,6 +875,7 @@ def main():
         "pct_of_peak": round(100 * value / peak, 2),
         "clock_mhz": {"step": None if step_mhz is None else round(step_mhz, 1),
                       "dominant_kernel": round(dom_mhz, 1) if dom_mhz else None,
+                      "per_kernel": timed_mhz,
                       "per_kernel_warmup": probe_mhz,
                       "source": "shader clock counter over the 100 MHz real-time counter, "
                                 "per workgroup of the GEMM kernels"},

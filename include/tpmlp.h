@@ -396,12 +396,13 @@ tpmlp_status tpmlp_timing_enable(int32_t enable, const char* name_filter);
 /* Fills up to `cap` entries; returns the number of distinct kernel names (or -1 on error). */
 int32_t tpmlp_timing_collect(const char** names, int64_t* counts, double* total_ms, int32_t cap);
 /*
- * Mean shader clock in MHz of the bf16/FP8 GEMM launches named `name` among
- * those timed before the last tpmlp_timing_collect (0 if none): while the
- * facility is enabled each such workgroup reads the shader clock counter and
- * the 100 MHz real-time counter at its start and end into a fixed device
- * array of 32768 workgroup entries (launches past that are timed without
- * it); the clock is the sum of cycles over the sum of real-time ticks.
+ * Mean shader clock in MHz of the bf16/FP8 GEMM launches named `name` made
+ * while the facility was enabled, up to the last tpmlp_timing_collect (0 if
+ * none; every such launch counts, whatever the name filter selects for
+ * events): each of their workgroups reads the shader clock counter and the
+ * 100 MHz real-time counter at its start and end into a fixed device array
+ * of 131072 workgroup entries, 4 MiB (launches past that go without); the
+ * clock is the sum of cycles over the sum of real-time ticks.
  * tpmlp_timing_enable clears the array (a blocking memset; where that fails
  * the facility times with events only), so the facility is not for use
  * under graph capture.

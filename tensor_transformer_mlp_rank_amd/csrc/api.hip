@@ -44,13 +44,14 @@ hipError_t take_event(hipEvent_t* ev) {
   return hipEventCreate(ev);
 }
 
-// Clock capture of the MFMA GEMM launches the facility times: each workgroup
-// writes (shader clock counter, real-time counter) at its start and end into
-// 4 slots of this array (one range of workgroups per launch, handed out in
-// launch order until the array is full). tpmlp_timing_collect turns them into
-// each kernel's mean shader clock: the sum of its workgroups' cycles over the
-// sum of their real-time ticks, at the counter's 100 MHz.
-constexpr int kClockSlots = 32768;
+// Clock capture of the MFMA GEMM launches while the facility is enabled
+// (every such launch, whatever the name filter selects for events): each
+// workgroup writes (shader clock counter, real-time counter) at its start and
+// end into 4 slots of this array (one range of workgroups per launch, handed
+// out in launch order until the array is full). tpmlp_timing_collect turns
+// them into each kernel's mean shader clock: the sum of its workgroups'
+// cycles over the sum of their real-time ticks, at the counter's 100 MHz.
+constexpr int kClockSlots = 131072;
 __device__ __align__(256) unsigned long long clock_slots[4 * kClockSlots];
 struct ClockRec {
   const char* name;
@@ -61,15 +62,12 @@ int g_clk_used = 0;
 std::vector<ClockRec> g_clk_recs;
 std::vector<std::pair<std::string, double>> g_clk_mhz;  // from the last collect
 
-bool timing_selects(const char* name) {
-  return g_timing && (g_filter.empty() || strstr(name, g_filter.c_str()) != nullptr);
-}
 
 // Points the launch's clock capture at the next free slots (or leaves it off).
 void clock_attach(const char* name, GemmArgs& g, int64_t nb) {
   g.clk = nullptr;
   g.clk_slots = 0;
-  if (!timing_selects(name) || !g_clk_dev || nb <= 0 || g_clk_used + nb > kClockSlots) return;
+  if (!g_timing || !g_clk_dev || nb <= 0 || g_clk_used + nb > kClockSlots) return;
   g.clk = g_clk_dev + 4 * (int64_t)g_clk_used;
   g.clk_slots = (int)nb;
   g_clk_recs.push_back({name, g_clk_used, (int)nb});
