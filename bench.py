@@ -12,6 +12,10 @@ oracle on the whole workload (max|gpu - oracle| / max|oracle| within 1e-5
 for fp32, 2e-2 for bf16, 6e-2 for e4m3) before anything is reported; on a
 miss the script exits with status 3 and prints no line.
 
+The timed steps follow untimed warm-up steps (by default as many as fill
+100 ms, at least 30: the shader clock ramps up over the first tens of
+milliseconds of load), so the line reports the sustained rate.
+
 Then prints one JSON line: TFLOP/s of the whole step (algorithmic FLOPs
 6*T*H*Fs*(G+1) over the measured time), its fraction of the vendor peak and
 of the peak at the shader clock the kernels measured themselves, the parity
@@ -31,6 +35,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -49,6 +54,12 @@ TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 6e-2}
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 HISTORY_LEN = 1024  # delayed-scaling amax history (the common default length)
+# default warm-up: the shader clock ramps up over the first tens of
+# milliseconds under load (a 400-step run of the 8192-hidden shard settles
+# after about 25 steps, 60 ms, and stays there), so the untimed steps fill
+# WARMUP_S of GPU time
+WARMUP_S = 0.1
+MIN_WARMUP = 30
 
 
 def traffic_file(name: str) -> str:
@@ -666,8 +677,11 @@ def moe_cpu_baseline(w, counts, rows: int, repeats: int = 3, gpu=None) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: as many as take "
+                         f"{WARMUP_S * 1e3:.0f} ms, at least {MIN_WARMUP}: the shader clock "
+                         "ramps up over the first tens of milliseconds of load)")
     ap.add_argument("--workload", type=int, default=3,
                     help="workload id (3: H=8192 TP=8 MLP shard; 6, 7: attention projections; "
                          "8, 9: mixture-of-experts expert MLPs)")
@@ -800,7 +814,18 @@ def main():
     # warm-up; its last (up to three) steps time every kernel, to find the
     # dominant one (the first step, with its one-off costs, only if it is the
     # only one)
-    nwarm = max(args.warmup, 1)
+    if args.warmup is None:
+        # two steps to estimate a step's time, then as many as fill WARMUP_S
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        per_step = (time.perf_counter() - t) / 2
+        args.warmup = max(MIN_WARMUP, 2 + math.ceil(max(WARMUP_S - 2 * per_step, 0.0) / per_step))
+        nwarm = args.warmup - 2
+    else:
+        nwarm = max(args.warmup, 1)
     probe_from = max(1, nwarm - 3) if nwarm > 1 else 0
     for i in range(nwarm):
         if i == probe_from:

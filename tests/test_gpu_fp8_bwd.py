@@ -302,9 +302,11 @@ def _fp8_block(tp, T, H, Fs, seed, prior=False):
 
 # (200, 384, 272): with 128-element FP8 stages, T=200 ragged with an even
 # number of stages (the weight gradients), H=384 a whole but odd number and
-# Fs=272 a ragged odd one (each starting with the zero stage)
+# Fs=272 a ragged odd one (each starting with the zero stage). (200, 2304,
+# 144): dW1 has 9 tile columns, more than its two stages, so most of the
+# workgroups own no stage of db1's column sum
 @pytest.mark.parametrize("T,H,Fs", [(300, 528, 272), (64, 256, 512), (37, 48, 32), (513, 1040, 400),
-                                    (200, 384, 272)])
+                                    (200, 384, 272), (200, 2304, 144)])
 def test_fp8_block_small_and_ragged(tp, T, H, Fs):
     _fp8_block(tp, T, H, Fs, seed=900 + T)
 

@@ -98,6 +98,8 @@ CASES = [
     ([1], 64, 16, "gelu", False),
     (list(range(0, 64 * 7, 7)), 256, 64, "gelu", True),
     ([1024, 768], 512, 512, "swiglu", False),
+    # 9 tile columns in each expert's dW1, more than its stages
+    ([130, 0, 64, 7], 2304, 80, "gelu", True),
 ]
 
 

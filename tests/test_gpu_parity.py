@@ -109,6 +109,25 @@ def test_block_more_tiles_than_workgroups(tp, act):
     check(gpu, ref, "bf16", ALL)
 
 
+@pytest.mark.parametrize("T,H,Fs", [(192, 2048, 256), (200, 2160, 272), (136, 16400, 64)])
+def test_db1_wide_dW1(tp, T, H, Fs):
+    """db1 fused into the dW1 product where dW1 has 8 or more tile columns
+    (the tile columns share out the k-stages, column bn taking stages bn,
+    bn + tiles_n, ...): 8 and 9 columns, and 65, more than the product's
+    stages, so that most workgroups own none; an odd whole number of stages
+    (T=192, the zero stage), a ragged one (T=200, T=136), and split-K where
+    the grid is small. Accumulates into prior gradients; every output
+    compared element by element."""
+    w = synth.WORKLOADS[2]
+    inp = synth.make_rank_inputs(w, tokens=T, hidden=H, ffn_shard=Fs, seed_base=640 + T)
+    prior = {"dW1": synth.grad_init(640, (Fs, H), 1),
+             "db1": synth.grad_init(640, (Fs,), 2),
+             "dW2": synth.grad_init(640, (H, Fs), 3)}
+    gpu = gpu_block(tp, inp, "gelu", "bf16", True, accumulate_into=prior)
+    ref = oracle_block(inp, "gelu", True, prior=prior)
+    check(gpu, ref, "bf16", ALL)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("act", ["gelu", "swiglu"])
 def test_wgrad_accumulate(tp, dtype, act):
@@ -124,6 +143,35 @@ def test_wgrad_accumulate(tp, dtype, act):
     gpu = gpu_block(tp, inp, act, dtype, has_bias, accumulate_into=prior)
     ref = oracle_block(inp, act, has_bias, prior=prior)
     check(gpu, ref, dtype, ("dW1", "db1", "dW2"))
+
+
+@pytest.mark.parametrize("T,H,Fs,act", [
+    (1024, 272, 144, "gelu"),     # 16 stages
+    (960, 528, 400, "swiglu"),    # 15 stages after the zero stage
+    (1088, 256, 256, "gelu"),     # 17 stages after the zero stage
+    (1500, 1040, 528, "gelu"),    # several tiles, ragged in every dimension
+])
+def test_wgrad_accumulate_long_k(tp, T, H, Fs, act):
+    """Weight gradients over 15 to 24 stages of tokens accumulating into
+    prior gradients of both signs and of a magnitude well above the
+    products, compared element by element, with rows and columns past the
+    ends of dW1 and dW2."""
+    w = synth.WORKLOADS[4 if act == "swiglu" else 2]
+    inp = synth.make_rank_inputs(w, tokens=T, hidden=H, ffn_shard=Fs, seed_base=71 + T % 13)
+    has_bias = act == "gelu"
+    G = 2 if act == "swiglu" else 1
+    prior = {"dW1": synth.grad_init(71, (G * Fs, H), 1) * 50,
+             "db1": synth.grad_init(71, (G * Fs,), 2) * 50 if has_bias else None,
+             "dW2": synth.grad_init(71, (H, Fs), 3) * 50}
+    gpu = gpu_block(tp, inp, act, "bf16", has_bias, accumulate_into=prior)
+    ref = oracle_block(inp, act, has_bias, prior=prior)
+    check(gpu, ref, "bf16", ("dW1", "db1", "dW2"))
+    # the sums without the prior, to the same bar: the products are not lost
+    # in the prior's magnitude
+    for k in ("dW1", "dW2"):
+        got = oracle.to_f64(gpu[k]) - oracle.to_f64(prior[k])
+        want = ref[k] - oracle.to_f64(prior[k])
+        assert rel_err(got, want) <= TOL["bf16"], k
 
 
 def test_zero_tokens(tp):
