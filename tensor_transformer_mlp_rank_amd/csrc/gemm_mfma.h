@@ -18,13 +18,16 @@
 //
 // Work decomposition: 256 threads = 4 waves in a 2 x 2 grid, one wave per
 // SIMD. Each wave owns a 128 x 128 sub-tile: for bf16, 8 x 8 accumulator
-// blocks of the 16x16x32 MFMA (v_mfma_f32_16x16x32_bf16); for FP8, 4 x 4
-// blocks of the 32x32x64 one (v_mfma_scale_f32_32x32x64_f8f6f4 with unit
-// scales, its format bits choosing E4M3 or E5M2 per operand). Either way 256
-// fp32 accumulator registers per lane (AGPRs). Per FLOP this reads half the
-// LDS bytes of a 128 x 64 wave tile. Under the chip's power limit the 16x16
-// bf16 MFMA sustains a higher clock than the 32x32 one (an MFMA-only loop
-// with random operands: 1.97 against 1.76 GHz, 8% more FLOP/s).
+// blocks of the 16x16x32 MFMA (v_mfma_f32_16x16x32_bf16); for FP8 with two
+// K-major operands (the forward products), 8 x 8 blocks of the 16x16x128
+// one (v_mfma_f32_16x16x128_f8f6f4, E4M3 x E4M3); for the other FP8
+// products, 4 x 4 blocks of the 32x32x64 one (v_mfma_scale_f32_32x32x64_f8f6f4
+// with unit scales, its format bits choosing E4M3 or E5M2 per operand).
+// Either way 256 fp32 accumulator registers per lane (AGPRs). Per FLOP this
+// reads half the LDS bytes of a 128 x 64 wave tile. Under the chip's power
+// limit the 16x16 MFMAs sustain a higher clock than the 32x32 ones (MFMA-only
+// loops with random operands: bf16 1.97 against 1.76 GHz, 8% more FLOP/s;
+// FP8 2.18 against 2.01 GHz, 8% more).
 //
 // Pipeline: K advances 128 bytes per row per stage (64 bf16 / 128 e4m3
 // elements, whole cache lines per request); a stage holds a 32 KiB A tile and
@@ -34,7 +37,7 @@
 // with buffer_load_dwordx4 ... lds (no staging registers, no LDS store
 // instructions); the buffer resource's range check turns reads past a
 // tensor's end into zeros. Within a stage (see stage_iter16 for bf16,
-// stage_iter and stage_iter_rolling for FP8) the MFMAs run from registers
+// stage_f16 and stage_iter_rolling for FP8) the MFMAs run from registers
 // while the LDS reads for the next k-steps and the loads of stage k+2 are
 // interleaved between them; barriers inside the stage hand the buffers over
 // (bf16: one when A is free, one when the next stage has landed). Each is a
@@ -429,6 +432,28 @@ __device__ __forceinline__ i32x8 frag_k_e4m3(const char* stage, int wrow, int la
   return r;
 }
 
+// e4m3, K-major tile, operand of the 16x16x128 MFMA: lane l takes row
+// wrow + 16 R + (l & 15), bytes 32 (l >> 4) .. +31 of the stage's 128
+// (chunks 2 (l >> 4) and 2 (l >> 4) + 1). As frag_k_bf16, the swizzle
+// depends on (l & 15) only, so the tile T and the row block R go into the
+// offset field.
+template <int T, int R>
+__device__ __forceinline__ i32x8 frag_k_e4m3_16(const char* stage, int wrow, int lane) {
+  const int row = wrow + (lane & 15);
+  const int c0 = (lane >> 4) << 1;
+  const uint32_t base = (uint32_t)(uintptr_t)(const TPMLP_LDS char*)stage + row * kRowBytes;
+  const uint32_t a0 = base + ((c0 ^ kswz(row)) << 4), a1 = base + (((c0 + 1) ^ kswz(row)) << 4);
+  constexpr int kOff = T + R * 16 * kRowBytes;
+  static_assert(kOff >= 0 && kOff < 65536, "DS offset field");
+  u32x4 lo, hi;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(lo) : "v"(a0), "i"(kOff));
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(hi) : "v"(a1), "i"(kOff));
+  i32x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
 // FP8 (either format), MN-major tile [128 k-rows][256 bytes]: the operand
 // of frag_k_e4m3 (lane l: column col0 + l%32, k 64 ks + 32 (l/32) .. +31)
 // through four 8-bit transpose reads. ds_read_b64_tr_b8 gives lane j of each
@@ -577,7 +602,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e, 
     if constexpr (LOADS) {
       if ((fm & 1) == 0) load_slabs(fm);
     }
-    if constexpr (IS_FP8) {
+    if constexpr (sizeof(acc[0][0]) == 64) {
       // 32x32 blocks: register j of block (fm, fn) is row 8 (j/4) + 4 (l/32)
       // + j%4, column 32 fn + l%32
 #pragma unroll
@@ -881,15 +906,19 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
 
   // accumulators: bf16, 8 x 8 blocks of the 16x16x32 MFMA (4 registers
   // each); FP8, 4 x 4 blocks of the 32x32x64 one (16 registers each)
-  constexpr int kAb = IS_FP8 ? 4 : 8;
-  using AccV = typename std::conditional<IS_FP8, f32x16, f32x4>::type;
+  // FP8 with two K-major operands runs the 16x16x128 MFMA (k-step = stage):
+  // bf16-like 8 x 8 blocks of 16x16; other FP8 products the 32x32x64 one
+  constexpr bool kF16 = IS_FP8 && A_K && B_K;
+  constexpr bool kAcc32 = IS_FP8 && !kF16;
+  constexpr int kAb = kAcc32 ? 4 : 8;
+  using AccV = typename std::conditional<kAcc32, f32x16, f32x4>::type;
   AccV acc[kAb][kAb];
 #pragma unroll
   for (int i = 0; i < kAb; ++i)
 #pragma unroll
     for (int j = 0; j < kAb; ++j)
 #pragma unroll
-      for (int r = 0; r < (IS_FP8 ? 16 : 4); ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < (kAcc32 ? 16 : 4); ++r) acc[i][j][r] = 0.f;
 
   // fused column sum: thread t owns 8 columns (chunk t%32) of k-rows t/32 + 8j.
   // The k-stages are shared out over the tile columns: the workgroup in tile
@@ -908,7 +937,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   for (int j = 0; j < kCs; ++j) csum[j] = 0.f;
 
   // A stage has two MFMA k-steps (bf16: 32 elements each, 64 MFMAs of
-  // 16x16x32; e4m3: 64 each, 16 MFMAs of 32x32x64). The fragments of k-step
+  // 16x16x32; FP8 with an MN-major operand: 64 each, 16 MFMAs of 32x32x64;
+  // the 16x16x128 schedule keeps its own fragments). The fragments of k-step
   // ks live in register slot ks: kFr per operand (bf16: A rows 128 wm + 16 f,
   // B rows 128 wn + 16 f, f = 0..7; FP8: 32-row blocks, f = 0..3).
   constexpr int kKs = 2;
@@ -940,8 +970,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   };
 
 
+  // (the 16x16x128 schedule issues its own MFMAs)
   auto mma = [&](int i) __attribute__((always_inline)) {
-    if constexpr (IS_FP8) {
+    if constexpr (kF16) {
+    } else if constexpr (IS_FP8) {
       // MFMA i of a stage: k-step i/16, row block (i/4)%4, column block i%4
       const int ks = i >> 4, fm = (i >> 2) & 3, fn = i & 3;
       acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -1003,67 +1035,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // loads in flight stays uniform, one wait count and no branches. Their
   // offsets fall outside the resources (no memory traffic), except for
   // folded K-major loaders, which read whatever lies behind the rows.
-  //
-  // FP8 stage kt with two K-major operands (32 MFMAs of 32x32x64 issued from
-  // registers, two k-steps; a scheduling barrier after every slot pins the
-  // interleave):
-  //   first quarter   MFMAs of k-step 0; reads of the stage's k-step 1
-  //   barrier         every wave has finished reading stage kt, so its
-  //                   buffer is free, and stage kt+1 has landed (this wave's
-  //                   loads: vmcnt(0); every wave's: the barrier)
-  //   middle half     MFMAs; the 16 loads of stage kt+2 into stage kt's
-  //                   buffer, one per slot
-  //   last quarter    MFMAs of k-step 1; reads of stage kt+1's k-step 0
-  // One barrier per stage: the loads of stage kt+1 have the last quarter of
-  // stage kt-1 and the first quarter of stage kt to land.
-  constexpr int kMma = 16 * kKs;
-  constexpr int kQ = kMma / 4;           // slots per quarter
-  constexpr int kHalfKs = kKs / 2;       // k-steps read per quarter
-  constexpr int kReadsQ = 8 * kHalfKs;   // fragments read per quarter
-  constexpr int kDmaEvery = (kMma / 2) / 16;
-  auto stage_iter = [&](int kt, auto FAST, auto PAR) __attribute__((always_inline)) {
-    const auto PAR1 = next_parity(PAR);  // stage kt+1
-    // Fragment reads are asm (not tracked by the compiler), two instructions
-    // per fragment. The last quarter read all of k-step 0, A0..3 then B0..3;
-    // MFMA i < 4 needs B_i, followed by three fragment reads (six
-    // instructions, counting this quarter's reads issued since), so a wait for
-    // at most 6 in flight precedes each of the first four MFMAs.
-    // reads of quarter slot q (kReadsQ fragments over kQ slots) of k-steps
-    // ks0, ks0 + 1
-    auto reads_at = [&](auto PR, auto Q, auto KS0) __attribute__((always_inline)) {
-      constexpr int q = decltype(Q)::value, ks0 = decltype(KS0)::value;
-      if constexpr (kReadsQ >= kQ) {
-        static_for<kReadsQ / kQ>([&](auto R) {
-          constexpr int j = q * (kReadsQ / kQ) + decltype(R)::value;
-          read_one(PR, IC<ks0 + j / 8>{}, IC<j & 7>{});
-        });
-      } else if constexpr (q % (kQ / kReadsQ) == 0) {
-        constexpr int j = q / (kQ / kReadsQ);
-        read_one(PR, IC<ks0 + j / 8>{}, IC<j & 7>{});
-      }
-    };
-    static_for<kQ>([&](auto I) {
-      if constexpr (decltype(I)::value < 4) wait_lds<6>();
-      mma(decltype(I)::value);
-      reads_at(PAR, I, IC<kHalfKs>{});
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    // the stage's one barrier: every wave is done reading stage kt (its
-    // buffer is free) and has stage kt+1 in LDS (its loads, issued in the
-    // middle half of stage kt-1, are the only ones in flight: vmcnt(0))
-    wait_and_barrier<0>();
-    static_for<2 * kQ>([&](auto I) {
-      constexpr int i = kQ + decltype(I)::value;
-      mma(i);
-      if constexpr ((i - kQ) % kDmaEvery == kDmaEvery - 1) issue_one(kt + kStages, (i - kQ) / kDmaEvery, FAST);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    static_for<kQ>([&](auto Q) {
-      mma(3 * kQ + decltype(Q)::value);
-      reads_at(PAR1, Q, IC<0>{});
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
+  constexpr int kMma = 16 * kKs;  // MFMAs per stage (FP8, 32x32x64)
 
   // FP8 stage kt with an MN-major operand (32 slots in two groups of 16,
   // group q issuing the MFMAs of k-step q): the 8 fragments of a k-step are
@@ -1185,6 +1157,58 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     });
   };
 
+  // FP8 stage kt with two K-major operands: 64 slots of one 16x16x128 MFMA
+  // (a stage is one k-step; row block r = i / 8, column block c = i % 8 of
+  // the wave tile). The B fragments of a stage are read during the stage
+  // before (gb[PAR]); the A fragments roll through three register sets (A_r
+  // in ga[r % 3]), each read seven slots before its row's first MFMA.
+  //   slots 0, 2, 4, 6       A loads 4..7 of stage kt+1
+  //   slot 8r + 1            A_{r+1} read (r = 0..6)
+  //   barrier before slot 8  every wave is done with stage kt-1 (the B tile of
+  //                          this buffer is free) and has stage kt+1's B tile
+  //                          (all but its eight A loads done)
+  //   slots 9, 11, .., 23    B loads of stage kt+2
+  //   slots 10, 16, .., 52   reads of stage kt+1's B fragments
+  //   barrier before slot 56 every wave has read A_7 (the A tile is free) and
+  //                          has stage kt+1's A tile (all but the B loads)
+  //   slot 57                A_0 of stage kt+1 read
+  //   slots 58..61           A loads 0..3 of stage kt+2
+  // A load has at least 48 slots to land; the waits before rows 2..6 let the
+  // one B fragment read issued since A_{r+1} stay in flight.
+  i32x8 ga[3], gb[2][8];
+  auto read16 = [&](auto PR, auto IS_B, auto IDX) __attribute__((always_inline)) {
+    constexpr int po = ParityOffset<decltype(PR)>::value;
+    constexpr int idx = decltype(IDX)::value;
+    if constexpr (decltype(IS_B)::value)
+      gb[decltype(PR)::value][idx] = frag_k_e4m3_16<po, idx>(smem + kTileB0, 128 * wn, lane);
+    else
+      ga[idx % 3] = frag_k_e4m3_16<po, idx>(smem, 128 * wm, lane);
+  };
+  auto stage_f16 = [&](int kt, auto FAST, auto PAR) __attribute__((always_inline)) {
+    const auto PAR1 = next_parity(PAR);  // stage kt+1
+    constexpr int par = decltype(PAR)::value;
+    wait_lds();  // this stage's B fragments and A_0 (read in the last)
+    asm volatile("s_nop 1");  // as in stage_iter16
+    static_for<64>([&](auto I) {
+      constexpr int i = decltype(I)::value, r = i >> 3, c = i & 7;
+      if constexpr (i == 8 || i == 56) wait_and_barrier<8>();
+      if constexpr (i > 8 && i < 56 && c == 0) wait_lds<2>();
+      {
+        auto& d = acc[r][c];
+        auto& a = ga[r % 3];
+        auto& b = gb[par][c];
+        asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+      }
+      if constexpr (c == 1 && r < 7) read16(PAR, std::false_type{}, IC<r + 1>{});
+      if constexpr (i >= 10 && i <= 52 && (i - 10) % 6 == 0) read16(PAR1, std::true_type{}, IC<(i - 10) / 6>{});
+      if constexpr (i == 57) read16(PAR1, std::false_type{}, IC<0>{});
+      if constexpr (i < 8 && (i & 1) == 0) issue_one(kt + 1, 4 + (i >> 1), FAST);
+      if constexpr (i >= 9 && i <= 23 && (i & 1) == 1) issue_one(kt + 2, 8 + ((i - 9) >> 1), FAST);
+      if constexpr (i >= 58 && i <= 61) issue_one(kt + 2, i - 58, FAST);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
   // prologue: stages 0 and 1 in flight; stage 0's first k-steps in registers.
   // A front pad stage is zeros written here with LDS stores (its A and B
   // tiles in buffer 0, 256 bytes per thread): no load of it is issued, and
@@ -1199,12 +1223,17 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   } else {
     issue(0);
   }
-  issue(1);
-  wait_and_barrier<16>();
-  // FP8: the rolling schedule pays off where a transpose-read operand makes
-  // the reads costly; with two K-major operands the quarter schedule measured
-  // slightly faster.
-  constexpr bool kRolling = !A_K || !B_K;
+  if constexpr (kF16) {
+    // stage 1: its B tile, then A loads 0..3 (the first stage issues 4..7)
+#pragma unroll
+    for (int j = 8; j < 16; ++j) issue_one(1, j, std::false_type{});
+#pragma unroll
+    for (int j = 0; j < 4; ++j) issue_one(1, j, std::false_type{});
+    wait_and_barrier<12>();
+  } else {
+    issue(1);
+    wait_and_barrier<16>();
+  }
   // The main loop runs two stages per iteration, even ones in buffer 0 and odd
   // ones in buffer 1, so each read's stage offset is an immediate and the
   // per-lane read addresses stay the same from stage to stage. An odd count
@@ -1263,17 +1292,27 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     static_for<kFr>(frag_keep);
   };
-  if constexpr (!IS_FP8) {
+  // the 16x16x128 schedule's reads in flight at its fences: stage 0's (or
+  // the stage past the end's) B fragments and A_0
+  auto frag_fence16 = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    static_for<8>([&](auto I) {
+      auto& rb = gb[0][decltype(I)::value];
+      asm volatile("" : "+v"(rb));
+    });
+    auto& ra = ga[0];
+    asm volatile("" : "+v"(ra));
+  };
+  if constexpr (kF16) {
+    static_for<8>([&](auto J) { read16(IC<0>{}, std::true_type{}, J); });
+    read16(IC<0>{}, std::false_type{}, IC<0>{});
+    frag_fence16();
+    main_loop(stage_f16);
+    frag_fence16();
+  } else if constexpr (!IS_FP8) {
     static_for<2 * kFr>([&](auto J) { read_one(IC<0>{}, IC<0>{}, J); });
     frag_fence();
     main_loop(stage_iter16);
-  } else if constexpr (!kRolling) {
-    static_for<kReadsQ>([&](auto J) {
-      constexpr int j = decltype(J)::value;
-      read_one(IC<0>{}, IC<j / 8>{}, IC<j & 7>{});
-    });
-    frag_fence();
-    main_loop(stage_iter);
   } else {
     static_for<8 * (kKs - 1)>([&](auto J) {
       constexpr int j = decltype(J)::value;
@@ -1282,8 +1321,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     frag_fence();
     main_loop(stage_iter_rolling);
   }
-  frag_fence();
-  if constexpr (!IS_FP8) {
+  if constexpr (!kF16) frag_fence();
+  if constexpr (!kAcc32) {
     // the last MFMAs (asm, unseen by the compiler's hazard checks) complete
     // before any instruction reads their accumulators
     asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
