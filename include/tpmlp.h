@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 7
+#define TPMLP_ABI_VERSION 8
 
 typedef enum {
   TPMLP_OK = 0,
@@ -87,7 +87,12 @@ typedef enum {
 
 typedef enum { TPMLP_F32 = 0, TPMLP_BF16 = 1, TPMLP_E4M3 = 2 } tpmlp_dtype;
 typedef enum { TPMLP_ACT_GELU_TANH = 0, TPMLP_ACT_SWIGLU = 1 } tpmlp_act;
-typedef enum { TPMLP_CALL_FWD = 0, TPMLP_CALL_DGRAD = 1, TPMLP_CALL_WGRAD = 2 } tpmlp_call;
+typedef enum {
+  TPMLP_CALL_FWD = 0,
+  TPMLP_CALL_DGRAD = 1,
+  TPMLP_CALL_WGRAD = 2,
+  TPMLP_CALL_WGRAD_RECOMPUTE = 3
+} tpmlp_call;
 
 /* Problem description (host memory). */
 typedef struct tpmlp_desc {
@@ -151,7 +156,9 @@ typedef struct tpmlp_fp8_scales {
  * fp32 partial sums of a split along K (optional: with fewer bytes the
  * products run unsplit, and the call needs only the db1 partials). Split
  * products are summed in a fixed order, so results stay reproducible, but
- * differ in rounding from unsplit ones.
+ * differ in rounding from unsplit ones. TPMLP_CALL_WGRAD_RECOMPUTE: the
+ * recomputed activation (T * Fs elements, rounded up to 256 bytes) plus the
+ * weight gradient's workspace. Returns 0 for an unknown call.
  */
 size_t tpmlp_workspace_size(const tpmlp_desc* desc, int32_t call);
 
@@ -210,6 +217,34 @@ tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* desc, const void* dy, const void*
                              const void* a_saved, const void* dH, float* dW1, float* db1,
                              float* dW2, int32_t accumulate, const tpmlp_fp8_scales* fp8,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Weight gradients with the activation recomputed instead of saved: the
+ * selective activation recomputation of the concept note "Megatron-LM /
+ * Megatron-Core" (section "Key math / How it works"), which trades a little
+ * compute for the memory of a_saved between the forward and the backward.
+ * Same arguments, results and errors as tpmlp_bwd_wgrad, with the saved
+ * pre-activation h_saved ([T, G*Fs], as tpmlp_fwd wrote it) in place of
+ * a_saved: the call first forms a = act(h_saved) in the workspace, with the
+ * forward epilogue's own function of h as stored, then runs the products of
+ * tpmlp_bwd_wgrad on it.
+ *   BF16, F32: a equals the forward's a_saved bit for bit, and so do the
+ *     results those of tpmlp_bwd_wgrad.
+ *   E4M3 (GELU): a's codes are E4M3(gelu(h) * (1 / fp8->a_scale_inv)), the
+ *     float32 factor recomputed from the dequantisation factor that the wgrad
+ *     call already takes; they match the forward's codes wherever that
+ *     factor equals the forward's (with delayed scaling the forward quantised
+ *     the float32 gelu(h) at a_history->scale, of which a_scale_inv is the
+ *     inverse).
+ * Workspace: tpmlp_workspace_size(desc, TPMLP_CALL_WGRAD_RECOMPUTE) bytes, the
+ * recomputed a (T * Fs elements, rounded up to 256 bytes) followed by
+ * tpmlp_bwd_wgrad's workspace (its split-K part optional as there).
+ */
+tpmlp_status tpmlp_bwd_wgrad_recompute(const tpmlp_desc* desc, const void* dy, const void* x,
+                                       const void* h_saved, const void* dH, float* dW1,
+                                       float* db1, float* dW2, int32_t accumulate,
+                                       const tpmlp_fp8_scales* fp8, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
 
 /*
  * tpmlp_bwd_wgrad without a workspace, for callers that cannot allocate

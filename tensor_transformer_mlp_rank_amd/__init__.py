@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libtpmlp.so")
 
 F32, BF16, E4M3 = 0, 1, 2
 GELU, SWIGLU = 0, 1
-CALL_FWD, CALL_DGRAD, CALL_WGRAD = 0, 1, 2
+CALL_FWD, CALL_DGRAD, CALL_WGRAD, CALL_WGRAD_RECOMPUTE = 0, 1, 2, 3
 
 STATUS = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_DTYPE", 4: "E_ALIGN", 5: "E_UNSUPPORTED",
           6: "E_WORKSPACE", 7: "E_HIP", 8: "E_SCRATCH"}
@@ -131,6 +131,8 @@ def _load():
     L.tpmlp_bwd_dgrad.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, psc, vp, sz, vp]
     L.tpmlp_bwd_wgrad.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, i32, psc, vp, sz, vp]
     L.tpmlp_bwd_wgrad_noalloc.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, i32, psc, vp]
+    L.tpmlp_bwd_wgrad_recompute.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, i32, psc, vp, sz,
+                                            vp]
     L.tpmlp_quantize_e4m3.argtypes = [i32, vp, i64, vp, vp, vp, vp, sz, vp]
     L.tpmlp_quantize_e5m2.argtypes = [i32, vp, i64, vp, vp, vp, vp, sz, vp]
     L.tpmlp_quantize_workspace_size.argtypes = [i64]
@@ -153,6 +155,7 @@ def _load():
     L.tpmlp_moe_workspace_size.argtypes = [pm]
     L.tpmlp_moe_workspace_size.restype = sz
     for f in ("tpmlp_fwd", "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad", "tpmlp_bwd_wgrad_noalloc",
+              "tpmlp_bwd_wgrad_recompute",
               "tpmlp_quantize_e4m3",
               "tpmlp_quantize_e5m2", "tpmlp_timing_enable", "tpmlp_attn_qkv_fwd",
               "tpmlp_attn_out_fwd", "tpmlp_attn_out_bwd_dgrad", "tpmlp_attn_out_bwd_wgrad",
@@ -250,6 +253,16 @@ def tpmlp_bwd_wgrad(desc, dy, x, a, dH, dW1, db1, dW2, accumulate=False, fp8=Non
                                _ptr(workspace), nbytes, _stream(stream)), "tpmlp_bwd_wgrad")
 
 
+def tpmlp_bwd_wgrad_recompute(desc, dy, x, h, dH, dW1, db1, dW2, accumulate=False, fp8=None,
+                              workspace=None, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sc = None if fp8 is None else ctypes.byref(fp8)
+    _check(lib.tpmlp_bwd_wgrad_recompute(ctypes.byref(desc), _ptr(dy), _ptr(x), _ptr(h),
+                                         _ptr(dH), _ptr(dW1), _ptr(db1), _ptr(dW2),
+                                         int(bool(accumulate)), sc, _ptr(workspace), nbytes,
+                                         _stream(stream)), "tpmlp_bwd_wgrad_recompute")
+
+
 def tpmlp_bwd_wgrad_noalloc(desc, dy, x, a, dH, dW1, db1, dW2, accumulate=False, fp8=None,
                             stream=None):
     sc = None if fp8 is None else ctypes.byref(fp8)
@@ -328,10 +341,12 @@ def bwd_dgrad(desc, dy, W1, W2, h, fp8=None, stream=None):
     return out
 
 
-def bwd_wgrad(desc, dy, x, a, dH, accumulate_into=None, fp8=None, stream=None):
+def bwd_wgrad(desc, dy, x, a, dH, accumulate_into=None, fp8=None, stream=None, recompute=False):
     """fp32 weight gradients. ``accumulate_into`` = dict dW1, db1, dW2 of
     existing fp32 buffers to add into (accumulate mode). For E4M3, ``fp8`` =
-    dict dy_scale_inv, x_scale_inv, a_scale_inv, dH_scale_inv."""
+    dict dy_scale_inv, x_scale_inv, a_scale_inv, dH_scale_inv. With
+    ``recompute``, ``a`` is the saved pre-activation h and the call recomputes
+    the activation from it (tpmlp_bwd_wgrad_recompute)."""
     dev = dy.device
     H, Fs = desc.hidden, desc.ffn_shard
     G = 2 if desc.act == SWIGLU else 1
@@ -341,11 +356,12 @@ def bwd_wgrad(desc, dy, x, a, dH, accumulate_into=None, fp8=None, stream=None):
         out = {"dW1": _empty((G * Fs, H), torch.float32, dev),
                "db1": _empty((G * Fs,), torch.float32, dev) if desc.has_bias else None,
                "dW2": _empty((H, Fs), torch.float32, dev)}
-    n = workspace_size(desc, CALL_WGRAD)
+    n = workspace_size(desc, CALL_WGRAD_RECOMPUTE if recompute else CALL_WGRAD)
     ws = _empty((n,), torch.uint8, dev) if n else None
     sc = None if fp8 is None else fp8_scales(**fp8)
-    tpmlp_bwd_wgrad(desc, dy, x, a, dH, out["dW1"], out.get("db1"), out["dW2"],
-                    accumulate=accumulate_into is not None, fp8=sc, workspace=ws, stream=stream)
+    call = tpmlp_bwd_wgrad_recompute if recompute else tpmlp_bwd_wgrad
+    call(desc, dy, x, a, dH, out["dW1"], out.get("db1"), out["dW2"],
+         accumulate=accumulate_into is not None, fp8=sc, workspace=ws, stream=stream)
     return out
 
 
@@ -553,7 +569,8 @@ def timing_collect(cap: int = 64) -> dict:
 
 __all__ = ["Desc", "Fp8Scales", "Fp8History", "DelayedScaling", "fp8_scales", "TpmlpError",
            "make_desc", "workspace_size", "tpmlp_fwd", "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad",
-           "tpmlp_bwd_wgrad_noalloc", "SCRATCH_BYTES",
+           "tpmlp_bwd_wgrad_noalloc", "tpmlp_bwd_wgrad_recompute", "SCRATCH_BYTES",
+           "CALL_FWD", "CALL_DGRAD", "CALL_WGRAD", "CALL_WGRAD_RECOMPUTE",
            "tpmlp_quantize_e4m3", "tpmlp_quantize_e5m2", "fwd", "bwd_dgrad", "bwd_wgrad",
            "quantize_e4m3", "quantize_e5m2", "timing_enable", "timing_collect", "timing_clock_mhz",
            "lib", "LIB_PATH",

@@ -219,8 +219,17 @@ WgradPlan wgrad_plan(const tpmlp_desc* d, bool split_ok) {
   return p;
 }
 
+// The recomputed activation a at the front of the recomputing weight-gradient
+// call's workspace: [T][Fs] of bf16, fp32 or E4M3 codes.
+size_t recompute_a_bytes(const tpmlp_desc* d) {
+  const size_t es = d->dtype == TPMLP_F32 ? 4 : d->dtype == TPMLP_BF16 ? 2 : 1;
+  return align_up((size_t)d->tokens * (size_t)d->ffn_shard * es, 256);
+}
+
 size_t workspace_bytes(const tpmlp_desc* d, int32_t call) {
   const bool fp8 = d->dtype == TPMLP_E4M3;
+  if (call == TPMLP_CALL_WGRAD_RECOMPUTE)
+    return recompute_a_bytes(d) + workspace_bytes(d, TPMLP_CALL_WGRAD);
   if (call == TPMLP_CALL_FWD && fp8) {
     // current scaling: bf16 a, then the partials; delayed scaling: partials only
     const size_t a_bytes = align_up((size_t)d->tokens * (size_t)d->ffn_shard * 2, 256);
@@ -238,6 +247,8 @@ size_t workspace_bytes(const tpmlp_desc* d, int32_t call) {
 // split-K).
 size_t workspace_min_bytes(const tpmlp_desc* d, int32_t call) {
   if (call == TPMLP_CALL_WGRAD) return wgrad_plan(d, false).colsum;
+  if (call == TPMLP_CALL_WGRAD_RECOMPUTE)
+    return recompute_a_bytes(d) + workspace_min_bytes(d, TPMLP_CALL_WGRAD);
   return workspace_bytes(d, call);
 }
 
@@ -586,7 +597,7 @@ const char* tpmlp_last_hip_error(void) { return g_last_hip_error.c_str(); }
 
 size_t tpmlp_workspace_size(const tpmlp_desc* desc, int32_t call) {
   if (check_desc(desc) != TPMLP_OK) return 0;
-  if (call < TPMLP_CALL_FWD || call > TPMLP_CALL_WGRAD) return 0;
+  if (call < TPMLP_CALL_FWD || call > TPMLP_CALL_WGRAD_RECOMPUTE) return 0;
   return workspace_bytes(desc, call);
 }
 
@@ -769,6 +780,29 @@ tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* d, const void* dy, const void* x,
   if (st != TPMLP_OK) return st;
   if ((st = check_workspace(d, TPMLP_CALL_WGRAD, ws, ws_bytes)) != TPMLP_OK) return st;
   return run_wgrad(d, dy, x, a_saved, dH, dW1, db1, dW2, accumulate, fp8, ws, ws_bytes, s);
+}
+
+tpmlp_status tpmlp_bwd_wgrad_recompute(const tpmlp_desc* d, const void* dy, const void* x,
+                                       const void* h_saved, const void* dH, float* dW1,
+                                       float* db1, float* dW2, int32_t accumulate,
+                                       const tpmlp_fp8_scales* fp8, void* ws, size_t ws_bytes,
+                                       hipStream_t s) {
+  tpmlp_status st = check_wgrad(d, dy, x, h_saved, dH, dW1, db1, dW2, accumulate, fp8);
+  if (st != TPMLP_OK) return st;
+  if ((st = check_workspace(d, TPMLP_CALL_WGRAD_RECOMPUTE, ws, ws_bytes)) != TPMLP_OK) return st;
+  // a = act(h) into the front of the workspace; the weight gradients use the rest
+  const size_t ab = recompute_a_bytes(d);
+  const Kind kind = d->dtype == TPMLP_F32 ? KIND_F32 : d->dtype == TPMLP_BF16 ? KIND_BF16 : KIND_E4M3;
+  const hipError_t err = timed(d->dtype == TPMLP_F32 ? "a_recompute.f32"
+                               : d->dtype == TPMLP_BF16 ? "a_recompute.bf16" : "a_recompute.e4m3",
+                               s, [&]() {
+    return act_recompute_launch(kind, d->act == TPMLP_ACT_SWIGLU, h_saved, d->tokens,
+                                d->ffn_shard, ws, kind == KIND_E4M3 ? fp8->a_scale_inv : nullptr,
+                                s);
+  });
+  if (err != hipSuccess) return hip_fail(err);
+  return run_wgrad(d, dy, x, ws, dH, dW1, db1, dW2, accumulate, fp8,
+                   static_cast<char*>(ws) + ab, ws_bytes - ab, s);
 }
 
 tpmlp_status tpmlp_bwd_wgrad_noalloc(const tpmlp_desc* d, const void* dy, const void* x,

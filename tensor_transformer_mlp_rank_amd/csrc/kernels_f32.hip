@@ -1,6 +1,6 @@
 // Instantiations and launchers of the fp32 (VALU) tile kernel, of the
-// E4M3 quantiser and of the reduction of the MFMA kernel's column-sum
-// partials.
+// E4M3 quantiser, of the reduction of the MFMA kernel's column-sum partials
+// and of the activation's recomputation from the saved pre-activation.
 #include "gemm_f32.h"
 #include "launch.h"
 #include "quant.h"
@@ -89,7 +89,76 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
   }
 }
 
+// a = act(h) for the weight gradients' recomputation: h is the saved
+// pre-activation [rows][G fs] (G = 2 for SwiGLU, gate then up), a goes to
+// [rows][fs] as bf16 or fp32 (OUT_E4M3 false: the type of h), or as E4M3
+// codes at the factor 1 / *scale_inv (OUT_E4M3). The activation is the
+// forward epilogue's own function of h as stored (gelu_f; silu_f(gate) * up),
+// so bf16 and fp32 results equal the forward's a bit for bit. Eight
+// consecutive elements per thread, grid-stride.
+template <typename T, bool SWIGLU, bool OUT_E4M3>
+__global__ void __launch_bounds__(256) act_recompute_kernel(const T* __restrict__ h, int64_t rows,
+                                                            int64_t fs, void* __restrict__ a,
+                                                            const float* __restrict__ scale_inv) {
+  const int64_t per_row = fs / 8;
+  const int64_t groups = rows * per_row;
+  const int64_t ldh = SWIGLU ? 2 * fs : fs;
+  float qs = 1.0f;
+  if constexpr (OUT_E4M3) qs = 1.0f / *scale_inv;
+  for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < groups;
+       gi += (int64_t)gridDim.x * 256) {
+    const int64_t r = gi / per_row, c = (gi - r * per_row) * 8;
+    const int64_t hi = r * ldh + c;
+    float v[8];
+    Elem<T>::load8(h, hi, v);
+    if constexpr (SWIGLU) {
+      float up[8];
+      Elem<T>::load8(h, hi + fs, up);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = silu_f(v[u]) * up[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = gelu_f(v[u]);
+    }
+    const int64_t ai = r * fs + c;
+    if constexpr (OUT_E4M3) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] *= qs;
+      *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(a) + ai) = pack_fp8x8<false>(v);
+    } else {
+      Elem<T>::store8(a, ai, v);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t act_recompute_launch(Kind kind, bool swiglu, const void* h, int64_t rows, int64_t fs,
+                                void* a, const float* scale_inv, hipStream_t s) {
+  const int64_t groups = rows * (fs / 8);
+  if (groups <= 0) return hipSuccess;
+  const int64_t want = (groups + 255) / 256;
+  const unsigned nb = (unsigned)(want > 4096 ? 4096 : want);
+  auto go = [&](auto kernel, const auto* hp) {
+    hipLaunchKernelGGL(kernel, dim3(nb), dim3(256), 0, s, hp, rows, fs, a, scale_inv);
+  };
+  if (kind == KIND_F32) {
+    const float* hp = static_cast<const float*>(h);
+    if (swiglu) go(act_recompute_kernel<float, true, false>, hp);
+    else go(act_recompute_kernel<float, false, false>, hp);
+  } else {
+    const bf16_t* hp = static_cast<const bf16_t*>(h);
+    if (kind == KIND_E4M3) {
+      if (swiglu) return hipErrorInvalidValue;
+      go(act_recompute_kernel<bf16_t, false, true>, hp);
+    } else if (swiglu) {
+      go(act_recompute_kernel<bf16_t, true, false>, hp);
+    } else {
+      go(act_recompute_kernel<bf16_t, false, false>, hp);
+    }
+  }
+  return hipGetLastError();
+}
 
 hipError_t splitk_reduce_launch(const float* part, int splits, int64_t M, int64_t N, void* out,
                                 bool out_bf16, const void* bias, int accumulate, hipStream_t s) {

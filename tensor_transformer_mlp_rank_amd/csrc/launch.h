@@ -58,6 +58,13 @@ hipError_t f32_launch(Step step, const GemmArgs& g, const EpiArgs& e, hipStream_
 hipError_t colsum_reduce_launch(const float* part, int nparts, int M, float* out, int accumulate,
                                 hipStream_t stream, int groups = 1);
 
+// a = act(h) from the saved pre-activation h ([rows][G fs], bf16 for
+// KIND_BF16 and KIND_E4M3, fp32 for KIND_F32) into a ([rows][fs]: bf16,
+// fp32, or E4M3 codes at the factor 1 / *scale_inv for KIND_E4M3, GELU
+// only).
+hipError_t act_recompute_launch(Kind kind, bool swiglu, const void* h, int64_t rows, int64_t fs,
+                                void* a, const float* scale_inv, hipStream_t stream);
+
 // Quantiser passes. src_bf16 selects the source type (bf16 or f32).
 int quant_parts(int64_t n);
 hipError_t amax_partial_launch(bool src_bf16, const void* src, int64_t n, float* partial,

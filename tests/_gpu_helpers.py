@@ -40,8 +40,10 @@ def to_dev(d: dict) -> dict:
 
 
 def gpu_block(tp, inp: dict, act: str, dtype: str, has_bias: bool, calls=("fwd", "dgrad", "wgrad"),
-              accumulate_into=None) -> dict:
-    """Run the requested calls on one rank's shard; returns CPU tensors."""
+              accumulate_into=None, recompute=False) -> dict:
+    """Run the requested calls on one rank's shard; returns CPU tensors.
+    ``recompute``: the weight gradients through tpmlp_bwd_wgrad_recompute,
+    from the saved h instead of a."""
     x = inp["x"]
     T, H = x.shape
     G = 2 if act == "swiglu" else 1
@@ -57,7 +59,8 @@ def gpu_block(tp, inp: dict, act: str, dtype: str, has_bias: bool, calls=("fwd",
         out.update(dH=g["dH"], dx=g["dx"])
         if "wgrad" in calls:
             acc = None if accumulate_into is None else to_dev(accumulate_into)
-            w = tp.bwd_wgrad(desc, dv["dy"], dv["x"], f["a"], g["dH"], accumulate_into=acc)
+            w = tp.bwd_wgrad(desc, dv["dy"], dv["x"], f["h"] if recompute else f["a"], g["dH"],
+                             accumulate_into=acc, recompute=recompute)
             out.update(dW1=w["dW1"], db1=w.get("db1"), dW2=w["dW2"])
     torch.cuda.synchronize()
     return {k: (None if v is None else v.cpu()) for k, v in out.items()}

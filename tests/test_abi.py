@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert tp.lib.tpmlp_abi_version() == 7
+    assert tp.lib.tpmlp_abi_version() == 8
     for s in range(9):
         assert len(tp.lib.tpmlp_strerror(s)) > 5
     assert tp.lib.tpmlp_last_hip_error() == b""
@@ -215,6 +215,44 @@ def test_wgrad_workspace():
     assert tp.lib.tpmlp_bwd_wgrad(*args, None, 0, None) == E_WS
     assert tp.lib.tpmlp_bwd_wgrad(*args, P, need - 1, None) == E_WS
     assert tp.lib.tpmlp_bwd_wgrad(*args, MIS, need, None) == E_ALIGN
+
+
+def wgrad_recompute(desc, dy=P, x=P, h=P, dH=P, dW1=P, db1=P, dW2=P, acc=0, fp8=None, ws=P,
+                    nbytes=1 << 40):
+    sc = None if fp8 is None else ctypes.byref(fp8)
+    return tp.lib.tpmlp_bwd_wgrad_recompute(ctypes.byref(desc), dy, x, h, dH, dW1, db1, dW2, acc,
+                                            sc, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("name", ["dy", "x", "h", "dH", "dW1", "dW2"])
+def test_wgrad_recompute_validation(name):
+    """The recomputing weight gradient checks its arguments as
+    tpmlp_bwd_wgrad does (h_saved in a_saved's place), then its workspace."""
+    assert wgrad_recompute(D(), **{name: None}) == E_NULL
+    assert wgrad_recompute(D(), **{name: MIS}) == E_ALIGN
+    assert wgrad_recompute(D(has_bias=True), db1=None) == E_NULL
+    assert wgrad_recompute(D(), acc=2) == E_DTYPE
+    assert wgrad_recompute(D(dtype="e4m3")) == E_NULL  # FP8 without scales
+    need = tp.workspace_size(D(), tp.CALL_WGRAD_RECOMPUTE)
+    assert wgrad_recompute(D(), ws=None, nbytes=0) == E_WS
+    assert wgrad_recompute(D(), nbytes=need - 1) == E_WS
+    assert wgrad_recompute(D(), ws=MIS, nbytes=need) == E_ALIGN
+
+
+def test_wgrad_recompute_workspace_size():
+    """The recomputed activation ([T][Fs] of the call's element type, rounded
+    up to 256 bytes) in front of the weight gradient's own workspace."""
+    for dt, es in (("bf16", 2), ("f32", 4), ("e4m3", 1)):
+        for act, bias in (("gelu", True), ("swiglu", False)):
+            if dt == "e4m3" and act == "swiglu":
+                continue
+            d = D(tokens=100, ffn_shard=144, dtype=dt, act=act, has_bias=bias)
+            a = (100 * 144 * es + 255) // 256 * 256
+            assert tp.workspace_size(d, tp.CALL_WGRAD_RECOMPUTE) == \
+                a + tp.workspace_size(d, tp.CALL_WGRAD), (dt, act)
+    assert tp.workspace_size(D(tokens=0), tp.CALL_WGRAD_RECOMPUTE) == \
+        tp.workspace_size(D(tokens=0), tp.CALL_WGRAD)
+    assert tp.workspace_size(D(), 4) == 0                         # invalid call
 
 
 def wgrad_noalloc(desc, dy=P, x=P, a=P, dH=P, dW1=P, db1=P, dW2=P, acc=0, fp8=None):

@@ -295,6 +295,17 @@ def _fp8_block(tp, T, H, Fs, seed, prior=False):
     errs["dx (chain)"] = rel_err(g2["dx"].cpu(), rg["dx"])
     for k in ("dW1", "db1", "dW2"):
         errs[k + " (chain)"] = rel_err(wg2[k].cpu(), rw[k])
+    # selective recomputation: a's codes from the saved h at 1 / a_scale_inv;
+    # where that factor is the forward's, the codes and so the results are
+    # the saved path's bit for bit
+    wg3 = tp.bwd_wgrad(desc, dev["dy"][0], dev["x"][0], f["h"], g2["dH"], accumulate_into=acc(),
+                       fp8=fp8_wgrad(ah.scale_inv, dh2.scale_inv), recompute=True)
+    torch.cuda.synchronize()
+    same_factor = _f32(_f32(1.0) / a_sinv) == a_scale
+    for k in ("dW1", "db1", "dW2"):
+        errs[k + " (recompute)"] = rel_err(wg3[k].cpu(), rw[k])
+        if same_factor:
+            assert torch.equal(wg3[k], wg2[k]), k
     say("    rel errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for k, v in errs.items():
         assert v <= TOL["e4m3"], (k, v)

@@ -174,6 +174,31 @@ def test_wgrad_accumulate_long_k(tp, T, H, Fs, act):
         assert rel_err(got, want) <= TOL["bf16"], k
 
 
+@pytest.mark.parametrize("act,dtype", [("gelu", "bf16"), ("swiglu", "bf16"), ("gelu", "f32"),
+                                       ("swiglu", "f32")])
+def test_wgrad_recompute(tp, act, dtype):
+    """Selective recomputation: tpmlp_bwd_wgrad_recompute forms a from the
+    saved h and gives tpmlp_bwd_wgrad's results from the saved a bit for bit
+    (the recomputed activation is the forward's), and so the oracle's to the
+    tolerance; ragged in every dimension, accumulating into prior
+    gradients."""
+    T, H, Fs = 1500, 1040, 528
+    w = synth.WORKLOADS[4 if act == "swiglu" else 2]
+    inp = synth.make_rank_inputs(w, tokens=T, hidden=H, ffn_shard=Fs, dtype=dtype, seed_base=87)
+    has_bias = act == "gelu"
+    G = 2 if act == "swiglu" else 1
+    prior = {"dW1": synth.grad_init(87, (G * Fs, H), 1),
+             "db1": synth.grad_init(87, (G * Fs,), 2) if has_bias else None,
+             "dW2": synth.grad_init(87, (H, Fs), 3)}
+    names = ("dW1", "db1", "dW2") if has_bias else ("dW1", "dW2")
+    saved = gpu_block(tp, inp, act, dtype, has_bias, accumulate_into=prior)
+    rec = gpu_block(tp, inp, act, dtype, has_bias, accumulate_into=prior, recompute=True)
+    for k in names:
+        assert torch.equal(saved[k], rec[k]), k
+    ref = oracle_block(inp, act, has_bias, prior=prior)
+    check(rec, ref, dtype, names)
+
+
 def test_zero_tokens(tp):
     """T = 0: forward and dgrad enqueue nothing; wgrad overwrites with zeros
     (accumulate = 0) or leaves the buffers alone (accumulate = 1)."""
