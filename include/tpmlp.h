@@ -152,11 +152,17 @@ typedef struct tpmlp_fp8_scales {
  * with current scaling, the bfloat16 activation before quantisation; the
  * size covers both modes), the E4M3 dgrad (amax partials of dH), and the
  * weight gradient: with bias, per-tile-column partial sums of db1 (needed),
- * and for BF16 products whose tile grid would leave compute units idle, the
- * fp32 partial sums of a split along K (optional: with fewer bytes the
- * products run unsplit, and the call needs only the db1 partials). Split
- * products are summed in a fixed order, so results stay reproducible, but
- * differ in rounding from unsplit ones. TPMLP_CALL_WGRAD_RECOMPUTE: the
+ * and for products whose tile grid would leave compute units idle, the
+ * fp32 partial sums of a split along K: for BF16 grids of few tiles, every
+ * tile split; for BF16 and E4M3 grids whose last round of tiles is a partial
+ * one (8 to 128 workgroups left over on the 256 compute units; products
+ * without the fused db1 column sums, of at least 16 K-stages), those last
+ * tiles split in two halves along K, each tile's halves added by whichever
+ * of its two workgroups ends second, plus one counter per such tile. This
+ * part is optional: with fewer bytes the products run unsplit, and the call
+ * needs only the db1 partials. Split products are summed in a fixed order,
+ * so results stay reproducible, but differ in rounding from unsplit ones.
+ * TPMLP_CALL_WGRAD_RECOMPUTE: the
  * recomputed activation (T * Fs elements, rounded up to 256 bytes) plus the
  * weight gradient's workspace. Returns 0 for an unknown call.
  */
@@ -210,8 +216,10 @@ tpmlp_status tpmlp_bwd_dgrad(const tpmlp_desc* desc, const void* dy, const void*
  * the column sums of the dequantised dH. fp8 must be non-NULL iff dtype is
  * E4M3. Workspace: tpmlp_workspace_size(desc, TPMLP_CALL_WGRAD) bytes (the
  * db1 partials are required with bias; the split-K part is optional).
- * Results are reproducible bit for bit: every sum is taken in a fixed order,
- * no atomics.
+ * Results are reproducible bit for bit: every sum is taken in a fixed order
+ * (the two halves of a tile split in two are added in one fp32 addition,
+ * whose result does not depend on which half ends first); no sum goes
+ * through atomics.
  */
 tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* desc, const void* dy, const void* x,
                              const void* a_saved, const void* dH, float* dW1, float* db1,

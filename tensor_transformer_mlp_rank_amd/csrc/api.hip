@@ -186,6 +186,33 @@ int fp8_fc1_parts(const tpmlp_desc* d) { return gemm_tiles(d->tokens, d->ffn_sha
 // e4m3 dgrad: fc2 dgrad's workgroups (M = T, N = Fs), one amax partial of dH each
 int fp8_dgrad_parts(const tpmlp_desc* d) { return gemm_tiles(d->tokens, d->ffn_shard); }
 
+// ---------------------------------------------------------------- partial last rounds
+// A weight gradient whose tiles leave a last round of r workgroups (8 <= r
+// <= 128) on the 256 compute units runs r rounded down to a multiple of 8 of
+// its tiles as two workgroups each, one per half of the K stages, so that the
+// last round fills the chip and takes half a tile's time. The halves meet in
+// the workspace (kernel: GemmArgs::tail_tiles). Only for unsplit MFMA
+// products without the fused column sum, of at least 16 stages.
+constexpr int kTailCUs = 256;
+int tail_plan(Kind kind, Step step, int64_t M, int64_t N, int64_t K) {
+  if (kind == KIND_F32 || step != WGRAD) return 0;
+  if (M <= 0 || N <= 0 || M > INT32_MAX || N > INT32_MAX) return 0;
+  GemmArgs g{};
+  g.M = (int)M;
+  g.N = (int)N;
+  const int tiles = mfma_grid(step, g);
+  const int64_t stages = (K + (kind == KIND_E4M3 ? 127 : 63)) / (kind == KIND_E4M3 ? 128 : 64);
+  if (stages < 16) return 0;
+  const int r = tiles % kTailCUs;
+  if (r < 8 || r > kTailCUs / 2) return 0;
+  return r & ~7;
+}
+size_t tail_count_bytes(int tail) { return align_up((size_t)tail * 4, 256); }
+// counters, then two 256 x 256 fp32 dumps per split tile
+size_t tail_bytes(int tail) {
+  return tail > 0 ? tail_count_bytes(tail) + (size_t)tail * 2 * 256 * 256 * 4 : 0;
+}
+
 // fc1 wgrad with bias: tile columns of dW1 = dH^T . x (N = H), each of which
 // writes one row of db1 partial sums
 int colsum_parts(const tpmlp_desc* d) {
@@ -197,25 +224,31 @@ int colsum_parts(const tpmlp_desc* d) {
 }
 
 // The MLP wgrad's split plans (fc2's dW2, fc1's dW1) and its workspace: the
-// db1 partial rows of the column sums (sp1 * tiles_n of them), then the
-// partial planes of the larger split product.
+// db1 partial rows of the column sums (sp1 * tiles_n of them), then one
+// region for the partial planes of the larger split product or the halves of
+// an unsplit product's partial last round (the products run one after the
+// other).
 struct WgradPlan {
   int sp2, sp1;
-  size_t colsum, planes;
+  int tail2, tail1;
+  size_t colsum, planes;  // planes: the shared region
 };
 WgradPlan wgrad_plan(const tpmlp_desc* d, bool split_ok) {
   const Kind kind = d->dtype == TPMLP_F32 ? KIND_F32 : d->dtype == TPMLP_BF16 ? KIND_BF16 : KIND_E4M3;
   const int64_t gfs = (d->act == TPMLP_ACT_SWIGLU ? 2 : 1) * d->ffn_shard;
-  WgradPlan p{1, 1, 0, 0};
+  WgradPlan p{1, 1, 0, 0, 0, 0};
   if (split_ok) {
     p.sp2 = plan_splits(kind, WGRAD, d->hidden, d->ffn_shard, d->tokens);
     p.sp1 = plan_splits(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, gfs, d->hidden, d->tokens);
+    if (p.sp2 < 2) p.tail2 = tail_plan(kind, WGRAD, d->hidden, d->ffn_shard, d->tokens);
+    if (p.sp1 < 2 && !d->has_bias) p.tail1 = tail_plan(kind, WGRAD, gfs, d->hidden, d->tokens);
   }
   if (d->has_bias && kind != KIND_F32)
     p.colsum = align_up((size_t)p.sp1 * (size_t)colsum_parts(d) * (size_t)gfs * 4, 256);
-  const size_t a = split_bytes(p.sp2, d->hidden, d->ffn_shard);
-  const size_t b = split_bytes(p.sp1, gfs, d->hidden);
-  p.planes = a > b ? a : b;
+  const size_t sizes[4] = {split_bytes(p.sp2, d->hidden, d->ffn_shard),
+                           split_bytes(p.sp1, gfs, d->hidden), tail_bytes(p.tail2),
+                           tail_bytes(p.tail1)};
+  for (size_t v : sizes) p.planes = v > p.planes ? v : p.planes;
   return p;
 }
 
@@ -269,14 +302,25 @@ tpmlp_status check_workspace(const tpmlp_desc* d, int32_t call, void* ws, size_t
 
 // ---------------------------------------------------------------- GEMM step dispatch
 // `label` names the launch for the timing facility (e.g. "fc1_fwd.bf16").
+// `tail` > 0: that many tiles of a partial last round run as two half-K
+// workgroups each, with tail_ws holding tail_bytes(tail) (see tail_plan).
 hipError_t run_step(Kind kind, Step step, const char* label, GemmArgs g, const EpiArgs& e,
-                    hipStream_t s) {
+                    hipStream_t s, int tail = 0, void* tail_ws = nullptr) {
   const int nb = (kind == KIND_F32) ? f32_grid(step, g) : mfma_grid(step, g);
   if (nb == 0) return hipSuccess;
-  if (kind != KIND_F32) clock_attach(label, g, nb);
+  if (kind != KIND_F32 && tail > 0) {
+    g.tail_tiles = tail;
+    g.tail_cnt = static_cast<int*>(tail_ws);
+    g.tail_ws = reinterpret_cast<float*>(static_cast<char*>(tail_ws) + tail_count_bytes(tail));
+  }
+  if (kind != KIND_F32) clock_attach(label, g, (int64_t)nb + g.tail_tiles);
   return timed(label, s, [&]() {
-    return kind == KIND_F32 ? f32_launch(step, g, e, s)
-                            : mfma_launch(kind == KIND_E4M3, step, g, e, s);
+    if (kind == KIND_F32) return f32_launch(step, g, e, s);
+    if (g.tail_tiles > 0) {
+      const hipError_t err = fill_zero_i32_launch(g.tail_cnt, g.tail_tiles, s);
+      if (err != hipSuccess) return err;
+    }
+    return mfma_launch(kind == KIND_E4M3, step, g, e, s);
   });
 }
 
@@ -285,8 +329,8 @@ hipError_t run_step(Kind kind, Step step, const char* label, GemmArgs g, const E
 // the product and its reduce together under `label`. A fused column sum then
 // writes sp * tiles_n partial rows.
 hipError_t run_gemm(Kind kind, Step step, const char* label, GemmArgs g, const EpiArgs& e,
-                    hipStream_t s, int sp, float* part) {
-  if (sp < 2) return run_step(kind, step, label, g, e, s);
+                    hipStream_t s, int sp, float* part, int tail = 0, void* tail_ws = nullptr) {
+  if (sp < 2) return run_step(kind, step, label, g, e, s, tail, tail_ws);
   if (mfma_grid(step, g) == 0) return hipSuccess;
   g.k_splits = sp;
   g.split_stages = (int)(((g.K + 63) / 64 + sp - 1) / sp);
@@ -514,7 +558,7 @@ tpmlp_status run_wgrad(const tpmlp_desc* d, const void* dy, const void* x, const
   e1.out = dW2; e1.ldo = Fs; e1.accumulate = accumulate;
   if (is_fp8) { e1.scale_a = fp8->dy_scale_inv; e1.scale_b = fp8->a_scale_inv; }
   GemmArgs g1 = make_gemm(dy, H, a_saved, Fs, H, Fs, T, 0);
-  hipError_t err = run_gemm(kind, WGRAD, label(kind, 4), g1, e1, s, p.sp2, planes);
+  hipError_t err = run_gemm(kind, WGRAD, label(kind, 4), g1, e1, s, p.sp2, planes, p.tail2, planes);
   if (err != hipSuccess) return hip_fail(err);
   // dW1 [GFs, H] = dH^T . x (+ db1 = column sums of dH). The fp32 kernel
   // writes db1 itself; the MFMA kernel writes per-tile-column partial sums
@@ -527,7 +571,7 @@ tpmlp_status run_wgrad(const tpmlp_desc* d, const void* dy, const void* x, const
   if (is_fp8) { e2.scale_a = fp8->dH_scale_inv; e2.scale_b = fp8->x_scale_inv; }
   GemmArgs g2 = make_gemm(dH, GFs, x, H, GFs, H, T, 0);
   err = run_gemm(kind, d->has_bias ? WGRAD_COLSUM : WGRAD, label(kind, 5), g2, e2, s, p.sp1,
-                 planes);
+                 planes, p.tail1, planes);
   if (err != hipSuccess) return hip_fail(err);
   if (parts) {
     err = timed(is_fp8 ? "db1_reduce.e4m3" : "db1_reduce.bf16", s, [&]() {

@@ -67,6 +67,17 @@ struct GemmArgs {
   // accumulate); a reduce pass forms the result
   int k_splits;
   int split_stages;
+  // a partial last round (ungrouped, unsplit products): the last tail_tiles
+  // tiles of the walk (a multiple of 8; the others a multiple of 8 too) are
+  // each taken by two workgroups, one per half of the K stages, placed on the
+  // same XCD; each dumps its accumulators to its half's 256 KiB of tail_ws
+  // ([tail_tiles][2][256 x 256] floats, in register order), then adds one to
+  // the tile's counter in tail_cnt ([tail_tiles], zero at the launch); the
+  // one that finds the other's count adds the other's dump to its own
+  // accumulators, runs the epilogue and sets the counter back to zero
+  int tail_tiles;
+  float* tail_ws;
+  int* tail_cnt;
   // clock capture (the timing facility), or null: each workgroup writes
   // (shader clock, real-time counter) at its start and end to
   // clk[4 * blockIdx.x .. +3] while blockIdx.x < clk_slots

@@ -142,9 +142,6 @@ __device__ __forceinline__ void tile_walk(int id, int tiles_m, int tiles_n, int 
   bm = first_m + in % gsz;
   bn = in / gsz;
 }
-__device__ __forceinline__ void tile_coords(const GemmArgs& g, int bid, int& bm, int& bn) {
-  tile_walk(xcd_remap(bid, g.tiles_m * g.tiles_n), g.tiles_m, g.tiles_n, g.group_m, bm, bn);
-}
 
 // Grouped products. Each wave scans the group counts 64 groups per pass with
 // a saturating prefix sum (every wave of a workgroup gets the same, uniform
@@ -522,10 +519,14 @@ __device__ __forceinline__ void wait_and_barrier() {
 // counter tracks both loads and stores, so a wait for a load issued after a
 // store also waits for the store, and per-group load/use pairs would
 // serialise the epilogue on memory latency.
+//
+// tail_other: the other half's accumulator dump of a split tile (register r
+// of this lane at float (r / 4) * 256 + r % 4 from it), added to the
+// accumulators as they are staged; null otherwise.
 template <bool IS_FP8, int EPI, typename OutT, bool LOADS, typename Acc>
 __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e, Acc& acc,
                                            char* smem, int wave, int lane, int m0, int n0,
-                                           float& amax) {
+                                           float& amax, const float* tail_other) {
   static_assert(std::is_same<OutT, bf16_t>::value, "MFMA activations and outputs are bf16");
   constexpr bool kPair = (EPI == EPI_SWIGLU);
   constexpr int kLd = 132;
@@ -602,25 +603,41 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e, 
     if constexpr (LOADS) {
       if ((fm & 1) == 0) load_slabs(fm);
     }
-    if constexpr (sizeof(acc[0][0]) == 64) {
-      // 32x32 blocks: register j of block (fm, fn) is row 8 (j/4) + 4 (l/32)
-      // + j%4, column 32 fn + l%32
+    // the slab's accumulators, in quarters of four dump chunks (chunks
+    // fm 16 + 4 qt .. +3; with tail_other their dump values are added)
 #pragma unroll
-      for (int fn = 0; fn < 4; ++fn)
+    for (int qt = 0; qt < 4; ++qt) {
+      f32x4 t[4];
+      if (tail_other) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
+        for (int k = 0; k < 4; ++k)
+          t[k] = *reinterpret_cast<const f32x4*>(tail_other + (fm * 16 + qt * 4 + k) * 256);
+      }
+      if constexpr (sizeof(acc[0][0]) == 64) {
+        // 32x32 blocks: register j of block (fm, fn) is row 8 (j/4) + 4 (l/32)
+        // + j%4, column 32 fn + l%32; its dump chunk (fm 4 + fn) 4 + j/4
+        const int fn = qt;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float v = acc[fm][fn][j];
           wl[(8 * (j >> 2) + 4 * (lane >> 5) + (j & 3)) * kLd + 32 * fn + (lane & 31)] =
-              acc[fm][fn][j];
-    } else {
-      // 16x16 blocks: register q of block (2 fm + h, c) is row 16 h + 4 (l/16)
-      // + q, column 16 c + l%16
+              tail_other ? v + t[j >> 2][j & 3] : v;
+        }
+      } else {
+        // 16x16 blocks: register q of block (2 fm + h, c) is row 16 h + 4 (l/16)
+        // + q, column 16 c + l%16; its dump chunk (2 fm + h) 8 + c
+        const int h = qt >> 1;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const int c = 4 * (qt & 1) + c4;
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            wl[(16 * h + 4 * (lane >> 4) + q) * kLd + 16 * c + (lane & 15)] = acc[2 * fm + h][c][q];
+          for (int q = 0; q < 4; ++q) {
+            const float v = acc[2 * fm + h][c][q];
+            wl[(16 * h + 4 * (lane >> 4) + q) * kLd + 16 * c + (lane & 15)] =
+                tail_other ? v + t[c4][q] : v;
+          }
+        }
+      }
     }
     if constexpr (LOADS) {
       if ((fm & 1) == 0) {
@@ -766,8 +783,26 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   int kt0 = 0;                              // first stage of this workgroup's K range
   int nk = (g.K + kStep - 1) / kStep;       // its number of stages
   int split = 0;
+  // the products whose partial last round the host may split: the weight
+  // gradients without a fused column sum (in the other kernels the code
+  // would cost registers their main loops do not have)
+  constexpr bool kTail = GROUP == GROUP_NONE && !COLSUM && !A_K && !B_K && EPI == EPI_F32;
+  int tail_p = -1, tail_h = 0;  // split tile of a partial last round, and its half
   if constexpr (GROUP == GROUP_NONE) {
-    if (g.k_splits > 1) {
+    const int full = g.tiles_m * g.tiles_n - (kTail ? g.tail_tiles : 0);
+    if (kTail && g.tail_tiles > 0 && (int)blockIdx.x >= full) {
+      // workgroup u of the tail runs on XCD x = blockIdx.x % 8: it takes half
+      // (u / 8) % 2 of tail tile x * (tail_tiles / 8) + u / 16, so both halves
+      // of a tile share an XCD (and its L2) and each XCD a run of the walk
+      const int u = (int)blockIdx.x - full;
+      tail_h = (u >> 3) & 1;
+      tail_p = ((int)blockIdx.x & 7) * (g.tail_tiles >> 3) + (u >> 4);
+      tile_walk(full + tail_p, g.tiles_m, g.tiles_n, g.group_m, bm, bn);
+      // the first half an even number of stages (see split-K)
+      const int half = (((nk + 1) >> 1) + 1) & ~1;
+      kt0 = tail_h ? half : 0;
+      nk = tail_h ? nk - half : (half < nk ? half : nk);
+    } else if (g.k_splits > 1) {
       // ids split-major: the workgroups of one XCD share a split's panels
       const int tiles = g.tiles_m * g.tiles_n;
       const int id = xcd_remap(blockIdx.x, tiles * g.k_splits);
@@ -777,7 +812,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
       nk = nk - kt0 < g.split_stages ? nk - kt0 : g.split_stages;
       e.out = static_cast<char*>(e.out) + (int64_t)split * g.M * e.ldo * 4;
     } else {
-      tile_coords(g, blockIdx.x, bm, bn);
+      tile_walk(xcd_remap(blockIdx.x, full), g.tiles_m, g.tiles_n, g.group_m, bm, bn);
     }
   } else {
     GroupHit hit;
@@ -1347,16 +1382,81 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     }
   }
 
+  // ---- a split tile of a partial last round: the two halves meet here
+  const float* tail_other = nullptr;
+  if constexpr (kTail) {
+    if (tail_p >= 0) {
+      // accumulator register r of lane l of wave w in 16-byte chunks: chunk
+      // c = r / 4 at floats (w * 64 + c) * 256 + 4 l of the half's 256 KiB
+      constexpr int kChunks = (int)(sizeof(AccV) / 16);  // per block
+      const int64_t half_floats = (int64_t)kBM * kBN;
+      // the lane's offset as a fresh value: not one the compiler would keep
+      // live across the main loop from the prologue's address arithmetic
+      int lane4 = 4 * (int)(threadIdx.x & 63);
+      asm volatile("" : "+v"(lane4));
+      float* mine = g.tail_ws + ((int64_t)tail_p * 2 + tail_h) * half_floats + wave * 16384 + lane4;
+      // Stored from the accumulator registers (asm with AGPR operands: with
+      // plain stores the compiler copies every accumulator to VGPRs first
+      // and spills); 1 KiB per wave and chunk, 16 bytes per lane. The
+      // compiler's hazard checks do not see asm stores: a VALU write to the
+      // data registers of a store of more than 8 bytes needs a wait state,
+      // and the compiler may stage the next chunk in the same registers, so
+      // each store is followed by two.
+      static_for<kAb * kAb>([&](auto B) {
+        constexpr int b = decltype(B)::value;
+        auto& v = acc[b / kAb][b % kAb];
+        float* p = mine + b * kChunks * 256;
+        if constexpr (kChunks == 1) {
+          asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" : : "v"(p), "a"(v) : "memory");
+        } else {
+          asm volatile(
+              "global_store_dwordx4 %0, %1, off\n\t"
+              "global_store_dwordx4 %0, %2, off offset:1024\n\t"
+              "global_store_dwordx4 %0, %3, off offset:2048\n\t"
+              "global_store_dwordx4 %0, %4, off offset:3072\n\t"
+              "s_nop 1"
+              :
+              : "v"(p), "a"(__builtin_shufflevector(v, v, 0, 1, 2, 3)),
+                "a"(__builtin_shufflevector(v, v, 4, 5, 6, 7)),
+                "a"(__builtin_shufflevector(v, v, 8, 9, 10, 11)),
+                "a"(__builtin_shufflevector(v, v, 12, 13, 14, 15))
+              : "memory");
+        }
+      });
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // every wave's dump has reached the L2
+      __shared__ int tail_seen;
+      if (tid == 0)
+        tail_seen = __hip_atomic_fetch_add(g.tail_cnt + tail_p, 1, __ATOMIC_ACQ_REL,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (tail_seen == 0) {
+        // the other half, still running, finishes the tile: this one runs
+        // the epilogue with no tensors (every access out of range, no memory
+        // traffic), the same code either way
+        e.out = nullptr;
+        e.out2 = nullptr;
+        e.aux = nullptr;
+      } else {
+        // the epilogue adds the other half's dump (its release, this
+        // atomic's acquire) as it stages the accumulators
+        tail_other =
+            g.tail_ws + ((int64_t)tail_p * 2 + (1 - tail_h)) * half_floats + wave * 16384 + lane4;
+        if (tid == 0) g.tail_cnt[tail_p] = 0;  // for the next launch
+      }
+    }
+  }
+
   __syncthreads();  // every wave is done reading the stage buffers
   float amax = 0.f;
   if constexpr (EPI == EPI_F32) {
     if (e.accumulate)
-      store_tile<IS_FP8, EPI, OutT, true>(g, e, acc, smem, wave, lane, m0, n0, amax);
+      store_tile<IS_FP8, EPI, OutT, true>(g, e, acc, smem, wave, lane, m0, n0, amax, tail_other);
     else
-      store_tile<IS_FP8, EPI, OutT, false>(g, e, acc, smem, wave, lane, m0, n0, amax);
+      store_tile<IS_FP8, EPI, OutT, false>(g, e, acc, smem, wave, lane, m0, n0, amax, tail_other);
   } else {
     constexpr bool kLoads = (EPI == EPI_DGELU || EPI == EPI_DSWIGLU || EPI == EPI_DGELU_Q);
-    store_tile<IS_FP8, EPI, OutT, kLoads>(g, e, acc, smem, wave, lane, m0, n0, amax);
+    store_tile<IS_FP8, EPI, OutT, kLoads>(g, e, acc, smem, wave, lane, m0, n0, amax, tail_other);
   }
   if constexpr (IS_FP8 && (EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_Q || EPI == EPI_DGELU_Q)) {
     amax = wave_max(amax);

@@ -131,7 +131,18 @@ __global__ void __launch_bounds__(256) act_recompute_kernel(const T* __restrict_
   }
 }
 
+__global__ void __launch_bounds__(256) fill_zero_i32_kernel(int* __restrict__ p, int n) {
+  for (int i = (int)(blockIdx.x * 256 + threadIdx.x); i < n; i += (int)(gridDim.x * 256)) p[i] = 0;
+}
+
 }  // namespace
+
+hipError_t fill_zero_i32_launch(int* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int nb = (n + 255) / 256 > 64 ? 64 : (n + 255) / 256;
+  hipLaunchKernelGGL(fill_zero_i32_kernel, dim3(nb), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
 
 hipError_t act_recompute_launch(Kind kind, bool swiglu, const void* h, int64_t rows, int64_t fs,
                                 void* a, const float* scale_inv, hipStream_t s) {

@@ -26,7 +26,7 @@ hipError_t launch_one(const GemmArgs& g, const EpiArgs& e, hipStream_t s, int64_
                                         hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
   });
   if (attr_err[dev] != hipSuccess) return attr_err[dev];
-  if (nb < 0) nb = (int64_t)g.tiles_m * g.tiles_n;
+  if (nb < 0) nb = (int64_t)g.tiles_m * g.tiles_n + g.tail_tiles;
   hipLaunchKernelGGL(k, dim3((unsigned)nb), dim3(kThreads), kSmemBytes, s, g, e);
   return hipGetLastError();
 }

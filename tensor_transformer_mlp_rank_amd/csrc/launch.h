@@ -65,6 +65,10 @@ hipError_t colsum_reduce_launch(const float* part, int nparts, int M, float* out
 hipError_t act_recompute_launch(Kind kind, bool swiglu, const void* h, int64_t rows, int64_t fs,
                                 void* a, const float* scale_inv, hipStream_t stream);
 
+// n ints at p set to zero (a kernel, so that the call can be captured into a
+// graph).
+hipError_t fill_zero_i32_launch(int* p, int n, hipStream_t stream);
+
 // Quantiser passes. src_bf16 selects the source type (bf16 or f32).
 int quant_parts(int64_t n);
 hipError_t amax_partial_launch(bool src_bf16, const void* src, int64_t n, float* partial,

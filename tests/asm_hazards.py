@@ -10,7 +10,11 @@ on the compiler's output over each kernel's control-flow graph:
   ``s_waitcnt lgkmcnt(N)`` leaves at most the N newest outstanding);
 * VALU to MFMA: an MFMA may not read a VGPR that a VALU instruction wrote
   fewer than two instructions earlier (the wait states the hardware does
-  not enforce).
+  not enforce);
+* store data: the instruction right after a global or buffer store of more
+  than 8 bytes may not write the store's data registers (VGPRs or AGPRs:
+  one wait state, which the compiler inserts for its own stores but not
+  after asm ones).
 
 ``exec``-conditional branches are taken as always taken: every lane of
 these kernels' waves is active.
@@ -26,6 +30,15 @@ def _regs(tok: str) -> frozenset:
         return frozenset(range(int(m.group(1)), int(m.group(2)) + 1))
     m = re.fullmatch(r'v(\d+)', tok)
     return frozenset({int(m.group(1))}) if m else frozenset()
+
+
+# AGPRs as register numbers 1000 and up (disjoint from the VGPRs)
+def _va_regs(tok: str) -> frozenset:
+    m = re.fullmatch(r'a\[(\d+):(\d+)\]', tok)
+    if m:
+        return frozenset(1000 + r for r in range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.fullmatch(r'a(\d+)', tok)
+    return frozenset({1000 + int(m.group(1))}) if m else _regs(tok)
 
 
 def _split(line: str):
@@ -143,13 +156,30 @@ def _valu_mfma(st, line, report):
     return (tuple(st) + (new,))[-2:]
 
 
+def _store_data(st, line, report):
+    op, ops = _split(line)
+    guarded = st[0] if st else frozenset()
+    if op.startswith('s_nop'):
+        return (frozenset(),)
+    if op.startswith('v_') and ops and (_va_regs(ops[0]) & guarded):
+        report(line)
+    wide = op.endswith(('_dwordx3', '_dwordx4', '_b96', '_b128'))
+    if wide and op.startswith('global_store') and len(ops) > 1:
+        return (_va_regs(ops[1]),)
+    if wide and op.startswith('buffer_store') and ops:
+        return (_va_regs(ops[0]),)
+    return (frozenset(),)
+
+
 def check(asm: str, prefix: str = '') -> dict:
-    """Violations of both rules per kernel whose name starts with `prefix`:
-    {name: {"inflight": [...], "valu_mfma": [...]}} (empty lists: clean)."""
+    """Violations of the rules per kernel whose name starts with `prefix`:
+    {name: {"inflight": [...], "valu_mfma": [...], "store_data": [...]}}
+    (empty lists: clean)."""
     out = {}
     for name, body in kernels(asm).items():
         if not name.startswith(prefix):
             continue
         out[name] = {"inflight": sorted(l for _, l in _solve(body, _inflight)),
-                     "valu_mfma": sorted(l for _, l in _solve(body, _valu_mfma))}
+                     "valu_mfma": sorted(l for _, l in _solve(body, _valu_mfma)),
+                     "store_data": sorted(l for _, l in _solve(body, _store_data))}
     return out

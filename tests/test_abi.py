@@ -177,8 +177,9 @@ def test_split_k_plans_through_workspace_sizes():
     assert got == _colsum_bytes(H, Fs, 4) + planes
     big = D(tokens=8192, hidden=8192, ffn_shard=4096)
     assert tp.workspace_size(big, tp.CALL_WGRAD) == _colsum_bytes(8192, 4096)
+    # FP8 never splits along K (its 64-tile dW2 takes the partial-round split instead)
     assert tp.workspace_size(D(tokens=8192, hidden=H, ffn_shard=Fs, dtype="e4m3"),
-                             tp.CALL_WGRAD) == _colsum_bytes(H, Fs)
+                             tp.CALL_WGRAD) == _colsum_bytes(H, Fs) + _tail_bytes(64)
     assert tp.workspace_size(D(tokens=8192, hidden=H, ffn_shard=Fs, dtype="f32"),
                              tp.CALL_WGRAD) == 0
     # too few stages to split (K = 512 tokens): the colsum rows only
@@ -190,6 +191,44 @@ def test_split_k_plans_through_workspace_sizes():
     # the attention out-projection backward at the 8192-hidden shard (128 tiles) splits in two
     a = tp.make_attn_desc(8192, 8192, 8, 8, 128, dtype="bf16", has_bias=True)
     assert tp.attn_workspace_size(a) >= 2 * 8192 * 1024 * 4
+
+
+def _tail_bytes(tiles):
+    return (tiles * 4 + 255) // 256 * 256 + tiles * 2 * 256 * 256 * 4
+
+
+def test_partial_last_round_plans_through_workspace_sizes():
+    """Weight gradients whose tiles leave a last round of 8 to 128 workgroups
+    on the 256 compute units run that many tiles (rounded down to a multiple
+    of 8) as two half-K workgroups each; the halves meet in the workspace (a
+    counter per tile, then two 256 x 256 fp32 dumps). At the SwiGLU
+    4096-hidden TP=2 shard (T = 8192, Fs = 7168) fc1's weight gradient
+    (56 x 16 = 896 tiles) splits 128 tiles; fc2's (448 tiles: a last round of
+    192) does not, nor do the other calls' products."""
+    sw = D(tokens=8192, hidden=4096, ffn_shard=7168, act="swiglu", has_bias=False)
+    assert tp.workspace_size(sw, tp.CALL_WGRAD) == _tail_bytes(128)
+    assert tp.workspace_size(sw, tp.CALL_DGRAD) == 0
+    assert tp.workspace_size(sw, tp.CALL_FWD) == 0
+    # with bias fc1's product (896 tiles) carries the fused column sum and does not
+    # split; fc2's (16 x 56 = 896 tiles) does
+    assert tp.workspace_size(D(tokens=8192, hidden=4096, ffn_shard=14336), tp.CALL_WGRAD) == \
+        _colsum_bytes(4096, 14336) + _tail_bytes(128)
+    # whole rounds (the 8192-hidden TP=8 shard): nothing to split
+    big = D(tokens=8192, hidden=8192, ffn_shard=4096)
+    assert tp.workspace_size(big, tp.CALL_WGRAD) == _colsum_bytes(8192, 4096)
+    # fewer than 16 stages of K: no split (K = T = 960 tokens is 15 stages of 64; 1024 is 16)
+    short = dict(hidden=4096, ffn_shard=7168, act="swiglu", has_bias=False)
+    assert tp.workspace_size(D(tokens=960, **short), tp.CALL_WGRAD) == 0
+    assert tp.workspace_size(D(tokens=1024, **short), tp.CALL_WGRAD) == _tail_bytes(128)
+    # a last round of 4 tiles (13 x 20 = 260): no split; of 12 (4 x 67 = 268): 8 of them split
+    assert tp.workspace_size(D(tokens=4096, hidden=13 * 256, ffn_shard=20 * 256, has_bias=False),
+                             tp.CALL_WGRAD) == 0
+    assert tp.workspace_size(D(tokens=4096, hidden=4 * 256, ffn_shard=67 * 256, has_bias=False),
+                             tp.CALL_WGRAD) == _tail_bytes(8)
+    # the fp32 kernel never splits
+    assert tp.workspace_size(D(tokens=8192, dtype="f32", **short), tp.CALL_WGRAD) == 0
+    # the allocation-free call never splits either: it needs no workspace without bias
+    assert tp.workspace_size(sw, tp.CALL_WGRAD) > 0
 
 
 @pytest.mark.parametrize("name", ["dy", "W1", "W2", "h", "dH", "dx"])

@@ -199,6 +199,49 @@ def test_wgrad_recompute(tp, act, dtype):
     check(rec, ref, dtype, names)
 
 
+@pytest.mark.parametrize("act,dtype", [("swiglu", "bf16"), ("gelu", "e4m3")])
+def test_wgrad_partial_last_round(tp, act, dtype):
+    """Weight gradients whose tile grid leaves a partial last round run its
+    tiles as two half-K workgroups that meet in the workspace: dW2 of
+    17 x 17 = 289 tiles (32 split), SwiGLU dW1 of 34 x 17 = 578 (64 split).
+    Compared with the unsplit product (the minimal workspace) to fp32
+    rounding, bit for bit between two runs, and accumulating into priors."""
+    T, H, Fs = 2048, 4352, 4352 - 16
+    G = 2 if act == "swiglu" else 1
+    has_bias = act == "gelu"
+    desc = tp.make_desc(T, H, Fs, act=act, dtype=dtype, has_bias=has_bias)
+    assert tp.workspace_size(desc, tp.CALL_WGRAD) > 0
+    gen = torch.Generator().manual_seed(5)
+    if dtype == "e4m3":
+        codes = lambda *sh: torch.randint(0, 120, sh, generator=gen, dtype=torch.uint8).cuda()
+        dy, x, a, dH = codes(T, H), codes(T, H), codes(T, Fs), codes(T, G * Fs)
+        one = torch.ones(1, dtype=torch.float32, device="cuda")
+        fp8 = tp.fp8_scales(x_scale_inv=one, a_scale_inv=one, dy_scale_inv=one, dH_scale_inv=one)
+    else:
+        bf = lambda *sh: torch.randn(*sh, generator=gen).to(torch.bfloat16).cuda()
+        dy, x, a, dH = bf(T, H), bf(T, H), bf(T, Fs), bf(T, G * Fs)
+        fp8 = None
+    prior = {"dW1": torch.randn(G * Fs, H, generator=gen), "dW2": torch.randn(H, Fs, generator=gen),
+             "db1": torch.randn(G * Fs, generator=gen) if has_bias else None}
+
+    def run(ws_bytes):
+        out = {k: (None if v is None else v.clone().cuda()) for k, v in prior.items()}
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        tp.tpmlp_bwd_wgrad(desc, dy, x, a, dH, out["dW1"], out["db1"], out["dW2"], accumulate=True,
+                           fp8=fp8, workspace=ws if ws_bytes else None)
+        torch.cuda.synchronize()
+        return {k: v for k, v in out.items() if v is not None}
+
+    full = tp.workspace_size(desc, tp.CALL_WGRAD)
+    split1, split2 = run(full), run(full)
+    # the minimal workspace: the db1 partial rows only (bias), or none
+    plain = run((((H + 255) // 256) * G * Fs * 4 + 255) // 256 * 256 if has_bias else 0)
+    for k in split1:
+        assert torch.equal(split1[k], split2[k]), k
+        assert rel_err(split1[k].cpu(), plain[k].cpu()) <= 1e-5, k
+    assert not torch.equal(split1["dW2"], plain["dW2"])  # the split ran (a different sum order)
+
+
 def test_zero_tokens(tp):
     """T = 0: forward and dgrad enqueue nothing; wgrad overwrites with zeros
     (accumulate = 0) or leaves the buffers alone (accumulate = 1)."""

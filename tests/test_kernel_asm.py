@@ -1,6 +1,7 @@
 """The MFMA kernels' device assembly keeps the rules of tests/asm_hazards.py
 (no use of a register while an asm LDS read into it is in flight; two wait
-states between a VALU write and an MFMA read of a VGPR), and no kernel uses
+states between a VALU write and an MFMA read of a VGPR; a wait state
+between a wide store and a write of its data registers), and no kernel uses
 scratch memory. Host only: the kernels are compiled for gfx950 to assembly
 with the library's own flags. The checker itself is first shown to catch
 planted violations in small hand-written sequences."""
@@ -56,6 +57,18 @@ _Zloop:
 \ts_cbranch_scc1 .LBB2_1
 \ts_endpgm
 .Lfunc_end2:
+_Zstore:
+\tglobal_store_dwordx4 v[8:9], a[0:3], off
+\tv_accvgpr_write_b32 a1, v250
+\tglobal_store_dwordx4 v[8:9], a[0:3], off
+\ts_nop 0
+\tv_accvgpr_write_b32 a1, v250
+\tbuffer_store_dwordx4 v[4:7], v1, s[0:3], 0 offen
+\tv_mov_b32_e32 v5, 0
+\tglobal_store_dwordx2 v[8:9], v[2:3], off
+\tv_mov_b32_e32 v2, 0
+\ts_endpgm
+.Lfunc_end3:
 """
 
 
@@ -64,7 +77,11 @@ def test_checker_catches_planted_violations():
     assert r["_Ztoy"]["inflight"] == ["v_mov_b32 v5, 0"]
     assert r["_Ztoy"]["valu_mfma"] == [
         "v_mfma_f32_16x16x32_bf16 a[0:3], v[8:11], v[12:15], a[0:3]"]
-    assert r["_Zclean"] == {"inflight": [], "valu_mfma": []}
+    assert r["_Zclean"] == {"inflight": [], "valu_mfma": [], "store_data": []}
+    # a 16-byte store's data registers written by the next instruction (twice);
+    # after a wait state, or for an 8-byte store, no finding
+    assert r["_Zstore"]["store_data"] == ["v_accvgpr_write_b32 a1, v250",
+                                          "v_mov_b32_e32 v5, 0"]
     # the read at the bottom of the loop is still in flight at the top
     assert r["_Zloop"]["inflight"] == ["v_add_u32_e32 v4, 1, v4"]
 
@@ -83,7 +100,8 @@ def mfma_asm(tmp_path_factory):
 def test_mfma_kernels_keep_the_asm_rules(mfma_asm):
     res = check(mfma_asm, prefix="_ZN5tpmlp16gemm_mfma_kernel")
     assert len(res) >= 20
-    bad = {k[:90]: v for k, v in res.items() if v["inflight"] or v["valu_mfma"]}
+    bad = {k[:90]: v for k, v in res.items()
+           if v["inflight"] or v["valu_mfma"] or v["store_data"]}
     assert not bad, bad
 
 
