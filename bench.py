@@ -127,7 +127,8 @@ def write_traffic(name, labels, setup, fetch_dir, write_dir, copy_fetch_dir, cop
     FETCH_SIZE and WRITE_SIZE runs of this script (KiB per dispatch), each
     scaled by what the same counter reads for the plain 1 GiB device copy of
     --copy-calibration. Dispatches of the library are matched to step labels
-    by launch order; a split-K product's reduce pass counts with its GEMM."""
+    by launch order; a split-K product's reduce pass counts with its GEMM, and
+    the fill that clears a split product's counters with the GEMM after it."""
     import statistics
     copy_bytes = float(COPY_BYTES)
 
@@ -149,8 +150,12 @@ def write_traffic(name, labels, setup, fetch_dir, write_dir, copy_fetch_dir, cop
         rows = rows[setup:]  # one-off set-up launches (the FP8 step quantises its inputs)
         li, step, cur, first = 0, 0, None, True
         sums = {}
+        held = []  # fills launched ahead of their product
         for r in rows:
             kn = kname(r)
+            if "fill_zero" in kn:
+                held.append(r)
+                continue
             if "splitk_reduce" in kn and cur is not None:
                 lab = cur  # the reduce pass of the product just launched
             else:
@@ -161,12 +166,15 @@ def write_traffic(name, labels, setup, fetch_dir, write_dir, copy_fetch_dir, cop
                     li, step = 0, step + 1
                 cur = lab
             k = per.setdefault(lab, {"kernels": []})
-            if first:
-                if kn not in k["kernels"]:
-                    k["kernels"].append(kn)
-            elif kn not in k["kernels"]:
-                raise SystemExit(f"dispatch order does not match the step: {kn} as {lab}")
-            sums.setdefault(lab, []).append(float(r["Counter_Value"]) * 1024.0 * scale[counter])
+            for n in [kname(x) for x in held] + [kn]:
+                if first:
+                    if n not in k["kernels"]:
+                        k["kernels"].append(n)
+                elif n not in k["kernels"]:
+                    raise SystemExit(f"dispatch order does not match the step: {n} as {lab}")
+            for x in held + [r]:
+                sums.setdefault(lab, []).append(float(x["Counter_Value"]) * 1024.0 * scale[counter])
+            held = []
         if li != 0 or step == 0:
             raise SystemExit(f"{d}: {len(rows)} library dispatches after the set-up, not whole "
                              f"steps of {labels}")

@@ -245,7 +245,8 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, char* lds_w
 //
 // K-major: instruction ii covers rows 8 ii .. +7 (a full 128-byte row each, so
 // every request is a whole cache line); lane l fetches row 8 ii + l/8,
-// logical chunk (l%8) ^ kswz(row).
+// logical chunk (l%8) ^ kswz(row) (kswz16(row) in the FP8 products of two
+// K-major operands).
 // For the gated fc1 the rows of one instruction all come from one half of W1
 // (gate: rs0, up: base1); which one depends on the instruction only, so the
 // choice is wave-uniform and the resource stays in scalar registers.
@@ -320,6 +321,16 @@ struct MNMajorLoader {
 // part measured conflict-free for the 32x32 operand's reads), XOR 2 when
 // krow / 8 is odd (for the 16x16 operand's, which pair k-rows 8 apart).
 __device__ __forceinline__ int kswz(int row) { return (row >> 1) & 7; }
+// FP8 K-major tiles of the 16x16x128 products: a lane reads chunks 2g, 2g+1
+// (g = lane / 16) of row lane % 16, and with kswz two of the four 16-lane
+// groups meet in the same 16-byte slots of a 256-byte window (2-way
+// conflicts, measured: half of all LDS cycles of these reads). Chunk c goes to
+// c ^ 2 ((row >> 1) & 3) ^ ((row >> 3) & 1), measured conflict-free.
+__device__ __forceinline__ int kswz16(int row) {
+  return (((row >> 1) & 3) << 1) ^ ((row >> 3) & 1);
+}
+template <bool F16>
+__device__ __forceinline__ int kswz_of(int row) { return F16 ? kswz16(row) : kswz(row); }
 __device__ __forceinline__ int mnswz(int kr) {
   return ((0xEA40 >> ((kr & 3) << 2)) & 15) ^ ((kr >> 2) & 2);
 }
@@ -439,7 +450,7 @@ __device__ __forceinline__ i32x8 frag_k_e4m3_16(const char* stage, int wrow, int
   const int row = wrow + (lane & 15);
   const int c0 = (lane >> 4) << 1;
   const uint32_t base = (uint32_t)(uintptr_t)(const TPMLP_LDS char*)stage + row * kRowBytes;
-  const uint32_t a0 = base + ((c0 ^ kswz(row)) << 4), a1 = base + (((c0 + 1) ^ kswz(row)) << 4);
+  const uint32_t a0 = base + ((c0 ^ kswz16(row)) << 4), a1 = base + (((c0 + 1) ^ kswz16(row)) << 4);
   constexpr int kOff = T + R * 16 * kRowBytes;
   static_assert(kOff >= 0 && kOff < 65536, "DS offset field");
   u32x4 lo, hi;
@@ -766,6 +777,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   static_assert(GROUP == GROUP_NONE || !IS_FP8, "grouped products are bf16");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   constexpr bool kPair = (EPI == EPI_SWIGLU);
+  constexpr bool kF16 = IS_FP8 && A_K && B_K;  // FP8 on the 16x16x128 MFMA
   constexpr int esz = IS_FP8 ? 1 : 2;
   constexpr int kStep = kRowBytes / esz;  // k elements per stage
   const int tid = threadIdx.x, lane = tid & 63;
@@ -856,7 +868,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = 8 * (wave * 8 + i) + (lane >> 3);
-      const int c = (lane & 7) ^ kswz(row);
+      const int c = (lane & 7) ^ kswz_of<kF16>(row);
       la.klim[i] = la.k_limit(m0 + row < g.M, la.kbytes, (uint32_t)(c << 4));
       la.voff[i] = (uint32_t)(row * ldb_) + (uint32_t)(c << 4);
     }
@@ -889,7 +901,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int row = 8 * (wave * 8 + i) + (lane >> 3);
-        const int c = (lane & 7) ^ kswz(row);
+        const int c = (lane & 7) ^ kswz_of<kF16>(row);
         const int f = (row >> 5) & 3;
         const int lr = ((row >> 7) << 6) + ((f & 1) << 5) + (row & 31);
         lb.klim[i] = lb.k_limit(n0 + lr < g.N, lb.kbytes, (uint32_t)(c << 4));
@@ -901,7 +913,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int row = 8 * (wave * 8 + i) + (lane >> 3);
-        const int c = (lane & 7) ^ kswz(row);
+        const int c = (lane & 7) ^ kswz_of<kF16>(row);
         lb.klim[i] = lb.k_limit(n0 + row < g.N, lb.kbytes, (uint32_t)(c << 4));
         lb.voff[i] = (uint32_t)(row * ldb_) + (uint32_t)(c << 4);
       }
@@ -943,7 +955,6 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   // each); FP8, 4 x 4 blocks of the 32x32x64 one (16 registers each)
   // FP8 with two K-major operands runs the 16x16x128 MFMA (k-step = stage):
   // bf16-like 8 x 8 blocks of 16x16; other FP8 products the 32x32x64 one
-  constexpr bool kF16 = IS_FP8 && A_K && B_K;
   constexpr bool kAcc32 = IS_FP8 && !kF16;
   constexpr int kAb = kAcc32 ? 4 : 8;
   using AccV = typename std::conditional<kAcc32, f32x16, f32x4>::type;
