@@ -1,17 +1,23 @@
-"""The per-rank GELU block with FP8 operands, forward and backward, float64.
+"""The per-rank block with FP8 operands, forward and backward, float64.
 
 Test infrastructure (see the package header). The inputs are the
 dequantised FP8 tensors the device consumes: x, W1, W2 from E4M3 codes and
 dy from E5M2 codes, each decode(code) * scale_inv. The block is then the
-plain one (column-parallel fc1, bias + GELU, row-parallel fc2, its data and
-weight gradients -- Megatron-LM code tour, "The Tensor-Parallel Primitives"
-and "The Transformer Stack"), with the two tensors that the block itself
-produces and feeds to a later product quantised on the way, at the scale
-the call is given (delayed scaling, see oracle.fp8):
+plain one (column-parallel fc1, bias + GELU or the gated SwiGLU, row-parallel
+fc2, its data and weight gradients -- Megatron-LM code tour, "The
+Tensor-Parallel Primitives" and "The Transformer Stack"; FP8 through
+Transformer Engine, concept note "Megatron-LM / Megatron-Core", "Key math /
+How it works"), with the two tensors that the block itself produces and
+feeds to a later product quantised on the way, at the scale the call is
+given (delayed scaling, see oracle.fp8):
 
-* the activation a, to E4M3, before fc2 and the fc2 weight gradient;
-* the gradient dH = dA * gelu'(h), to E5M2, before the fc1 data and weight
-  gradients and the bias gradient.
+* the activation a (gelu(h), or silu(gate) * up for the gated block), to
+  E4M3, before fc2 and the fc2 weight gradient;
+* the gradient dH (dA * gelu'(h), or both halves [dA * up * silu'(gate) |
+  dA * silu(gate)]), to E5M2 with one scale for the whole tensor, before the
+  fc1 data and weight gradients and the bias gradient.
+
+The gated block's h is [gate | up] along the features, as in oracle.block.
 
 Everything else is float64 on those values: h = x W1^T + b1 is kept
 exact and the activation, forward and backward, is taken of it (the plain
@@ -28,7 +34,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .activations import gelu_tanh, gelu_tanh_grad
+from .activations import gelu_tanh, gelu_tanh_grad, silu, silu_grad
 from .fp8 import dequantize, quantize
 
 
@@ -45,13 +51,23 @@ def round_bf16(v) -> np.ndarray:
     return b.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
-def rank_forward_fp8(x, W1, b1, W2, a_scale) -> dict:
-    """h = x W1^T + b1; a = gelu(h); a quantised to E4M3 at a_scale (codes,
-    and a_q = decode(code) / a_scale); y = a_q W2^T. amax = max |a|. All
-    float64 except the quantiser's float32 product. "h_exact" is the same
-    array as "h" (the name the tests bound the device's stored h against)."""
+def _act(h, act: str):
+    if act == "gelu":
+        return gelu_tanh(h)
+    if act == "swiglu":
+        fs = h.shape[1] // 2
+        return silu(h[:, :fs]) * h[:, fs:]
+    raise ValueError(f"unknown activation {act!r}")
+
+
+def rank_forward_fp8(x, W1, b1, W2, a_scale, act: str = "gelu") -> dict:
+    """h = x W1^T + b1; a = gelu(h), or silu(gate) * up with h = [gate | up];
+    a quantised to E4M3 at a_scale (codes, and a_q = decode(code) / a_scale);
+    y = a_q W2^T. amax = max |a|. All float64 except the quantiser's float32
+    product. "h_exact" is the same array as "h" (the name the tests bound
+    the device's stored h against)."""
     h = x @ W1.T + (0.0 if b1 is None else b1)
-    a = gelu_tanh(h)
+    a = _act(h, act)
     codes = quantize(a, "e4m3", a_scale)
     a_q = dequantize(codes, "e4m3", _inv(a_scale))
     y = a_q @ W2.T
@@ -60,12 +76,19 @@ def rank_forward_fp8(x, W1, b1, W2, a_scale) -> dict:
             "amax": amax}
 
 
-def rank_dgrad_fp8(dy, W1, W2, h, dH_scale) -> dict:
-    """dA = dy W2; dH = dA * gelu'(h) (h as given: the forward's exact h);
-    dH quantised to E5M2 at dH_scale (codes, and dH_q); dx = dH_q W1.
-    amax = max |dH|."""
+def rank_dgrad_fp8(dy, W1, W2, h, dH_scale, act: str = "gelu") -> dict:
+    """dA = dy W2; dH = dA * gelu'(h), or [dA * up * silu'(gate) |
+    dA * silu(gate)] (h as given: the forward's exact h); dH quantised to
+    E5M2 at dH_scale (codes, and dH_q); dx = dH_q W1. amax = max |dH|."""
     dA = dy @ W2
-    dH = dA * gelu_tanh_grad(h)
+    if act == "gelu":
+        dH = dA * gelu_tanh_grad(h)
+    elif act == "swiglu":
+        fs = h.shape[1] // 2
+        gate, up = h[:, :fs], h[:, fs:]
+        dH = np.concatenate([dA * up * silu_grad(gate), dA * silu(gate)], axis=1)
+    else:
+        raise ValueError(f"unknown activation {act!r}")
     codes = quantize(dH, "e5m2", dH_scale)
     dH_q = dequantize(codes, "e5m2", _inv(dH_scale))
     dx = dH_q @ W1

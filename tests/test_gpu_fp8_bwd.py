@@ -150,6 +150,9 @@ def _check_h(h_dev, h_exact):
 # = 0.798 for the tanh form (both maxima found on a fine grid of the oracle's
 # functions; the second is gelu''(0)).
 GELU_SLOPE, GELU_CURV = 1.13, 0.80
+# The same for SiLU: |silu'| <= 1.0998 (near z = 2.4) and |silu''| <= 1/2
+# (silu''(0)).
+SILU_SLOPE, SILU_CURV = 1.10, 0.50
 
 
 def _h_span(h, lo, hi):

@@ -491,21 +491,23 @@ def test_round_bf16_matches_torch_cast():
     assert round_bf16(np.float32(1 + 3 * 2.0 ** -8)) == 1 + 2.0 ** -6
 
 
-def test_fp8_block_is_the_plain_block_within_quantisation_bounds():
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_fp8_block_is_the_plain_block_within_quantisation_bounds(act):
     """The FP8 block's unquantised intermediates are the plain block's; its
     outputs differ from the plain block by no more than the rounding bound
     of the quantised intermediates (a in E4M3, dH in E5M2) carried through
     the following products."""
     rng = np.random.default_rng(17)
     T, H, Fs = 24, 40, 32
+    G = 2 if act == "swiglu" else 1
     x = rng.standard_normal((T, H))
-    W1 = rng.standard_normal((Fs, H)) * 0.2
-    b1 = rng.standard_normal(Fs) * 0.1
+    W1 = rng.standard_normal((G * Fs, H)) * 0.2
+    b1 = rng.standard_normal(G * Fs) * 0.1
     W2 = rng.standard_normal((H, Fs)) * 0.2
     dy = rng.standard_normal((T, H))
-    f = ob.rank_forward(x, W1, b1, W2, "gelu")
+    f = ob.rank_forward(x, W1, b1, W2, act)
     a_scale = np.float32(448.0 / np.max(np.abs(f["a"])))
-    q = oracle.rank_forward_fp8(x, W1, b1, W2, a_scale)
+    q = oracle.rank_forward_fp8(x, W1, b1, W2, a_scale, act)
     # the unquantised intermediates are the plain block's, float64 throughout
     assert np.allclose(q["h"], f["h"], rtol=0, atol=1e-13)
     assert np.allclose(q["a"], f["a"], rtol=0, atol=1e-13)
@@ -514,9 +516,9 @@ def test_fp8_block_is_the_plain_block_within_quantisation_bounds():
     assert np.all(np.abs(q["a_q"] - q["a"]) <= da)
     assert np.all(np.abs(q["y"] - f["y"]) <= da @ np.abs(W2.T) + 1e-12)
     assert np.any(q["a_q"] != q["a"])               # the quantisation is not a no-op
-    g = ob.rank_dgrad(dy, W1, W2, f["h"], "gelu")
+    g = ob.rank_dgrad(dy, W1, W2, f["h"], act)
     dH_scale = np.float32(57344.0 / np.max(np.abs(g["dH"])) / 4)
-    p = oracle.rank_dgrad_fp8(dy, W1, W2, f["h"], dH_scale)
+    p = oracle.rank_dgrad_fp8(dy, W1, W2, f["h"], dH_scale, act)
     assert np.allclose(p["dH"], g["dH"], rtol=0, atol=1e-12)
     dh = np.maximum(np.abs(g["dH"]) * 2.0 ** -3, 2.0 ** -17 / float(dH_scale)) * (1 + 1e-6)
     assert np.all(np.abs(p["dH_q"] - g["dH"]) <= dh)
@@ -528,8 +530,38 @@ def test_fp8_block_is_the_plain_block_within_quantisation_bounds():
     assert np.all(np.abs(w["db1"] - ref["db1"]) <= dh.sum(axis=0) + 1e-12)
     # with every intermediate exactly representable the FP8 block is the plain one:
     # an all-zero gradient quantises exactly
-    z = oracle.rank_dgrad_fp8(np.zeros((T, H)), W1, W2, f["h"], dH_scale)
+    z = oracle.rank_dgrad_fp8(np.zeros((T, H)), W1, W2, f["h"], dH_scale, act)
     assert np.all(z["dH_codes"] & 0x7F == 0) and np.all(z["dx"] == 0)
+    if act == "swiglu":
+        # the gate half of dH carries up * silu'(gate), the up half silu(gate):
+        # with up = 0 the gate half vanishes and the up half does not
+        fs = Fs
+        W1z = W1.copy()
+        W1z[fs:] = 0.0
+        fz = oracle.rank_forward_fp8(x, W1z, np.concatenate([b1[:fs], np.zeros(fs)]), W2,
+                                     a_scale, act)
+        assert np.all(fz["a"] == 0) and np.all(fz["a_codes"] & 0x7F == 0)
+        gz = oracle.rank_dgrad_fp8(dy, W1z, W2, fz["h"], dH_scale, act)
+        assert np.all(gz["dH"][:, :fs] == 0) and np.any(gz["dH"][:, fs:] != 0)
+    with pytest.raises(ValueError):
+        oracle.rank_forward_fp8(x, W1, b1, W2, a_scale, "relu")
+
+
+def test_activation_bounds_of_the_fp8_gpu_windows():
+    """The slope and curvature bounds the FP8 GPU tests widen their windows
+    with hold for the oracle's activations on a fine grid (the maxima of
+    |gelu'|, |gelu''|, |silu'|, |silu''|; second derivatives by central
+    differences of the first)."""
+    from test_gpu_fp8_bwd import GELU_CURV, GELU_SLOPE, SILU_CURV, SILU_SLOPE
+    from oracle.activations import gelu_tanh_grad, silu_grad
+    z = np.linspace(-30.0, 30.0, 600001)
+    e = 1e-5
+    for grad, slope, curv in ((gelu_tanh_grad, GELU_SLOPE, GELU_CURV),
+                              (silu_grad, SILU_SLOPE, SILU_CURV)):
+        g1 = np.abs(grad(z))
+        g2 = np.abs((grad(z + e) - grad(z - e)) / (2 * e))
+        assert np.max(g1) <= slope and np.max(g1) > 0.97 * slope
+        assert np.max(g2) <= curv and np.max(g2) > 0.97 * curv
 
 
 # ---------------------------------------------------------------- inputs
