@@ -239,10 +239,10 @@ def _mlp_oracle(w, calls, x, W1, b1, W2, dy, fp8, a_scale, dH_scale) -> dict:
     import oracle
     out = {}
     if fp8:
-        f = oracle.rank_forward_fp8(x, W1, b1, W2, a_scale)
+        f = oracle.rank_forward_fp8(x, W1, b1, W2, a_scale, w.act)
         out.update(y=f["y"], h=f["h"], a=f["a"])
         if "dgrad" in calls:
-            g = oracle.rank_dgrad_fp8(dy, W1, W2, f["h"], dH_scale)
+            g = oracle.rank_dgrad_fp8(dy, W1, W2, f["h"], dH_scale, w.act)
             out.update(dx=g["dx"])
             if "wgrad" in calls:
                 out.update(oracle.rank_wgrad_fp8(dy, x, f["a_q"], g["dH_q"]))

@@ -33,7 +33,7 @@
  *   TPMLP_F32  : everything float32.
  *   TPMLP_BF16 : x, W1, b1, W2, dy, h, a, dH, y_partial, dx_partial bfloat16;
  *                products accumulate in float32.
- *   TPMLP_E4M3 : GELU only. FP8 with per-tensor float32 dequantisation
+ *   TPMLP_E4M3 : GELU or SwiGLU. FP8 with per-tensor float32 dequantisation
  *                factors (scale_inv): forward tensors in OCP E4M3, gradients
  *                in OCP E5M2 (Transformer Engine's default "hybrid" format;
  *                the pages name FP8 through Transformer Engine, code tour
@@ -45,7 +45,8 @@
  *                (scale = 448 / amax(a); 1 when amax is 0 or the quotient
  *                overflows) or delayed
  *                scaling (tpmlp_fp8_history), and dH (E5M2, dgrad) with
- *                delayed scaling. Codes saturate at the largest finite value
+ *                delayed scaling; for SwiGLU both halves of dH take the one
+ *                scale and amax. Codes saturate at the largest finite value
  *                (448, 57344) and are rounded to nearest even.
  *
  * Ownership: the caller allocates and frees every buffer, the workspace too
@@ -79,7 +80,7 @@ typedef enum {
   TPMLP_E_SHAPE = 2,       /* T < 0, H <= 0, Fs <= 0, H or Fs not a multiple of 16, or too large */
   TPMLP_E_DTYPE = 3,       /* unknown dtype or activation code */
   TPMLP_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
-  TPMLP_E_UNSUPPORTED = 5, /* valid but not provided (E4M3 SwiGLU, SwiGLU bias) */
+  TPMLP_E_UNSUPPORTED = 5, /* valid but not provided (SwiGLU bias; E4M3 attention; MoE not BF16) */
   TPMLP_E_WORKSPACE = 6,   /* workspace NULL or smaller than tpmlp_workspace_size */
   TPMLP_E_HIP = 7,         /* a HIP runtime call failed while enqueuing */
   TPMLP_E_SCRATCH = 8      /* too large for the fixed scratch of tpmlp_bwd_wgrad_noalloc */
@@ -193,7 +194,7 @@ tpmlp_status tpmlp_fwd(const tpmlp_desc* desc, const void* x, const void* W1_sha
  *   GELU:   dH = dA * gelu'(h)
  *   SwiGLU: dH = [dA * up * silu'(gate) | dA * silu(gate)]  (gate, up = halves of h)
  *   dx_partial = dH . W1_shard.
- * dH is written (the caller keeps it for tpmlp_bwd_wgrad). For E4M3 (GELU):
+ * dH is written (the caller keeps it for tpmlp_bwd_wgrad). For E4M3:
  * dy is E5M2 codes; dA is the accumulator times dy_scale_inv * w2_scale_inv;
  * dH is quantised to E5M2 in the epilogue at fp8->dH_history->scale and the
  * history updated; dx_partial = dH_codes . W1_codes times
@@ -238,11 +239,11 @@ tpmlp_status tpmlp_bwd_wgrad(const tpmlp_desc* desc, const void* dy, const void*
  * tpmlp_bwd_wgrad on it.
  *   BF16, F32: a equals the forward's a_saved bit for bit, and so do the
  *     results those of tpmlp_bwd_wgrad.
- *   E4M3 (GELU): a's codes are E4M3(gelu(h) * (1 / fp8->a_scale_inv)), the
+ *   E4M3: a's codes are E4M3(act(h) * (1 / fp8->a_scale_inv)), the
  *     float32 factor recomputed from the dequantisation factor that the wgrad
  *     call already takes; they match the forward's codes wherever that
  *     factor equals the forward's (with delayed scaling the forward quantised
- *     the float32 gelu(h) at a_history->scale, of which a_scale_inv is the
+ *     the float32 act(h) at a_history->scale, of which a_scale_inv is the
  *     inverse).
  * Workspace: tpmlp_workspace_size(desc, TPMLP_CALL_WGRAD_RECOMPUTE) bytes, the
  * recomputed a (T * Fs elements, rounded up to 256 bytes) followed by

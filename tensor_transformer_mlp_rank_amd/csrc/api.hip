@@ -120,7 +120,6 @@ tpmlp_status check_desc(const tpmlp_desc* d) {
   if (!grid_fits(d->tokens, d->hidden > g * d->ffn_shard ? d->hidden : g * d->ffn_shard))
     return TPMLP_E_SHAPE;
   if (d->act == TPMLP_ACT_SWIGLU && d->has_bias) return TPMLP_E_UNSUPPORTED;
-  if (d->dtype == TPMLP_E4M3 && d->act != TPMLP_ACT_GELU_TANH) return TPMLP_E_UNSUPPORTED;
   return TPMLP_OK;
 }
 
@@ -181,8 +180,14 @@ int gemm_tiles(int64_t M, int64_t N) {
   return mfma_grid(FC2_FWD, g);
 }
 
-// e4m3 forward: fc1's workgroups, one amax partial each
-int fp8_fc1_parts(const tpmlp_desc* d) { return gemm_tiles(d->tokens, d->ffn_shard); }
+// e4m3 forward: fc1's workgroups, one amax partial each (the gated fc1 runs
+// 256 x 128 pair tiles)
+int fp8_fc1_parts(const tpmlp_desc* d) {
+  GemmArgs g{};
+  g.M = (int)d->tokens;
+  g.N = (int)d->ffn_shard;
+  return mfma_grid(d->act == TPMLP_ACT_SWIGLU ? FC1_FWD_SWIGLU_Q : FC1_FWD_GELU_Q, g);
+}
 // e4m3 dgrad: fc2 dgrad's workgroups (M = T, N = Fs), one amax partial of dH each
 int fp8_dgrad_parts(const tpmlp_desc* d) { return gemm_tiles(d->tokens, d->ffn_shard); }
 
@@ -625,7 +630,8 @@ const char* tpmlp_strerror(tpmlp_status s) {
     case TPMLP_E_DTYPE: return "unknown dtype, activation or flag value";
     case TPMLP_E_ALIGN: return "a pointer is not 16-byte aligned";
     case TPMLP_E_UNSUPPORTED:
-      return "combination not provided (E4M3 SwiGLU, SwiGLU bias, E4M3 attention projections)";
+      return "combination not provided (SwiGLU bias, E4M3 attention projections, expert MLPs "
+             "other than BF16)";
     case TPMLP_E_WORKSPACE: return "workspace missing or too small";
     case TPMLP_E_HIP: return "HIP runtime error while enqueuing (see tpmlp_last_hip_error)";
     case TPMLP_E_SCRATCH:
@@ -697,13 +703,13 @@ tpmlp_status tpmlp_fwd(const tpmlp_desc* d, const void* x, const void* W1, const
     if (T > 0) {
       EpiArgs e1{};
       e1.out = a_saved; e1.ldo = Fs;
-      e1.out2 = h_saved; e1.ldo2 = Fs;
+      e1.out2 = h_saved; e1.ldo2 = GFs;
       e1.bias = d->has_bias ? b1 : nullptr;
       e1.scale_a = fp8->x_scale_inv; e1.scale_b = fp8->w1_scale_inv;
       e1.q_scale = ah->scale;
       e1.amax_part = parts;
       GemmArgs g1 = make_gemm(x, H, W1, H, T, Fs, H, Fs);
-      err = run_step(kind, FC1_FWD_GELU_Q, label(kind, 0), g1, e1, s);
+      err = run_step(kind, swiglu ? FC1_FWD_SWIGLU_Q : FC1_FWD_GELU_Q, label(kind, 0), g1, e1, s);
       if (err != hipSuccess) return hip_fail(err);
     }
     err = timed("a_scale_update.e4m3", s, [&]() {
@@ -729,12 +735,12 @@ tpmlp_status tpmlp_fwd(const tpmlp_desc* d, const void* x, const void* W1, const
   if (T > 0) {
     EpiArgs e1{};
     e1.out = a_bf16; e1.ldo = Fs;
-    e1.out2 = h_saved; e1.ldo2 = Fs;
+    e1.out2 = h_saved; e1.ldo2 = GFs;
     e1.bias = d->has_bias ? b1 : nullptr;
     e1.scale_a = fp8->x_scale_inv; e1.scale_b = fp8->w1_scale_inv;
     e1.amax_part = parts;
     GemmArgs g1 = make_gemm(x, H, W1, H, T, Fs, H, Fs);
-    err = run_step(kind, FC1_FWD_GELU, label(kind, 0), g1, e1, s);
+    err = run_step(kind, swiglu ? FC1_FWD_SWIGLU : FC1_FWD_GELU, label(kind, 0), g1, e1, s);
     if (err != hipSuccess) return hip_fail(err);
   }
   err = timed("quantize_a.e4m3", s, [&]() {
@@ -798,7 +804,7 @@ tpmlp_status tpmlp_bwd_dgrad(const tpmlp_desc* d, const void* dy, const void* W1
     e1.scale_a = fp8->dy_scale_inv; e1.scale_b = fp8->w2_scale_inv;
     e1.q_scale = hh->scale;
     e1.amax_part = parts;
-    err = run_step(kind, FC2_DGRAD_GELU_Q, label(kind, 2), g1, e1, s);
+    err = run_step(kind, swiglu ? FC2_DGRAD_SWIGLU_Q : FC2_DGRAD_GELU_Q, label(kind, 2), g1, e1, s);
     if (err != hipSuccess) return hip_fail(err);
     err = timed("dH_scale_update.e4m3", s, [&]() {
       return delayed_update_launch(parts, fp8_dgrad_parts(d), hh->amax_history, hh->len,

@@ -11,6 +11,8 @@
 //   EPI_DSWIGLU   out[col] = acc * u * silu'(g); out[col + Fs] = acc * silu(g)
 //   EPI_BIAS_GELU_Q  as EPI_BIAS_GELU; out = E4M3 codes of a * q_scale (a in fp32)
 //   EPI_DGELU_Q   as EPI_DGELU; out = E5M2 codes of dH * q_scale
+//   EPI_SWIGLU_Q  as EPI_SWIGLU; out = E4M3 codes of a * q_scale (a in fp32)
+//   EPI_DSWIGLU_Q as EPI_DSWIGLU; both halves E5M2 codes of dH * q_scale
 //   EPI_BIAS      out = alpha * acc + bias[col]        (packed q, k, v)
 // (FP8 codes saturate at the format's largest finite value; the quantising
 // epilogues also fold max |value| into a per-workgroup amax.)
@@ -34,6 +36,8 @@ enum EpiKind : int {
   EPI_BIAS_GELU_Q = 6,  // EPI_BIAS_GELU, a quantised to E4M3 at *q_scale
   EPI_DGELU_Q = 7,      // EPI_DGELU, dH quantised to E5M2 at *q_scale
   EPI_BIAS = 8,         // bias added, no activation (attention's QKV projection)
+  EPI_SWIGLU_Q = 9,     // EPI_SWIGLU, a quantised to E4M3 at *q_scale
+  EPI_DSWIGLU_Q = 10,   // EPI_DSWIGLU, dH quantised to E5M2 at *q_scale
 };
 
 // Grouped products (the expert MLPs of a mixture-of-experts layer): group e

@@ -539,12 +539,14 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e, 
                                            char* smem, int wave, int lane, int m0, int n0,
                                            float& amax, const float* tail_other) {
   static_assert(std::is_same<OutT, bf16_t>::value, "MFMA activations and outputs are bf16");
-  constexpr bool kPair = (EPI == EPI_SWIGLU);
+  constexpr bool kPair = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q);
   constexpr int kLd = 132;
   constexpr int kT = kPair ? 4 : 8;         // row groups per lane and slab
   constexpr int kRowStep = kPair ? 8 : 4;   // rows between them
-  constexpr int kPre = (EPI == EPI_F32 || EPI == EPI_DSWIGLU) ? 2 : 1;  // 16 B loads per group
-  constexpr bool kQ8 = (EPI == EPI_BIAS_GELU_Q || EPI == EPI_DGELU_Q);  // FP8 codes out
+  constexpr bool kDSw = (EPI == EPI_DSWIGLU || EPI == EPI_DSWIGLU_Q);
+  constexpr int kPre = (EPI == EPI_F32 || kDSw) ? 2 : 1;  // 16 B loads per group
+  constexpr bool kQ8 = (EPI == EPI_BIAS_GELU_Q || EPI == EPI_DGELU_Q || EPI == EPI_SWIGLU_Q ||
+                        EPI == EPI_DSWIGLU_Q);  // FP8 codes out
   constexpr int kOes = (EPI == EPI_F32) ? 4 : kQ8 ? 1 : 2;  // primary output element bytes
   constexpr uint32_t kBf = 2;
   const int wm = wave >> 1, wn = wave & 1;
@@ -592,7 +594,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e, 
         for (int t = 0; t < kT; ++t) {
           const uint32_t o = goff(e.ldaux, kBf, t);
           pre[s][t][0] = buf_load16(rs, o);
-          if constexpr (EPI == EPI_DSWIGLU)
+          if constexpr (kDSw)
             pre[s][t][kPre - 1] = buf_load16(rs, o + (uint32_t)g.pair_off * kBf);
         }
       }
@@ -715,7 +717,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e, 
           }
           buf_store16(ro, goff(e.ldo, kBf, t), aw);
         }
-      } else if constexpr (EPI == EPI_SWIGLU) {
+      } else if constexpr (kPair) {
         float up[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) up[u] = src[64 + u] * alpha;
@@ -728,7 +730,30 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e, 
         unpack_bf16x8(uw, up);
 #pragma unroll
         for (int u = 0; u < 8; ++u) v[u] = silu_f(v[u]) * up[u];
-        buf_store16(ro, goff(e.ldo, kBf, t), pack_bf16x8(v));
+        // rows past M and columns past N leave the amax out
+        const bool row_ok = oob == 0u && wrow + 32 * fm + rl + kRowStep * t < g.M;
+        if constexpr (kQ8) {
+          // codes straight from the fp32 activation, amax of the same values
+          if (row_ok) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[u]));
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] *= qs;
+          buf_store8(ro, goff(e.ldo, 1, t), pack_fp8x8<false>(v));
+        } else {
+          const u32x4 aw = pack_bf16x8(v);
+          if constexpr (IS_FP8) {
+            // amax of a as stored in bf16, the values the quantiser reads
+            float ar[8];
+            unpack_bf16x8(aw, ar);
+            if (row_ok) {
+#pragma unroll
+              for (int u = 0; u < 8; ++u) amax = __builtin_fmaxf(amax, __builtin_fabsf(ar[u]));
+            }
+          }
+          buf_store16(ro, goff(e.ldo, kBf, t), aw);
+        }
       } else if constexpr (EPI == EPI_DGELU || EPI == EPI_DGELU_Q) {
         float h[8];
         unpack_bf16x8(pre[s][t][0], h);
@@ -745,7 +770,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e, 
         } else {
           buf_store16(ro, goff(e.ldo, kBf, t), pack_bf16x8(v));
         }
-      } else if constexpr (EPI == EPI_DSWIGLU) {
+      } else if constexpr (kDSw) {
         float gt[8], up[8], dg[8];
         unpack_bf16x8(pre[s][t][0], gt);
         unpack_bf16x8(pre[s][t][1], up);
@@ -754,9 +779,27 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const EpiArgs& e, 
           dg[u] = v[u] * up[u] * silu_grad_f(gt[u]);
           v[u] = v[u] * silu_f(gt[u]);
         }
-        const uint32_t o = goff(e.ldo, kBf, t);
-        buf_store16(ro, o, pack_bf16x8(dg));
-        buf_store16(ro, o + (uint32_t)g.pair_off * kBf, pack_bf16x8(v));
+        if constexpr (kQ8) {
+          // both halves at the one scale of dH, amax over both
+          if (oob == 0u && wrow + 32 * fm + rl + kRowStep * t < g.M) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(dg[u]),
+                                                           __builtin_fabsf(v[u])));
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            dg[u] *= qs;
+            v[u] *= qs;
+          }
+          const uint32_t o = goff(e.ldo, 1, t);
+          buf_store8(ro, o, pack_fp8x8<true>(dg));
+          buf_store8(ro, o + (uint32_t)g.pair_off, pack_fp8x8<true>(v));
+        } else {
+          const uint32_t o = goff(e.ldo, kBf, t);
+          buf_store16(ro, o, pack_bf16x8(dg));
+          buf_store16(ro, o + (uint32_t)g.pair_off * kBf, pack_bf16x8(v));
+        }
       }
     }
   }
@@ -776,7 +819,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
   static_assert(IS_FP8 || FMT == 0, "formats select FP8 encodings");
   static_assert(GROUP == GROUP_NONE || !IS_FP8, "grouped products are bf16");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  constexpr bool kPair = (EPI == EPI_SWIGLU);
+  constexpr bool kPair = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q);
   constexpr bool kF16 = IS_FP8 && A_K && B_K;  // FP8 on the 16x16x128 MFMA
   constexpr int esz = IS_FP8 ? 1 : 2;
   constexpr int kStep = kRowBytes / esz;  // k elements per stage
@@ -1466,10 +1509,12 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     else
       store_tile<IS_FP8, EPI, OutT, false>(g, e, acc, smem, wave, lane, m0, n0, amax, tail_other);
   } else {
-    constexpr bool kLoads = (EPI == EPI_DGELU || EPI == EPI_DSWIGLU || EPI == EPI_DGELU_Q);
+    constexpr bool kLoads = (EPI == EPI_DGELU || EPI == EPI_DSWIGLU || EPI == EPI_DGELU_Q ||
+                             EPI == EPI_DSWIGLU_Q);
     store_tile<IS_FP8, EPI, OutT, kLoads>(g, e, acc, smem, wave, lane, m0, n0, amax, tail_other);
   }
-  if constexpr (IS_FP8 && (EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_Q || EPI == EPI_DGELU_Q)) {
+  if constexpr (IS_FP8 && (EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_Q || EPI == EPI_DGELU_Q ||
+                          EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q || EPI == EPI_DSWIGLU_Q)) {
     amax = wave_max(amax);
     __shared__ float wmax[4];
     if (lane == 0) wmax[wave] = amax;

@@ -160,8 +160,8 @@ hipError_t act_recompute_launch(Kind kind, bool swiglu, const void* h, int64_t r
   } else {
     const bf16_t* hp = static_cast<const bf16_t*>(h);
     if (kind == KIND_E4M3) {
-      if (swiglu) return hipErrorInvalidValue;
-      go(act_recompute_kernel<bf16_t, false, true>, hp);
+      if (swiglu) go(act_recompute_kernel<bf16_t, true, true>, hp);
+      else go(act_recompute_kernel<bf16_t, false, true>, hp);
     } else if (swiglu) {
       go(act_recompute_kernel<bf16_t, true, false>, hp);
     } else {

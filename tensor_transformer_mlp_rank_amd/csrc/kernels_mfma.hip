@@ -34,7 +34,7 @@ hipError_t launch_one(const GemmArgs& g, const EpiArgs& e, hipStream_t s, int64_
 }  // namespace
 
 int mfma_grid(Step step, GemmArgs& g) {
-  const bool pair = (step == FC1_FWD_SWIGLU);
+  const bool pair = (step == FC1_FWD_SWIGLU || step == FC1_FWD_SWIGLU_Q);
   g.tiles_m = (g.M + kBM - 1) / kBM;
   const int bn = pair ? kBN / 2 : kBN;
   g.tiles_n = (g.N + bn - 1) / bn;
@@ -107,9 +107,13 @@ hipError_t mfma_launch(bool fp8, Step step, const GemmArgs& g, const EpiArgs& e,
     switch (step) {
       case FC1_FWD_GELU: return launch_one<true, true, true, EPI_BIAS_GELU, false>(g, e, s);
       case FC1_FWD_GELU_Q: return launch_one<true, true, true, EPI_BIAS_GELU_Q, false>(g, e, s);
+      case FC1_FWD_SWIGLU: return launch_one<true, true, true, EPI_SWIGLU, false>(g, e, s);
+      case FC1_FWD_SWIGLU_Q: return launch_one<true, true, true, EPI_SWIGLU_Q, false>(g, e, s);
       case FC2_FWD: return launch_one<true, true, true, EPI_STORE, false>(g, e, s);
       case FC2_DGRAD_GELU_Q:
         return launch_one<true, true, false, EPI_DGELU_Q, false, kA5>(g, e, s);
+      case FC2_DGRAD_SWIGLU_Q:
+        return launch_one<true, true, false, EPI_DSWIGLU_Q, false, kA5>(g, e, s);
       case FC1_DGRAD: return launch_one<true, true, false, EPI_STORE, false, kA5>(g, e, s);
       case WGRAD: return launch_one<true, false, false, EPI_F32, false, kA5>(g, e, s);
       case WGRAD_COLSUM: return launch_one<true, false, false, EPI_F32, true, kA5>(g, e, s);

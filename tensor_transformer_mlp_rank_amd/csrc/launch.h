@@ -21,6 +21,8 @@ enum Step : int {
   FC1_FWD_GELU_Q,     // e4m3: as FC1_FWD_GELU, a quantised to e4m3 in the epilogue
   FC2_DGRAD_GELU_Q,   // e4m3 weights, e5m2 dy: dH quantised to e5m2 in the epilogue
   QKV_FWD_BIAS,       // attention: x . Wqkv^T + bias -> packed q, k, v
+  FC1_FWD_SWIGLU_Q,   // e4m3: as FC1_FWD_SWIGLU, a quantised to e4m3 in the epilogue
+  FC2_DGRAD_SWIGLU_Q, // e4m3 weights, e5m2 dy: both halves of dH quantised to e5m2
   kNumSteps
 };
 

@@ -65,7 +65,8 @@ def D(**kw):
     (dict(tokens=1 << 30, hidden=1 << 21), E_SHAPE),   # a tile grid past 2^31 workgroups
     (dict(ffn_shard=(1 << 22) - 16 + 32, act="swiglu", has_bias=False), E_SHAPE),
     (dict(dtype=9), E_DTYPE), (dict(act=4), E_DTYPE),
-    (dict(act="swiglu", has_bias=True), E_UNSUP), (dict(act="swiglu", dtype="e4m3", has_bias=False), E_UNSUP),
+    (dict(act="swiglu", has_bias=True), E_UNSUP),
+    (dict(act="swiglu", dtype="e4m3", has_bias=True), E_UNSUP),
 ])
 def test_desc_validation(kw, code):
     assert fwd(D(**kw)) == code
@@ -109,7 +110,14 @@ def test_fp8_rules():
     assert wgrad(d8) == E_NULL
     assert dgrad(D(), fp8=sc) == E_DTYPE
     assert wgrad(D(), fp8=sc) == E_DTYPE
-    assert fwd(D(dtype="e4m3", act="swiglu", has_bias=False), fp8=sc) == E_UNSUP
+    # the gated block in E4M3: the same checks (its workspace has the pair
+    # tiles' amax partials)
+    d8g = D(dtype="e4m3", act="swiglu", has_bias=False)
+    need_g = tp.workspace_size(d8g, tp.CALL_FWD)
+    assert need_g >= 64 * 128 * 2
+    assert fwd(d8g, fp8=sc) == E_WS
+    assert fwd(d8g, fp8=sc, ws=P, nbytes=need_g - 1) == E_WS
+    assert dgrad(d8g) == E_NULL
 
 
 def _hist(length=4, reserved=0, ptrs=True):
@@ -160,6 +168,15 @@ def test_workspace_sizes():
     assert tp.workspace_size(D(dtype="f32"), tp.CALL_WGRAD) == 0
     assert tp.workspace_size(D(hidden=3), tp.CALL_FWD) == 0      # invalid desc
     assert tp.workspace_size(D(dtype="e4m3"), 7) == 0            # invalid call
+    # E4M3 forward: bf16 a (current scaling), then one amax partial per fc1
+    # workgroup: 32 x 8 tiles of 256 x 256 for GELU, 32 x 16 pair tiles of
+    # 256 x 128 for the gated block
+    a_bytes = 8192 * 2048 * 2
+    for act, parts in (("gelu", 32 * 8), ("swiglu", 32 * 16)):
+        d = D(tokens=8192, hidden=4096, ffn_shard=2048, dtype="e4m3", act=act,
+              has_bias=act == "gelu")
+        assert tp.workspace_size(d, tp.CALL_FWD) == a_bytes + (parts * 4 + 4 + 255) // 256 * 256
+        assert tp.workspace_size(d, tp.CALL_DGRAD) == (32 * 8 * 4 + 4 + 255) // 256 * 256
 
 
 def _colsum_bytes(H, GFs, splits=1):
@@ -283,8 +300,6 @@ def test_wgrad_recompute_workspace_size():
     up to 256 bytes) in front of the weight gradient's own workspace."""
     for dt, es in (("bf16", 2), ("f32", 4), ("e4m3", 1)):
         for act, bias in (("gelu", True), ("swiglu", False)):
-            if dt == "e4m3" and act == "swiglu":
-                continue
             d = D(tokens=100, ffn_shard=144, dtype=dt, act=act, has_bias=bias)
             a = (100 * 144 * es + 255) // 256 * 256
             assert tp.workspace_size(d, tp.CALL_WGRAD_RECOMPUTE) == \

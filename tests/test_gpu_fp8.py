@@ -67,7 +67,7 @@ def test_quantizer_all_zero_and_empty(tp):
     assert float(amax.cpu()[0]) == 0.0 and float(sinv.cpu()[0]) == 1.0
 
 
-def _fp8_case(tp, inp):
+def _fp8_case(tp, inp, act="gelu"):
     """Quantise x, W1, W2 on the GPU, check codes against the oracle, run the
     e4m3 forward; returns (gpu outputs, oracle dequantised inputs)."""
     q = {}
@@ -81,22 +81,26 @@ def _fp8_case(tp, inp):
         q[k] = (codes, sinv)
         deq[k] = oracle.dequantize_e4m3(rc, rsinv)
     T, H = inp["x"].shape
-    Fs = inp["W1"].shape[0]
-    desc = tp.make_desc(T, H, Fs, act="gelu", dtype="e4m3", has_bias=True)
-    b1 = inp["b1"].cuda()
-    say(f"  e4m3 fwd T={T} H={H} Fs={Fs}")
+    Fs = inp["W2"].shape[1]
+    desc = tp.make_desc(T, H, Fs, act=act, dtype="e4m3", has_bias=inp["b1"] is not None)
+    b1 = None if inp["b1"] is None else inp["b1"].cuda()
+    say(f"  e4m3 {act} fwd T={T} H={H} Fs={Fs}")
     out = tp.fwd(desc, q["x"][0], q["W1"][0], b1, q["W2"][0],
                  fp8_in_scales=(q["x"][1], q["W1"][1], q["W2"][1]))
     torch.cuda.synchronize()
     return {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in out.items()}, deq
 
 
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
 @pytest.mark.parametrize("T,H,Fs", [(300, 528, 272), (64, 256, 512), (1, 32, 16)])
-def test_fp8_forward_small(tp, T, H, Fs):
-    w = synth.WORKLOADS[5]
-    inp = synth.make_rank_inputs(w, tokens=T, hidden=H, ffn_shard=Fs, seed_base=500 + T)
-    gpu, deq = _fp8_case(tp, inp)
-    ref = oracle.rank_forward(deq["x"], deq["W1"], oracle.to_f64(inp["b1"]), deq["W2"], "gelu")
+def test_fp8_forward_small(tp, T, H, Fs, act):
+    """Current scaling (a through bf16 and the quantiser); act "swiglu": the
+    gated block, with the gated workload's value distributions."""
+    w = synth.WORKLOADS[4 if act == "swiglu" else 5]
+    inp = synth.make_rank_inputs(w, tokens=T, hidden=H, ffn_shard=Fs, dtype="e4m3",
+                                 seed_base=500 + T)
+    gpu, deq = _fp8_case(tp, inp, act)
+    ref = oracle.rank_forward(deq["x"], deq["W1"], oracle.to_f64(inp["b1"]), deq["W2"], act)
     e_y = rel_err(gpu["y"], ref["y"])
     e_h = rel_err(gpu["h"], ref["h"])
     # the quantised activation, dequantised with the reported scale
