@@ -97,10 +97,11 @@ def measured_traffic(name: str, kernel: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
-def step_labels(w, calls) -> list:
+def step_labels(w, calls, wgrad_t=False) -> list:
     """The library's launches in one step (the given entry points among
     forward, dgrad, wgrad), in order, under the names its timing facility
-    gives them."""
+    gives them. wgrad_t: the E4M3 weight gradients from token-contiguous
+    operands (a and dH transposed first)."""
     sfx = "." + w.dtype
     fp8 = w.dtype == "e4m3"
     seq = []
@@ -109,10 +110,13 @@ def step_labels(w, calls) -> list:
     if "dgrad" in calls:
         seq += ["fc2_dgrad", "dH_scale_update", "fc1_dgrad"] if fp8 else ["fc2_dgrad", "fc1_dgrad"]
     if "wgrad" in calls:
+        if wgrad_t:
+            seq += ["transpose_u8", "transpose_u8"]
         seq += ["fc2_wgrad", "fc1_wgrad"]
         if w.has_bias and w.dtype != "f32":
-            seq.append("db1_reduce")  # adds up the fused column-sum partials
-    return [k + sfx for k in seq]
+            # adds up the fused column-sum partials, or sums dH's token-contiguous rows
+            seq.append("db1_rowsum" if wgrad_t else "db1_reduce")
+    return [k if k == "transpose_u8" else k + sfx for k in seq]
 
 
 def _counter_rows(d: str) -> list:
@@ -398,8 +402,12 @@ class Job:
         self.__dict__.update(kw)
 
 
-def mlp_job(tp, torch, w, calls, dev) -> Job:
-    """The MLP block: forward, dgrad, wgrad (accumulate) on one rank's shard."""
+def mlp_job(tp, torch, w, calls, dev, wgrad_t=False) -> Job:
+    """The MLP block: forward, dgrad, wgrad (accumulate) on one rank's shard.
+    wgrad_t (E4M3): the weight gradients through tpmlp_bwd_wgrad_t, with x
+    and dy given token-contiguous as well (transposed with the inputs'
+    quantisation, before the timed steps) and a and dH transposed inside the
+    step."""
     import synth
     inp = synth.make_rank_inputs(w)
     d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
@@ -435,7 +443,13 @@ def mlp_job(tp, torch, w, calls, dev) -> Job:
                                     dy_scale_inv=sinv["dy"], dH_history=dH_hist)
         sc["wgrad"] = tp.fp8_scales(x_scale_inv=sinv["x"], a_scale_inv=a_hist.scale_inv,
                                     dy_scale_inv=sinv["dy"], dH_scale_inv=dH_hist.scale_inv)
+        if wgrad_t:
+            d["x_t"], d["dy_t"] = tp.transpose_u8(d["x"]), tp.transpose_u8(d["dy"])
+            buf["a_t"] = torch.empty((Fs, tp.token_ld(T)), dtype=torch.uint8, device=dev)
+            buf["dH_t"] = torch.empty((G * Fs, tp.token_ld(T)), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
+    elif wgrad_t:
+        raise SystemExit("--wgrad-t: E4M3 workloads only")
     stream = torch.cuda.current_stream()
 
     def fwd():
@@ -447,6 +461,13 @@ def mlp_job(tp, torch, w, calls, dev) -> Job:
                            fp8=sc["dgrad"], workspace=ws["dgrad"], stream=stream)
 
     def wgrad():
+        if wgrad_t:
+            tp.tpmlp_transpose_u8(buf["a"], T, Fs, buf["a_t"], stream=stream)
+            tp.tpmlp_transpose_u8(buf["dH"], T, G * Fs, buf["dH_t"], stream=stream)
+            tp.tpmlp_bwd_wgrad_t(desc, d["dy_t"], d["x_t"], buf["a_t"], buf["dH_t"], buf["dW1"],
+                                 buf["db1"], buf["dW2"], accumulate=True, fp8=sc["wgrad"],
+                                 stream=stream)
+            return
         tp.tpmlp_bwd_wgrad(desc, d["dy"], d["x"], buf["a"], buf["dH"], buf["dW1"], buf["db1"],
                            buf["dW2"], accumulate=True, fp8=sc["wgrad"], workspace=ws["wgrad"],
                            stream=stream)
@@ -485,13 +506,14 @@ def mlp_job(tp, torch, w, calls, dev) -> Job:
     return Job(
         name=w.name, dtype=w.dtype, stream=stream,
         fns=[(c, fns[c]) for c in calls], parity_step=parity_step,
-        labels=step_labels(w, calls), flops=w.flops(calls=calls),
+        labels=step_labels(w, calls, wgrad_t), flops=w.flops(calls=calls),
         # fc1's GEMMs have T*H*G*Fs multiply-adds each, fc2's T*H*Fs
         gemm_flops=lambda lab: 2.0 * T * H * Fs * (G if lab.startswith("fc1") else 1),
         metric=f"TFLOP/s per-rank TP-MLP {what} ({w.dtype}) and % of MFMA peak, 1 MI355X",
         config={"workload": w.name, "tokens": T, "batch": w.batch, "seq_len": w.seq,
                 "hidden": H, "ffn": w.ffn, "tp": w.tp, "ffn_shard": Fs, "act": w.act,
-                "parallelism": "one TP rank's shard on one GPU"},
+                "parallelism": "one TP rank's shard on one GPU",
+                **({"wgrad_operands": "token-contiguous"} if wgrad_t else {})},
         cpu=lambda n, gpu: cpu_baseline(w, calls, n, gpu=gpu))
 
 
@@ -693,6 +715,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3,
                     help="workload id (3: H=8192 TP=8 MLP shard; 6, 7: attention projections; "
                          "8, 9: mixture-of-experts expert MLPs)")
+    ap.add_argument("--wgrad-t", action="store_true",
+                    help="E4M3 MLP: weight gradients from token-contiguous operands "
+                         "(tpmlp_bwd_wgrad_t; a and dH transposed inside the step)")
     ap.add_argument("--calls", default=None,
                     help="MLP: entry points of a step, comma-separated among fwd,dgrad,wgrad "
                          "(default: the workload's)")
@@ -752,8 +777,10 @@ def main():
                 labels.append("dbqkv_reduce" + sfx)
             setup = 0
         else:
-            labels = step_labels(w, calls)
-            setup = 8 if w.dtype == "e4m3" else 0  # the FP8 step quantises its four inputs
+            labels = step_labels(w, calls, args.wgrad_t)
+            # the FP8 step quantises its four inputs (and with --wgrad-t
+            # transposes x and dy)
+            setup = (10 if args.wgrad_t else 8) if w.dtype == "e4m3" else 0
         out = write_traffic(w.name, labels, setup, *args.write_traffic, args.command)
         print(json.dumps(out["kernels"], indent=1))
         return
@@ -782,7 +809,7 @@ def main():
     elif attn:
         job = attn_job(tp, torch, w, dev)
     else:
-        job = mlp_job(tp, torch, w, calls, dev)
+        job = mlp_job(tp, torch, w, calls, dev, args.wgrad_t)
     stream = job.stream
 
     # parity first: one step in the timed steps' launch configuration, its
@@ -843,7 +870,8 @@ def main():
     per = tp.timing_collect()
     probe_mhz = {k: round(tp.timing_clock_mhz(k), 1) for k in per}
     tp.timing_enable(False)
-    if list(per) != job.labels:
+    # (a label launched twice in a step, the transposes of --wgrad-t, is one entry)
+    if list(per) != list(dict.fromkeys(job.labels)):
         raise SystemExit(f"unexpected launch sequence {list(per)}")
     dominant = max(per, key=lambda k: per[k][1])
     breakdown = {k: round(v[1] / v[0], 4) for k, v in per.items()}

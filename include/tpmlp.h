@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 8
+#define TPMLP_ABI_VERSION 9
 
 typedef enum {
   TPMLP_OK = 0,
@@ -254,6 +254,37 @@ tpmlp_status tpmlp_bwd_wgrad_recompute(const tpmlp_desc* desc, const void* dy, c
                                        float* db1, float* dW2, int32_t accumulate,
                                        const tpmlp_fp8_scales* fp8, void* workspace,
                                        size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Byte transpose into the token-contiguous layout of tpmlp_bwd_wgrad_t:
+ * dst[c][r] = src[r][c] for the row-major src [rows][cols] (1-byte codes,
+ * cols a multiple of 16), dst [cols][Tp] with Tp = rows rounded up to a
+ * multiple of 16 and dst's columns [rows, Tp) zero (the cast-transpose
+ * layout in which FP8 training keeps the operands it reads along the tokens).
+ * src and dst are device pointers, 16-byte aligned, not overlapping.
+ * TPMLP_E_SHAPE for negative sizes or cols not a multiple of 16.
+ */
+tpmlp_status tpmlp_transpose_u8(const void* src, int64_t rows, int64_t cols, void* dst,
+                                hipStream_t stream);
+
+/*
+ * tpmlp_bwd_wgrad for E4M3 from token-contiguous copies of its four operands
+ * (the tokens are the products' K): dy_t [H][Tp] (E5M2), x_t [H][Tp] (E4M3),
+ * a_t [Fs][Tp] (E4M3), dH_t [G*Fs][Tp] (E5M2), Tp = T rounded up to a multiple
+ * of 16, columns [T, Tp) zero, as tpmlp_transpose_u8 writes them. With both
+ * operands of each product contiguous along K, the products run the forward's
+ * FP8 schedule instead of reading 8-bit data through LDS transposes.
+ * Same arguments otherwise, and the same results up to the float32 rounding
+ * of the sums (a different MFMA shape): dW2 = dy^T . a, dW1 = dH^T . x, each
+ * times its operands' dequantisation factors, db1 = the dequantised dH
+ * summed over the tokens (has_bias); accumulate as tpmlp_bwd_wgrad.
+ * Reproducible bit for bit. No workspace. TPMLP_E_UNSUPPORTED unless dtype
+ * is E4M3.
+ */
+tpmlp_status tpmlp_bwd_wgrad_t(const tpmlp_desc* desc, const void* dy_t, const void* x_t,
+                               const void* a_t, const void* dH_t, float* dW1, float* db1,
+                               float* dW2, int32_t accumulate, const tpmlp_fp8_scales* fp8,
+                               hipStream_t stream);
 
 /*
  * tpmlp_bwd_wgrad without a workspace, for callers that cannot allocate

@@ -133,6 +133,8 @@ def _load():
     L.tpmlp_bwd_wgrad_noalloc.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, i32, psc, vp]
     L.tpmlp_bwd_wgrad_recompute.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, i32, psc, vp, sz,
                                             vp]
+    L.tpmlp_bwd_wgrad_t.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, i32, psc, vp]
+    L.tpmlp_transpose_u8.argtypes = [vp, i64, i64, vp, vp]
     L.tpmlp_quantize_e4m3.argtypes = [i32, vp, i64, vp, vp, vp, vp, sz, vp]
     L.tpmlp_quantize_e5m2.argtypes = [i32, vp, i64, vp, vp, vp, vp, sz, vp]
     L.tpmlp_quantize_workspace_size.argtypes = [i64]
@@ -155,7 +157,7 @@ def _load():
     L.tpmlp_moe_workspace_size.argtypes = [pm]
     L.tpmlp_moe_workspace_size.restype = sz
     for f in ("tpmlp_fwd", "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad", "tpmlp_bwd_wgrad_noalloc",
-              "tpmlp_bwd_wgrad_recompute",
+              "tpmlp_bwd_wgrad_recompute", "tpmlp_bwd_wgrad_t", "tpmlp_transpose_u8",
               "tpmlp_quantize_e4m3",
               "tpmlp_quantize_e5m2", "tpmlp_timing_enable", "tpmlp_attn_qkv_fwd",
               "tpmlp_attn_out_fwd", "tpmlp_attn_out_bwd_dgrad", "tpmlp_attn_out_bwd_wgrad",
@@ -271,6 +273,19 @@ def tpmlp_bwd_wgrad_noalloc(desc, dy, x, a, dH, dW1, db1, dW2, accumulate=False,
                                        _stream(stream)), "tpmlp_bwd_wgrad_noalloc")
 
 
+def tpmlp_bwd_wgrad_t(desc, dy_t, x_t, a_t, dH_t, dW1, db1, dW2, accumulate=False, fp8=None,
+                      stream=None):
+    sc = None if fp8 is None else ctypes.byref(fp8)
+    _check(lib.tpmlp_bwd_wgrad_t(ctypes.byref(desc), _ptr(dy_t), _ptr(x_t), _ptr(a_t),
+                                 _ptr(dH_t), _ptr(dW1), _ptr(db1), _ptr(dW2),
+                                 int(bool(accumulate)), sc, _stream(stream)), "tpmlp_bwd_wgrad_t")
+
+
+def tpmlp_transpose_u8(src, rows, cols, dst, stream=None):
+    _check(lib.tpmlp_transpose_u8(_ptr(src), rows, cols, _ptr(dst), _stream(stream)),
+           "tpmlp_transpose_u8")
+
+
 SCRATCH_BYTES = 8 << 20  # TPMLP_SCRATCH_BYTES
 
 
@@ -362,6 +377,37 @@ def bwd_wgrad(desc, dy, x, a, dH, accumulate_into=None, fp8=None, stream=None, r
     call = tpmlp_bwd_wgrad_recompute if recompute else tpmlp_bwd_wgrad
     call(desc, dy, x, a, dH, out["dW1"], out.get("db1"), out["dW2"],
          accumulate=accumulate_into is not None, fp8=sc, workspace=ws, stream=stream)
+    return out
+
+
+def token_ld(T):
+    """Row length of the token-contiguous layout: T rounded up to 16."""
+    return (T + 15) // 16 * 16
+
+
+def transpose_u8(src, stream=None):
+    """The token-contiguous copy [cols, token_ld(rows)] of a [rows, cols]
+    uint8 tensor of FP8 codes (tpmlp_transpose_u8)."""
+    rows, cols = src.shape
+    dst = _empty((cols, token_ld(rows)), torch.uint8, src.device)
+    tpmlp_transpose_u8(src, rows, cols, dst, stream)
+    return dst
+
+
+def bwd_wgrad_t(desc, dy_t, x_t, a_t, dH_t, accumulate_into=None, fp8=None, stream=None):
+    """bwd_wgrad for E4M3 from token-contiguous operands (tpmlp_bwd_wgrad_t)."""
+    dev = dy_t.device
+    H, Fs = desc.hidden, desc.ffn_shard
+    G = 2 if desc.act == SWIGLU else 1
+    if accumulate_into is not None:
+        out = accumulate_into
+    else:
+        out = {"dW1": _empty((G * Fs, H), torch.float32, dev),
+               "db1": _empty((G * Fs,), torch.float32, dev) if desc.has_bias else None,
+               "dW2": _empty((H, Fs), torch.float32, dev)}
+    sc = None if fp8 is None else fp8_scales(**fp8)
+    tpmlp_bwd_wgrad_t(desc, dy_t, x_t, a_t, dH_t, out["dW1"], out.get("db1"), out["dW2"],
+                      accumulate=accumulate_into is not None, fp8=sc, stream=stream)
     return out
 
 
@@ -570,6 +616,7 @@ def timing_collect(cap: int = 64) -> dict:
 __all__ = ["Desc", "Fp8Scales", "Fp8History", "DelayedScaling", "fp8_scales", "TpmlpError",
            "make_desc", "workspace_size", "tpmlp_fwd", "tpmlp_bwd_dgrad", "tpmlp_bwd_wgrad",
            "tpmlp_bwd_wgrad_noalloc", "tpmlp_bwd_wgrad_recompute", "SCRATCH_BYTES",
+           "tpmlp_bwd_wgrad_t", "tpmlp_transpose_u8", "token_ld", "transpose_u8", "bwd_wgrad_t",
            "CALL_FWD", "CALL_DGRAD", "CALL_WGRAD", "CALL_WGRAD_RECOMPUTE",
            "tpmlp_quantize_e4m3", "tpmlp_quantize_e5m2", "fwd", "bwd_dgrad", "bwd_wgrad",
            "quantize_e4m3", "quantize_e5m2", "timing_enable", "timing_collect", "timing_clock_mhz",

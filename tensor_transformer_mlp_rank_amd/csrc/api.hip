@@ -855,6 +855,60 @@ tpmlp_status tpmlp_bwd_wgrad_recompute(const tpmlp_desc* d, const void* dy, cons
                    static_cast<char*>(ws) + ab, ws_bytes - ab, s);
 }
 
+// Row stride of a token-contiguous copy: T rounded up to 16 bytes.
+int64_t token_ld(int64_t T) { return (T + 15) / 16 * 16; }
+
+tpmlp_status tpmlp_transpose_u8(const void* src, int64_t rows, int64_t cols, void* dst,
+                                hipStream_t s) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0 || rows > kMaxTokens || cols > kMaxDim)
+    return TPMLP_E_SHAPE;
+  if (rows == 0 || cols == 0) return TPMLP_OK;
+  tpmlp_status st = check_ptrs({src, dst});
+  if (st != TPMLP_OK) return st;
+  const hipError_t err = timed("transpose_u8", s, [&]() {
+    return transpose_u8_launch(src, rows, cols, dst, token_ld(rows), s);
+  });
+  return err == hipSuccess ? TPMLP_OK : hip_fail(err);
+}
+
+tpmlp_status tpmlp_bwd_wgrad_t(const tpmlp_desc* d, const void* dy_t, const void* x_t,
+                               const void* a_t, const void* dH_t, float* dW1, float* db1,
+                               float* dW2, int32_t accumulate, const tpmlp_fp8_scales* fp8,
+                               hipStream_t s) {
+  tpmlp_status st = check_wgrad(d, dy_t, x_t, a_t, dH_t, dW1, db1, dW2, accumulate, fp8);
+  if (st != TPMLP_OK) return st;
+  if (d->dtype != TPMLP_E4M3) return TPMLP_E_UNSUPPORTED;
+  const int64_t T = d->tokens, H = d->hidden, Fs = d->ffn_shard;
+  const int64_t GFs = d->act == TPMLP_ACT_SWIGLU ? 2 * Fs : Fs;
+  hipError_t err;
+  // no tokens: accumulating adds nothing; otherwise the products of K = 0
+  // write zeros (every operand range empty) and db1 sums nothing
+  if (T == 0 && accumulate) return TPMLP_OK;
+  const int64_t ld = token_ld(T);
+  // dW2 [H, Fs] = dy^T . a: A = dy_t [M=H][K=T], B = a_t [N=Fs][K=T], both K-major
+  EpiArgs e1{};
+  e1.out = dW2; e1.ldo = Fs; e1.accumulate = accumulate;
+  e1.scale_a = fp8->dy_scale_inv; e1.scale_b = fp8->a_scale_inv;
+  GemmArgs g1 = make_gemm(dy_t, ld, a_t, ld, H, Fs, T, 0);
+  err = run_step(KIND_E4M3, WGRAD_T, label(KIND_E4M3, 4), g1, e1, s);
+  if (err != hipSuccess) return hip_fail(err);
+  // dW1 [GFs, H] = dH^T . x: A = dH_t [M=GFs][K=T], B = x_t [N=H][K=T]
+  EpiArgs e2{};
+  e2.out = dW1; e2.ldo = H; e2.accumulate = accumulate;
+  e2.scale_a = fp8->dH_scale_inv; e2.scale_b = fp8->x_scale_inv;
+  GemmArgs g2 = make_gemm(dH_t, ld, x_t, ld, GFs, H, T, 0);
+  err = run_step(KIND_E4M3, WGRAD_T, label(KIND_E4M3, 5), g2, e2, s);
+  if (err != hipSuccess) return hip_fail(err);
+  if (d->has_bias) {
+    // db1 = the rows of dH_t summed, dequantised
+    err = timed("db1_rowsum.e4m3", s, [&]() {
+      return rowsum_e5m2_launch(dH_t, GFs, T, ld, fp8->dH_scale_inv, db1, accumulate, s);
+    });
+    if (err != hipSuccess) return hip_fail(err);
+  }
+  return TPMLP_OK;
+}
+
 tpmlp_status tpmlp_bwd_wgrad_noalloc(const tpmlp_desc* d, const void* dy, const void* x,
                                      const void* a_saved, const void* dH, float* dW1,
                                      float* db1, float* dW2, int32_t accumulate,

@@ -1286,7 +1286,16 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
         auto& d = acc[r][c];
         auto& a = ga[r % 3];
         auto& b = gb[par][c];
-        asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+        // operand formats: cbsz / blgp 1 = E5M2 (A / B), 0 = E4M3
+        if constexpr ((FMT & 3) == 1)
+          asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1" : "+a"(d) : "v"(a), "v"(b));
+        else if constexpr ((FMT & 3) == 2)
+          asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 blgp:1" : "+a"(d) : "v"(a), "v"(b));
+        else if constexpr ((FMT & 3) == 3)
+          asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:1" : "+a"(d)
+                       : "v"(a), "v"(b));
+        else
+          asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
       }
       if constexpr (c == 1 && r < 7) read16(PAR, std::false_type{}, IC<r + 1>{});
       if constexpr (i >= 10 && i <= 52 && (i - 10) % 6 == 0) read16(PAR1, std::true_type{}, IC<(i - 10) / 6>{});
@@ -1344,17 +1353,22 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
       stage(kt + 1, FAST, IC<1>{});
     }
   };
-  auto main_loop = [&](auto stage) __attribute__((always_inline)) {
+  // `after`: the fence after the loop, inside each loop form, so that no
+  // read is in flight where the two forms' paths meet
+  auto main_loop = [&](auto stage, auto after) __attribute__((always_inline)) {
     if constexpr (!A_K && !B_K) {
       pair_loop(stage, std::false_type{}, nk + pad);
+      after();
     } else {
       static_assert(!COLSUM, "the fused column sum reads an MN-major A tile");
       if (g.K % kStep == 0) {
         if constexpr (A_K) la.fold_rows();
         if constexpr (B_K) lb.fold_rows();
         pair_loop(stage, std::true_type{}, nk + pad);
+        after();
       } else {
         pair_loop(stage, std::false_type{}, nk + pad);
+        after();
       }
     }
   };
@@ -1396,21 +1410,19 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(const GemmArgs g
     static_for<8>([&](auto J) { read16(IC<0>{}, std::true_type{}, J); });
     read16(IC<0>{}, std::false_type{}, IC<0>{});
     frag_fence16();
-    main_loop(stage_f16);
-    frag_fence16();
+    main_loop(stage_f16, frag_fence16);
   } else if constexpr (!IS_FP8) {
     static_for<2 * kFr>([&](auto J) { read_one(IC<0>{}, IC<0>{}, J); });
     frag_fence();
-    main_loop(stage_iter16);
+    main_loop(stage_iter16, frag_fence);
   } else {
     static_for<8 * (kKs - 1)>([&](auto J) {
       constexpr int j = decltype(J)::value;
       read_one(IC<0>{}, IC<j / 8>{}, IC<j & 7>{});
     });
     frag_fence();
-    main_loop(stage_iter_rolling);
+    main_loop(stage_iter_rolling, frag_fence);
   }
-  if constexpr (!kF16) frag_fence();
   if constexpr (!kAcc32) {
     // the last MFMAs (asm, unseen by the compiler's hazard checks) complete
     // before any instruction reads their accumulators

@@ -135,7 +135,93 @@ __global__ void __launch_bounds__(256) fill_zero_i32_kernel(int* __restrict__ p,
   for (int i = (int)(blockIdx.x * 256 + threadIdx.x); i < n; i += (int)(gridDim.x * 256)) p[i] = 0;
 }
 
+// Byte transpose: dst[c][r] = src[r][c] for src [rows][cols] (cols a
+// multiple of 16), dst [cols][ld] (ld a multiple of 16, at least rows), the
+// columns r in [rows, ld) of dst zero. One 64 x 64 tile per block: each
+// thread loads 16 bytes of a source row into LDS, then gathers 16 bytes of
+// one source column (a destination row) and stores them with one 16-byte
+// store.
+__global__ void __launch_bounds__(256) transpose_u8_kernel(const uint8_t* __restrict__ src,
+                                                           int64_t rows, int64_t cols,
+                                                           uint8_t* __restrict__ dst, int64_t ld) {
+  __shared__ uint8_t tile[64][64 + 4];
+  const int t = threadIdx.x, q = t >> 2, k = t & 3;
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  {
+    const int64_t r = r0 + q, c = c0 + 16 * k;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < rows && c < cols) v = *reinterpret_cast<const u32x4*>(src + r * cols + c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(&tile[q][16 * k + 4 * j]) = v[j];
+  }
+  __syncthreads();
+  const int64_t c = c0 + q, r = r0 + 16 * k;  // destination row c, bytes r .. r+15
+  if (c < cols && r < ld) {
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) w |= (uint32_t)tile[16 * k + 4 * j + b][q] << (8 * b);
+      o[j] = w;
+    }
+    *reinterpret_cast<u32x4*>(dst + c * ld + r) = o;
+  }
+}
+
+// db1 from a token-contiguous E5M2 dH^T [rows][ld]: out[f] (+)= scale_inv *
+// sum over t < n of decode(dH^T[f][t]); one block per row, a fixed order of
+// the partial sums (reproducible bit for bit).
+__global__ void __launch_bounds__(256) rowsum_e5m2_kernel(const uint8_t* __restrict__ src,
+                                                          int64_t n, int64_t ld,
+                                                          const float* __restrict__ scale_inv,
+                                                          float* __restrict__ out, int accumulate) {
+  const uint8_t* row = src + (int64_t)blockIdx.x * ld;
+  float s = 0.f;
+  for (int64_t i = 16 * (int64_t)threadIdx.x; i < n; i += 16 * 256) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(row + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)v[j], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)v[j], true);
+      const float e[4] = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (i + 4 * j + b < n) s += e[b];
+    }
+  }
+  __shared__ float red[256];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float v = red[0] * *scale_inv;
+    out[blockIdx.x] = accumulate ? out[blockIdx.x] + v : v;
+  }
+}
+
 }  // namespace
+
+hipError_t transpose_u8_launch(const void* src, int64_t rows, int64_t cols, void* dst, int64_t ld,
+                               hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  const int64_t gx = (rows + 63) / 64, gy = (cols + 63) / 64;
+  if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_u8_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(src), rows, cols, static_cast<uint8_t*>(dst), ld);
+  return hipGetLastError();
+}
+
+hipError_t rowsum_e5m2_launch(const void* src, int64_t rows, int64_t n, int64_t ld,
+                              const float* scale_inv, float* out, int accumulate, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rowsum_e5m2_kernel, dim3((unsigned)rows), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(src), n, ld, scale_inv, out, accumulate);
+  return hipGetLastError();
+}
 
 hipError_t fill_zero_i32_launch(int* p, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;

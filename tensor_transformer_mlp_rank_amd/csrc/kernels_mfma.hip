@@ -117,6 +117,7 @@ hipError_t mfma_launch(bool fp8, Step step, const GemmArgs& g, const EpiArgs& e,
       case FC1_DGRAD: return launch_one<true, true, false, EPI_STORE, false, kA5>(g, e, s);
       case WGRAD: return launch_one<true, false, false, EPI_F32, false, kA5>(g, e, s);
       case WGRAD_COLSUM: return launch_one<true, false, false, EPI_F32, true, kA5>(g, e, s);
+      case WGRAD_T: return launch_one<true, true, true, EPI_F32, false, kA5>(g, e, s);
       default: return hipErrorInvalidValue;
     }
   }

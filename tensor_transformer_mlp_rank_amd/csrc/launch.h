@@ -23,6 +23,8 @@ enum Step : int {
   QKV_FWD_BIAS,       // attention: x . Wqkv^T + bias -> packed q, k, v
   FC1_FWD_SWIGLU_Q,   // e4m3: as FC1_FWD_SWIGLU, a quantised to e4m3 in the epilogue
   FC2_DGRAD_SWIGLU_Q, // e4m3 weights, e5m2 dy: both halves of dH quantised to e5m2
+  WGRAD_T,            // e4m3: A^T . B over tokens from token-contiguous copies of both
+                      // operands (A e5m2) -> fp32
   kNumSteps
 };
 
@@ -70,6 +72,13 @@ hipError_t act_recompute_launch(Kind kind, bool swiglu, const void* h, int64_t r
 // n ints at p set to zero (a kernel, so that the call can be captured into a
 // graph).
 hipError_t fill_zero_i32_launch(int* p, int n, hipStream_t stream);
+// dst [cols][ld] = transpose of the byte array src [rows][cols] (cols and ld
+// multiples of 16, ld >= rows; dst's columns [rows, ld) zero)
+hipError_t transpose_u8_launch(const void* src, int64_t rows, int64_t cols, void* dst, int64_t ld,
+                               hipStream_t stream);
+// out[f] (+)= *scale_inv * sum over t < n of E5M2 src[f][t] (rows rows of ld bytes)
+hipError_t rowsum_e5m2_launch(const void* src, int64_t rows, int64_t n, int64_t ld,
+                              const float* scale_inv, float* out, int accumulate, hipStream_t stream);
 
 // Quantiser passes. src_bf16 selects the source type (bf16 or f32).
 int quant_parts(int64_t n);

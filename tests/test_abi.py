@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert tp.lib.tpmlp_abi_version() == 8
+    assert tp.lib.tpmlp_abi_version() == 9
     for s in range(9):
         assert len(tp.lib.tpmlp_strerror(s)) > 5
     assert tp.lib.tpmlp_last_hip_error() == b""
@@ -293,6 +293,45 @@ def test_wgrad_recompute_validation(name):
     assert wgrad_recompute(D(), ws=None, nbytes=0) == E_WS
     assert wgrad_recompute(D(), nbytes=need - 1) == E_WS
     assert wgrad_recompute(D(), ws=MIS, nbytes=need) == E_ALIGN
+
+
+def wgrad_t(desc, dy=P, x=P, a=P, dH=P, dW1=P, db1=P, dW2=P, acc=0, fp8=None):
+    sc = None if fp8 is None else ctypes.byref(fp8)
+    return tp.lib.tpmlp_bwd_wgrad_t(ctypes.byref(desc), dy, x, a, dH, dW1, db1, dW2, acc, sc,
+                                    None)
+
+
+@pytest.mark.parametrize("name", ["dy", "x", "a", "dH", "dW1", "dW2"])
+def test_wgrad_t_validation(name):
+    """The token-contiguous weight gradient checks its arguments as
+    tpmlp_bwd_wgrad does; it is E4M3 only and takes no workspace."""
+    d8 = D(dtype="e4m3")
+    full = dict(dy_scale_inv=P, x_scale_inv=P, a_scale_inv=P, dH_scale_inv=P)
+    sc = tp.Fp8Scales(**full)
+    assert wgrad_t(d8, fp8=sc, **{name: None}) == E_NULL
+    assert wgrad_t(d8, fp8=sc, **{name: MIS}) == E_ALIGN
+    assert wgrad_t(d8, fp8=sc, db1=None) == E_NULL          # bias without db1
+    assert wgrad_t(d8, fp8=sc, acc=2) == E_DTYPE
+    assert wgrad_t(d8) == E_NULL                            # FP8 without scales
+    for k in full:
+        assert wgrad_t(d8, fp8=tp.Fp8Scales(**dict(full, **{k: None}))) == E_NULL
+    assert wgrad_t(D(), fp8=None) == E_UNSUP                # bf16: not this entry
+    assert wgrad_t(D(dtype="f32")) == E_UNSUP
+    assert wgrad_t(D(hidden=3), fp8=sc) == E_SHAPE
+
+
+def test_transpose_u8_validation():
+    """Sizes: cols a multiple of 16, neither negative; empty arrays are a
+    no-op (nothing enqueued, NULL pointers accepted)."""
+    T = tp.lib.tpmlp_transpose_u8
+    assert T(P, 4, 24, P, None) == E_SHAPE
+    assert T(P, -1, 16, P, None) == E_SHAPE
+    assert T(P, 4, -16, P, None) == E_SHAPE
+    assert T(None, 0, 16, None, None) == 0
+    assert T(None, 7, 0, None, None) == 0
+    assert T(None, 4, 16, P, None) == E_NULL
+    assert T(P, 4, 16, MIS, None) == E_ALIGN
+    assert tp.token_ld(0) == 0 and tp.token_ld(1) == 16 and tp.token_ld(32) == 32
 
 
 def test_wgrad_recompute_workspace_size():

@@ -345,6 +345,14 @@ def _fp8_block(tp, T, H, Fs, seed, prior=False, act="gelu"):
                       accumulate_into=acc(), fp8=fp8_wgrad(cu(a_sinv), cu(dH_sinv)))
     torch.cuda.synchronize()
     exact = {k: rel_err(wg[k].cpu(), rw[k]) for k in wkeys}
+    # the same from token-contiguous copies of the codes (tpmlp_bwd_wgrad_t)
+    codes_t = {"dy": tp.transpose_u8(dev["dy"][0]), "x": tp.transpose_u8(dev["x"][0]),
+               "a": tp.transpose_u8(torch.from_numpy(rf["a_codes"]).cuda()),
+               "dH": tp.transpose_u8(torch.from_numpy(rg["dH_codes"]).cuda())}
+    wt = tp.bwd_wgrad_t(desc, codes_t["dy"], codes_t["x"], codes_t["a"], codes_t["dH"],
+                        accumulate_into=acc(), fp8=fp8_wgrad(cu(a_sinv), cu(dH_sinv)))
+    torch.cuda.synchronize()
+    exact.update({k + " (t)": rel_err(wt[k].cpu(), rw[k]) for k in wkeys})
     say("    given codes: " + " ".join(f"{k}={v:.2e}" for k, v in exact.items()))
     for k, v in exact.items():
         assert v <= EXACT_TOL, (k, v)
@@ -371,6 +379,14 @@ def _fp8_block(tp, T, H, Fs, seed, prior=False, act="gelu"):
         chain[k] = rel_err(wg2[k].cpu(), rw[k])
         excess = np.abs(oracle.to_f64(wg2[k].cpu()) - rw[k]) - bound[k] - EXACT_TOL * _amax(rw[k])
         assert np.all(excess <= 0), (k, float(np.max(excess)))
+    # the chain's weight gradients from token-contiguous copies of its codes
+    wt2 = tp.bwd_wgrad_t(desc, codes_t["dy"], codes_t["x"], tp.transpose_u8(f["a"]),
+                         tp.transpose_u8(g2["dH"]), accumulate_into=acc(),
+                         fp8=fp8_wgrad(ah.scale_inv, dh2.scale_inv))
+    torch.cuda.synchronize()
+    for k in wkeys:
+        e_t = rel_err(wt2[k].cpu(), oracle.to_f64(wg2[k].cpu()))
+        assert e_t <= EXACT_TOL, (k, e_t)
     # selective recomputation: a's codes from the saved h at 1 / a_scale_inv;
     # where that factor is the forward's, the codes and so the results are
     # the saved path's bit for bit (dW1 and db1, which do not read a, always)
@@ -463,6 +479,36 @@ def test_fp8_zero_tokens_still_step_the_histories(tp):
             assert float(hist.scale.cpu()[0]) == float(want_s), fmt
             assert float(hist.scale_inv.cpu()[0]) == float(want_si), fmt
         assert torch.all(dW1 == 0) and torch.all(db1 == 0) and torch.all(dW2 == 0)
+        # the token-contiguous entry: the same zeros, and accumulating adds nothing
+        for t in (dW1, db1, dW2):
+            t.fill_(7.0)
+        sc_w = tp.fp8_scales(x_scale_inv=one(), a_scale_inv=one(), dy_scale_inv=one(),
+                             dH_scale_inv=one())
+        tp.tpmlp_bwd_wgrad_t(desc, anyp, anyp, anyp, anyp, dW1, db1, dW2, accumulate=True,
+                             fp8=sc_w)
+        torch.cuda.synchronize()
+        assert torch.all(dW1 == 7) and torch.all(db1 == 7) and torch.all(dW2 == 7)
+        tp.tpmlp_bwd_wgrad_t(desc, anyp, anyp, anyp, anyp, dW1, db1, dW2, accumulate=False,
+                             fp8=sc_w)
+        torch.cuda.synchronize()
+        assert torch.all(dW1 == 0) and torch.all(db1 == 0) and torch.all(dW2 == 0)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 16), (37, 48), (64, 64), (300, 528), (513, 1040),
+                                       (4200, 4208)])
+def test_transpose_u8_exact(tp, rows, cols):
+    """The token-contiguous copy: every byte transposed, the padding columns
+    [rows, round_up(rows, 16)) zero (including bytes that are NaN codes)."""
+    rng = np.random.default_rng(rows * 7 + cols)
+    src = rng.integers(0, 256, size=(rows, cols), dtype=np.uint8)
+    say(f"  transpose {rows} x {cols}")
+    got = tp.transpose_u8(torch.from_numpy(src).cuda())
+    torch.cuda.synchronize()
+    ld = (rows + 15) // 16 * 16
+    want = np.zeros((cols, ld), np.uint8)
+    want[:, :rows] = src.T
+    assert got.shape == (cols, ld)
+    assert np.array_equal(got.cpu().numpy(), want)
 
 
 def test_fp8_block_full_size_sampled(tp):
