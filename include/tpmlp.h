@@ -279,7 +279,10 @@ tpmlp_status tpmlp_transpose_u8(const void* src, int64_t rows, int64_t cols, voi
  * times its operands' dequantisation factors, db1 = the dequantised dH
  * summed over the tokens (has_bias); accumulate as tpmlp_bwd_wgrad.
  * Reproducible bit for bit. No workspace. TPMLP_E_UNSUPPORTED unless dtype
- * is E4M3.
+ * is E4M3; TPMLP_E_SHAPE for Tp above 2^23 - 256 (a tile's 256 rows of Tp
+ * bytes are addressed with 32-bit offsets). The products and the pages'
+ * weight-gradient step: code tour "The Tensor-Parallel Primitives"; FP8
+ * through Transformer Engine: concept note "Key math / How it works".
  */
 tpmlp_status tpmlp_bwd_wgrad_t(const tpmlp_desc* desc, const void* dy_t, const void* x_t,
                                const void* a_t, const void* dH_t, float* dW1, float* db1,

@@ -857,6 +857,7 @@ tpmlp_status tpmlp_bwd_wgrad_recompute(const tpmlp_desc* d, const void* dy, cons
 
 // Row stride of a token-contiguous copy: T rounded up to 16 bytes.
 int64_t token_ld(int64_t T) { return (T + 15) / 16 * 16; }
+constexpr int64_t kMaxTokenLdT = (int64_t(1) << 23) - 256;
 
 tpmlp_status tpmlp_transpose_u8(const void* src, int64_t rows, int64_t cols, void* dst,
                                 hipStream_t s) {
@@ -880,6 +881,9 @@ tpmlp_status tpmlp_bwd_wgrad_t(const tpmlp_desc* d, const void* dy_t, const void
   if (d->dtype != TPMLP_E4M3) return TPMLP_E_UNSUPPORTED;
   const int64_t T = d->tokens, H = d->hidden, Fs = d->ffn_shard;
   const int64_t GFs = d->act == TPMLP_ACT_SWIGLU ? 2 * Fs : Fs;
+  // a 256-row tile of a token-contiguous operand is addressed with 32-bit
+  // offsets from its first row: 256 rows of Tp bytes must stay below 2^31
+  if (token_ld(T) > kMaxTokenLdT) return TPMLP_E_SHAPE;
   hipError_t err;
   // no tokens: accumulating adds nothing; otherwise the products of K = 0
   // write zeros (every operand range empty) and db1 sums nothing

@@ -318,6 +318,8 @@ def test_wgrad_t_validation(name):
     assert wgrad_t(D(), fp8=None) == E_UNSUP                # bf16: not this entry
     assert wgrad_t(D(dtype="f32")) == E_UNSUP
     assert wgrad_t(D(hidden=3), fp8=sc) == E_SHAPE
+    # token-contiguous rows past 2^23 - 256 bytes: 256 of them overflow 32-bit offsets
+    assert wgrad_t(D(dtype="e4m3", tokens=(1 << 23) - 255), fp8=sc) == E_SHAPE
 
 
 def test_transpose_u8_validation():
