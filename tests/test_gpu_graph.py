@@ -3,9 +3,11 @@ forward, dgrad and weight gradients with accumulation; the attention
 projections; the grouped expert MLPs) is captured once on a side stream and
 replayed several times, with eager work and synchronisations between the
 replays. The library enqueues kernels only (no memory set or copy nodes, no
-allocation), so every replay must reproduce the eager results bit for bit
-(the kernels are deterministic: fixed summation orders, no atomics); the
-accumulating weight gradients must grow by exactly one step per replay."""
+allocation; the counters of a split partial last round are cleared by a
+kernel), so every replay must reproduce the eager results bit for bit (the
+kernels are deterministic: fixed summation orders, no sum through atomics);
+the accumulating weight gradients must grow by exactly one step per
+replay."""
 import pytest
 import torch
 
@@ -49,9 +51,12 @@ def _replays(g, snapshot, n=3):
     return got
 
 
+# (2048, 4352, 4336): the weight gradients' 289- and 578-tile grids split their
+# partial last round (counters cleared in the graph, halves met through the
+# workspace on every replay)
+@pytest.mark.parametrize("T,H,Fs", [(1030, 528, 272), (2048, 4352, 4336)])
 @pytest.mark.parametrize("act,bias", [("gelu", True), ("swiglu", False)])
-def test_mlp_step_in_a_graph(tp, act, bias):
-    T, H, Fs = 1030, 528, 272
+def test_mlp_step_in_a_graph(tp, act, bias, T, H, Fs):
     w = synth.WORKLOADS[2 if act == "gelu" else 4]
     inp = synth.make_rank_inputs(w, tokens=T, hidden=H, ffn_shard=Fs, seed_base=31)
     G = 2 if act == "swiglu" else 1
