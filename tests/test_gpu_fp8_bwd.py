@@ -105,11 +105,14 @@ def _scale_for(amax, fmt):
 # Error bounds for device results that decide a rounding. The FP8 matrix
 # instructions do not sum their products exactly in float32: measured against
 # exact sums, their results carry errors up to about 3e-5 of the largest
-# |result| of a product (5e-5 with heavy-tailed inputs), some hundred float32
-# ulps, so the bound on a product sum is 1.5e-4 of the largest |sum| in its
-# tensor; on the float32 activation arithmetic after it, 1e-5 of the value.
+# |result| of a product (5e-5 with heavy-tailed inputs, and up to 1.1e-4 for
+# the gated block's weight gradients over about 100 tokens, whose operands
+# are products of Gaussians), some hundred float32 ulps, so the bound on a
+# product sum is 1.5e-4 of the largest |sum| in its tensor; on the float32
+# activation arithmetic after it, 1e-5 of the value.
 SUM_ERR, REL_ERR = 1.5e-4, 1e-5
-EXACT_TOL = 1e-4     # products of identical FP8 inputs, against max |oracle|
+# products of identical FP8 inputs, against max |oracle|: the same bound
+EXACT_TOL = SUM_ERR
 
 
 def _valid_rounding(got, t, d, rnd):
