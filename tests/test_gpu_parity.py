@@ -327,6 +327,8 @@ def test_wgrad_split_k(tp, act, bias):
     (1 << 20, 64, 64, "bf16"),       # a million tokens: 4096 M-tiles, weight gradients over K = 2^20
     (256, 1 << 16, 256, "bf16"),     # a 65536-wide hidden dimension: K = 2^16 for fc1 and dgrad
     (1 << 18, 64, 48, "f32"),        # the fp32 kernel over many tokens
+    (32, 1 << 21, 16, "bf16"),       # the widest hidden size the calls accept (K = 2^21 for fc1)
+    (48, 16, 1 << 21, "bf16"),       # the widest ffn shard they accept (K = 2^21 for fc2)
 ])
 def test_extreme_shapes(tp, T, H, Fs, dtype):
     """Very long token counts and very wide rows (64-bit offsets, large tile
