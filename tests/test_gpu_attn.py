@@ -74,6 +74,9 @@ def _check(got, ref, tol, names=NAMES + ("q", "k", "v")):
 @pytest.mark.parametrize("T,H,nq,nkv,hn,bias", [
     (300, 528, 4, 2, 64, True), (37, 48, 2, 1, 16, False), (513, 1040, 6, 3, 32, True),
     (1, 64, 1, 1, 16, True), (4096, 1024, 8, 8, 64, True), (260, 272, 3, 3, 128, False),
+    # the widest hidden size the calls accept (2^21), and the widest q|k|v
+    # (3 x 699040 = 2^21 - 32 features; K = 699040 for the out-projection)
+    (32, 1 << 21, 1, 1, 16, True), (16, 64, 1, 1, 699040, False),
 ])
 def test_attn_small_and_ragged(tp, T, H, nq, nkv, hn, bias):
     w = synth.ATTN_WORKLOADS[6]

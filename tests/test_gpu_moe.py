@@ -100,6 +100,8 @@ CASES = [
     ([1024, 768], 512, 512, "swiglu", False),
     # 9 tile columns in each expert's dW1, more than its stages
     ([130, 0, 64, 7], 2304, 80, "gelu", True),
+    # the most experts the calls accept (1024), each with 0 to 4 rows
+    ([(7 * i) % 5 for i in range(1024)], 64, 16, "gelu", True),
 ]
 
 
